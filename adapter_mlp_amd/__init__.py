@@ -1,0 +1,324 @@
+"""Fused LoRA / QLoRA projections for AMD MI355X (gfx950).
+
+Thin Python layer over the C-ABI library ``liblora_mi355x.so``: it allocates
+outputs and workspace with PyTorch (device memory and streams only), fills
+the C descriptors and calls the library.  All arithmetic runs in the
+library's HIP kernels.
+
+Layouts follow the C header: W [n_in, n_out], A [n_in, r], B [r, n_out],
+row-major; bf16 or fp32 compute; NF4 bases in bf16.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+from typing import Optional
+
+from . import _lib as L
+
+__all__ = [
+    "Proj", "NF4Weight", "load", "LoraError",
+    "mlp_fwd", "mlp_bwd", "mlp_workspace_size",
+    "qkv_fwd", "qkv_bwd", "o_fwd", "o_bwd",
+    "nf4_quantize", "nf4_dequant", "nf4_unpack_codes", "nf4_gemm", "nf4_codebook",
+]
+
+load = L.load
+LoraError = L.LoraError
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return L.LORA_BF16
+    if t.dtype == torch.float32:
+        return L.LORA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ws(nbytes: int, device):
+    torch = _torch()
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+@dataclass
+class NF4Weight:
+    """NF4-packed weight W [rows, cols] (device tensors)."""
+
+    codes: object  # uint8 [numel/2]
+    q8: object     # int8 [numel/64]
+    s2: object     # float32 [numel/16384]
+    mu: object     # float32 [1]
+    rows: int
+    cols: int
+
+    def c_struct(self) -> L.lora_nf4:
+        return L.lora_nf4(_ptr(self.codes), _ptr(self.q8), _ptr(self.s2), _ptr(self.mu), self.rows, self.cols)
+
+
+@dataclass
+class Proj:
+    """One LoRA projection: dense W or NF4 weight, adapters A, B and scale s."""
+
+    A: object
+    B: object
+    scale: float
+    W: object = None
+    nf4: Optional[NF4Weight] = None
+
+    def c_struct(self, keep: list) -> L.lora_proj:
+        p = L.lora_proj()
+        p.W = _ptr(self.W)
+        if self.nf4 is not None:
+            s = self.nf4.c_struct()
+            keep.append(s)
+            p.nf4 = C.pointer(s)
+        p.A = _ptr(self.A)
+        p.B = _ptr(self.B)
+        p.scale = float(self.scale)
+        return p
+
+
+# ---------------------------------------------------------------------------
+# MLP
+# ---------------------------------------------------------------------------
+
+def mlp_workspace_size(T, H, I, r, act="swiglu", dtype=L.LORA_BF16):
+    d = L.lora_mlp_desc(T, H, I, r, L.ACT_CODES[act], dtype)
+    f, b = C.c_size_t(), C.c_size_t()
+    L.call("lora_mlp_workspace_size", C.byref(d), C.byref(f), C.byref(b))
+    return f.value, b.value
+
+
+def mlp_fwd(X, gate: Proj, up: Proj, down: Proj, act="swiglu", *, Y=None, saved=None, ws=None, stream=None):
+    """Y = down(phi(gate(X)) * up(X)).  Returns (Y, saved) with saved = dict(e, g, U)."""
+    torch = _torch()
+    T, H = X.shape
+    I = gate.B.shape[1]
+    r = gate.A.shape[1]
+    dt = _dtype_code(X)
+    d = L.lora_mlp_desc(T, H, I, r, L.ACT_CODES[act], dt)
+    fb, _ = mlp_workspace_size(T, H, I, r, act, dt)
+    if Y is None:
+        Y = torch.empty((T, H), dtype=X.dtype, device=X.device)
+    if saved is None:
+        saved = dict(e=torch.empty((T, I), dtype=X.dtype, device=X.device),
+                     g=torch.empty((T, I), dtype=X.dtype, device=X.device),
+                     U=torch.empty((T, 3 * r), dtype=X.dtype, device=X.device))
+    if ws is None:
+        ws = _ws(fb, X.device)
+    keep = []
+    sv = L.lora_mlp_saved(_ptr(saved["e"]), _ptr(saved["g"]), _ptr(saved["U"]))
+    L.call("lora_mlp_fwd", C.byref(d), _ptr(X), C.byref(gate.c_struct(keep)), C.byref(up.c_struct(keep)),
+           C.byref(down.c_struct(keep)), _ptr(Y), C.byref(sv), _ptr(ws), ws.numel(), _stream(stream))
+    return Y, saved
+
+
+def mlp_bwd(dY, X, saved, gate: Proj, up: Proj, down: Proj, act="swiglu", *, dX=None, grads=None, ws=None,
+            stream=None):
+    """Returns (dX, grads) with grads = dict(dA_gate, dB_gate, dA_up, dB_up, dA_down, dB_down)."""
+    torch = _torch()
+    T, H = X.shape
+    I = gate.B.shape[1]
+    r = gate.A.shape[1]
+    dt = _dtype_code(X)
+    d = L.lora_mlp_desc(T, H, I, r, L.ACT_CODES[act], dt)
+    _, bb = mlp_workspace_size(T, H, I, r, act, dt)
+    if dX is None:
+        dX = torch.empty_like(X)
+    if grads is None:
+        grads = dict(dA_gate=torch.empty_like(gate.A), dB_gate=torch.empty_like(gate.B),
+                     dA_up=torch.empty_like(up.A), dB_up=torch.empty_like(up.B),
+                     dA_down=torch.empty_like(down.A), dB_down=torch.empty_like(down.B))
+    if ws is None:
+        ws = _ws(bb, X.device)
+    keep = []
+    sv = L.lora_mlp_saved(_ptr(saved["e"]), _ptr(saved["g"]), _ptr(saved["U"]))
+    gr = L.lora_mlp_grads(*(_ptr(grads[k]) for k in ("dA_gate", "dB_gate", "dA_up", "dB_up", "dA_down", "dB_down")))
+    L.call("lora_mlp_bwd", C.byref(d), _ptr(dY), _ptr(X), C.byref(sv), C.byref(gate.c_struct(keep)),
+           C.byref(up.c_struct(keep)), C.byref(down.c_struct(keep)), _ptr(dX), C.byref(gr), _ptr(ws),
+           ws.numel(), _stream(stream))
+    return dX, grads
+
+
+# ---------------------------------------------------------------------------
+# Q/K/V and O
+# ---------------------------------------------------------------------------
+
+def qkv_workspace_size(T, H, Nq, Nk, Nv, r, dtype=L.LORA_BF16):
+    d = L.lora_qkv_desc(T, H, Nq, Nk, Nv, r, dtype, 0)
+    f, b = C.c_size_t(), C.c_size_t()
+    L.call("lora_qkv_workspace_size", C.byref(d), C.byref(f), C.byref(b))
+    return f.value, b.value
+
+
+def qkv_fwd(X, q: Proj, k: Proj, v: Proj, *, out=None, U=None, ws=None, stream=None):
+    """Returns (Q, K, V, U) with U = [X A_q | X A_k | X A_v]."""
+    torch = _torch()
+    T, H = X.shape
+    Ns = [p.B.shape[1] for p in (q, k, v)]
+    r = q.A.shape[1]
+    dt = _dtype_code(X)
+    d = L.lora_qkv_desc(T, H, Ns[0], Ns[1], Ns[2], r, dt, 0)
+    fb, _ = qkv_workspace_size(T, H, *Ns, r, dt)
+    if out is None:
+        out = [torch.empty((T, n), dtype=X.dtype, device=X.device) for n in Ns]
+    if U is None:
+        U = torch.empty((T, 3 * r), dtype=X.dtype, device=X.device)
+    if ws is None:
+        ws = _ws(fb, X.device)
+    keep = []
+    L.call("lora_qkv_fwd", C.byref(d), _ptr(X), C.byref(q.c_struct(keep)), C.byref(k.c_struct(keep)),
+           C.byref(v.c_struct(keep)), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _ptr(U), _ptr(ws), ws.numel(),
+           _stream(stream))
+    return out[0], out[1], out[2], U
+
+
+def qkv_bwd(dQ, dK, dV, X, U, q: Proj, k: Proj, v: Proj, *, dX=None, grads=None, ws=None, stream=None):
+    torch = _torch()
+    T, H = X.shape
+    Ns = [p.B.shape[1] for p in (q, k, v)]
+    r = q.A.shape[1]
+    dt = _dtype_code(X)
+    d = L.lora_qkv_desc(T, H, Ns[0], Ns[1], Ns[2], r, dt, 0)
+    _, bb = qkv_workspace_size(T, H, *Ns, r, dt)
+    if dX is None:
+        dX = torch.empty_like(X)
+    if grads is None:
+        grads = dict(dA_q=torch.empty_like(q.A), dB_q=torch.empty_like(q.B), dA_k=torch.empty_like(k.A),
+                     dB_k=torch.empty_like(k.B), dA_v=torch.empty_like(v.A), dB_v=torch.empty_like(v.B))
+    if ws is None:
+        ws = _ws(bb, X.device)
+    keep = []
+    gr = L.lora_qkv_grads(*(_ptr(grads[n]) for n in ("dA_q", "dB_q", "dA_k", "dB_k", "dA_v", "dB_v")))
+    L.call("lora_qkv_bwd", C.byref(d), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(X), _ptr(U), C.byref(q.c_struct(keep)),
+           C.byref(k.c_struct(keep)), C.byref(v.c_struct(keep)), _ptr(dX), C.byref(gr), _ptr(ws), ws.numel(),
+           _stream(stream))
+    return dX, grads
+
+
+def o_workspace_size(T, K, N, r, dtype=L.LORA_BF16):
+    d = L.lora_o_desc(T, K, N, r, dtype, 0)
+    f, b = C.c_size_t(), C.c_size_t()
+    L.call("lora_o_workspace_size", C.byref(d), C.byref(f), C.byref(b))
+    return f.value, b.value
+
+
+def o_fwd(X, o: Proj, *, Y=None, U=None, ws=None, stream=None):
+    """Returns (Y, U)."""
+    torch = _torch()
+    T, K = X.shape
+    N = o.B.shape[1]
+    r = o.A.shape[1]
+    dt = _dtype_code(X)
+    d = L.lora_o_desc(T, K, N, r, dt, 0)
+    fb, _ = o_workspace_size(T, K, N, r, dt)
+    if Y is None:
+        Y = torch.empty((T, N), dtype=X.dtype, device=X.device)
+    if U is None:
+        U = torch.empty((T, r), dtype=X.dtype, device=X.device)
+    if ws is None:
+        ws = _ws(fb, X.device)
+    keep = []
+    L.call("lora_o_fwd", C.byref(d), _ptr(X), C.byref(o.c_struct(keep)), _ptr(Y), _ptr(U), _ptr(ws), ws.numel(),
+           _stream(stream))
+    return Y, U
+
+
+def o_bwd(dY, X, U, o: Proj, *, dX=None, dA=None, dB=None, ws=None, stream=None):
+    """Returns (dX, dA, dB)."""
+    torch = _torch()
+    T, K = X.shape
+    N = o.B.shape[1]
+    r = o.A.shape[1]
+    dt = _dtype_code(X)
+    d = L.lora_o_desc(T, K, N, r, dt, 0)
+    _, bb = o_workspace_size(T, K, N, r, dt)
+    dX = torch.empty_like(X) if dX is None else dX
+    dA = torch.empty_like(o.A) if dA is None else dA
+    dB = torch.empty_like(o.B) if dB is None else dB
+    if ws is None:
+        ws = _ws(bb, X.device)
+    keep = []
+    L.call("lora_o_bwd", C.byref(d), _ptr(dY), _ptr(X), _ptr(U), C.byref(o.c_struct(keep)), _ptr(dX), _ptr(dA),
+           _ptr(dB), _ptr(ws), ws.numel(), _stream(stream))
+    return dX, dA, dB
+
+
+# ---------------------------------------------------------------------------
+# NF4
+# ---------------------------------------------------------------------------
+
+def nf4_codebook():
+    buf = (C.c_float * 16)()
+    L.load().lora_nf4_codebook(buf)
+    return list(buf)
+
+
+def nf4_quantize(W, *, stream=None) -> NF4Weight:
+    """Quantize a device weight W [rows, cols] (fp32 or bf16) to NF4 on the GPU."""
+    torch = _torch()
+    rows, cols = W.shape
+    n = rows * cols
+    nbytes = C.c_size_t()
+    L.call("lora_nf4_quantize_workspace_size", rows, cols, C.byref(nbytes))
+    dev = W.device
+    w = NF4Weight(codes=torch.empty(n // 2, dtype=torch.uint8, device=dev),
+                  q8=torch.empty(n // 64, dtype=torch.int8, device=dev),
+                  s2=torch.empty(n // 16384, dtype=torch.float32, device=dev),
+                  mu=torch.empty(1, dtype=torch.float32, device=dev), rows=rows, cols=cols)
+    ws = _ws(nbytes.value, dev)
+    L.call("lora_nf4_quantize", _ptr(W), rows, cols, _dtype_code(W), _ptr(w.codes), _ptr(w.q8), _ptr(w.s2),
+           _ptr(w.mu), _ptr(ws), ws.numel(), _stream(stream))
+    return w
+
+
+def nf4_dequant(w: NF4Weight, dtype=None, *, stream=None):
+    torch = _torch()
+    dtype = torch.bfloat16 if dtype is None else dtype
+    out = torch.empty((w.rows, w.cols), dtype=dtype, device=w.codes.device)
+    s = w.c_struct()
+    L.call("lora_nf4_dequant", C.byref(s), _ptr(out), _dtype_code(out), _stream(stream))
+    return out
+
+
+def nf4_unpack_codes(w: NF4Weight, *, stream=None):
+    torch = _torch()
+    out = torch.empty(w.rows * w.cols, dtype=torch.uint8, device=w.codes.device)
+    s = w.c_struct()
+    L.call("lora_nf4_unpack_codes", C.byref(s), _ptr(out), _stream(stream))
+    return out
+
+
+def nf4_gemm(X, w: NF4Weight, A=None, B=None, scale=0.0, trans=False, *, Y=None, ws=None, stream=None):
+    """trans=False: Y = X deq(W) + s (X A) B;  trans=True: Y = X deq(W)^T + s (X B^T) A^T."""
+    torch = _torch()
+    T = X.shape[0]
+    r = 0 if A is None else A.shape[1]
+    nbytes = C.c_size_t()
+    L.call("lora_nf4_gemm_workspace_size", T, w.rows, w.cols, r, int(trans), C.byref(nbytes))
+    n_out = w.rows if trans else w.cols
+    if Y is None:
+        Y = torch.empty((T, n_out), dtype=X.dtype, device=X.device)
+    if ws is None:
+        ws = _ws(nbytes.value, X.device)
+    s = w.c_struct()
+    L.call("lora_nf4_gemm", T, int(trans), _ptr(X), C.byref(s), _ptr(A), _ptr(B), r, float(scale), _ptr(Y),
+           _ptr(ws), ws.numel(), _stream(stream))
+    return Y

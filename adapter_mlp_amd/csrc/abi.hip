@@ -1,0 +1,1113 @@
+// C-ABI entry points: argument validation, workspace planning and the kernel
+// sequence of each call.  Every check runs on the host before the first
+// enqueue, so a call that returns an error has enqueued nothing.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "common.hpp"
+#include "kernels.hpp"
+#include "trace.hpp"
+
+using namespace lora;
+
+namespace {
+
+thread_local std::string g_last_error = "no error";
+
+lora_status fail(lora_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+lora_status fail(lora_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+#define CHECK(cond, status, ...)          \
+  do {                                    \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+#define LAUNCH(expr)                                                              \
+  do {                                                                            \
+    hipError_t e_ = (expr);                                                       \
+    if (e_ != hipSuccess) return fail(LORA_EDEVICE, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+// LAUNCH with the launch bracketed for lora_trace_* under `name`.
+#define LAUNCHN(name, stream, expr)       \
+  do {                                    \
+    TraceScope ts_(name, stream);         \
+    LAUNCH(expr);                         \
+  } while (0)
+
+inline int64_t pad16(int64_t x) { return (x + 15) / 16 * 16; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Ctx {
+  bool bf16;
+  size_t es;  // element size
+  int64_t rl(int64_t w) const { return bf16 ? pad16(w) : w; }  // LoRA tail width in the GEMM
+};
+
+// Bump allocator over the caller's workspace (256-byte aligned pieces).
+struct Ws {
+  char* base;
+  size_t off = 0;
+  explicit Ws(void* b) : base(static_cast<char*>(b)) {}
+  void* take(size_t bytes) {
+    off = (off + 255) & ~(size_t)255;
+    void* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  }
+};
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+lora_status check_dtype(int32_t dtype, Ctx& c) {
+  CHECK(dtype == LORA_F32 || dtype == LORA_BF16, LORA_EDTYPE, "unknown dtype %d", dtype);
+  c.bf16 = dtype == LORA_BF16;
+  c.es = c.bf16 ? 2 : 4;
+  return LORA_OK;
+}
+
+lora_status check_dim(const Ctx& c, int64_t v, const char* name) {
+  CHECK(v > 0, LORA_ESHAPE, "%s = %lld must be positive", name, (long long)v);
+  if (c.bf16) CHECK(v % 64 == 0, LORA_ESHAPE, "%s = %lld must be a multiple of 64 for bf16", name, (long long)v);
+  return LORA_OK;
+}
+
+lora_status check_rank(const Ctx& c, int64_t r, int group) {
+  CHECK(r >= 1 && r <= 64, LORA_ESHAPE, "rank r = %lld must be in [1, 64]", (long long)r);
+  if (c.bf16) {
+    CHECK(r % 8 == 0, LORA_ESHAPE, "rank r = %lld must be a multiple of 8 for bf16", (long long)r);
+    CHECK(r * group <= 64, LORA_ESHAPE, "adapter group width %lld exceeds 64", (long long)(r * group));
+  }
+  return LORA_OK;
+}
+
+lora_status check_ptr(const Ctx& c, const void* p, const char* name) {
+  CHECK(p != nullptr, LORA_EINVAL, "%s is NULL", name);
+  CHECK(aligned(p, c.bf16 ? 16 : 4), LORA_EALIGN, "%s is not %d-byte aligned", name, c.bf16 ? 16 : 4);
+  return LORA_OK;
+}
+
+// A tensor with T rows may be NULL when T == 0 (an empty allocation).
+lora_status check_tptr(const Ctx& c, const void* p, int64_t T, const char* name) {
+  if (T == 0 && p == nullptr) return LORA_OK;
+  return check_ptr(c, p, name);
+}
+
+#define TRY(expr)                    \
+  do {                               \
+    lora_status s_ = (expr);         \
+    if (s_ != LORA_OK) return s_;    \
+  } while (0)
+
+lora_status check_nf4(const lora_nf4* q, int64_t rows, int64_t cols, const char* name) {
+  CHECK(q->codes && q->q8 && q->s2 && q->mu, LORA_EINVAL, "%s: NF4 array pointer is NULL", name);
+  CHECK(q->rows == rows && q->cols == cols, LORA_ESHAPE,
+        "%s: NF4 weight is [%lld, %lld], expected [%lld, %lld]", name, (long long)q->rows,
+        (long long)q->cols, (long long)rows, (long long)cols);
+  CHECK((rows * cols) % NF4_GROUP == 0, LORA_ESHAPE, "%s: NF4 numel %lld not a multiple of %lld", name,
+        (long long)(rows * cols), (long long)NF4_GROUP);
+  CHECK(aligned(q->codes, 4) && aligned(q->s2, 4) && aligned(q->mu, 4), LORA_EALIGN,
+        "%s: NF4 codes/s2/mu must be 4-byte aligned", name);
+  return LORA_OK;
+}
+
+lora_status check_proj(const Ctx& c, const lora_proj* p, int64_t n_in, int64_t n_out, const char* name) {
+  CHECK(p != nullptr, LORA_EINVAL, "%s is NULL", name);
+  CHECK((p->W != nullptr) != (p->nf4 != nullptr), LORA_EINVAL, "%s: exactly one of W and nf4 must be set", name);
+  if (p->nf4) {
+    CHECK(c.bf16, LORA_EUNSUPPORTED, "%s: NF4 base needs the bf16 compute dtype", name);
+    TRY(check_nf4(p->nf4, n_in, n_out, name));
+  } else {
+    TRY(check_ptr(c, p->W, name));
+  }
+  TRY(check_ptr(c, p->A, name));
+  TRY(check_ptr(c, p->B, name));
+  CHECK(std::isfinite(p->scale), LORA_EINVAL, "%s: scale is not finite", name);
+  return LORA_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const char* x = static_cast<const char*>(a);
+  const char* y = static_cast<const char*>(b);
+  return x < y + nb && y < x + na;
+}
+
+BSrc bsrc(const lora_proj* p, int64_t ld) {
+  BSrc s{};
+  if (p->nf4) {
+    s.codes = p->nf4->codes;
+    s.q8 = p->nf4->q8;
+    s.s2 = p->nf4->s2;
+    s.mu = p->nf4->mu;
+    s.wcols = p->nf4->cols;
+  } else {
+    s.p = p->W;
+    s.ld = ld;
+  }
+  return s;
+}
+
+const void* coff(const void* p, int64_t elems, const Ctx& c) {
+  return static_cast<const char*>(p) + elems * (int64_t)c.es;
+}
+void* offw(void* p, int64_t elems, const Ctx& c) { return static_cast<char*>(p) + elems * (int64_t)c.es; }
+
+hipError_t gemm_on(const Ctx& c, GemmArgs& g, hipStream_t st) {
+  const int64_t rows = gemm_tile_rows(c.bf16);
+  const int64_t cols = gemm_tile_cols(c.bf16, g.dual != 0);
+  g.ntile_m = cdiv(g.M, rows);
+  int64_t tiles = 0;
+  for (int p = 0; p < g.nreg; ++p) {
+    g.reg[p].tile0 = tiles;
+    tiles += cdiv(g.reg[p].N, cols);
+  }
+  g.ntile_n = tiles;
+  char name[48];
+  std::snprintf(name, sizeof name, "gemm_%s_%s%s%s", g.bkind == B_NN ? "nn" : "nt",
+                g.epi == EPI_STORE ? "store" : (g.epi == EPI_ACT_FWD ? "act_fwd" : "act_bwd"),
+                g.nf4 ? "_nf4" : "", c.bf16 ? "" : "_f32");
+  TraceScope ts(name, st);
+  return c.bf16 ? launch_gemm_bf16(g, st) : launch_gemm_f32(g, st);
+}
+
+RowProjArgs rowproj_args(const void* Z, int64_t ldz, int64_t T, int64_t K, const void* Bt, int64_t ldb,
+                         int R, int R2, int seg_w) {
+  RowProjArgs a{};
+  a.Z = Z;
+  a.ldz = ldz;
+  a.T = T;
+  a.K = K;
+  a.Bt = Bt;
+  a.ldb = ldb;
+  a.R = R;
+  a.R2 = R2;
+  a.seg_w = seg_w;
+  return a;
+}
+
+ColProjArgs colproj_args(const void* Z, int64_t ldz, int64_t T, int64_t K, const void* P, int64_t ldp, int R,
+                         int seg_w, bool transposed, float* partial) {
+  ColProjArgs a{};
+  a.Z = Z;
+  a.ldz = ldz;
+  a.T = T;
+  a.K = K;
+  a.P = P;
+  a.ldp = ldp;
+  a.R = R;
+  a.seg_w = seg_w;
+  a.transposed = transposed ? 1 : 0;
+  a.partial = partial;
+  return a;
+}
+
+PackPart part(const void* src, int64_t ld, int64_t v0, int64_t nv, int k0, int w, bool nn) {
+  PackPart p{};
+  p.src = src;
+  p.ld = ld;
+  p.v0 = v0;
+  p.nv = nv;
+  p.k0 = k0;
+  p.w = w;
+  p.nn = nn ? 1 : 0;
+  return p;
+}
+
+lora_status check_ws(const void* ws, size_t have, size_t need) {
+  CHECK(have >= need, LORA_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", have, need);
+  CHECK(need == 0 || ws != nullptr, LORA_EWORKSPACE, "workspace is NULL");
+  CHECK(aligned(ws, 16), LORA_EALIGN, "workspace is not 16-byte aligned");
+  return LORA_OK;
+}
+
+float* partial_buf(Ws& w, const Ctx& c, int64_t T, int64_t K, int R) {
+  if (!c.bf16) return nullptr;
+  return static_cast<float*>(w.take((size_t)colproj_partial_floats(T, K, R) * 4));
+}
+
+// ---------------------------------------------------------------------------
+// MLP
+// ---------------------------------------------------------------------------
+struct MlpPlan {
+  void *At_gu, *Us_gu, *BLt_gu, *h, *At_d, *Us_d, *BLt_d;                  // forward
+  void *Ps_d, *BLt_dh, *hb, *dg, *de, *Ps_ug, *BLt_dx;                      // backward
+  float* partial;
+  size_t fwd_bytes, bwd_bytes;
+};
+
+MlpPlan plan_mlp(const Ctx& c, const lora_mlp_desc& d, void* ws_fwd, void* ws_bwd) {
+  MlpPlan p{};
+  const int64_t T = d.T, H = d.H, I = d.I, r = d.r;
+  const int64_t RLg = c.rl(2 * r), RLd = c.rl(r);
+  Ws f(ws_fwd);
+  p.At_gu = f.take(2 * r * H * c.es);
+  p.Us_gu = f.take(T * RLg * c.es);
+  p.BLt_gu = f.take(2 * I * RLg * c.es);
+  p.h = f.take(T * I * c.es);
+  p.At_d = f.take(r * I * c.es);
+  p.Us_d = f.take(T * RLd * c.es);
+  p.BLt_d = f.take(H * RLd * c.es);
+  p.fwd_bytes = f.off;
+  Ws b(ws_bwd);
+  p.Ps_d = b.take(T * RLd * c.es);
+  p.BLt_dh = b.take(I * RLd * c.es);
+  p.hb = b.take(T * I * c.es);
+  p.dg = b.take(T * I * c.es);
+  p.de = b.take(T * I * c.es);
+  p.Ps_ug = b.take(T * RLg * c.es);
+  p.BLt_dx = b.take(H * RLg * c.es);
+  int64_t pf = 0;
+  if (c.bf16) {
+    const int64_t cands[4] = {colproj_partial_floats(T, H, (int)r), colproj_partial_floats(T, I, (int)r),
+                              colproj_partial_floats(T, H, (int)(2 * r)), 0};
+    for (int i = 0; i < 3; ++i) pf = cands[i] > pf ? cands[i] : pf;
+  }
+  p.partial = static_cast<float*>(b.take((size_t)pf * 4));
+  p.bwd_bytes = b.off;
+  return p;
+}
+
+lora_status validate_mlp(const lora_mlp_desc* d, Ctx& c) {
+  CHECK(d != nullptr, LORA_EINVAL, "desc is NULL");
+  TRY(check_dtype(d->dtype, c));
+  CHECK(d->act == LORA_ACT_SWIGLU || d->act == LORA_ACT_GEGLU_TANH, LORA_EINVAL, "unknown activation %d", d->act);
+  CHECK(d->T >= 0, LORA_ESHAPE, "T = %lld is negative", (long long)d->T);
+  TRY(check_dim(c, d->H, "H"));
+  TRY(check_dim(c, d->I, "I"));
+  TRY(check_rank(c, d->r, 2));
+  return LORA_OK;
+}
+
+
+// ---------------------------------------------------------------------------
+// Q/K/V and O
+// ---------------------------------------------------------------------------
+struct QkvPlan {
+  void *At, *Us, *BLt;     // forward
+  void *Ps, *BLt_dx;       // backward
+  float* partial;
+  size_t fwd_bytes, bwd_bytes;
+};
+
+QkvPlan plan_qkv(const Ctx& c, const lora_qkv_desc& d, void* wf, void* wb) {
+  QkvPlan p{};
+  const int64_t T = d.T, H = d.H, r = d.r, N = d.Nq + d.Nk + d.Nv;
+  const int64_t RL = c.rl(3 * r);
+  Ws f(wf);
+  p.At = f.take(3 * r * H * c.es);
+  p.Us = f.take(T * RL * c.es);
+  p.BLt = f.take(N * RL * c.es);
+  p.fwd_bytes = f.off;
+  Ws b(wb);
+  p.Ps = b.take(T * RL * c.es);
+  p.BLt_dx = b.take(H * RL * c.es);
+  int64_t pf = 0;
+  if (c.bf16) {
+    const int64_t cand[4] = {colproj_partial_floats(T, d.Nq, (int)r), colproj_partial_floats(T, d.Nk, (int)r),
+                             colproj_partial_floats(T, d.Nv, (int)r), colproj_partial_floats(T, H, (int)(3 * r))};
+    for (int i = 0; i < 4; ++i) pf = cand[i] > pf ? cand[i] : pf;
+  }
+  p.partial = static_cast<float*>(b.take((size_t)pf * 4));
+  p.bwd_bytes = b.off;
+  return p;
+}
+
+lora_status validate_qkv(const lora_qkv_desc* d, Ctx& c) {
+  CHECK(d != nullptr, LORA_EINVAL, "desc is NULL");
+  TRY(check_dtype(d->dtype, c));
+  CHECK(d->reserved == 0, LORA_EINVAL, "reserved field must be 0");
+  CHECK(d->T >= 0, LORA_ESHAPE, "T = %lld is negative", (long long)d->T);
+  TRY(check_dim(c, d->H, "H"));
+  TRY(check_dim(c, d->Nq, "Nq"));
+  TRY(check_dim(c, d->Nk, "Nk"));
+  TRY(check_dim(c, d->Nv, "Nv"));
+  TRY(check_rank(c, d->r, 3));
+  return LORA_OK;
+}
+
+struct OPlan {
+  void *At, *Us, *BLt, *U_tmp;
+  void *Ps, *BLt_dx;
+  float* partial;
+  size_t fwd_bytes, bwd_bytes;
+};
+
+// Shared by lora_o_* and lora_nf4_gemm: n_in = K, n_out = N.
+OPlan plan_o(const Ctx& c, int64_t T, int64_t K, int64_t N, int64_t r, bool tmp_u, void* wf, void* wb) {
+  OPlan p{};
+  const int64_t RL = c.rl(r);
+  Ws f(wf);
+  p.At = f.take(r * K * c.es);
+  p.Us = f.take(T * RL * c.es);
+  p.BLt = f.take(N * RL * c.es);
+  p.U_tmp = tmp_u ? f.take(T * r * c.es) : nullptr;
+  p.fwd_bytes = f.off;
+  Ws b(wb);
+  p.Ps = b.take(T * RL * c.es);
+  p.BLt_dx = b.take(K * RL * c.es);
+  int64_t pf = 0;
+  if (c.bf16) {
+    const int64_t a = colproj_partial_floats(T, N, (int)r), bb = colproj_partial_floats(T, K, (int)r);
+    pf = a > bb ? a : bb;
+  }
+  p.partial = static_cast<float*>(b.take((size_t)pf * 4));
+  p.bwd_bytes = b.off;
+  return p;
+}
+
+lora_status validate_o(const lora_o_desc* d, Ctx& c) {
+  CHECK(d != nullptr, LORA_EINVAL, "desc is NULL");
+  TRY(check_dtype(d->dtype, c));
+  CHECK(d->reserved == 0, LORA_EINVAL, "reserved field must be 0");
+  CHECK(d->T >= 0, LORA_ESHAPE, "T = %lld is negative", (long long)d->T);
+  TRY(check_dim(c, d->K, "K"));
+  TRY(check_dim(c, d->N, "N"));
+  TRY(check_rank(c, d->r, 1));
+  return LORA_OK;
+}
+
+// Forward of one projection: Y = X W + s (X A) B, U = X A (to U if non-NULL).
+lora_status proj_forward(const Ctx& c, int64_t T, int64_t K, int64_t N, int64_t r, const void* X,
+                         const lora_proj* o, void* Y, void* U, const OPlan& p, hipStream_t st) {
+  const int64_t RL = c.rl(r);
+  const bool lora = r > 0;
+  GemmArgs g{};
+  if (lora) {
+    const void* srcs[1] = {o->A};
+    LAUNCHN("pack", st, launch_pack_cat_t(c.bf16, p.At, K, (int)r, (int)r, 1, srcs, st));
+    RowProjArgs ra = rowproj_args(X, K, T, K, p.At, K, (int)r, (int)RL, (int)r);
+    ra.scales[0] = o->scale;
+    ra.out1 = U;
+    ra.ld1 = r;
+    ra.out2 = p.Us;
+    ra.ld2 = RL;
+    LAUNCHN("rowproj", st, launch_rowproj(c.bf16, ra, st));
+    PackLoraArgs pl{};
+    pl.out = p.BLt;
+    pl.vcols = N;
+    pl.RL = (int)RL;
+    pl.nparts = 1;
+    pl.part[0] = part(o->B, N, 0, N, 0, (int)r, true);
+    LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, pl, st));
+    g.AL = p.Us;
+    g.ldal = RL;
+    g.RL = (int)RL;
+    g.BLt = p.BLt;
+    g.ldbl = RL;
+  }
+  g.M = T;
+  g.nseg = 1;
+  g.nreg = 1;
+  g.epi = EPI_STORE;
+  g.nf4 = o->nf4 != nullptr;
+  g.bkind = B_NN;
+  g.seg[0].A = X;
+  g.seg[0].lda = K;
+  g.seg[0].K = K;
+  g.seg[0].b[0][0] = bsrc(o, N);
+  g.reg[0].N = N;
+  g.reg[0].out = Y;
+  g.reg[0].ldo = N;
+  LAUNCH(gemm_on(c, g, st));
+  return LORA_OK;
+}
+
+// Input-gradient GEMM of one projection: dX = dY W^T + (s P) A^T with
+// s P = Ps [T, RL] (already formed); A rows feed the LoRA tail.
+lora_status proj_input_grad(const Ctx& c, int64_t T, int64_t K, int64_t N, int64_t r, const void* dY,
+                            const lora_proj* o, void* dX, const OPlan& p, hipStream_t st) {
+  const int64_t RL = c.rl(r);
+  GemmArgs g{};
+  if (r > 0) {
+    PackLoraArgs pl{};
+    pl.out = p.BLt_dx;
+    pl.vcols = K;
+    pl.RL = (int)RL;
+    pl.nparts = 1;
+    pl.part[0] = part(o->A, r, 0, K, 0, (int)r, false);
+    LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, pl, st));
+    g.AL = p.Ps;
+    g.ldal = RL;
+    g.RL = (int)RL;
+    g.BLt = p.BLt_dx;
+    g.ldbl = RL;
+  }
+  g.M = T;
+  g.nseg = 1;
+  g.nreg = 1;
+  g.epi = EPI_STORE;
+  g.nf4 = o->nf4 != nullptr;
+  g.bkind = B_NT;
+  g.seg[0].A = dY;
+  g.seg[0].lda = N;
+  g.seg[0].K = N;
+  g.seg[0].b[0][0] = bsrc(o, N);
+  g.reg[0].N = K;
+  g.reg[0].out = dX;
+  g.reg[0].ldo = K;
+  LAUNCH(gemm_on(c, g, st));
+  return LORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lora_version(void) { return LORA_MI355X_VERSION; }
+
+const char* lora_strerror(lora_status s) {
+  switch (s) {
+    case LORA_OK: return "success";
+    case LORA_EINVAL: return "invalid argument";
+    case LORA_ESHAPE: return "unsupported shape";
+    case LORA_EDTYPE: return "invalid or mismatched dtype";
+    case LORA_EALIGN: return "misaligned pointer";
+    case LORA_EWORKSPACE: return "workspace missing or too small";
+    case LORA_EUNSUPPORTED: return "unsupported combination";
+    case LORA_EDEVICE: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* lora_last_error(void) { return g_last_error.c_str(); }
+
+void lora_nf4_codebook(float* out) {
+  if (out) std::memcpy(out, kNF4Levels, sizeof(kNF4Levels));
+}
+
+lora_status lora_mlp_workspace_size(const lora_mlp_desc* d, size_t* fwd, size_t* bwd) {
+  Ctx c{};
+  TRY(validate_mlp(d, c));
+  MlpPlan p = plan_mlp(c, *d, nullptr, nullptr);
+  if (fwd) *fwd = p.fwd_bytes;
+  if (bwd) *bwd = p.bwd_bytes;
+  return LORA_OK;
+}
+
+lora_status lora_mlp_fwd(const lora_mlp_desc* d, const void* X, const lora_proj* gate, const lora_proj* up,
+                         const lora_proj* down, void* Y, const lora_mlp_saved* saved, void* ws, size_t ws_bytes,
+                         void* stream) {
+  Ctx c{};
+  TRY(validate_mlp(d, c));
+  const int64_t T = d->T, H = d->H, I = d->I, r = d->r;
+  TRY(check_tptr(c, X, T, "X"));
+  TRY(check_tptr(c, Y, T, "Y"));
+  CHECK(saved != nullptr, LORA_EINVAL, "saved is NULL");
+  TRY(check_tptr(c, saved->e, T, "saved.e"));
+  TRY(check_tptr(c, saved->g, T, "saved.g"));
+  TRY(check_tptr(c, saved->U, T, "saved.U"));
+  TRY(check_proj(c, gate, H, I, "gate"));
+  TRY(check_proj(c, up, H, I, "up"));
+  TRY(check_proj(c, down, I, H, "down"));
+  CHECK(!overlaps(Y, T * H * c.es, X, T * H * c.es), LORA_EUNSUPPORTED, "Y aliases X");
+  MlpPlan need = plan_mlp(c, *d, nullptr, nullptr);
+  TRY(check_ws(ws, ws_bytes, need.fwd_bytes));
+  if (T == 0) return LORA_OK;
+  MlpPlan p = plan_mlp(c, *d, ws, nullptr);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t RLg = c.rl(2 * r), RLd = c.rl(r);
+
+  // adapter inputs of gate and up in one pass over X: [U_g | U_u] = X [A_g | A_u]
+  const void* srcs_gu[2] = {gate->A, up->A};
+  LAUNCHN("pack", st, launch_pack_cat_t(c.bf16, p.At_gu, H, (int)(2 * r), (int)r, 2, srcs_gu, st));
+  RowProjArgs ra = rowproj_args(X, H, T, H, p.At_gu, H, (int)(2 * r), (int)RLg, (int)r);
+  ra.scales[0] = gate->scale;
+  ra.scales[1] = up->scale;
+  ra.out1 = saved->U;
+  ra.ld1 = 3 * r;
+  ra.off1 = 0;
+  ra.out2 = p.Us_gu;
+  ra.ld2 = RLg;
+  LAUNCHN("rowproj", st, launch_rowproj(c.bf16, ra, st));
+
+  PackLoraArgs pl{};
+  pl.out = p.BLt_gu;
+  pl.vcols = 2 * I;
+  pl.RL = (int)RLg;
+  pl.nparts = 2;
+  pl.part[0] = part(gate->B, I, 0, I, 0, (int)r, true);
+  pl.part[1] = part(up->B, I, I, I, (int)r, (int)r, true);
+  LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, pl, st));
+
+  // gate/up GEMM with the activation epilogue
+  GemmArgs g{};
+  g.M = T;
+  g.nseg = 1;
+  g.nreg = 1;
+  g.dual = 1;
+  g.epi = EPI_ACT_FWD;
+  g.act = d->act;
+  g.nf4 = gate->nf4 != nullptr;
+  CHECK((gate->nf4 != nullptr) == (up->nf4 != nullptr), LORA_EUNSUPPORTED, "gate and up must both be NF4 or both dense");
+  g.bkind = B_NN;
+  g.seg[0].A = X;
+  g.seg[0].lda = H;
+  g.seg[0].K = H;
+  g.seg[0].b[0][0] = bsrc(gate, I);
+  g.seg[0].b[0][1] = bsrc(up, I);
+  g.reg[0].N = I;
+  g.reg[0].vcol0[0] = 0;
+  g.reg[0].vcol0[1] = I;
+  g.AL = p.Us_gu;
+  g.ldal = RLg;
+  g.RL = (int)RLg;
+  g.BLt = p.BLt_gu;
+  g.ldbl = RLg;
+  g.e_out = saved->e;
+  g.g_out = saved->g;
+  g.h_out = p.h;
+  g.ld_act = I;
+  LAUNCH(gemm_on(c, g, st));
+
+  // U_d = h A_d, then the down GEMM
+  const void* srcs_d[1] = {down->A};
+  LAUNCHN("pack", st, launch_pack_cat_t(c.bf16, p.At_d, I, (int)r, (int)r, 1, srcs_d, st));
+  RowProjArgs rd = rowproj_args(p.h, I, T, I, p.At_d, I, (int)r, (int)RLd, (int)r);
+  rd.scales[0] = down->scale;
+  rd.out1 = saved->U;
+  rd.ld1 = 3 * r;
+  rd.off1 = 2 * r;
+  rd.out2 = p.Us_d;
+  rd.ld2 = RLd;
+  LAUNCHN("rowproj", st, launch_rowproj(c.bf16, rd, st));
+  PackLoraArgs pd{};
+  pd.out = p.BLt_d;
+  pd.vcols = H;
+  pd.RL = (int)RLd;
+  pd.nparts = 1;
+  pd.part[0] = part(down->B, H, 0, H, 0, (int)r, true);
+  LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, pd, st));
+
+  GemmArgs gd{};
+  gd.M = T;
+  gd.nseg = 1;
+  gd.nreg = 1;
+  gd.epi = EPI_STORE;
+  gd.nf4 = down->nf4 != nullptr;
+  gd.bkind = B_NN;
+  gd.seg[0].A = p.h;
+  gd.seg[0].lda = I;
+  gd.seg[0].K = I;
+  gd.seg[0].b[0][0] = bsrc(down, H);
+  gd.reg[0].N = H;
+  gd.reg[0].out = Y;
+  gd.reg[0].ldo = H;
+  gd.AL = p.Us_d;
+  gd.ldal = RLd;
+  gd.RL = (int)RLd;
+  gd.BLt = p.BLt_d;
+  gd.ldbl = RLd;
+  LAUNCH(gemm_on(c, gd, st));
+  return LORA_OK;
+}
+
+lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, const lora_mlp_saved* saved,
+                         const lora_proj* gate, const lora_proj* up, const lora_proj* down, void* dX,
+                         const lora_mlp_grads* gr, void* ws, size_t ws_bytes, void* stream) {
+  Ctx c{};
+  TRY(validate_mlp(d, c));
+  const int64_t T = d->T, H = d->H, I = d->I, r = d->r;
+  TRY(check_tptr(c, dY, T, "dY"));
+  TRY(check_tptr(c, X, T, "X"));
+  TRY(check_tptr(c, dX, T, "dX"));
+  CHECK(saved != nullptr, LORA_EINVAL, "saved is NULL");
+  TRY(check_tptr(c, saved->e, T, "saved.e"));
+  TRY(check_tptr(c, saved->g, T, "saved.g"));
+  TRY(check_tptr(c, saved->U, T, "saved.U"));
+  CHECK(gr != nullptr, LORA_EINVAL, "grads is NULL");
+  TRY(check_ptr(c, gr->dA_gate, "dA_gate"));
+  TRY(check_ptr(c, gr->dB_gate, "dB_gate"));
+  TRY(check_ptr(c, gr->dA_up, "dA_up"));
+  TRY(check_ptr(c, gr->dB_up, "dB_up"));
+  TRY(check_ptr(c, gr->dA_down, "dA_down"));
+  TRY(check_ptr(c, gr->dB_down, "dB_down"));
+  TRY(check_proj(c, gate, H, I, "gate"));
+  TRY(check_proj(c, up, H, I, "up"));
+  TRY(check_proj(c, down, I, H, "down"));
+  CHECK((gate->nf4 != nullptr) == (up->nf4 != nullptr), LORA_EUNSUPPORTED, "gate and up must both be NF4 or both dense");
+  CHECK(!overlaps(dX, T * H * c.es, X, T * H * c.es), LORA_EUNSUPPORTED, "dX aliases X (in-place dX is not supported)");
+  MlpPlan need = plan_mlp(c, *d, nullptr, nullptr);
+  TRY(check_ws(ws, ws_bytes, need.bwd_bytes));
+  MlpPlan p = plan_mlp(c, *d, nullptr, ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t RLg = c.rl(2 * r), RLd = c.rl(r);
+  const void* U = saved->U;
+
+  // P_d = dY B_d^T, formed once (scaled copy feeds dA_d and the dh GEMM)
+  RowProjArgs r1 = rowproj_args(dY, H, T, H, down->B, H, (int)r, (int)RLd, (int)r);
+  r1.scales[0] = down->scale;
+  r1.out2 = p.Ps_d;
+  r1.ld2 = RLd;
+  LAUNCHN("rowproj", st, launch_rowproj(c.bf16, r1, st));
+  // dB_d = s_d U_d^T dY
+  ColProjArgs c1 = colproj_args(dY, H, T, H, coff(U, 2 * r, c), 3 * r, (int)r, (int)r, true, p.partial);
+  c1.scales[0] = down->scale;
+  c1.dest[0] = gr->dB_down;
+  LAUNCHN("colproj", st, launch_colproj(c.bf16, c1, st));
+
+  // dh GEMM with the activation-gradient epilogue -> dg, de, h
+  PackLoraArgs pl{};
+  pl.out = p.BLt_dh;
+  pl.vcols = I;
+  pl.RL = (int)RLd;
+  pl.nparts = 1;
+  pl.part[0] = part(down->A, r, 0, I, 0, (int)r, false);
+  LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, pl, st));
+  GemmArgs g{};
+  g.M = T;
+  g.nseg = 1;
+  g.nreg = 1;
+  g.epi = EPI_ACT_BWD;
+  g.act = d->act;
+  g.nf4 = down->nf4 != nullptr;
+  g.bkind = B_NT;
+  g.seg[0].A = dY;
+  g.seg[0].lda = H;
+  g.seg[0].K = H;
+  g.seg[0].b[0][0] = bsrc(down, H);
+  g.reg[0].N = I;
+  g.AL = p.Ps_d;
+  g.ldal = RLd;
+  g.RL = (int)RLd;
+  g.BLt = p.BLt_dh;
+  g.ldbl = RLd;
+  g.e_in = saved->e;
+  g.g_in = saved->g;
+  g.dg_out = p.dg;
+  g.de_out = p.de;
+  g.h_out = p.hb;
+  g.ld_act = I;
+  LAUNCH(gemm_on(c, g, st));
+
+  // dA_d = s_d h^T P_d  (P_d already scaled)
+  ColProjArgs c2 = colproj_args(p.hb, I, T, I, p.Ps_d, RLd, (int)r, (int)r, false, p.partial);
+  c2.scales[0] = 1.0f;
+  c2.dest[0] = gr->dA_down;
+  LAUNCHN("colproj", st, launch_colproj(c.bf16, c2, st));
+
+  // P_u = dg B_u^T, P_g = de B_g^T, each formed once: [s_u P_u | s_g P_g]
+  RowProjArgs r2 = rowproj_args(p.dg, I, T, I, up->B, I, (int)r, (int)r, (int)r);
+  r2.scales[0] = up->scale;
+  r2.out2 = p.Ps_ug;
+  r2.ld2 = RLg;
+  LAUNCHN("rowproj", st, launch_rowproj(c.bf16, r2, st));
+  RowProjArgs r3 = rowproj_args(p.de, I, T, I, gate->B, I, (int)r, (int)(RLg - r), (int)r);
+  r3.scales[0] = gate->scale;
+  r3.out2 = offw(p.Ps_ug, r, c);
+  r3.ld2 = RLg;
+  LAUNCHN("rowproj", st, launch_rowproj(c.bf16, r3, st));
+
+  // dB_u = s_u U_u^T dg, dB_g = s_g U_g^T de
+  ColProjArgs c3 = colproj_args(p.dg, I, T, I, coff(U, r, c), 3 * r, (int)r, (int)r, true, p.partial);
+  c3.scales[0] = up->scale;
+  c3.dest[0] = gr->dB_up;
+  LAUNCHN("colproj", st, launch_colproj(c.bf16, c3, st));
+  ColProjArgs c4 = colproj_args(p.de, I, T, I, U, 3 * r, (int)r, (int)r, true, p.partial);
+  c4.scales[0] = gate->scale;
+  c4.dest[0] = gr->dB_gate;
+  LAUNCHN("colproj", st, launch_colproj(c.bf16, c4, st));
+
+  // [dA_u | dA_g] = X^T [s_u P_u | s_g P_g] in one pass over X
+  ColProjArgs c5 = colproj_args(X, H, T, H, p.Ps_ug, RLg, (int)(2 * r), (int)r, false, p.partial);
+  c5.scales[0] = 1.0f;
+  c5.scales[1] = 1.0f;
+  c5.dest[0] = gr->dA_up;
+  c5.dest[1] = gr->dA_gate;
+  LAUNCHN("colproj", st, launch_colproj(c.bf16, c5, st));
+
+  // dX = dg W_u^T + de W_g^T + [s_u P_u | s_g P_g] [A_u | A_g]^T
+  PackLoraArgs px{};
+  px.out = p.BLt_dx;
+  px.vcols = H;
+  px.RL = (int)RLg;
+  px.nparts = 2;
+  px.part[0] = part(up->A, r, 0, H, 0, (int)r, false);
+  px.part[1] = part(gate->A, r, 0, H, (int)r, (int)r, false);
+  LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, px, st));
+  GemmArgs gx{};
+  gx.M = T;
+  gx.nseg = 2;
+  gx.nreg = 1;
+  gx.epi = EPI_STORE;
+  gx.nf4 = up->nf4 != nullptr;
+  gx.bkind = B_NT;
+  gx.seg[0].A = p.dg;
+  gx.seg[0].lda = I;
+  gx.seg[0].K = I;
+  gx.seg[0].b[0][0] = bsrc(up, I);
+  gx.seg[1].A = p.de;
+  gx.seg[1].lda = I;
+  gx.seg[1].K = I;
+  gx.seg[1].b[0][0] = bsrc(gate, I);
+  gx.reg[0].N = H;
+  gx.reg[0].out = dX;
+  gx.reg[0].ldo = H;
+  gx.AL = p.Ps_ug;
+  gx.ldal = RLg;
+  gx.RL = (int)RLg;
+  gx.BLt = p.BLt_dx;
+  gx.ldbl = RLg;
+  if (T > 0) LAUNCH(gemm_on(c, gx, st));
+  return LORA_OK;
+}
+
+
+// ---------------------------------------------------------------------------
+// Q/K/V
+// ---------------------------------------------------------------------------
+lora_status lora_qkv_workspace_size(const lora_qkv_desc* d, size_t* fwd, size_t* bwd) {
+  Ctx c{};
+  TRY(validate_qkv(d, c));
+  QkvPlan p = plan_qkv(c, *d, nullptr, nullptr);
+  if (fwd) *fwd = p.fwd_bytes;
+  if (bwd) *bwd = p.bwd_bytes;
+  return LORA_OK;
+}
+
+lora_status lora_qkv_fwd(const lora_qkv_desc* d, const void* X, const lora_proj* q, const lora_proj* k,
+                         const lora_proj* v, void* Q, void* K, void* V, void* U, void* ws, size_t ws_bytes,
+                         void* stream) {
+  Ctx c{};
+  TRY(validate_qkv(d, c));
+  const int64_t T = d->T, H = d->H, r = d->r, Nq = d->Nq, Nk = d->Nk, Nv = d->Nv;
+  TRY(check_tptr(c, X, T, "X"));
+  TRY(check_tptr(c, Q, T, "Q"));
+  TRY(check_tptr(c, K, T, "K"));
+  TRY(check_tptr(c, V, T, "V"));
+  TRY(check_tptr(c, U, T, "U"));
+  TRY(check_proj(c, q, H, Nq, "q"));
+  TRY(check_proj(c, k, H, Nk, "k"));
+  TRY(check_proj(c, v, H, Nv, "v"));
+  CHECK(((q->nf4 != nullptr) == (k->nf4 != nullptr)) && ((k->nf4 != nullptr) == (v->nf4 != nullptr)),
+        LORA_EUNSUPPORTED, "q, k, v must all be NF4 or all dense");
+  QkvPlan need = plan_qkv(c, *d, nullptr, nullptr);
+  TRY(check_ws(ws, ws_bytes, need.fwd_bytes));
+  if (T == 0) return LORA_OK;
+  QkvPlan p = plan_qkv(c, *d, ws, nullptr);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t RL = c.rl(3 * r);
+
+  // [U_q | U_k | U_v] = X [A_q | A_k | A_v] in one pass over X
+  const void* srcs[3] = {q->A, k->A, v->A};
+  LAUNCHN("pack", st, launch_pack_cat_t(c.bf16, p.At, H, (int)(3 * r), (int)r, 3, srcs, st));
+  RowProjArgs ra = rowproj_args(X, H, T, H, p.At, H, (int)(3 * r), (int)RL, (int)r);
+  ra.scales[0] = q->scale;
+  ra.scales[1] = k->scale;
+  ra.scales[2] = v->scale;
+  ra.out1 = U;
+  ra.ld1 = 3 * r;
+  ra.out2 = p.Us;
+  ra.ld2 = RL;
+  LAUNCHN("rowproj", st, launch_rowproj(c.bf16, ra, st));
+  PackLoraArgs pl{};
+  pl.out = p.BLt;
+  pl.vcols = Nq + Nk + Nv;
+  pl.RL = (int)RL;
+  pl.nparts = 3;
+  pl.part[0] = part(q->B, Nq, 0, Nq, 0, (int)r, true);
+  pl.part[1] = part(k->B, Nk, Nq, Nk, (int)r, (int)r, true);
+  pl.part[2] = part(v->B, Nv, Nq + Nk, Nv, (int)(2 * r), (int)r, true);
+  LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, pl, st));
+
+  GemmArgs g{};
+  g.M = T;
+  g.nseg = 1;
+  g.nreg = 3;
+  g.epi = EPI_STORE;
+  g.nf4 = q->nf4 != nullptr;
+  g.bkind = B_NN;
+  g.seg[0].A = X;
+  g.seg[0].lda = H;
+  g.seg[0].K = H;
+  g.seg[0].b[0][0] = bsrc(q, Nq);
+  g.seg[0].b[1][0] = bsrc(k, Nk);
+  g.seg[0].b[2][0] = bsrc(v, Nv);
+  const int64_t Ns[3] = {Nq, Nk, Nv};
+  void* outs[3] = {Q, K, V};
+  int64_t v0 = 0;
+  for (int i = 0; i < 3; ++i) {
+    g.reg[i].N = Ns[i];
+    g.reg[i].out = outs[i];
+    g.reg[i].ldo = Ns[i];
+    g.reg[i].vcol0[0] = v0;
+    v0 += Ns[i];
+  }
+  g.AL = p.Us;
+  g.ldal = RL;
+  g.RL = (int)RL;
+  g.BLt = p.BLt;
+  g.ldbl = RL;
+  LAUNCH(gemm_on(c, g, st));
+  return LORA_OK;
+}
+
+lora_status lora_qkv_bwd(const lora_qkv_desc* d, const void* dQ, const void* dK, const void* dV, const void* X,
+                         const void* U, const lora_proj* q, const lora_proj* k, const lora_proj* v, void* dX,
+                         const lora_qkv_grads* gr, void* ws, size_t ws_bytes, void* stream) {
+  Ctx c{};
+  TRY(validate_qkv(d, c));
+  const int64_t T = d->T, H = d->H, r = d->r, Nq = d->Nq, Nk = d->Nk, Nv = d->Nv;
+  TRY(check_tptr(c, dQ, T, "dQ"));
+  TRY(check_tptr(c, dK, T, "dK"));
+  TRY(check_tptr(c, dV, T, "dV"));
+  TRY(check_tptr(c, X, T, "X"));
+  TRY(check_tptr(c, U, T, "U"));
+  TRY(check_tptr(c, dX, T, "dX"));
+  CHECK(gr != nullptr, LORA_EINVAL, "grads is NULL");
+  TRY(check_ptr(c, gr->dA_q, "dA_q"));
+  TRY(check_ptr(c, gr->dB_q, "dB_q"));
+  TRY(check_ptr(c, gr->dA_k, "dA_k"));
+  TRY(check_ptr(c, gr->dB_k, "dB_k"));
+  TRY(check_ptr(c, gr->dA_v, "dA_v"));
+  TRY(check_ptr(c, gr->dB_v, "dB_v"));
+  TRY(check_proj(c, q, H, Nq, "q"));
+  TRY(check_proj(c, k, H, Nk, "k"));
+  TRY(check_proj(c, v, H, Nv, "v"));
+  CHECK(((q->nf4 != nullptr) == (k->nf4 != nullptr)) && ((k->nf4 != nullptr) == (v->nf4 != nullptr)),
+        LORA_EUNSUPPORTED, "q, k, v must all be NF4 or all dense");
+  CHECK(!overlaps(dX, T * H * c.es, X, T * H * c.es), LORA_EUNSUPPORTED, "dX aliases X (in-place dX is not supported)");
+  QkvPlan need = plan_qkv(c, *d, nullptr, nullptr);
+  TRY(check_ws(ws, ws_bytes, need.bwd_bytes));
+  QkvPlan p = plan_qkv(c, *d, nullptr, ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t RL = c.rl(3 * r);
+  const lora_proj* projs[3] = {q, k, v};
+  const void* dZ[3] = {dQ, dK, dV};
+  const int64_t Ns[3] = {Nq, Nk, Nv};
+  void* dBs[3] = {gr->dB_q, gr->dB_k, gr->dB_v};
+
+  // P_p = dZ_p B_p^T, each formed once: [s_q P_q | s_k P_k | s_v P_v]
+  for (int i = 0; i < 3; ++i) {
+    const int R2 = (i == 2) ? (int)(RL - 2 * r) : (int)r;
+    RowProjArgs ra = rowproj_args(dZ[i], Ns[i], T, Ns[i], projs[i]->B, Ns[i], (int)r, R2, (int)r);
+    ra.scales[0] = projs[i]->scale;
+    ra.out2 = offw(p.Ps, i * r, c);
+    ra.ld2 = RL;
+    LAUNCHN("rowproj", st, launch_rowproj(c.bf16, ra, st));
+  }
+  // dB_p = s_p U_p^T dZ_p
+  for (int i = 0; i < 3; ++i) {
+    ColProjArgs ca = colproj_args(dZ[i], Ns[i], T, Ns[i], coff(U, i * r, c), 3 * r, (int)r, (int)r, true, p.partial);
+    ca.scales[0] = projs[i]->scale;
+    ca.dest[0] = dBs[i];
+    LAUNCHN("colproj", st, launch_colproj(c.bf16, ca, st));
+  }
+  // [dA_q | dA_k | dA_v] = X^T [s P] in one pass over X
+  ColProjArgs cx = colproj_args(X, H, T, H, p.Ps, RL, (int)(3 * r), (int)r, false, p.partial);
+  cx.scales[0] = cx.scales[1] = cx.scales[2] = 1.0f;
+  cx.dest[0] = gr->dA_q;
+  cx.dest[1] = gr->dA_k;
+  cx.dest[2] = gr->dA_v;
+  LAUNCHN("colproj", st, launch_colproj(c.bf16, cx, st));
+  // dX = sum_p dZ_p W_p^T + [s P] [A_q | A_k | A_v]^T
+  PackLoraArgs pl{};
+  pl.out = p.BLt_dx;
+  pl.vcols = H;
+  pl.RL = (int)RL;
+  pl.nparts = 3;
+  for (int i = 0; i < 3; ++i) pl.part[i] = part(projs[i]->A, r, 0, H, (int)(i * r), (int)r, false);
+  LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, pl, st));
+  GemmArgs g{};
+  g.M = T;
+  g.nseg = 3;
+  g.nreg = 1;
+  g.epi = EPI_STORE;
+  g.nf4 = q->nf4 != nullptr;
+  g.bkind = B_NT;
+  for (int i = 0; i < 3; ++i) {
+    g.seg[i].A = dZ[i];
+    g.seg[i].lda = Ns[i];
+    g.seg[i].K = Ns[i];
+    g.seg[i].b[0][0] = bsrc(projs[i], Ns[i]);
+  }
+  g.reg[0].N = H;
+  g.reg[0].out = dX;
+  g.reg[0].ldo = H;
+  g.AL = p.Ps;
+  g.ldal = RL;
+  g.RL = (int)RL;
+  g.BLt = p.BLt_dx;
+  g.ldbl = RL;
+  LAUNCH(gemm_on(c, g, st));
+  return LORA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// O (single projection)
+// ---------------------------------------------------------------------------
+lora_status lora_o_workspace_size(const lora_o_desc* d, size_t* fwd, size_t* bwd) {
+  Ctx c{};
+  TRY(validate_o(d, c));
+  OPlan p = plan_o(c, d->T, d->K, d->N, d->r, false, nullptr, nullptr);
+  if (fwd) *fwd = p.fwd_bytes;
+  if (bwd) *bwd = p.bwd_bytes;
+  return LORA_OK;
+}
+
+lora_status lora_o_fwd(const lora_o_desc* d, const void* X, const lora_proj* o, void* Y, void* U, void* ws,
+                       size_t ws_bytes, void* stream) {
+  Ctx c{};
+  TRY(validate_o(d, c));
+  const int64_t T = d->T;
+  TRY(check_tptr(c, X, T, "X"));
+  TRY(check_tptr(c, Y, T, "Y"));
+  TRY(check_tptr(c, U, T, "U"));
+  TRY(check_proj(c, o, d->K, d->N, "o"));
+  OPlan need = plan_o(c, d->T, d->K, d->N, d->r, false, nullptr, nullptr);
+  TRY(check_ws(ws, ws_bytes, need.fwd_bytes));
+  if (d->T == 0) return LORA_OK;
+  OPlan p = plan_o(c, d->T, d->K, d->N, d->r, false, ws, nullptr);
+  return proj_forward(c, d->T, d->K, d->N, d->r, X, o, Y, U, p, static_cast<hipStream_t>(stream));
+}
+
+lora_status lora_o_bwd(const lora_o_desc* d, const void* dY, const void* X, const void* U, const lora_proj* o,
+                       void* dX, void* dA, void* dB, void* ws, size_t ws_bytes, void* stream) {
+  Ctx c{};
+  TRY(validate_o(d, c));
+  const int64_t T = d->T, K = d->K, N = d->N, r = d->r;
+  TRY(check_tptr(c, dY, T, "dY"));
+  TRY(check_tptr(c, X, T, "X"));
+  TRY(check_tptr(c, U, T, "U"));
+  TRY(check_tptr(c, dX, T, "dX"));
+  TRY(check_ptr(c, dA, "dA"));
+  TRY(check_ptr(c, dB, "dB"));
+  TRY(check_proj(c, o, K, N, "o"));
+  CHECK(!overlaps(dX, T * K * c.es, X, T * K * c.es), LORA_EUNSUPPORTED, "dX aliases X (in-place dX is not supported)");
+  OPlan need = plan_o(c, T, K, N, r, false, nullptr, nullptr);
+  TRY(check_ws(ws, ws_bytes, need.bwd_bytes));
+  OPlan p = plan_o(c, T, K, N, r, false, nullptr, ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t RL = c.rl(r);
+  // P = dY B^T, formed once
+  RowProjArgs ra = rowproj_args(dY, N, T, N, o->B, N, (int)r, (int)RL, (int)r);
+  ra.scales[0] = o->scale;
+  ra.out2 = p.Ps;
+  ra.ld2 = RL;
+  LAUNCHN("rowproj", st, launch_rowproj(c.bf16, ra, st));
+  // dB = s U^T dY ; dA = X^T (s P)
+  ColProjArgs cb = colproj_args(dY, N, T, N, U, r, (int)r, (int)r, true, p.partial);
+  cb.scales[0] = o->scale;
+  cb.dest[0] = dB;
+  LAUNCHN("colproj", st, launch_colproj(c.bf16, cb, st));
+  ColProjArgs ca = colproj_args(X, K, T, K, p.Ps, RL, (int)r, (int)r, false, p.partial);
+  ca.scales[0] = 1.0f;
+  ca.dest[0] = dA;
+  LAUNCHN("colproj", st, launch_colproj(c.bf16, ca, st));
+  if (T == 0) return LORA_OK;
+  return proj_input_grad(c, T, K, N, r, dY, o, dX, p, st);
+}
+
+// ---------------------------------------------------------------------------
+// NF4
+// ---------------------------------------------------------------------------
+lora_status lora_nf4_quantize_workspace_size(int64_t rows, int64_t cols, size_t* bytes) {
+  CHECK(rows > 0 && cols > 0, LORA_ESHAPE, "NF4 weight must be non-empty");
+  CHECK((rows * cols) % NF4_GROUP == 0, LORA_ESHAPE, "NF4 numel %lld not a multiple of %lld",
+        (long long)(rows * cols), (long long)NF4_GROUP);
+  if (bytes) *bytes = nf4_quantize_ws_bytes(rows * cols);
+  return LORA_OK;
+}
+
+lora_status lora_nf4_quantize(const void* W, int64_t rows, int64_t cols, int32_t dtype, uint8_t* codes, int8_t* q8,
+                              float* s2, float* mu, void* ws, size_t ws_bytes, void* stream) {
+  Ctx c{};
+  TRY(check_dtype(dtype, c));
+  size_t need = 0;
+  TRY(lora_nf4_quantize_workspace_size(rows, cols, &need));
+  CHECK(W && codes && q8 && s2 && mu, LORA_EINVAL, "NULL argument");
+  CHECK(aligned(W, c.es) && aligned(codes, 16) && aligned(s2, 4) && aligned(mu, 4), LORA_EALIGN,
+        "W must be element-aligned, codes 16-byte aligned, s2 and mu 4-byte aligned");
+  TRY(check_ws(ws, ws_bytes, need));
+  LAUNCHN("nf4_quantize", static_cast<hipStream_t>(stream), launch_nf4_quantize(W, rows * cols, c.bf16, codes, q8, s2, mu, ws, static_cast<hipStream_t>(stream)));
+  return LORA_OK;
+}
+
+lora_status lora_nf4_dequant(const lora_nf4* w, void* out, int32_t dtype, void* stream) {
+  Ctx c{};
+  TRY(check_dtype(dtype, c));
+  CHECK(w != nullptr && out != nullptr, LORA_EINVAL, "NULL argument");
+  CHECK(w->rows > 0 && w->cols > 0, LORA_ESHAPE, "NF4 weight must be non-empty");
+  TRY(check_nf4(w, w->rows, w->cols, "W"));
+  CHECK(aligned(out, 16), LORA_EALIGN, "out must be 16-byte aligned");
+  LAUNCHN("nf4_dequant", static_cast<hipStream_t>(stream), launch_nf4_dequant(w->codes, w->q8, w->s2, w->mu, w->rows * w->cols, out, c.bf16,
+                            static_cast<hipStream_t>(stream)));
+  return LORA_OK;
+}
+
+lora_status lora_nf4_unpack_codes(const lora_nf4* w, uint8_t* out, void* stream) {
+  CHECK(w != nullptr && out != nullptr, LORA_EINVAL, "NULL argument");
+  CHECK(w->rows > 0 && w->cols > 0, LORA_ESHAPE, "NF4 weight must be non-empty");
+  TRY(check_nf4(w, w->rows, w->cols, "W"));
+  CHECK(aligned(out, 8), LORA_EALIGN, "out must be 8-byte aligned");
+  LAUNCHN("nf4_unpack", static_cast<hipStream_t>(stream), launch_nf4_unpack(w->codes, w->rows * w->cols, out, static_cast<hipStream_t>(stream)));
+  return LORA_OK;
+}
+
+lora_status lora_nf4_gemm_workspace_size(int64_t T, int64_t rows, int64_t cols, int64_t r, int32_t trans,
+                                         size_t* bytes) {
+  Ctx c{};
+  TRY(check_dtype(LORA_BF16, c));
+  CHECK(T >= 0, LORA_ESHAPE, "T is negative");
+  CHECK(trans == 0 || trans == 1, LORA_EINVAL, "trans must be 0 or 1");
+  TRY(check_dim(c, rows, "rows"));
+  TRY(check_dim(c, cols, "cols"));
+  if (r != 0) TRY(check_rank(c, r, 1));
+  OPlan p = plan_o(c, T, rows, cols, r, trans == 0, nullptr, nullptr);
+  if (bytes) *bytes = trans ? p.bwd_bytes : p.fwd_bytes;
+  return LORA_OK;
+}
+
+lora_status lora_nf4_gemm(int64_t T, int32_t trans, const void* X, const lora_nf4* W, const void* A, const void* B,
+                          int64_t r, float scale, void* Y, void* ws, size_t ws_bytes, void* stream) {
+  Ctx c{};
+  TRY(check_dtype(LORA_BF16, c));
+  CHECK(W != nullptr, LORA_EINVAL, "W is NULL");
+  CHECK((A == nullptr) == (B == nullptr), LORA_EINVAL, "A and B must both be set or both be NULL");
+  const int64_t rr = A ? r : 0;
+  size_t need = 0;
+  TRY(lora_nf4_gemm_workspace_size(T, W->rows, W->cols, rr, trans, &need));
+  TRY(check_tptr(c, X, T, "X"));
+  TRY(check_tptr(c, Y, T, "Y"));
+  TRY(check_nf4(W, W->rows, W->cols, "W"));
+  if (rr > 0) {
+    TRY(check_ptr(c, A, "A"));
+    TRY(check_ptr(c, B, "B"));
+    CHECK(std::isfinite(scale), LORA_EINVAL, "scale is not finite");
+  }
+  lora_proj o{};
+  o.nf4 = W;
+  o.A = A;
+  o.B = B;
+  o.scale = scale;
+  TRY(check_ws(ws, ws_bytes, need));
+  if (T == 0) return LORA_OK;
+  const int64_t K = W->rows, N = W->cols;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (trans == 0) {
+    OPlan p = plan_o(c, T, K, N, rr, true, ws, nullptr);
+    return proj_forward(c, T, K, N, rr, X, &o, Y, p.U_tmp, p, st);
+  }
+  OPlan p = plan_o(c, T, K, N, rr, false, nullptr, ws);
+  if (rr > 0) {
+    const int64_t RL = c.rl(rr);
+    RowProjArgs ra = rowproj_args(X, N, T, N, B, N, (int)rr, (int)RL, (int)rr);
+    ra.scales[0] = scale;
+    ra.out2 = p.Ps;
+    ra.ld2 = RL;
+    LAUNCHN("rowproj", st, launch_rowproj(c.bf16, ra, st));
+  }
+  return proj_input_grad(c, T, K, N, rr, X, &o, Y, p, st);
+}
+
+}  // extern "C"

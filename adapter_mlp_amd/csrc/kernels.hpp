@@ -1,0 +1,161 @@
+// Kernel argument structs and host-side launchers shared by the kernel
+// translation units and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lora {
+
+// ---------------------------------------------------------------------------
+// Tiled GEMM with a LoRA tail and fused epilogues.
+//
+//   C[m, n] = sum_s sum_k A_s[m, k] B_s[k, n]  +  sum_k AL[m, k] BL[k, n]
+//
+// Main segments s (at most 3) are concatenated along K; each has its own A
+// ([M, K_s] row-major) and, per output region and column group, its own B.
+// B orientation is the same for all main segments:
+//   B_NN: B_s is [K_s, N] row-major (the weight W [in, out] of a forward);
+//   B_NT: B_s is [N, K_s] row-major (W used transposed, an input gradient).
+// The LoRA tail AL [M, RL] / BLt [vcols, RL] always comes K-contiguous; BLt
+// row v is the adapter column that feeds output column n of region p and
+// column group c, v = vcol0[p][c] + n (built by lora_pack_* on the host side).
+// Up to 3 output regions split the N range (Q/K/V); in "dual" mode every
+// tile interleaves two column groups (gate, up) over the same output columns
+// so the activation epilogue sees e and g of one element in one lane.
+// ---------------------------------------------------------------------------
+enum { B_NN = 0, B_NT = 1 };
+enum { EPI_STORE = 0, EPI_ACT_FWD = 1, EPI_ACT_BWD = 2 };
+
+struct BSrc {
+  const void* p;  // dense base (compute dtype) or nullptr for NF4
+  int64_t ld;
+  const uint8_t* codes;  // NF4
+  const int8_t* q8;
+  const float* s2;
+  const float* mu;
+  int64_t wcols;  // row length of the logical NF4 weight
+};
+
+struct GemmSeg {
+  const void* A;
+  int64_t lda;
+  int64_t K;
+  BSrc b[3][2];  // [region][column group]
+};
+
+struct GemmRegion {
+  int64_t N;
+  int64_t tile0;  // first n-tile of this region
+  void* out;      // EPI_STORE output
+  int64_t ldo;
+  int64_t vcol0[2];
+};
+
+struct GemmArgs {
+  int64_t M;
+  int32_t nseg, nreg;
+  int32_t dual, epi, act, nf4, bkind, pad_;
+  GemmSeg seg[3];
+  GemmRegion reg[3];
+  int64_t ntile_m, ntile_n;
+  const void* AL;  // LoRA tail (nullptr / RL == 0: none)
+  int64_t ldal;
+  int32_t RL, pad2_;
+  const void* BLt;
+  int64_t ldbl;
+  // EPI_ACT_FWD: e_out, g_out, h_out [M, N] ; EPI_ACT_BWD: e_in, g_in -> dg_out, de_out, h_out
+  void* e_out;
+  void* g_out;
+  void* h_out;
+  const void* e_in;
+  const void* g_in;
+  void* dg_out;
+  void* de_out;
+  int64_t ld_act;
+};
+
+// Columns of output covered by one n-tile.
+int64_t gemm_tile_cols(bool bf16, bool dual);
+int64_t gemm_tile_rows(bool bf16);
+hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// Rank-r products.
+// rowproj:  Out[t, j] = sum_k Z[t, k] Bt[j, k]   (j < R, R <= 64)
+//   writes out1[t, off1 + j] = Out (unscaled)              if out1
+//          out2[t, j] = scale(j) * Out, zero for R <= j < R2   if out2
+//   scale(j) = scales[j / seg_w] (seg_w = width of each adapter in the group)
+// colproj:  Out[k, j] = sum_t Z[t, k] P[t, j] (j < R)
+//   written to dest[q] for j in [q*seg_w, (q+1)*seg_w) times scales[q],
+//   transposed ([seg_w, K]) or not ([K, seg_w]).
+// ---------------------------------------------------------------------------
+struct RowProjArgs {
+  const void* Z;
+  int64_t ldz, T, K;
+  const void* Bt;
+  int64_t ldb;
+  int32_t R, R2, seg_w, pad_;
+  float scales[4];
+  void* out1;
+  int64_t ld1, off1;
+  void* out2;
+  int64_t ld2;
+};
+
+struct ColProjArgs {
+  const void* Z;
+  int64_t ldz, T, K;
+  const void* P;
+  int64_t ldp;
+  int32_t R, seg_w, transposed, nchunk;
+  float scales[4];
+  void* dest[4];
+  float* partial;  // bf16 path: [nchunk, K, R] fp32 scratch
+};
+
+hipError_t launch_rowproj(bool bf16, const RowProjArgs& a, hipStream_t st);
+hipError_t launch_colproj(bool bf16, const ColProjArgs& a, hipStream_t st);
+// partial-buffer floats the bf16 colproj needs for (T, K, R)
+int64_t colproj_partial_floats(int64_t T, int64_t K, int R);
+int colproj_nchunk(int64_t T, int64_t K);
+
+// ---------------------------------------------------------------------------
+// Small packing kernels (adapter operands in the layout the kernels read).
+// pack_cat_t:  out[j, k] = src_q[k, j - q*w] for j < nparts*w, 0 for j < Rpad
+//              (A_p [K, w] of several adapters -> one K-contiguous [Rpad, K]).
+// pack_lora_b: builds BLt [vcols, RL]: for part descriptors (v0, nv, k0, w, src,
+//              ld, nn): BLt[v0 + n, k0 + i] = nn ? src[i*ld + n] : src[n*ld + i]
+//              for n < nv, i < w; everything else 0.
+// ---------------------------------------------------------------------------
+struct PackPart {
+  const void* src;
+  int64_t ld;
+  int64_t v0, nv;
+  int32_t k0, w, nn, pad_;
+};
+struct PackLoraArgs {
+  void* out;
+  int64_t vcols;
+  int32_t RL, nparts;
+  PackPart part[6];
+};
+hipError_t launch_pack_lora_b(bool bf16, const PackLoraArgs& a, hipStream_t st);
+hipError_t launch_pack_cat_t(bool bf16, void* out, int64_t K, int Rpad, int w, int nparts,
+                             const void* const* srcs, hipStream_t st);
+hipError_t launch_zero(void* p, int64_t bytes, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// NF4 kernels.
+// ---------------------------------------------------------------------------
+hipError_t launch_nf4_quantize(const void* W, int64_t numel, bool bf16, uint8_t* codes,
+                               int8_t* q8, float* s2, float* mu, void* ws, hipStream_t st);
+size_t nf4_quantize_ws_bytes(int64_t numel);
+hipError_t launch_nf4_dequant(const uint8_t* codes, const int8_t* q8, const float* s2,
+                              const float* mu, int64_t numel, void* out, bool bf16,
+                              hipStream_t st);
+hipError_t launch_nf4_unpack(const uint8_t* codes, int64_t numel, uint8_t* out, hipStream_t st);
+extern const float kNF4Levels[16];
+
+}  // namespace lora

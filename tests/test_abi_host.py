@@ -1,0 +1,171 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+The library loads, exports every function the header declares, and rejects
+bad arguments with the documented status before touching the GPU (every
+check here fails validation, so nothing is enqueued).
+"""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lora_mi355x.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from adapter_mlp_amd import _lib
+
+    _lib.load()
+    return _lib
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lora_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(L):
+    names = header_functions()
+    assert len(names) >= 19
+    lib = L.load()
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in the header but not exported"
+    assert set(names) == set(L.SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_version_and_strerror(L):
+    lib = L.load()
+    assert lib.lora_version() == 1
+    for s in range(8):
+        assert lib.lora_strerror(s)
+    assert lib.lora_strerror(0) == b"success"
+
+
+def test_codebook_matches_oracle_table(L):
+    from oracle.nf4 import NF4_LEVELS
+
+    buf = (C.c_float * 16)()
+    L.load().lora_nf4_codebook(buf)
+    got = np.array(list(buf), dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32), NF4_LEVELS.view(np.uint32))
+
+
+def _status(L, name, *args):
+    lib = L.load()
+    return getattr(lib, name)(*args)
+
+
+FAKE = 1 << 20  # 16-byte aligned non-NULL address; never dereferenced (validation fails first)
+
+
+def _proj(L, W=FAKE, A=FAKE, B=FAKE, scale=2.0, nf4=None):
+    p = L.lora_proj()
+    p.W, p.A, p.B, p.scale = W, A, B, scale
+    if nf4 is not None:
+        p.nf4 = C.pointer(nf4)
+    return p
+
+
+def test_mlp_validation_statuses(L):
+    sz = C.c_size_t
+    f, b = sz(), sz()
+    d = L.lora_mlp_desc(128, 256, 720, 16, 0, L.LORA_BF16)
+    assert _status(L, "lora_mlp_workspace_size", C.byref(d), C.byref(f), C.byref(b)) == L.LORA_ESHAPE  # 720 % 64
+    d = L.lora_mlp_desc(128, 256, 768, 16, 0, L.LORA_BF16)
+    assert _status(L, "lora_mlp_workspace_size", C.byref(d), C.byref(f), C.byref(b)) == L.LORA_OK
+    assert f.value > 0 and b.value > 0
+    d32 = L.lora_mlp_desc(128, 256, 720, 8, 0, L.LORA_F32)
+    assert _status(L, "lora_mlp_workspace_size", C.byref(d32), C.byref(f), C.byref(b)) == L.LORA_OK
+    bad = [
+        (L.lora_mlp_desc(128, 256, 768, 16, 7, L.LORA_BF16), L.LORA_EINVAL),  # activation
+        (L.lora_mlp_desc(128, 256, 768, 16, 0, 9), L.LORA_EDTYPE),
+        (L.lora_mlp_desc(-1, 256, 768, 16, 0, L.LORA_BF16), L.LORA_ESHAPE),
+        (L.lora_mlp_desc(128, 0, 768, 16, 0, L.LORA_BF16), L.LORA_ESHAPE),
+        (L.lora_mlp_desc(128, 256, 768, 12, 0, L.LORA_BF16), L.LORA_ESHAPE),  # r % 8
+        (L.lora_mlp_desc(128, 256, 768, 40, 0, L.LORA_BF16), L.LORA_ESHAPE),  # 2r > 64
+        (L.lora_mlp_desc(128, 256, 768, 0, 0, L.LORA_F32), L.LORA_ESHAPE),
+    ]
+    for desc, want in bad:
+        assert _status(L, "lora_mlp_workspace_size", C.byref(desc), C.byref(f), C.byref(b)) == want
+
+
+def test_mlp_fwd_rejects_before_enqueue(L):
+    d = L.lora_mlp_desc(128, 256, 768, 16, 0, L.LORA_BF16)
+    f, b = C.c_size_t(), C.c_size_t()
+    _status(L, "lora_mlp_workspace_size", C.byref(d), C.byref(f), C.byref(b))
+    sv = L.lora_mlp_saved(FAKE, FAKE, FAKE)
+    g, u, dn = _proj(L), _proj(L), _proj(L)
+
+    def fwd(X=FAKE, Y=FAKE * 2, saved=sv, gate=g, ws=FAKE, nbytes=f.value):
+        return _status(L, "lora_mlp_fwd", C.byref(d), X, C.byref(gate), C.byref(u), C.byref(dn), Y,
+                       C.byref(saved), ws, nbytes, None)
+
+    assert fwd(X=None) == L.LORA_EINVAL
+    assert fwd(X=FAKE + 2) == L.LORA_EALIGN
+    assert fwd(nbytes=f.value - 1) == L.LORA_EWORKSPACE
+    assert fwd(ws=None) == L.LORA_EWORKSPACE
+    assert fwd(gate=_proj(L, W=None)) == L.LORA_EINVAL  # neither W nor nf4
+    assert fwd(gate=_proj(L, scale=float("nan"))) == L.LORA_EINVAL
+    assert fwd(saved=L.lora_mlp_saved(FAKE, None, FAKE)) == L.LORA_EINVAL
+    assert fwd(Y=FAKE) == L.LORA_EUNSUPPORTED  # Y aliases X
+    assert b"alias" in L.load().lora_last_error()
+
+
+def test_nf4_validation(L):
+    nbytes = C.c_size_t()
+    assert _status(L, "lora_nf4_quantize_workspace_size", 64, 256, C.byref(nbytes)) == L.LORA_OK
+    assert _status(L, "lora_nf4_quantize_workspace_size", 64, 200, C.byref(nbytes)) == L.LORA_ESHAPE
+    q = L.lora_nf4(FAKE, FAKE, FAKE, FAKE, 256, 768)
+    # NF4 base with fp32 compute is unsupported
+    d = L.lora_o_desc(64, 256, 768, 8, L.LORA_F32, 0)
+    f, b = C.c_size_t(), C.c_size_t()
+    _status(L, "lora_o_workspace_size", C.byref(d), C.byref(f), C.byref(b))
+    o = _proj(L, W=None, nf4=q)
+    st = _status(L, "lora_o_fwd", C.byref(d), FAKE, C.byref(o), FAKE * 2, FAKE * 3, FAKE * 4, f.value, None)
+    assert st == L.LORA_EUNSUPPORTED
+    # shape mismatch between descriptor and NF4 weight
+    d16 = L.lora_o_desc(64, 256, 1024, 16, L.LORA_BF16, 0)
+    _status(L, "lora_o_workspace_size", C.byref(d16), C.byref(f), C.byref(b))
+    st = _status(L, "lora_o_fwd", C.byref(d16), FAKE, C.byref(o), FAKE * 2, FAKE * 3, FAKE * 4, f.value, None)
+    assert st == L.LORA_ESHAPE
+    # numel not a multiple of 64 * 256
+    q2 = L.lora_nf4(FAKE, FAKE, FAKE, FAKE, 64, 64)
+    st = _status(L, "lora_nf4_dequant", C.byref(q2), FAKE, L.LORA_BF16, None)
+    assert st == L.LORA_ESHAPE
+    st = _status(L, "lora_nf4_gemm_workspace_size", 64, 256, 768, 16, 2, C.byref(nbytes))
+    assert st == L.LORA_EINVAL  # trans must be 0/1
+
+
+def test_qkv_o_validation(L):
+    f, b = C.c_size_t(), C.c_size_t()
+    d = L.lora_qkv_desc(100, 4096, 4096, 1024, 1024, 16, L.LORA_BF16, 0)
+    assert _status(L, "lora_qkv_workspace_size", C.byref(d), C.byref(f), C.byref(b)) == L.LORA_OK
+    d = L.lora_qkv_desc(100, 4096, 4096, 1024, 1024, 24, L.LORA_BF16, 0)  # 3r = 72 > 64
+    assert _status(L, "lora_qkv_workspace_size", C.byref(d), C.byref(f), C.byref(b)) == L.LORA_ESHAPE
+    d = L.lora_qkv_desc(100, 4096, 4096, 1024, 1024, 16, L.LORA_BF16, 1)
+    assert _status(L, "lora_qkv_workspace_size", C.byref(d), C.byref(f), C.byref(b)) == L.LORA_EINVAL
+    d = L.lora_o_desc(0, 4096, 4096, 16, L.LORA_BF16, 0)
+    assert _status(L, "lora_o_workspace_size", C.byref(d), C.byref(f), C.byref(b)) == L.LORA_OK
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    from adapter_mlp_amd import _lib
+
+    with pytest.raises(RuntimeError, match="build it"):
+        _load_fresh(str(tmp_path / "missing.so"))
+
+
+def _load_fresh(path):
+    from adapter_mlp_amd import _lib
+
+    saved = _lib._lib
+    _lib._lib = None
+    try:
+        return _lib.load(path)
+    finally:
+        _lib._lib = saved

@@ -1,0 +1,298 @@
+"""GPU parity of the HIP path against the CPU oracle on the same seeded inputs.
+
+Shapes here span several 256-row / 256-column tiles with ragged tails and
+run in seconds on the oracle; the five benchmark shapes are in
+test_gpu_configs.py.  Bar: max|err|/max|ref| <= 2e-2 per output tensor in
+bf16 (fp32 accumulation), <= 1e-5 in fp32; NF4 codes and dequantized weights
+bit-exact.
+"""
+import numpy as np
+import pytest
+
+from oracle import lora as OL
+from oracle import nf4 as ON
+from workload import WorkloadConfig, make_attn_inputs, make_mlp_inputs
+from _util import TOL, assert_close, dev, host, proj_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lm():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import adapter_mlp_amd
+
+    adapter_mlp_amd.load()
+    return adapter_mlp_amd
+
+
+def _mlp_case(lm, cfg, act, seed=None):
+    inp = make_mlp_inputs(cfg, seed=seed)
+    dt = cfg.dtype
+    tol = TOL[dt]
+    X, dY = dev(inp["X"], dt), dev(inp["dY"], dt)
+    g, u, d = (proj_dev(inp[k], dt) for k in ("gate", "up", "down"))
+    Y, saved = lm.mlp_fwd(X, g, u, d, act)
+    dX, grads = lm.mlp_bwd(dY, X, saved, g, u, d, act)
+    import torch
+
+    torch.cuda.synchronize()
+    Yr, sr = OL.mlp_fwd(inp["X"], inp["gate"], inp["up"], inp["down"], act)
+    gr = OL.mlp_bwd(inp["dY"], inp["X"], sr, inp["gate"], inp["up"], inp["down"], act)
+    assert_close("Y", host(Y), Yr, tol)
+    assert_close("e", host(saved["e"]), sr["e"], tol)
+    assert_close("g", host(saved["g"]), sr["g"], tol)
+    r = cfg.r
+    Ur = np.concatenate([sr["U_g"], sr["U_u"], sr["U_d"]], axis=1)
+    assert_close("U", host(saved["U"]), Ur, tol)
+    assert_close("dX", host(dX), gr["dX"], tol)
+    for k_dev, k_ref in (("dA_gate", "dA_g"), ("dB_gate", "dB_g"), ("dA_up", "dA_u"), ("dB_up", "dB_u"),
+                         ("dA_down", "dA_d"), ("dB_down", "dB_d")):
+        assert_close(k_dev, host(grads[k_dev]), gr[k_ref], tol)
+    return Y, dX, grads
+
+
+@pytest.mark.parametrize("act", ["swiglu", "geglu_tanh"])
+def test_mlp_bf16_ragged(lm, act):
+    cfg = WorkloadConfig(90, "mlp", T=300, H=512, I=1088, r=16, alpha=32, dtype="bf16", act=act)
+    _mlp_case(lm, cfg, act)
+
+
+def test_mlp_bf16_rank8_scale_not_power_of_two(lm):
+    cfg = WorkloadConfig(91, "mlp", T=200, H=256, I=640, r=8, alpha=12, dtype="bf16", act="swiglu")
+    _mlp_case(lm, cfg, "swiglu")
+
+
+def test_mlp_fp32_tiny_config(lm):
+    from workload import CONFIGS
+
+    _mlp_case(lm, CONFIGS[1], "swiglu")
+
+
+def test_mlp_fp32_odd_shapes(lm):
+    cfg = WorkloadConfig(92, "mlp", T=37, H=72, I=100, r=3, alpha=5, dtype="f32", act="geglu_tanh",
+                         rms_inputs=False)
+    _mlp_case(lm, cfg, "geglu_tanh")
+
+
+def _qkv_case(lm, cfg):
+    import torch
+
+    inp = make_attn_inputs(cfg)
+    dt = cfg.dtype
+    tol = TOL[dt]
+    X = dev(inp["X"], dt)
+    q, k, v = (proj_dev(inp[n], dt) for n in ("q", "k", "v"))
+    Q, K, V, U = lm.qkv_fwd(X, q, k, v)
+    dQ, dK, dV = (dev(inp[n], dt) for n in ("dQ", "dK", "dV"))
+    dX, grads = lm.qkv_bwd(dQ, dK, dV, X, U, q, k, v)
+    Xo = dev(inp["Xo"], dt)
+    o = proj_dev(inp["o"], dt)
+    Yo, Uo = lm.o_fwd(Xo, o)
+    dXo, dAo, dBo = lm.o_bwd(dev(inp["dO"], dt), Xo, Uo, o)
+    torch.cuda.synchronize()
+    (Qr, Kr, Vr), sr = OL.qkv_fwd(inp["X"], inp["q"], inp["k"], inp["v"])
+    gr = OL.qkv_bwd(inp["dQ"], inp["dK"], inp["dV"], inp["X"], sr, inp["q"], inp["k"], inp["v"])
+    for name, a, b in (("Q", Q, Qr), ("K", K, Kr), ("V", V, Vr)):
+        assert_close(name, host(a), b, tol)
+    assert_close("U", host(U), np.concatenate([sr["U_q"], sr["U_k"], sr["U_v"]], axis=1), tol)
+    assert_close("dX", host(dX), gr["dX"], tol)
+    for n in ("dA_q", "dB_q", "dA_k", "dB_k", "dA_v", "dB_v"):
+        assert_close(n, host(grads[n]), gr[n], tol)
+    Yr, so = OL.o_fwd(inp["Xo"], inp["o"])
+    go = OL.o_bwd(inp["dO"], inp["Xo"], so, inp["o"])
+    assert_close("O", host(Yo), Yr, tol)
+    assert_close("dX_o", host(dXo), go["dX"], tol)
+    assert_close("dA_o", host(dAo), go["dA"], tol)
+    assert_close("dB_o", host(dBo), go["dB"], tol)
+
+
+def test_qkv_o_bf16_ragged(lm):
+    cfg = WorkloadConfig(93, "attn", T=300, H=512, r=16, alpha=32, dtype="bf16", Nq=512, Nk=192, Nv=128)
+    _qkv_case(lm, cfg)
+
+
+def test_qkv_o_fp32(lm):
+    cfg = WorkloadConfig(94, "attn", T=50, H=96, r=4, alpha=8, dtype="f32", Nq=96, Nk=32, Nv=40)
+    _qkv_case(lm, cfg)
+
+
+# ---------------------------------------------------------------------------
+# NF4
+# ---------------------------------------------------------------------------
+
+def _nf4_dev(lm, W32):
+    import torch
+
+    w = lm.nf4_quantize(dev(W32, "bf16"))
+    torch.cuda.synchronize()
+    return w
+
+
+def _check_nf4_bitexact(lm, W32, w):
+    q = ON.quantize(W32)
+    assert np.array_equal(w.codes.cpu().numpy(), q["codes"]), "packed codes differ"
+    assert np.array_equal(w.q8.cpu().numpy(), q["q8"]), "q8 differ"
+    assert np.array_equal(w.s2.cpu().numpy().view(np.uint32), q["s2"].view(np.uint32)), "s2 differ"
+    assert w.mu.cpu().numpy().view(np.uint32)[0] == np.float32(q["mu"]).view(np.uint32), "mu differs"
+    return q
+
+
+def test_nf4_quantize_dequant_unpack_bitexact(lm):
+    import torch
+
+    rng = np.random.default_rng(95)
+    W = ON.round_to_bf16((rng.standard_normal((512, 256)) / 16).astype(np.float32))
+    W[3, :64] = 0.0  # an all-zero block
+    w = _nf4_dev(lm, W)
+    q = _check_nf4_bitexact(lm, W, w)
+    codes = lm.nf4_unpack_codes(w)
+    d32 = lm.nf4_dequant(w, torch.float32)
+    d16 = lm.nf4_dequant(w, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy(), ON.unpack_codes(q["codes"]))
+    assert np.array_equal(d32.cpu().numpy().view(np.uint32), ON.dequantize(q, "f32").view(np.uint32))
+    ref16 = ON.dequantize(q, "bf16")
+    got16 = d16.view(torch.int16).cpu().numpy().astype(np.uint16).astype(np.uint32) << 16
+    assert np.array_equal(got16, ref16.view(np.uint32))
+
+
+def test_nf4_quantize_fp32_input_bitexact(lm):
+    import torch
+
+    rng = np.random.default_rng(96)
+    W = (rng.standard_normal((128, 256)) * 0.05).astype(np.float32)
+    w = lm.nf4_quantize(dev(W, "f32"))
+    torch.cuda.synchronize()
+    _check_nf4_bitexact(lm, W, w)
+
+
+@pytest.mark.parametrize("act", ["swiglu", "geglu_tanh"])
+def test_qlora_mlp_bf16(lm, act):
+    import torch
+
+    cfg = WorkloadConfig(97, "mlp", T=300, H=512, I=1024, r=16, alpha=32, dtype="bf16", act=act, nf4=True)
+    inp = make_mlp_inputs(cfg)
+    nf4 = {k: _nf4_dev(lm, inp[k]["W"]) for k in ("gate", "up", "down")}
+    for k in nf4:
+        q = _check_nf4_bitexact(lm, inp[k]["W"], nf4[k])
+        inp[k] = dict(inp[k], W=ON.dequantize(q, "bf16"))
+    X, dY = dev(inp["X"]), dev(inp["dY"])
+    g, u, d = (proj_dev(inp[k], "bf16", nf4=nf4[k]) for k in ("gate", "up", "down"))
+    Y, saved = lm.mlp_fwd(X, g, u, d, act)
+    dX, grads = lm.mlp_bwd(dY, X, saved, g, u, d, act)
+    torch.cuda.synchronize()
+    Yr, sr = OL.mlp_fwd(inp["X"], inp["gate"], inp["up"], inp["down"], act)
+    gr = OL.mlp_bwd(inp["dY"], inp["X"], sr, inp["gate"], inp["up"], inp["down"], act)
+    assert_close("Y", host(Y), Yr, TOL["bf16"])
+    assert_close("dX", host(dX), gr["dX"], TOL["bf16"])
+    for k_dev, k_ref in (("dA_gate", "dA_g"), ("dB_gate", "dB_g"), ("dA_up", "dA_u"), ("dB_up", "dB_u"),
+                         ("dA_down", "dA_d"), ("dB_down", "dB_d")):
+        assert_close(k_dev, host(grads[k_dev]), gr[k_ref], TOL["bf16"])
+
+
+@pytest.mark.parametrize("trans", [False, True])
+@pytest.mark.parametrize("with_lora", [False, True])
+def test_nf4_gemm(lm, trans, with_lora):
+    import torch
+
+    rng = np.random.default_rng(98)
+    rows, cols, T, r, s = 512, 768, 300, 16, 2.0
+    W = ON.round_to_bf16((rng.standard_normal((rows, cols)) / np.sqrt(rows)).astype(np.float32))
+    A = ON.round_to_bf16(rng.uniform(-1, 1, (rows, r)).astype(np.float32) / np.sqrt(rows))
+    B = ON.round_to_bf16((rng.standard_normal((r, cols)) * 0.02).astype(np.float32))
+    X = ON.round_to_bf16(rng.standard_normal((T, cols if trans else rows)).astype(np.float32))
+    w = _nf4_dev(lm, W)
+    q = _check_nf4_bitexact(lm, W, w)
+    Wd = ON.dequantize(q, "bf16")
+    Y = lm.nf4_gemm(dev(X), w, dev(A) if with_lora else None, dev(B) if with_lora else None, s, trans)
+    torch.cuda.synchronize()
+    if not trans:
+        ref = X @ Wd + (s * ((X @ A) @ B) if with_lora else 0)
+    else:
+        ref = X @ Wd.T + (s * ((X @ B.T) @ A.T) if with_lora else 0)
+    assert_close("Y", host(Y), ref, TOL["bf16"])
+
+
+# ---------------------------------------------------------------------------
+# Edge cases and invariants
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [0, 1, 255, 257])
+def test_mlp_edge_token_counts(lm, T):
+    import torch
+
+    cfg = WorkloadConfig(99, "mlp", T=T, H=256, I=320, r=16, alpha=32, dtype="bf16")
+    inp = make_mlp_inputs(cfg)
+    X, dY = dev(inp["X"]), dev(inp["dY"])
+    g, u, d = (proj_dev(inp[k]) for k in ("gate", "up", "down"))
+    Y, saved = lm.mlp_fwd(X, g, u, d)
+    grads = dict(dA_gate=torch.full_like(g.A, 7.0), dB_gate=torch.full_like(g.B, 7.0),
+                 dA_up=torch.full_like(u.A, 7.0), dB_up=torch.full_like(u.B, 7.0),
+                 dA_down=torch.full_like(d.A, 7.0), dB_down=torch.full_like(d.B, 7.0))
+    dX, grads = lm.mlp_bwd(dY, X, saved, g, u, d, grads=grads)
+    torch.cuda.synchronize()
+    Yr, sr = OL.mlp_fwd(inp["X"], inp["gate"], inp["up"], inp["down"])
+    gr = OL.mlp_bwd(inp["dY"], inp["X"], sr, inp["gate"], inp["up"], inp["down"])
+    if T == 0:
+        for kk, vv in grads.items():
+            assert torch.all(vv == 0), kk  # outputs are overwritten, not accumulated
+        return
+    assert_close("Y", host(Y), Yr, TOL["bf16"])
+    assert_close("dX", host(dX), gr["dX"], TOL["bf16"])
+    assert_close("dA_gate", host(grads["dA_gate"]), gr["dA_g"], TOL["bf16"])
+    assert_close("dB_down", host(grads["dB_down"]), gr["dB_d"], TOL["bf16"])
+
+
+def test_mlp_B_zero_gives_zero_dA_and_base_output(lm):
+    import torch
+
+    cfg = WorkloadConfig(100, "mlp", T=260, H=256, I=384, r=16, alpha=32, dtype="bf16")
+    inp = make_mlp_inputs(cfg)
+    for k in ("gate", "up", "down"):
+        inp[k]["B"] = np.zeros_like(inp[k]["B"])
+    X, dY = dev(inp["X"]), dev(inp["dY"])
+    g, u, d = (proj_dev(inp[k]) for k in ("gate", "up", "down"))
+    Y, saved = lm.mlp_fwd(X, g, u, d)
+    dX, grads = lm.mlp_bwd(dY, X, saved, g, u, d)
+    torch.cuda.synchronize()
+    for kk in ("dA_gate", "dA_up", "dA_down"):
+        assert torch.all(grads[kk] == 0), kk
+    Yr, sr = OL.mlp_fwd(inp["X"], inp["gate"], inp["up"], inp["down"])
+    assert_close("Y", host(Y), Yr, TOL["bf16"])
+
+
+def test_deterministic_repeat(lm):
+    import torch
+
+    cfg = WorkloadConfig(101, "mlp", T=300, H=512, I=640, r=16, alpha=32, dtype="bf16")
+    inp = make_mlp_inputs(cfg)
+    X, dY = dev(inp["X"]), dev(inp["dY"])
+    g, u, d = (proj_dev(inp[k]) for k in ("gate", "up", "down"))
+    outs = []
+    for _ in range(2):
+        Y, saved = lm.mlp_fwd(X, g, u, d)
+        dX, grads = lm.mlp_bwd(dY, X, saved, g, u, d)
+        torch.cuda.synchronize()
+        outs.append([Y.clone(), dX.clone()] + [grads[k].clone() for k in sorted(grads)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_errors_enqueue_nothing(lm):
+    import torch
+
+    X = torch.zeros((64, 256), dtype=torch.bfloat16, device="cuda:0")
+    A = torch.zeros((256, 16), dtype=torch.bfloat16, device="cuda:0")
+    B = torch.zeros((16, 320), dtype=torch.bfloat16, device="cuda:0")
+    W = torch.zeros((256, 320), dtype=torch.bfloat16, device="cuda:0")
+    p = lm.Proj(A=A, B=B, scale=1.0, W=W)
+    with pytest.raises(lm.LoraError) as ei:
+        lm.o_fwd(X, p, ws=torch.empty(1, dtype=torch.uint8, device="cuda:0"))
+    assert ei.value.status == 5  # LORA_EWORKSPACE
+    with pytest.raises(lm.LoraError) as ei:
+        lm.o_bwd(torch.zeros((64, 320), dtype=torch.bfloat16, device="cuda:0"), X,
+                 torch.zeros((64, 16), dtype=torch.bfloat16, device="cuda:0"), p, dX=X)
+    assert ei.value.status == 6  # LORA_EUNSUPPORTED (dX aliases X)
