@@ -21,6 +21,7 @@ __all__ = [
     "mlp_fwd", "mlp_bwd", "mlp_workspace_size",
     "qkv_fwd", "qkv_bwd", "o_fwd", "o_bwd",
     "nf4_quantize", "nf4_dequant", "nf4_unpack_codes", "nf4_gemm", "nf4_codebook",
+    "trace_begin", "trace_end",
 ]
 
 load = L.load
@@ -322,3 +323,21 @@ def nf4_gemm(X, w: NF4Weight, A=None, B=None, scale=0.0, trans=False, *, Y=None,
     L.call("lora_nf4_gemm", T, int(trans), _ptr(X), C.byref(s), _ptr(A), _ptr(B), r, float(scale), _ptr(Y),
            _ptr(ws), ws.numel(), _stream(stream))
     return Y
+
+
+# ---------------------------------------------------------------------------
+# Kernel timing
+# ---------------------------------------------------------------------------
+
+def trace_begin(prefix: str = "") -> None:
+    """Record HIP-event durations of the library's launches (optionally only
+    kernel families whose name starts with ``prefix``)."""
+    L.call("lora_trace_begin", prefix.encode() if prefix else None)
+
+
+def trace_end() -> dict:
+    """Stop recording; returns {family: (launches, total_ms)}."""
+    buf = (L.lora_trace_entry * 64)()
+    n = C.c_int32()
+    L.call("lora_trace_end", buf, 64, C.byref(n))
+    return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms) for i in range(min(n.value, 64))}

@@ -86,7 +86,7 @@ SIGNATURES = {
     "lora_nf4_unpack_codes": (i32, [P(lora_nf4), vp, vp]),
     "lora_nf4_gemm_workspace_size": (i32, [i64, i64, i64, i64, i32, P(sz)]),
     "lora_nf4_gemm": (i32, [i64, i32, vp, P(lora_nf4), vp, vp, i64, C.c_float, vp, vp, sz, vp]),
-    "lora_trace_begin": (i32, []),
+    "lora_trace_begin": (i32, [C.c_char_p]),
     "lora_trace_end": (i32, [P(lora_trace_entry), i32, P(i32)]),
 }
 

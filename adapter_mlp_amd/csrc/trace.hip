@@ -16,6 +16,7 @@ struct Rec {
 
 std::mutex g_mu;
 bool g_on = false;
+std::string g_prefix;
 std::vector<Rec> g_recs;
 std::vector<hipEvent_t> g_pool;
 
@@ -40,6 +41,7 @@ bool trace_on() {
 void* trace_start(const char* name, hipStream_t st) {
   std::lock_guard<std::mutex> lk(g_mu);
   if (!g_on) return nullptr;
+  if (!g_prefix.empty() && std::strncmp(name, g_prefix.c_str(), g_prefix.size()) != 0) return nullptr;
   Rec r{name, get_event(), get_event()};
   if (!r.start || !r.stop) return nullptr;
   if (hipEventRecord(r.start, st) != hipSuccess) return nullptr;
@@ -60,8 +62,9 @@ using namespace lora;
 
 extern "C" {
 
-lora_status lora_trace_begin(void) {
+lora_status lora_trace_begin(const char* prefix) {
   std::lock_guard<std::mutex> lk(g_mu);
+  g_prefix = prefix ? prefix : "";
   for (auto& r : g_recs) {
     g_pool.push_back(r.start);
     g_pool.push_back(r.stop);

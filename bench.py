@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused LoRA-MLP forward + backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2|3|4|5]
+
+A step is one forward and one backward of the whole path on one batch of
+synthetic, seeded inputs already resident in HBM: for the MLP shapes
+lora_mlp_fwd + lora_mlp_bwd, for the attention shape lora_qkv_fwd/bwd +
+lora_o_fwd/bwd.  The default workload is the Llama-3-8B-shaped SwiGLU LoRA
+MLP (8192 tokens, 4096 -> 14336 -> 4096, r = 16, alpha = 32, bf16 with fp32
+accumulation).
+
+Prints one JSON line with the throughput (tokens/s over the timed steps),
+the roofline of the dominant kernel (timed live with HIP events on the
+library's launch stream) and the CPU oracle timed on a bounded token sample
+on this host ("cpu_baseline").
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 flop/clk x 2.4 GHz (dense)
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_flops(cfg, name):
+    """Algorithmic flops of one launch of a GEMM family for this workload."""
+    T, r = cfg.T, cfg.r
+    if cfg.kind == "mlp":
+        H, I = cfg.H, cfg.I
+        table = {
+            "gemm_nn_act_fwd": 2 * T * H * (2 * I) + 2 * T * r * (2 * I),  # gate+up, incl. U B
+            "gemm_nn_store": 2 * T * I * H + 2 * T * r * H,                  # down
+            "gemm_nt_act_bwd": 2 * T * H * I + 2 * T * r * I,                # dh
+            "gemm_nt_store": 2 * T * (2 * I) * H + 2 * T * (2 * r) * H,      # dX
+        }
+    else:
+        H, N = cfg.H, cfg.Nq + cfg.Nk + cfg.Nv
+        table = {
+            "gemm_nn_store": None,  # QKV and O share the family; averaged below
+            "gemm_nt_store": None,
+        }
+        qkv_f = 2 * T * H * N + 2 * T * r * N
+        o_f = 2 * T * cfg.Nq * H + 2 * T * r * H
+        table["gemm_nn_store"] = (qkv_f + o_f) / 2
+        qkv_b = 2 * T * N * H + 2 * T * (3 * r) * H
+        o_b = 2 * T * H * cfg.Nq + 2 * T * r * cfg.Nq
+        table["gemm_nt_store"] = (qkv_b + o_b) / 2
+    base = name.replace("_nf4", "")
+    return table.get(base)
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in ("gemm_bf16.hip", "common.hpp"):
+        with open(os.path.join(ROOT, "adapter_mlp_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel, workload_tag):
+    """HBM bytes per launch from the committed PMC summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload_tag}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for ln in f:
+            if "=" in ln and not ln.startswith("#"):
+                k, v = ln.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_digest") != source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------
+# Workloads
+# ---------------------------------------------------------------------------
+
+class MlpStep:
+    def __init__(self, cfg, inp, lm, torch):
+        self.cfg, self.lm = cfg, lm
+        dev = lambda a: torch.from_numpy(a).to("cuda:0").to(torch.bfloat16)  # noqa: E731
+        self.X, self.dY = dev(inp["X"]), dev(inp["dY"])
+        self.p = {}
+        for k in ("gate", "up", "down"):
+            nf4 = None
+            if cfg.nf4:
+                nf4 = lm.nf4_quantize(dev(inp[k]["W"]))
+            self.p[k] = lm.Proj(A=dev(inp[k]["A"]), B=dev(inp[k]["B"]), scale=inp[k]["s"],
+                                W=None if cfg.nf4 else dev(inp[k]["W"]), nf4=nf4)
+        T, H, I, r = cfg.T, cfg.H, cfg.I, cfg.r
+        fb, bb = lm.mlp_workspace_size(T, H, I, r, cfg.act)
+        bf = torch.bfloat16
+        self.Y = torch.empty((T, H), dtype=bf, device="cuda:0")
+        self.saved = dict(e=torch.empty((T, I), dtype=bf, device="cuda:0"),
+                          g=torch.empty((T, I), dtype=bf, device="cuda:0"),
+                          U=torch.empty((T, 3 * r), dtype=bf, device="cuda:0"))
+        self.dX = torch.empty_like(self.X)
+        self.grads = {n: torch.empty_like(getattr(self.p[k], m)) for n, k, m in
+                      (("dA_gate", "gate", "A"), ("dB_gate", "gate", "B"), ("dA_up", "up", "A"),
+                       ("dB_up", "up", "B"), ("dA_down", "down", "A"), ("dB_down", "down", "B"))}
+        self.wsf = torch.empty(fb, dtype=torch.uint8, device="cuda:0")
+        self.wsb = torch.empty(bb, dtype=torch.uint8, device="cuda:0")
+
+    def __call__(self):
+        lm, p = self.lm, self.p
+        lm.mlp_fwd(self.X, p["gate"], p["up"], p["down"], self.cfg.act, Y=self.Y, saved=self.saved, ws=self.wsf)
+        lm.mlp_bwd(self.dY, self.X, self.saved, p["gate"], p["up"], p["down"], self.cfg.act, dX=self.dX,
+                   grads=self.grads, ws=self.wsb)
+
+
+class AttnStep:
+    def __init__(self, cfg, inp, lm, torch):
+        self.cfg, self.lm = cfg, lm
+        dev = lambda a: torch.from_numpy(a).to("cuda:0").to(torch.bfloat16)  # noqa: E731
+        self.t = {k: dev(inp[k]) for k in ("X", "Xo", "dQ", "dK", "dV", "dO")}
+        self.p = {k: lm.Proj(A=dev(inp[k]["A"]), B=dev(inp[k]["B"]), scale=inp[k]["s"], W=dev(inp[k]["W"]))
+                  for k in ("q", "k", "v", "o")}
+        T, H, r = cfg.T, cfg.H, cfg.r
+        bf = torch.bfloat16
+        self.qkv = [torch.empty((T, n), dtype=bf, device="cuda:0") for n in (cfg.Nq, cfg.Nk, cfg.Nv)]
+        self.U = torch.empty((T, 3 * r), dtype=bf, device="cuda:0")
+        self.Yo = torch.empty((T, H), dtype=bf, device="cuda:0")
+        self.Uo = torch.empty((T, r), dtype=bf, device="cuda:0")
+        self.dX = torch.empty_like(self.t["X"])
+        self.dXo = torch.empty_like(self.t["Xo"])
+        self.g = {n: torch.empty_like(getattr(self.p[k], m)) for n, k, m in
+                  (("dA_q", "q", "A"), ("dB_q", "q", "B"), ("dA_k", "k", "A"), ("dB_k", "k", "B"),
+                   ("dA_v", "v", "A"), ("dB_v", "v", "B"))}
+        self.dAo = torch.empty_like(self.p["o"].A)
+        self.dBo = torch.empty_like(self.p["o"].B)
+
+    def __call__(self):
+        lm, p, t = self.lm, self.p, self.t
+        lm.qkv_fwd(t["X"], p["q"], p["k"], p["v"], out=self.qkv, U=self.U)
+        lm.o_fwd(t["Xo"], p["o"], Y=self.Yo, U=self.Uo)
+        lm.o_bwd(t["dO"], t["Xo"], self.Uo, p["o"], dX=self.dXo, dA=self.dAo, dB=self.dBo)
+        lm.qkv_bwd(t["dQ"], t["dK"], t["dV"], t["X"], self.U, p["q"], p["k"], p["v"], dX=self.dX, grads=self.g)
+
+
+def cpu_baseline(cfg, inp, seconds):
+    """The oracle as it stands, on the first Ts tokens of the same inputs."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import lora as OL
+    from oracle import nf4 as ON
+
+    if cfg.kind == "mlp":
+        projs = {k: inp[k] for k in ("gate", "up", "down")}
+        if cfg.nf4:  # the QLoRA oracle: the dense oracle on the dequantized base
+            projs = {k: dict(v, W=ON.dequantize(ON.quantize(v["W"]), "bf16")) for k, v in projs.items()}
+
+        def run(ts):
+            X, dY = inp["X"][:ts], inp["dY"][:ts]
+            Y, s = OL.mlp_fwd(X, projs["gate"], projs["up"], projs["down"], cfg.act)
+            OL.mlp_bwd(dY, X, s, projs["gate"], projs["up"], projs["down"], cfg.act)
+    else:
+        def run(ts):
+            X, Xo = inp["X"][:ts], inp["Xo"][:ts]
+            (_, _, _), s = OL.qkv_fwd(X, inp["q"], inp["k"], inp["v"])
+            _, so = OL.o_fwd(Xo, inp["o"])
+            OL.o_bwd(inp["dO"][:ts], Xo, so, inp["o"])
+            OL.qkv_bwd(inp["dQ"][:ts], inp["dK"][:ts], inp["dV"][:ts], X, s, inp["q"], inp["k"], inp["v"])
+
+    ts = min(128, cfg.T)
+    t0 = time.perf_counter()
+    run(ts)
+    probe = time.perf_counter() - t0
+    ts = int(max(128, min(cfg.T, (seconds / max(probe, 1e-3)) * ts)) // 128 * 128)
+    t0 = time.perf_counter()
+    run(ts)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("internal_api") == "openblas"]
+                  or [1])
+    return {"value": ts / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {ts} of {cfg.T} tokens, full-size weights, fp32 numpy oracle fwd+bwd "
+                      f"({dt:.1f} s)", "seconds": round(dt, 2), "cpu_count": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the fused LoRA path runs on a single MI355X here and "
+              "--gpus N with N > 1 is not supported (see the sharding notes in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import adapter_mlp_amd as lm
+    from workload import CONFIGS, make_attn_inputs, make_mlp_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    lm.load()
+    cfg = CONFIGS[args.config]
+    log(f"[bench] config {cfg.cid}: {cfg.note}; generating seeded inputs")
+    t0 = time.time()
+    inp = make_mlp_inputs(cfg) if cfg.kind == "mlp" else make_attn_inputs(cfg)
+    log(f"[bench] inputs ready in {time.time() - t0:.1f} s")
+    step = MlpStep(cfg, inp, lm, torch) if cfg.kind == "mlp" else AttnStep(cfg, inp, lm, torch)
+    torch.cuda.synchronize()
+
+    # warm-up; the first warm-up step also finds the dominant GEMM family
+    lm.trace_begin("")
+    step()
+    torch.cuda.synchronize()
+    fams = lm.trace_end()
+    for _ in range(max(args.warmup - 1, 0)):
+        step()
+    torch.cuda.synchronize()
+    gemms = {k: v for k, v in fams.items() if k.startswith("gemm")}
+    dominant = max(gemms, key=lambda k: gemms[k][1])
+    log("[bench] warm-up per-family ms: " + ", ".join(f"{k}={v[1]:.3f}" for k, v in fams.items()))
+
+    # timed region: only the dominant family carries event pairs
+    lm.trace_begin(dominant)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    traced = lm.trace_end()
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    tokens_s = cfg.T / (ms_step / 1e3)
+    tflops = cfg.flops() / (ms_step / 1e3) / 1e12
+    launches, kms = traced.get(dominant, (0, 0.0))
+    avg_ms = kms / max(launches, 1)
+    fl = kernel_flops(cfg, dominant)
+    achieved = fl / (avg_ms / 1e3) / 1e12 if fl and avg_ms > 0 else None
+    workload_tag = {2: "llama3_8b_mlp", 3: "gemma_geglu_mlp", 4: "llama3_8b_qlora_mlp", 5: "llama3_8b_qkvo"}[cfg.cid]
+    traffic = read_traffic(dominant, workload_tag)
+    log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step ({wall / args.steps * 1e3:.3f} ms wall), "
+        f"{tokens_s:,.0f} tokens/s, {tflops:.1f} TFLOP/s; {dominant}: {avg_ms:.3f} ms/launch")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a token sample")
+        cpu = cpu_baseline(cfg, inp, args.cpu_seconds)
+        log(f"[bench] oracle: {cpu['value']:.1f} tokens/s on {cpu['cores']} threads ({cpu['sample']})")
+
+    out = {
+        "metric": "LoRA-MLP fwd+bwd tokens/s at Llama-3-8B MLP shape; % bf16 MFMA peak"
+        if cfg.kind == "mlp" else "LoRA QKV+O fwd+bwd tokens/s at Llama-3-8B attention shapes",
+        "value": tokens_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; random-init weights and adapters of the named shapes)",
+        "config": {"workload": cfg.note, "tokens": cfg.T, "hidden": cfg.H,
+                   **({"intermediate": cfg.I, "activation": cfg.act} if cfg.kind == "mlp"
+                      else {"q": cfg.Nq, "k": cfg.Nk, "v": cfg.Nv, "o": [cfg.Nq, cfg.H]}),
+                   "rank": cfg.r, "alpha": cfg.alpha, "base": "nf4" if cfg.nf4 else "bf16",
+                   "parallelism": "single GPU"},
+        "tflops": tflops,
+        "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "roofline": {"bound": "mfma", "kernel": dominant, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": (achieved / PEAK_BF16_TFLOPS) if achieved else None,
+                     "traffic": traffic, "flops_per_launch": fl, "avg_launch_ms": avg_ms,
+                     "launches_timed": launches},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -301,8 +301,9 @@ typedef struct lora_trace_entry {
   double total_ms;
 } lora_trace_entry;
 
-/* Start recording (clears earlier records). */
-lora_status lora_trace_begin(void);
+/* Start recording (clears earlier records).  `prefix` limits recording to
+ * kernel families whose name starts with it (NULL or "" records all). */
+lora_status lora_trace_begin(const char* prefix);
 
 /* Stop recording, wait for the recorded events, and write up to `max` entries
  * (one per kernel family, in first-launch order) to out; *count receives the
