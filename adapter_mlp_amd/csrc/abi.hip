@@ -92,6 +92,14 @@ lora_status check_rank(const Ctx& c, int64_t r, int group) {
   return LORA_OK;
 }
 
+// Kernels address each operand with 32-bit byte offsets.
+lora_status check_extent(const Ctx& c, int64_t rows, int64_t cols, const char* what) {
+  const int64_t lim = ((int64_t)1 << 31) - 4096;
+  CHECK(rows <= lim / (cols * (int64_t)c.es), LORA_ESHAPE, "%s (%lld x %lld) exceeds 2 GiB", what,
+        (long long)rows, (long long)cols);
+  return LORA_OK;
+}
+
 lora_status check_ptr(const Ctx& c, const void* p, const char* name) {
   CHECK(p != nullptr, LORA_EINVAL, "%s is NULL", name);
   CHECK(aligned(p, c.bf16 ? 16 : 4), LORA_EALIGN, "%s is not %d-byte aligned", name, c.bf16 ? 16 : 4);
@@ -163,7 +171,8 @@ const void* coff(const void* p, int64_t elems, const Ctx& c) {
 }
 void* offw(void* p, int64_t elems, const Ctx& c) { return static_cast<char*>(p) + elems * (int64_t)c.es; }
 
-hipError_t gemm_on(const Ctx& c, GemmArgs& g, hipStream_t st) {
+hipError_t gemm_on(const Ctx& c, GemmArgs& g, hipStream_t st, int64_t lora_vcols) {
+  g.lora_vcols = lora_vcols;
   const int64_t rows = gemm_tile_rows(c.bf16);
   const int64_t cols = gemm_tile_cols(c.bf16, g.dual != 0);
   g.ntile_m = cdiv(g.M, rows);
@@ -286,6 +295,8 @@ lora_status validate_mlp(const lora_mlp_desc* d, Ctx& c) {
   TRY(check_dim(c, d->H, "H"));
   TRY(check_dim(c, d->I, "I"));
   TRY(check_rank(c, d->r, 2));
+  TRY(check_extent(c, d->T, d->I > d->H ? d->I : d->H, "an activation"));
+  TRY(check_extent(c, d->H, d->I, "a weight"));
   return LORA_OK;
 }
 
@@ -333,6 +344,9 @@ lora_status validate_qkv(const lora_qkv_desc* d, Ctx& c) {
   TRY(check_dim(c, d->Nk, "Nk"));
   TRY(check_dim(c, d->Nv, "Nv"));
   TRY(check_rank(c, d->r, 3));
+  const int64_t nmax = d->H > d->Nq ? d->H : d->Nq;
+  TRY(check_extent(c, d->T, nmax, "an activation"));
+  TRY(check_extent(c, d->H, d->Nq, "a weight"));
   return LORA_OK;
 }
 
@@ -374,6 +388,8 @@ lora_status validate_o(const lora_o_desc* d, Ctx& c) {
   TRY(check_dim(c, d->K, "K"));
   TRY(check_dim(c, d->N, "N"));
   TRY(check_rank(c, d->r, 1));
+  TRY(check_extent(c, d->T, d->K > d->N ? d->K : d->N, "an activation"));
+  TRY(check_extent(c, d->K, d->N, "the weight"));
   return LORA_OK;
 }
 
@@ -419,7 +435,7 @@ lora_status proj_forward(const Ctx& c, int64_t T, int64_t K, int64_t N, int64_t 
   g.reg[0].N = N;
   g.reg[0].out = Y;
   g.reg[0].ldo = N;
-  LAUNCH(gemm_on(c, g, st));
+  LAUNCH(gemm_on(c, g, st, N));
   return LORA_OK;
 }
 
@@ -456,7 +472,7 @@ lora_status proj_input_grad(const Ctx& c, int64_t T, int64_t K, int64_t N, int64
   g.reg[0].N = K;
   g.reg[0].out = dX;
   g.reg[0].ldo = K;
-  LAUNCH(gemm_on(c, g, st));
+  LAUNCH(gemm_on(c, g, st, K));
   return LORA_OK;
 }
 
@@ -568,7 +584,7 @@ lora_status lora_mlp_fwd(const lora_mlp_desc* d, const void* X, const lora_proj*
   g.g_out = saved->g;
   g.h_out = p.h;
   g.ld_act = I;
-  LAUNCH(gemm_on(c, g, st));
+  LAUNCH(gemm_on(c, g, st, 2 * I));
 
   // U_d = h A_d, then the down GEMM
   const void* srcs_d[1] = {down->A};
@@ -608,7 +624,7 @@ lora_status lora_mlp_fwd(const lora_mlp_desc* d, const void* X, const lora_proj*
   gd.RL = (int)RLd;
   gd.BLt = p.BLt_d;
   gd.ldbl = RLd;
-  LAUNCH(gemm_on(c, gd, st));
+  LAUNCH(gemm_on(c, gd, st, H));
   return LORA_OK;
 }
 
@@ -688,7 +704,7 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, 
   g.de_out = p.de;
   g.h_out = p.hb;
   g.ld_act = I;
-  LAUNCH(gemm_on(c, g, st));
+  LAUNCH(gemm_on(c, g, st, I));
 
   // dA_d = s_d h^T P_d  (P_d already scaled)
   ColProjArgs c2 = colproj_args(p.hb, I, T, I, p.Ps_d, RLd, (int)r, (int)r, false, p.partial);
@@ -758,7 +774,7 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, 
   gx.RL = (int)RLg;
   gx.BLt = p.BLt_dx;
   gx.ldbl = RLg;
-  if (T > 0) LAUNCH(gemm_on(c, gx, st));
+  if (T > 0) LAUNCH(gemm_on(c, gx, st, H));
   return LORA_OK;
 }
 
@@ -848,7 +864,7 @@ lora_status lora_qkv_fwd(const lora_qkv_desc* d, const void* X, const lora_proj*
   g.RL = (int)RL;
   g.BLt = p.BLt;
   g.ldbl = RL;
-  LAUNCH(gemm_on(c, g, st));
+  LAUNCH(gemm_on(c, g, st, Nq + Nk + Nv));
   return LORA_OK;
 }
 
@@ -939,7 +955,7 @@ lora_status lora_qkv_bwd(const lora_qkv_desc* d, const void* dQ, const void* dK,
   g.RL = (int)RL;
   g.BLt = p.BLt_dx;
   g.ldbl = RL;
-  LAUNCH(gemm_on(c, g, st));
+  LAUNCH(gemm_on(c, g, st, H));
   return LORA_OK;
 }
 

@@ -7,20 +7,25 @@
 // products of the unsloth LoRA_MLP / LoRA_QKV / LoRA_W hunks):
 //   forward   Z = X W + (s X A) B        (B operand [K, N], N-contiguous: "NN")
 //   backward  dX = dZ W^T + (s P) A^T    (B operand [N, K], K-contiguous: "NT")
-// The adapter term is one more K-step of the same MFMA loop: [X | sU] [W ; B].
+// The adapter term is one more K tile of the same MFMA loop: [X | sU] [W ; B].
 //
-// Epilogues run on the accumulators in registers:
+// Epilogues run on the accumulators right after the K loop:
 //   EPI_STORE    round to bf16, store;
 //   EPI_ACT_FWD  (gate/up tiles) e, g -> bf16, h = phi(e) g from the rounded
 //                e, g, store e, g, h;
 //   EPI_ACT_BWD  dh -> load e, g, recompute h, dg = dh phi(e),
 //                de = dh g phi'(e), store dg, de, h.
+// Each wavefront stages its results through a private LDS region so global
+// loads and stores move whole 16-byte chunks of consecutive columns.
 //
 // MFMA roles.  The weight tile is the MFMA "A" source (32 rows = output
 // columns n) and the activation tile the "B" source (32 columns = rows m), so
-// each lane ends with 4 consecutive output columns of one row: the epilogue
-// writes 8-byte vectors and the gated activation finds e and g of the same
-// element in the same lane.
+// each lane ends with 4 consecutive output columns of one row, and the gated
+// activation finds e and g of the same element in the same lane.
+//
+// Operands are read with buffer loads: the descriptor base advances by one K
+// tile per step (scalar work only) and rows past the end of a matrix read as
+// zero, which covers ragged M and N tiles without clamping.
 //
 // NN weight tiles (forward) are transposed on the way into LDS: each thread
 // loads an 8x8 bf16 sub-block (8 rows of 16 bytes) and transposes it in
@@ -32,52 +37,82 @@
 // looks up its level, and fl32(level * absmax) is rounded to bf16 before the
 // 16 bytes go to LDS ("loralei" README, section "Use": unpack and
 // double-scale reconstruction fused into the matmul).
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace lora {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64, NTH = 256;
+constexpr int BM = 256, BK = 64, NTH = 256;
 constexpr int TILE_CHUNKS = 256 * 8;  // 16-byte chunks per 256 x 64 bf16 tile
+constexpr int OOB = 0x7ffffff0;       // a buffer offset past every operand: loads return 0
 
 // XOR swizzle of the 16-byte chunk index inside a 128-byte LDS row.  Rows read
 // together by an MFMA fragment load (8 consecutive rows) and rows written
-// together by the transposing store (rows 8 apart) land in different banks.
+// together by the transposing store land in different banks.
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Values the compiler cannot prove uniform are moved to scalar registers.
+__device__ __forceinline__ int64_t uni64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Buffer descriptor over [p, p + bytes) (bytes < 2^31); every input is uniform.
+__device__ __forceinline__ rsrc_t rsrc(const void* p, int64_t bytes) {
+  if (bytes < 0) bytes = 0;
+  const int64_t base = uni64(reinterpret_cast<int64_t>(p));
+  const int n = __builtin_amdgcn_readfirstlane((int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), (short)0, n, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t bload4(rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ int bload1s(rsrc_t r, int off) {
+  return (int)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+
+// Wavefront-local LDS hand-off between lanes (each wavefront stages into its
+// own LDS region in the epilogue, so no block barrier is needed).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 // Block -> tile.  Workgroups are dispatched round-robin over the 8 XCDs, so
 // block b runs on XCD b % 8.  Re-number blocks so that each XCD receives a
 // contiguous run of logical tiles, and walk logical tiles in groups of 8
 // m-tiles (n-major inside a group) so the 32 tiles an XCD holds at once share
 // 8 activation panels and 4 weight panels in its L2.
-__device__ __forceinline__ void tile_coords(int64_t bid, int64_t nb, int64_t ntm, int64_t ntn,
-                                            int64_t& tm, int64_t& tn) {
-  const int64_t q = nb >> 3, rem = nb & 7, x = bid & 7, j = bid >> 3;
-  const int64_t lid = (x < rem) ? x * (q + 1) + j : rem * (q + 1) + (x - rem) * q + j;
-  const int64_t G = 8;
-  const int64_t per_group = G * ntn;
-  const int64_t grp = lid / per_group;
-  const int64_t first_m = grp * G;
-  const int64_t gsize = (ntm - first_m < G) ? (ntm - first_m) : G;
-  const int64_t in_g = lid - grp * per_group;
+__device__ __forceinline__ void tile_coords(int bid, int nb, int ntm, int ntn, int& tm, int& tn) {
+  const int q = nb >> 3, rem = nb & 7, x = bid & 7, j = bid >> 3;
+  const int lid = (x < rem) ? x * (q + 1) + j : rem * (q + 1) + (x - rem) * q + j;
+  const int G = 8;
+  const int per_group = G * ntn;
+  const int grp = lid / per_group;
+  const int first_m = grp * G;
+  const int gsize = (ntm - first_m < G) ? (ntm - first_m) : G;
+  const int in_g = lid - grp * per_group;
   tm = first_m + in_g % gsize;
   tn = in_g / gsize;
 }
 
-// Tile-local weight row nl (0..255) -> (column group, output column).
+// Tile-local weight row nl (0..255) -> output column.  Dual tiles hold
+// [gate 64 | up 64] for wavefront column 0, then the same for column 1.
 template <bool DUAL>
-__device__ __forceinline__ void colmap(int nl, int64_t tnl, int& cg, int64_t& n) {
-  if constexpr (DUAL) {
-    cg = (nl >> 6) & 1;
-    n = tnl * 128 + (int64_t)(nl >> 7) * 64 + (nl & 63);
-  } else {
-    cg = 0;
-    n = tnl * 256 + nl;
-  }
+__device__ __forceinline__ int64_t colmap(int nl, int64_t tnl) {
+  if constexpr (DUAL) return tnl * 128 + (int64_t)(nl >> 7) * 64 + (nl & 63);
+  else return tnl * 256 + nl;
 }
-
-__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 // 8x8 bf16 transpose: r[i] holds row i (8 values, 2 per dword); o[j] receives
 // column j (the 8 row values, 2 per dword).
@@ -106,22 +141,34 @@ __device__ __forceinline__ u32x4 nf4_decode8(uint32_t w, float absmax, const flo
   return o;
 }
 
+// Calls f(integral_constant<int, 0..3>) so accumulator indices stay
+// compile-time constants (a runtime index would move the accumulators to
+// scratch memory).
+template <typename F>
+__device__ __forceinline__ void for4(F&& f) {
+  f(std::integral_constant<int, 0>{});
+  f(std::integral_constant<int, 1>{});
+  f(std::integral_constant<int, 2>{});
+  f(std::integral_constant<int, 3>{});
+}
+
 struct Stage {
   u32x4 a[8];
-  u32x4 b[8];       // dense rows, or b[i].x = NF4 code dword
-  float bs2[8];     // NF4: scaler-block scale per row
-  float bmu[8];     // NF4: mean absmax of the row's weight
-  int bq8[8];       // NF4: block code per row
+  u32x4 b[8];   // dense rows, or b[i][0] = NF4 code dword
+  float bs2[8];
+  int bq8[8];
 };
 
 template <int BKIND, bool NF4, bool DUAL, int EPI>
 __global__ __launch_bounds__(NTH, 1) void gemm_bf16_kernel(const GemmArgs args) {
-  __shared__ u32x4 sA[2 * TILE_CHUNKS];
-  __shared__ u32x4 sB[2 * TILE_CHUNKS];
+  __shared__ u32x4 smem[4 * TILE_CHUNKS];  // A: 2 buffers, B: 2 buffers; reused by the epilogue
   __shared__ float s_lut[16];
+  u32x4* const sA = smem;
+  u32x4* const sB = smem + 2 * TILE_CHUNKS;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
   if (NF4 && tid < 16) {
@@ -129,123 +176,127 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_kernel(const GemmArgs args) 
     s_lut[tid] = lv[tid];
   }
 
-  int64_t tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, args.ntile_m, args.ntile_n, tm, tn);
+  // Tile coordinates are uniform; keep them (and all that derives from them)
+  // in scalar registers so buffer descriptors stay scalar.
+  int tm, tn;
+  tile_coords((int)blockIdx.x, (int)gridDim.x, (int)args.ntile_m, (int)args.ntile_n, tm, tn);
+  tm = __builtin_amdgcn_readfirstlane(tm);
+  tn = __builtin_amdgcn_readfirstlane(tn);
   int reg = 0;
 #pragma unroll
   for (int p = 1; p < 3; ++p)
     if (p < args.nreg && tn >= args.reg[p].tile0) reg = p;
-  const int64_t tnl = tn - args.reg[reg].tile0;
-  const int64_t NR = args.reg[reg].N;
+  reg = __builtin_amdgcn_readfirstlane(reg);
+  const int64_t tnl = uni64(tn - args.reg[reg].tile0);
+  const int64_t NR = uni64(args.reg[reg].N);
   const int64_t M = args.M;
-  const int64_t m0 = tm * BM;
+  const int64_t m0 = (int64_t)tm * BM;
 
-  // Per-thread constant load geometry.
-  const int a_c = tid & 7;          // 16-byte chunk in a 64-wide K slice
-  const int a_r0 = tid >> 3;        // first of 8 rows (stride 32)
-  const int nn_n8 = tid & 31;       // NN: 8-column group
-  const int nn_k8 = tid >> 5;       // NN: 8-row group of K
-
-  // Weight-row geometry (clamped to valid memory; clamped rows only feed
-  // output columns that are never stored).
-  // Row a_r0 + 32 i of a dual tile is in column group (i >> 1) & 1 for every
-  // lane (a_r0 < 32), so the group index is a compile-time constant.
-  int64_t nt_col[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int cg;
-    int64_t n;
-    colmap<DUAL>(a_r0 + 32 * i, tnl, cg, n);
-    nt_col[i] = n < NR ? n : NR - 1;
-  }
-  auto nt_cg = [](int i) { return DUAL ? ((i >> 1) & 1) : 0; };
-  int nn_cg;
-  int64_t nn_col;
-  {
-    int64_t n;
-    colmap<DUAL>(nn_n8 * 8, tnl, nn_cg, n);
-    nn_col = n < NR ? n : NR - 8;
-  }
-  int64_t a_row[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t m = m0 + a_r0 + 32 * i;
-    a_row[i] = m < M ? m : M - 1;
-  }
+  // Per-thread load geometry.
+  //  A and NT weights: 16-byte chunk a_c of rows a_r0 + 32 i.
+  //  NN weights: wavefront w owns tile columns 64w..64w+63 (one column group
+  //  of a dual tile); lane = 8 k8 + n8 loads K rows 8 k8..+7, columns 8 n8..+7.
+  const int a_c = tid & 7;
+  const int a_r0 = tid >> 3;
+  const int nn_n8 = lane & 7, nn_k8 = lane >> 3;
+  const int nn_cg = DUAL ? (wave & 1) : 0;
+  const int64_t nn_col = colmap<DUAL>(wave * 64 + nn_n8 * 8, tnl);
 
   int64_t ktiles = 0;
   for (int s = 0; s < args.nseg; ++s) ktiles += args.seg[s].K / BK;
   const bool has_lora = args.RL > 0;
   const int64_t KT = ktiles + (has_lora ? 1 : 0);
 
-  // --- global -> registers for one K tile ---------------------------------
-  auto load_tile = [&](Stage& st, int seg, int64_t k0, bool lora) {
-    if (lora) {
-      const int nch = args.RL >> 3;
-      const char* AL = static_cast<const char*>(args.AL);
-      const char* BL = static_cast<const char*>(args.BLt);
+  // Segment state (uniform): current segment and the K offset inside it.
+  int seg = 0;
+  int64_t k0 = 0;
+  int a_off[8];  // byte offsets of this thread's 8 A rows (OOB past M)
+  int b_off[8];  // dense: byte offsets of its 8 weight rows; NF4: element index
+  auto seg_setup = [&](int s) {
+    const GemmSeg& S = args.seg[s];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        st.a[i] = u32x4{0, 0, 0, 0};
-        st.b[i] = u32x4{0, 0, 0, 0};
-        if (a_c < nch) {
-          st.a[i] = ld16(AL + (a_row[i] * args.ldal + a_c * 8) * 2);
-          const int64_t v = args.reg[reg].vcol0[nt_cg(i)] + nt_col[i];
-          st.b[i] = ld16(BL + (v * args.ldbl + a_c * 8) * 2);
-        }
-      }
-      return;
+    for (int i = 0; i < 8; ++i) {
+      const int64_t m = m0 + a_r0 + 32 * i;
+      a_off[i] = m < M ? (int)((m * S.lda + a_c * 8) * 2) : OOB;
     }
-    const GemmSeg& S = args.seg[seg];
-    const char* A = static_cast<const char*>(S.A);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) st.a[i] = ld16(A + (a_row[i] * S.lda + k0 + a_c * 8) * 2);
     if constexpr (BKIND == B_NT) {
+      const BSrc& B = S.b[reg][0];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const BSrc& B = S.b[reg][nt_cg(i)];
-        if constexpr (NF4) {
-          const int64_t flat = nt_col[i] * B.wcols + k0 + a_c * 8;
-          st.b[i][0] = *reinterpret_cast<const uint32_t*>(B.codes + (flat >> 1));
-          st.bq8[i] = B.q8[flat >> 6];
-          st.bs2[i] = B.s2[flat >> 14];
-          st.bmu[i] = *B.mu;
-        } else {
-          st.b[i] = ld16(static_cast<const char*>(B.p) + (nt_col[i] * B.ld + k0 + a_c * 8) * 2);
-        }
+        const int64_t n = colmap<DUAL>(a_r0 + 32 * i, tnl);
+        if constexpr (NF4) b_off[i] = n < NR ? (int)(n * B.wcols + a_c * 8) : OOB;
+        else b_off[i] = n < NR ? (int)((n * B.ld + a_c * 8) * 2) : OOB;
       }
     } else {
-      // In dual tiles the lanes of a wavefront read both column groups; pick
-      // the source per lane with selects on uniformly loaded descriptors.
-      const BSrc& B0 = S.b[reg][0];
-      const BSrc& B1 = S.b[reg][DUAL ? 1 : 0];
-      const bool g1 = DUAL && nn_cg == 1;
-      if constexpr (NF4) {
-        const uint8_t* codes = g1 ? B1.codes : B0.codes;
-        const int8_t* q8 = g1 ? B1.q8 : B0.q8;
-        const float* s2 = g1 ? B1.s2 : B0.s2;
-        const float mu = g1 ? *B1.mu : *B0.mu;
-        const int64_t wcols = g1 ? B1.wcols : B0.wcols;
+      const BSrc& B = S.b[reg][nn_cg];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int64_t flat = (k0 + nn_k8 * 8 + i) * wcols + nn_col;
-          st.b[i][0] = *reinterpret_cast<const uint32_t*>(codes + (flat >> 1));
-          st.bq8[i] = q8[flat >> 6];
-          st.bs2[i] = s2[flat >> 14];
-          st.bmu[i] = mu;
-        }
-      } else {
-        const char* bp = static_cast<const char*>(g1 ? B1.p : B0.p);
-        const int64_t ld = g1 ? B1.ld : B0.ld;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          st.b[i] = ld16(bp + ((k0 + nn_k8 * 8 + i) * ld + nn_col) * 2);
+      for (int i = 0; i < 8; ++i) {
+        if constexpr (NF4) b_off[i] = (int)((nn_k8 * 8 + i) * B.wcols + nn_col);
+        else b_off[i] = (int)(((nn_k8 * 8 + i) * B.ld + nn_col) * 2);
       }
     }
   };
 
-  // --- registers -> LDS -----------------------------------------------------
-  auto store_tile = [&](Stage& st, int buf, bool lora) {
+  // --- global -> registers for one main K tile ---------------------------------
+  auto load_main = [&](Stage& st) {
+    const GemmSeg& S = args.seg[seg];
+    const rsrc_t ra = rsrc(static_cast<const char*>(S.A) + k0 * 2, M * S.lda * 2 - k0 * 2);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.a[i] = bload16(ra, a_off[i]);
+    const BSrc& B = S.b[reg][BKIND == B_NN ? nn_cg : 0];
+    if constexpr (NF4) {
+      // weight rows x cols = (NT: N x K_s, NN: K_s x N); tile start in elements
+      const int64_t numel = (BKIND == B_NT ? NR : S.K) * B.wcols;
+      const int64_t kofs = BKIND == B_NT ? k0 : k0 * B.wcols;
+      const rsrc_t rc = rsrc(B.codes + kofs / 2, numel / 2 - kofs / 2);
+      const rsrc_t rq = rsrc(B.q8, numel / 64);
+      const rsrc_t rs = rsrc(B.s2, (numel / NF4_GROUP) * 4);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bool ok = b_off[i] != OOB;
+        const uint32_t flat = (uint32_t)b_off[i] + (uint32_t)kofs;
+        st.b[i][0] = bload4(rc, ok ? (int)((uint32_t)b_off[i] >> 1) : OOB);
+        st.bq8[i] = bload1s(rq, ok ? (int)(flat >> 6) : OOB);
+        st.bs2[i] = __uint_as_float(bload4(rs, ok ? (int)((flat >> 14) << 2) : OOB));
+      }
+    } else {
+      const int64_t total = (BKIND == B_NT ? NR : S.K) * B.ld * 2;
+      const int64_t adv = (BKIND == B_NT ? k0 : k0 * B.ld) * 2;
+      const rsrc_t rb = rsrc(static_cast<const char*>(B.p) + adv, total - adv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) st.b[i] = bload16(rb, b_off[i]);
+    }
+  };
+
+  // NF4 codes -> bf16 (at LDS-store time, after the loads have landed).
+  auto decode_nf4 = [&](Stage& st) {
+    if constexpr (NF4) {
+      const float mu = *args.seg[seg].b[reg][BKIND == B_NN ? nn_cg : 0].mu;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        st.b[i] = nf4_decode8(st.b[i][0], nf4_absmax((int8_t)st.bq8[i], st.bs2[i], mu), s_lut);
+    } else {
+      (void)st;
+    }
+  };
+
+  // --- the LoRA tile: A_L [M, RL] and BLt [vcols, RL], both K-contiguous -----
+  auto load_lora = [&](Stage& st) {
+    const rsrc_t ra = rsrc(args.AL, M * args.ldal * 2);
+    const rsrc_t rb = rsrc(args.BLt, args.lora_vcols * args.ldbl * 2);
+    const bool chunk_ok = a_c < (args.RL >> 3);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t m = m0 + a_r0 + 32 * i;
+      st.a[i] = bload16(ra, (chunk_ok && m < M) ? (int)((m * args.ldal + a_c * 8) * 2) : OOB);
+      const int64_t n = colmap<DUAL>(a_r0 + 32 * i, tnl);
+      const int64_t v = args.reg[reg].vcol0[DUAL ? ((i >> 1) & 1) : 0] + n;
+      st.b[i] = bload16(rb, (chunk_ok && n < NR) ? (int)((v * args.ldbl + a_c * 8) * 2) : OOB);
+    }
+  };
+
+  // --- registers -> LDS ---------------------------------------------------------
+  auto store_tile = [&](const Stage& st, int buf, bool kcontig_b) {
     u32x4* dA = sA + buf * TILE_CHUNKS;
     u32x4* dB = sB + buf * TILE_CHUNKS;
 #pragma unroll
@@ -253,25 +304,18 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_kernel(const GemmArgs args) 
       const int row = a_r0 + 32 * i;
       dA[row * 8 + (a_c ^ swz(row))] = st.a[i];
     }
-    if (lora || BKIND == B_NT) {
+    if (kcontig_b) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int row = a_r0 + 32 * i;
-        u32x4 v = st.b[i];
-        if (NF4 && !lora) v = nf4_decode8(st.b[i][0], nf4_absmax((int8_t)st.bq8[i], st.bs2[i], st.bmu[i]), s_lut);
-        dB[row * 8 + (a_c ^ swz(row))] = v;
+        dB[row * 8 + (a_c ^ swz(row))] = st.b[i];
       }
     } else {
-      u32x4 rows[8], cols[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if constexpr (NF4) rows[i] = nf4_decode8(st.b[i][0], nf4_absmax((int8_t)st.bq8[i], st.bs2[i], st.bmu[i]), s_lut);
-        else rows[i] = st.b[i];
-      }
-      transpose8x8(rows, cols);
+      u32x4 cols[8];
+      transpose8x8(st.b, cols);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int row = nn_n8 * 8 + j;
+        const int row = wave * 64 + nn_n8 * 8 + j;
         dB[row * 8 + (nn_k8 ^ swz(row))] = cols[j];
       }
     }
@@ -283,169 +327,212 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_kernel(const GemmArgs args) 
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-  auto kstep = [&](const u32x4* tA, const u32x4* tB, int ks) {
-    {
+  // 4 K-steps of 16 over one LDS buffer; fragments of step s+1 are read while
+  // the MFMAs of step s issue.
+  auto compute = [&](int buf) {
+    const u32x4* tA = sA + buf * TILE_CHUNKS;
+    const u32x4* tB = sB + buf * TILE_CHUNKS;
+    bf16x8 fa[2][4], fb[2][4];
+    auto frags = [&](int ks, bf16x8 (&xa)[4], bf16x8 (&xb)[4]) {
       const int c = ks * 2 + (lane >> 5);
-      bf16x8 fa[4], fb[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rn = wn * 128 + i * 32 + (lane & 31);
-        fa[i] = __builtin_bit_cast(bf16x8, tB[rn * 8 + (c ^ swz(rn))]);
+        xa[i] = __builtin_bit_cast(bf16x8, tB[rn * 8 + (c ^ swz(rn))]);
         const int rm = wm * 128 + i * 32 + (lane & 31);
-        fb[i] = __builtin_bit_cast(bf16x8, tA[rm * 8 + (c ^ swz(rm))]);
+        xb[i] = __builtin_bit_cast(bf16x8, tA[rm * 8 + (c ^ swz(rm))]);
       }
+    };
+    frags(0, fa[0], fb[0]);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks < 3) frags(ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][i], fb[ks & 1][j], acc[i][j], 0, 0, 0);
     }
   };
-  // Every tile runs the same 4 K-steps: the LoRA tile is zero-padded past RL.
-  // (One uniform path keeps the accumulators in place in AGPRs; a separate
-  // short path for the LoRA tile made the compiler copy them.)
-  auto compute = [&](int buf) {
-    const u32x4* tA = sA + buf * TILE_CHUNKS;
-    const u32x4* tB = sB + buf * TILE_CHUNKS;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) kstep(tA, tB, ks);
+
+  auto advance = [&]() {
+    k0 += BK;
+    if (k0 >= args.seg[seg].K && seg + 1 < args.nseg) {
+      ++seg;
+      k0 = 0;
+      seg_setup(seg);
+    }
   };
 
   // --- main loop: prefetch tile t+1 into registers while tile t computes ---
   Stage st;
-  int ld_seg = 0;
-  int64_t ld_k0 = 0;
-  auto next_pos = [&]() {
-    ld_k0 += BK;
-    if (ld_seg < args.nseg && ld_k0 >= args.seg[ld_seg].K) {
-      ++ld_seg;
-      ld_k0 = 0;
-    }
-  };
-  const bool first_lora = ld_seg >= args.nseg;
-  load_tile(st, ld_seg, ld_k0, first_lora);
+  seg_setup(0);
+  load_main(st);
   __syncthreads();  // s_lut ready
-  store_tile(st, 0, first_lora);
-  next_pos();
+  decode_nf4(st);
+  store_tile(st, 0, BKIND == B_NT);
   __syncthreads();
 
   for (int64_t t = 0; t < KT; ++t) {
     const int buf = (int)(t & 1);
     const bool has_next = t + 1 < KT;
-    const bool nxt_lora = ld_seg >= args.nseg;
-    if (has_next) load_tile(st, ld_seg, ld_k0, nxt_lora);
+    const bool next_lora = has_lora && t + 1 == ktiles;
+    if (has_next) {
+      if (next_lora) {
+        load_lora(st);
+      } else {
+        advance();
+        load_main(st);
+      }
+    }
     compute(buf);
     if (has_next) {
-      store_tile(st, buf ^ 1, nxt_lora);
-      next_pos();
+      if (!next_lora) decode_nf4(st);
+      store_tile(st, buf ^ 1, next_lora || BKIND == B_NT);
     }
     __syncthreads();
   }
 
-  // --- epilogue --------------------------------------------------------------
-  const int mlane = lane & 31;
-  const int nhalf = (lane >> 5) * 4;
+  // --- epilogue: per-wavefront LDS staging, coalesced global access ----------
+  const int64_t mw = m0 + wm * 128;           // first row of this wavefront
+  const int64_t nbase = colmap<DUAL>(wn * 128, tnl);  // first output column
   if constexpr (EPI == EPI_STORE) {
+    // bf16 staging [32 rows][128 cols], row stride 136 elements
+    uint16_t* stg = reinterpret_cast<uint16_t*>(smem) + wave * (32 * 136);
     char* out = static_cast<char*>(args.reg[reg].out);
     const int64_t ldo = args.reg[reg].ldo;
+    for4([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t m = m0 + wm * 128 + j * 32 + mlane;
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int nl = wn * 128 + i * 32 + 8 * g + nhalf;
-          int cg;
-          int64_t n;
-          colmap<DUAL>(nl, tnl, cg, n);
-          if (m < M && n < NR) {
-            u32x2 v;
-            v[0] = pack_bf2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
-            v[1] = pack_bf2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-            *reinterpret_cast<u32x2*>(out + (m * ldo + n) * 2) = v;
-          }
+          const int col = i * 32 + 8 * g + 4 * (lane >> 5);
+          u32x2 v;
+          v[0] = pack_bf2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
+          v[1] = pack_bf2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+          *reinterpret_cast<u32x2*>(stg + (lane & 31) * 136 + col) = v;
         }
+      wave_sync();
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int row = it * 4 + (lane >> 4), c8 = lane & 15;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * 136 + c8 * 8);
+        const int64_t m = mw + j * 32 + row;
+        const int64_t n = nbase + c8 * 8;
+        if (m < M && n < NR) *reinterpret_cast<u32x4*>(out + (m * ldo + n) * 2) = v;
       }
-    }
+      wave_sync();
+    });
   } else if constexpr (EPI == EPI_ACT_FWD) {
     static_assert(DUAL, "activation forward needs gate/up tiles");
+    // three bf16 arrays [32 rows][64 cols] (e, g, h), row stride 72 elements
+    constexpr int ARR = 32 * 72;
+    uint16_t* stg = reinterpret_cast<uint16_t*>(smem) + wave * (3 * ARR);
     char* eo = static_cast<char*>(args.e_out);
     char* go = static_cast<char*>(args.g_out);
     char* ho = static_cast<char*>(args.h_out);
     const int64_t ld = args.ld_act;
+    for4([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t m = m0 + wm * 128 + j * 32 + mlane;
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int nl = wn * 128 + i * 32 + 8 * g + nhalf;
-          int cg;
-          int64_t n;
-          colmap<DUAL>(nl, tnl, cg, n);
-          if (m < M && n < NR) {
-            u32x2 ev, gv, hv;
+          const int col = i * 32 + 8 * g + 4 * (lane >> 5);
+          u32x2 ev, gv, hv;
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              ev[h] = pack_bf2(acc[i][j][4 * g + 2 * h], acc[i][j][4 * g + 2 * h + 1]);
-              gv[h] = pack_bf2(acc[i + 2][j][4 * g + 2 * h], acc[i + 2][j][4 * g + 2 * h + 1]);
-              float p0, p1;
-              act_fwd<false>(args.act, lo_bf(ev[h]), p0);
-              act_fwd<false>(args.act, hi_bf(ev[h]), p1);
-              hv[h] = pack_bf2(p0 * lo_bf(gv[h]), p1 * hi_bf(gv[h]));
-            }
-            const int64_t off = (m * ld + n) * 2;
-            *reinterpret_cast<u32x2*>(eo + off) = ev;
-            *reinterpret_cast<u32x2*>(go + off) = gv;
-            *reinterpret_cast<u32x2*>(ho + off) = hv;
+          for (int h = 0; h < 2; ++h) {
+            ev[h] = pack_bf2(acc[i][j][4 * g + 2 * h], acc[i][j][4 * g + 2 * h + 1]);
+            gv[h] = pack_bf2(acc[i + 2][j][4 * g + 2 * h], acc[i + 2][j][4 * g + 2 * h + 1]);
+            float p0, p1;
+            act_fwd<false>(args.act, lo_bf(ev[h]), p0);
+            act_fwd<false>(args.act, hi_bf(ev[h]), p1);
+            hv[h] = pack_bf2(p0 * lo_bf(gv[h]), p1 * hi_bf(gv[h]));
           }
+          const int o = (lane & 31) * 72 + col;
+          *reinterpret_cast<u32x2*>(stg + o) = ev;
+          *reinterpret_cast<u32x2*>(stg + ARR + o) = gv;
+          *reinterpret_cast<u32x2*>(stg + 2 * ARR + o) = hv;
+        }
+      wave_sync();
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int row = it * 8 + (lane >> 3), c8 = lane & 7;
+        const int64_t m = mw + j * 32 + row;
+        const int64_t n = nbase + c8 * 8;
+        if (m < M && n < NR) {
+          const int o = row * 72 + c8 * 8;
+          const int64_t off = (m * ld + n) * 2;
+          *reinterpret_cast<u32x4*>(eo + off) = *reinterpret_cast<const u32x4*>(stg + o);
+          *reinterpret_cast<u32x4*>(go + off) = *reinterpret_cast<const u32x4*>(stg + ARR + o);
+          *reinterpret_cast<u32x4*>(ho + off) = *reinterpret_cast<const u32x4*>(stg + 2 * ARR + o);
         }
       }
-    }
+      wave_sync();
+    });
   } else {
+    // fp32 staging of dh [32 rows][128 cols], row stride 132 floats
+    float* stg = reinterpret_cast<float*>(smem) + wave * (32 * 132);
     const char* ei = static_cast<const char*>(args.e_in);
     const char* gi = static_cast<const char*>(args.g_in);
     char* dgo = static_cast<char*>(args.dg_out);
     char* deo = static_cast<char*>(args.de_out);
     char* ho = static_cast<char*>(args.h_out);
     const int64_t ld = args.ld_act;
+    for4([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t m = m0 + wm * 128 + j * 32 + mlane;
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int nl = wn * 128 + i * 32 + 8 * g + nhalf;
-          int cg;
-          int64_t n;
-          colmap<DUAL>(nl, tnl, cg, n);
-          if (m < M && n < NR) {
-            const int64_t off = (m * ld + n) * 2;
-            const u32x2 ev = *reinterpret_cast<const u32x2*>(ei + off);
-            const u32x2 gv = *reinterpret_cast<const u32x2*>(gi + off);
-            u32x2 dgv, dev, hv;
+          const int col = i * 32 + 8 * g + 4 * (lane >> 5);
+          *reinterpret_cast<f32x4*>(stg + (lane & 31) * 132 + col) =
+              f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+        }
+      wave_sync();
+      u32x4 ev[8], gv[8];
+      f32x4 d0[8], d1[8];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              float d0 = acc[i][j][4 * g + 2 * h], d1 = acc[i][j][4 * g + 2 * h + 1];
-              float e0 = lo_bf(ev[h]), e1 = hi_bf(ev[h]);
-              float g0 = lo_bf(gv[h]), g1 = hi_bf(gv[h]);
-              float p0, q0, p1, q1;
-              act_fwd_bwd<false>(args.act, e0, p0, q0);
-              act_fwd_bwd<false>(args.act, e1, p1, q1);
-              hv[h] = pack_bf2(p0 * g0, p1 * g1);
-              dgv[h] = pack_bf2(d0 * p0, d1 * p1);
-              dev[h] = pack_bf2(d0 * g0 * q0, d1 * g1 * q1);
-            }
-            *reinterpret_cast<u32x2*>(dgo + off) = dgv;
-            *reinterpret_cast<u32x2*>(deo + off) = dev;
-            *reinterpret_cast<u32x2*>(ho + off) = hv;
-          }
+      for (int it = 0; it < 8; ++it) {
+        const int row = it * 4 + (lane >> 4), c8 = lane & 15;
+        const int64_t m = mw + j * 32 + row;
+        const int64_t n = nbase + c8 * 8;
+        const bool ok = m < M && n < NR;
+        const int64_t off = ok ? (m * ld + n) * 2 : 0;
+        ev[it] = ok ? *reinterpret_cast<const u32x4*>(ei + off) : u32x4{0, 0, 0, 0};
+        gv[it] = ok ? *reinterpret_cast<const u32x4*>(gi + off) : u32x4{0, 0, 0, 0};
+        d0[it] = *reinterpret_cast<const f32x4*>(stg + row * 132 + c8 * 8);
+        d1[it] = *reinterpret_cast<const f32x4*>(stg + row * 132 + c8 * 8 + 4);
+      }
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int row = it * 4 + (lane >> 4), c8 = lane & 15;
+        const int64_t m = mw + j * 32 + row;
+        const int64_t n = nbase + c8 * 8;
+        u32x4 dgv, dev, hv;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float dha = q < 2 ? d0[it][2 * q] : d1[it][2 * q - 4];
+          const float dhb = q < 2 ? d0[it][2 * q + 1] : d1[it][2 * q - 3];
+          const float e0 = lo_bf(ev[it][q]), e1 = hi_bf(ev[it][q]);
+          const float g0 = lo_bf(gv[it][q]), g1 = hi_bf(gv[it][q]);
+          float p0, s0, p1, s1;
+          act_fwd_bwd<false>(args.act, e0, p0, s0);
+          act_fwd_bwd<false>(args.act, e1, p1, s1);
+          hv[q] = pack_bf2(p0 * g0, p1 * g1);
+          dgv[q] = pack_bf2(dha * p0, dhb * p1);
+          dev[q] = pack_bf2(dha * g0 * s0, dhb * g1 * s1);
+        }
+        if (m < M && n < NR) {
+          const int64_t off = (m * ld + n) * 2;
+          *reinterpret_cast<u32x4*>(dgo + off) = dgv;
+          *reinterpret_cast<u32x4*>(deo + off) = dev;
+          *reinterpret_cast<u32x4*>(ho + off) = hv;
         }
       }
-    }
+      wave_sync();
+    });
   }
 }
 

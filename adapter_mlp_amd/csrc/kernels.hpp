@@ -64,6 +64,7 @@ struct GemmArgs {
   int32_t RL, pad2_;
   const void* BLt;
   int64_t ldbl;
+  int64_t lora_vcols;  // rows of BLt
   // EPI_ACT_FWD: e_out, g_out, h_out [M, N] ; EPI_ACT_BWD: e_in, g_in -> dg_out, de_out, h_out
   void* e_out;
   void* g_out;
