@@ -159,8 +159,177 @@ struct Stage {
   int bq8[8];
 };
 
+// Epilogue: each wavefront stages its results (WN output tile columns x 128
+// rows; accumulator block i covers tile columns 32 i.., block j rows 32 j..)
+// through a private LDS region -- the operand buffers are free once the K
+// loop has ended -- so global loads and stores move 16-byte chunks of
+// consecutive columns.  In dual tiles blocks i < NI/2 hold gate columns and
+// blocks i + NI/2 the up columns of the same outputs.
+template <int WN, bool DUAL, int EPI>
+__device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], u32x4* smem, const GemmArgs& args,
+                                               int reg, int64_t mw, int64_t nbase, int64_t NR, int64_t M, int wave,
+                                               int lane) {
+  constexpr int NI = WN / 32;
+  if constexpr (EPI == EPI_STORE) {
+    constexpr int LD = WN + 8;           // bf16 staging [32][WN], padded rows
+    constexpr int CPR = WN / 8;          // 16-byte chunks per row
+    constexpr int RPP = 64 / CPR;        // rows per pass
+    uint16_t* stg = reinterpret_cast<uint16_t*>(smem) + wave * (32 * LD);
+    char* out = static_cast<char*>(args.reg[reg].out);
+    const int64_t ldo = args.reg[reg].ldo;
+    for4([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = i * 32 + 8 * g + 4 * (lane >> 5);
+          u32x2 v;
+          v[0] = pack_bf2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
+          v[1] = pack_bf2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+          *reinterpret_cast<u32x2*>(stg + (lane & 31) * LD + col) = v;
+        }
+      wave_sync();
+#pragma unroll
+      for (int it = 0; it < 32 / RPP; ++it) {
+        const int row = it * RPP + lane / CPR, c8 = lane % CPR;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * LD + c8 * 8);
+        const int64_t m = mw + j * 32 + row;
+        const int64_t n = nbase + c8 * 8;
+        if (m < M && n < NR) *reinterpret_cast<u32x4*>(out + (m * ldo + n) * 2) = v;
+      }
+      wave_sync();
+    });
+  } else if constexpr (EPI == EPI_ACT_FWD) {
+    static_assert(DUAL, "activation forward needs gate/up tiles");
+    constexpr int W2 = WN / 2;           // output columns per wavefront
+    constexpr int LD = W2 + 8;
+    constexpr int ARR = 32 * LD;
+    constexpr int CPR = W2 / 8;
+    constexpr int RPP = 64 / CPR;
+    uint16_t* stg = reinterpret_cast<uint16_t*>(smem) + wave * (3 * ARR);
+    char* eo = static_cast<char*>(args.e_out);
+    char* go = static_cast<char*>(args.g_out);
+    char* ho = static_cast<char*>(args.h_out);
+    const int64_t ld = args.ld_act;
+    for4([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+#pragma unroll
+      for (int i = 0; i < NI / 2; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = i * 32 + 8 * g + 4 * (lane >> 5);
+          u32x2 ev, gv, hv;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            ev[h] = pack_bf2(acc[i][j][4 * g + 2 * h], acc[i][j][4 * g + 2 * h + 1]);
+            gv[h] = pack_bf2(acc[i + NI / 2][j][4 * g + 2 * h], acc[i + NI / 2][j][4 * g + 2 * h + 1]);
+            float p0, p1;
+            act_fwd<false>(args.act, lo_bf(ev[h]), p0);
+            act_fwd<false>(args.act, hi_bf(ev[h]), p1);
+            hv[h] = pack_bf2(p0 * lo_bf(gv[h]), p1 * hi_bf(gv[h]));
+          }
+          const int o = (lane & 31) * LD + col;
+          *reinterpret_cast<u32x2*>(stg + o) = ev;
+          *reinterpret_cast<u32x2*>(stg + ARR + o) = gv;
+          *reinterpret_cast<u32x2*>(stg + 2 * ARR + o) = hv;
+        }
+      wave_sync();
+#pragma unroll
+      for (int it = 0; it < 32 / RPP; ++it) {
+        const int row = it * RPP + lane / CPR, c8 = lane % CPR;
+        const int64_t m = mw + j * 32 + row;
+        const int64_t n = nbase + c8 * 8;
+        if (m < M && n < NR) {
+          const int o = row * LD + c8 * 8;
+          const int64_t off = (m * ld + n) * 2;
+          *reinterpret_cast<u32x4*>(eo + off) = *reinterpret_cast<const u32x4*>(stg + o);
+          *reinterpret_cast<u32x4*>(go + off) = *reinterpret_cast<const u32x4*>(stg + ARR + o);
+          *reinterpret_cast<u32x4*>(ho + off) = *reinterpret_cast<const u32x4*>(stg + 2 * ARR + o);
+        }
+      }
+      wave_sync();
+    });
+  } else {
+    constexpr int LD = WN + 4;           // fp32 staging [32][WN]
+    constexpr int CPR = WN / 8;          // 8-float groups per row
+    constexpr int RPP = 64 / CPR;
+    constexpr int PASSES = 32 / RPP;
+    float* stg = reinterpret_cast<float*>(smem) + wave * (32 * LD);
+    const char* ei = static_cast<const char*>(args.e_in);
+    const char* gi = static_cast<const char*>(args.g_in);
+    char* dgo = static_cast<char*>(args.dg_out);
+    char* deo = static_cast<char*>(args.de_out);
+    char* ho = static_cast<char*>(args.h_out);
+    const int64_t ld = args.ld_act;
+    for4([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = i * 32 + 8 * g + 4 * (lane >> 5);
+          *reinterpret_cast<f32x4*>(stg + (lane & 31) * LD + col) =
+              f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+        }
+      wave_sync();
+      u32x4 ev[PASSES], gv[PASSES];
+      f32x4 d0[PASSES], d1[PASSES];
+#pragma unroll
+      for (int it = 0; it < PASSES; ++it) {
+        const int row = it * RPP + lane / CPR, c8 = lane % CPR;
+        const int64_t m = mw + j * 32 + row;
+        const int64_t n = nbase + c8 * 8;
+        const bool ok = m < M && n < NR;
+        const int64_t off = ok ? (m * ld + n) * 2 : 0;
+        ev[it] = ok ? *reinterpret_cast<const u32x4*>(ei + off) : u32x4{0, 0, 0, 0};
+        gv[it] = ok ? *reinterpret_cast<const u32x4*>(gi + off) : u32x4{0, 0, 0, 0};
+        d0[it] = *reinterpret_cast<const f32x4*>(stg + row * LD + c8 * 8);
+        d1[it] = *reinterpret_cast<const f32x4*>(stg + row * LD + c8 * 8 + 4);
+      }
+#pragma unroll
+      for (int it = 0; it < PASSES; ++it) {
+        const int row = it * RPP + lane / CPR, c8 = lane % CPR;
+        const int64_t m = mw + j * 32 + row;
+        const int64_t n = nbase + c8 * 8;
+        u32x4 dgv, dev, hv;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float dha = q < 2 ? d0[it][2 * q] : d1[it][2 * q - 4];
+          const float dhb = q < 2 ? d0[it][2 * q + 1] : d1[it][2 * q - 3];
+          const float e0 = lo_bf(ev[it][q]), e1 = hi_bf(ev[it][q]);
+          const float g0 = lo_bf(gv[it][q]), g1 = hi_bf(gv[it][q]);
+          float p0, s0, p1, s1;
+          act_fwd_bwd<false>(args.act, e0, p0, s0);
+          act_fwd_bwd<false>(args.act, e1, p1, s1);
+          hv[q] = pack_bf2(p0 * g0, p1 * g1);
+          dgv[q] = pack_bf2(dha * p0, dhb * p1);
+          dev[q] = pack_bf2(dha * g0 * s0, dhb * g1 * s1);
+        }
+        if (m < M && n < NR) {
+          const int64_t off = (m * ld + n) * 2;
+          *reinterpret_cast<u32x4*>(dgo + off) = dgv;
+          *reinterpret_cast<u32x4*>(deo + off) = dev;
+          *reinterpret_cast<u32x4*>(ho + off) = hv;
+        }
+      }
+      wave_sync();
+    });
+  }
+}
+
+template <bool DUAL, int EPI>
+__device__ __forceinline__ void run_epilogue(f32x16 (&acc)[4][4], u32x4* smem, const GemmArgs& args, int reg,
+                                             int64_t m0, int64_t tnl, int64_t NR, int64_t M, int wave, int lane) {
+  const int wm = wave >> 1, wn = wave & 1;
+  run_epilogue_w<128, DUAL, EPI>(acc, smem, args, reg, m0 + wm * 128, colmap<DUAL>(wn * 128, tnl), NR, M, wave,
+                                 lane);
+}
+
+// NF4 weights: the previous loop (register prefetch of one tile, LoRA tile
+// through its own path), kept while the dense kernel is tuned.
 template <int BKIND, bool NF4, bool DUAL, int EPI>
-__global__ __launch_bounds__(NTH, 1) void gemm_bf16_kernel(const GemmArgs args) {
+__global__ __launch_bounds__(NTH, 1) void gemm_nf4_kernel(const GemmArgs args) {
   __shared__ u32x4 smem[4 * TILE_CHUNKS];  // A: 2 buffers, B: 2 buffers; reused by the epilogue
   __shared__ float s_lut[16];
   u32x4* const sA = smem;
@@ -260,7 +429,7 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_kernel(const GemmArgs args) 
         st.bs2[i] = __uint_as_float(bload4(rs, ok ? (int)((flat >> 14) << 2) : OOB));
       }
     } else {
-      const int64_t total = (BKIND == B_NT ? NR : S.K) * B.ld * 2;
+      const int64_t total = BKIND == B_NT ? NR * B.ld * 2 : ((S.K - 1) * B.ld + NR) * 2;
       const int64_t adv = (BKIND == B_NT ? k0 : k0 * B.ld) * 2;
       const rsrc_t rb = rsrc(static_cast<const char*>(B.p) + adv, total - adv);
 #pragma unroll
@@ -393,154 +562,199 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_kernel(const GemmArgs args) 
     __syncthreads();
   }
 
-  // --- epilogue: per-wavefront LDS staging, coalesced global access ----------
-  const int64_t mw = m0 + wm * 128;           // first row of this wavefront
-  const int64_t nbase = colmap<DUAL>(wn * 128, tnl);  // first output column
-  if constexpr (EPI == EPI_STORE) {
-    // bf16 staging [32 rows][128 cols], row stride 136 elements
-    uint16_t* stg = reinterpret_cast<uint16_t*>(smem) + wave * (32 * 136);
-    char* out = static_cast<char*>(args.reg[reg].out);
-    const int64_t ldo = args.reg[reg].ldo;
-    for4([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
+  run_epilogue<DUAL, EPI>(acc, smem, args, reg, m0, tnl, NR, M, wave, lane);
+}
+
+
+// ---------------------------------------------------------------------------
+// Dense weights: 8 wavefronts (2 per SIMD) per 256x256 block tile, each
+// wavefront a 128x64 sub-tile (8 accumulators of 32x32, 128 AGPRs), so one
+// wavefront's LDS or barrier wait is covered by the other's MFMAs on the same
+// SIMD.  Wavefronts 0-3 stage the weight tile, 4-7 the activation tile.  The
+// LoRA term arrives as the last K segment (zero-padded to 64), so every K
+// step runs the same code.
+//
+// Dual (gate/up) tiles: compute wavefront (wm, wn) owns tile columns
+// 64 wn .. 64 wn + 63 = [gate 32 | up 32] of output columns 32 wn .. 32 wn + 31.
+// ---------------------------------------------------------------------------
+constexpr int NTH8 = 512;
+
+template <int BKIND, bool DUAL, int EPI>
+__global__ __launch_bounds__(NTH8, 1) void gemm_dense_kernel(const GemmArgs args) {
+  static_assert(!(DUAL && BKIND == B_NT), "gate/up tiles read forward (NN) weights");
+  __shared__ u32x4 smem[4 * TILE_CHUNKS];
+  u32x4* const sA = smem;
+  u32x4* const sB = smem + 2 * TILE_CHUNKS;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
+  const int wm = wave >> 2, wn = wave & 3;
+
+  int tm, tn;
+  tile_coords((int)blockIdx.x, (int)gridDim.x, (int)args.ntile_m, (int)args.ntile_n, tm, tn);
+  tm = __builtin_amdgcn_readfirstlane(tm);
+  tn = __builtin_amdgcn_readfirstlane(tn);
+  int reg = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+  for (int p = 1; p < 3; ++p)
+    if (p < args.nreg && tn >= args.reg[p].tile0) reg = p;
+  reg = __builtin_amdgcn_readfirstlane(reg);
+  const int64_t tnl = uni64(tn - args.reg[reg].tile0);
+  const int64_t NR = uni64(args.reg[reg].N);
+  const int64_t M = args.M;
+  const int64_t m0 = (int64_t)tm * BM;
+
+  // Loader geometry (256 threads per operand).
+  const bool loads_b = wave < 4;
+  const int ltid = tid & 255;
+  const int a_c = ltid & 7;          // 16-byte chunk of a 64-wide K slice
+  const int a_r0 = ltid >> 3;        // rows a_r0 + 32 i
+  // NN weights, one 8x8 block per lane.  Dual: loader wavefront w holds
+  // column group w & 1 (gate / up) of compute columns 2 (w >> 1) + g.
+  int nn_row0;                       // first LDS weight row of this lane's block
+  int nn_k8;
+  int bcg = 0;
+  uint32_t ncol;                     // first output column of the block
+  if constexpr (DUAL) {
+    const int w = wave & 3, g = lane >> 5, k8 = (lane >> 2) & 7, n8 = lane & 3;
+    const int cwn = 2 * (w >> 1) + g, part = w & 1;
+    nn_row0 = cwn * 64 + part * 32 + n8 * 8;
+    nn_k8 = k8;
+    bcg = __builtin_amdgcn_readfirstlane(part);
+    ncol = (uint32_t)(tnl * 128 + cwn * 32 + n8 * 8);
+  } else {
+    const int w = wave & 3, k8 = lane >> 3, n8 = lane & 7;
+    nn_row0 = w * 64 + n8 * 8;
+    nn_k8 = k8;
+    ncol = (uint32_t)(tnl * 256 + nn_row0);
+  }
+  const uint32_t arow0 = (uint32_t)(m0 + a_r0);
+  const uint32_t brow0 = (uint32_t)(tnl * 256 + a_r0);  // NT weight rows (non-dual)
+
+  int64_t KT = 0;
+  for (int s = 0; s < args.nseg; ++s) KT += args.seg[s].K / BK;
+
+  int pseg = 0;
+  int64_t pk0 = 0;
+  auto advance = [&]() {
+    pk0 += BK;
+    if (pk0 >= args.seg[pseg].K && pseg + 1 < args.nseg) {
+      ++pseg;
+      pk0 = 0;
+    }
+  };
+
+  u32x4 R[8];
+  auto load = [&]() {
+    const GemmSeg& S = args.seg[pseg];
+    if (!loads_b) {
+      const int64_t lda = S.lda;
+      const rsrc_t ra = rsrc(static_cast<const char*>(S.A) + pk0 * 2, M * lda * 2 - pk0 * 2);
+      const uint32_t lda2 = (uint32_t)(lda * 2);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = i * 32 + 8 * g + 4 * (lane >> 5);
-          u32x2 v;
-          v[0] = pack_bf2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
-          v[1] = pack_bf2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-          *reinterpret_cast<u32x2*>(stg + (lane & 31) * 136 + col) = v;
-        }
-      wave_sync();
+      for (int i = 0; i < 8; ++i) R[i] = bload16(ra, (int)((arow0 + 32 * i) * lda2 + a_c * 16));
+    } else {
+      const BSrc& B = S.b[reg][bcg];
+      const int64_t ld = B.ld;
+      const uint32_t ld2 = (uint32_t)(ld * 2);
+      if constexpr (BKIND == B_NT) {
+        const rsrc_t rb = rsrc(static_cast<const char*>(B.p) + pk0 * 2, NR * ld * 2 - pk0 * 2);
 #pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int row = it * 4 + (lane >> 4), c8 = lane & 15;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * 136 + c8 * 8);
-        const int64_t m = mw + j * 32 + row;
-        const int64_t n = nbase + c8 * 8;
-        if (m < M && n < NR) *reinterpret_cast<u32x4*>(out + (m * ldo + n) * 2) = v;
+        for (int i = 0; i < 8; ++i) R[i] = bload16(rb, (int)((brow0 + 32 * i) * ld2 + a_c * 16));
+      } else {
+        const rsrc_t rb = rsrc(static_cast<const char*>(B.p) + pk0 * ld * 2, ((S.K - 1 - pk0) * ld + NR) * 2);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) R[i] = bload16(rb, (int)((uint32_t)(nn_k8 * 8 + i) * ld2 + ncol * 2));
       }
-      wave_sync();
-    });
-  } else if constexpr (EPI == EPI_ACT_FWD) {
-    static_assert(DUAL, "activation forward needs gate/up tiles");
-    // three bf16 arrays [32 rows][64 cols] (e, g, h), row stride 72 elements
-    constexpr int ARR = 32 * 72;
-    uint16_t* stg = reinterpret_cast<uint16_t*>(smem) + wave * (3 * ARR);
-    char* eo = static_cast<char*>(args.e_out);
-    char* go = static_cast<char*>(args.g_out);
-    char* ho = static_cast<char*>(args.h_out);
-    const int64_t ld = args.ld_act;
-    for4([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
+    }
+  };
+
+  auto store = [&](int buf) {
+    if (!loads_b || BKIND == B_NT) {
+      u32x4* d = (loads_b ? sB : sA) + buf * TILE_CHUNKS;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = a_r0 + 32 * i;
+        d[row * 8 + (a_c ^ swz(row))] = R[i];
+      }
+    } else {
+      u32x4* dB = sB + buf * TILE_CHUNKS;
+      u32x4 cols[8];
+      transpose8x8(R, cols);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int row = nn_row0 + j;
+        dB[row * 8 + (nn_k8 ^ swz(row))] = cols[j];
+      }
+    }
+  };
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  auto compute = [&](int buf) {
+    const u32x4* tA = sA + buf * TILE_CHUNKS;
+    const u32x4* tB = sB + buf * TILE_CHUNKS;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int c = ks * 2 + (lane >> 5);
+      bf16x8 fa[2], fb[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int rn = wn * 64 + i * 32 + (lane & 31);
+        fa[i] = __builtin_bit_cast(bf16x8, tB[rn * 8 + (c ^ swz(rn))]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rm = wm * 128 + j * 32 + (lane & 31);
+        fb[j] = __builtin_bit_cast(bf16x8, tA[rm * 8 + (c ^ swz(rm))]);
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = i * 32 + 8 * g + 4 * (lane >> 5);
-          u32x2 ev, gv, hv;
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            ev[h] = pack_bf2(acc[i][j][4 * g + 2 * h], acc[i][j][4 * g + 2 * h + 1]);
-            gv[h] = pack_bf2(acc[i + 2][j][4 * g + 2 * h], acc[i + 2][j][4 * g + 2 * h + 1]);
-            float p0, p1;
-            act_fwd<false>(args.act, lo_bf(ev[h]), p0);
-            act_fwd<false>(args.act, hi_bf(ev[h]), p1);
-            hv[h] = pack_bf2(p0 * lo_bf(gv[h]), p1 * hi_bf(gv[h]));
-          }
-          const int o = (lane & 31) * 72 + col;
-          *reinterpret_cast<u32x2*>(stg + o) = ev;
-          *reinterpret_cast<u32x2*>(stg + ARR + o) = gv;
-          *reinterpret_cast<u32x2*>(stg + 2 * ARR + o) = hv;
-        }
-      wave_sync();
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int row = it * 8 + (lane >> 3), c8 = lane & 7;
-        const int64_t m = mw + j * 32 + row;
-        const int64_t n = nbase + c8 * 8;
-        if (m < M && n < NR) {
-          const int o = row * 72 + c8 * 8;
-          const int64_t off = (m * ld + n) * 2;
-          *reinterpret_cast<u32x4*>(eo + off) = *reinterpret_cast<const u32x4*>(stg + o);
-          *reinterpret_cast<u32x4*>(go + off) = *reinterpret_cast<const u32x4*>(stg + ARR + o);
-          *reinterpret_cast<u32x4*>(ho + off) = *reinterpret_cast<const u32x4*>(stg + 2 * ARR + o);
-        }
-      }
-      wave_sync();
-    });
-  } else {
-    // fp32 staging of dh [32 rows][128 cols], row stride 132 floats
-    float* stg = reinterpret_cast<float*>(smem) + wave * (32 * 132);
-    const char* ei = static_cast<const char*>(args.e_in);
-    const char* gi = static_cast<const char*>(args.g_in);
-    char* dgo = static_cast<char*>(args.dg_out);
-    char* deo = static_cast<char*>(args.de_out);
-    char* ho = static_cast<char*>(args.h_out);
-    const int64_t ld = args.ld_act;
-    for4([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = i * 32 + 8 * g + 4 * (lane >> 5);
-          *reinterpret_cast<f32x4*>(stg + (lane & 31) * 132 + col) =
-              f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-        }
-      wave_sync();
-      u32x4 ev[8], gv[8];
-      f32x4 d0[8], d1[8];
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int row = it * 4 + (lane >> 4), c8 = lane & 15;
-        const int64_t m = mw + j * 32 + row;
-        const int64_t n = nbase + c8 * 8;
-        const bool ok = m < M && n < NR;
-        const int64_t off = ok ? (m * ld + n) * 2 : 0;
-        ev[it] = ok ? *reinterpret_cast<const u32x4*>(ei + off) : u32x4{0, 0, 0, 0};
-        gv[it] = ok ? *reinterpret_cast<const u32x4*>(gi + off) : u32x4{0, 0, 0, 0};
-        d0[it] = *reinterpret_cast<const f32x4*>(stg + row * 132 + c8 * 8);
-        d1[it] = *reinterpret_cast<const f32x4*>(stg + row * 132 + c8 * 8 + 4);
-      }
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int row = it * 4 + (lane >> 4), c8 = lane & 15;
-        const int64_t m = mw + j * 32 + row;
-        const int64_t n = nbase + c8 * 8;
-        u32x4 dgv, dev, hv;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float dha = q < 2 ? d0[it][2 * q] : d1[it][2 * q - 4];
-          const float dhb = q < 2 ? d0[it][2 * q + 1] : d1[it][2 * q - 3];
-          const float e0 = lo_bf(ev[it][q]), e1 = hi_bf(ev[it][q]);
-          const float g0 = lo_bf(gv[it][q]), g1 = hi_bf(gv[it][q]);
-          float p0, s0, p1, s1;
-          act_fwd_bwd<false>(args.act, e0, p0, s0);
-          act_fwd_bwd<false>(args.act, e1, p1, s1);
-          hv[q] = pack_bf2(p0 * g0, p1 * g1);
-          dgv[q] = pack_bf2(dha * p0, dhb * p1);
-          dev[q] = pack_bf2(dha * g0 * s0, dhb * g1 * s1);
-        }
-        if (m < M && n < NR) {
-          const int64_t off = (m * ld + n) * 2;
-          *reinterpret_cast<u32x4*>(dgo + off) = dgv;
-          *reinterpret_cast<u32x4*>(deo + off) = dev;
-          *reinterpret_cast<u32x4*>(ho + off) = hv;
-        }
-      }
-      wave_sync();
-    });
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // --- main loop: tile t+1 loads into registers while tile t computes --------
+  load();
+  store(0);
+  __syncthreads();
+  for (int64_t t = 0; t < KT; ++t) {
+    const int buf = (int)(t & 1);
+    const bool has_next = t + 1 < KT;
+    if (has_next) {
+      advance();
+      load();
+    }
+    compute(buf);
+    if (has_next) store(buf ^ 1);
+    __syncthreads();
   }
+
+  const int64_t mw = m0 + wm * 128;
+  const int64_t nbase = DUAL ? tnl * 128 + wn * 32 : tnl * 256 + wn * 64;
+  run_epilogue_w<64, DUAL, EPI>(acc, smem, args, reg, mw, nbase, NR, M, wave, lane);
+}
+
+template <int BKIND, bool DUAL, int EPI>
+hipError_t launch_dense(const GemmArgs& a, hipStream_t st) {
+  const int64_t nb = a.ntile_m * a.ntile_n;
+  if (nb == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_dense_kernel<BKIND, DUAL, EPI>), dim3((unsigned)nb), dim3(NTH8), 0, st, a);
+  return hipGetLastError();
 }
 
 template <int BKIND, bool NF4, bool DUAL, int EPI>
 hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
   const int64_t nb = a.ntile_m * a.ntile_n;
   if (nb == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BKIND, NF4, DUAL, EPI>), dim3((unsigned)nb), dim3(NTH), 0, st, a);
+  hipLaunchKernelGGL((gemm_nf4_kernel<BKIND, NF4, DUAL, EPI>), dim3((unsigned)nb), dim3(NTH), 0, st, a);
   return hipGetLastError();
 }
 
@@ -553,21 +767,18 @@ int64_t gemm_tile_cols(bool bf16, bool dual) {
 int64_t gemm_tile_rows(bool bf16) { return bf16 ? 256 : 64; }
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
-  const bool nf4 = a.nf4 != 0;
-  if (a.bkind == B_NN) {
-    if (a.epi == EPI_ACT_FWD) {
-      return nf4 ? launch_t<B_NN, true, true, EPI_ACT_FWD>(a, st)
-                 : launch_t<B_NN, false, true, EPI_ACT_FWD>(a, st);
-    }
-    return nf4 ? launch_t<B_NN, true, false, EPI_STORE>(a, st)
-               : launch_t<B_NN, false, false, EPI_STORE>(a, st);
+  if (a.nf4) {
+    if (a.bkind == B_NN)
+      return a.epi == EPI_ACT_FWD ? launch_t<B_NN, true, true, EPI_ACT_FWD>(a, st)
+                                  : launch_t<B_NN, true, false, EPI_STORE>(a, st);
+    return a.epi == EPI_ACT_BWD ? launch_t<B_NT, true, false, EPI_ACT_BWD>(a, st)
+                                : launch_t<B_NT, true, false, EPI_STORE>(a, st);
   }
-  if (a.epi == EPI_ACT_BWD) {
-    return nf4 ? launch_t<B_NT, true, false, EPI_ACT_BWD>(a, st)
-               : launch_t<B_NT, false, false, EPI_ACT_BWD>(a, st);
-  }
-  return nf4 ? launch_t<B_NT, true, false, EPI_STORE>(a, st)
-             : launch_t<B_NT, false, false, EPI_STORE>(a, st);
+  if (a.bkind == B_NN)
+    return a.epi == EPI_ACT_FWD ? launch_dense<B_NN, true, EPI_ACT_FWD>(a, st)
+                                : launch_dense<B_NN, false, EPI_STORE>(a, st);
+  return a.epi == EPI_ACT_BWD ? launch_dense<B_NT, false, EPI_ACT_BWD>(a, st)
+                              : launch_dense<B_NT, false, EPI_STORE>(a, st);
 }
 
 }  // namespace lora

@@ -56,7 +56,7 @@ struct GemmArgs {
   int64_t M;
   int32_t nseg, nreg;
   int32_t dual, epi, act, nf4, bkind, pad_;
-  GemmSeg seg[3];
+  GemmSeg seg[4];  // up to 3 main segments + the LoRA tail as a segment
   GemmRegion reg[3];
   int64_t ntile_m, ntile_n;
   const void* AL;  // LoRA tail (nullptr / RL == 0: none)
@@ -126,9 +126,11 @@ int colproj_nchunk(int64_t T, int64_t K);
 // Small packing kernels (adapter operands in the layout the kernels read).
 // pack_cat_t:  out[j, k] = src_q[k, j - q*w] for j < nparts*w, 0 for j < Rpad
 //              (A_p [K, w] of several adapters -> one K-contiguous [Rpad, K]).
-// pack_lora_b: builds BLt [vcols, RL]: for part descriptors (v0, nv, k0, w, src,
-//              ld, nn): BLt[v0 + n, k0 + i] = nn ? src[i*ld + n] : src[n*ld + i]
-//              for n < nv, i < w; everything else 0.
+// pack_lora_b: builds the adapter operand of the GEMM's LoRA K tile over vcols
+//              virtual columns and RL rows of K: for part descriptors (v0, nv,
+//              k0, w, src, ld, nn), value(v0 + n, k0 + i) = nn ? src[i*ld + n]
+//              : src[n*ld + i] for n < nv, i < w, everything else 0; stored
+//              [vcols, RL] (K-contiguous) or, with kmajor, [RL, vcols].
 // ---------------------------------------------------------------------------
 struct PackPart {
   const void* src;
@@ -140,6 +142,7 @@ struct PackLoraArgs {
   void* out;
   int64_t vcols;
   int32_t RL, nparts;
+  int32_t kmajor, pad_;
   PackPart part[6];
 };
 hipError_t launch_pack_lora_b(bool bf16, const PackLoraArgs& a, hipStream_t st);

@@ -240,7 +240,8 @@ __global__ void pack_lora_b_kernel(const PackLoraArgs a) {
       val = q.nn ? src[i * q.ld + n] : src[n * q.ld + i];
     }
   }
-  static_cast<E*>(a.out)[e] = val;
+  const int64_t o = a.kmajor ? (int64_t)kk * a.vcols + v : e;
+  static_cast<E*>(a.out)[o] = val;
 }
 
 struct CatSrcs {
