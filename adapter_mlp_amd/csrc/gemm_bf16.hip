@@ -165,16 +165,22 @@ struct Stage {
 // loop has ended -- so global loads and stores move 16-byte chunks of
 // consecutive columns.  In dual tiles blocks i < NI/2 hold gate columns and
 // blocks i + NI/2 the up columns of the same outputs.
+// Staging bytes one wavefront needs for a WN-column epilogue.
+template <int WN, int EPI>
+constexpr int epi_stage_bytes() {
+  return EPI == EPI_STORE ? 32 * (WN + 8) * 2 : EPI == EPI_ACT_FWD ? 3 * 32 * (WN / 2 + 8) * 2 : 32 * (WN + 4) * 4;
+}
+
 template <int WN, bool DUAL, int EPI>
-__device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], u32x4* smem, const GemmArgs& args,
-                                               int reg, int64_t mw, int64_t nbase, int64_t NR, int64_t M, int wave,
+__device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* wstage, const GemmArgs& args,
+                                               int reg, int64_t mw, int64_t nbase, int64_t NR, int64_t M,
                                                int lane) {
   constexpr int NI = WN / 32;
   if constexpr (EPI == EPI_STORE) {
     constexpr int LD = WN + 8;           // bf16 staging [32][WN], padded rows
     constexpr int CPR = WN / 8;          // 16-byte chunks per row
     constexpr int RPP = 64 / CPR;        // rows per pass
-    uint16_t* stg = reinterpret_cast<uint16_t*>(smem) + wave * (32 * LD);
+    uint16_t* stg = reinterpret_cast<uint16_t*>(wstage);
     char* out = static_cast<char*>(args.reg[reg].out);
     const int64_t ldo = args.reg[reg].ldo;
     for4([&](auto jc) {
@@ -207,7 +213,7 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], u32x4*
     constexpr int ARR = 32 * LD;
     constexpr int CPR = W2 / 8;
     constexpr int RPP = 64 / CPR;
-    uint16_t* stg = reinterpret_cast<uint16_t*>(smem) + wave * (3 * ARR);
+    uint16_t* stg = reinterpret_cast<uint16_t*>(wstage);
     char* eo = static_cast<char*>(args.e_out);
     char* go = static_cast<char*>(args.g_out);
     char* ho = static_cast<char*>(args.h_out);
@@ -255,7 +261,7 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], u32x4*
     constexpr int CPR = WN / 8;          // 8-float groups per row
     constexpr int RPP = 64 / CPR;
     constexpr int PASSES = 32 / RPP;
-    float* stg = reinterpret_cast<float*>(smem) + wave * (32 * LD);
+    float* stg = reinterpret_cast<float*>(wstage);
     const char* ei = static_cast<const char*>(args.e_in);
     const char* gi = static_cast<const char*>(args.g_in);
     char* dgo = static_cast<char*>(args.dg_out);
@@ -322,8 +328,8 @@ template <bool DUAL, int EPI>
 __device__ __forceinline__ void run_epilogue(f32x16 (&acc)[4][4], u32x4* smem, const GemmArgs& args, int reg,
                                              int64_t m0, int64_t tnl, int64_t NR, int64_t M, int wave, int lane) {
   const int wm = wave >> 1, wn = wave & 1;
-  run_epilogue_w<128, DUAL, EPI>(acc, smem, args, reg, m0 + wm * 128, colmap<DUAL>(wn * 128, tnl), NR, M, wave,
-                                 lane);
+  char* wstage = reinterpret_cast<char*>(smem) + wave * epi_stage_bytes<128, EPI>();
+  run_epilogue_w<128, DUAL, EPI>(acc, wstage, args, reg, m0 + wm * 128, colmap<DUAL>(wn * 128, tnl), NR, M, lane);
 }
 
 // NF4 weights: the previous loop (register prefetch of one tile, LoRA tile
@@ -567,24 +573,69 @@ __global__ __launch_bounds__(NTH, 1) void gemm_nf4_kernel(const GemmArgs args) {
 
 
 // ---------------------------------------------------------------------------
-// Dense weights: 8 wavefronts (2 per SIMD) per 256x256 block tile, each
-// wavefront a 128x64 sub-tile (8 accumulators of 32x32, 128 AGPRs), so one
-// wavefront's LDS or barrier wait is covered by the other's MFMAs on the same
-// SIMD.  Wavefronts 0-3 stage the weight tile, 4-7 the activation tile.  The
-// LoRA term arrives as the last K segment (zero-padded to 64), so every K
-// step runs the same code.
+// Dense weights: operands go from global memory straight into LDS
+// (buffer_load_dwordx4 ... lds: lane i of a load writes bytes 16 i .. 16 i + 15
+// of a 1 KB LDS block whose base is in M0), so no registers or LDS-write
+// instructions are spent on staging and the next K tile streams in while the
+// current one is multiplied.  8 wavefronts (2 per SIMD), each a 128x64
+// sub-tile: 8 accumulators of 32x32 and 128 registers of results.
 //
-// Dual (gate/up) tiles: compute wavefront (wm, wn) owns tile columns
-// 64 wn .. 64 wn + 63 = [gate 32 | up 32] of output columns 32 wn .. 32 wn + 31.
+// LDS per stage (two stages, 64 KB each):
+//   activation tile: 256 rows x 64 K, 128-byte rows, 16-byte chunks XOR-swizzled
+//                    by swz(row); read with ds_read_b128;
+//   weights, NT:     the same layout over 256 output columns;
+//   weights, NN:     two halves of [64 K][128 N] (256-byte rows; for gate/up
+//                    tiles half 0 holds gate and half 1 up columns), chunk c
+//                    of row k stored at c ^ 4 (k & 3); fragments are read
+//                    with ds_read_b64_tr_b16, which hands lane 16 g + i the
+//                    4 values of column i that lanes 16 g + 4 j + i / 4 point
+//                    at (j = 0..3), i.e. the K-contiguous MFMA operand.
 // ---------------------------------------------------------------------------
 constexpr int NTH8 = 512;
+constexpr int STAGE_BYTES = 65536;
+constexpr int B_OFF = 32768;
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor as four scalar words (base, stride 0, byte size, format)
+// for the inline-assembly load below; every input is uniform.
+__device__ __forceinline__ i32x4 rsrc_words(const void* p, int64_t bytes) {
+  if (bytes < 0) bytes = 0;
+  const uint64_t base = (uint64_t)uni64(reinterpret_cast<int64_t>(p));
+  const int n = __builtin_amdgcn_readfirstlane((int)bytes);
+  return i32x4{(int)(uint32_t)base, (int)((base >> 32) & 0xffff), n, 0x00020000};
+}
+
+// 16 bytes per lane from global memory into LDS: lane i writes bytes
+// lds_addr + 16 i .. + 15; offsets past the descriptor's size read zero.
+// Issued as inline assembly so that the compiler does not wait for these
+// loads before unrelated LDS reads (it cannot tell the stages apart); the
+// kernel waits with vmcnt(0) and a barrier before it reads the stage.
+__device__ __forceinline__ void dma16(const i32x4& r, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(lds_addr)
+               : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const lds_char* p) { return (uint32_t)(uintptr_t)p; }
+__device__ __forceinline__ u32x4 lds_read16(const lds_char* p) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(p);
+}
+__device__ __forceinline__ uint64_t lds_read_tr(const lds_char* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(uint64_t, v);
+}
 
 template <int BKIND, bool DUAL, int EPI>
 __global__ __launch_bounds__(NTH8, 1) void gemm_dense_kernel(const GemmArgs args) {
   static_assert(!(DUAL && BKIND == B_NT), "gate/up tiles read forward (NN) weights");
-  __shared__ u32x4 smem[4 * TILE_CHUNKS];
-  u32x4* const sA = smem;
-  u32x4* const sB = smem + 2 * TILE_CHUNKS;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * STAGE_BYTES];
+  lds_char* const lds = (lds_char*)smem_raw;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -605,90 +656,82 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_dense_kernel(const GemmArgs args
   const int64_t M = args.M;
   const int64_t m0 = (int64_t)tm * BM;
 
-  // Loader geometry (256 threads per operand).
-  const bool loads_b = wave < 4;
-  const int ltid = tid & 255;
-  const int a_c = ltid & 7;          // 16-byte chunk of a 64-wide K slice
-  const int a_r0 = ltid >> 3;        // rows a_r0 + 32 i
-  // NN weights, one 8x8 block per lane.  Dual: loader wavefront w holds
-  // column group w & 1 (gate / up) of compute columns 2 (w >> 1) + g.
-  int nn_row0;                       // first LDS weight row of this lane's block
-  int nn_k8;
-  int bcg = 0;
-  uint32_t ncol;                     // first output column of the block
-  if constexpr (DUAL) {
-    const int w = wave & 3, g = lane >> 5, k8 = (lane >> 2) & 7, n8 = lane & 3;
-    const int cwn = 2 * (w >> 1) + g, part = w & 1;
-    nn_row0 = cwn * 64 + part * 32 + n8 * 8;
-    nn_k8 = k8;
-    bcg = __builtin_amdgcn_readfirstlane(part);
-    ncol = (uint32_t)(tnl * 128 + cwn * 32 + n8 * 8);
-  } else {
-    const int w = wave & 3, k8 = lane >> 3, n8 = lane & 7;
-    nn_row0 = w * 64 + n8 * 8;
-    nn_k8 = k8;
-    ncol = (uint32_t)(tnl * 256 + nn_row0);
-  }
-  const uint32_t arow0 = (uint32_t)(m0 + a_r0);
-  const uint32_t brow0 = (uint32_t)(tnl * 256 + a_r0);  // NT weight rows (non-dual)
-
   int64_t KT = 0;
   for (int s = 0; s < args.nseg; ++s) KT += args.seg[s].K / BK;
 
-  int pseg = 0;
-  int64_t pk0 = 0;
-  auto advance = [&]() {
-    pk0 += BK;
-    if (pk0 >= args.seg[pseg].K && pseg + 1 < args.nseg) {
-      ++pseg;
-      pk0 = 0;
-    }
-  };
-
-  u32x4 R[8];
-  auto load = [&]() {
-    const GemmSeg& S = args.seg[pseg];
-    if (!loads_b) {
+  // ---- loads: every wavefront issues 4 activation and 4 weight 1 KB blocks ----
+  // activation / NT-weight block q: rows 8 q .. 8 q + 7 of the tile
+  const int krow_a = lane >> 3;                 // row inside the block
+  const int bhalf = wave >> 2;                  // NN weight half loaded by this wavefront
+  // NN block q' (0..15) of a half: K rows 4 q' .. 4 q' + 3, 16 chunks each
+  const int nn_kr = lane >> 4;
+  const int nn_c = (lane & 15) ^ (4 * (nn_kr & 3));
+  auto issue = [&](int seg, int64_t pk0, int st) {
+    const GemmSeg& S = args.seg[seg];
+    const uint32_t stage = lds_addr(lds) + st * STAGE_BYTES;
+    {
       const int64_t lda = S.lda;
-      const rsrc_t ra = rsrc(static_cast<const char*>(S.A) + pk0 * 2, M * lda * 2 - pk0 * 2);
-      const uint32_t lda2 = (uint32_t)(lda * 2);
+      const i32x4 ra = rsrc_words(static_cast<const char*>(S.A) + (m0 * lda + pk0) * 2, (M - m0) * lda * 2 - pk0 * 2);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) R[i] = bload16(ra, (int)((arow0 + 32 * i) * lda2 + a_c * 16));
-    } else {
-      const BSrc& B = S.b[reg][bcg];
+      for (int i = 0; i < 4; ++i) {
+        const int q = wave * 4 + i;
+        const int row = 8 * q + krow_a;
+        const uint32_t off = (uint32_t)row * (uint32_t)(lda * 2) + (uint32_t)(((lane & 7) ^ swz(row)) * 16);
+        dma16(ra, off, stage + q * 1024);
+      }
+    }
+    if constexpr (BKIND == B_NT) {
+      const BSrc& B = S.b[reg][0];
       const int64_t ld = B.ld;
-      const uint32_t ld2 = (uint32_t)(ld * 2);
-      if constexpr (BKIND == B_NT) {
-        const rsrc_t rb = rsrc(static_cast<const char*>(B.p) + pk0 * 2, NR * ld * 2 - pk0 * 2);
+      const i32x4 rb = rsrc_words(static_cast<const char*>(B.p) + (tnl * 256 * ld + pk0) * 2,
+                             (NR - tnl * 256) * ld * 2 - pk0 * 2);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) R[i] = bload16(rb, (int)((brow0 + 32 * i) * ld2 + a_c * 16));
-      } else {
-        const rsrc_t rb = rsrc(static_cast<const char*>(B.p) + pk0 * ld * 2, ((S.K - 1 - pk0) * ld + NR) * 2);
+      for (int i = 0; i < 4; ++i) {
+        const int q = wave * 4 + i;
+        const int row = 8 * q + krow_a;
+        const uint32_t off = (uint32_t)row * (uint32_t)(ld * 2) + (uint32_t)(((lane & 7) ^ swz(row)) * 16);
+        dma16(rb, off, stage + B_OFF + q * 1024);
+      }
+    } else {
+      const BSrc& B = S.b[reg][DUAL ? bhalf : 0];
+      const int64_t ld = B.ld;
+      const int64_t ncol0 = DUAL ? tnl * 128 : tnl * 256 + bhalf * 128;
+      const i32x4 rb = rsrc_words(static_cast<const char*>(B.p) + (pk0 * ld + ncol0) * 2,
+                             ((S.K - 1 - pk0) * ld + NR - ncol0) * 2);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) R[i] = bload16(rb, (int)((uint32_t)(nn_k8 * 8 + i) * ld2 + ncol * 2));
+      for (int i = 0; i < 4; ++i) {
+        const int qh = (wave & 3) * 4 + i;  // block inside the half
+        const int kr = 4 * qh + nn_kr;
+        const uint32_t off = (uint32_t)kr * (uint32_t)(ld * 2) + (uint32_t)(nn_c * 16);
+        dma16(rb, off, stage + B_OFF + bhalf * 16384 + qh * 1024);
       }
     }
   };
 
-  auto store = [&](int buf) {
-    if (!loads_b || BKIND == B_NT) {
-      u32x4* d = (loads_b ? sB : sA) + buf * TILE_CHUNKS;
+  // ---- fragment addresses (bytes inside a stage) ----
+  // activation rows wm*128 + 32 j + lane%32, chunk 2 ks + lane/32
+  // NN weights: lane s of read h (0, 1) of K slice ks points at K row
+  //   16 ks + 8 (g >> 1) + 4 h + (s & 15) / 4 and columns nb + 16 (g & 1) + 4 (s & 3), g = s / 16
+  int nn_lane = 0;
+  int nn_half[2], nn_nb[2];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = a_r0 + 32 * i;
-        d[row * 8 + (a_c ^ swz(row))] = R[i];
-      }
-    } else {
-      u32x4* dB = sB + buf * TILE_CHUNKS;
-      u32x4 cols[8];
-      transpose8x8(R, cols);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int row = nn_row0 + j;
-        dB[row * 8 + (nn_k8 ^ swz(row))] = cols[j];
-      }
-    }
+  for (int i = 0; i < 2; ++i) {
+    nn_half[i] = DUAL ? i : (wn >> 1);
+    nn_nb[i] = DUAL ? wn * 32 : (wn & 1) * 64 + 32 * i;
+  }
+  {
+    const int g = lane >> 4, s15 = lane & 15;
+    nn_lane = (8 * (g >> 1) + (s15 >> 2)) * 256 + (lane & 1) * 8;
+  }
+  auto nn_addr = [&](int i) -> int {  // without the 16 ks + 4 h row term
+    const int g = lane >> 4;
+    const int n = nn_nb[i] + 16 * (g & 1) + 4 * (lane & 3);
+    const int kr = ((lane & 15) >> 2);  // K row & 3 of every read of this lane
+    return B_OFF + nn_half[i] * 16384 + nn_lane + (((n >> 3) ^ (4 * kr)) * 16);
   };
+  int fa_nn[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) fa_nn[i] = nn_addr(i);
 
   f32x16 acc[2][4];
 #pragma unroll
@@ -696,22 +739,32 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_dense_kernel(const GemmArgs args
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-  auto compute = [&](int buf) {
-    const u32x4* tA = sA + buf * TILE_CHUNKS;
-    const u32x4* tB = sB + buf * TILE_CHUNKS;
+  auto compute = [&](int st) {
+    const lds_char* const stage = lds + st * STAGE_BYTES;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int c = ks * 2 + (lane >> 5);
       bf16x8 fa[2], fb[4];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int rn = wn * 64 + i * 32 + (lane & 31);
-        fa[i] = __builtin_bit_cast(bf16x8, tB[rn * 8 + (c ^ swz(rn))]);
+        if constexpr (BKIND == B_NN) {
+          const lds_char* p = stage + fa_nn[i] + (16 * ks) * 256;
+          const uint64_t lo = lds_read_tr(p);
+          const uint64_t hi = lds_read_tr(p + 4 * 256);
+          u32x4 v;
+          v[0] = (uint32_t)lo;
+          v[1] = (uint32_t)(lo >> 32);
+          v[2] = (uint32_t)hi;
+          v[3] = (uint32_t)(hi >> 32);
+          fa[i] = __builtin_bit_cast(bf16x8, v);
+        } else {
+          const int rn = wn * 64 + i * 32 + (lane & 31);
+          fa[i] = __builtin_bit_cast(bf16x8, lds_read16(stage + B_OFF + rn * 128 + (((2 * ks + (lane >> 5)) ^ swz(rn)) * 16)));
+        }
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int rm = wm * 128 + j * 32 + (lane & 31);
-        fb[j] = __builtin_bit_cast(bf16x8, tA[rm * 8 + (c ^ swz(rm))]);
+        fb[j] = __builtin_bit_cast(bf16x8, lds_read16(stage + rm * 128 + (((2 * ks + (lane >> 5)) ^ swz(rm)) * 16)));
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -721,25 +774,32 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_dense_kernel(const GemmArgs args
     }
   };
 
-  // --- main loop: tile t+1 loads into registers while tile t computes --------
-  load();
-  store(0);
-  __syncthreads();
+  // ---- main loop: K tile t + 1 streams into the other stage during tile t ----
+  int seg = 0;
+  int64_t k0 = 0;
+  issue(0, 0, 0);
   for (int64_t t = 0; t < KT; ++t) {
-    const int buf = (int)(t & 1);
-    const bool has_next = t + 1 < KT;
-    if (has_next) {
-      advance();
-      load();
+    __builtin_amdgcn_s_waitcnt(0x0070 | 0x3f00);  // vmcnt(0): this wavefront's blocks of tile t are in LDS
+    __syncthreads();                                // everyone's are; stage (t+1)&1 is no longer read
+    if (t + 1 < KT) {
+      k0 += BK;
+      if (k0 >= args.seg[seg].K) {
+        ++seg;
+        k0 = 0;
+      }
+      issue(seg, k0, (int)((t + 1) & 1));
     }
-    compute(buf);
-    if (has_next) store(buf ^ 1);
-    __syncthreads();
+    compute((int)(t & 1));
   }
+  __syncthreads();
 
+  // epilogue staging: a private region per wavefront
+  constexpr int EB = epi_stage_bytes<64, EPI>();
+  static_assert(8 * EB <= 2 * STAGE_BYTES, "epilogue staging exceeds LDS");
+  char* const wstage = smem_raw + wave * EB;
   const int64_t mw = m0 + wm * 128;
   const int64_t nbase = DUAL ? tnl * 128 + wn * 32 : tnl * 256 + wn * 64;
-  run_epilogue_w<64, DUAL, EPI>(acc, smem, args, reg, mw, nbase, NR, M, wave, lane);
+  run_epilogue_w<64, DUAL, EPI>(acc, wstage, args, reg, mw, nbase, NR, M, lane);
 }
 
 template <int BKIND, bool DUAL, int EPI>

@@ -205,6 +205,9 @@ def main():
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the timed steps, run a plain fp32 elementwise copy (negation) of MIB MiB "
+                         "three times, the known-size kernel that scales HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the fused LoRA path runs on a single MI355X here and "
@@ -262,6 +265,17 @@ def main():
     traffic = read_traffic(dominant, workload_tag)
     log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step ({wall / args.steps * 1e3:.3f} ms wall), "
         f"{tokens_s:,.0f} tokens/s, {tflops:.1f} TFLOP/s; {dominant}: {avg_ms:.3f} ms/launch")
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, device="cuda", dtype=torch.float32)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 3 x neg over {args.copy_calibration} MiB fp32 "
+            f"(reads {n * 4} B, writes {n * 4} B per launch)")
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
