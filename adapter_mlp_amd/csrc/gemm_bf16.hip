@@ -573,16 +573,21 @@ __global__ __launch_bounds__(NTH, 1) void gemm_nf4_kernel(const GemmArgs args) {
 
 
 // ---------------------------------------------------------------------------
-// Dense weights: operands go from global memory straight into LDS
-// (buffer_load_dwordx4 ... lds: lane i of a load writes bytes 16 i .. 16 i + 15
-// of a 1 KB LDS block whose base is in M0), so no registers or LDS-write
-// instructions are spent on staging and the next K tile streams in while the
-// current one is multiplied.  8 wavefronts (2 per SIMD), each a 128x64
-// sub-tile: 8 accumulators of 32x32 and 128 registers of results.
+// Dense weights.  8 wavefronts in two groups of 4, one wavefront of each
+// group on every SIMD, working in alternating phases separated by barriers:
+// while group 0 runs a cluster of 32 MFMAs on fragments already in its
+// registers, group 1 reads the fragments of its next cluster from LDS, and
+// then the roles swap -- the SIMD's matrix unit always has one wavefront
+// feeding it and LDS latency never sits between two MFMAs.  Each wavefront
+// owns a 128x64 sub-tile (8 accumulators of 32x32); group g covers tile rows
+// 128 g .. 128 g + 127.
 //
-// LDS per stage (two stages, 64 KB each):
-//   activation tile: 256 rows x 64 K, 128-byte rows, 16-byte chunks XOR-swizzled
-//                    by swz(row); read with ds_read_b128;
+// Operands go from global memory straight into LDS (buffer_load_dwordx4 ...
+// lds: lane i of a load writes bytes 16 i .. 16 i + 15 of a 1 KB LDS block
+// whose base is in M0), issued by group 0 two K steps ahead into a 2-stage
+// ring of 64 KB stages:
+//   activation tile: 256 rows x 64 K, 128-byte rows, 16-byte chunk c of row r
+//                    stored at c ^ swz(r); read with ds_read_b128;
 //   weights, NT:     the same layout over 256 output columns;
 //   weights, NN:     two halves of [64 K][128 N] (256-byte rows; for gate/up
 //                    tiles half 0 holds gate and half 1 up columns), chunk c
@@ -594,9 +599,9 @@ __global__ __launch_bounds__(NTH, 1) void gemm_nf4_kernel(const GemmArgs args) {
 constexpr int NTH8 = 512;
 constexpr int STAGE_BYTES = 65536;
 constexpr int B_OFF = 32768;
+constexpr int HALF_BYTES = 16384;
 
 typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -640,7 +645,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_dense_kernel(const GemmArgs args
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave >> 2, wn = wave & 3;                    // wm: the group
 
   int tm, tn;
   tile_coords((int)blockIdx.x, (int)gridDim.x, (int)args.ntile_m, (int)args.ntile_n, tm, tn);
@@ -656,94 +661,100 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_dense_kernel(const GemmArgs args
   const int64_t M = args.M;
   const int64_t m0 = (int64_t)tm * BM;
 
-  int64_t KT = 0;
-  for (int s = 0; s < args.nseg; ++s) KT += args.seg[s].K / BK;
+  int KT = 0;
+  for (int s = 0; s < args.nseg; ++s) KT += (int)(args.seg[s].K / BK);
 
-  // ---- loads: every wavefront issues 4 activation and 4 weight 1 KB blocks ----
-  // activation / NT-weight block q: rows 8 q .. 8 q + 7 of the tile
-  const int krow_a = lane >> 3;                 // row inside the block
-  const int bhalf = wave >> 2;                  // NN weight half loaded by this wavefront
-  // NN block q' (0..15) of a half: K rows 4 q' .. 4 q' + 3, 16 chunks each
-  const int nn_kr = lane >> 4;
-  const int nn_c = (lane & 15) ^ (4 * (nn_kr & 3));
-  auto issue = [&](int seg, int64_t pk0, int st) {
-    const GemmSeg& S = args.seg[seg];
+  // ---- loads (group 0): per K step each of its wavefronts issues 8
+  // activation and 8 weight 1 KB blocks ----
+  // K-contiguous block q = 8 wn + i holds rows 8 q + lane / 8; its row r has
+  // swz(r) = (lane / 8) ^ i, so lane takes logical chunk (lane % 8) ^ (lane / 8) ^ i.
+  // NN block q' = 8 (wn & 1) + i of half wn >> 1 holds K rows 4 q' + lane / 16,
+  // lane takes logical chunk (lane % 16) ^ 4 (lane / 16).
+  const int kc_row = wn * 64 + (lane >> 3);
+  const int kc_x = (lane & 7) ^ (lane >> 3);
+  const int nn_row = (wn & 1) * 32 + (lane >> 4);
+  const int nn_chunk = (lane & 15) ^ (4 * ((lane >> 4) & 3));
+  int lseg = 0;
+  int64_t lk0 = 0;
+  auto issue = [&](int st) {
+    const GemmSeg& S = args.seg[lseg];
     const uint32_t stage = lds_addr(lds) + st * STAGE_BYTES;
+    // opaque copies: keep the per-lane terms from being expanded per block
+    // and hoisted out of the K loop (16 live offsets would not fit)
+    int x = kc_x, r = kc_row;
+    asm volatile("" : "+v"(x), "+v"(r));
     {
-      const int64_t lda = S.lda;
-      const i32x4 ra = rsrc_words(static_cast<const char*>(S.A) + (m0 * lda + pk0) * 2, (M - m0) * lda * 2 - pk0 * 2);
+      const uint32_t lda2 = (uint32_t)(S.lda * 2);
+      const i32x4 ra = rsrc_words(static_cast<const char*>(S.A) + (m0 * S.lda + lk0) * 2,
+                                  (M - m0) * S.lda * 2 - lk0 * 2);
+      const uint32_t base = (uint32_t)r * lda2;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int q = wave * 4 + i;
-        const int row = 8 * q + krow_a;
-        const uint32_t off = (uint32_t)row * (uint32_t)(lda * 2) + (uint32_t)(((lane & 7) ^ swz(row)) * 16);
-        dma16(ra, off, stage + q * 1024);
-      }
+      for (int i = 0; i < 8; ++i)
+        dma16(ra, base + (uint32_t)(8 * i) * lda2 + (uint32_t)((x ^ i) << 4), stage + (wn * 8 + i) * 1024);
     }
     if constexpr (BKIND == B_NT) {
       const BSrc& B = S.b[reg][0];
-      const int64_t ld = B.ld;
-      const i32x4 rb = rsrc_words(static_cast<const char*>(B.p) + (tnl * 256 * ld + pk0) * 2,
-                             (NR - tnl * 256) * ld * 2 - pk0 * 2);
+      const uint32_t ld2 = (uint32_t)(B.ld * 2);
+      const i32x4 rb = rsrc_words(static_cast<const char*>(B.p) + (tnl * 256 * B.ld + lk0) * 2,
+                                  (NR - tnl * 256) * B.ld * 2 - lk0 * 2);
+      const uint32_t base = (uint32_t)r * ld2;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int q = wave * 4 + i;
-        const int row = 8 * q + krow_a;
-        const uint32_t off = (uint32_t)row * (uint32_t)(ld * 2) + (uint32_t)(((lane & 7) ^ swz(row)) * 16);
-        dma16(rb, off, stage + B_OFF + q * 1024);
-      }
+      for (int i = 0; i < 8; ++i)
+        dma16(rb, base + (uint32_t)(8 * i) * ld2 + (uint32_t)((x ^ i) << 4), stage + B_OFF + (wn * 8 + i) * 1024);
     } else {
-      const BSrc& B = S.b[reg][DUAL ? bhalf : 0];
-      const int64_t ld = B.ld;
-      const int64_t ncol0 = DUAL ? tnl * 128 : tnl * 256 + bhalf * 128;
-      const i32x4 rb = rsrc_words(static_cast<const char*>(B.p) + (pk0 * ld + ncol0) * 2,
-                             ((S.K - 1 - pk0) * ld + NR - ncol0) * 2);
+      const int half = wn >> 1;
+      const BSrc& B = S.b[reg][DUAL ? half : 0];
+      const uint32_t ld2 = (uint32_t)(B.ld * 2);
+      const int64_t ncol0 = DUAL ? tnl * 128 : tnl * 256 + half * 128;
+      const i32x4 rb = rsrc_words(static_cast<const char*>(B.p) + (lk0 * B.ld + ncol0) * 2,
+                                  ((S.K - 1 - lk0) * B.ld + NR - ncol0) * 2);
+      int nr = nn_row, nc = nn_chunk;
+      asm volatile("" : "+v"(nr), "+v"(nc));
+      const uint32_t base = (uint32_t)nr * ld2 + (uint32_t)(nc << 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int qh = (wave & 3) * 4 + i;  // block inside the half
-        const int kr = 4 * qh + nn_kr;
-        const uint32_t off = (uint32_t)kr * (uint32_t)(ld * 2) + (uint32_t)(nn_c * 16);
-        dma16(rb, off, stage + B_OFF + bhalf * 16384 + qh * 1024);
-      }
+      for (int i = 0; i < 8; ++i)
+        dma16(rb, base + (uint32_t)(4 * i) * ld2, stage + B_OFF + half * HALF_BYTES + ((wn & 1) * 8 + i) * 1024);
+    }
+    lk0 += BK;
+    if (lk0 >= S.K) {
+      ++lseg;
+      lk0 = 0;
     }
   };
 
-  // ---- fragment addresses (bytes inside a stage) ----
-  // activation rows wm*128 + 32 j + lane%32, chunk 2 ks + lane/32
+  // ---- fragment reads ----
   // NN weights: lane s of read h (0, 1) of K slice ks points at K row
   //   16 ks + 8 (g >> 1) + 4 h + (s & 15) / 4 and columns nb + 16 (g & 1) + 4 (s & 3), g = s / 16
-  int nn_lane = 0;
-  int nn_half[2], nn_nb[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    nn_half[i] = DUAL ? i : (wn >> 1);
-    nn_nb[i] = DUAL ? wn * 32 : (wn & 1) * 64 + 32 * i;
-  }
-  {
-    const int g = lane >> 4, s15 = lane & 15;
-    nn_lane = (8 * (g >> 1) + (s15 >> 2)) * 256 + (lane & 1) * 8;
-  }
-  auto nn_addr = [&](int i) -> int {  // without the 16 ks + 4 h row term
-    const int g = lane >> 4;
-    const int n = nn_nb[i] + 16 * (g & 1) + 4 * (lane & 3);
-    const int kr = ((lane & 15) >> 2);  // K row & 3 of every read of this lane
-    return B_OFF + nn_half[i] * 16384 + nn_lane + (((n >> 3) ^ (4 * kr)) * 16);
-  };
   int fa_nn[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) fa_nn[i] = nn_addr(i);
+  for (int i = 0; i < 2; ++i) {
+    const int half = DUAL ? i : (wn >> 1);
+    const int nb = DUAL ? wn * 32 : (wn & 1) * 64 + 32 * i;
+    const int g = lane >> 4;
+    const int n = nb + 16 * (g & 1) + 4 * (lane & 3);
+    const int kr = (lane & 15) >> 2;  // K row & 3 of every read of this lane
+    fa_nn[i] = B_OFF + half * HALF_BYTES + (8 * (g >> 1) + kr) * 256 + (((n >> 3) ^ (4 * kr)) * 16) + (lane & 1) * 8;
+  }
 
-  f32x16 acc[2][4];
+  // K-contiguous tiles: row r0 + 32 j (r0 = first row of the sub-tile + lane % 32)
+  // has swz = swz(r0) ^ 4 (j & 1), so chunk 2 ks + lane / 32 sits at
+  // (2 ks ^ 4 (j & 1)) ^ x with x = (lane / 32) ^ swz(r0): four per-lane offsets
+  // cover every (ks, j); the row term is an immediate.
+  auto kc_offsets = [&](int r0, int (&o)[4]) {
+    const int x = (lane >> 5) ^ swz(r0);
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int y = 0; y < 4; ++y) o[y] = r0 * 128 + (((2 * y) ^ x) * 16);
+  };
+  int ao[4];
+  kc_offsets(wm * 128 + (lane & 31), ao);
+  int bo[4];
+  if constexpr (BKIND == B_NT) kc_offsets(wn * 64 + (lane & 31), bo);
 
-  auto compute = [&](int st) {
+  bf16x8 fa[4][2], fb[4][4];
+  auto read = [&](int st) {
     const lds_char* const stage = lds + st * STAGE_BYTES;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 fa[2], fb[4];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         if constexpr (BKIND == B_NN) {
@@ -755,45 +766,80 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_dense_kernel(const GemmArgs args
           v[1] = (uint32_t)(lo >> 32);
           v[2] = (uint32_t)hi;
           v[3] = (uint32_t)(hi >> 32);
-          fa[i] = __builtin_bit_cast(bf16x8, v);
+          fa[ks][i] = __builtin_bit_cast(bf16x8, v);
         } else {
-          const int rn = wn * 64 + i * 32 + (lane & 31);
-          fa[i] = __builtin_bit_cast(bf16x8, lds_read16(stage + B_OFF + rn * 128 + (((2 * ks + (lane >> 5)) ^ swz(rn)) * 16)));
+          const int y = ((2 * ks) ^ (4 * (i & 1))) >> 1;
+          fa[ks][i] = __builtin_bit_cast(bf16x8, lds_read16(stage + B_OFF + bo[y] + i * 32 * 128));
         }
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int rm = wm * 128 + j * 32 + (lane & 31);
-        fb[j] = __builtin_bit_cast(bf16x8, lds_read16(stage + rm * 128 + (((2 * ks + (lane >> 5)) ^ swz(rm)) * 16)));
+        const int y = ((2 * ks) ^ (4 * (j & 1))) >> 1;
+        fb[ks][j] = __builtin_bit_cast(bf16x8, lds_read16(stage + ao[y] + j * 32 * 128));
       }
+    }
+  };
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  auto mma = [&]() {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0);
   };
 
-  // ---- main loop: K tile t + 1 streams into the other stage during tile t ----
-  int seg = 0;
-  int64_t k0 = 0;
-  issue(0, 0, 0);
-  for (int64_t t = 0; t < KT; ++t) {
-    __builtin_amdgcn_s_waitcnt(0x0070 | 0x3f00);  // vmcnt(0): this wavefront's blocks of tile t are in LDS
-    __syncthreads();                                // everyone's are; stage (t+1)&1 is no longer read
-    if (t + 1 < KT) {
-      k0 += BK;
-      if (k0 >= args.seg[seg].K) {
-        ++seg;
-        k0 = 0;
-      }
-      issue(seg, k0, (int)((t + 1) & 1));
+  // ---- phases.  Every wavefront passes 2 + 2 KT barriers. ----
+  //   prologue  g0: load steps 0, 1; wait for step 0 | barrier | g0: read 0 | barrier
+  //   step t    X: g0 MFMA t, wait for step t+1 loads   g1 read t     | barrier
+  //             Y: g0 load t+2, read t+1               g1 MFMA t     | barrier
+  // Stage t & 1 is last read in X(t) and reloaded in Y(t); step t+1 is read
+  // by group 0 in Y(t) after the barrier that follows its loads' vmcnt wait.
+  // sched_barrier(0) keeps the compiler from moving work across phase
+  // boundaries (MFMAs touch no memory, so it would otherwise let them drift
+  // past the barriers and break the alternation).
+  auto phase_end = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if (wm == 0) {
+    issue(0);
+    if (KT > 1) {
+      issue(1);
+      __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16): step 0's 16 blocks of this wavefront are in
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
     }
-    compute((int)(t & 1));
+    phase_end();
+    read(0);
+    phase_end();
+    for (int t = 0; t < KT; ++t) {
+      mma();
+      if (t + 1 < KT) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): step t+1 is in LDS
+      phase_end();
+      if (t + 2 < KT) issue(t & 1);
+      if (t + 1 < KT) read((t + 1) & 1);
+      phase_end();
+    }
+  } else {
+    phase_end();
+    phase_end();
+    for (int t = 0; t < KT; ++t) {
+      read(t & 1);
+      phase_end();
+      mma();
+      phase_end();
+    }
   }
-  __syncthreads();
 
-  // epilogue staging: a private region per wavefront
+  // epilogue staging: a private region per wavefront (operand stages are no longer read)
   constexpr int EB = epi_stage_bytes<64, EPI>();
   static_assert(8 * EB <= 2 * STAGE_BYTES, "epilogue staging exceeds LDS");
   char* const wstage = smem_raw + wave * EB;
