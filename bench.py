@@ -63,6 +63,86 @@ def kernel_flops(cfg, name):
     return table.get(base)
 
 
+# Kernel names (as rocprofv3 prints them) of each GEMM family: the dense
+# kernel's template arguments are <B orientation, gate/up tiles, epilogue>.
+FAMILY_KERNEL = {
+    "gemm_nn_act_fwd": "gemm_dense_kernel<0, true, 1>",
+    "gemm_nn_store": "gemm_dense_kernel<0, false, 0>",
+    "gemm_nt_act_bwd": "gemm_dense_kernel<1, false, 2>",
+    "gemm_nt_store": "gemm_dense_kernel<1, false, 0>",
+    "gemm_nn_act_fwd_nf4": "gemm_nf4_kernel<0, true, true, 1>",
+    "gemm_nn_store_nf4": "gemm_nf4_kernel<0, true, false, 0>",
+    "gemm_nt_act_bwd_nf4": "gemm_nf4_kernel<1, true, false, 2>",
+    "gemm_nt_store_nf4": "gemm_nf4_kernel<1, true, false, 0>",
+}
+COPY_KERNEL = "neg_kernel"  # the --copy-calibration kernel
+
+
+def pmc_summary(fetch_csv, write_csv, config_id):
+    """Per-launch HBM bytes of every GEMM family from two rocprofv3 --pmc
+    runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the
+    same counter reads for the known-size copy of --copy-calibration.  Writes
+    profiles/<family>_<workload>_traffic.txt and prints the table."""
+    import csv
+
+    def per_kernel(path, counter):
+        acc = {}
+        for row in csv.DictReader(open(path)):
+            if row["Counter_Name"] != counter:
+                continue
+            acc.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+        return acc
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+
+    def find(acc, key):
+        vals = [v for k, vs in acc.items() if key in k for v in vs]
+        return sum(vals) / len(vals) if vals else None
+
+    from workload import CONFIGS
+    cfg = CONFIGS[config_id]
+    # the calibration copy moves the same number of bytes each way
+    cf, cw = find(f, COPY_KERNEL), find(w, COPY_KERNEL)
+    if cf is None or cw is None:
+        raise SystemExit("no calibration copy kernel in the counter files (run with --copy-calibration)")
+    # the copy's true size is logged by bench.py; the counter files only hold KiB:
+    # WRITE_SIZE of the copy is taken as exact when it equals a whole MiB count
+    true_kib = round(cw / 1024) * 1024
+    kf, kw = true_kib / cf, true_kib / cw
+    tag = workload_tag(cfg)
+    out = []
+    for fam, kname in FAMILY_KERNEL.items():
+        a, b = find(f, kname), find(w, kname)
+        if a is None or b is None:
+            continue
+        hbm = (a * kf + b * kw) * 1024
+        path = os.path.join(ROOT, "profiles", f"{fam}_{tag}_traffic.txt")
+        with open(path, "w") as fh:
+            fh.write(f"# HBM traffic per launch of {kname} ({fam}), workload {cfg.note}\n")
+            fh.write("# from two rocprofv3 --pmc runs over bench.py (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),\n")
+            fh.write(f"# each scaled by the same counter on a {true_kib // 1024} MiB fp32 copy kernel of known size\n")
+            fh.write("#   cd /tmp && export TMPDIR=/tmp\n")
+            fh.write(f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o pf -- python3 <repo>/bench.py "
+                     f"--config {config_id} --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration {true_kib // 1024}\n")
+            fh.write("#   rocprofv3 --pmc WRITE_SIZE ... (same)\n")
+            fh.write(f"#   python3 bench.py --config {config_id} --pmc-summary pf_counter_collection.csv pw_counter_collection.csv\n")
+            fh.write(f"source_digest = {source_digest()}\n")
+            fh.write(f"fetch_kib_raw = {a:.1f}\nwrite_kib_raw = {b:.1f}\n")
+            fh.write(f"copy_fetch_kib_raw = {cf:.1f}\ncopy_write_kib_raw = {cw:.1f}\ncopy_true_kib = {true_kib}\n")
+            fh.write(f"fetch_scale = {kf:.4f}\nwrite_scale = {kw:.4f}\n")
+            fh.write(f"hbm_read_bytes_per_launch = {a * kf * 1024:.0f}\nhbm_write_bytes_per_launch = {b * kw * 1024:.0f}\n")
+            fh.write(f"hbm_bytes_per_launch = {hbm:.0f}\n")
+        out.append((fam, a * kf * 1024, b * kw * 1024))
+    for fam, rd, wr in out:
+        print(f"{fam:22s} read {rd / 1e9:8.3f} GB  write {wr / 1e9:8.3f} GB per launch")
+    print(f"calibration: FETCH x{kf:.4f}, WRITE x{kw:.4f}")
+
+
+def workload_tag(cfg):
+    return {2: "llama3_8b_mlp", 3: "gemma_geglu_mlp", 4: "llama3_8b_qlora_mlp", 5: "llama3_8b_qkvo"}[cfg.cid]
+
+
 def source_digest():
     h = hashlib.sha256()
     for f in ("gemm_bf16.hip", "common.hpp"):
@@ -71,10 +151,10 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel, workload_tag):
+def read_traffic(kernel, tag):
     """HBM bytes per launch from the committed PMC summary, if it was taken
     on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload_tag}_traffic.txt")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{tag}_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -205,10 +285,15 @@ def main():
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU run: turn two rocprofv3 --pmc counter files into profiles/*_traffic.txt")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run a plain fp32 elementwise copy (negation) of MIB MiB "
                          "three times, the known-size kernel that scales HBM byte counters")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.config)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the fused LoRA path runs on a single MI355X here and "
               "--gpus N with N > 1 is not supported (see the sharding notes in DESIGN.md).", file=sys.stderr)
@@ -261,8 +346,7 @@ def main():
     avg_ms = kms / max(launches, 1)
     fl = kernel_flops(cfg, dominant)
     achieved = fl / (avg_ms / 1e3) / 1e12 if fl and avg_ms > 0 else None
-    workload_tag = {2: "llama3_8b_mlp", 3: "gemma_geglu_mlp", 4: "llama3_8b_qlora_mlp", 5: "llama3_8b_qkvo"}[cfg.cid]
-    traffic = read_traffic(dominant, workload_tag)
+    traffic = read_traffic(dominant, workload_tag(cfg))
     log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step ({wall / args.steps * 1e3:.3f} ms wall), "
         f"{tokens_s:,.0f} tokens/s, {tflops:.1f} TFLOP/s; {dominant}: {avg_ms:.3f} ms/launch")
 
