@@ -584,8 +584,12 @@ __global__ __launch_bounds__(NTH, 1) void gemm_nf4_kernel(const GemmArgs args) {
 //
 // Operands go from global memory straight into LDS (buffer_load_dwordx4 ...
 // lds: lane i of a load writes bytes 16 i .. 16 i + 15 of a 1 KB LDS block
-// whose base is in M0), issued by group 0 two K steps ahead into a 2-stage
-// ring of 64 KB stages:
+// whose base is in M0), two K steps ahead.  The loads are split between the
+// groups so that each phase moves the same 32 KB per CU: group 0 loads the
+// activation tiles (in its read phase Y) into a 2-slot ring, group 1 the
+// weight tiles (in its read phase X) into a 3-slot ring; with three weight
+// slots the weights of step t+2 can be written while both groups still read
+// those of steps t and t+1.  LDS: 2 x 32 KB + 3 x 32 KB = 160 KB.
 //   activation tile: 256 rows x 64 K, 128-byte rows, 16-byte chunk c of row r
 //                    stored at c ^ swz(r); read with ds_read_b128;
 //   weights, NT:     the same layout over 256 output columns;
@@ -597,8 +601,10 @@ __global__ __launch_bounds__(NTH, 1) void gemm_nf4_kernel(const GemmArgs args) {
 //                    at (j = 0..3), i.e. the K-contiguous MFMA operand.
 // ---------------------------------------------------------------------------
 constexpr int NTH8 = 512;
-constexpr int STAGE_BYTES = 65536;
-constexpr int B_OFF = 32768;
+constexpr int SLOT_BYTES = 32768;
+constexpr int A_SLOTS = 2, W_SLOTS = 3;
+constexpr int W_RING = A_SLOTS * SLOT_BYTES;  // weight ring after the activation ring
+constexpr int LDS_BYTES = (A_SLOTS + W_SLOTS) * SLOT_BYTES;
 constexpr int HALF_BYTES = 16384;
 
 typedef __attribute__((address_space(3))) char lds_char;
@@ -616,14 +622,15 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* p, int64_t bytes) {
 }
 
 // 16 bytes per lane from global memory into LDS: lane i writes bytes
-// lds_addr + 16 i .. + 15; offsets past the descriptor's size read zero.
+// lds_addr + 16 i .. + 15 with the bytes at voff + soff of the descriptor;
+// offsets past the descriptor's size read zero.
 // Issued as inline assembly so that the compiler does not wait for these
 // loads before unrelated LDS reads (it cannot tell the stages apart); the
 // kernel waits with vmcnt(0) and a barrier before it reads the stage.
-__device__ __forceinline__ void dma16(const i32x4& r, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+__device__ __forceinline__ void dma16(const i32x4& r, uint32_t voff, uint32_t lds_addr, uint32_t soff = 0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
                :
-               : "v"(voff), "s"(r), "s"(lds_addr)
+               : "v"(voff), "s"(r), "s"(lds_addr), "s"(soff)
                : "memory", "m0");
 }
 __device__ __forceinline__ uint32_t lds_addr(const lds_char* p) { return (uint32_t)(uintptr_t)p; }
@@ -639,7 +646,7 @@ __device__ __forceinline__ uint64_t lds_read_tr(const lds_char* p) {
 template <int BKIND, bool DUAL, int EPI>
 __global__ __launch_bounds__(NTH8, 1) void gemm_dense_kernel(const GemmArgs args) {
   static_assert(!(DUAL && BKIND == B_NT), "gate/up tiles read forward (NN) weights");
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[LDS_BYTES];
   lds_char* const lds = (lds_char*)smem_raw;
 
   const int tid = threadIdx.x;
@@ -664,8 +671,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_dense_kernel(const GemmArgs args
   int KT = 0;
   for (int s = 0; s < args.nseg; ++s) KT += (int)(args.seg[s].K / BK);
 
-  // ---- loads (group 0): per K step each of its wavefronts issues 8
-  // activation and 8 weight 1 KB blocks ----
+  // ---- loads: 8 blocks of 1 KB per wavefront and step ----
   // K-contiguous block q = 8 wn + i holds rows 8 q + lane / 8; its row r has
   // swz(r) = (lane / 8) ^ i, so lane takes logical chunk (lane % 8) ^ (lane / 8) ^ i.
   // NN block q' = 8 (wn & 1) + i of half wn >> 1 holds K rows 4 q' + lane / 16,
@@ -674,33 +680,45 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_dense_kernel(const GemmArgs args
   const int kc_x = (lane & 7) ^ (lane >> 3);
   const int nn_row = (wn & 1) * 32 + (lane >> 4);
   const int nn_chunk = (lane & 15) ^ (4 * ((lane >> 4) & 3));
+  // each group walks the K steps with its own cursor (segment, offset)
   int lseg = 0;
   int64_t lk0 = 0;
-  auto issue = [&](int st) {
+  auto advance = [&](const GemmSeg& S) {
+    lk0 += BK;
+    if (lk0 >= S.K) {
+      ++lseg;
+      lk0 = 0;
+    }
+  };
+  auto issue_a = [&](int slot) {  // group 0: activation tile of the next step
     const GemmSeg& S = args.seg[lseg];
-    const uint32_t stage = lds_addr(lds) + st * STAGE_BYTES;
+    const uint32_t dst = lds_addr(lds) + slot * SLOT_BYTES + wn * 8 * 1024;
     // opaque copies: keep the per-lane terms from being expanded per block
-    // and hoisted out of the K loop (16 live offsets would not fit)
+    // and hoisted out of the K loop (8 live offsets would not fit)
     int x = kc_x, r = kc_row;
     asm volatile("" : "+v"(x), "+v"(r));
-    {
-      const uint32_t lda2 = (uint32_t)(S.lda * 2);
-      const i32x4 ra = rsrc_words(static_cast<const char*>(S.A) + (m0 * S.lda + lk0) * 2,
-                                  (M - m0) * S.lda * 2 - lk0 * 2);
-      const uint32_t base = (uint32_t)r * lda2;
+    const uint32_t lda2 = (uint32_t)(S.lda * 2);
+    const i32x4 ra = rsrc_words(static_cast<const char*>(S.A) + (m0 * S.lda + lk0) * 2,
+                                (M - m0) * S.lda * 2 - lk0 * 2);
+    const uint32_t base = (uint32_t)r * lda2;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        dma16(ra, base + (uint32_t)(8 * i) * lda2 + (uint32_t)((x ^ i) << 4), stage + (wn * 8 + i) * 1024);
-    }
+    for (int i = 0; i < 8; ++i) dma16(ra, base + (uint32_t)((x ^ i) << 4), dst + i * 1024, (uint32_t)(8 * i) * lda2);
+    advance(S);
+  };
+  auto issue_w = [&](int slot) {  // group 1: weight tile of the next step
+    const GemmSeg& S = args.seg[lseg];
+    const uint32_t wslot = lds_addr(lds) + W_RING + slot * SLOT_BYTES;
     if constexpr (BKIND == B_NT) {
       const BSrc& B = S.b[reg][0];
+      int x = kc_x, r = kc_row;
+      asm volatile("" : "+v"(x), "+v"(r));
       const uint32_t ld2 = (uint32_t)(B.ld * 2);
       const i32x4 rb = rsrc_words(static_cast<const char*>(B.p) + (tnl * 256 * B.ld + lk0) * 2,
                                   (NR - tnl * 256) * B.ld * 2 - lk0 * 2);
       const uint32_t base = (uint32_t)r * ld2;
+      const uint32_t dst = wslot + wn * 8 * 1024;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        dma16(rb, base + (uint32_t)(8 * i) * ld2 + (uint32_t)((x ^ i) << 4), stage + B_OFF + (wn * 8 + i) * 1024);
+      for (int i = 0; i < 8; ++i) dma16(rb, base + (uint32_t)((x ^ i) << 4), dst + i * 1024, (uint32_t)(8 * i) * ld2);
     } else {
       const int half = wn >> 1;
       const BSrc& B = S.b[reg][DUAL ? half : 0];
@@ -711,15 +729,11 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_dense_kernel(const GemmArgs args
       int nr = nn_row, nc = nn_chunk;
       asm volatile("" : "+v"(nr), "+v"(nc));
       const uint32_t base = (uint32_t)nr * ld2 + (uint32_t)(nc << 4);
+      const uint32_t dst = wslot + half * HALF_BYTES + (wn & 1) * 8 * 1024;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        dma16(rb, base + (uint32_t)(4 * i) * ld2, stage + B_OFF + half * HALF_BYTES + ((wn & 1) * 8 + i) * 1024);
+      for (int i = 0; i < 8; ++i) dma16(rb, base, dst + i * 1024, (uint32_t)(4 * i) * ld2);
     }
-    lk0 += BK;
-    if (lk0 >= S.K) {
-      ++lseg;
-      lk0 = 0;
-    }
+    advance(S);
   };
 
   // ---- fragment reads ----
@@ -733,9 +747,8 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_dense_kernel(const GemmArgs args
     const int g = lane >> 4;
     const int n = nb + 16 * (g & 1) + 4 * (lane & 3);
     const int kr = (lane & 15) >> 2;  // K row & 3 of every read of this lane
-    fa_nn[i] = B_OFF + half * HALF_BYTES + (8 * (g >> 1) + kr) * 256 + (((n >> 3) ^ (4 * kr)) * 16) + (lane & 1) * 8;
+    fa_nn[i] = half * HALF_BYTES + (8 * (g >> 1) + kr) * 256 + (((n >> 3) ^ (4 * kr)) * 16) + (lane & 1) * 8;
   }
-
   // K-contiguous tiles: row r0 + 32 j (r0 = first row of the sub-tile + lane % 32)
   // has swz = swz(r0) ^ 4 (j & 1), so chunk 2 ks + lane / 32 sits at
   // (2 ks ^ 4 (j & 1)) ^ x with x = (lane / 32) ^ swz(r0): four per-lane offsets
@@ -751,14 +764,15 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_dense_kernel(const GemmArgs args
   if constexpr (BKIND == B_NT) kc_offsets(wn * 64 + (lane & 31), bo);
 
   bf16x8 fa[4][2], fb[4][4];
-  auto read = [&](int st) {
-    const lds_char* const stage = lds + st * STAGE_BYTES;
+  auto read = [&](int aslot, int wslot) {
+    const lds_char* const at = lds + aslot * SLOT_BYTES;
+    const lds_char* const wt = lds + W_RING + wslot * SLOT_BYTES;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         if constexpr (BKIND == B_NN) {
-          const lds_char* p = stage + fa_nn[i] + (16 * ks) * 256;
+          const lds_char* p = wt + fa_nn[i] + (16 * ks) * 256;
           const uint64_t lo = lds_read_tr(p);
           const uint64_t hi = lds_read_tr(p + 4 * 256);
           u32x4 v;
@@ -769,13 +783,13 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_dense_kernel(const GemmArgs args
           fa[ks][i] = __builtin_bit_cast(bf16x8, v);
         } else {
           const int y = ((2 * ks) ^ (4 * (i & 1))) >> 1;
-          fa[ks][i] = __builtin_bit_cast(bf16x8, lds_read16(stage + B_OFF + bo[y] + i * 32 * 128));
+          fa[ks][i] = __builtin_bit_cast(bf16x8, lds_read16(wt + bo[y] + i * 32 * 128));
         }
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int y = ((2 * ks) ^ (4 * (j & 1))) >> 1;
-        fb[ks][j] = __builtin_bit_cast(bf16x8, lds_read16(stage + ao[y] + j * 32 * 128));
+        fb[ks][j] = __builtin_bit_cast(bf16x8, lds_read16(at + ao[y] + j * 32 * 128));
       }
     }
   };
@@ -796,52 +810,69 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_dense_kernel(const GemmArgs args
   };
 
   // ---- phases.  Every wavefront passes 2 + 2 KT barriers. ----
-  //   prologue  g0: load steps 0, 1; wait for step 0 | barrier | g0: read 0 | barrier
-  //   step t    X: g0 MFMA t, wait for step t+1 loads   g1 read t     | barrier
-  //             Y: g0 load t+2, read t+1               g1 MFMA t     | barrier
-  // Stage t & 1 is last read in X(t) and reloaded in Y(t); step t+1 is read
-  // by group 0 in Y(t) after the barrier that follows its loads' vmcnt wait.
-  // sched_barrier(0) keeps the compiler from moving work across phase
-  // boundaries (MFMAs touch no memory, so it would otherwise let them drift
-  // past the barriers and break the alternation).
+  //   prologue  g0 loads A 0, 1   g1 loads W 0, 1; each waits for step 0 | barrier
+  //             g0 reads step 0                                         | barrier
+  //   step t    X: g0 MFMA t, waits for A t+1
+  //                g1 loads W t+2, reads step t, waits for W t+1        | barrier
+  //             Y: g0 loads A t+2, reads step t+1
+  //                g1 MFMA t                                            | barrier
+  // A t+2 goes to activation slot t & 1 after its last read (g1, X(t));
+  // W t+2 goes to weight slot (t+2) % 3, last read in X(t-1).
   auto phase_end = [&]() {
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
   };
   if (wm == 0) {
-    issue(0);
+    issue_a(0);
     if (KT > 1) {
-      issue(1);
-      __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16): step 0's 16 blocks of this wavefront are in
+      issue_a(1);
+      __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): A 0 is in
     } else {
       __builtin_amdgcn_s_waitcnt(0x0F70);
     }
     phase_end();
-    read(0);
+    read(0, 0);
     phase_end();
     for (int t = 0; t < KT; ++t) {
       mma();
-      if (t + 1 < KT) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): step t+1 is in LDS
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): A t+1 is in
       phase_end();
-      if (t + 2 < KT) issue(t & 1);
-      if (t + 1 < KT) read((t + 1) & 1);
+      if (t + 2 < KT) issue_a(t & 1);
+      if (t + 1 < KT) read((t + 1) & 1, (t + 1) % 3);
       phase_end();
     }
   } else {
+    issue_w(0);
+    if (KT > 1) {
+      issue_w(1);
+      __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): W 0 is in
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
     phase_end();
     phase_end();
+    int ws = 0;  // weight slot of step t
     for (int t = 0; t < KT; ++t) {
-      read(t & 1);
+      const int ws2 = ws == 0 ? 2 : ws - 1;  // (t + 2) % 3
+      if (t + 2 < KT) {
+        issue_w(ws2);
+        read(t & 1, ws);
+        __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): W t+1 is in (W t+2 may still fly)
+      } else {
+        read(t & 1, ws);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+      }
       phase_end();
       mma();
       phase_end();
+      ws = ws == 2 ? 0 : ws + 1;
     }
   }
 
-  // epilogue staging: a private region per wavefront (operand stages are no longer read)
+  // epilogue staging: a private region per wavefront (operand slots are no longer read)
   constexpr int EB = epi_stage_bytes<64, EPI>();
-  static_assert(8 * EB <= 2 * STAGE_BYTES, "epilogue staging exceeds LDS");
+  static_assert(8 * EB <= LDS_BYTES, "epilogue staging exceeds LDS");
   char* const wstage = smem_raw + wave * EB;
   const int64_t mw = m0 + wm * 128;
   const int64_t nbase = DUAL ? tnl * 128 + wn * 32 : tnl * 256 + wn * 64;
