@@ -41,6 +41,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "lds_dma.hpp"
 
 namespace lora {
 namespace {
@@ -55,13 +56,6 @@ constexpr int OOB = 0x7ffffff0;       // a buffer offset past every operand: loa
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-// Values the compiler cannot prove uniform are moved to scalar registers.
-__device__ __forceinline__ int64_t uni64(int64_t x) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
-  return (int64_t)(((uint64_t)hi << 32) | lo);
-}
 
 // Buffer descriptor over [p, p + bytes) (bytes < 2^31); every input is uniform.
 __device__ __forceinline__ rsrc_t rsrc(const void* p, int64_t bytes) {
@@ -607,42 +601,6 @@ constexpr int W_RING = A_SLOTS * SLOT_BYTES;  // weight ring after the activatio
 constexpr int LDS_BYTES = (A_SLOTS + W_SLOTS) * SLOT_BYTES;
 constexpr int HALF_BYTES = 16384;
 
-typedef __attribute__((address_space(3))) char lds_char;
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer descriptor as four scalar words (base, stride 0, byte size, format)
-// for the inline-assembly load below; every input is uniform.
-__device__ __forceinline__ i32x4 rsrc_words(const void* p, int64_t bytes) {
-  if (bytes < 0) bytes = 0;
-  const uint64_t base = (uint64_t)uni64(reinterpret_cast<int64_t>(p));
-  const int n = __builtin_amdgcn_readfirstlane((int)bytes);
-  return i32x4{(int)(uint32_t)base, (int)((base >> 32) & 0xffff), n, 0x00020000};
-}
-
-// 16 bytes per lane from global memory into LDS: lane i writes bytes
-// lds_addr + 16 i .. + 15 with the bytes at voff + soff of the descriptor;
-// offsets past the descriptor's size read zero.
-// Issued as inline assembly so that the compiler does not wait for these
-// loads before unrelated LDS reads (it cannot tell the stages apart); the
-// kernel waits with vmcnt(0) and a barrier before it reads the stage.
-__device__ __forceinline__ void dma16(const i32x4& r, uint32_t voff, uint32_t lds_addr, uint32_t soff = 0) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
-               :
-               : "v"(voff), "s"(r), "s"(lds_addr), "s"(soff)
-               : "memory", "m0");
-}
-__device__ __forceinline__ uint32_t lds_addr(const lds_char* p) { return (uint32_t)(uintptr_t)p; }
-__device__ __forceinline__ u32x4 lds_read16(const lds_char* p) {
-  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(p);
-}
-__device__ __forceinline__ uint64_t lds_read_tr(const lds_char* p) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(p));
-  return __builtin_bit_cast(uint64_t, v);
-}
-
 template <int BKIND, bool DUAL, int EPI>
 __global__ __launch_bounds__(NTH8, 1) void gemm_dense_kernel(const GemmArgs args) {
   static_assert(!(DUAL && BKIND == B_NT), "gate/up tiles read forward (NN) weights");
@@ -772,15 +730,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_dense_kernel(const GemmArgs args
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         if constexpr (BKIND == B_NN) {
-          const lds_char* p = wt + fa_nn[i] + (16 * ks) * 256;
-          const uint64_t lo = lds_read_tr(p);
-          const uint64_t hi = lds_read_tr(p + 4 * 256);
-          u32x4 v;
-          v[0] = (uint32_t)lo;
-          v[1] = (uint32_t)(lo >> 32);
-          v[2] = (uint32_t)hi;
-          v[3] = (uint32_t)(hi >> 32);
-          fa[ks][i] = __builtin_bit_cast(bf16x8, v);
+          fa[ks][i] = lds_read_tr8(wt + fa_nn[i] + (16 * ks) * 256, 4 * 256);
         } else {
           const int y = ((2 * ks) ^ (4 * (i & 1))) >> 1;
           fa[ks][i] = __builtin_bit_cast(bf16x8, lds_read16(wt + bo[y] + i * 32 * 128));

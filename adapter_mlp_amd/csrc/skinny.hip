@@ -7,13 +7,16 @@
 // colproj   Out[k, j] = sum_t Z[t, k] P[t, j]       (K x R, reduction over T)
 //   the adapter gradients dA = s X^T P and dB = s U^T dZ (stored transposed).
 //
-// Both stream one large operand (Z) once from HBM.  The bf16 versions feed
-// v_mfma_f32_16x16x32_bf16 straight from 16-byte global loads (rowproj) or
-// through a transposing LDS stage (colproj, whose contraction runs down the
-// columns of Z).  Reductions are deterministic: fixed wave order in LDS for
-// rowproj, per-chunk partials summed in ascending chunk order for colproj.
+// Both are bound by streaming Z ([T, K] bf16) from HBM once.  The bf16
+// versions move Z in 1 KB global-to-LDS loads through a ring of LDS slots
+// several steps deep (enough bytes in flight per CU to cover HBM latency),
+// and feed v_mfma_f32_16x16x32_bf16 from LDS: row-contiguous operands with
+// ds_read_b128, the T-contiguous operands of colproj with the transposing
+// ds_read_b64_tr_b16.  Reductions are deterministic: fixed wave order in LDS
+// for rowproj, per-chunk partials summed in ascending chunk order for colproj.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "lds_dma.hpp"
 
 namespace lora {
 namespace {
@@ -21,57 +24,135 @@ namespace {
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 // ---------------------------------------------------------------------------
-// rowproj, bf16: one block = 16 rows of Z, 4 wavefronts splitting K in
-// interleaved 32-wide steps.  Lane l holds row (l & 15), K group (l >> 4).
+// rowproj, bf16.  Block = 32 rows of Z over all of K, 4 wavefronts.  Per
+// 256-column chunk, Z [32 x 256] and Bt [16 NJ x 256] land in one ring slot;
+// wavefront w multiplies the chunk's K steps 2w and 2w+1 (32 columns each)
+// into acc[row block][column block]; the four partial sums are added in
+// fixed order at the end.  Slot rows are 512 bytes; 16-byte chunk c of row r
+// is stored at c ^ (r & 15), so the 16 rows of a fragment read hit 16
+// different bank groups.
 // ---------------------------------------------------------------------------
 template <int NJ>
-__global__ __launch_bounds__(256) void rowproj_bf16_kernel(const RowProjArgs a) {
-  __shared__ float red[4][16][NJ * 16];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t t0 = (int64_t)blockIdx.x * 16;
-  const int64_t row = t0 + (lane & 15) < a.T ? t0 + (lane & 15) : a.T - 1;
-  const int kg = lane >> 4;
-  const char* Z = static_cast<const char*>(a.Z) + (row * a.ldz + kg * 8) * 2;
-  const char* Bt = static_cast<const char*>(a.Bt);
-  const int64_t nsteps = a.K >> 5;
+struct RowProjCfg {
+  static constexpr int ZB = 32 * 512;          // Z bytes per slot
+  static constexpr int BB = NJ * 16 * 512;     // Bt bytes per slot
+  static constexpr int SB = ZB + BB;
+  static constexpr int NST = NJ == 1 ? 6 : NJ == 2 ? 5 : NJ == 3 ? 4 : 3;
+  static constexpr int D = 4 + 2 * NJ;         // loads per wavefront and chunk
+};
 
-  f32x4 acc[NJ];
-#pragma unroll
-  for (int jb = 0; jb < NJ; ++jb) acc[jb] = f32x4{0, 0, 0, 0};
-  const char* bptr[NJ];
-  bool bval[NJ];
-#pragma unroll
-  for (int jb = 0; jb < NJ; ++jb) {
-    const int j = jb * 16 + (lane & 15);
-    bval[jb] = j < a.R;
-    bptr[jb] = Bt + ((int64_t)(bval[jb] ? j : 0) * a.ldb + kg * 8) * 2;
-  }
-#pragma unroll 4
-  for (int64_t ks = w; ks < nsteps; ks += 4) {
-    const u32x4 zv = ld16(Z + ks * 64);
-    const bf16x8 za = __builtin_bit_cast(bf16x8, zv);
-#pragma unroll
-    for (int jb = 0; jb < NJ; ++jb) {
-      u32x4 bv = ld16(bptr[jb] + ks * 64);
-      if (!bval[jb]) bv = u32x4{0, 0, 0, 0};
-      acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(za, __builtin_bit_cast(bf16x8, bv), acc[jb], 0, 0, 0);
+template <int D, int K>
+__device__ __forceinline__ void wait_steps_after(int after) {
+  // vmcnt(D * after) for after = 0 .. K (compile-time immediates)
+  if constexpr (K > 0) {
+    if (after >= K) {
+      wait_vmcnt<D * K>();
+      return;
     }
+    wait_steps_after<D, K - 1>(after);
+  } else {
+    wait_vmcnt<0>();
   }
-  // acc[jb][v] = Out[t0 + 4 (lane >> 4) + v, 16 jb + (lane & 15)] (this wave's K share)
+}
+
+template <int NJ>
+__global__ __launch_bounds__(256) void rowproj_bf16_kernel(const RowProjArgs a) {
+  using C = RowProjCfg<NJ>;
+  __shared__ __attribute__((aligned(1024))) char ring[C::NST * C::SB];
+  lds_char* const lds = (lds_char*)ring;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t t0 = (int64_t)blockIdx.x * 32;
+  const int64_t rows = a.T - t0 < 32 ? a.T - t0 : 32;
+  const int nch = (int)((a.K + 255) / 256);
+  const uint32_t ldz2 = (uint32_t)(a.ldz * 2), ldb2 = (uint32_t)(a.ldb * 2);
+  // rows past T and adapter rows past R read as zero
+  const i32x4 rz = rsrc_words(static_cast<const char*>(a.Z) + t0 * a.ldz * 2, rows * a.ldz * 2);
+  const i32x4 rb = rsrc_words(a.Bt, (int64_t)a.R * a.ldb * 2);
+
+  // load blocks of this wavefront: Z blocks 4w..4w+3 (rows 2q, 2q+1), Bt
+  // blocks 2NJ w .. (rows 2q', 2q'+1); lane -> row q*2 + lane/32, chunk lane%32
+  const int hrow = lane >> 5, pc = lane & 31;
+  uint32_t zoff[4], boff[2 * NJ];
 #pragma unroll
-  for (int jb = 0; jb < NJ; ++jb)
+  for (int i = 0; i < 4; ++i) {
+    const int row = 2 * (4 * w + i) + hrow;
+    zoff[i] = (uint32_t)row * ldz2 + (uint32_t)((pc ^ (row & 15)) * 16);
+  }
 #pragma unroll
-    for (int v = 0; v < 4; ++v) red[w][4 * (lane >> 4) + v][jb * 16 + (lane & 15)] = acc[jb][v];
+  for (int i = 0; i < 2 * NJ; ++i) {
+    const int row = 2 * (2 * NJ * w + i) + hrow;
+    boff[i] = (uint32_t)row * ldb2 + (uint32_t)((pc ^ (row & 15)) * 16);
+  }
+  auto issue = [&](int c, int slot) {
+    const uint32_t base = lds_addr(lds) + slot * C::SB;
+    const uint32_t soff = (uint32_t)c * 512;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(rz, zoff[i], base + (4 * w + i) * 1024, soff);
+#pragma unroll
+    for (int i = 0; i < 2 * NJ; ++i) dma16(rb, boff[i], base + C::ZB + (2 * NJ * w + i) * 1024, soff);
+  };
+
+  f32x4 acc[2][NJ];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NJ; ++nb) acc[mb][nb] = f32x4{0, 0, 0, 0};
+  // fragment chunk of K step ks (0..7) for this lane: 4 ks + lane / 16, stored
+  // at that ^ (lane & 15) in rows mb*16 + lane%16 and nb*16 + lane%16
+  const int rl = lane & 15;
+  auto compute = [&](int c, int slot) {
+    const lds_char* zs = lds + slot * C::SB;
+    const lds_char* bs = zs + C::ZB;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ks = 2 * w + i;
+      if ((int64_t)c * 256 + ks * 32 >= a.K) continue;  // K tail (uniform)
+      const int off = ((4 * ks + (lane >> 4)) ^ rl) * 16;
+      bf16x8 za[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        za[mb] = __builtin_bit_cast(bf16x8, lds_read16(zs + (mb * 16 + rl) * 512 + off));
+#pragma unroll
+      for (int nb = 0; nb < NJ; ++nb) {
+        const bf16x8 bb = __builtin_bit_cast(bf16x8, lds_read16(bs + (nb * 16 + rl) * 512 + off));
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(za[mb], bb, acc[mb][nb], 0, 0, 0);
+      }
+    }
+  };
+
+  const int pre = nch < C::NST - 1 ? nch : C::NST - 1;
+  for (int c = 0; c < pre; ++c) issue(c, c);
+  for (int c = 0; c < nch; ++c) {
+    const int after = (nch - 1 - c) < (C::NST - 2) ? (nch - 1 - c) : (C::NST - 2);
+    wait_steps_after<C::D, C::NST - 2>(after);  // chunk c of this wavefront has landed
+    __syncthreads();                            // everyone's has; chunk c-1's slot is free
+    if (c + C::NST - 1 < nch) issue(c + C::NST - 1, (c + C::NST - 1) % C::NST);
+    compute(c, c % C::NST);
+  }
+  __syncthreads();
+
+  // acc[mb][nb][v] = Out[t0 + 16 mb + 4 (lane >> 4) + v, 16 nb + lane % 16] (K share of wavefront w)
+  float* red = reinterpret_cast<float*>(ring);  // [4][32][16 NJ]
+  constexpr int RW = NJ * 16;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NJ; ++nb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[(w * 32 + mb * 16 + 4 * (lane >> 4) + v) * RW + nb * 16 + rl] = acc[mb][nb][v];
   __syncthreads();
   const int R2 = a.R2 > a.R ? a.R2 : a.R;
-  for (int e = tid; e < 16 * R2; e += 256) {
-    const int rl = e / R2, j = e % R2;
-    const int64_t t = t0 + rl;
+  for (int e = tid; e < 32 * R2; e += 256) {
+    const int r = e / R2, j = e % R2;
+    const int64_t t = t0 + r;
     if (t >= a.T) continue;
     float v = 0.0f;
-    if (j < a.R) v = ((red[0][rl][j] + red[1][rl][j]) + red[2][rl][j]) + red[3][rl][j];
-    if (a.out1 && j < a.R)
-      static_cast<uint16_t*>(a.out1)[t * a.ld1 + a.off1 + j] = (uint16_t)f2bf(v);
+    if (j < a.R) v = ((red[(0 * 32 + r) * RW + j] + red[(1 * 32 + r) * RW + j]) + red[(2 * 32 + r) * RW + j]) +
+                     red[(3 * 32 + r) * RW + j];
+    if (a.out1 && j < a.R) static_cast<uint16_t*>(a.out1)[t * a.ld1 + a.off1 + j] = (uint16_t)f2bf(v);
     if (a.out2) {
       const float sc = j < a.R ? a.scales[j / a.seg_w] : 0.0f;
       static_cast<uint16_t*>(a.out2)[t * a.ld2 + j] = (uint16_t)f2bf(sc * v);
@@ -99,97 +180,119 @@ __global__ void rowproj_f32_kernel(const RowProjArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// colproj, bf16.  Block = 64 columns of Z (k) x one chunk of T.  Per 256-row
-// step: Z [256 x 64] and P [256 x R] are loaded as 8x8 sub-blocks, transposed
-// in registers and stored T-contiguous in LDS (Zt [64][256], Pt [R][256]);
-// then wave w multiplies Zt rows 16w..16w+15 by Pt over the 256 rows.
-// LDS rows are 32 chunks of 16 bytes, chunk index XOR-swizzled by the row.
+// colproj, bf16.  Block = 256 columns of Z (k) x one chunk of T (a multiple
+// of 32 rows), 4 wavefronts.  Per 32-row step, Z [32 x 256] and P [32 x PW]
+// land in one ring slot; wavefront w owns columns 64 w .. 64 w + 63 (four
+// 16-row MFMA blocks of Z^T) and accumulates over the chunk.  Both operands
+// are T-contiguous in the MFMA, so they are read with ds_read_b64_tr_b16:
+// lane s of a read points at row 8 g + 4 h + (s & 15) / 4 (g = s / 16,
+// h = 0, 1) and 4 columns at 4 (s & 3).  Z slot rows are 512 bytes, 16-byte
+// chunk c of row t stored at c ^ zswz(t); the 16 rows x 32 bytes of one
+// transposing read then fall on every bank group exactly twice.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void transpose8x8(const u32x4 (&r)[8], u32x4 (&o)[8]) {
-#pragma unroll
-  for (int p = 0; p < 4; ++p)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t lo = r[2 * q][p], hi = r[2 * q + 1][p];
-      o[2 * p][q] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-      o[2 * p + 1][q] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
-    }
-}
+__device__ __forceinline__ int zswz(int t) { return 2 * ((t & 3) + 4 * ((t >> 3) & 1)); }
+
+template <int NJ>
+struct ColProjCfg {
+  static constexpr int PW = NJ == 3 ? 64 : NJ * 16;  // staged P columns
+  static constexpr int ZB = 32 * 512;
+  static constexpr int PB = 32 * PW * 2;             // 1, 2 or 4 KB
+  static constexpr int NPB = PB / 1024;              // P load blocks per step
+  static constexpr int SB = ZB + PB;
+  static constexpr int NST = 6;
+};
 
 template <int NJ>
 __global__ __launch_bounds__(256) void colproj_bf16_kernel(const ColProjArgs a, int64_t rows_per_chunk) {
-  __shared__ u32x4 Zt[64 * 32];
-  __shared__ u32x4 Pt[NJ * 16 * 32];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t k0 = (int64_t)blockIdx.x * 64;
+  using C = ColProjCfg<NJ>;
+  __shared__ __attribute__((aligned(1024))) char ring[C::NST * C::SB];
+  lds_char* const lds = (lds_char*)ring;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t k0 = (int64_t)blockIdx.x * 256;
   const int64_t c = blockIdx.y;
   const int64_t tbeg = c * rows_per_chunk;
-  int64_t tend = tbeg + rows_per_chunk;
-  if (tend > a.T) tend = a.T;
-  const char* Z = static_cast<const char*>(a.Z);
-  const char* P = static_cast<const char*>(a.P);
-  const int kc = tid & 7, tg = tid >> 3;   // Z: 8-column chunk, 8-row group
-  const int npair = (a.R >> 3) * 32;       // P: (8-column chunk, 8-row group) pairs
-  const int pjc = tid >> 5, ptg = tid & 31;
+  const int64_t tend = tbeg + rows_per_chunk < a.T ? tbeg + rows_per_chunk : a.T;
+  const int nsteps = (int)((tend - tbeg + 31) / 32);
+  const uint32_t ldz2 = (uint32_t)(a.ldz * 2), ldp2 = (uint32_t)(a.ldp * 2);
+  // rows past T read as zero; columns past K (last column block) only reach
+  // outputs k >= K, which are not stored
+  const i32x4 rz = rsrc_words(static_cast<const char*>(a.Z) + (tbeg * a.ldz + k0) * 2,
+                              (a.T - tbeg) * a.ldz * 2 - k0 * 2);
+  const i32x4 rp = rsrc_words(static_cast<const char*>(a.P) + tbeg * a.ldp * 2, (a.T - tbeg) * a.ldp * 2);
 
-  f32x4 acc[NJ];
+  // Z blocks 4w..4w+3 (rows 2q, 2q+1; lane -> row 2q + lane/32, chunk lane%32);
+  // P block w if w < NPB (rows 32/NPB per block, PW/8 chunks per row)
+  const int hrow = lane >> 5, pc = lane & 31;
+  uint32_t zoff[4];
 #pragma unroll
-  for (int jb = 0; jb < NJ; ++jb) acc[jb] = f32x4{0, 0, 0, 0};
-
-  for (int64_t ts = tbeg; ts < tend; ts += 256) {
-    {
-      u32x4 r[8], o[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t t = ts + tg * 8 + i;
-        r[i] = t < tend ? ld16(Z + (t * a.ldz + k0 + kc * 8) * 2) : u32x4{0, 0, 0, 0};
-      }
-      transpose8x8(r, o);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int row = kc * 8 + j;
-        Zt[row * 32 + (tg ^ (row & 31))] = o[j];
-      }
-    }
-    if (tid < npair) {
-      u32x4 r[8], o[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t t = ts + ptg * 8 + i;
-        r[i] = t < tend ? ld16(P + (t * a.ldp + pjc * 8) * 2) : u32x4{0, 0, 0, 0};
-      }
-      transpose8x8(r, o);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int row = pjc * 8 + j;
-        Pt[row * 32 + (ptg ^ (row & 31))] = o[j];
-      }
-    }
-    // rows of Pt past R hold stale data only for j >= R, which is never stored
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int ch = s * 4 + (lane >> 4);
-      const int zr = w * 16 + (lane & 15);
-      const bf16x8 za = __builtin_bit_cast(bf16x8, Zt[zr * 32 + (ch ^ (zr & 31))]);
-#pragma unroll
-      for (int jb = 0; jb < NJ; ++jb) {
-        const int pr = jb * 16 + (lane & 15);
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, Pt[pr * 32 + (ch ^ (pr & 31))]);
-        acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(za, pb, acc[jb], 0, 0, 0);
-      }
-    }
-    __syncthreads();
+  for (int i = 0; i < 4; ++i) {
+    const int row = 2 * (4 * w + i) + hrow;
+    zoff[i] = (uint32_t)row * ldz2 + (uint32_t)((pc ^ zswz(row)) * 16);
   }
-  // acc[jb][v] = Out[k0 + 16 w + 4 (lane >> 4) + v, 16 jb + (lane & 15)]
+  constexpr int PCH = C::PW / 8;  // 16-byte chunks per P row
+  const int prow = w * (64 / PCH) + lane / PCH;
+  const uint32_t poff = (uint32_t)prow * ldp2 + (uint32_t)((lane % PCH) * 16);
+  const bool pload = w < C::NPB;
+  auto issue = [&](int s, int slot) {
+    const uint32_t base = lds_addr(lds) + slot * C::SB;
+    const uint32_t zs = (uint32_t)s * 32 * ldz2, ps = (uint32_t)s * 32 * ldp2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(rz, zoff[i], base + (4 * w + i) * 1024, zs);
+    if (pload) dma16(rp, poff, base + C::ZB + w * 1024, ps);
+  };
+
+  f32x4 acc[4][NJ];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int nb = 0; nb < NJ; ++nb) acc[mi][nb] = f32x4{0, 0, 0, 0};
+  // transposing-read addresses (bytes in a slot), read h adds 4 rows
+  const int g = lane >> 4, i15 = lane & 15;
+  const int tr = 8 * g + (i15 >> 2);  // row of read h = 0
+  int zaddr[4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    const int col = 16 * (4 * w + mi) + 4 * (i15 & 3);
+    zaddr[mi] = tr * 512 + (((col >> 3) ^ zswz(tr)) * 16) + (col & 7) * 2;
+  }
+  auto compute = [&](int slot) {
+    const lds_char* zs = lds + slot * C::SB;
+    const lds_char* ps = zs + C::ZB;
+    bf16x8 pb[NJ];
+#pragma unroll
+    for (int nb = 0; nb < NJ; ++nb) pb[nb] = lds_read_tr8(ps + tr * (C::PW * 2) + (16 * nb + 4 * (i15 & 3)) * 2, 4 * C::PW * 2);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const bf16x8 za = lds_read_tr8(zs + zaddr[mi], 4 * 512);
+#pragma unroll
+      for (int nb = 0; nb < NJ; ++nb)
+        acc[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(za, pb[nb], acc[mi][nb], 0, 0, 0);
+    }
+  };
+
+  const int pre = nsteps < C::NST - 1 ? nsteps : C::NST - 1;
+  for (int s = 0; s < pre; ++s) issue(s, s);
+  for (int s = 0; s < nsteps; ++s) {
+    const int after = (nsteps - 1 - s) < (C::NST - 2) ? (nsteps - 1 - s) : (C::NST - 2);
+    if (pload) wait_steps_after<5, C::NST - 2>(after);
+    else wait_steps_after<4, C::NST - 2>(after);
+    __syncthreads();
+    if (s + C::NST - 1 < nsteps) issue(s + C::NST - 1, (s + C::NST - 1) % C::NST);
+    compute(s % C::NST);
+  }
+
+  // acc[mi][nb][v] = Out[k0 + 16 (4w + mi) + 4 (lane >> 4) + v, 16 nb + lane % 16]
   const int Rp = NJ * 16;
 #pragma unroll
-  for (int jb = 0; jb < NJ; ++jb)
+  for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t k = k0 + w * 16 + 4 * (lane >> 4) + v;
-      a.partial[(c * a.K + k) * Rp + jb * 16 + (lane & 15)] = acc[jb][v];
-    }
+    for (int nb = 0; nb < NJ; ++nb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t k = k0 + 16 * (4 * w + mi) + 4 * (lane >> 4) + v;
+        if (k < a.K) a.partial[(c * a.K + k) * Rp + nb * 16 + i15] = acc[mi][nb][v];
+      }
 }
 
 __device__ __forceinline__ void colproj_store(const ColProjArgs& a, bool bf16, int64_t k, int j, float v) {
@@ -269,10 +372,10 @@ inline unsigned nblk(int64_t n, int b) { return (unsigned)((n + b - 1) / b); }
 }  // namespace
 
 int colproj_nchunk(int64_t T, int64_t K) {
-  const int64_t steps = (T + 255) / 256;
+  const int64_t steps = (T + 31) / 32;
   if (steps == 0) return 0;
-  const int64_t kblocks = K / 64;
-  int64_t want = (2048 + kblocks - 1) / kblocks;
+  const int64_t kblocks = (K + 255) / 256;
+  int64_t want = (512 + kblocks - 1) / kblocks;  // about two blocks per CU
   if (want < 1) want = 1;
   return (int)(want < steps ? want : steps);
 }
@@ -289,7 +392,7 @@ hipError_t launch_rowproj(bool bf16, const RowProjArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(rowproj_f32_kernel, dim3(nblk(a.T * R2, 256)), dim3(256), 0, st, a);
     return hipGetLastError();
   }
-  const dim3 grid(nblk(a.T, 16));
+  const dim3 grid(nblk(a.T, 32));
   switch ((a.R + 15) / 16) {
     case 1: hipLaunchKernelGGL(rowproj_bf16_kernel<1>, grid, dim3(256), 0, st, a); break;
     case 2: hipLaunchKernelGGL(rowproj_bf16_kernel<2>, grid, dim3(256), 0, st, a); break;
@@ -309,11 +412,11 @@ hipError_t launch_colproj(bool bf16, const ColProjArgs& a0, hipStream_t st) {
   const int NJ = (a.R + 15) / 16;
   a.nchunk = colproj_nchunk(a.T, a.K);
   if (a.nchunk > 0) {
-    const int64_t steps = (a.T + 255) / 256;
+    const int64_t steps = (a.T + 31) / 32;
     const int64_t steps_per_chunk = (steps + a.nchunk - 1) / a.nchunk;
-    const int64_t rows_per_chunk = steps_per_chunk * 256;
+    const int64_t rows_per_chunk = steps_per_chunk * 32;
     a.nchunk = (int)((a.T + rows_per_chunk - 1) / rows_per_chunk);
-    const dim3 grid((unsigned)(a.K / 64), (unsigned)a.nchunk);
+    const dim3 grid((unsigned)((a.K + 255) / 256), (unsigned)a.nchunk);
     switch (NJ) {
       case 1: hipLaunchKernelGGL(colproj_bf16_kernel<1>, grid, dim3(256), 0, st, a, rows_per_chunk); break;
       case 2: hipLaunchKernelGGL(colproj_bf16_kernel<2>, grid, dim3(256), 0, st, a, rows_per_chunk); break;
