@@ -749,7 +749,10 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_dense_kernel(const GemmArgs args
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  // the MFMA phase runs at raised wavefront priority, so the SIMD's other
+  // wavefront (in its read phase) cannot delay the MFMA issue
   auto mma = [&]() {
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -757,6 +760,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_dense_kernel(const GemmArgs args
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- phases.  Every wavefront passes 2 + 2 KT barriers. ----
