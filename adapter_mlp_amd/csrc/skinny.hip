@@ -34,11 +34,15 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<
 // ---------------------------------------------------------------------------
 template <int NJ>
 struct RowProjCfg {
+  static constexpr int NW = 8;                  // wavefronts per block (one K step of 8 each)
   static constexpr int ZB = 32 * 512;          // Z bytes per slot
   static constexpr int BB = NJ * 16 * 512;     // Bt bytes per slot
   static constexpr int SB = ZB + BB;
   static constexpr int NST = NJ == 1 ? 6 : NJ == 2 ? 5 : NJ == 3 ? 4 : 3;
-  static constexpr int D = 4 + 2 * NJ;         // loads per wavefront and chunk
+  static constexpr int ZPW = 16 / NW;          // Z blocks per wavefront and chunk
+  static constexpr int BPW = 8 * NJ / NW;      // Bt blocks per wavefront and chunk
+  static constexpr int D = ZPW + BPW;          // loads per wavefront and chunk
+  static constexpr int KPW = 8 / NW;           // K steps per wavefront and chunk
 };
 
 template <int D, int K>
@@ -56,7 +60,7 @@ __device__ __forceinline__ void wait_steps_after(int after) {
 }
 
 template <int NJ>
-__global__ __launch_bounds__(256) void rowproj_bf16_kernel(const RowProjArgs a) {
+__global__ __launch_bounds__(RowProjCfg<NJ>::NW * 64) void rowproj_bf16_kernel(const RowProjArgs a) {
   using C = RowProjCfg<NJ>;
   __shared__ __attribute__((aligned(1024))) char ring[C::NST * C::SB];
   lds_char* const lds = (lds_char*)ring;
@@ -70,27 +74,27 @@ __global__ __launch_bounds__(256) void rowproj_bf16_kernel(const RowProjArgs a) 
   const i32x4 rz = rsrc_words(static_cast<const char*>(a.Z) + t0 * a.ldz * 2, rows * a.ldz * 2);
   const i32x4 rb = rsrc_words(a.Bt, (int64_t)a.R * a.ldb * 2);
 
-  // load blocks of this wavefront: Z blocks 4w..4w+3 (rows 2q, 2q+1), Bt
-  // blocks 2NJ w .. (rows 2q', 2q'+1); lane -> row q*2 + lane/32, chunk lane%32
+  // load blocks of this wavefront: Z blocks ZPW w .. (rows 2q, 2q+1), Bt
+  // blocks BPW w .. (rows 2q', 2q'+1); lane -> row q*2 + lane/32, chunk lane%32
   const int hrow = lane >> 5, pc = lane & 31;
-  uint32_t zoff[4], boff[2 * NJ];
+  uint32_t zoff[C::ZPW], boff[C::BPW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 2 * (4 * w + i) + hrow;
+  for (int i = 0; i < C::ZPW; ++i) {
+    const int row = 2 * (C::ZPW * w + i) + hrow;
     zoff[i] = (uint32_t)row * ldz2 + (uint32_t)((pc ^ (row & 15)) * 16);
   }
 #pragma unroll
-  for (int i = 0; i < 2 * NJ; ++i) {
-    const int row = 2 * (2 * NJ * w + i) + hrow;
+  for (int i = 0; i < C::BPW; ++i) {
+    const int row = 2 * (C::BPW * w + i) + hrow;
     boff[i] = (uint32_t)row * ldb2 + (uint32_t)((pc ^ (row & 15)) * 16);
   }
   auto issue = [&](int c, int slot) {
     const uint32_t base = lds_addr(lds) + slot * C::SB;
     const uint32_t soff = (uint32_t)c * 512;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(rz, zoff[i], base + (4 * w + i) * 1024, soff);
+    for (int i = 0; i < C::ZPW; ++i) dma16(rz, zoff[i], base + (C::ZPW * w + i) * 1024, soff);
 #pragma unroll
-    for (int i = 0; i < 2 * NJ; ++i) dma16(rb, boff[i], base + C::ZB + (2 * NJ * w + i) * 1024, soff);
+    for (int i = 0; i < C::BPW; ++i) dma16(rb, boff[i], base + C::ZB + (C::BPW * w + i) * 1024, soff);
   };
 
   f32x4 acc[2][NJ];
@@ -105,8 +109,8 @@ __global__ __launch_bounds__(256) void rowproj_bf16_kernel(const RowProjArgs a) 
     const lds_char* zs = lds + slot * C::SB;
     const lds_char* bs = zs + C::ZB;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int ks = 2 * w + i;
+    for (int i = 0; i < C::KPW; ++i) {
+      const int ks = C::KPW * w + i;
       if ((int64_t)c * 256 + ks * 32 >= a.K) continue;  // K tail (uniform)
       const int off = ((4 * ks + (lane >> 4)) ^ rl) * 16;
       bf16x8 za[2];
@@ -135,7 +139,7 @@ __global__ __launch_bounds__(256) void rowproj_bf16_kernel(const RowProjArgs a) 
   __syncthreads();
 
   // acc[mb][nb][v] = Out[t0 + 16 mb + 4 (lane >> 4) + v, 16 nb + lane % 16] (K share of wavefront w)
-  float* red = reinterpret_cast<float*>(ring);  // [4][32][16 NJ]
+  float* red = reinterpret_cast<float*>(ring);  // [NW][32][16 NJ]
   constexpr int RW = NJ * 16;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
@@ -145,13 +149,15 @@ __global__ __launch_bounds__(256) void rowproj_bf16_kernel(const RowProjArgs a) 
       for (int v = 0; v < 4; ++v) red[(w * 32 + mb * 16 + 4 * (lane >> 4) + v) * RW + nb * 16 + rl] = acc[mb][nb][v];
   __syncthreads();
   const int R2 = a.R2 > a.R ? a.R2 : a.R;
-  for (int e = tid; e < 32 * R2; e += 256) {
+  for (int e = tid; e < 32 * R2; e += C::NW * 64) {
     const int r = e / R2, j = e % R2;
     const int64_t t = t0 + r;
     if (t >= a.T) continue;
     float v = 0.0f;
-    if (j < a.R) v = ((red[(0 * 32 + r) * RW + j] + red[(1 * 32 + r) * RW + j]) + red[(2 * 32 + r) * RW + j]) +
-                     red[(3 * 32 + r) * RW + j];
+    if (j < a.R) {
+#pragma unroll
+      for (int q = 0; q < C::NW; ++q) v += red[(q * 32 + r) * RW + j];  // fixed order
+    }
     if (a.out1 && j < a.R) static_cast<uint16_t*>(a.out1)[t * a.ld1 + a.off1 + j] = (uint16_t)f2bf(v);
     if (a.out2) {
       const float sc = j < a.R ? a.scales[j / a.seg_w] : 0.0f;
@@ -199,7 +205,7 @@ struct ColProjCfg {
   static constexpr int PB = 32 * PW * 2;             // 1, 2 or 4 KB
   static constexpr int NPB = PB / 1024;              // P load blocks per step
   static constexpr int SB = ZB + PB;
-  static constexpr int NST = 6;
+  static constexpr int NST = 4;
 };
 
 template <int NJ>
@@ -394,10 +400,10 @@ hipError_t launch_rowproj(bool bf16, const RowProjArgs& a, hipStream_t st) {
   }
   const dim3 grid(nblk(a.T, 32));
   switch ((a.R + 15) / 16) {
-    case 1: hipLaunchKernelGGL(rowproj_bf16_kernel<1>, grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL(rowproj_bf16_kernel<2>, grid, dim3(256), 0, st, a); break;
-    case 3: hipLaunchKernelGGL(rowproj_bf16_kernel<3>, grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL(rowproj_bf16_kernel<4>, grid, dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL(rowproj_bf16_kernel<1>, grid, dim3(RowProjCfg<1>::NW * 64), 0, st, a); break;
+    case 2: hipLaunchKernelGGL(rowproj_bf16_kernel<2>, grid, dim3(RowProjCfg<2>::NW * 64), 0, st, a); break;
+    case 3: hipLaunchKernelGGL(rowproj_bf16_kernel<3>, grid, dim3(RowProjCfg<3>::NW * 64), 0, st, a); break;
+    default: hipLaunchKernelGGL(rowproj_bf16_kernel<4>, grid, dim3(RowProjCfg<4>::NW * 64), 0, st, a); break;
   }
   return hipGetLastError();
 }
