@@ -139,6 +139,47 @@ def pmc_summary(fetch_csv, write_csv, config_id):
     print(f"calibration: FETCH x{kf:.4f}, WRITE x{kw:.4f}")
 
 
+def trace_summary(stats_csv, bench_log, config_id):
+    """Per-kernel durations from a rocprofv3 --kernel-trace --stats run over
+    bench.py (its *_kernel_stats.csv) next to the bench line the same run
+    printed.  Writes profiles/<dominant family>_<workload>_kernel_trace.txt."""
+    import csv
+    import json
+    import re
+
+    from workload import CONFIGS
+    cfg = CONFIGS[config_id]
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [l for l in open(bench_log) if l.startswith("{")]
+    d = json.loads(lines[-1]) if lines else None
+
+    def short(n):
+        n = n.replace("lora::(anonymous namespace)::", "").replace("void ", "")
+        return re.sub(r"\(lora::\w+(, \w+)*\)$", "", n)[:70]
+
+    fam = d["roofline"]["kernel"] if d else "gemm"
+    path = os.path.join(ROOT, "profiles", f"{fam}_{workload_tag(cfg)}_kernel_trace.txt")
+    with open(path, "w") as f:
+        f.write(f"# rocprofv3 kernel trace summary, workload {cfg.note}\n")
+        f.write("# command (repository root on the GPU host; 3 warm-up + 10 timed steps):\n")
+        f.write("#   cd /tmp && export TMPDIR=/tmp\n")
+        f.write(f"#   rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o kt -- python3 <repo>/bench.py "
+                f"--config {config_id} --steps 10 --warmup 3 --no-cpu-baseline > kt.log\n")
+        f.write(f"#   python3 bench.py --config {config_id} --trace-summary <dir>/kt_kernel_stats.csv kt.log\n")
+        f.write(f"source_digest = {source_digest()}\n")
+        f.write("# durations in microseconds\n\n")
+        f.write(f"{'kernel':70s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}\n")
+        for r in rows:
+            f.write(f"{short(r['Name']):70s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.1f} "
+                    f"{float(r['MinNs']) / 1e3:10.1f} {float(r['MaxNs']) / 1e3:10.1f} {float(r['Percentage']):6.2f}\n")
+        if d:
+            f.write("\n# bench.py line of the same run (live HIP-event timing of the dominant kernel):\n")
+            f.write(f"#   ms_per_step = {d['ms_per_step']:.4f}, tokens/s = {d['value']:.0f}, "
+                    f"{fam} avg_launch_ms = {d['roofline']['avg_launch_ms']:.4f}, "
+                    f"achieved = {d['roofline']['achieved']:.1f} {d['roofline']['unit']}\n")
+    print(f"wrote {path}")
+
+
 def workload_tag(cfg):
     return {2: "llama3_8b_mlp", 3: "gemma_geglu_mlp", 4: "llama3_8b_qlora_mlp", 5: "llama3_8b_qkvo"}[cfg.cid]
 
@@ -287,6 +328,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU run: turn two rocprofv3 --pmc counter files into profiles/*_traffic.txt")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("STATS_CSV", "BENCH_LOG"),
+                    help="no GPU run: turn a rocprofv3 --kernel-trace --stats run into profiles/*_kernel_trace.txt")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run a plain fp32 elementwise copy (negation) of MIB MiB "
                          "three times, the known-size kernel that scales HBM byte counters")
@@ -294,9 +337,12 @@ def main():
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.config)
         return
+    if args.trace_summary:
+        trace_summary(args.trace_summary[0], args.trace_summary[1], args.config)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the fused LoRA path runs on a single MI355X here and "
-              "--gpus N with N > 1 is not supported (see the sharding notes in DESIGN.md).", file=sys.stderr)
+              "--gpus N with N > 1 is not supported.", file=sys.stderr)
         sys.exit(2)
 
     import torch
