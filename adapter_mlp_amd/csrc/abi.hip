@@ -174,8 +174,8 @@ void* offw(void* p, int64_t elems, const Ctx& c) { return static_cast<char*>(p) 
 
 hipError_t gemm_on(const Ctx& c, GemmArgs& g, hipStream_t st, int64_t lora_vcols) {
   g.lora_vcols = lora_vcols;
-  if (c.bf16 && !g.nf4 && g.RL > 0) {
-    // The dense bf16 kernel runs the LoRA term as one more 64-wide K segment:
+  if (c.bf16 && g.RL > 0) {
+    // The bf16 kernel runs the LoRA term as one more 64-wide K segment:
     // A = AL [M, 64], B = the packed adapter operand in the main operand's
     // orientation ([64, vcols] for NN, [vcols, 64] for NT), offset to each
     // region's / column group's first virtual column.
@@ -441,7 +441,7 @@ lora_status proj_forward(const Ctx& c, int64_t T, int64_t K, int64_t N, int64_t 
     pl.RL = (int)RL;
     pl.nparts = 1;
     pl.part[0] = part(o->B, N, 0, N, 0, (int)r, true);
-    pl.kmajor = (c.bf16 && o->nf4 == nullptr) ? 1 : 0;  // NN dense GEMM reads [RL, vcols]
+    pl.kmajor = c.bf16 ? 1 : 0;  // the bf16 NN GEMM reads [RL, vcols]
     LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, pl, st));
     g.AL = p.Us;
     g.ldal = RL;
@@ -581,7 +581,7 @@ lora_status lora_mlp_fwd(const lora_mlp_desc* d, const void* X, const lora_proj*
   pl.nparts = 2;
   pl.part[0] = part(gate->B, I, 0, I, 0, (int)r, true);
   pl.part[1] = part(up->B, I, I, I, (int)r, (int)r, true);
-  pl.kmajor = (c.bf16 && gate->nf4 == nullptr) ? 1 : 0;  // NN dense GEMM reads [RL, vcols]
+  pl.kmajor = c.bf16 ? 1 : 0;  // the bf16 NN GEMM reads [RL, vcols]
   LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, pl, st));
 
   // gate/up GEMM with the activation epilogue
@@ -631,7 +631,7 @@ lora_status lora_mlp_fwd(const lora_mlp_desc* d, const void* X, const lora_proj*
   pd.RL = (int)RLd;
   pd.nparts = 1;
   pd.part[0] = part(down->B, H, 0, H, 0, (int)r, true);
-  pd.kmajor = (c.bf16 && down->nf4 == nullptr) ? 1 : 0;  // NN dense GEMM reads [RL, vcols]
+  pd.kmajor = c.bf16 ? 1 : 0;  // the bf16 NN GEMM reads [RL, vcols]
   LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, pd, st));
 
   GemmArgs gd{};
@@ -863,7 +863,7 @@ lora_status lora_qkv_fwd(const lora_qkv_desc* d, const void* X, const lora_proj*
   pl.part[0] = part(q->B, Nq, 0, Nq, 0, (int)r, true);
   pl.part[1] = part(k->B, Nk, Nq, Nk, (int)r, (int)r, true);
   pl.part[2] = part(v->B, Nv, Nq + Nk, Nv, (int)(2 * r), (int)r, true);
-  pl.kmajor = (c.bf16 && q->nf4 == nullptr) ? 1 : 0;  // NN dense GEMM reads [RL, vcols]
+  pl.kmajor = c.bf16 ? 1 : 0;  // the bf16 NN GEMM reads [RL, vcols]
   LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, pl, st));
 
   GemmArgs g{};

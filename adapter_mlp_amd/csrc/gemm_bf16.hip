@@ -1,6 +1,7 @@
-// bf16 GEMM core for gfx950: 256x256x64 block tiles, 4 wavefronts (2 x 2),
-// each wavefront a 128x128 sub-tile of v_mfma_f32_32x32x16_bf16 products with
-// fp32 accumulation, operands staged through double-buffered LDS.
+// bf16 GEMM core for gfx950: 256x256x64 block tiles, 8 wavefronts in two
+// groups that alternate between MFMA clusters and LDS fragment reads,
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulation, operands moved from global
+// memory into LDS without passing through registers.
 //
 // What it computes (the base projections and the adapter term of the LoRA
 // projections, "LoRA Optimizations" section "Custom autograd functions"; the
@@ -23,20 +24,16 @@
 // each lane ends with 4 consecutive output columns of one row, and the gated
 // activation finds e and g of the same element in the same lane.
 //
-// Operands are read with buffer loads: the descriptor base advances by one K
-// tile per step (scalar work only) and rows past the end of a matrix read as
+// Operands are read with buffer loads: rows past the end of a matrix read as
 // zero, which covers ragged M and N tiles without clamping.
 //
-// NN weight tiles (forward) are transposed on the way into LDS: each thread
-// loads an 8x8 bf16 sub-block (8 rows of 16 bytes) and transposes it in
-// registers with v_perm_b32 before writing 8 K-contiguous 16-byte rows.
-//
-// NF4 weights are unpacked in registers on the same path: a 32-bit load
-// holds 8 codes of one 64-element block; the block's absmax is rebuilt from
-// its int8 code, its scaler block's fp32 scale and the global mean, each code
-// looks up its level, and fl32(level * absmax) is rounded to bf16 before the
-// 16 bytes go to LDS ("loralei" README, section "Use": unpack and
-// double-scale reconstruction fused into the matmul).
+// NF4 base weights (QLoRA) are unpacked inside the same loop.  Per 64-element
+// block, the absmax is rebuilt from its int8 code, its scaler block's fp32
+// scale and the global mean; the 16 products fl32(level * absmax) are rounded
+// to bf16 once into a register table, and every 4-bit code is looked up in it
+// with byte permutes.  The bf16 tile then goes to LDS in the dense layout
+// ("loralei" README, section "Use": unpack and double-scale reconstruction
+// fused into the matmul).
 #include <type_traits>
 
 #include "common.hpp"
@@ -46,33 +43,12 @@
 namespace lora {
 namespace {
 
-constexpr int BM = 256, BK = 64, NTH = 256;
-constexpr int TILE_CHUNKS = 256 * 8;  // 16-byte chunks per 256 x 64 bf16 tile
-constexpr int OOB = 0x7ffffff0;       // a buffer offset past every operand: loads return 0
+constexpr int BM = 256, BK = 64;
 
 // XOR swizzle of the 16-byte chunk index inside a 128-byte LDS row.  Rows read
 // together by an MFMA fragment load (8 consecutive rows) and rows written
-// together by the transposing store land in different banks.
+// together land in different banks.
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
-
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-// Buffer descriptor over [p, p + bytes) (bytes < 2^31); every input is uniform.
-__device__ __forceinline__ rsrc_t rsrc(const void* p, int64_t bytes) {
-  if (bytes < 0) bytes = 0;
-  const int64_t base = uni64(reinterpret_cast<int64_t>(p));
-  const int n = __builtin_amdgcn_readfirstlane((int)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), (short)0, n, 0x00020000);
-}
-__device__ __forceinline__ u32x4 bload16(rsrc_t r, int off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ __forceinline__ uint32_t bload4(rsrc_t r, int off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-}
-__device__ __forceinline__ int bload1s(rsrc_t r, int off) {
-  return (int)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
-}
 
 // Wavefront-local LDS hand-off between lanes (each wavefront stages into its
 // own LDS region in the epilogue, so no block barrier is needed).
@@ -100,41 +76,6 @@ __device__ __forceinline__ void tile_coords(int bid, int nb, int ntm, int ntn, i
   tn = in_g / gsize;
 }
 
-// Tile-local weight row nl (0..255) -> output column.  Dual tiles hold
-// [gate 64 | up 64] for wavefront column 0, then the same for column 1.
-template <bool DUAL>
-__device__ __forceinline__ int64_t colmap(int nl, int64_t tnl) {
-  if constexpr (DUAL) return tnl * 128 + (int64_t)(nl >> 7) * 64 + (nl & 63);
-  else return tnl * 256 + nl;
-}
-
-// 8x8 bf16 transpose: r[i] holds row i (8 values, 2 per dword); o[j] receives
-// column j (the 8 row values, 2 per dword).
-__device__ __forceinline__ void transpose8x8(const u32x4 (&r)[8], u32x4 (&o)[8]) {
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t lo = r[2 * q][p], hi = r[2 * q + 1][p];
-      o[2 * p][q] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-      o[2 * p + 1][q] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
-    }
-  }
-}
-
-// 8 NF4 codes (one dword, element 2q in the high nibble of byte q) -> 8 bf16.
-__device__ __forceinline__ u32x4 nf4_decode8(uint32_t w, float absmax, const float* lut) {
-  u32x4 o;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t byte = (w >> (8 * q)) & 0xffu;
-    const float v0 = __fmul_rn(lut[byte >> 4], absmax);
-    const float v1 = __fmul_rn(lut[byte & 0xfu], absmax);
-    o[q] = pack_bf2(v0, v1);
-  }
-  return o;
-}
-
 // Calls f(integral_constant<int, 0..3>) so accumulator indices stay
 // compile-time constants (a runtime index would move the accumulators to
 // scratch memory).
@@ -145,13 +86,6 @@ __device__ __forceinline__ void for4(F&& f) {
   f(std::integral_constant<int, 2>{});
   f(std::integral_constant<int, 3>{});
 }
-
-struct Stage {
-  u32x4 a[8];
-  u32x4 b[8];   // dense rows, or b[i][0] = NF4 code dword
-  float bs2[8];
-  int bq8[8];
-};
 
 // Epilogue: each wavefront stages its results (WN output tile columns x 128
 // rows; accumulator block i covers tile columns 32 i.., block j rows 32 j..)
@@ -318,253 +252,47 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
   }
 }
 
-template <bool DUAL, int EPI>
-__device__ __forceinline__ void run_epilogue(f32x16 (&acc)[4][4], u32x4* smem, const GemmArgs& args, int reg,
-                                             int64_t m0, int64_t tnl, int64_t NR, int64_t M, int wave, int lane) {
-  const int wm = wave >> 1, wn = wave & 1;
-  char* wstage = reinterpret_cast<char*>(smem) + wave * epi_stage_bytes<128, EPI>();
-  run_epilogue_w<128, DUAL, EPI>(acc, wstage, args, reg, m0 + wm * 128, colmap<DUAL>(wn * 128, tnl), NR, M, lane);
-}
-
-// NF4 weights: the previous loop (register prefetch of one tile, LoRA tile
-// through its own path), kept while the dense kernel is tuned.
-template <int BKIND, bool NF4, bool DUAL, int EPI>
-__global__ __launch_bounds__(NTH, 1) void gemm_nf4_kernel(const GemmArgs args) {
-  __shared__ u32x4 smem[4 * TILE_CHUNKS];  // A: 2 buffers, B: 2 buffers; reused by the epilogue
-  __shared__ float s_lut[16];
-  u32x4* const sA = smem;
-  u32x4* const sB = smem + 2 * TILE_CHUNKS;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
-
-  if (NF4 && tid < 16) {
-    const float lv[16] = LORA_NF4_LEVELS_INIT;
-    s_lut[tid] = lv[tid];
+// NF4 level table of one block: the 16 products fl32(level_c * absmax)
+// rounded to bf16, kept as two byte planes of four dwords (entry c is byte
+// c % 4 of dword c / 4 of each plane).
+struct Nf4Planes {
+  uint32_t lo[4], hi[4];
+};
+__device__ __forceinline__ Nf4Planes nf4_planes(float absmax) {
+  const float lv[16] = LORA_NF4_LEVELS_INIT;
+  Nf4Planes p;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t a = pack_bf2(__fmul_rn(lv[4 * q], absmax), __fmul_rn(lv[4 * q + 1], absmax));
+    const uint32_t b = pack_bf2(__fmul_rn(lv[4 * q + 2], absmax), __fmul_rn(lv[4 * q + 3], absmax));
+    p.lo[q] = __builtin_amdgcn_perm(b, a, 0x06040200u);
+    p.hi[q] = __builtin_amdgcn_perm(b, a, 0x07050301u);
   }
-
-  // Tile coordinates are uniform; keep them (and all that derives from them)
-  // in scalar registers so buffer descriptors stay scalar.
-  int tm, tn;
-  tile_coords((int)blockIdx.x, (int)gridDim.x, (int)args.ntile_m, (int)args.ntile_n, tm, tn);
-  tm = __builtin_amdgcn_readfirstlane(tm);
-  tn = __builtin_amdgcn_readfirstlane(tn);
-  int reg = 0;
-#pragma unroll
-  for (int p = 1; p < 3; ++p)
-    if (p < args.nreg && tn >= args.reg[p].tile0) reg = p;
-  reg = __builtin_amdgcn_readfirstlane(reg);
-  const int64_t tnl = uni64(tn - args.reg[reg].tile0);
-  const int64_t NR = uni64(args.reg[reg].N);
-  const int64_t M = args.M;
-  const int64_t m0 = (int64_t)tm * BM;
-
-  // Per-thread load geometry.
-  //  A and NT weights: 16-byte chunk a_c of rows a_r0 + 32 i.
-  //  NN weights: wavefront w owns tile columns 64w..64w+63 (one column group
-  //  of a dual tile); lane = 8 k8 + n8 loads K rows 8 k8..+7, columns 8 n8..+7.
-  const int a_c = tid & 7;
-  const int a_r0 = tid >> 3;
-  const int nn_n8 = lane & 7, nn_k8 = lane >> 3;
-  const int nn_cg = DUAL ? (wave & 1) : 0;
-  const int64_t nn_col = colmap<DUAL>(wave * 64 + nn_n8 * 8, tnl);
-
-  int64_t ktiles = 0;
-  for (int s = 0; s < args.nseg; ++s) ktiles += args.seg[s].K / BK;
-  const bool has_lora = args.RL > 0;
-  const int64_t KT = ktiles + (has_lora ? 1 : 0);
-
-  // Segment state (uniform): current segment and the K offset inside it.
-  int seg = 0;
-  int64_t k0 = 0;
-  int a_off[8];  // byte offsets of this thread's 8 A rows (OOB past M)
-  int b_off[8];  // dense: byte offsets of its 8 weight rows; NF4: element index
-  auto seg_setup = [&](int s) {
-    const GemmSeg& S = args.seg[s];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t m = m0 + a_r0 + 32 * i;
-      a_off[i] = m < M ? (int)((m * S.lda + a_c * 8) * 2) : OOB;
-    }
-    if constexpr (BKIND == B_NT) {
-      const BSrc& B = S.b[reg][0];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t n = colmap<DUAL>(a_r0 + 32 * i, tnl);
-        if constexpr (NF4) b_off[i] = n < NR ? (int)(n * B.wcols + a_c * 8) : OOB;
-        else b_off[i] = n < NR ? (int)((n * B.ld + a_c * 8) * 2) : OOB;
-      }
-    } else {
-      const BSrc& B = S.b[reg][nn_cg];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if constexpr (NF4) b_off[i] = (int)((nn_k8 * 8 + i) * B.wcols + nn_col);
-        else b_off[i] = (int)(((nn_k8 * 8 + i) * B.ld + nn_col) * 2);
-      }
-    }
-  };
-
-  // --- global -> registers for one main K tile ---------------------------------
-  auto load_main = [&](Stage& st) {
-    const GemmSeg& S = args.seg[seg];
-    const rsrc_t ra = rsrc(static_cast<const char*>(S.A) + k0 * 2, M * S.lda * 2 - k0 * 2);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) st.a[i] = bload16(ra, a_off[i]);
-    const BSrc& B = S.b[reg][BKIND == B_NN ? nn_cg : 0];
-    if constexpr (NF4) {
-      // weight rows x cols = (NT: N x K_s, NN: K_s x N); tile start in elements
-      const int64_t numel = (BKIND == B_NT ? NR : S.K) * B.wcols;
-      const int64_t kofs = BKIND == B_NT ? k0 : k0 * B.wcols;
-      const rsrc_t rc = rsrc(B.codes + kofs / 2, numel / 2 - kofs / 2);
-      const rsrc_t rq = rsrc(B.q8, numel / 64);
-      const rsrc_t rs = rsrc(B.s2, (numel / NF4_GROUP) * 4);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const bool ok = b_off[i] != OOB;
-        const uint32_t flat = (uint32_t)b_off[i] + (uint32_t)kofs;
-        st.b[i][0] = bload4(rc, ok ? (int)((uint32_t)b_off[i] >> 1) : OOB);
-        st.bq8[i] = bload1s(rq, ok ? (int)(flat >> 6) : OOB);
-        st.bs2[i] = __uint_as_float(bload4(rs, ok ? (int)((flat >> 14) << 2) : OOB));
-      }
-    } else {
-      const int64_t total = BKIND == B_NT ? NR * B.ld * 2 : ((S.K - 1) * B.ld + NR) * 2;
-      const int64_t adv = (BKIND == B_NT ? k0 : k0 * B.ld) * 2;
-      const rsrc_t rb = rsrc(static_cast<const char*>(B.p) + adv, total - adv);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) st.b[i] = bload16(rb, b_off[i]);
-    }
-  };
-
-  // NF4 codes -> bf16 (at LDS-store time, after the loads have landed).
-  auto decode_nf4 = [&](Stage& st) {
-    if constexpr (NF4) {
-      const float mu = *args.seg[seg].b[reg][BKIND == B_NN ? nn_cg : 0].mu;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        st.b[i] = nf4_decode8(st.b[i][0], nf4_absmax((int8_t)st.bq8[i], st.bs2[i], mu), s_lut);
-    } else {
-      (void)st;
-    }
-  };
-
-  // --- the LoRA tile: A_L [M, RL] and BLt [vcols, RL], both K-contiguous -----
-  auto load_lora = [&](Stage& st) {
-    const rsrc_t ra = rsrc(args.AL, M * args.ldal * 2);
-    const rsrc_t rb = rsrc(args.BLt, args.lora_vcols * args.ldbl * 2);
-    const bool chunk_ok = a_c < (args.RL >> 3);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t m = m0 + a_r0 + 32 * i;
-      st.a[i] = bload16(ra, (chunk_ok && m < M) ? (int)((m * args.ldal + a_c * 8) * 2) : OOB);
-      const int64_t n = colmap<DUAL>(a_r0 + 32 * i, tnl);
-      const int64_t v = args.reg[reg].vcol0[DUAL ? ((i >> 1) & 1) : 0] + n;
-      st.b[i] = bload16(rb, (chunk_ok && n < NR) ? (int)((v * args.ldbl + a_c * 8) * 2) : OOB);
-    }
-  };
-
-  // --- registers -> LDS ---------------------------------------------------------
-  auto store_tile = [&](const Stage& st, int buf, bool kcontig_b) {
-    u32x4* dA = sA + buf * TILE_CHUNKS;
-    u32x4* dB = sB + buf * TILE_CHUNKS;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = a_r0 + 32 * i;
-      dA[row * 8 + (a_c ^ swz(row))] = st.a[i];
-    }
-    if (kcontig_b) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = a_r0 + 32 * i;
-        dB[row * 8 + (a_c ^ swz(row))] = st.b[i];
-      }
-    } else {
-      u32x4 cols[8];
-      transpose8x8(st.b, cols);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int row = wave * 64 + nn_n8 * 8 + j;
-        dB[row * 8 + (nn_k8 ^ swz(row))] = cols[j];
-      }
-    }
-  };
-
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-
-  // 4 K-steps of 16 over one LDS buffer; fragments of step s+1 are read while
-  // the MFMAs of step s issue.
-  auto compute = [&](int buf) {
-    const u32x4* tA = sA + buf * TILE_CHUNKS;
-    const u32x4* tB = sB + buf * TILE_CHUNKS;
-    bf16x8 fa[2][4], fb[2][4];
-    auto frags = [&](int ks, bf16x8 (&xa)[4], bf16x8 (&xb)[4]) {
-      const int c = ks * 2 + (lane >> 5);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rn = wn * 128 + i * 32 + (lane & 31);
-        xa[i] = __builtin_bit_cast(bf16x8, tB[rn * 8 + (c ^ swz(rn))]);
-        const int rm = wm * 128 + i * 32 + (lane & 31);
-        xb[i] = __builtin_bit_cast(bf16x8, tA[rm * 8 + (c ^ swz(rm))]);
-      }
-    };
-    frags(0, fa[0], fb[0]);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (ks < 3) frags(ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][i], fb[ks & 1][j], acc[i][j], 0, 0, 0);
-    }
-  };
-
-  auto advance = [&]() {
-    k0 += BK;
-    if (k0 >= args.seg[seg].K && seg + 1 < args.nseg) {
-      ++seg;
-      k0 = 0;
-      seg_setup(seg);
-    }
-  };
-
-  // --- main loop: prefetch tile t+1 into registers while tile t computes ---
-  Stage st;
-  seg_setup(0);
-  load_main(st);
-  __syncthreads();  // s_lut ready
-  decode_nf4(st);
-  store_tile(st, 0, BKIND == B_NT);
-  __syncthreads();
-
-  for (int64_t t = 0; t < KT; ++t) {
-    const int buf = (int)(t & 1);
-    const bool has_next = t + 1 < KT;
-    const bool next_lora = has_lora && t + 1 == ktiles;
-    if (has_next) {
-      if (next_lora) {
-        load_lora(st);
-      } else {
-        advance();
-        load_main(st);
-      }
-    }
-    compute(buf);
-    if (has_next) {
-      if (!next_lora) decode_nf4(st);
-      store_tile(st, buf ^ 1, next_lora || BKIND == B_NT);
-    }
-    __syncthreads();
-  }
-
-  run_epilogue<DUAL, EPI>(acc, smem, args, reg, m0, tnl, NR, M, wave, lane);
+  return p;
 }
-
+// Byte k of the result is plane entry (code k): sel holds the codes' low 3
+// bits, fsel = k + 4 * (bit 3 of code k) picks entries 0-7 or 8-15.
+__device__ __forceinline__ uint32_t nf4_lookup(const uint32_t (&pl)[4], uint32_t sel, uint32_t fsel) {
+  const uint32_t a = __builtin_amdgcn_perm(pl[1], pl[0], sel);
+  const uint32_t b = __builtin_amdgcn_perm(pl[3], pl[2], sel);
+  return __builtin_amdgcn_perm(b, a, fsel);
+}
+// 8 codes of one dword (element 2j in the high nibble of byte j, element
+// 2j + 1 in its low nibble) -> 8 bf16 in element order.
+__device__ __forceinline__ u32x4 nf4_decode8(uint32_t w, const Nf4Planes& p) {
+  const uint32_t se = (w >> 4) & 0x07070707u, fe = ((w >> 5) & 0x04040404u) | 0x03020100u;
+  const uint32_t so = w & 0x07070707u, fo = ((w >> 1) & 0x04040404u) | 0x03020100u;
+  const uint32_t le = nf4_lookup(p.lo, se, fe), he = nf4_lookup(p.hi, se, fe);
+  const uint32_t lo = nf4_lookup(p.lo, so, fo), ho = nf4_lookup(p.hi, so, fo);
+  const uint32_t e01 = __builtin_amdgcn_perm(he, le, 0x05010400u), e23 = __builtin_amdgcn_perm(he, le, 0x07030602u);
+  const uint32_t o01 = __builtin_amdgcn_perm(ho, lo, 0x05010400u), o23 = __builtin_amdgcn_perm(ho, lo, 0x07030602u);
+  u32x4 r;
+  r[0] = __builtin_amdgcn_perm(o01, e01, 0x05040100u);
+  r[1] = __builtin_amdgcn_perm(o01, e01, 0x07060302u);
+  r[2] = __builtin_amdgcn_perm(o23, e23, 0x05040100u);
+  r[3] = __builtin_amdgcn_perm(o23, e23, 0x07060302u);
+  return r;
+}
 
 // ---------------------------------------------------------------------------
 // Dense weights.  8 wavefronts in two groups of 4, one wavefront of each
@@ -594,21 +322,36 @@ __global__ __launch_bounds__(NTH, 1) void gemm_nf4_kernel(const GemmArgs args) {
 //                    4 values of column i that lanes 16 g + 4 j + i / 4 point
 //                    at (j = 0..3), i.e. the K-contiguous MFMA operand.
 // ---------------------------------------------------------------------------
+//
+// NF4 weights.  The weight group loads, per K step, the packed codes (8 KB)
+// and for each of the tile's 256 blocks the dword holding its int8 scale code
+// and its fp32 second-level scale (1 KB each) into a 3-slot code ring, three
+// steps ahead.  Both groups unpack, during their MFMA clusters, half of every
+// block each into a 2-slot bf16 weight ring with the dense layout: group 1
+// the upper 32 elements of step t+2 in Y(t), group 0 the lower 32 elements of
+// step t+1 in X(t).  A weight slot is rewritten only after both groups have
+// read it, so two slots suffice, and 30 KB of code ring fit beside them.  The
+// adapter K tile is dense and is loaded like a dense weight tile.
+// ---------------------------------------------------------------------------
 constexpr int NTH8 = 512;
 constexpr int SLOT_BYTES = 32768;
-constexpr int A_SLOTS = 2, W_SLOTS = 3;
+constexpr int A_SLOTS = 2;
 constexpr int W_RING = A_SLOTS * SLOT_BYTES;  // weight ring after the activation ring
-constexpr int LDS_BYTES = (A_SLOTS + W_SLOTS) * SLOT_BYTES;
+constexpr int LDS_BYTES = 5 * SLOT_BYTES;     // dense: 3 weight slots; NF4: 2 + code ring
 constexpr int HALF_BYTES = 16384;
+constexpr int CODE_RING = W_RING + 2 * SLOT_BYTES;
+constexpr int CODE_SLOT = 10240;  // codes 8 KB | scale-code dwords 1 KB | fp32 scales 1 KB
+static_assert(CODE_RING + 3 * CODE_SLOT <= LDS_BYTES, "NF4 code ring exceeds LDS");
 
-template <int BKIND, bool DUAL, int EPI>
-__global__ __launch_bounds__(NTH8, 1) void gemm_dense_kernel(const GemmArgs args) {
+template <int BKIND, bool DUAL, int EPI, bool NF4>
+__global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   static_assert(!(DUAL && BKIND == B_NT), "gate/up tiles read forward (NN) weights");
   __shared__ __attribute__((aligned(1024))) char smem_raw[LDS_BYTES];
   lds_char* const lds = (lds_char*)smem_raw;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  const int lane_id = lane;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
   const int wm = wave >> 2, wn = wave & 3;                    // wm: the group
 
@@ -626,8 +369,12 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_dense_kernel(const GemmArgs args
   const int64_t M = args.M;
   const int64_t m0 = (int64_t)tm * BM;
 
-  int KT = 0;
-  for (int s = 0; s < args.nseg; ++s) KT += (int)(args.seg[s].K / BK);
+  int KT = 0, KN = 0;  // all K steps; NF4 steps (the NF4 segments come first)
+  for (int s = 0; s < args.nseg; ++s) {
+    const int k = (int)(args.seg[s].K / BK);
+    KT += k;
+    if (NF4 && args.seg[s].b[reg][0].codes != nullptr) KN += k;
+  }
 
   // ---- loads: 8 blocks of 1 KB per wavefront and step ----
   // K-contiguous block q = 8 wn + i holds rows 8 q + lane / 8; its row r has
@@ -692,6 +439,101 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_dense_kernel(const GemmArgs args
       for (int i = 0; i < 8; ++i) dma16(rb, base, dst + i * 1024, (uint32_t)(4 * i) * ld2);
     }
     advance(S);
+  };
+
+  // ---- NF4: code staging and unpacking ----
+  // Block j (0..63) of wavefront column wn; its first element sits at
+  //   NN: weight row k0 + 32 (wn & 1) + j / 2, column c0 + 64 (j & 1)
+  //       (c0: first column of the tile's half wn / 2),
+  //   NT: weight row (= output column) 256 tnl + 64 wn + j, column k0.
+  // Returns its flat element index, or a value past every NF4 array for
+  // columns (NN) or rows (NT) outside the region, so its loads read zero.
+  auto nf4_flat = [&](const BSrc& B, int k0, int j) -> uint32_t {
+    const int wcols = (int)B.wcols;
+    if constexpr (BKIND == B_NN) {
+      const int col = (DUAL ? (int)tnl * 128 : (int)tnl * 256 + 128 * (wn >> 1)) + 64 * (j & 1);
+      const int row = k0 + 32 * (wn & 1) + (j >> 1);
+      return col < (int)NR ? (uint32_t)row * (uint32_t)wcols + (uint32_t)col : 0xffffff80u;
+    } else {
+      const int row = (int)tnl * 256 + 64 * wn + j;
+      return row < (int)NR ? (uint32_t)row * (uint32_t)wcols + (uint32_t)k0 : 0xffffff80u;
+    }
+  };
+  auto nf4_src = [&](const GemmSeg& S) -> const BSrc& { return S.b[reg][(BKIND == B_NN && DUAL) ? (wn >> 1) : 0]; };
+  // group 1: codes and scales of the next NF4 step into code slot `slot`
+  auto issue_codes = [&](int slot) {
+    const GemmSeg& S = args.seg[lseg];
+    const BSrc& B = nf4_src(S);
+    const int64_t numel = (BKIND == B_NN ? S.K : NR) * B.wcols;
+    const i32x4 rc = rsrc_words(B.codes, numel / 2);
+    const i32x4 rq = rsrc_words(B.q8, numel / 64);
+    const i32x4 rs = rsrc_words(B.s2, numel / NF4_GROUP * 4);
+    const uint32_t cs = lds_addr(lds) + CODE_RING + slot * CODE_SLOT;
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    // codes of block b at cs + 32 b: lane l of load j takes half l & 1 of block 64 wn + 32 j + l / 2
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t f = nf4_flat(B, (int)lk0, 32 * j + (l >> 1));
+      dma16(rc, (f >> 1) + 16 * (l & 1), cs + 2048 * wn + 1024 * j);
+    }
+    // lane l: block 64 wn + l; the aligned dword holding its scale code, and its fp32 scale
+    const uint32_t f = nf4_flat(B, (int)lk0, l);
+    dma4(rq, (f >> 6) & ~3u, cs + 8192 + 256 * wn);
+    dma4(rs, (f >> 14) << 2, cs + 9216 + 256 * wn);
+    advance(S);
+  };
+  // each group walks the NF4 steps it unpacks with a cursor of its own
+  int dseg = 0, dk0 = 0;
+  // unpack half h (elements 32 h .. 32 h + 31) of block 64 wn + lane from code
+  // slot cslot into weight slot wslot
+  auto unpack = [&](int cslot, int wslot, int h) {
+    const GemmSeg& S = args.seg[dseg];
+    const BSrc& B = nf4_src(S);
+    // uniform: a scalar load (a vector load would make the compiler wait for
+    // the global -> LDS loads in flight)
+    const float mu = *(const __attribute__((address_space(4))) float*)(uintptr_t)B.mu;
+    const lds_char* cs = lds + CODE_RING + cslot * CODE_SLOT;
+    // opaque copy: keeps the per-lane terms below from being hoisted out of
+    // the K loop, where they would stay live through the read phases
+    int lane = lane_id;
+    asm volatile("" : "+v"(lane));
+    const int b = 64 * wn + lane;
+    const u32x4 w = lds_read16(cs + 32 * b + 16 * h);
+    const uint32_t q8w = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(cs + 8192 + 4 * b);
+    const float s2 = *reinterpret_cast<const __attribute__((address_space(3))) float*>(cs + 9216 + 4 * b);
+    // byte of the scale code inside its aligned dword: block index mod 4
+    // (block index = (row wcols + col) / 64 with col a multiple of 64)
+    uint32_t qb;
+    if constexpr (BKIND == B_NN) {
+      const uint32_t row = (uint32_t)(dk0 + 32 * (wn & 1)) + (uint32_t)(lane >> 1);
+      qb = row * (uint32_t)(B.wcols >> 6) + (uint32_t)(lane & 1) +
+           (uint32_t)(DUAL ? tnl * 2 : tnl * 4 + 2 * (wn >> 1));
+    } else {
+      qb = (uint32_t)((int)tnl * 256 + 64 * wn + lane) * (uint32_t)(B.wcols >> 6) + (uint32_t)(dk0 >> 6);
+    }
+    const int8_t q8 = (int8_t)(q8w >> (8 * (qb & 3)));
+    const Nf4Planes pl = nf4_planes(nf4_absmax(q8, s2, mu));
+    lds_char* const wt = lds + W_RING + wslot * SLOT_BYTES;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const u32x4 v = nf4_decode8(w[d], pl);
+      int off;
+      if constexpr (BKIND == B_NN) {
+        const int k = 32 * (wn & 1) + (lane >> 1);
+        const int c = 8 * (lane & 1) + 4 * h + d;
+        off = (wn >> 1) * HALF_BYTES + k * 256 + ((c ^ (4 * (k & 3))) << 4);
+      } else {
+        const int c = 4 * h + d;
+        off = b * 128 + ((c ^ swz(b)) << 4);
+      }
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(wt + off) = v;
+    }
+    dk0 += BK;
+    if (dk0 >= (int)S.K) {
+      ++dseg;
+      dk0 = 0;
+    }
   };
 
   // ---- fragment reads ----
@@ -777,50 +619,123 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_dense_kernel(const GemmArgs args
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
   };
-  if (wm == 0) {
-    issue_a(0);
-    if (KT > 1) {
-      issue_a(1);
-      __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): A 0 is in
-    } else {
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-    }
-    phase_end();
-    read(0, 0);
-    phase_end();
-    for (int t = 0; t < KT; ++t) {
-      mma();
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): A t+1 is in
-      phase_end();
-      if (t + 2 < KT) issue_a(t & 1);
-      if (t + 1 < KT) read((t + 1) & 1, (t + 1) % 3);
-      phase_end();
-    }
-  } else {
-    issue_w(0);
-    if (KT > 1) {
-      issue_w(1);
-      __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): W 0 is in
-    } else {
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-    }
-    phase_end();
-    phase_end();
-    int ws = 0;  // weight slot of step t
-    for (int t = 0; t < KT; ++t) {
-      const int ws2 = ws == 0 ? 2 : ws - 1;  // (t + 2) % 3
-      if (t + 2 < KT) {
-        issue_w(ws2);
-        read(t & 1, ws);
-        __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): W t+1 is in (W t+2 may still fly)
+  if constexpr (!NF4) {
+    if (wm == 0) {
+      issue_a(0);
+      if (KT > 1) {
+        issue_a(1);
+        __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): A 0 is in
       } else {
-        read(t & 1, ws);
         __builtin_amdgcn_s_waitcnt(0x0F70);
       }
       phase_end();
-      mma();
+      read(0, 0);
       phase_end();
-      ws = ws == 2 ? 0 : ws + 1;
+      for (int t = 0; t < KT; ++t) {
+        mma();
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): A t+1 is in
+        phase_end();
+        if (t + 2 < KT) issue_a(t & 1);
+        if (t + 1 < KT) read((t + 1) & 1, (t + 1) % 3);
+        phase_end();
+      }
+    } else {
+      issue_w(0);
+      if (KT > 1) {
+        issue_w(1);
+        __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): W 0 is in
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+      }
+      phase_end();
+      phase_end();
+      int ws = 0;  // weight slot of step t
+      for (int t = 0; t < KT; ++t) {
+        const int ws2 = ws == 0 ? 2 : ws - 1;  // (t + 2) % 3
+        if (t + 2 < KT) {
+          issue_w(ws2);
+          read(t & 1, ws);
+          __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): W t+1 is in (W t+2 may still fly)
+        } else {
+          read(t & 1, ws);
+          __builtin_amdgcn_s_waitcnt(0x0F70);
+        }
+        phase_end();
+        mma();
+        phase_end();
+        ws = ws == 2 ? 0 : ws + 1;
+      }
+    }
+  } else {
+    // ---- NF4 phases (steps t < KN unpacked, the adapter step t = KN loaded) ----
+    //   P1  g0 loads A 0, 1             g1 loads codes 0, 1, 2, waits for codes 0   | barrier
+    //   P2  g0 unpacks W 0 (lower half)  g1 unpacks W 0 (upper), waits for codes 1
+    //       g0 waits for A 0                                                         | barrier
+    //   P3  g0 reads step 0              g1 unpacks W 1 (upper) or loads the adapter W 1 | barrier
+    //   X(t)  g0 MFMA t, unpacks W t+1 (lower), waits for A t+1
+    //         g1 loads codes t+3, reads step t, waits for codes t+2 (and adapter W)  | barrier
+    //   Y(t)  g0 loads A t+2, reads step t+1
+    //         g1 MFMA t, unpacks W t+2 (upper) or loads the adapter W t+2           | barrier
+    // Weight slot of step t: t & 1; code slot: t % 3.
+    const bool lora_step = KT > KN;  // the last step is the dense adapter tile
+    if (wm == 0) {
+      issue_a(0);
+      if (KT > 1) issue_a(1);
+      phase_end();
+      unpack(0, 0, 0);
+      if (KT > 1) wait_vmcnt<8>();
+      else wait_vmcnt<0>();
+      phase_end();
+      read(0, 0);
+      phase_end();
+      int cs1 = 1;  // code slot of step t + 1
+      for (int t = 0; t < KT; ++t) {
+        mma();
+        if (t + 1 < KN) unpack(cs1, (t + 1) & 1, 0);
+        wait_vmcnt<0>();  // A t+1 is in
+        phase_end();
+        if (t + 2 < KT) issue_a(t & 1);
+        if (t + 1 < KT) read((t + 1) & 1, (t + 1) & 1);
+        phase_end();
+        cs1 = cs1 == 2 ? 0 : cs1 + 1;
+      }
+    } else {
+      issue_codes(0);
+      if (KN > 1) issue_codes(1);
+      if (KN > 2) {
+        issue_codes(2);
+        wait_vmcnt<8>();
+      } else if (KN > 1) {
+        wait_vmcnt<4>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      phase_end();
+      unpack(0, 0, 1);
+      if (KN > 2) wait_vmcnt<4>();
+      else wait_vmcnt<0>();
+      phase_end();
+      if (KN > 1) unpack(1, 1, 1);
+      else if (lora_step) issue_w(1);
+      phase_end();
+      int cs0 = 0;  // code slot of step t (= that of step t + 3)
+      for (int t = 0; t < KT; ++t) {
+        const int cs2 = cs0 == 0 ? 2 : cs0 - 1;  // (t + 2) % 3
+        if (t + 3 < KN) {
+          issue_codes(cs0);
+          read(t & 1, t & 1);
+          wait_vmcnt<4>();  // codes t+2 are in (codes t+3 may still fly)
+        } else {
+          read(t & 1, t & 1);
+          wait_vmcnt<0>();
+        }
+        phase_end();
+        mma();
+        if (t + 2 < KN) unpack(cs2, t & 1, 1);
+        else if (lora_step && t + 2 == KN) issue_w(t & 1);
+        phase_end();
+        cs0 = cs0 == 2 ? 0 : cs0 + 1;
+      }
     }
   }
 
@@ -833,20 +748,19 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_dense_kernel(const GemmArgs args
   run_epilogue_w<64, DUAL, EPI>(acc, wstage, args, reg, mw, nbase, NR, M, lane);
 }
 
-template <int BKIND, bool DUAL, int EPI>
-hipError_t launch_dense(const GemmArgs& a, hipStream_t st) {
+template <int BKIND, bool DUAL, int EPI, bool NF4>
+hipError_t launch(const GemmArgs& a, hipStream_t st) {
   const int64_t nb = a.ntile_m * a.ntile_n;
   if (nb == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_dense_kernel<BKIND, DUAL, EPI>), dim3((unsigned)nb), dim3(NTH8), 0, st, a);
+  hipLaunchKernelGGL((gemm_kernel<BKIND, DUAL, EPI, NF4>), dim3((unsigned)nb), dim3(NTH8), 0, st, a);
   return hipGetLastError();
 }
 
-template <int BKIND, bool NF4, bool DUAL, int EPI>
-hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
-  const int64_t nb = a.ntile_m * a.ntile_n;
-  if (nb == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_nf4_kernel<BKIND, NF4, DUAL, EPI>), dim3((unsigned)nb), dim3(NTH), 0, st, a);
-  return hipGetLastError();
+template <bool NF4>
+hipError_t launch_family(const GemmArgs& a, hipStream_t st) {
+  if (a.bkind == B_NN)
+    return a.epi == EPI_ACT_FWD ? launch<B_NN, true, EPI_ACT_FWD, NF4>(a, st) : launch<B_NN, false, EPI_STORE, NF4>(a, st);
+  return a.epi == EPI_ACT_BWD ? launch<B_NT, false, EPI_ACT_BWD, NF4>(a, st) : launch<B_NT, false, EPI_STORE, NF4>(a, st);
 }
 
 }  // namespace
@@ -858,18 +772,7 @@ int64_t gemm_tile_cols(bool bf16, bool dual) {
 int64_t gemm_tile_rows(bool bf16) { return bf16 ? 256 : 64; }
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
-  if (a.nf4) {
-    if (a.bkind == B_NN)
-      return a.epi == EPI_ACT_FWD ? launch_t<B_NN, true, true, EPI_ACT_FWD>(a, st)
-                                  : launch_t<B_NN, true, false, EPI_STORE>(a, st);
-    return a.epi == EPI_ACT_BWD ? launch_t<B_NT, true, false, EPI_ACT_BWD>(a, st)
-                                : launch_t<B_NT, true, false, EPI_STORE>(a, st);
-  }
-  if (a.bkind == B_NN)
-    return a.epi == EPI_ACT_FWD ? launch_dense<B_NN, true, EPI_ACT_FWD>(a, st)
-                                : launch_dense<B_NN, false, EPI_STORE>(a, st);
-  return a.epi == EPI_ACT_BWD ? launch_dense<B_NT, false, EPI_ACT_BWD>(a, st)
-                              : launch_dense<B_NT, false, EPI_STORE>(a, st);
+  return a.nf4 ? launch_family<true>(a, st) : launch_family<false>(a, st);
 }
 
 }  // namespace lora

@@ -35,10 +35,24 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* p, int64_t bytes) {
 // loads before unrelated LDS reads (it cannot tell ring slots apart); the
 // kernels wait with an explicit vmcnt and a barrier before they read a slot,
 // and they issue no other vector-memory loads while such loads are in flight.
+// lds_addr and soff must be uniform; they are moved to scalar registers here
+// (a no-op when they already are) because the instruction takes them there.
 __device__ __forceinline__ void dma16(const i32x4& r, uint32_t voff, uint32_t lds_addr, uint32_t soff = 0) {
+  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
+  soff = __builtin_amdgcn_readfirstlane(soff);
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
                :
                : "v"(voff), "s"(r), "s"(lds_addr), "s"(soff)
+               : "memory", "m0");
+}
+
+// 4 bytes per lane: lane i writes bytes lds_addr + 4 i .. + 3 with the dword
+// at voff of the descriptor (zero past its size); same rules as dma16.
+__device__ __forceinline__ void dma4(const i32x4& r, uint32_t voff, uint32_t lds_addr) {
+  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(lds_addr)
                : "memory", "m0");
 }
 

@@ -64,16 +64,16 @@ def kernel_flops(cfg, name):
 
 
 # Kernel names (as rocprofv3 prints them) of each GEMM family: the dense
-# kernel's template arguments are <B orientation, gate/up tiles, epilogue>.
+# kernel's template arguments are <B orientation, gate/up tiles, epilogue, NF4 weights>.
 FAMILY_KERNEL = {
-    "gemm_nn_act_fwd": "gemm_dense_kernel<0, true, 1>",
-    "gemm_nn_store": "gemm_dense_kernel<0, false, 0>",
-    "gemm_nt_act_bwd": "gemm_dense_kernel<1, false, 2>",
-    "gemm_nt_store": "gemm_dense_kernel<1, false, 0>",
-    "gemm_nn_act_fwd_nf4": "gemm_nf4_kernel<0, true, true, 1>",
-    "gemm_nn_store_nf4": "gemm_nf4_kernel<0, true, false, 0>",
-    "gemm_nt_act_bwd_nf4": "gemm_nf4_kernel<1, true, false, 2>",
-    "gemm_nt_store_nf4": "gemm_nf4_kernel<1, true, false, 0>",
+    "gemm_nn_act_fwd": "gemm_kernel<0, true, 1, false>",
+    "gemm_nn_act_fwd_nf4": "gemm_kernel<0, true, 1, true>",
+    "gemm_nn_store": "gemm_kernel<0, false, 0, false>",
+    "gemm_nn_store_nf4": "gemm_kernel<0, false, 0, true>",
+    "gemm_nt_act_bwd": "gemm_kernel<1, false, 2, false>",
+    "gemm_nt_act_bwd_nf4": "gemm_kernel<1, false, 2, true>",
+    "gemm_nt_store": "gemm_kernel<1, false, 0, false>",
+    "gemm_nt_store_nf4": "gemm_kernel<1, false, 0, true>",
 }
 COPY_KERNEL = "neg_kernel"  # the --copy-calibration kernel
 

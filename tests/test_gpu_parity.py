@@ -193,13 +193,16 @@ def test_qlora_mlp_bf16(lm, act):
         assert_close(k_dev, host(grads[k_dev]), gr[k_ref], TOL["bf16"])
 
 
+# (rows, cols) of the NF4 weight: K = rows (forward) or cols (transposed) is
+# 1, 2, 3 or more K steps of 64, and N leaves ragged tiles of 64 or 128.
+@pytest.mark.parametrize("shape", [(512, 768), (64, 512), (128, 384), (192, 256)])
 @pytest.mark.parametrize("trans", [False, True])
 @pytest.mark.parametrize("with_lora", [False, True])
-def test_nf4_gemm(lm, trans, with_lora):
+def test_nf4_gemm(lm, shape, trans, with_lora):
     import torch
 
     rng = np.random.default_rng(98)
-    rows, cols, T, r, s = 512, 768, 300, 16, 2.0
+    (rows, cols), T, r, s = shape, 300, 16, 2.0
     W = ON.round_to_bf16((rng.standard_normal((rows, cols)) / np.sqrt(rows)).astype(np.float32))
     A = ON.round_to_bf16(rng.uniform(-1, 1, (rows, r)).astype(np.float32) / np.sqrt(rows))
     B = ON.round_to_bf16((rng.standard_normal((r, cols)) * 0.02).astype(np.float32))
