@@ -290,10 +290,13 @@ def nf4_quantize(W, *, stream=None) -> NF4Weight:
     return w
 
 
-def nf4_dequant(w: NF4Weight, dtype=None, *, stream=None):
+def nf4_dequant(w: NF4Weight, dtype=None, *, out=None, stream=None):
     torch = _torch()
     dtype = torch.bfloat16 if dtype is None else dtype
-    out = torch.empty((w.rows, w.cols), dtype=dtype, device=w.codes.device)
+    if out is None:
+        out = torch.empty((w.rows, w.cols), dtype=dtype, device=w.codes.device)
+    if tuple(out.shape) != (w.rows, w.cols) or out.dtype != dtype or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous [{w.rows}, {w.cols}] {dtype} tensor")
     s = w.c_struct()
     L.call("lora_nf4_dequant", C.byref(s), _ptr(out), _dtype_code(out), _stream(stream))
     return out

@@ -341,7 +341,9 @@ constexpr int LDS_BYTES = 5 * SLOT_BYTES;     // dense: 3 weight slots; NF4: 2 +
 constexpr int HALF_BYTES = 16384;
 constexpr int CODE_RING = W_RING + 2 * SLOT_BYTES;
 constexpr int CODE_SLOT = 10240;  // codes 8 KB | scale-code dwords 1 KB | fp32 scales 1 KB
-static_assert(CODE_RING + 3 * CODE_SLOT <= LDS_BYTES, "NF4 code ring exceeds LDS");
+constexpr int SPARE = CODE_RING + 3 * CODE_SLOT;  // target of the stores of an idle unpack
+constexpr int SPARE_BYTES = 2048;
+static_assert(SPARE + SPARE_BYTES <= LDS_BYTES, "NF4 code ring exceeds LDS");
 
 template <int BKIND, bool DUAL, int EPI, bool NF4>
 __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
@@ -370,10 +372,14 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   const int64_t m0 = (int64_t)tm * BM;
 
   int KT = 0, KN = 0;  // all K steps; NF4 steps (the NF4 segments come first)
+  int nseg_nf4 = 0;
   for (int s = 0; s < args.nseg; ++s) {
     const int k = (int)(args.seg[s].K / BK);
     KT += k;
-    if (NF4 && args.seg[s].b[reg][0].codes != nullptr) KN += k;
+    if (NF4 && args.seg[s].b[reg][0].codes != nullptr) {
+      KN += k;
+      ++nseg_nf4;
+    }
   }
 
   // ---- loads: 8 blocks of 1 KB per wavefront and step ----
@@ -486,9 +492,12 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   // each group walks the NF4 steps it unpacks with a cursor of its own
   int dseg = 0, dk0 = 0;
   // unpack half h (elements 32 h .. 32 h + 31) of block 64 wn + lane from code
-  // slot cslot into weight slot wslot
-  auto unpack = [&](int cslot, int wslot, int h) {
-    const GemmSeg& S = args.seg[dseg];
+  // slot cslot into weight slot wslot.  Without `live` (no step left to
+  // unpack) the same work runs on stale codes and its stores go to 2 KB of
+  // otherwise unused LDS, so the call has no branch and shares one
+  // scheduling region with the MFMA cluster it is interleaved with.
+  auto unpack = [&](int cslot, int wslot, int h, bool live) {
+    const GemmSeg& S = args.seg[dseg < nseg_nf4 ? dseg : nseg_nf4 - 1];
     const BSrc& B = nf4_src(S);
     // uniform: a scalar load (a vector load would make the compiler wait for
     // the global -> LDS loads in flight)
@@ -514,7 +523,8 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
     }
     const int8_t q8 = (int8_t)(q8w >> (8 * (qb & 3)));
     const Nf4Planes pl = nf4_planes(nf4_absmax(q8, s2, mu));
-    lds_char* const wt = lds + W_RING + wslot * SLOT_BYTES;
+    lds_char* const wt = lds + (live ? W_RING + wslot * SLOT_BYTES : SPARE);
+    const int omask = live ? 0x7fffffff : SPARE_BYTES - 1;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       const u32x4 v = nf4_decode8(w[d], pl);
@@ -527,13 +537,12 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
         const int c = 4 * h + d;
         off = b * 128 + ((c ^ swz(b)) << 4);
       }
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(wt + off) = v;
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(wt + (off & omask)) = v;
     }
-    dk0 += BK;
-    if (dk0 >= (int)S.K) {
-      ++dseg;
-      dk0 = 0;
-    }
+    const int nk0 = dk0 + BK;
+    const bool wrap = nk0 >= (int)S.K;
+    dseg = live && wrap ? dseg + 1 : dseg;
+    dk0 = live ? (wrap ? 0 : nk0) : dk0;
   };
 
   // ---- fragment reads ----
@@ -593,8 +602,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
   // the MFMA phase runs at raised wavefront priority, so the SIMD's other
   // wavefront (in its read phase) cannot delay the MFMA issue
-  auto mma = [&]() {
-    __builtin_amdgcn_s_setprio(1);
+  auto mma_body = [&]() {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -602,6 +610,25 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0);
+  };
+  auto mma = [&]() {
+    __builtin_amdgcn_s_setprio(1);
+    mma_body();
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // MFMA cluster with an unpack interleaved: its LDS reads first, then about
+  // five of its vector instructions after each MFMA
+  auto mma_unpack = [&](int cslot, int wslot, int h, bool live) {
+    __builtin_amdgcn_s_setprio(1);
+    mma_body();
+    unpack(cslot, wslot, h, live);
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // their addresses
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -682,7 +709,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
       issue_a(0);
       if (KT > 1) issue_a(1);
       phase_end();
-      unpack(0, 0, 0);
+      unpack(0, 0, 0, true);
       if (KT > 1) wait_vmcnt<8>();
       else wait_vmcnt<0>();
       phase_end();
@@ -690,8 +717,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
       phase_end();
       int cs1 = 1;  // code slot of step t + 1
       for (int t = 0; t < KT; ++t) {
-        mma();
-        if (t + 1 < KN) unpack(cs1, (t + 1) & 1, 0);
+        mma_unpack(cs1, (t + 1) & 1, 0, t + 1 < KN);
         wait_vmcnt<0>();  // A t+1 is in
         phase_end();
         if (t + 2 < KT) issue_a(t & 1);
@@ -711,11 +737,11 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
         wait_vmcnt<0>();
       }
       phase_end();
-      unpack(0, 0, 1);
+      unpack(0, 0, 1, true);
       if (KN > 2) wait_vmcnt<4>();
       else wait_vmcnt<0>();
       phase_end();
-      if (KN > 1) unpack(1, 1, 1);
+      if (KN > 1) unpack(1, 1, 1, true);
       else if (lora_step) issue_w(1);
       phase_end();
       int cs0 = 0;  // code slot of step t (= that of step t + 3)
@@ -730,9 +756,8 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
           wait_vmcnt<0>();
         }
         phase_end();
-        mma();
-        if (t + 2 < KN) unpack(cs2, t & 1, 1);
-        else if (lora_step && t + 2 == KN) issue_w(t & 1);
+        mma_unpack(cs2, t & 1, 1, t + 2 < KN);
+        if (lora_step && t + 2 == KN) issue_w(t & 1);
         phase_end();
         cs0 = cs0 == 2 ? 0 : cs0 + 1;
       }

@@ -212,6 +212,48 @@ def read_traffic(kernel, tag):
         return None
 
 
+def nf4_bytes(rows, cols):
+    """Bytes of one NF4 weight: codes (2 per byte), int8 scale codes per 64
+    elements, fp32 second-level scales per 64 x 256 elements, the fp32 mean."""
+    n = rows * cols
+    return n // 2 + n // 64 + 4 * (n // (64 * 256)) + 4
+
+
+def nf4_report(cfg, step, lm, torch, reps=5):
+    """QLoRA extras: per NF4 GEMM family, the packed weight bytes it reads
+    once per launch over its average launch time (the weight stream rate),
+    and the standalone dequant kernel (codes + scales in, bf16 out) against
+    HBM, timed on the gate weight."""
+    H, I = cfg.H, cfg.I
+    w = {"gemm_nn_act_fwd_nf4": 2 * nf4_bytes(H, I), "gemm_nn_store_nf4": nf4_bytes(I, H),
+         "gemm_nt_act_bwd_nf4": nf4_bytes(I, H), "gemm_nt_store_nf4": 2 * nf4_bytes(H, I)}
+    lm.trace_begin("gemm")
+    for _ in range(reps):
+        step()
+    torch.cuda.synchronize()
+    fams = lm.trace_end()
+    stream = {}
+    for fam, b in w.items():
+        if fam in fams:
+            ms = fams[fam][1] / fams[fam][0]
+            stream[fam] = {"weight_bytes": b, "avg_launch_ms": ms, "GB_s": b / (ms / 1e3) / 1e9}
+    q = step.p["gate"].nf4
+    out = torch.empty((H, I), dtype=torch.bfloat16, device="cuda:0")
+    lm.nf4_dequant(q, torch.bfloat16, out=out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        lm.nf4_dequant(q, torch.bfloat16, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    moved = nf4_bytes(H, I) + 2 * H * I
+    return {"weight_stream": stream,
+            "dequant": {"shape": [H, I], "bytes": moved, "ms": ms, "GB_s": moved / (ms / 1e3) / 1e9,
+                        "hbm_frac": moved / (ms / 1e3) / (PEAK_HBM_GBS * 1e9)}}
+
+
 # ---------------------------------------------------------------------------
 # Workloads
 # ---------------------------------------------------------------------------
@@ -407,6 +449,8 @@ def main():
             f"(reads {n * 4} B, writes {n * 4} B per launch)")
         del src, dst
 
+    nf4 = nf4_report(cfg, step, lm, torch) if cfg.nf4 else None
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a token sample")
@@ -440,6 +484,8 @@ def main():
                      "launches_timed": launches},
         "cpu_baseline": cpu,
     }
+    if nf4:
+        out["nf4"] = nf4
     print(json.dumps(out), flush=True)
 
 
