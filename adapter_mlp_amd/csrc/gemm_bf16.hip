@@ -391,60 +391,95 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   const int kc_x = (lane & 7) ^ (lane >> 3);
   const int nn_row = (wn & 1) * 32 + (lane >> 4);
   const int nn_chunk = (lane & 15) ^ (4 * ((lane >> 4) & 3));
-  // each group walks the K steps with its own cursor (segment, offset)
-  int lseg = 0;
-  int64_t lk0 = 0;
-  auto advance = [&](const GemmSeg& S) {
+  // Each group walks the K steps with a load cursor of its own (group 0: the
+  // activation tiles; group 1: the weight tiles, or an NF4 segment's codes and
+  // scales).  The current segment's window is kept in scalar registers and
+  // advanced by one K step per load; the segment table in the kernel
+  // arguments is read only when a segment starts, not at the head of every
+  // read phase.
+  int lseg = 0, lsteps = 0, lk0 = 0;
+  const char* lp = nullptr;  // dense operand at the next K step
+  int64_t ln = 0;            // bytes from lp to the end of its window
+  uint32_t lld2 = 0;         // row pitch in bytes
+  int64_t lstep = 0;         // bytes lp advances per K step
+  const uint8_t* lcodes = nullptr;  // NF4 segment
+  const int8_t* lq8 = nullptr;
+  const float* ls2 = nullptr;
+  int64_t lnumel = 0;
+  int lwcols = 0;
+  // every field is assigned on every call (selects, no early exits), so the
+  // cursor stays in scalar registers
+  auto cur_begin = [&]() {
+    const GemmSeg& S = args.seg[lseg];
+    const BSrc& B = S.b[reg][(BKIND == B_NN && DUAL) ? (wn >> 1) : 0];
+    lsteps = (int)(S.K / BK);
+    lk0 = 0;
+    const char* pw;
+    int64_t nw, sw;
+    if constexpr (BKIND == B_NT) {
+      pw = static_cast<const char*>(B.p) + tnl * 256 * B.ld * 2;
+      nw = (NR - tnl * 256) * B.ld * 2;
+      sw = BK * 2;
+    } else {
+      const int64_t ncol0 = DUAL ? tnl * 128 : tnl * 256 + (wn >> 1) * 128;
+      pw = static_cast<const char*>(B.p) + ncol0 * 2;
+      nw = ((S.K - 1) * B.ld + NR - ncol0) * 2;
+      sw = (int64_t)BK * B.ld * 2;
+    }
+    const bool act = wm == 0;
+    lp = act ? static_cast<const char*>(S.A) + m0 * S.lda * 2 : pw;
+    ln = act ? (M - m0) * S.lda * 2 : nw;
+    lld2 = (uint32_t)((act ? S.lda : B.ld) * 2);
+    lstep = act ? (int64_t)BK * 2 : sw;
+    if constexpr (NF4) {  // NF4 segment (group 1): codes and scales
+      lcodes = B.codes;
+      lq8 = B.q8;
+      ls2 = B.s2;
+      lwcols = (int)B.wcols;
+      lnumel = (BKIND == B_NN ? S.K : NR) * B.wcols;
+    }
+  };
+  cur_begin();
+  auto advance = [&]() {
+    lp += lstep;
+    ln -= lstep;
     lk0 += BK;
-    if (lk0 >= S.K) {
+    if (--lsteps == 0 && lseg + 1 < args.nseg) {
       ++lseg;
-      lk0 = 0;
+      cur_begin();
     }
   };
   auto issue_a = [&](int slot) {  // group 0: activation tile of the next step
-    const GemmSeg& S = args.seg[lseg];
     const uint32_t dst = lds_addr(lds) + slot * SLOT_BYTES + wn * 8 * 1024;
     // opaque copies: keep the per-lane terms from being expanded per block
     // and hoisted out of the K loop (8 live offsets would not fit)
     int x = kc_x, r = kc_row;
     asm volatile("" : "+v"(x), "+v"(r));
-    const uint32_t lda2 = (uint32_t)(S.lda * 2);
-    const i32x4 ra = rsrc_words(static_cast<const char*>(S.A) + (m0 * S.lda + lk0) * 2,
-                                (M - m0) * S.lda * 2 - lk0 * 2);
-    const uint32_t base = (uint32_t)r * lda2;
+    const i32x4 ra = rsrc_words(lp, ln);
+    const uint32_t base = (uint32_t)r * lld2;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dma16(ra, base + (uint32_t)((x ^ i) << 4), dst + i * 1024, (uint32_t)(8 * i) * lda2);
-    advance(S);
+    for (int i = 0; i < 8; ++i) dma16(ra, base + (uint32_t)((x ^ i) << 4), dst + i * 1024, (uint32_t)(8 * i) * lld2);
+    advance();
   };
-  auto issue_w = [&](int slot) {  // group 1: weight tile of the next step
-    const GemmSeg& S = args.seg[lseg];
+  auto issue_w = [&](int slot) {  // group 1: (dense) weight tile of the next step
     const uint32_t wslot = lds_addr(lds) + W_RING + slot * SLOT_BYTES;
+    const i32x4 rb = rsrc_words(lp, ln);
     if constexpr (BKIND == B_NT) {
-      const BSrc& B = S.b[reg][0];
       int x = kc_x, r = kc_row;
       asm volatile("" : "+v"(x), "+v"(r));
-      const uint32_t ld2 = (uint32_t)(B.ld * 2);
-      const i32x4 rb = rsrc_words(static_cast<const char*>(B.p) + (tnl * 256 * B.ld + lk0) * 2,
-                                  (NR - tnl * 256) * B.ld * 2 - lk0 * 2);
-      const uint32_t base = (uint32_t)r * ld2;
+      const uint32_t base = (uint32_t)r * lld2;
       const uint32_t dst = wslot + wn * 8 * 1024;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dma16(rb, base + (uint32_t)((x ^ i) << 4), dst + i * 1024, (uint32_t)(8 * i) * ld2);
+      for (int i = 0; i < 8; ++i) dma16(rb, base + (uint32_t)((x ^ i) << 4), dst + i * 1024, (uint32_t)(8 * i) * lld2);
     } else {
-      const int half = wn >> 1;
-      const BSrc& B = S.b[reg][DUAL ? half : 0];
-      const uint32_t ld2 = (uint32_t)(B.ld * 2);
-      const int64_t ncol0 = DUAL ? tnl * 128 : tnl * 256 + half * 128;
-      const i32x4 rb = rsrc_words(static_cast<const char*>(B.p) + (lk0 * B.ld + ncol0) * 2,
-                                  ((S.K - 1 - lk0) * B.ld + NR - ncol0) * 2);
       int nr = nn_row, nc = nn_chunk;
       asm volatile("" : "+v"(nr), "+v"(nc));
-      const uint32_t base = (uint32_t)nr * ld2 + (uint32_t)(nc << 4);
-      const uint32_t dst = wslot + half * HALF_BYTES + (wn & 1) * 8 * 1024;
+      const uint32_t base = (uint32_t)nr * lld2 + (uint32_t)(nc << 4);
+      const uint32_t dst = wslot + (wn >> 1) * HALF_BYTES + (wn & 1) * 8 * 1024;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dma16(rb, base, dst + i * 1024, (uint32_t)(4 * i) * ld2);
+      for (int i = 0; i < 8; ++i) dma16(rb, base, dst + i * 1024, (uint32_t)(4 * i) * lld2);
     }
-    advance(S);
+    advance();
   };
 
   // ---- NF4: code staging and unpacking ----
@@ -454,8 +489,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   //   NT: weight row (= output column) 256 tnl + 64 wn + j, column k0.
   // Returns its flat element index, or a value past every NF4 array for
   // columns (NN) or rows (NT) outside the region, so its loads read zero.
-  auto nf4_flat = [&](const BSrc& B, int k0, int j) -> uint32_t {
-    const int wcols = (int)B.wcols;
+  auto nf4_flat = [&](int wcols, int k0, int j) -> uint32_t {
     if constexpr (BKIND == B_NN) {
       const int col = (DUAL ? (int)tnl * 128 : (int)tnl * 256 + 128 * (wn >> 1)) + 64 * (j & 1);
       const int row = k0 + 32 * (wn & 1) + (j >> 1);
@@ -468,26 +502,23 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   auto nf4_src = [&](const GemmSeg& S) -> const BSrc& { return S.b[reg][(BKIND == B_NN && DUAL) ? (wn >> 1) : 0]; };
   // group 1: codes and scales of the next NF4 step into code slot `slot`
   auto issue_codes = [&](int slot) {
-    const GemmSeg& S = args.seg[lseg];
-    const BSrc& B = nf4_src(S);
-    const int64_t numel = (BKIND == B_NN ? S.K : NR) * B.wcols;
-    const i32x4 rc = rsrc_words(B.codes, numel / 2);
-    const i32x4 rq = rsrc_words(B.q8, numel / 64);
-    const i32x4 rs = rsrc_words(B.s2, numel / NF4_GROUP * 4);
+    const i32x4 rc = rsrc_words(lcodes, lnumel / 2);
+    const i32x4 rq = rsrc_words(lq8, lnumel / 64);
+    const i32x4 rs = rsrc_words(ls2, lnumel / NF4_GROUP * 4);
     const uint32_t cs = lds_addr(lds) + CODE_RING + slot * CODE_SLOT;
     int l = lane;
     asm volatile("" : "+v"(l));
     // codes of block b at cs + 32 b: lane l of load j takes half l & 1 of block 64 wn + 32 j + l / 2
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const uint32_t f = nf4_flat(B, (int)lk0, 32 * j + (l >> 1));
+      const uint32_t f = nf4_flat(lwcols, lk0, 32 * j + (l >> 1));
       dma16(rc, (f >> 1) + 16 * (l & 1), cs + 2048 * wn + 1024 * j);
     }
     // lane l: block 64 wn + l; the aligned dword holding its scale code, and its fp32 scale
-    const uint32_t f = nf4_flat(B, (int)lk0, l);
+    const uint32_t f = nf4_flat(lwcols, lk0, l);
     dma4(rq, (f >> 6) & ~3u, cs + 8192 + 256 * wn);
     dma4(rs, (f >> 14) << 2, cs + 9216 + 256 * wn);
-    advance(S);
+    advance();
   };
   // each group walks the NF4 steps it unpacks with a cursor of its own
   int dseg = 0, dk0 = 0;
