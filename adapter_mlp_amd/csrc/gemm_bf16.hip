@@ -667,8 +667,8 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   //   prologue  g0 loads A 0, 1   g1 loads W 0, 1; each waits for step 0 | barrier
   //             g0 reads step 0                                         | barrier
   //   step t    X: g0 MFMA t, waits for A t+1
-  //                g1 loads W t+2, reads step t, waits for W t+1        | barrier
-  //             Y: g0 loads A t+2, reads step t+1
+  //                g1 reads step t, loads W t+2, waits for W t+1        | barrier
+  //             Y: g0 reads step t+1, loads A t+2
   //                g1 MFMA t                                            | barrier
   // A t+2 goes to activation slot t & 1 after its last read (g1, X(t));
   // W t+2 goes to weight slot (t+2) % 3, last read in X(t-1).
@@ -693,8 +693,9 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
         mma();
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): A t+1 is in
         phase_end();
-        if (t + 2 < KT) issue_a(t & 1);
+        // fragment reads first: they are the phase's critical path
         if (t + 1 < KT) read((t + 1) & 1, (t + 1) % 3);
+        if (t + 2 < KT) issue_a(t & 1);
         phase_end();
       }
     } else {
@@ -711,8 +712,8 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
       for (int t = 0; t < KT; ++t) {
         const int ws2 = ws == 0 ? 2 : ws - 1;  // (t + 2) % 3
         if (t + 2 < KT) {
-          issue_w(ws2);
           read(t & 1, ws);
+          issue_w(ws2);
           __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): W t+1 is in (W t+2 may still fly)
         } else {
           read(t & 1, ws);
@@ -731,8 +732,8 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
     //       g0 waits for A 0                                                         | barrier
     //   P3  g0 reads step 0              g1 unpacks W 1 (upper) or loads the adapter W 1 | barrier
     //   X(t)  g0 MFMA t, unpacks W t+1 (lower), waits for A t+1
-    //         g1 loads codes t+3, reads step t, waits for codes t+2 (and adapter W)  | barrier
-    //   Y(t)  g0 loads A t+2, reads step t+1
+    //         g1 reads step t, loads codes t+3, waits for codes t+2 (and adapter W)  | barrier
+    //   Y(t)  g0 reads step t+1, loads A t+2
     //         g1 MFMA t, unpacks W t+2 (upper) or loads the adapter W t+2           | barrier
     // Weight slot of step t: t & 1; code slot: t % 3.
     const bool lora_step = KT > KN;  // the last step is the dense adapter tile
@@ -751,8 +752,8 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
         mma_unpack(cs1, (t + 1) & 1, 0, t + 1 < KN);
         wait_vmcnt<0>();  // A t+1 is in
         phase_end();
-        if (t + 2 < KT) issue_a(t & 1);
         if (t + 1 < KT) read((t + 1) & 1, (t + 1) & 1);
+        if (t + 2 < KT) issue_a(t & 1);
         phase_end();
         cs1 = cs1 == 2 ? 0 : cs1 + 1;
       }
@@ -779,8 +780,8 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
       for (int t = 0; t < KT; ++t) {
         const int cs2 = cs0 == 0 ? 2 : cs0 - 1;  // (t + 2) % 3
         if (t + 3 < KN) {
-          issue_codes(cs0);
           read(t & 1, t & 1);
+          issue_codes(cs0);
           wait_vmcnt<4>();  // codes t+2 are in (codes t+3 may still fly)
         } else {
           read(t & 1, t & 1);
