@@ -278,6 +278,7 @@ struct MlpPlan {
   void *At_gu, *Us_gu, *BLt_gu, *h, *At_d, *Us_d, *BLt_d;                  // forward
   void *Ps_d, *BLt_dh, *hb, *dg, *de, *Ps_ug, *BLt_dx;                      // backward
   float* partial;
+  float* rpartial;  // rowproj partials of the fused dY / dg / de passes
   size_t fwd_bytes, bwd_bytes;
 };
 
@@ -309,6 +310,7 @@ MlpPlan plan_mlp(const Ctx& c, const lora_mlp_desc& d, void* ws_fwd, void* ws_bw
     for (int i = 0; i < 3; ++i) pf = cands[i] > pf ? cands[i] : pf;
   }
   p.partial = static_cast<float*>(b.take((size_t)pf * 4));
+  p.rpartial = c.bf16 ? static_cast<float*>(b.take((size_t)rowcol_partial_floats(T, I > H ? I : H) * 4)) : nullptr;
   p.bwd_bytes = b.off;
   return p;
 }
@@ -689,17 +691,16 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, 
   const int64_t RLg = c.rl(2 * r), RLd = c.rl(r);
   const void* U = saved->U;
 
-  // P_d = dY B_d^T, formed once (scaled copy feeds dA_d and the dh GEMM)
+  // one pass over dY: P_d = dY B_d^T, formed once (scaled copy feeds dA_d and
+  // the dh GEMM), and dB_d = s_d U_d^T dY
   RowProjArgs r1 = rowproj_args(dY, H, T, H, down->B, H, (int)r, (int)RLd, (int)r);
   r1.scales[0] = down->scale;
   r1.out2 = p.Ps_d;
   r1.ld2 = RLd;
-  LAUNCHN("rowproj", st, launch_rowproj(c.bf16, r1, st));
-  // dB_d = s_d U_d^T dY
   ColProjArgs c1 = colproj_args(dY, H, T, H, coff(U, 2 * r, c), 3 * r, (int)r, (int)r, true, p.partial);
   c1.scales[0] = down->scale;
   c1.dest[0] = gr->dB_down;
-  LAUNCHN("colproj", st, launch_colproj(c.bf16, c1, st));
+  LAUNCHN("rowcol", st, launch_rowcol(c.bf16, c1, r1, p.rpartial, st));
 
   // dh GEMM with the activation-gradient epilogue -> dg, de, h
   PackLoraArgs pl{};
@@ -741,27 +742,24 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, 
   c2.dest[0] = gr->dA_down;
   LAUNCHN("colproj", st, launch_colproj(c.bf16, c2, st));
 
-  // P_u = dg B_u^T, P_g = de B_g^T, each formed once: [s_u P_u | s_g P_g]
+  // one pass over dg: P_u = dg B_u^T (formed once, into [s_u P_u | s_g P_g])
+  // and dB_u = s_u U_u^T dg; the same over de for P_g and dB_g
   RowProjArgs r2 = rowproj_args(p.dg, I, T, I, up->B, I, (int)r, (int)r, (int)r);
   r2.scales[0] = up->scale;
   r2.out2 = p.Ps_ug;
   r2.ld2 = RLg;
-  LAUNCHN("rowproj", st, launch_rowproj(c.bf16, r2, st));
+  ColProjArgs c3 = colproj_args(p.dg, I, T, I, coff(U, r, c), 3 * r, (int)r, (int)r, true, p.partial);
+  c3.scales[0] = up->scale;
+  c3.dest[0] = gr->dB_up;
+  LAUNCHN("rowcol", st, launch_rowcol(c.bf16, c3, r2, p.rpartial, st));
   RowProjArgs r3 = rowproj_args(p.de, I, T, I, gate->B, I, (int)r, (int)(RLg - r), (int)r);
   r3.scales[0] = gate->scale;
   r3.out2 = offw(p.Ps_ug, r, c);
   r3.ld2 = RLg;
-  LAUNCHN("rowproj", st, launch_rowproj(c.bf16, r3, st));
-
-  // dB_u = s_u U_u^T dg, dB_g = s_g U_g^T de
-  ColProjArgs c3 = colproj_args(p.dg, I, T, I, coff(U, r, c), 3 * r, (int)r, (int)r, true, p.partial);
-  c3.scales[0] = up->scale;
-  c3.dest[0] = gr->dB_up;
-  LAUNCHN("colproj", st, launch_colproj(c.bf16, c3, st));
   ColProjArgs c4 = colproj_args(p.de, I, T, I, U, 3 * r, (int)r, (int)r, true, p.partial);
   c4.scales[0] = gate->scale;
   c4.dest[0] = gr->dB_gate;
-  LAUNCHN("colproj", st, launch_colproj(c.bf16, c4, st));
+  LAUNCHN("rowcol", st, launch_rowcol(c.bf16, c4, r3, p.rpartial, st));
 
   // [dA_u | dA_g] = X^T [s_u P_u | s_g P_g] in one pass over X
   ColProjArgs c5 = colproj_args(X, H, T, H, p.Ps_ug, RLg, (int)(2 * r), (int)r, false, p.partial);

@@ -114,10 +114,22 @@ struct ColProjArgs {
   float scales[4];
   void* dest[4];
   float* partial;  // bf16 path: [nchunk, K, R] fp32 scratch
+  // fused rowproj over the same Z (launch_rowcol): Bt [R1, K] (R1 <= 16),
+  // per-column-block partials [K / 256, T, 16] fp32
+  const void* Bt;
+  int64_t ldb;
+  int32_t R1, pad_;
+  float* rpartial;
 };
 
 hipError_t launch_rowproj(bool bf16, const RowProjArgs& a, hipStream_t st);
 hipError_t launch_colproj(bool bf16, const ColProjArgs& a, hipStream_t st);
+// rowproj r and colproj c over the same Z [T, K] in one pass (bf16, r.R <= 16):
+// the colproj blocks also form r's product over their 256 columns; a
+// fixed-order reduce then writes r's outputs.  Other cases run the two
+// kernels one after the other.  rpartial: rowcol_partial_floats(T, K) floats.
+hipError_t launch_rowcol(bool bf16, const ColProjArgs& c, const RowProjArgs& r, float* rpartial, hipStream_t st);
+int64_t rowcol_partial_floats(int64_t T, int64_t K);
 // partial-buffer floats the bf16 colproj needs for (T, K, R)
 int64_t colproj_partial_floats(int64_t T, int64_t K, int R);
 int colproj_nchunk(int64_t T, int64_t K);

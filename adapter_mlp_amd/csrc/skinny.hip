@@ -208,10 +208,17 @@ struct ColProjCfg {
   static constexpr int NST = 4;
 };
 
-template <int NJ>
+// With ROW, the block also forms a rowproj over its 256 columns: Out[t, j] =
+// sum_k Z[t, k] Bt[j, k] for every 32-row step, written as that column
+// block's partial.  The Bt slice [16 x 256] is loaded once into LDS (rows of
+// 512 bytes, chunk c of row j at c ^ j) and from there into registers; per
+// step, wavefronts 0, 1 (even steps) or 2, 3 (odd steps) each take one
+// 16-row half with 8 16x16x32 MFMAs, reading Z K-contiguously from the slot.
+template <int NJ, bool ROW>
 __global__ __launch_bounds__(256) void colproj_bf16_kernel(const ColProjArgs a, int64_t rows_per_chunk) {
   using C = ColProjCfg<NJ>;
-  __shared__ __attribute__((aligned(1024))) char ring[C::NST * C::SB];
+  constexpr int BTB = ROW ? 8192 : 0;  // Bt slice after the ring
+  __shared__ __attribute__((aligned(1024))) char ring[C::NST * C::SB + BTB];
   lds_char* const lds = (lds_char*)ring;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -277,6 +284,40 @@ __global__ __launch_bounds__(256) void colproj_bf16_kernel(const ColProjArgs a, 
     }
   };
 
+  // ---- fused rowproj (ROW) ----
+  bf16x8 btf[ROW ? 8 : 1];
+  auto row_step = [&](int s, int slot) {
+    if constexpr (ROW) {
+      if ((w >> 1) != (s & 1)) return;  // two wavefronts per step
+      const int rb = w & 1;             // 16-row half of the step
+      const lds_char* zs = lds + slot * C::SB;
+      const int r = rb * 16 + (lane & 15);
+      f32x4 acc_r = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int cz = 4 * ks + (lane >> 4);
+        const bf16x8 za = __builtin_bit_cast(bf16x8, lds_read16(zs + r * 512 + ((cz ^ zswz(r)) * 16)));
+        acc_r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(za, btf[ks], acc_r, 0, 0, 0);
+      }
+      // acc_r[v] = Out[row rb * 16 + 4 (lane >> 4) + v of the step, j = lane % 16]
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t t = tbeg + 32 * (int64_t)s + rb * 16 + 4 * (lane >> 4) + v;
+        if (t < tend) a.rpartial[((int64_t)blockIdx.x * a.T + t) * 16 + (lane & 15)] = acc_r[v];
+      }
+    }
+  };
+
+  if constexpr (ROW) {
+    // Bt slice: rows past R1 read zero; two 1 KB loads per wavefront (rows 2q, 2q+1)
+    const i32x4 rbt = rsrc_words(static_cast<const char*>(a.Bt) + k0 * 2, (int64_t)a.R1 * a.ldb * 2 - k0 * 2);
+    const uint32_t ldb2 = (uint32_t)(a.ldb * 2);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = 2 * (2 * w + i) + hrow;
+      dma16(rbt, (uint32_t)row * ldb2 + (uint32_t)((pc ^ row) * 16), lds_addr(lds) + C::NST * C::SB + (2 * w + i) * 1024);
+    }
+  }
   const int pre = nsteps < C::NST - 1 ? nsteps : C::NST - 1;
   for (int s = 0; s < pre; ++s) issue(s, s);
   for (int s = 0; s < nsteps; ++s) {
@@ -284,8 +325,23 @@ __global__ __launch_bounds__(256) void colproj_bf16_kernel(const ColProjArgs a, 
     if (pload) wait_steps_after<5, C::NST - 2>(after);
     else wait_steps_after<4, C::NST - 2>(after);
     __syncthreads();
+    if constexpr (ROW) {
+      if (s == 0) {  // the Bt slice (loaded before step 0) is in: fragments for all 8 K steps;
+        // columns past K (last block) are zeroed, whole fragments since K is a multiple of 64
+        const lds_char* bs = lds + C::NST * C::SB;
+        const int j = lane & 15;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const int cb = 4 * ks + (lane >> 4);
+          const u32x4 v = lds_read16(bs + j * 512 + ((cb ^ j) * 16));
+          const bool in = k0 + 8 * cb < a.K;
+          btf[ks] = __builtin_bit_cast(bf16x8, in ? v : u32x4{0, 0, 0, 0});
+        }
+      }
+    }
     if (s + C::NST - 1 < nsteps) issue(s + C::NST - 1, (s + C::NST - 1) % C::NST);
     compute(s % C::NST);
+    row_step(s, s % C::NST);
   }
 
   // acc[mi][nb][v] = Out[k0 + 16 (4w + mi) + 4 (lane >> 4) + v, 16 nb + lane % 16]
@@ -423,16 +479,63 @@ hipError_t launch_colproj(bool bf16, const ColProjArgs& a0, hipStream_t st) {
     const int64_t rows_per_chunk = steps_per_chunk * 32;
     a.nchunk = (int)((a.T + rows_per_chunk - 1) / rows_per_chunk);
     const dim3 grid((unsigned)((a.K + 255) / 256), (unsigned)a.nchunk);
-    switch (NJ) {
-      case 1: hipLaunchKernelGGL(colproj_bf16_kernel<1>, grid, dim3(256), 0, st, a, rows_per_chunk); break;
-      case 2: hipLaunchKernelGGL(colproj_bf16_kernel<2>, grid, dim3(256), 0, st, a, rows_per_chunk); break;
-      case 3: hipLaunchKernelGGL(colproj_bf16_kernel<3>, grid, dim3(256), 0, st, a, rows_per_chunk); break;
-      default: hipLaunchKernelGGL(colproj_bf16_kernel<4>, grid, dim3(256), 0, st, a, rows_per_chunk); break;
+    if (a.rpartial != nullptr) {  // fused rowproj (launch_rowcol): NJ == 1
+      hipLaunchKernelGGL((colproj_bf16_kernel<1, true>), grid, dim3(256), 0, st, a, rows_per_chunk);
+    } else {
+      switch (NJ) {
+        case 1: hipLaunchKernelGGL((colproj_bf16_kernel<1, false>), grid, dim3(256), 0, st, a, rows_per_chunk); break;
+        case 2: hipLaunchKernelGGL((colproj_bf16_kernel<2, false>), grid, dim3(256), 0, st, a, rows_per_chunk); break;
+        case 3: hipLaunchKernelGGL((colproj_bf16_kernel<3, false>), grid, dim3(256), 0, st, a, rows_per_chunk); break;
+        default: hipLaunchKernelGGL((colproj_bf16_kernel<4, false>), grid, dim3(256), 0, st, a, rows_per_chunk); break;
+      }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(colproj_reduce_kernel, dim3(nblk(a.K * a.R, 256)), dim3(256), 0, st, a, NJ * 16);
+  return hipGetLastError();
+}
+
+namespace {
+// Out[t, j] of a fused rowproj: the column blocks' partials summed in
+// ascending block order, then written as the rowproj kernel writes it.
+__global__ void rowproj_reduce_kernel(const RowProjArgs a, const float* rpartial, int nb) {
+  const int R2 = a.R2 > a.R ? a.R2 : a.R;
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= a.T * R2) return;
+  const int64_t t = e / R2;
+  const int j = (int)(e % R2);
+  float v = 0.0f;
+  if (j < a.R)
+    for (int b = 0; b < nb; ++b) v += rpartial[((int64_t)b * a.T + t) * 16 + j];
+  if (a.out1 && j < a.R) static_cast<uint16_t*>(a.out1)[t * a.ld1 + a.off1 + j] = (uint16_t)f2bf(v);
+  if (a.out2) {
+    const float sc = j < a.R ? a.scales[j / a.seg_w] : 0.0f;
+    static_cast<uint16_t*>(a.out2)[t * a.ld2 + j] = (uint16_t)f2bf(sc * v);
+  }
+}
+}  // namespace
+
+int64_t rowcol_partial_floats(int64_t T, int64_t K) { return ((K + 255) / 256) * T * 16; }
+
+hipError_t launch_rowcol(bool bf16, const ColProjArgs& c0, const RowProjArgs& r, float* rpartial, hipStream_t st) {
+  const bool fused = bf16 && rpartial != nullptr && r.R <= 16 && r.Z == c0.Z && r.ldz == c0.ldz && r.T == c0.T &&
+                     r.K == c0.K && r.K % 8 == 0 && c0.R <= 16 && c0.T > 0;
+  if (!fused) {
+    hipError_t e = launch_rowproj(bf16, r, st);
+    if (e != hipSuccess) return e;
+    return launch_colproj(bf16, c0, st);
+  }
+  ColProjArgs c = c0;
+  c.Bt = r.Bt;
+  c.ldb = r.ldb;
+  c.R1 = r.R;
+  c.rpartial = rpartial;
+  hipError_t e = launch_colproj(true, c, st);
+  if (e != hipSuccess) return e;
+  const int R2 = r.R2 > r.R ? r.R2 : r.R;
+  hipLaunchKernelGGL(rowproj_reduce_kernel, dim3(nblk(r.T * R2, 256)), dim3(256), 0, st, r, rpartial,
+                     (int)((r.K + 255) / 256));
   return hipGetLastError();
 }
 
