@@ -336,6 +336,7 @@ struct QkvPlan {
   void *At, *Us, *BLt;     // forward
   void *Ps, *BLt_dx;       // backward
   float* partial;
+  float* rpartial;         // rowproj partials of the fused dQ / dK / dV passes
   size_t fwd_bytes, bwd_bytes;
 };
 
@@ -358,6 +359,9 @@ QkvPlan plan_qkv(const Ctx& c, const lora_qkv_desc& d, void* wf, void* wb) {
     for (int i = 0; i < 4; ++i) pf = cand[i] > pf ? cand[i] : pf;
   }
   p.partial = static_cast<float*>(b.take((size_t)pf * 4));
+  int64_t nmax = d.Nq > d.Nk ? d.Nq : d.Nk;
+  nmax = nmax > d.Nv ? nmax : d.Nv;
+  p.rpartial = c.bf16 ? static_cast<float*>(b.take((size_t)rowcol_partial_floats(T, nmax) * 4)) : nullptr;
   p.bwd_bytes = b.off;
   return p;
 }
@@ -382,6 +386,7 @@ struct OPlan {
   void *At, *Us, *BLt, *U_tmp;
   void *Ps, *BLt_dx;
   float* partial;
+  float* rpartial;  // rowproj partials of the fused dY pass
   size_t fwd_bytes, bwd_bytes;
 };
 
@@ -404,6 +409,7 @@ OPlan plan_o(const Ctx& c, int64_t T, int64_t K, int64_t N, int64_t r, bool tmp_
     pf = a > bb ? a : bb;
   }
   p.partial = static_cast<float*>(b.take((size_t)pf * 4));
+  p.rpartial = c.bf16 ? static_cast<float*>(b.take((size_t)rowcol_partial_floats(T, N) * 4)) : nullptr;
   p.bwd_bytes = b.off;
   return p;
 }
@@ -931,21 +937,18 @@ lora_status lora_qkv_bwd(const lora_qkv_desc* d, const void* dQ, const void* dK,
   const int64_t Ns[3] = {Nq, Nk, Nv};
   void* dBs[3] = {gr->dB_q, gr->dB_k, gr->dB_v};
 
-  // P_p = dZ_p B_p^T, each formed once: [s_q P_q | s_k P_k | s_v P_v]
+  // one pass over each dZ_p: P_p = dZ_p B_p^T, formed once into
+  // [s_q P_q | s_k P_k | s_v P_v], and dB_p = s_p U_p^T dZ_p
   for (int i = 0; i < 3; ++i) {
     const int R2 = (i == 2) ? (int)(RL - 2 * r) : (int)r;
     RowProjArgs ra = rowproj_args(dZ[i], Ns[i], T, Ns[i], projs[i]->B, Ns[i], (int)r, R2, (int)r);
     ra.scales[0] = projs[i]->scale;
     ra.out2 = offw(p.Ps, i * r, c);
     ra.ld2 = RL;
-    LAUNCHN("rowproj", st, launch_rowproj(c.bf16, ra, st));
-  }
-  // dB_p = s_p U_p^T dZ_p
-  for (int i = 0; i < 3; ++i) {
     ColProjArgs ca = colproj_args(dZ[i], Ns[i], T, Ns[i], coff(U, i * r, c), 3 * r, (int)r, (int)r, true, p.partial);
     ca.scales[0] = projs[i]->scale;
     ca.dest[0] = dBs[i];
-    LAUNCHN("colproj", st, launch_colproj(c.bf16, ca, st));
+    LAUNCHN("rowcol", st, launch_rowcol(c.bf16, ca, ra, p.rpartial, st));
   }
   // [dA_q | dA_k | dA_v] = X^T [s P] in one pass over X
   ColProjArgs cx = colproj_args(X, H, T, H, p.Ps, RL, (int)(3 * r), (int)r, false, p.partial);
@@ -1033,17 +1036,16 @@ lora_status lora_o_bwd(const lora_o_desc* d, const void* dY, const void* X, cons
   OPlan p = plan_o(c, T, K, N, r, false, nullptr, ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t RL = c.rl(r);
-  // P = dY B^T, formed once
+  // one pass over dY: P = dY B^T, formed once, and dB = s U^T dY
   RowProjArgs ra = rowproj_args(dY, N, T, N, o->B, N, (int)r, (int)RL, (int)r);
   ra.scales[0] = o->scale;
   ra.out2 = p.Ps;
   ra.ld2 = RL;
-  LAUNCHN("rowproj", st, launch_rowproj(c.bf16, ra, st));
-  // dB = s U^T dY ; dA = X^T (s P)
   ColProjArgs cb = colproj_args(dY, N, T, N, U, r, (int)r, (int)r, true, p.partial);
   cb.scales[0] = o->scale;
   cb.dest[0] = dB;
-  LAUNCHN("colproj", st, launch_colproj(c.bf16, cb, st));
+  LAUNCHN("rowcol", st, launch_rowcol(c.bf16, cb, ra, p.rpartial, st));
+  // dA = X^T (s P)
   ColProjArgs ca = colproj_args(X, K, T, K, p.Ps, RL, (int)r, (int)r, false, p.partial);
   ca.scales[0] = 1.0f;
   ca.dest[0] = dA;
