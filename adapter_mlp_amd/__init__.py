@@ -6,7 +6,8 @@ the C descriptors and calls the library.  All arithmetic runs in the
 library's HIP kernels.
 
 Layouts follow the C header: W [n_in, n_out], A [n_in, r], B [r, n_out],
-row-major; bf16 or fp32 compute; NF4 bases in bf16.
+row-major; bf16 or fp32 compute; NF4 bases in bf16.  bf16 inputs with fp32
+adapters select the fp32 LoRA-gradient mode (fp32 dA, dB).
 """
 from __future__ import annotations
 
@@ -45,6 +46,25 @@ def _dtype_code(t) -> int:
     if t.dtype == torch.float32:
         return L.LORA_F32
     raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _call_dtype(X, projs) -> int:
+    """dtype code of a call: X's dtype, or the fp32 LoRA-gradient mode
+    (LORA_BF16_F32LORA) when X is bf16 and the adapters are fp32.  Dense
+    bases must have X's dtype."""
+    torch = _torch()
+    ad = {t.dtype for p in projs for t in (p.A, p.B)}
+    if len(ad) != 1:
+        raise TypeError(f"the adapters of one call must share a dtype, got {sorted(map(str, ad))}")
+    for p in projs:
+        if p.W is not None and p.W.dtype != X.dtype:
+            raise TypeError(f"base weight dtype {p.W.dtype} differs from the input dtype {X.dtype}")
+    (a,) = ad
+    if a == X.dtype:
+        return _dtype_code(X)
+    if X.dtype == torch.bfloat16 and a == torch.float32:
+        return L.LORA_BF16_F32LORA
+    raise TypeError(f"adapters in {a} with inputs in {X.dtype} are not supported")
 
 
 def _stream(stream) -> int:
@@ -113,7 +133,7 @@ def mlp_fwd(X, gate: Proj, up: Proj, down: Proj, act="swiglu", *, Y=None, saved=
     T, H = X.shape
     I = gate.B.shape[1]
     r = gate.A.shape[1]
-    dt = _dtype_code(X)
+    dt = _call_dtype(X, (gate, up, down))
     d = L.lora_mlp_desc(T, H, I, r, L.ACT_CODES[act], dt)
     fb, _ = mlp_workspace_size(T, H, I, r, act, dt)
     if Y is None:
@@ -138,7 +158,7 @@ def mlp_bwd(dY, X, saved, gate: Proj, up: Proj, down: Proj, act="swiglu", *, dX=
     T, H = X.shape
     I = gate.B.shape[1]
     r = gate.A.shape[1]
-    dt = _dtype_code(X)
+    dt = _call_dtype(X, (gate, up, down))
     d = L.lora_mlp_desc(T, H, I, r, L.ACT_CODES[act], dt)
     _, bb = mlp_workspace_size(T, H, I, r, act, dt)
     if dX is None:
@@ -175,7 +195,7 @@ def qkv_fwd(X, q: Proj, k: Proj, v: Proj, *, out=None, U=None, ws=None, stream=N
     T, H = X.shape
     Ns = [p.B.shape[1] for p in (q, k, v)]
     r = q.A.shape[1]
-    dt = _dtype_code(X)
+    dt = _call_dtype(X, (q, k, v))
     d = L.lora_qkv_desc(T, H, Ns[0], Ns[1], Ns[2], r, dt, 0)
     fb, _ = qkv_workspace_size(T, H, *Ns, r, dt)
     if out is None:
@@ -196,7 +216,7 @@ def qkv_bwd(dQ, dK, dV, X, U, q: Proj, k: Proj, v: Proj, *, dX=None, grads=None,
     T, H = X.shape
     Ns = [p.B.shape[1] for p in (q, k, v)]
     r = q.A.shape[1]
-    dt = _dtype_code(X)
+    dt = _call_dtype(X, (q, k, v))
     d = L.lora_qkv_desc(T, H, Ns[0], Ns[1], Ns[2], r, dt, 0)
     _, bb = qkv_workspace_size(T, H, *Ns, r, dt)
     if dX is None:
@@ -227,7 +247,7 @@ def o_fwd(X, o: Proj, *, Y=None, U=None, ws=None, stream=None):
     T, K = X.shape
     N = o.B.shape[1]
     r = o.A.shape[1]
-    dt = _dtype_code(X)
+    dt = _call_dtype(X, (o,))
     d = L.lora_o_desc(T, K, N, r, dt, 0)
     fb, _ = o_workspace_size(T, K, N, r, dt)
     if Y is None:
@@ -248,7 +268,7 @@ def o_bwd(dY, X, U, o: Proj, *, dX=None, dA=None, dB=None, ws=None, stream=None)
     T, K = X.shape
     N = o.B.shape[1]
     r = o.A.shape[1]
-    dt = _dtype_code(X)
+    dt = _call_dtype(X, (o,))
     d = L.lora_o_desc(T, K, N, r, dt, 0)
     _, bb = o_workspace_size(T, K, N, r, dt)
     dX = torch.empty_like(X) if dX is None else dX

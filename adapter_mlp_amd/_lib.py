@@ -12,7 +12,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblora_mi355x.so")
 
 LORA_OK, LORA_EINVAL, LORA_ESHAPE, LORA_EDTYPE, LORA_EALIGN, LORA_EWORKSPACE, LORA_EUNSUPPORTED, LORA_EDEVICE = range(8)
-LORA_F32, LORA_BF16 = 0, 1
+LORA_F32, LORA_BF16, LORA_BF16_F32LORA = 0, 1, 2
 LORA_ACT_SWIGLU, LORA_ACT_GEGLU_TANH = 0, 1
 ACT_CODES = {"swiglu": LORA_ACT_SWIGLU, "geglu_tanh": LORA_ACT_GEGLU_TANH}
 STATUS_NAMES = {0: "LORA_OK", 1: "LORA_EINVAL", 2: "LORA_ESHAPE", 3: "LORA_EDTYPE", 4: "LORA_EALIGN",

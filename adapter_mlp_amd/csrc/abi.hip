@@ -51,7 +51,8 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct Ctx {
   bool bf16;
-  size_t es;  // element size
+  bool f32lora;  // LORA_BF16_F32LORA: fp32 adapters and adapter gradients
+  size_t es;     // element size of the activations and the base
   // Width of the GEMM's LoRA K tile: one full 64-wide tile (zero-padded) in bf16.
   int64_t rl(int64_t w) const { return bf16 ? 64 : w; }
 };
@@ -71,9 +72,12 @@ struct Ws {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-lora_status check_dtype(int32_t dtype, Ctx& c) {
-  CHECK(dtype == LORA_F32 || dtype == LORA_BF16, LORA_EDTYPE, "unknown dtype %d", dtype);
-  c.bf16 = dtype == LORA_BF16;
+// `adapters` admits LORA_BF16_F32LORA (the calls that take adapters).
+lora_status check_dtype(int32_t dtype, Ctx& c, bool adapters = false) {
+  CHECK(dtype == LORA_F32 || dtype == LORA_BF16 || (adapters && dtype == LORA_BF16_F32LORA), LORA_EDTYPE,
+        "unknown dtype %d", dtype);
+  c.bf16 = dtype != LORA_F32;
+  c.f32lora = dtype == LORA_BF16_F32LORA;
   c.es = c.bf16 ? 2 : 4;
   return LORA_OK;
 }
@@ -231,9 +235,11 @@ RowProjArgs rowproj_args(const void* Z, int64_t ldz, int64_t T, int64_t K, const
   return a;
 }
 
-ColProjArgs colproj_args(const void* Z, int64_t ldz, int64_t T, int64_t K, const void* P, int64_t ldp, int R,
-                         int seg_w, bool transposed, float* partial) {
+// Every colproj output is an adapter gradient: fp32 in the fp32 LoRA-gradient mode.
+ColProjArgs colproj_args(const Ctx& c, const void* Z, int64_t ldz, int64_t T, int64_t K, const void* P, int64_t ldp,
+                         int R, int seg_w, bool transposed, float* partial) {
   ColProjArgs a{};
+  a.out_f32 = c.f32lora ? 1 : 0;
   a.Z = Z;
   a.ldz = ldz;
   a.T = T;
@@ -266,6 +272,50 @@ lora_status check_ws(const void* ws, size_t have, size_t need) {
   return LORA_OK;
 }
 
+// fp32 LoRA-gradient mode: each call first casts its fp32 adapters to bf16
+// (round to nearest even) into its workspace and then runs the bf16 path on
+// the casts.  The cast area comes first in both workspaces.
+struct AdapterDims {
+  int64_t n_in, n_out;
+};
+
+int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
+
+size_t staged_bytes(const Ctx& c, const AdapterDims* d, int n, int64_t r) {
+  if (!c.f32lora) return 0;
+  int64_t b = 0;
+  for (int i = 0; i < n; ++i) b += round256(d[i].n_in * r * 2) + round256(r * d[i].n_out * 2);
+  return (size_t)b;
+}
+
+// out[i] = in[i] with A, B replaced by their bf16 casts in `area` (the
+// staged_bytes area) when c.f32lora, else a plain copy.  Returns the cast
+// launch's arguments (no segments unless c.f32lora).
+CastArgs stage_adapters(const Ctx& c, void* area, const lora_proj* const* in, const AdapterDims* d, int n,
+                        int64_t r, lora_proj* out) {
+  CastArgs a{};
+  char* q = static_cast<char*>(area);
+  for (int i = 0; i < n; ++i) {
+    out[i] = *in[i];
+    if (!c.f32lora) continue;
+    uint16_t* Ab = reinterpret_cast<uint16_t*>(q);
+    q += round256(d[i].n_in * r * 2);
+    uint16_t* Bb = reinterpret_cast<uint16_t*>(q);
+    q += round256(r * d[i].n_out * 2);
+    a.seg[a.nseg++] = CastSeg{static_cast<const float*>(in[i]->A), Ab, d[i].n_in * r};
+    a.seg[a.nseg++] = CastSeg{static_cast<const float*>(in[i]->B), Bb, r * d[i].n_out};
+    out[i].A = Ab;
+    out[i].B = Bb;
+  }
+  return a;
+}
+
+#define STAGE(area, in, dims, n, r, out, st)                      \
+  do {                                                            \
+    const CastArgs ca_ = stage_adapters(c, area, in, dims, n, r, out); \
+    if (c.f32lora) LAUNCHN("cast", st, launch_cast_bf16(ca_, st)); \
+  } while (0)
+
 float* partial_buf(Ws& w, const Ctx& c, int64_t T, int64_t K, int R) {
   if (!c.bf16) return nullptr;
   return static_cast<float*>(w.take((size_t)colproj_partial_floats(T, K, R) * 4));
@@ -275,6 +325,7 @@ float* partial_buf(Ws& w, const Ctx& c, int64_t T, int64_t K, int R) {
 // MLP
 // ---------------------------------------------------------------------------
 struct MlpPlan {
+  void *ad_f, *ad_b;  // adapter casts (fp32 LoRA-gradient mode), fwd / bwd workspace
   void *At_gu, *Us_gu, *BLt_gu, *h, *At_d, *Us_d, *BLt_d;                  // forward
   void *Ps_d, *BLt_dh, *hb, *dg, *de, *Ps_ug, *BLt_dx;                      // backward
   float* partial;
@@ -286,7 +337,9 @@ MlpPlan plan_mlp(const Ctx& c, const lora_mlp_desc& d, void* ws_fwd, void* ws_bw
   MlpPlan p{};
   const int64_t T = d.T, H = d.H, I = d.I, r = d.r;
   const int64_t RLg = c.rl(2 * r), RLd = c.rl(r);
+  const AdapterDims ad[3] = {{H, I}, {H, I}, {I, H}};
   Ws f(ws_fwd);
+  p.ad_f = f.take(staged_bytes(c, ad, 3, r));
   p.At_gu = f.take(2 * r * H * c.es);
   p.Us_gu = f.take(T * RLg * c.es);
   p.BLt_gu = f.take(2 * I * RLg * c.es);
@@ -296,6 +349,7 @@ MlpPlan plan_mlp(const Ctx& c, const lora_mlp_desc& d, void* ws_fwd, void* ws_bw
   p.BLt_d = f.take(H * RLd * c.es);
   p.fwd_bytes = f.off;
   Ws b(ws_bwd);
+  p.ad_b = b.take(staged_bytes(c, ad, 3, r));
   p.Ps_d = b.take(T * RLd * c.es);
   p.BLt_dh = b.take(I * RLd * c.es);
   p.hb = b.take(T * I * c.es);
@@ -317,7 +371,7 @@ MlpPlan plan_mlp(const Ctx& c, const lora_mlp_desc& d, void* ws_fwd, void* ws_bw
 
 lora_status validate_mlp(const lora_mlp_desc* d, Ctx& c) {
   CHECK(d != nullptr, LORA_EINVAL, "desc is NULL");
-  TRY(check_dtype(d->dtype, c));
+  TRY(check_dtype(d->dtype, c, true));
   CHECK(d->act == LORA_ACT_SWIGLU || d->act == LORA_ACT_GEGLU_TANH, LORA_EINVAL, "unknown activation %d", d->act);
   CHECK(d->T >= 0, LORA_ESHAPE, "T = %lld is negative", (long long)d->T);
   TRY(check_dim(c, d->H, "H"));
@@ -333,6 +387,7 @@ lora_status validate_mlp(const lora_mlp_desc* d, Ctx& c) {
 // Q/K/V and O
 // ---------------------------------------------------------------------------
 struct QkvPlan {
+  void *ad_f, *ad_b;       // adapter casts (fp32 LoRA-gradient mode)
   void *At, *Us, *BLt;     // forward
   void *Ps, *BLt_dx;       // backward
   float* partial;
@@ -344,12 +399,15 @@ QkvPlan plan_qkv(const Ctx& c, const lora_qkv_desc& d, void* wf, void* wb) {
   QkvPlan p{};
   const int64_t T = d.T, H = d.H, r = d.r, N = d.Nq + d.Nk + d.Nv;
   const int64_t RL = c.rl(3 * r);
+  const AdapterDims ad[3] = {{H, d.Nq}, {H, d.Nk}, {H, d.Nv}};
   Ws f(wf);
+  p.ad_f = f.take(staged_bytes(c, ad, 3, r));
   p.At = f.take(3 * r * H * c.es);
   p.Us = f.take(T * RL * c.es);
   p.BLt = f.take(N * RL * c.es);
   p.fwd_bytes = f.off;
   Ws b(wb);
+  p.ad_b = b.take(staged_bytes(c, ad, 3, r));
   p.Ps = b.take(T * RL * c.es);
   p.BLt_dx = b.take(H * RL * c.es);
   int64_t pf = 0;
@@ -368,7 +426,7 @@ QkvPlan plan_qkv(const Ctx& c, const lora_qkv_desc& d, void* wf, void* wb) {
 
 lora_status validate_qkv(const lora_qkv_desc* d, Ctx& c) {
   CHECK(d != nullptr, LORA_EINVAL, "desc is NULL");
-  TRY(check_dtype(d->dtype, c));
+  TRY(check_dtype(d->dtype, c, true));
   CHECK(d->reserved == 0, LORA_EINVAL, "reserved field must be 0");
   CHECK(d->T >= 0, LORA_ESHAPE, "T = %lld is negative", (long long)d->T);
   TRY(check_dim(c, d->H, "H"));
@@ -383,6 +441,7 @@ lora_status validate_qkv(const lora_qkv_desc* d, Ctx& c) {
 }
 
 struct OPlan {
+  void *ad_f, *ad_b;  // adapter casts (fp32 LoRA-gradient mode)
   void *At, *Us, *BLt, *U_tmp;
   void *Ps, *BLt_dx;
   float* partial;
@@ -394,13 +453,16 @@ struct OPlan {
 OPlan plan_o(const Ctx& c, int64_t T, int64_t K, int64_t N, int64_t r, bool tmp_u, void* wf, void* wb) {
   OPlan p{};
   const int64_t RL = c.rl(r);
+  const AdapterDims ad[1] = {{K, N}};
   Ws f(wf);
+  p.ad_f = f.take(staged_bytes(c, ad, 1, r));
   p.At = f.take(r * K * c.es);
   p.Us = f.take(T * RL * c.es);
   p.BLt = f.take(N * RL * c.es);
   p.U_tmp = tmp_u ? f.take(T * r * c.es) : nullptr;
   p.fwd_bytes = f.off;
   Ws b(wb);
+  p.ad_b = b.take(staged_bytes(c, ad, 1, r));
   p.Ps = b.take(T * RL * c.es);
   p.BLt_dx = b.take(K * RL * c.es);
   int64_t pf = 0;
@@ -416,7 +478,7 @@ OPlan plan_o(const Ctx& c, int64_t T, int64_t K, int64_t N, int64_t r, bool tmp_
 
 lora_status validate_o(const lora_o_desc* d, Ctx& c) {
   CHECK(d != nullptr, LORA_EINVAL, "desc is NULL");
-  TRY(check_dtype(d->dtype, c));
+  TRY(check_dtype(d->dtype, c, true));
   CHECK(d->reserved == 0, LORA_EINVAL, "reserved field must be 0");
   CHECK(d->T >= 0, LORA_ESHAPE, "T = %lld is negative", (long long)d->T);
   TRY(check_dim(c, d->K, "K"));
@@ -568,6 +630,13 @@ lora_status lora_mlp_fwd(const lora_mlp_desc* d, const void* X, const lora_proj*
   MlpPlan p = plan_mlp(c, *d, ws, nullptr);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t RLg = c.rl(2 * r), RLd = c.rl(r);
+  const lora_proj* in[3] = {gate, up, down};
+  const AdapterDims ad[3] = {{H, I}, {H, I}, {I, H}};
+  lora_proj sp[3];
+  STAGE(p.ad_f, in, ad, 3, r, sp, st);
+  gate = &sp[0];
+  up = &sp[1];
+  down = &sp[2];
 
   // adapter inputs of gate and up in one pass over X: [U_g | U_u] = X [A_g | A_u]
   const void* srcs_gu[2] = {gate->A, up->A};
@@ -695,6 +764,13 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, 
   MlpPlan p = plan_mlp(c, *d, nullptr, ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t RLg = c.rl(2 * r), RLd = c.rl(r);
+  const lora_proj* in[3] = {gate, up, down};
+  const AdapterDims ad[3] = {{H, I}, {H, I}, {I, H}};
+  lora_proj sp[3];
+  STAGE(p.ad_b, in, ad, 3, r, sp, st);
+  gate = &sp[0];
+  up = &sp[1];
+  down = &sp[2];
   const void* U = saved->U;
 
   // one pass over dY: P_d = dY B_d^T, formed once (scaled copy feeds dA_d and
@@ -703,7 +779,7 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, 
   r1.scales[0] = down->scale;
   r1.out2 = p.Ps_d;
   r1.ld2 = RLd;
-  ColProjArgs c1 = colproj_args(dY, H, T, H, coff(U, 2 * r, c), 3 * r, (int)r, (int)r, true, p.partial);
+  ColProjArgs c1 = colproj_args(c, dY, H, T, H, coff(U, 2 * r, c), 3 * r, (int)r, (int)r, true, p.partial);
   c1.scales[0] = down->scale;
   c1.dest[0] = gr->dB_down;
   LAUNCHN("rowcol", st, launch_rowcol(c.bf16, c1, r1, p.rpartial, st));
@@ -743,7 +819,7 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, 
   LAUNCH(gemm_on(c, g, st, I));
 
   // dA_d = s_d h^T P_d  (P_d already scaled)
-  ColProjArgs c2 = colproj_args(p.hb, I, T, I, p.Ps_d, RLd, (int)r, (int)r, false, p.partial);
+  ColProjArgs c2 = colproj_args(c, p.hb, I, T, I, p.Ps_d, RLd, (int)r, (int)r, false, p.partial);
   c2.scales[0] = 1.0f;
   c2.dest[0] = gr->dA_down;
   LAUNCHN("colproj", st, launch_colproj(c.bf16, c2, st));
@@ -754,7 +830,7 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, 
   r2.scales[0] = up->scale;
   r2.out2 = p.Ps_ug;
   r2.ld2 = RLg;
-  ColProjArgs c3 = colproj_args(p.dg, I, T, I, coff(U, r, c), 3 * r, (int)r, (int)r, true, p.partial);
+  ColProjArgs c3 = colproj_args(c, p.dg, I, T, I, coff(U, r, c), 3 * r, (int)r, (int)r, true, p.partial);
   c3.scales[0] = up->scale;
   c3.dest[0] = gr->dB_up;
   LAUNCHN("rowcol", st, launch_rowcol(c.bf16, c3, r2, p.rpartial, st));
@@ -762,13 +838,13 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, 
   r3.scales[0] = gate->scale;
   r3.out2 = offw(p.Ps_ug, r, c);
   r3.ld2 = RLg;
-  ColProjArgs c4 = colproj_args(p.de, I, T, I, U, 3 * r, (int)r, (int)r, true, p.partial);
+  ColProjArgs c4 = colproj_args(c, p.de, I, T, I, U, 3 * r, (int)r, (int)r, true, p.partial);
   c4.scales[0] = gate->scale;
   c4.dest[0] = gr->dB_gate;
   LAUNCHN("rowcol", st, launch_rowcol(c.bf16, c4, r3, p.rpartial, st));
 
   // [dA_u | dA_g] = X^T [s_u P_u | s_g P_g] in one pass over X
-  ColProjArgs c5 = colproj_args(X, H, T, H, p.Ps_ug, RLg, (int)(2 * r), (int)r, false, p.partial);
+  ColProjArgs c5 = colproj_args(c, X, H, T, H, p.Ps_ug, RLg, (int)(2 * r), (int)r, false, p.partial);
   c5.scales[0] = 1.0f;
   c5.scales[1] = 1.0f;
   c5.dest[0] = gr->dA_up;
@@ -846,6 +922,13 @@ lora_status lora_qkv_fwd(const lora_qkv_desc* d, const void* X, const lora_proj*
   QkvPlan p = plan_qkv(c, *d, ws, nullptr);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t RL = c.rl(3 * r);
+  const lora_proj* in[3] = {q, k, v};
+  const AdapterDims ad[3] = {{H, Nq}, {H, Nk}, {H, Nv}};
+  lora_proj sp[3];
+  STAGE(p.ad_f, in, ad, 3, r, sp, st);
+  q = &sp[0];
+  k = &sp[1];
+  v = &sp[2];
 
   // [U_q | U_k | U_v] = X [A_q | A_k | A_v] in one pass over X
   const void* srcs[3] = {q->A, k->A, v->A};
@@ -932,6 +1015,13 @@ lora_status lora_qkv_bwd(const lora_qkv_desc* d, const void* dQ, const void* dK,
   QkvPlan p = plan_qkv(c, *d, nullptr, ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t RL = c.rl(3 * r);
+  const lora_proj* in[3] = {q, k, v};
+  const AdapterDims ad[3] = {{H, Nq}, {H, Nk}, {H, Nv}};
+  lora_proj sp[3];
+  STAGE(p.ad_b, in, ad, 3, r, sp, st);
+  q = &sp[0];
+  k = &sp[1];
+  v = &sp[2];
   const lora_proj* projs[3] = {q, k, v};
   const void* dZ[3] = {dQ, dK, dV};
   const int64_t Ns[3] = {Nq, Nk, Nv};
@@ -945,13 +1035,13 @@ lora_status lora_qkv_bwd(const lora_qkv_desc* d, const void* dQ, const void* dK,
     ra.scales[0] = projs[i]->scale;
     ra.out2 = offw(p.Ps, i * r, c);
     ra.ld2 = RL;
-    ColProjArgs ca = colproj_args(dZ[i], Ns[i], T, Ns[i], coff(U, i * r, c), 3 * r, (int)r, (int)r, true, p.partial);
+    ColProjArgs ca = colproj_args(c, dZ[i], Ns[i], T, Ns[i], coff(U, i * r, c), 3 * r, (int)r, (int)r, true, p.partial);
     ca.scales[0] = projs[i]->scale;
     ca.dest[0] = dBs[i];
     LAUNCHN("rowcol", st, launch_rowcol(c.bf16, ca, ra, p.rpartial, st));
   }
   // [dA_q | dA_k | dA_v] = X^T [s P] in one pass over X
-  ColProjArgs cx = colproj_args(X, H, T, H, p.Ps, RL, (int)(3 * r), (int)r, false, p.partial);
+  ColProjArgs cx = colproj_args(c, X, H, T, H, p.Ps, RL, (int)(3 * r), (int)r, false, p.partial);
   cx.scales[0] = cx.scales[1] = cx.scales[2] = 1.0f;
   cx.dest[0] = gr->dA_q;
   cx.dest[1] = gr->dA_k;
@@ -1015,7 +1105,11 @@ lora_status lora_o_fwd(const lora_o_desc* d, const void* X, const lora_proj* o, 
   TRY(check_ws(ws, ws_bytes, need.fwd_bytes));
   if (d->T == 0) return LORA_OK;
   OPlan p = plan_o(c, d->T, d->K, d->N, d->r, false, ws, nullptr);
-  return proj_forward(c, d->T, d->K, d->N, d->r, X, o, Y, U, p, static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const AdapterDims ad[1] = {{d->K, d->N}};
+  lora_proj sp[1];
+  STAGE(p.ad_f, &o, ad, 1, d->r, sp, st);
+  return proj_forward(c, d->T, d->K, d->N, d->r, X, &sp[0], Y, U, p, st);
 }
 
 lora_status lora_o_bwd(const lora_o_desc* d, const void* dY, const void* X, const void* U, const lora_proj* o,
@@ -1036,17 +1130,21 @@ lora_status lora_o_bwd(const lora_o_desc* d, const void* dY, const void* X, cons
   OPlan p = plan_o(c, T, K, N, r, false, nullptr, ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t RL = c.rl(r);
+  const AdapterDims ad[1] = {{K, N}};
+  lora_proj sp[1];
+  STAGE(p.ad_b, &o, ad, 1, r, sp, st);
+  o = &sp[0];
   // one pass over dY: P = dY B^T, formed once, and dB = s U^T dY
   RowProjArgs ra = rowproj_args(dY, N, T, N, o->B, N, (int)r, (int)RL, (int)r);
   ra.scales[0] = o->scale;
   ra.out2 = p.Ps;
   ra.ld2 = RL;
-  ColProjArgs cb = colproj_args(dY, N, T, N, U, r, (int)r, (int)r, true, p.partial);
+  ColProjArgs cb = colproj_args(c, dY, N, T, N, U, r, (int)r, (int)r, true, p.partial);
   cb.scales[0] = o->scale;
   cb.dest[0] = dB;
   LAUNCHN("rowcol", st, launch_rowcol(c.bf16, cb, ra, p.rpartial, st));
   // dA = X^T (s P)
-  ColProjArgs ca = colproj_args(X, K, T, K, p.Ps, RL, (int)r, (int)r, false, p.partial);
+  ColProjArgs ca = colproj_args(c, X, K, T, K, p.Ps, RL, (int)r, (int)r, false, p.partial);
   ca.scales[0] = 1.0f;
   ca.dest[0] = dA;
   LAUNCHN("colproj", st, launch_colproj(c.bf16, ca, st));

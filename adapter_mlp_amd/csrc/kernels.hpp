@@ -118,7 +118,8 @@ struct ColProjArgs {
   // per-column-block partials [K / 256, T, 16] fp32
   const void* Bt;
   int64_t ldb;
-  int32_t R1, pad_;
+  int32_t R1;
+  int32_t out_f32;  // bf16 path: dest[] are fp32 (else bf16)
   float* rpartial;
 };
 
@@ -161,6 +162,19 @@ hipError_t launch_pack_lora_b(bool bf16, const PackLoraArgs& a, hipStream_t st);
 hipError_t launch_pack_cat_t(bool bf16, void* out, int64_t K, int Rpad, int w, int nparts,
                              const void* const* srcs, hipStream_t st);
 hipError_t launch_zero(void* p, int64_t bytes, hipStream_t st);
+
+// fp32 -> bf16 (round to nearest even) of up to six arrays in one launch: the
+// adapter cast of the fp32 LoRA-gradient mode.
+struct CastSeg {
+  const float* src;
+  uint16_t* dst;
+  int64_t n;
+};
+struct CastArgs {
+  CastSeg seg[6];
+  int32_t nseg;
+};
+hipError_t launch_cast_bf16(const CastArgs& a, hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // NF4 kernels.

@@ -372,7 +372,7 @@ __global__ void colproj_reduce_kernel(const ColProjArgs a, int Rp) {
   const int j = (int)(e % a.R);
   float v = 0.0f;
   for (int c = 0; c < a.nchunk; ++c) v += a.partial[(c * a.K + k) * Rp + j];
-  colproj_store(a, true, k, j, v);
+  colproj_store(a, a.out_f32 == 0, k, j, v);
 }
 
 __global__ void colproj_f32_kernel(const ColProjArgs a) {
@@ -422,6 +422,12 @@ __global__ void pack_cat_t_kernel(E* out, int64_t K, int Rpad, int w, int nparts
   E val = E(0);
   if (j < nparts * w) val = static_cast<const E*>(srcs.s[j / w])[k * w + (j % w)];
   out[e] = val;
+}
+
+__global__ void cast_bf16_kernel(const CastArgs a) {
+  const CastSeg& q = a.seg[blockIdx.y];
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < q.n; e += (int64_t)gridDim.x * blockDim.x)
+    q.dst[e] = (uint16_t)f2bf(q.src[e]);
 }
 
 __global__ void zero_kernel(uint32_t* p, int64_t n) {
@@ -559,6 +565,15 @@ hipError_t launch_pack_cat_t(bool bf16, void* out, int64_t K, int Rpad, int w, i
   else
     hipLaunchKernelGGL(pack_cat_t_kernel<float>, dim3(nblk(n, 256)), dim3(256), 0, st,
                        static_cast<float*>(out), K, Rpad, w, nparts, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_bf16(const CastArgs& a, hipStream_t st) {
+  int64_t nmax = 0;
+  for (int i = 0; i < a.nseg; ++i) nmax = a.seg[i].n > nmax ? a.seg[i].n : nmax;
+  if (a.nseg <= 0 || nmax == 0) return hipSuccess;
+  const unsigned bx = nblk(nmax, 256) < 256 ? nblk(nmax, 256) : 256u;
+  hipLaunchKernelGGL(cast_bf16_kernel, dim3(bx, (unsigned)a.nseg), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -262,16 +262,18 @@ class MlpStep:
     def __init__(self, cfg, inp, lm, torch):
         self.cfg, self.lm = cfg, lm
         dev = lambda a: torch.from_numpy(a).to("cuda:0").to(torch.bfloat16)  # noqa: E731
+        adt = torch.float32 if cfg.lora_dtype == "f32" else torch.bfloat16
+        adev = lambda a: torch.from_numpy(a).to("cuda:0").to(adt)  # noqa: E731
         self.X, self.dY = dev(inp["X"]), dev(inp["dY"])
         self.p = {}
         for k in ("gate", "up", "down"):
             nf4 = None
             if cfg.nf4:
                 nf4 = lm.nf4_quantize(dev(inp[k]["W"]))
-            self.p[k] = lm.Proj(A=dev(inp[k]["A"]), B=dev(inp[k]["B"]), scale=inp[k]["s"],
+            self.p[k] = lm.Proj(A=adev(inp[k]["A"]), B=adev(inp[k]["B"]), scale=inp[k]["s"],
                                 W=None if cfg.nf4 else dev(inp[k]["W"]), nf4=nf4)
         T, H, I, r = cfg.T, cfg.H, cfg.I, cfg.r
-        fb, bb = lm.mlp_workspace_size(T, H, I, r, cfg.act)
+        fb, bb = lm.mlp_workspace_size(T, H, I, r, cfg.act, lm._call_dtype(self.X, list(self.p.values())))
         bf = torch.bfloat16
         self.Y = torch.empty((T, H), dtype=bf, device="cuda:0")
         self.saved = dict(e=torch.empty((T, I), dtype=bf, device="cuda:0"),
@@ -295,8 +297,10 @@ class AttnStep:
     def __init__(self, cfg, inp, lm, torch):
         self.cfg, self.lm = cfg, lm
         dev = lambda a: torch.from_numpy(a).to("cuda:0").to(torch.bfloat16)  # noqa: E731
+        adt = torch.float32 if cfg.lora_dtype == "f32" else torch.bfloat16
+        adev = lambda a: torch.from_numpy(a).to("cuda:0").to(adt)  # noqa: E731
         self.t = {k: dev(inp[k]) for k in ("X", "Xo", "dQ", "dK", "dV", "dO")}
-        self.p = {k: lm.Proj(A=dev(inp[k]["A"]), B=dev(inp[k]["B"]), scale=inp[k]["s"], W=dev(inp[k]["W"]))
+        self.p = {k: lm.Proj(A=adev(inp[k]["A"]), B=adev(inp[k]["B"]), scale=inp[k]["s"], W=dev(inp[k]["W"]))
                   for k in ("q", "k", "v", "o")}
         T, H, r = cfg.T, cfg.H, cfg.r
         bf = torch.bfloat16
@@ -366,6 +370,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--lora-dtype", default="bf16", choices=["bf16", "f32"],
+                    help="f32: fp32 adapters and adapter gradients with bf16 inputs (fp32 LoRA-gradient mode)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -395,7 +401,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     lm.load()
     cfg = CONFIGS[args.config]
-    log(f"[bench] config {cfg.cid}: {cfg.note}; generating seeded inputs")
+    if args.lora_dtype == "f32":
+        cfg = cfg.with_(lora_dtype="f32")
+    log(f"[bench] config {cfg.cid}: {cfg.note}; adapters {args.lora_dtype}; generating seeded inputs")
     t0 = time.time()
     inp = make_mlp_inputs(cfg) if cfg.kind == "mlp" else make_attn_inputs(cfg)
     log(f"[bench] inputs ready in {time.time() - t0:.1f} s")
@@ -475,6 +483,7 @@ def main():
                    **({"intermediate": cfg.I, "activation": cfg.act} if cfg.kind == "mlp"
                       else {"q": cfg.Nq, "k": cfg.Nk, "v": cfg.Nv, "o": [cfg.Nq, cfg.H]}),
                    "rank": cfg.r, "alpha": cfg.alpha, "base": "nf4" if cfg.nf4 else "bf16",
+                   "adapters": args.lora_dtype,
                    "parallelism": "single GPU"},
         "tflops": tflops,
         "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,

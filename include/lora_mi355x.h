@@ -34,7 +34,14 @@
  * dtype.  One compute dtype per call: LORA_BF16 (bf16 in and out, fp32
  *   accumulation) or LORA_F32 (fp32 throughout).  Every dense tensor of the
  *   call (X, W, A, B, outputs, saved tensors) has that dtype.  NF4 bases need
- *   LORA_BF16.
+ *   bf16 compute (LORA_BF16 or LORA_BF16_F32LORA).
+ *   LORA_BF16_F32LORA is the fp32 LoRA-gradient mode ([LO] "FP32 LoRA
+ *   gradients"): the adapters A, B and the gradients dA, dB are fp32; every
+ *   other tensor (X, W, dY, outputs, saved e, g, U, dX) is bf16.  Each call
+ *   first casts A and B to bf16 (round to nearest even) into its workspace and
+ *   runs the bf16 path on the casts; dA and dB are the fp32 sums of the bf16
+ *   products, times s, stored without the final rounding to bf16.  The
+ *   rank-r intermediates (U, P) stay bf16, as in LORA_BF16.
  * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *   enqueue work on it and return; inputs are read-only; results are ready
  *   when the stream reaches them.  Calls on distinct streams with distinct
@@ -44,7 +51,7 @@
  *   nothing and writes nothing.  A launch failure reported by the HIP runtime
  *   after enqueue returns LORA_EDEVICE.  lora_last_error() gives a text detail
  *   of the calling thread's last failure.
- * Shapes (bf16).  T >= 0 is any token count (T = 0 is a no-op that still
+ * Shapes (both bf16 modes).  T >= 0 is any token count (T = 0 is a no-op that still
  *   zero-fills adapter gradients).  Feature widths (H, I, Nq, Nk, Nv, K, N)
  *   must be positive multiples of 64 and r a multiple of 8 in [8, 64], with
  *   the concatenated adapter width of a shared-input group (2r for gate/up,
@@ -75,7 +82,7 @@ typedef enum lora_status {
   LORA_EDEVICE = 7       /* HIP runtime reported an error */
 } lora_status;
 
-typedef enum lora_dtype { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
+typedef enum lora_dtype { LORA_F32 = 0, LORA_BF16 = 1, LORA_BF16_F32LORA = 2 } lora_dtype;
 
 /* Gated activation phi of h = phi(e) * g ([LO] "Triton kernels"):
  *   SWIGLU:      phi(x) = x * sigmoid(x)
@@ -104,7 +111,8 @@ typedef struct lora_nf4 {
 } lora_nf4;
 
 /* One LoRA projection: exactly one of W (dense, compute dtype) and nf4 is
- * non-NULL.  A [n_in, r], B [r, n_out] in the compute dtype; scale = s. */
+ * non-NULL.  A [n_in, r], B [r, n_out] in the compute dtype (fp32 under
+ * LORA_BF16_F32LORA); scale = s. */
 typedef struct lora_proj {
   const void* W;
   const lora_nf4* nf4;
@@ -146,7 +154,8 @@ typedef struct lora_mlp_saved {
   void* U;
 } lora_mlp_saved;
 
-/* Adapter gradients written by the backward (each the layout of its A/B). */
+/* Adapter gradients written by the backward (each the layout and dtype of its
+ * A/B). */
 typedef struct lora_mlp_grads {
   void* dA_gate;
   void* dB_gate;

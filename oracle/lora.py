@@ -24,6 +24,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from .nf4 import round_to_bf16
+
 # --------------------------------------------------------------------------
 # Activations.  "LoRA Optimizations", section "Triton kernels": the MLP uses a
 # SwiGLU or a GeGLU activation with fused forward and backward kernels; the
@@ -187,6 +189,27 @@ def o_fwd(X, o):
 def o_bwd(dY, X, saved, o, hoist=True):
     dX, dA, dB = proj_bwd(dY, X, o["W"], o["A"], o["B"], o["s"], saved["U"], hoist)
     return dict(dX=dX, dA=dA, dB=dB)
+
+
+# --------------------------------------------------------------------------
+# fp32 LoRA-gradient mode ("LoRA Optimizations", section "FP32 LoRA
+# gradients"): the adapters and their gradients are fp32 while the products
+# keep 16-bit inputs, and the parameter gradients come out in fp32.  The
+# unsloth diff's backward casts every adapter to the compute dtype before its
+# first product (``gateA.to(dtype)`` and so on in LoRA_MLP and LoRA_QKV), so
+# the mode multiplies with the adapters rounded to bf16.
+# --------------------------------------------------------------------------
+
+
+def to_compute_adapters(p):
+    """Projection dict with A and B rounded to bf16 (nearest even), held in
+    fp32: the adapters the fp32 LoRA-gradient mode multiplies with.  Given
+    these, the functions above produce that mode's outputs; its dA and dB are
+    their fp32 gradients as they stand, with no rounding to bf16."""
+    q = dict(p)
+    q["A"] = round_to_bf16(np.asarray(p["A"], dtype=np.float32))
+    q["B"] = round_to_bf16(np.asarray(p["B"], dtype=np.float32))
+    return q
 
 
 def as_dtype(p, dtype):

@@ -39,8 +39,11 @@ def assert_close(name, got, ref, tol):
     assert e <= tol, f"{name}: max|err|/max|ref| = {e:.3e} > {tol:g}"
 
 
-def proj_dev(p, dtype="bf16", nf4=None):
+def proj_dev(p, dtype="bf16", nf4=None, adapters=None):
+    """Device projection; ``adapters="f32"`` keeps A and B in fp32 (the fp32
+    LoRA-gradient mode when ``dtype`` is bf16)."""
     import adapter_mlp_amd as lm
 
-    return lm.Proj(A=dev(p["A"], dtype), B=dev(p["B"], dtype), scale=p["s"],
+    ad = adapters or dtype
+    return lm.Proj(A=dev(p["A"], ad), B=dev(p["B"], ad), scale=p["s"],
                    W=None if nf4 is not None else dev(p["W"], dtype), nf4=nf4)

@@ -169,3 +169,47 @@ def _load_fresh(path):
         return _lib.load(path)
     finally:
         _lib._lib = saved
+
+
+def test_fp32_lora_mode_workspace_and_dtype_rules(L):
+    """LORA_BF16_F32LORA (fp32 adapters and adapter gradients, bf16 otherwise)
+    has the bf16 shape rules, and each workspace grows by the bf16 casts of
+    the adapters (each cast 256-byte aligned)."""
+    sz = C.c_size_t
+    T, H, I, r = 300, 256, 768, 16
+    fb, bb, ff, bf = sz(), sz(), sz(), sz()
+    d = L.lora_mlp_desc(T, H, I, r, 0, L.LORA_BF16)
+    assert _status(L, "lora_mlp_workspace_size", C.byref(d), C.byref(fb), C.byref(bb)) == L.LORA_OK
+    d2 = L.lora_mlp_desc(T, H, I, r, 0, L.LORA_BF16_F32LORA)
+    assert _status(L, "lora_mlp_workspace_size", C.byref(d2), C.byref(ff), C.byref(bf)) == L.LORA_OK
+    cast = 3 * (H * r * 2 + r * I * 2)  # every piece here is already a multiple of 256 bytes
+    assert ff.value - fb.value == cast and bf.value - bb.value == cast
+    bad = L.lora_mlp_desc(T, H, 720, r, 0, L.LORA_BF16_F32LORA)  # bf16 rule: widths % 64
+    assert _status(L, "lora_mlp_workspace_size", C.byref(bad), C.byref(ff), C.byref(bf)) == L.LORA_ESHAPE
+    dq = L.lora_qkv_desc(T, H, 256, 128, 64, r, L.LORA_BF16_F32LORA, 0)
+    assert _status(L, "lora_qkv_workspace_size", C.byref(dq), C.byref(ff), C.byref(bf)) == L.LORA_OK
+    do = L.lora_o_desc(T, 256, 512, r, L.LORA_BF16_F32LORA, 0)
+    assert _status(L, "lora_o_workspace_size", C.byref(do), C.byref(ff), C.byref(bf)) == L.LORA_OK
+    # the NF4 format calls take a tensor dtype, not a mode
+    nbytes = sz()
+    assert _status(L, "lora_nf4_quantize_workspace_size", 256, 256, C.byref(nbytes)) == L.LORA_OK
+    assert _status(L, "lora_nf4_quantize", FAKE, 256, 256, L.LORA_BF16_F32LORA, FAKE, FAKE, FAKE, FAKE, FAKE,
+                   nbytes.value, None) == L.LORA_EDTYPE
+
+
+def test_binding_picks_fp32_lora_mode_from_adapter_dtype():
+    import torch
+
+    import adapter_mlp_amd as lm
+    from adapter_mlp_amd import _lib
+
+    X = torch.zeros(4, 64, dtype=torch.bfloat16)
+    p32 = lm.Proj(A=torch.zeros(64, 8), B=torch.zeros(8, 64), scale=1.0, W=torch.zeros(64, 64, dtype=torch.bfloat16))
+    p16 = lm.Proj(A=torch.zeros(64, 8, dtype=torch.bfloat16), B=torch.zeros(8, 64, dtype=torch.bfloat16), scale=1.0,
+                  W=torch.zeros(64, 64, dtype=torch.bfloat16))
+    assert lm._call_dtype(X, (p32,)) == _lib.LORA_BF16_F32LORA
+    assert lm._call_dtype(X, (p16,)) == _lib.LORA_BF16
+    with pytest.raises(TypeError):
+        lm._call_dtype(X, (p32, p16))  # mixed adapter dtypes
+    with pytest.raises(TypeError):
+        lm._call_dtype(X.float(), (p16,))  # bf16 adapters with fp32 inputs

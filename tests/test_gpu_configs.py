@@ -34,11 +34,11 @@ def lm():
     return adapter_mlp_amd
 
 
-def _mlp_full(lm, cid):
+def _mlp_full(lm, cid, lora_dtype=""):
     import torch
 
-    cfg = CONFIGS[cid]
-    say(f"config {cid}: generating inputs ({cfg.note})")
+    cfg = CONFIGS[cid].with_(lora_dtype=lora_dtype)
+    say(f"config {cid}: generating inputs ({cfg.note}{', fp32 adapters' if lora_dtype else ''})")
     inp = make_mlp_inputs(cfg)
     nf4 = {}
     if cfg.nf4:
@@ -55,10 +55,16 @@ def _mlp_full(lm, cid):
             inp[k] = dict(inp[k], W=ON.dequantize(q, "bf16"))
     say(f"config {cid}: GPU forward + backward")
     X, dY = dev(inp["X"]), dev(inp["dY"])
-    g, u, d = (proj_dev(inp[k], "bf16", nf4=nf4.get(k)) for k in ("gate", "up", "down"))
+    g, u, d = (proj_dev(inp[k], "bf16", nf4=nf4.get(k), adapters=lora_dtype or None) for k in ("gate", "up", "down"))
     Y, saved = lm.mlp_fwd(X, g, u, d, cfg.act)
     dX, grads = lm.mlp_bwd(dY, X, saved, g, u, d, cfg.act)
     torch.cuda.synchronize()
+    if lora_dtype:
+        # the oracle multiplies with the adapters as the mode casts them; the
+        # mode's gradients are fp32
+        assert all(t.dtype == torch.float32 for t in grads.values())
+        for k in ("gate", "up", "down"):
+            inp[k] = OL.to_compute_adapters(inp[k])
     got = dict(Y=host(Y), e=host(saved["e"]), g=host(saved["g"]), U=host(saved["U"]), dX=host(dX),
                **{k: host(v) for k, v in grads.items()})
     del X, dY, Y, saved, dX, grads
@@ -80,6 +86,10 @@ def _mlp_full(lm, cid):
 
 def test_config2_llama3_8b_mlp_swiglu(lm):
     _mlp_full(lm, 2)
+
+
+def test_config2_fp32_lora_gradients(lm):
+    _mlp_full(lm, 2, lora_dtype="f32")
 
 
 def test_config3_gemma_geglu_tanh(lm):

@@ -120,6 +120,97 @@ def test_qkv_o_fp32(lm):
 
 
 # ---------------------------------------------------------------------------
+# fp32 LoRA-gradient mode: bf16 inputs, fp32 adapters and adapter gradients
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("act", ["swiglu", "geglu_tanh"])
+def test_fp32_lora_mode_mlp(lm, act):
+    """Against the oracle fed the adapters as the mode casts them (bf16), and
+    against the bf16 mode on the same casts: the forward outputs must agree
+    bit for bit and the mode's fp32 gradients must round to the bf16 mode's."""
+    import torch
+
+    cfg = WorkloadConfig(95, "mlp", T=300, H=512, I=1088, r=16, alpha=32, dtype="bf16", act=act,
+                         lora_dtype="f32")
+    inp = make_mlp_inputs(cfg)
+    X, dY = dev(inp["X"]), dev(inp["dY"])
+    g, u, d = (proj_dev(inp[k], adapters="f32") for k in ("gate", "up", "down"))
+    Y, saved = lm.mlp_fwd(X, g, u, d, act)
+    dX, grads = lm.mlp_bwd(dY, X, saved, g, u, d, act)
+    cast = {k: OL.to_compute_adapters(inp[k]) for k in ("gate", "up", "down")}
+    g16, u16, d16 = (proj_dev(cast[k]) for k in ("gate", "up", "down"))
+    Y16, saved16 = lm.mlp_fwd(X, g16, u16, d16, act)
+    dX16, grads16 = lm.mlp_bwd(dY, X, saved16, g16, u16, d16, act)
+    torch.cuda.synchronize()
+    assert all(t.dtype == torch.float32 for t in grads.values())
+    Yr, sr = OL.mlp_fwd(inp["X"], cast["gate"], cast["up"], cast["down"], act)
+    gr = OL.mlp_bwd(inp["dY"], inp["X"], sr, cast["gate"], cast["up"], cast["down"], act)
+    tol = TOL["bf16"]
+    assert_close("Y", host(Y), Yr, tol)
+    assert_close("dX", host(dX), gr["dX"], tol)
+    for k_dev, k_ref in (("dA_gate", "dA_g"), ("dB_gate", "dB_g"), ("dA_up", "dA_u"), ("dB_up", "dB_u"),
+                         ("dA_down", "dA_d"), ("dB_down", "dB_d")):
+        assert_close(k_dev, host(grads[k_dev]), gr[k_ref], tol)
+        assert torch.equal(grads[k_dev].to(torch.bfloat16), grads16[k_dev]), k_dev
+    for a, b in ((Y, Y16), (saved["e"], saved16["e"]), (saved["g"], saved16["g"]), (saved["U"], saved16["U"]),
+                 (dX, dX16)):
+        assert torch.equal(a, b)
+
+
+def _small_ints(rng, shape, p_nonzero, bump=1.0):
+    """Values in {-1, 0, 1} (nonzero with probability p_nonzero), times bump."""
+    v = rng.integers(0, 2, shape) * 2 - 1
+    return (v * (rng.random(shape) < p_nonzero) * bump).astype(np.float32)
+
+
+def test_fp32_lora_mode_qkv_o_gradients_exact(lm):
+    """Inputs in {-1, 0, 1} and adapters a * (1 + 2^-10) that the mode's cast
+    rounds to a: every rank-r intermediate is a small integer (exact in bf16)
+    and every gradient an integer below 2^24 (exact in fp32 in any order), so
+    the mode's fp32 dA and dB must equal the oracle's bit for bit.  Many of
+    them are not bf16 values, so a rounded gradient would fail."""
+    import torch
+
+    rng = np.random.default_rng(96)
+    T, H, Ns, r, s = 1000, 256, (256, 128, 64), 16, 2.0
+    bump = np.float32(1 + 2.0 ** -10)
+
+    def proj(n_in, n_out):
+        W = ON.round_to_bf16((rng.standard_normal((n_in, n_out)) / 16).astype(np.float32))
+        return dict(W=W, A=_small_ints(rng, (n_in, r), 0.25, bump), B=_small_ints(rng, (r, n_out), 0.25, bump), s=s)
+
+    X = _small_ints(rng, (T, H), 0.5)
+    q, k, v = (proj(H, n) for n in Ns)
+    dZ = [_small_ints(rng, (T, n), 0.5) for n in Ns]
+    o = proj(Ns[0], H)
+    Xo, dO = _small_ints(rng, (T, Ns[0]), 0.5), _small_ints(rng, (T, H), 0.5)
+
+    Xd = dev(X)
+    qd, kd, vd, od = (proj_dev(p, adapters="f32") for p in (q, k, v, o))
+    _, _, _, U = lm.qkv_fwd(Xd, qd, kd, vd)
+    _, grads = lm.qkv_bwd(*(dev(z) for z in dZ), Xd, U, qd, kd, vd)
+    Xod = dev(Xo)
+    _, Uo = lm.o_fwd(Xod, od)
+    _, dAo, dBo = lm.o_bwd(dev(dO), Xod, Uo, od)
+    torch.cuda.synchronize()
+
+    qc, kc, vc, oc = (OL.to_compute_adapters(p) for p in (q, k, v, o))
+    _, sr = OL.qkv_fwd(X, qc, kc, vc)
+    assert max(np.abs(sr[n]).max() for n in ("U_q", "U_k", "U_v")) <= 256  # exact in bf16
+    gr = OL.qkv_bwd(*dZ, X, sr, qc, kc, vc)
+    _, so = OL.o_fwd(Xo, oc)
+    gor = OL.o_bwd(dO, Xo, so, oc)
+    got = {n: host(grads[n]) for n in grads}
+    got.update(dA_o=host(dAo), dB_o=host(dBo))
+    ref = {n: gr[n] for n in grads}
+    ref.update(dA_o=gor["dA"], dB_o=gor["dB"])
+    for n in got:
+        assert np.abs(ref[n]).max() < 2 ** 24
+        assert np.array_equal(got[n], ref[n]), f"{n}: {np.abs(got[n] - ref[n]).max()}"
+    assert any(np.any(ON.round_to_bf16(ref[n]) != ref[n]) for n in ref)
+
+
+# ---------------------------------------------------------------------------
 # NF4
 # ---------------------------------------------------------------------------
 

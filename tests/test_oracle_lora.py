@@ -259,3 +259,44 @@ def test_adapter_parameter_count_matches_page(golden_dir):
         assert Z.shape == (2, b) and U.shape == (2, r)
         per_layer += r * (n_in + n_out)
     assert per_layer * layers == total
+
+
+def test_fp32_lora_mode_matches_integer_brute_force():
+    """fp32 LoRA-gradient mode ("LoRA Optimizations", section "FP32 LoRA
+    gradients"): the adapters are rounded to bf16 before the products and the
+    gradients come out in fp32 without a final rounding.  With small integer
+    inputs and adapters of the form a * (1 + 2^-10) (which round to the
+    integer a), every product and sum is an exact integer, so the mode's
+    gradients must equal Python-integer brute force over the rounded
+    adapters exactly, and must hold values that a bf16 result could not."""
+    rng = np.random.default_rng(5)
+    T, K, N, r, s = 300, 12, 10, 3, 2.0
+
+    def ints(shape, p):
+        return (rng.integers(-3, 4, shape) * (rng.random(shape) < p)).astype(np.float32)
+
+    X, dY = ints((T, K), 0.8), ints((T, N), 0.8)
+    A_int, B_int = ints((K, r), 0.7), ints((r, N), 0.7)
+    W = rng.standard_normal((K, N)).astype(np.float32)
+    bump = np.float32(1 + 2.0 ** -10)
+    o = dict(W=W, A=A_int * bump, B=B_int * bump, s=s)
+    assert not np.array_equal(o["A"], A_int)  # the fp32 adapters are not integers
+    oc = L.to_compute_adapters(o)
+    assert np.array_equal(oc["A"], A_int) and np.array_equal(oc["B"], B_int)
+    Y, saved = L.o_fwd(X, oc)
+    got = L.o_bwd(dY, X, saved, oc)
+    assert got["dA"].dtype == np.float32 and got["dB"].dtype == np.float32
+
+    Xi, dYi = X.astype(int).tolist(), dY.astype(int).tolist()
+    Ai, Bi = A_int.astype(int).tolist(), B_int.astype(int).tolist()
+    U = [[sum(Xi[t][k] * Ai[k][i] for k in range(K)) for i in range(r)] for t in range(T)]
+    P = [[sum(dYi[t][n] * Bi[i][n] for n in range(N)) for i in range(r)] for t in range(T)]
+    dA = [[2 * sum(Xi[t][k] * P[t][i] for t in range(T)) for i in range(r)] for k in range(K)]
+    dB = [[2 * sum(U[t][i] * dYi[t][n] for t in range(T)) for n in range(N)] for i in range(r)]
+    assert np.array_equal(got["dA"], np.array(dA, np.float32))
+    assert np.array_equal(got["dB"], np.array(dB, np.float32))
+    # sharp: rounding these gradients to bf16 would change some of them
+    from oracle.nf4 import round_to_bf16
+
+    for g in (got["dA"], got["dB"]):
+        assert np.any(round_to_bf16(g) != g)

@@ -15,7 +15,8 @@ Distributions follow the workload descriptions of the five benchmark shapes:
 For 16-bit configurations every tensor is rounded to bfloat16
 (round-to-nearest-even) here, once, and handed out as float32 arrays that hold
 bf16-representable values, so that the oracle and the GPU path consume
-identical numbers.
+identical numbers.  The one exception is ``lora_dtype="f32"`` (the fp32
+LoRA-gradient mode): there the adapters ``A`` and ``B`` stay full fp32 values.
 
 Every tensor has its own stream: ``numpy.random.default_rng([seed, fnv1a(name)])``
 with ``seed = 1000 + config id`` unless a caller passes another seed.
@@ -71,6 +72,7 @@ class WorkloadConfig:
     Nk: int = 0
     Nv: int = 0
     rms_inputs: bool = True  # X / dY rows RMS-normalised (RMSNorm-output stand-in)
+    lora_dtype: str = ""  # "f32": adapters stay fp32 with bf16 inputs (fp32 LoRA-gradient mode)
     note: str = field(default="", compare=False)
 
     @property
@@ -141,7 +143,11 @@ def make_proj(cfg: WorkloadConfig, prefix: str, n_in: int, n_out: int, seed=None
     W = _normal(seed, prefix + ".W", (n_in, n_out), 1.0 / np.sqrt(n_in))
     A = _uniform(seed, prefix + ".A", (n_in, cfg.r), 1.0 / np.sqrt(n_in))
     B = _normal(seed, prefix + ".B", (cfg.r, n_out), 0.02)
-    return dict(W=_finish(W, cfg), A=_finish(A, cfg), B=_finish(B, cfg), s=float(cfg.scale))
+    if cfg.lora_dtype == "f32":
+        A, B = (np.ascontiguousarray(x, np.float32) for x in (A, B))
+    else:
+        A, B = _finish(A, cfg), _finish(B, cfg)
+    return dict(W=_finish(W, cfg), A=A, B=B, s=float(cfg.scale))
 
 
 def make_activation(cfg, name, T, n, seed=None, rms=None):
