@@ -20,6 +20,7 @@ from . import _lib as L
 __all__ = [
     "Proj", "NF4Weight", "load", "LoraError",
     "mlp_fwd", "mlp_bwd", "mlp_workspace_size",
+    "relu2_mlp_fwd", "relu2_mlp_bwd", "relu2_mlp_workspace_size",
     "qkv_fwd", "qkv_bwd", "o_fwd", "o_bwd",
     "nf4_quantize", "nf4_dequant", "nf4_unpack_codes", "nf4_gemm", "nf4_codebook",
     "trace_begin", "trace_end",
@@ -175,6 +176,64 @@ def mlp_bwd(dY, X, saved, gate: Proj, up: Proj, down: Proj, act="swiglu", *, dX=
     L.call("lora_mlp_bwd", C.byref(d), _ptr(dY), _ptr(X), C.byref(sv), C.byref(gate.c_struct(keep)),
            C.byref(up.c_struct(keep)), C.byref(down.c_struct(keep)), _ptr(dX), C.byref(gr), _ptr(ws),
            ws.numel(), _stream(stream))
+    return dX, grads
+
+
+# ---------------------------------------------------------------------------
+# Ungated ReLU^2 MLP
+# ---------------------------------------------------------------------------
+
+def relu2_mlp_workspace_size(T, H, I, r, dtype=L.LORA_BF16):
+    d = L.lora_relu2_mlp_desc(T, H, I, r, dtype, 0)
+    f, b = C.c_size_t(), C.c_size_t()
+    L.call("lora_relu2_mlp_workspace_size", C.byref(d), C.byref(f), C.byref(b))
+    return f.value, b.value
+
+
+def relu2_mlp_fwd(X, up: Proj, down: Proj, *, Y=None, saved=None, ws=None, stream=None):
+    """Y = down(relu(up(X))^2).  Returns (Y, saved) with saved = dict(u, U)."""
+    torch = _torch()
+    T, H = X.shape
+    I = up.B.shape[1]
+    r = up.A.shape[1]
+    dt = _call_dtype(X, (up, down))
+    d = L.lora_relu2_mlp_desc(T, H, I, r, dt, 0)
+    fb, _ = relu2_mlp_workspace_size(T, H, I, r, dt)
+    if Y is None:
+        Y = torch.empty((T, H), dtype=X.dtype, device=X.device)
+    if saved is None:
+        saved = dict(u=torch.empty((T, I), dtype=X.dtype, device=X.device),
+                     U=torch.empty((T, 2 * r), dtype=X.dtype, device=X.device))
+    if ws is None:
+        ws = _ws(fb, X.device)
+    keep = []
+    sv = L.lora_relu2_mlp_saved(_ptr(saved["u"]), _ptr(saved["U"]))
+    L.call("lora_relu2_mlp_fwd", C.byref(d), _ptr(X), C.byref(up.c_struct(keep)), C.byref(down.c_struct(keep)),
+           _ptr(Y), C.byref(sv), _ptr(ws), ws.numel(), _stream(stream))
+    return Y, saved
+
+
+def relu2_mlp_bwd(dY, X, saved, up: Proj, down: Proj, *, dX=None, grads=None, ws=None, stream=None):
+    """Returns (dX, grads) with grads = dict(dA_up, dB_up, dA_down, dB_down)."""
+    torch = _torch()
+    T, H = X.shape
+    I = up.B.shape[1]
+    r = up.A.shape[1]
+    dt = _call_dtype(X, (up, down))
+    d = L.lora_relu2_mlp_desc(T, H, I, r, dt, 0)
+    _, bb = relu2_mlp_workspace_size(T, H, I, r, dt)
+    if dX is None:
+        dX = torch.empty_like(X)
+    if grads is None:
+        grads = dict(dA_up=torch.empty_like(up.A), dB_up=torch.empty_like(up.B),
+                     dA_down=torch.empty_like(down.A), dB_down=torch.empty_like(down.B))
+    if ws is None:
+        ws = _ws(bb, X.device)
+    keep = []
+    sv = L.lora_relu2_mlp_saved(_ptr(saved["u"]), _ptr(saved["U"]))
+    gr = L.lora_relu2_mlp_grads(*(_ptr(grads[k]) for k in ("dA_up", "dB_up", "dA_down", "dB_down")))
+    L.call("lora_relu2_mlp_bwd", C.byref(d), _ptr(dY), _ptr(X), C.byref(sv), C.byref(up.c_struct(keep)),
+           C.byref(down.c_struct(keep)), _ptr(dX), C.byref(gr), _ptr(ws), ws.numel(), _stream(stream))
     return dX, grads
 
 

@@ -44,6 +44,18 @@ class lora_mlp_grads(C.Structure):
     _fields_ = [("dA_gate", vp), ("dB_gate", vp), ("dA_up", vp), ("dB_up", vp), ("dA_down", vp), ("dB_down", vp)]
 
 
+class lora_relu2_mlp_desc(C.Structure):
+    _fields_ = [("T", i64), ("H", i64), ("I", i64), ("r", i64), ("dtype", i32), ("reserved", i32)]
+
+
+class lora_relu2_mlp_saved(C.Structure):
+    _fields_ = [("u", vp), ("U", vp)]
+
+
+class lora_relu2_mlp_grads(C.Structure):
+    _fields_ = [("dA_up", vp), ("dB_up", vp), ("dA_down", vp), ("dB_down", vp)]
+
+
 class lora_qkv_desc(C.Structure):
     _fields_ = [("T", i64), ("H", i64), ("Nq", i64), ("Nk", i64), ("Nv", i64), ("r", i64),
                 ("dtype", i32), ("reserved", i32)]
@@ -72,6 +84,11 @@ SIGNATURES = {
                            P(lora_mlp_saved), vp, sz, vp]),
     "lora_mlp_bwd": (i32, [P(lora_mlp_desc), vp, vp, P(lora_mlp_saved), P(lora_proj), P(lora_proj),
                            P(lora_proj), vp, P(lora_mlp_grads), vp, sz, vp]),
+    "lora_relu2_mlp_workspace_size": (i32, [P(lora_relu2_mlp_desc), P(sz), P(sz)]),
+    "lora_relu2_mlp_fwd": (i32, [P(lora_relu2_mlp_desc), vp, P(lora_proj), P(lora_proj), vp,
+                                 P(lora_relu2_mlp_saved), vp, sz, vp]),
+    "lora_relu2_mlp_bwd": (i32, [P(lora_relu2_mlp_desc), vp, vp, P(lora_relu2_mlp_saved), P(lora_proj),
+                                 P(lora_proj), vp, P(lora_relu2_mlp_grads), vp, sz, vp]),
     "lora_qkv_workspace_size": (i32, [P(lora_qkv_desc), P(sz), P(sz)]),
     "lora_qkv_fwd": (i32, [P(lora_qkv_desc), vp, P(lora_proj), P(lora_proj), P(lora_proj), vp, vp, vp, vp,
                            vp, sz, vp]),

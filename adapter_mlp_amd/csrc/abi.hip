@@ -214,7 +214,11 @@ hipError_t gemm_on(const Ctx& c, GemmArgs& g, hipStream_t st, int64_t lora_vcols
   g.ntile_n = tiles;
   char name[48];
   std::snprintf(name, sizeof name, "gemm_%s_%s%s%s", g.bkind == B_NN ? "nn" : "nt",
-                g.epi == EPI_STORE ? "store" : (g.epi == EPI_ACT_FWD ? "act_fwd" : "act_bwd"),
+                g.epi == EPI_STORE      ? "store"
+                : g.epi == EPI_ACT_FWD  ? "act_fwd"
+                : g.epi == EPI_ACT_BWD  ? "act_bwd"
+                : g.epi == EPI_ACT1_FWD ? "relu2_fwd"
+                                        : "relu2_bwd",
                 g.nf4 ? "_nf4" : "", c.bf16 ? "" : "_f32");
   TraceScope ts(name, st);
   return c.bf16 ? launch_gemm_bf16(g, st) : launch_gemm_f32(g, st);
@@ -382,6 +386,65 @@ lora_status validate_mlp(const lora_mlp_desc* d, Ctx& c) {
   return LORA_OK;
 }
 
+
+// ---------------------------------------------------------------------------
+// Ungated ReLU^2 MLP
+// ---------------------------------------------------------------------------
+struct Relu2Plan {
+  void *ad_f, *ad_b;                                          // adapter casts (fp32 LoRA-gradient mode)
+  void *At_u, *Us_u, *BLt_u, *h, *At_d, *Us_d, *BLt_d;        // forward
+  void *Ps_d, *BLt_dh, *hb, *du, *Ps_u, *BLt_dx;              // backward
+  float* partial;
+  float* rpartial;  // rowproj partials of the fused dY / du passes
+  size_t fwd_bytes, bwd_bytes;
+};
+
+Relu2Plan plan_relu2(const Ctx& c, const lora_relu2_mlp_desc& d, void* ws_fwd, void* ws_bwd) {
+  Relu2Plan p{};
+  const int64_t T = d.T, H = d.H, I = d.I, r = d.r;
+  const int64_t RL = c.rl(r);
+  const AdapterDims ad[2] = {{H, I}, {I, H}};
+  Ws f(ws_fwd);
+  p.ad_f = f.take(staged_bytes(c, ad, 2, r));
+  p.At_u = f.take(r * H * c.es);
+  p.Us_u = f.take(T * RL * c.es);
+  p.BLt_u = f.take(I * RL * c.es);
+  p.h = f.take(T * I * c.es);
+  p.At_d = f.take(r * I * c.es);
+  p.Us_d = f.take(T * RL * c.es);
+  p.BLt_d = f.take(H * RL * c.es);
+  p.fwd_bytes = f.off;
+  Ws b(ws_bwd);
+  p.ad_b = b.take(staged_bytes(c, ad, 2, r));
+  p.Ps_d = b.take(T * RL * c.es);
+  p.BLt_dh = b.take(I * RL * c.es);
+  p.hb = b.take(T * I * c.es);
+  p.du = b.take(T * I * c.es);
+  p.Ps_u = b.take(T * RL * c.es);
+  p.BLt_dx = b.take(H * RL * c.es);
+  int64_t pf = 0;
+  if (c.bf16) {
+    const int64_t a = colproj_partial_floats(T, H, (int)r), bb = colproj_partial_floats(T, I, (int)r);
+    pf = a > bb ? a : bb;
+  }
+  p.partial = static_cast<float*>(b.take((size_t)pf * 4));
+  p.rpartial = c.bf16 ? static_cast<float*>(b.take((size_t)rowcol_partial_floats(T, I > H ? I : H) * 4)) : nullptr;
+  p.bwd_bytes = b.off;
+  return p;
+}
+
+lora_status validate_relu2(const lora_relu2_mlp_desc* d, Ctx& c) {
+  CHECK(d != nullptr, LORA_EINVAL, "desc is NULL");
+  TRY(check_dtype(d->dtype, c, true));
+  CHECK(d->reserved == 0, LORA_EINVAL, "reserved field must be 0");
+  CHECK(d->T >= 0, LORA_ESHAPE, "T = %lld is negative", (long long)d->T);
+  TRY(check_dim(c, d->H, "H"));
+  TRY(check_dim(c, d->I, "I"));
+  TRY(check_rank(c, d->r, 1));
+  TRY(check_extent(c, d->T, d->I > d->H ? d->I : d->H, "an activation"));
+  TRY(check_extent(c, d->H, d->I, "a weight"));
+  return LORA_OK;
+}
 
 // ---------------------------------------------------------------------------
 // Q/K/V and O
@@ -887,6 +950,257 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, 
   return LORA_OK;
 }
 
+
+// ---------------------------------------------------------------------------
+// Ungated ReLU^2 MLP
+// ---------------------------------------------------------------------------
+lora_status lora_relu2_mlp_workspace_size(const lora_relu2_mlp_desc* d, size_t* fwd, size_t* bwd) {
+  Ctx c{};
+  TRY(validate_relu2(d, c));
+  Relu2Plan p = plan_relu2(c, *d, nullptr, nullptr);
+  if (fwd) *fwd = p.fwd_bytes;
+  if (bwd) *bwd = p.bwd_bytes;
+  return LORA_OK;
+}
+
+lora_status lora_relu2_mlp_fwd(const lora_relu2_mlp_desc* d, const void* X, const lora_proj* up,
+                               const lora_proj* down, void* Y, const lora_relu2_mlp_saved* saved, void* ws,
+                               size_t ws_bytes, void* stream) {
+  Ctx c{};
+  TRY(validate_relu2(d, c));
+  const int64_t T = d->T, H = d->H, I = d->I, r = d->r;
+  TRY(check_tptr(c, X, T, "X"));
+  TRY(check_tptr(c, Y, T, "Y"));
+  CHECK(saved != nullptr, LORA_EINVAL, "saved is NULL");
+  TRY(check_tptr(c, saved->u, T, "saved.u"));
+  TRY(check_tptr(c, saved->U, T, "saved.U"));
+  TRY(check_proj(c, up, H, I, "up"));
+  TRY(check_proj(c, down, I, H, "down"));
+  CHECK(!overlaps(Y, T * H * c.es, X, T * H * c.es), LORA_EUNSUPPORTED, "Y aliases X");
+  Relu2Plan need = plan_relu2(c, *d, nullptr, nullptr);
+  TRY(check_ws(ws, ws_bytes, need.fwd_bytes));
+  if (T == 0) return LORA_OK;
+  Relu2Plan p = plan_relu2(c, *d, ws, nullptr);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t RL = c.rl(r);
+  const lora_proj* in[2] = {up, down};
+  const AdapterDims ad[2] = {{H, I}, {I, H}};
+  lora_proj sp[2];
+  STAGE(p.ad_f, in, ad, 2, r, sp, st);
+  up = &sp[0];
+  down = &sp[1];
+
+  // U_u = X A_u, then the up GEMM with the ReLU^2 epilogue (u, h)
+  const void* srcs_u[1] = {up->A};
+  LAUNCHN("pack", st, launch_pack_cat_t(c.bf16, p.At_u, H, (int)r, (int)r, 1, srcs_u, st));
+  RowProjArgs ru = rowproj_args(X, H, T, H, p.At_u, H, (int)r, (int)RL, (int)r);
+  ru.scales[0] = up->scale;
+  ru.out1 = saved->U;
+  ru.ld1 = 2 * r;
+  ru.off1 = 0;
+  ru.out2 = p.Us_u;
+  ru.ld2 = RL;
+  LAUNCHN("rowproj", st, launch_rowproj(c.bf16, ru, st));
+  PackLoraArgs pu{};
+  pu.out = p.BLt_u;
+  pu.vcols = I;
+  pu.RL = (int)RL;
+  pu.nparts = 1;
+  pu.part[0] = part(up->B, I, 0, I, 0, (int)r, true);
+  pu.kmajor = c.bf16 ? 1 : 0;  // the bf16 NN GEMM reads [RL, vcols]
+  LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, pu, st));
+  GemmArgs g{};
+  g.M = T;
+  g.nseg = 1;
+  g.nreg = 1;
+  g.epi = EPI_ACT1_FWD;
+  g.nf4 = up->nf4 != nullptr;
+  g.bkind = B_NN;
+  g.seg[0].A = X;
+  g.seg[0].lda = H;
+  g.seg[0].K = H;
+  g.seg[0].b[0][0] = bsrc(up, I);
+  g.reg[0].N = I;
+  g.AL = p.Us_u;
+  g.ldal = RL;
+  g.RL = (int)RL;
+  g.BLt = p.BLt_u;
+  g.ldbl = RL;
+  g.e_out = saved->u;
+  g.h_out = p.h;
+  g.ld_act = I;
+  LAUNCH(gemm_on(c, g, st, I));
+
+  // U_d = h A_d, then the down GEMM
+  const void* srcs_d[1] = {down->A};
+  LAUNCHN("pack", st, launch_pack_cat_t(c.bf16, p.At_d, I, (int)r, (int)r, 1, srcs_d, st));
+  RowProjArgs rd = rowproj_args(p.h, I, T, I, p.At_d, I, (int)r, (int)RL, (int)r);
+  rd.scales[0] = down->scale;
+  rd.out1 = saved->U;
+  rd.ld1 = 2 * r;
+  rd.off1 = r;
+  rd.out2 = p.Us_d;
+  rd.ld2 = RL;
+  LAUNCHN("rowproj", st, launch_rowproj(c.bf16, rd, st));
+  PackLoraArgs pd{};
+  pd.out = p.BLt_d;
+  pd.vcols = H;
+  pd.RL = (int)RL;
+  pd.nparts = 1;
+  pd.part[0] = part(down->B, H, 0, H, 0, (int)r, true);
+  pd.kmajor = c.bf16 ? 1 : 0;
+  LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, pd, st));
+  GemmArgs gd{};
+  gd.M = T;
+  gd.nseg = 1;
+  gd.nreg = 1;
+  gd.epi = EPI_STORE;
+  gd.nf4 = down->nf4 != nullptr;
+  gd.bkind = B_NN;
+  gd.seg[0].A = p.h;
+  gd.seg[0].lda = I;
+  gd.seg[0].K = I;
+  gd.seg[0].b[0][0] = bsrc(down, H);
+  gd.reg[0].N = H;
+  gd.reg[0].out = Y;
+  gd.reg[0].ldo = H;
+  gd.AL = p.Us_d;
+  gd.ldal = RL;
+  gd.RL = (int)RL;
+  gd.BLt = p.BLt_d;
+  gd.ldbl = RL;
+  LAUNCH(gemm_on(c, gd, st, H));
+  return LORA_OK;
+}
+
+lora_status lora_relu2_mlp_bwd(const lora_relu2_mlp_desc* d, const void* dY, const void* X,
+                               const lora_relu2_mlp_saved* saved, const lora_proj* up, const lora_proj* down,
+                               void* dX, const lora_relu2_mlp_grads* gr, void* ws, size_t ws_bytes,
+                               void* stream) {
+  Ctx c{};
+  TRY(validate_relu2(d, c));
+  const int64_t T = d->T, H = d->H, I = d->I, r = d->r;
+  TRY(check_tptr(c, dY, T, "dY"));
+  TRY(check_tptr(c, X, T, "X"));
+  TRY(check_tptr(c, dX, T, "dX"));
+  CHECK(saved != nullptr, LORA_EINVAL, "saved is NULL");
+  TRY(check_tptr(c, saved->u, T, "saved.u"));
+  TRY(check_tptr(c, saved->U, T, "saved.U"));
+  CHECK(gr != nullptr, LORA_EINVAL, "grads is NULL");
+  TRY(check_ptr(c, gr->dA_up, "dA_up"));
+  TRY(check_ptr(c, gr->dB_up, "dB_up"));
+  TRY(check_ptr(c, gr->dA_down, "dA_down"));
+  TRY(check_ptr(c, gr->dB_down, "dB_down"));
+  TRY(check_proj(c, up, H, I, "up"));
+  TRY(check_proj(c, down, I, H, "down"));
+  CHECK(!overlaps(dX, T * H * c.es, X, T * H * c.es), LORA_EUNSUPPORTED, "dX aliases X (in-place dX is not supported)");
+  Relu2Plan need = plan_relu2(c, *d, nullptr, nullptr);
+  TRY(check_ws(ws, ws_bytes, need.bwd_bytes));
+  Relu2Plan p = plan_relu2(c, *d, nullptr, ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t RL = c.rl(r);
+  const lora_proj* in[2] = {up, down};
+  const AdapterDims ad[2] = {{H, I}, {I, H}};
+  lora_proj sp[2];
+  STAGE(p.ad_b, in, ad, 2, r, sp, st);
+  up = &sp[0];
+  down = &sp[1];
+  const void* U = saved->U;
+
+  // one pass over dY: P_d = dY B_d^T, formed once (scaled copy feeds dA_d and
+  // the dh GEMM), and dB_d = s_d U_d^T dY
+  RowProjArgs r1 = rowproj_args(dY, H, T, H, down->B, H, (int)r, (int)RL, (int)r);
+  r1.scales[0] = down->scale;
+  r1.out2 = p.Ps_d;
+  r1.ld2 = RL;
+  ColProjArgs c1 = colproj_args(c, dY, H, T, H, coff(U, r, c), 2 * r, (int)r, (int)r, true, p.partial);
+  c1.scales[0] = down->scale;
+  c1.dest[0] = gr->dB_down;
+  LAUNCHN("rowcol", st, launch_rowcol(c.bf16, c1, r1, p.rpartial, st));
+
+  // dh GEMM with the ReLU^2 gradient epilogue -> du, h
+  PackLoraArgs pl{};
+  pl.out = p.BLt_dh;
+  pl.vcols = I;
+  pl.RL = (int)RL;
+  pl.nparts = 1;
+  pl.part[0] = part(down->A, r, 0, I, 0, (int)r, false);
+  LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, pl, st));
+  GemmArgs g{};
+  g.M = T;
+  g.nseg = 1;
+  g.nreg = 1;
+  g.epi = EPI_ACT1_BWD;
+  g.nf4 = down->nf4 != nullptr;
+  g.bkind = B_NT;
+  g.seg[0].A = dY;
+  g.seg[0].lda = H;
+  g.seg[0].K = H;
+  g.seg[0].b[0][0] = bsrc(down, H);
+  g.reg[0].N = I;
+  g.AL = p.Ps_d;
+  g.ldal = RL;
+  g.RL = (int)RL;
+  g.BLt = p.BLt_dh;
+  g.ldbl = RL;
+  g.e_in = saved->u;
+  g.dg_out = p.du;
+  g.h_out = p.hb;
+  g.ld_act = I;
+  LAUNCH(gemm_on(c, g, st, I));
+
+  // dA_d = s_d h^T P_d  (P_d already scaled)
+  ColProjArgs c2 = colproj_args(c, p.hb, I, T, I, p.Ps_d, RL, (int)r, (int)r, false, p.partial);
+  c2.scales[0] = 1.0f;
+  c2.dest[0] = gr->dA_down;
+  LAUNCHN("colproj", st, launch_colproj(c.bf16, c2, st));
+
+  // one pass over du: P_u = du B_u^T (formed once) and dB_u = s_u U_u^T du
+  RowProjArgs r2 = rowproj_args(p.du, I, T, I, up->B, I, (int)r, (int)RL, (int)r);
+  r2.scales[0] = up->scale;
+  r2.out2 = p.Ps_u;
+  r2.ld2 = RL;
+  ColProjArgs c3 = colproj_args(c, p.du, I, T, I, U, 2 * r, (int)r, (int)r, true, p.partial);
+  c3.scales[0] = up->scale;
+  c3.dest[0] = gr->dB_up;
+  LAUNCHN("rowcol", st, launch_rowcol(c.bf16, c3, r2, p.rpartial, st));
+
+  // dA_u = X^T (s_u P_u)
+  ColProjArgs c4 = colproj_args(c, X, H, T, H, p.Ps_u, RL, (int)r, (int)r, false, p.partial);
+  c4.scales[0] = 1.0f;
+  c4.dest[0] = gr->dA_up;
+  LAUNCHN("colproj", st, launch_colproj(c.bf16, c4, st));
+
+  // dX = du W_u^T + (s_u P_u) A_u^T
+  PackLoraArgs px{};
+  px.out = p.BLt_dx;
+  px.vcols = H;
+  px.RL = (int)RL;
+  px.nparts = 1;
+  px.part[0] = part(up->A, r, 0, H, 0, (int)r, false);
+  LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, px, st));
+  GemmArgs gx{};
+  gx.M = T;
+  gx.nseg = 1;
+  gx.nreg = 1;
+  gx.epi = EPI_STORE;
+  gx.nf4 = up->nf4 != nullptr;
+  gx.bkind = B_NT;
+  gx.seg[0].A = p.du;
+  gx.seg[0].lda = I;
+  gx.seg[0].K = I;
+  gx.seg[0].b[0][0] = bsrc(up, I);
+  gx.reg[0].N = H;
+  gx.reg[0].out = dX;
+  gx.reg[0].ldo = H;
+  gx.AL = p.Ps_u;
+  gx.ldal = RL;
+  gx.RL = (int)RL;
+  gx.BLt = p.BLt_dx;
+  gx.ldbl = RL;
+  if (T > 0) LAUNCH(gemm_on(c, gx, st, H));
+  return LORA_OK;
+}
 
 // ---------------------------------------------------------------------------
 // Q/K/V

@@ -87,6 +87,15 @@ __device__ __forceinline__ void act_fwd_bwd(int act, float x, float& phi, float&
   }
 }
 
+// Ungated ReLU^2 MLP activation, h = phi(u): phi(x) = max(x, 0)^2 and
+// phi'(x) = 2 max(x, 0) ("LoRA Optimizations", section "FP32 LoRA gradients":
+// the ReLU^2 MLPs of Nemotron-H with a fused activation derivative).
+__device__ __forceinline__ float relu2(float x) {
+  const float r = x > 0.0f ? x : 0.0f;
+  return r * r;
+}
+__device__ __forceinline__ float relu2_grad(float x) { return x > 0.0f ? 2.0f * x : 0.0f; }
+
 // ---------------------------------------------------------------------------
 // NF4 levels (QLoRA paper, appendix): asymmetric N(0,1) quantiles normalised
 // to [-1, 1] with an exact zero.  The library's own copy; lora_nf4_codebook()

@@ -15,7 +15,10 @@
 //   EPI_ACT_FWD  (gate/up tiles) e, g -> bf16, h = phi(e) g from the rounded
 //                e, g, store e, g, h;
 //   EPI_ACT_BWD  dh -> load e, g, recompute h, dg = dh phi(e),
-//                de = dh g phi'(e), store dg, de, h.
+//                de = dh g phi'(e), store dg, de, h;
+//   EPI_ACT1_FWD (ungated ReLU^2 MLP) u -> bf16, h = relu(u)^2 from the
+//                rounded u, store u, h;
+//   EPI_ACT1_BWD dh -> load u, recompute h, du = dh 2 relu(u), store du, h.
 // Each wavefront stages its results through a private LDS region so global
 // loads and stores move whole 16-byte chunks of consecutive columns.
 //
@@ -96,7 +99,10 @@ __device__ __forceinline__ void for4(F&& f) {
 // Staging bytes one wavefront needs for a WN-column epilogue.
 template <int WN, int EPI>
 constexpr int epi_stage_bytes() {
-  return EPI == EPI_STORE ? 32 * (WN + 8) * 2 : EPI == EPI_ACT_FWD ? 3 * 32 * (WN / 2 + 8) * 2 : 32 * (WN + 4) * 4;
+  return EPI == EPI_STORE      ? 32 * (WN + 8) * 2
+         : EPI == EPI_ACT_FWD  ? 3 * 32 * (WN / 2 + 8) * 2
+         : EPI == EPI_ACT1_FWD ? 2 * 32 * (WN + 8) * 2
+                               : 32 * (WN + 4) * 4;
 }
 
 template <int WN, bool DUAL, int EPI>
@@ -184,7 +190,50 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
       }
       wave_sync();
     });
+  } else if constexpr (EPI == EPI_ACT1_FWD) {
+    constexpr int LD = WN + 8;           // bf16 staging [2][32][WN]: u, h
+    constexpr int ARR = 32 * LD;
+    constexpr int CPR = WN / 8;
+    constexpr int RPP = 64 / CPR;
+    uint16_t* stg = reinterpret_cast<uint16_t*>(wstage);
+    char* uo = static_cast<char*>(args.e_out);
+    char* ho = static_cast<char*>(args.h_out);
+    const int64_t ld = args.ld_act;
+    for4([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = i * 32 + 8 * g + 4 * (lane >> 5);
+          u32x2 uv, hv;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            uv[h] = pack_bf2(acc[i][j][4 * g + 2 * h], acc[i][j][4 * g + 2 * h + 1]);
+            hv[h] = pack_bf2(relu2(lo_bf(uv[h])), relu2(hi_bf(uv[h])));
+          }
+          const int o = (lane & 31) * LD + col;
+          *reinterpret_cast<u32x2*>(stg + o) = uv;
+          *reinterpret_cast<u32x2*>(stg + ARR + o) = hv;
+        }
+      wave_sync();
+#pragma unroll
+      for (int it = 0; it < 32 / RPP; ++it) {
+        const int row = it * RPP + lane / CPR, c8 = lane % CPR;
+        const int64_t m = mw + j * 32 + row;
+        const int64_t n = nbase + c8 * 8;
+        if (m < M && n < NR) {
+          const int o = row * LD + c8 * 8;
+          const int64_t off = (m * ld + n) * 2;
+          *reinterpret_cast<u32x4*>(uo + off) = *reinterpret_cast<const u32x4*>(stg + o);
+          *reinterpret_cast<u32x4*>(ho + off) = *reinterpret_cast<const u32x4*>(stg + ARR + o);
+        }
+      }
+      wave_sync();
+    });
   } else {
+    // EPI_ACT_BWD (gated) or EPI_ACT1_BWD (ungated ReLU^2: du = dh phi'(u) into dg_out)
+    constexpr bool GATED = EPI == EPI_ACT_BWD;
     constexpr int LD = WN + 4;           // fp32 staging [32][WN]
     constexpr int CPR = WN / 8;          // 8-float groups per row
     constexpr int RPP = 64 / CPR;
@@ -217,7 +266,7 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
         const bool ok = m < M && n < NR;
         const int64_t off = ok ? (m * ld + n) * 2 : 0;
         ev[it] = ok ? *reinterpret_cast<const u32x4*>(ei + off) : u32x4{0, 0, 0, 0};
-        gv[it] = ok ? *reinterpret_cast<const u32x4*>(gi + off) : u32x4{0, 0, 0, 0};
+        if constexpr (GATED) gv[it] = ok ? *reinterpret_cast<const u32x4*>(gi + off) : u32x4{0, 0, 0, 0};
         d0[it] = *reinterpret_cast<const f32x4*>(stg + row * LD + c8 * 8);
         d1[it] = *reinterpret_cast<const f32x4*>(stg + row * LD + c8 * 8 + 4);
       }
@@ -232,18 +281,23 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
           const float dha = q < 2 ? d0[it][2 * q] : d1[it][2 * q - 4];
           const float dhb = q < 2 ? d0[it][2 * q + 1] : d1[it][2 * q - 3];
           const float e0 = lo_bf(ev[it][q]), e1 = hi_bf(ev[it][q]);
-          const float g0 = lo_bf(gv[it][q]), g1 = hi_bf(gv[it][q]);
-          float p0, s0, p1, s1;
-          act_fwd_bwd<false>(args.act, e0, p0, s0);
-          act_fwd_bwd<false>(args.act, e1, p1, s1);
-          hv[q] = pack_bf2(p0 * g0, p1 * g1);
-          dgv[q] = pack_bf2(dha * p0, dhb * p1);
-          dev[q] = pack_bf2(dha * g0 * s0, dhb * g1 * s1);
+          if constexpr (GATED) {
+            const float g0 = lo_bf(gv[it][q]), g1 = hi_bf(gv[it][q]);
+            float p0, s0, p1, s1;
+            act_fwd_bwd<false>(args.act, e0, p0, s0);
+            act_fwd_bwd<false>(args.act, e1, p1, s1);
+            hv[q] = pack_bf2(p0 * g0, p1 * g1);
+            dgv[q] = pack_bf2(dha * p0, dhb * p1);
+            dev[q] = pack_bf2(dha * g0 * s0, dhb * g1 * s1);
+          } else {
+            hv[q] = pack_bf2(relu2(e0), relu2(e1));
+            dgv[q] = pack_bf2(dha * relu2_grad(e0), dhb * relu2_grad(e1));
+          }
         }
         if (m < M && n < NR) {
           const int64_t off = (m * ld + n) * 2;
           *reinterpret_cast<u32x4*>(dgo + off) = dgv;
-          *reinterpret_cast<u32x4*>(deo + off) = dev;
+          if constexpr (GATED) *reinterpret_cast<u32x4*>(deo + off) = dev;
           *reinterpret_cast<u32x4*>(ho + off) = hv;
         }
       }
@@ -815,9 +869,14 @@ hipError_t launch(const GemmArgs& a, hipStream_t st) {
 
 template <bool NF4>
 hipError_t launch_family(const GemmArgs& a, hipStream_t st) {
-  if (a.bkind == B_NN)
-    return a.epi == EPI_ACT_FWD ? launch<B_NN, true, EPI_ACT_FWD, NF4>(a, st) : launch<B_NN, false, EPI_STORE, NF4>(a, st);
-  return a.epi == EPI_ACT_BWD ? launch<B_NT, false, EPI_ACT_BWD, NF4>(a, st) : launch<B_NT, false, EPI_STORE, NF4>(a, st);
+  if (a.bkind == B_NN) {
+    if (a.epi == EPI_ACT_FWD) return launch<B_NN, true, EPI_ACT_FWD, NF4>(a, st);
+    if (a.epi == EPI_ACT1_FWD) return launch<B_NN, false, EPI_ACT1_FWD, NF4>(a, st);
+    return launch<B_NN, false, EPI_STORE, NF4>(a, st);
+  }
+  if (a.epi == EPI_ACT_BWD) return launch<B_NT, false, EPI_ACT_BWD, NF4>(a, st);
+  if (a.epi == EPI_ACT1_BWD) return launch<B_NT, false, EPI_ACT1_BWD, NF4>(a, st);
+  return launch<B_NT, false, EPI_STORE, NF4>(a, st);
 }
 
 }  // namespace

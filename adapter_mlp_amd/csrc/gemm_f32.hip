@@ -1,7 +1,7 @@
 // fp32 GEMM for the fp32 compute dtype: the same contraction, segments,
-// regions, LoRA tail and epilogues as the bf16 MFMA kernel, computed with
-// fp32 FMAs (no reduced-precision operands), 64x64 tiles, 4x4 outputs per
-// thread, bounds-checked loads so any shape works.
+// regions, LoRA tail and epilogues (gated and ungated) as the bf16 MFMA
+// kernel, computed with fp32 FMAs (no reduced-precision operands), 64x64
+// tiles, 4x4 outputs per thread, bounds-checked loads so any shape works.
 //
 // In dual (gate/up) tiles a thread's four tile columns are
 // {gate n, gate n+1, up n, up n+1}, so e and g of one element meet in one
@@ -113,6 +113,27 @@ __global__ __launch_bounds__(NTH) void gemm_f32_kernel(const GemmArgs args) {
         static_cast<float*>(args.e_out)[off] = e;
         static_cast<float*>(args.g_out)[off] = g;
         static_cast<float*>(args.h_out)[off] = phi * g;
+      }
+    } else if (args.epi == EPI_ACT1_FWD) {
+      for (int j = 0; j < 4; ++j) {
+        int cg;
+        int64_t n;
+        colmap32(false, tx * 4 + j, tnl, cg, n);
+        if (n >= R.N) continue;
+        const int64_t off = m * args.ld_act + n;
+        static_cast<float*>(args.e_out)[off] = acc[i][j];
+        static_cast<float*>(args.h_out)[off] = relu2(acc[i][j]);
+      }
+    } else if (args.epi == EPI_ACT1_BWD) {
+      for (int j = 0; j < 4; ++j) {
+        int cg;
+        int64_t n;
+        colmap32(false, tx * 4 + j, tnl, cg, n);
+        if (n >= R.N) continue;
+        const int64_t off = m * args.ld_act + n;
+        const float u = static_cast<const float*>(args.e_in)[off];
+        static_cast<float*>(args.h_out)[off] = relu2(u);
+        static_cast<float*>(args.dg_out)[off] = acc[i][j] * relu2_grad(u);
       }
     } else {
       for (int j = 0; j < 4; ++j) {

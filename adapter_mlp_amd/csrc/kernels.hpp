@@ -25,7 +25,7 @@ namespace lora {
 // so the activation epilogue sees e and g of one element in one lane.
 // ---------------------------------------------------------------------------
 enum { B_NN = 0, B_NT = 1 };
-enum { EPI_STORE = 0, EPI_ACT_FWD = 1, EPI_ACT_BWD = 2 };
+enum { EPI_STORE = 0, EPI_ACT_FWD = 1, EPI_ACT_BWD = 2, EPI_ACT1_FWD = 3, EPI_ACT1_BWD = 4 };
 
 struct BSrc {
   const void* p;  // dense base (compute dtype) or nullptr for NF4
@@ -66,6 +66,7 @@ struct GemmArgs {
   int64_t ldbl;
   int64_t lora_vcols;  // rows of BLt
   // EPI_ACT_FWD: e_out, g_out, h_out [M, N] ; EPI_ACT_BWD: e_in, g_in -> dg_out, de_out, h_out
+  // EPI_ACT1_FWD (ungated ReLU^2): e_out = u, h_out ; EPI_ACT1_BWD: e_in = u -> dg_out = du, h_out
   void* e_out;
   void* g_out;
   void* h_out;

@@ -47,6 +47,14 @@ def kernel_flops(cfg, name):
             "gemm_nt_act_bwd": 2 * T * H * I + 2 * T * r * I,                # dh
             "gemm_nt_store": 2 * T * (2 * I) * H + 2 * T * (2 * r) * H,      # dX
         }
+    elif cfg.kind == "relu2":
+        H, I = cfg.H, cfg.I
+        table = {
+            "gemm_nn_relu2_fwd": 2 * T * H * I + 2 * T * r * I,             # up, incl. U B
+            "gemm_nn_store": 2 * T * I * H + 2 * T * r * H,                  # down
+            "gemm_nt_relu2_bwd": 2 * T * H * I + 2 * T * r * I,              # dh
+            "gemm_nt_store": 2 * T * I * H + 2 * T * r * H,                  # dX
+        }
     else:
         H, N = cfg.H, cfg.Nq + cfg.Nk + cfg.Nv
         table = {
@@ -74,6 +82,10 @@ FAMILY_KERNEL = {
     "gemm_nt_act_bwd_nf4": "gemm_kernel<1, false, 2, true>",
     "gemm_nt_store": "gemm_kernel<1, false, 0, false>",
     "gemm_nt_store_nf4": "gemm_kernel<1, false, 0, true>",
+    "gemm_nn_relu2_fwd": "gemm_kernel<0, false, 3, false>",
+    "gemm_nn_relu2_fwd_nf4": "gemm_kernel<0, false, 3, true>",
+    "gemm_nt_relu2_bwd": "gemm_kernel<1, false, 4, false>",
+    "gemm_nt_relu2_bwd_nf4": "gemm_kernel<1, false, 4, true>",
 }
 COPY_KERNEL = "neg_kernel"  # the --copy-calibration kernel
 
@@ -181,7 +193,8 @@ def trace_summary(stats_csv, bench_log, config_id):
 
 
 def workload_tag(cfg):
-    return {2: "llama3_8b_mlp", 3: "gemma_geglu_mlp", 4: "llama3_8b_qlora_mlp", 5: "llama3_8b_qkvo"}[cfg.cid]
+    return {2: "llama3_8b_mlp", 3: "gemma_geglu_mlp", 4: "llama3_8b_qlora_mlp", 5: "llama3_8b_qkvo",
+            6: "nemotron_h_relu2_mlp"}[cfg.cid]
 
 
 def source_digest():
@@ -293,6 +306,35 @@ class MlpStep:
                    grads=self.grads, ws=self.wsb)
 
 
+class Relu2Step:
+    def __init__(self, cfg, inp, lm, torch):
+        self.cfg, self.lm = cfg, lm
+        dev = lambda a: torch.from_numpy(a).to("cuda:0").to(torch.bfloat16)  # noqa: E731
+        adt = torch.float32 if cfg.lora_dtype == "f32" else torch.bfloat16
+        adev = lambda a: torch.from_numpy(a).to("cuda:0").to(adt)  # noqa: E731
+        self.X, self.dY = dev(inp["X"]), dev(inp["dY"])
+        self.p = {k: lm.Proj(A=adev(inp[k]["A"]), B=adev(inp[k]["B"]), scale=inp[k]["s"], W=dev(inp[k]["W"]))
+                  for k in ("up", "down")}
+        T, H, I, r = cfg.T, cfg.H, cfg.I, cfg.r
+        fb, bb = lm.relu2_mlp_workspace_size(T, H, I, r, lm._call_dtype(self.X, list(self.p.values())))
+        bf = torch.bfloat16
+        self.Y = torch.empty((T, H), dtype=bf, device="cuda:0")
+        self.saved = dict(u=torch.empty((T, I), dtype=bf, device="cuda:0"),
+                          U=torch.empty((T, 2 * r), dtype=bf, device="cuda:0"))
+        self.dX = torch.empty_like(self.X)
+        self.grads = {n: torch.empty_like(getattr(self.p[k], m)) for n, k, m in
+                      (("dA_up", "up", "A"), ("dB_up", "up", "B"), ("dA_down", "down", "A"),
+                       ("dB_down", "down", "B"))}
+        self.wsf = torch.empty(fb, dtype=torch.uint8, device="cuda:0")
+        self.wsb = torch.empty(bb, dtype=torch.uint8, device="cuda:0")
+
+    def __call__(self):
+        lm, p = self.lm, self.p
+        lm.relu2_mlp_fwd(self.X, p["up"], p["down"], Y=self.Y, saved=self.saved, ws=self.wsf)
+        lm.relu2_mlp_bwd(self.dY, self.X, self.saved, p["up"], p["down"], dX=self.dX, grads=self.grads,
+                         ws=self.wsb)
+
+
 class AttnStep:
     def __init__(self, cfg, inp, lm, torch):
         self.cfg, self.lm = cfg, lm
@@ -341,6 +383,11 @@ def cpu_baseline(cfg, inp, seconds):
             X, dY = inp["X"][:ts], inp["dY"][:ts]
             Y, s = OL.mlp_fwd(X, projs["gate"], projs["up"], projs["down"], cfg.act)
             OL.mlp_bwd(dY, X, s, projs["gate"], projs["up"], projs["down"], cfg.act)
+    elif cfg.kind == "relu2":
+        def run(ts):
+            X, dY = inp["X"][:ts], inp["dY"][:ts]
+            Y, s = OL.relu2_mlp_fwd(X, inp["up"], inp["down"])
+            OL.relu2_mlp_bwd(dY, X, s, inp["up"], inp["down"])
     else:
         def run(ts):
             X, Xo = inp["X"][:ts], inp["Xo"][:ts]
@@ -369,7 +416,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5, 6])
     ap.add_argument("--lora-dtype", default="bf16", choices=["bf16", "f32"],
                     help="f32: fp32 adapters and adapter gradients with bf16 inputs (fp32 LoRA-gradient mode)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
@@ -396,7 +443,7 @@ def main():
     import torch
 
     import adapter_mlp_amd as lm
-    from workload import CONFIGS, make_attn_inputs, make_mlp_inputs
+    from workload import CONFIGS, make_inputs
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     lm.load()
@@ -405,9 +452,9 @@ def main():
         cfg = cfg.with_(lora_dtype="f32")
     log(f"[bench] config {cfg.cid}: {cfg.note}; adapters {args.lora_dtype}; generating seeded inputs")
     t0 = time.time()
-    inp = make_mlp_inputs(cfg) if cfg.kind == "mlp" else make_attn_inputs(cfg)
+    inp = make_inputs(cfg)
     log(f"[bench] inputs ready in {time.time() - t0:.1f} s")
-    step = MlpStep(cfg, inp, lm, torch) if cfg.kind == "mlp" else AttnStep(cfg, inp, lm, torch)
+    step = {"mlp": MlpStep, "relu2": Relu2Step, "attn": AttnStep}[cfg.kind](cfg, inp, lm, torch)
     torch.cuda.synchronize()
 
     # warm-up; the first warm-up step also finds the dominant GEMM family
@@ -466,8 +513,9 @@ def main():
         log(f"[bench] oracle: {cpu['value']:.1f} tokens/s on {cpu['cores']} threads ({cpu['sample']})")
 
     out = {
-        "metric": "LoRA-MLP fwd+bwd tokens/s at Llama-3-8B MLP shape; % bf16 MFMA peak"
-        if cfg.kind == "mlp" else "LoRA QKV+O fwd+bwd tokens/s at Llama-3-8B attention shapes",
+        "metric": {"mlp": "LoRA-MLP fwd+bwd tokens/s at Llama-3-8B MLP shape; % bf16 MFMA peak",
+                   "relu2": "ReLU^2 LoRA-MLP fwd+bwd tokens/s at a Nemotron-H-8B-like MLP shape",
+                   "attn": "LoRA QKV+O fwd+bwd tokens/s at Llama-3-8B attention shapes"}[cfg.kind],
         "value": tokens_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -481,6 +529,7 @@ def main():
         "data": "synthetic (seeded; random-init weights and adapters of the named shapes)",
         "config": {"workload": cfg.note, "tokens": cfg.T, "hidden": cfg.H,
                    **({"intermediate": cfg.I, "activation": cfg.act} if cfg.kind == "mlp"
+                      else {"intermediate": cfg.I, "activation": "relu2"} if cfg.kind == "relu2"
                       else {"q": cfg.Nq, "k": cfg.Nk, "v": cfg.Nv, "o": [cfg.Nq, cfg.H]}),
                    "rank": cfg.r, "alpha": cfg.alpha, "base": "nf4" if cfg.nf4 else "bf16",
                    "adapters": args.lora_dtype,

@@ -193,6 +193,57 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* desc, const void* dY, const void* 
                          void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Ungated ReLU^2 LoRA MLP ([LO] "FP32 LoRA gradients": the dense ReLU^2     */
+/* MLPs of Nemotron-H, up and down LoRA projections with a fused ReLU^2      */
+/* activation derivative)                                                    */
+/* ------------------------------------------------------------------------ */
+
+typedef struct lora_relu2_mlp_desc {
+  int64_t T;        /* tokens */
+  int64_t H;        /* hidden size (width of X and Y) */
+  int64_t I;        /* intermediate size (width of u and h) */
+  int64_t r;        /* adapter rank, shared by up and down */
+  int32_t dtype;    /* lora_dtype */
+  int32_t reserved; /* must be 0 */
+} lora_relu2_mlp_desc;
+
+/* Saved by the forward (caller-owned, compute dtype): u [T, I] = the up
+ * projection; U [T, 2r] = [X A_up | h A_down] (unscaled adapter inputs). */
+typedef struct lora_relu2_mlp_saved {
+  void* u;
+  void* U;
+} lora_relu2_mlp_saved;
+
+typedef struct lora_relu2_mlp_grads {
+  void* dA_up;
+  void* dB_up;
+  void* dA_down;
+  void* dB_down;
+} lora_relu2_mlp_grads;
+
+lora_status lora_relu2_mlp_workspace_size(const lora_relu2_mlp_desc* desc, size_t* fwd_bytes,
+                                          size_t* bwd_bytes);
+
+/* Forward:  u = Z_up(X), h = max(u, 0)^2, Y = Z_down(h).  In bf16, u is
+ * rounded to bf16 and h is formed from the rounded u (the backward recomputes
+ * h bit for bit).  X [T, H] -> Y [T, H]; writes saved->u, saved->U.  The bf16
+ * rank limit is r <= 64. */
+lora_status lora_relu2_mlp_fwd(const lora_relu2_mlp_desc* desc, const void* X, const lora_proj* up,
+                               const lora_proj* down, void* Y, const lora_relu2_mlp_saved* saved, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* Backward, given dY [T, H] and the forward's X and saved tensors:
+ *   P_d = dY B_d^T (formed once), dh = dY W_d^T + s_d P_d A_d^T,
+ *   dA_d = s_d h^T P_d, dB_d = s_d U_d^T dY, du = dh * 2 max(u, 0),
+ *   P_u = du B_u^T (formed once), dA_u = s_u X^T P_u, dB_u = s_u U_u^T du,
+ *   dX = du W_u^T + s_u P_u A_u^T.
+ * Outputs are overwritten.  dX must not alias X. */
+lora_status lora_relu2_mlp_bwd(const lora_relu2_mlp_desc* desc, const void* dY, const void* X,
+                               const lora_relu2_mlp_saved* saved, const lora_proj* up, const lora_proj* down,
+                               void* dX, const lora_relu2_mlp_grads* grads, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* LoRA Q/K/V projections of one input ([UD] LoRA_QKV; [LO] attention       */
 /* patch: apply_qkv)                                                         */
 /* ------------------------------------------------------------------------ */

@@ -15,7 +15,8 @@ Every function works in the dtype of its inputs (float32 for parity, float64
 for the pins) and uses nothing but numpy array expressions and ``@``.
 
 Parity pins (tests/test_oracle_lora.py): central finite differences in
-float64 for every gradient, the merged-weight closed form ``W + s*A@B``,
+float64 for every gradient (gated and ReLU^2 MLPs, QKV, O), the merged-weight
+closed form ``W + s*A@B``,
 B = 0 / A = 0 / s = 0 special cases, hoisted-vs-recomputed bitwise identity,
 token permutation, QKV = three single projections, activation special values
 and the exact-GELU bound.
@@ -156,6 +157,44 @@ def mlp_bwd(dY, X, saved, gate, up, down, act="swiglu", hoist=True):
     dX_g, dA_g, dB_g = proj_bwd(de, X, gate["W"], gate["A"], gate["B"], gate["s"], saved["U_g"], hoist)
     dX = dX_u + dX_g
     return dict(dX=dX, dA_g=dA_g, dB_g=dB_g, dA_u=dA_u, dB_u=dB_u, dA_d=dA_d, dB_d=dB_d)
+
+
+# --------------------------------------------------------------------------
+# Ungated ReLU^2 MLP ("LoRA Optimizations", section "FP32 LoRA gradients":
+# the dense ReLU^2 MLPs of Nemotron-H run up and down LoRA projections with a
+# fused ReLU^2 activation derivative).  u = up projection, h = max(u, 0)^2,
+# Y = down projection of h; there is no gate.
+# --------------------------------------------------------------------------
+
+
+def relu2(x):
+    r = np.maximum(x, 0)
+    return r * r
+
+
+def relu2_grad(x):
+    return 2 * np.maximum(x, 0)
+
+
+def relu2_mlp_fwd(X, up, down):
+    """Forward.  Returns (Y, saved) with saved = dict(u, U_u, U_d)."""
+    u, U_u = proj_fwd(X, up["W"], up["A"], up["B"], up["s"])
+    h = relu2(u)
+    Y, U_d = proj_fwd(h, down["W"], down["A"], down["B"], down["s"])
+    return Y, dict(u=u, U_u=U_u, U_d=U_d)
+
+
+def relu2_mlp_bwd(dY, X, saved, up, down, hoist=True):
+    """Backward: the down projection's gradients at h = relu2(u) give dh, the
+    activation derivative gives du = dh * 2 max(u, 0), and the up
+    projection's gradients at X follow.  Returns dict(dX, dA_u, dB_u, dA_d,
+    dB_d)."""
+    u = saved["u"]
+    h = relu2(u)
+    dh, dA_d, dB_d = proj_bwd(dY, h, down["W"], down["A"], down["B"], down["s"], saved["U_d"], hoist)
+    du = dh * relu2_grad(u)
+    dX, dA_u, dB_u = proj_bwd(du, X, up["W"], up["A"], up["B"], up["s"], saved["U_u"], hoist)
+    return dict(dX=dX, dA_u=dA_u, dB_u=dB_u, dA_d=dA_d, dB_d=dB_d)
 
 
 # --------------------------------------------------------------------------

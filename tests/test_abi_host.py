@@ -213,3 +213,34 @@ def test_binding_picks_fp32_lora_mode_from_adapter_dtype():
         lm._call_dtype(X, (p32, p16))  # mixed adapter dtypes
     with pytest.raises(TypeError):
         lm._call_dtype(X.float(), (p16,))  # bf16 adapters with fp32 inputs
+
+
+def test_relu2_mlp_validation(L):
+    sz = C.c_size_t
+    f, b = sz(), sz()
+    ok = L.lora_relu2_mlp_desc(300, 256, 768, 64, L.LORA_BF16, 0)  # r = 64: one adapter per input
+    assert _status(L, "lora_relu2_mlp_workspace_size", C.byref(ok), C.byref(f), C.byref(b)) == L.LORA_OK
+    assert f.value > 0 and b.value > 0
+    bad = [
+        (L.lora_relu2_mlp_desc(300, 256, 720, 16, L.LORA_BF16, 0), L.LORA_ESHAPE),  # 720 % 64
+        (L.lora_relu2_mlp_desc(300, 256, 768, 72, L.LORA_BF16, 0), L.LORA_ESHAPE),  # r > 64
+        (L.lora_relu2_mlp_desc(300, 256, 768, 16, L.LORA_BF16, 1), L.LORA_EINVAL),  # reserved
+        (L.lora_relu2_mlp_desc(-1, 256, 768, 16, L.LORA_BF16, 0), L.LORA_ESHAPE),
+        (L.lora_relu2_mlp_desc(300, 256, 768, 16, 5, 0), L.LORA_EDTYPE),
+    ]
+    for desc, want in bad:
+        assert _status(L, "lora_relu2_mlp_workspace_size", C.byref(desc), C.byref(f), C.byref(b)) == want
+    d = L.lora_relu2_mlp_desc(128, 256, 768, 16, L.LORA_BF16, 0)
+    _status(L, "lora_relu2_mlp_workspace_size", C.byref(d), C.byref(f), C.byref(b))
+    sv = L.lora_relu2_mlp_saved(FAKE, FAKE)
+    up, dn = _proj(L), _proj(L)
+
+    def fwd(X=FAKE, Y=FAKE * 2, saved=sv, ws=FAKE, nbytes=f.value):
+        return _status(L, "lora_relu2_mlp_fwd", C.byref(d), X, C.byref(up), C.byref(dn), Y, C.byref(saved), ws,
+                       nbytes, None)
+
+    assert fwd(X=None) == L.LORA_EINVAL
+    assert fwd(X=FAKE + 2) == L.LORA_EALIGN
+    assert fwd(nbytes=f.value - 1) == L.LORA_EWORKSPACE
+    assert fwd(saved=L.lora_relu2_mlp_saved(FAKE, None)) == L.LORA_EINVAL
+    assert fwd(Y=FAKE) == L.LORA_EUNSUPPORTED  # Y aliases X

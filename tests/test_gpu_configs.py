@@ -1,4 +1,4 @@
-"""Full-size parity on the four GPU benchmark shapes.
+"""Full-size parity on the GPU benchmark shapes.
 
 The same calls bench.py times (lora_mlp_fwd/bwd, lora_qkv_fwd/bwd,
 lora_o_fwd/bwd, lora_nf4_quantize) run at full size on seeded inputs, and
@@ -13,7 +13,7 @@ import pytest
 
 from oracle import lora as OL
 from oracle import nf4 as ON
-from workload import CONFIGS, make_attn_inputs, make_mlp_inputs
+from workload import CONFIGS, make_attn_inputs, make_mlp_inputs, make_relu2_inputs
 from _util import TOL, assert_close, dev, host, proj_dev
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -130,3 +130,31 @@ def test_config5_qkv_o(lm):
     assert_close("dX_o", host(dXo), gor["dX"], tol)
     assert_close("dA_o", host(dAo), gor["dA"], tol)
     assert_close("dB_o", host(dBo), gor["dB"], tol)
+
+
+def test_config6_relu2_mlp(lm):
+    import torch
+
+    cfg = CONFIGS[6]
+    say(f"config 6: generating inputs ({cfg.note})")
+    inp = make_relu2_inputs(cfg)
+    X, dY = dev(inp["X"]), dev(inp["dY"])
+    up, down = (proj_dev(inp[k]) for k in ("up", "down"))
+    say("config 6: GPU forward + backward")
+    Y, saved = lm.relu2_mlp_fwd(X, up, down)
+    dX, grads = lm.relu2_mlp_bwd(dY, X, saved, up, down)
+    torch.cuda.synchronize()
+    got = dict(Y=host(Y), u=host(saved["u"]), U=host(saved["U"]), dX=host(dX),
+               **{k: host(v) for k, v in grads.items()})
+    del X, dY, Y, saved, dX, grads
+    torch.cuda.empty_cache()
+    say("config 6: oracle")
+    Yr, sr = OL.relu2_mlp_fwd(inp["X"], inp["up"], inp["down"])
+    gr = OL.relu2_mlp_bwd(inp["dY"], inp["X"], sr, inp["up"], inp["down"])
+    tol = TOL["bf16"]
+    assert_close("Y", got["Y"], Yr, tol)
+    assert_close("u", got["u"], sr["u"], tol)
+    assert_close("U", got["U"], np.concatenate([sr["U_u"], sr["U_d"]], axis=1), tol)
+    assert_close("dX", got["dX"], gr["dX"], tol)
+    for k_dev, k_ref in (("dA_up", "dA_u"), ("dB_up", "dB_u"), ("dA_down", "dA_d"), ("dB_down", "dB_d")):
+        assert_close(k_dev, got[k_dev], gr[k_ref], tol)

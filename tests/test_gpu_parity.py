@@ -11,7 +11,7 @@ import pytest
 
 from oracle import lora as OL
 from oracle import nf4 as ON
-from workload import WorkloadConfig, make_attn_inputs, make_mlp_inputs
+from workload import WorkloadConfig, make_attn_inputs, make_mlp_inputs, make_relu2_inputs
 from _util import TOL, assert_close, dev, host, proj_dev
 
 pytestmark = pytest.mark.gpu
@@ -117,6 +117,91 @@ def test_qkv_o_bf16_ragged(lm):
 def test_qkv_o_fp32(lm):
     cfg = WorkloadConfig(94, "attn", T=50, H=96, r=4, alpha=8, dtype="f32", Nq=96, Nk=32, Nv=40)
     _qkv_case(lm, cfg)
+
+
+# ---------------------------------------------------------------------------
+# Ungated ReLU^2 MLP
+# ---------------------------------------------------------------------------
+
+def _relu2_case(lm, cfg, nf4=False):
+    import torch
+
+    inp = make_relu2_inputs(cfg)
+    dt = cfg.dtype
+    nf = {}
+    if nf4:
+        for k in ("up", "down"):
+            w = lm.nf4_quantize(dev(inp[k]["W"]))
+            q = ON.quantize(inp[k]["W"])
+            torch.cuda.synchronize()
+            assert np.array_equal(w.codes.cpu().numpy(), q["codes"]), f"{k}: NF4 codes differ"
+            nf[k] = w
+            inp[k] = dict(inp[k], W=ON.dequantize(q, "bf16"))
+    ad = cfg.lora_dtype or None
+    X, dY = dev(inp["X"], dt), dev(inp["dY"], dt)
+    up, down = (proj_dev(inp[k], dt, nf4=nf.get(k), adapters=ad) for k in ("up", "down"))
+    Y, saved = lm.relu2_mlp_fwd(X, up, down)
+    dX, grads = lm.relu2_mlp_bwd(dY, X, saved, up, down)
+    torch.cuda.synchronize()
+    if ad:
+        assert all(t.dtype == torch.float32 for t in grads.values())
+        inp = dict(inp, up=OL.to_compute_adapters(inp["up"]), down=OL.to_compute_adapters(inp["down"]))
+    Yr, sr = OL.relu2_mlp_fwd(inp["X"], inp["up"], inp["down"])
+    gr = OL.relu2_mlp_bwd(inp["dY"], inp["X"], sr, inp["up"], inp["down"])
+    tol = TOL[dt]
+    assert_close("Y", host(Y), Yr, tol)
+    assert_close("u", host(saved["u"]), sr["u"], tol)
+    assert_close("U", host(saved["U"]), np.concatenate([sr["U_u"], sr["U_d"]], axis=1), tol)
+    assert_close("dX", host(dX), gr["dX"], tol)
+    for k_dev, k_ref in (("dA_up", "dA_u"), ("dB_up", "dB_u"), ("dA_down", "dA_d"), ("dB_down", "dB_d")):
+        assert_close(k_dev, host(grads[k_dev]), gr[k_ref], tol)
+    return Y, dX, grads
+
+
+def test_relu2_mlp_bf16_ragged(lm):
+    cfg = WorkloadConfig(97, "relu2", T=300, H=512, I=1088, r=16, alpha=32, dtype="bf16")
+    _relu2_case(lm, cfg)
+
+
+def test_relu2_mlp_bf16_rank32(lm):
+    cfg = WorkloadConfig(98, "relu2", T=200, H=256, I=640, r=32, alpha=16, dtype="bf16")
+    _relu2_case(lm, cfg)
+
+
+def test_relu2_mlp_fp32_odd_shapes(lm):
+    cfg = WorkloadConfig(99, "relu2", T=37, H=72, I=100, r=3, alpha=5, dtype="f32", rms_inputs=False)
+    _relu2_case(lm, cfg)
+
+
+def test_relu2_mlp_nf4_base(lm):
+    cfg = WorkloadConfig(100, "relu2", T=260, H=256, I=512, r=16, alpha=32, dtype="bf16", nf4=True)
+    _relu2_case(lm, cfg, nf4=True)
+
+
+def test_relu2_mlp_fp32_lora_mode(lm):
+    cfg = WorkloadConfig(101, "relu2", T=300, H=512, I=1088, r=16, alpha=32, dtype="bf16", lora_dtype="f32")
+    _relu2_case(lm, cfg)
+
+
+@pytest.mark.parametrize("T", [0, 1, 257])
+def test_relu2_mlp_edge_token_counts(lm, T):
+    import torch
+
+    cfg = WorkloadConfig(102, "relu2", T=T, H=256, I=512, r=16, alpha=32, dtype="bf16")
+    if T > 0:
+        _relu2_case(lm, cfg)
+        return
+    inp = make_relu2_inputs(cfg)
+    X = torch.empty((0, cfg.H), dtype=torch.bfloat16, device="cuda:0")
+    up, down = (proj_dev(inp[k]) for k in ("up", "down"))
+    Y, saved = lm.relu2_mlp_fwd(X, up, down)
+    grads = {k: torch.full_like(v, 7.0) for k, v in (("dA_up", up.A), ("dB_up", up.B), ("dA_down", down.A),
+                                                      ("dB_down", down.B))}
+    dX, grads = lm.relu2_mlp_bwd(X, X, saved, up, down, grads=grads)
+    torch.cuda.synchronize()
+    assert Y.shape == (0, cfg.H) and dX.shape == (0, cfg.H)
+    for k, v in grads.items():
+        assert not v.any(), f"{k} not zero-filled at T = 0"
 
 
 # ---------------------------------------------------------------------------

@@ -300,3 +300,51 @@ def test_fp32_lora_mode_matches_integer_brute_force():
 
     for g in (got["dA"], got["dB"]):
         assert np.any(round_to_bf16(g) != g)
+
+
+def _relu2_problem(seed=6, T=4, H=8, I=12, r=2):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((T, H))
+    dY = rng.standard_normal((T, H))
+    up = _proj(rng, H, I, r, 1.25)
+    down = _proj(rng, I, H, r, 2.0)
+    return X, dY, up, down
+
+
+def test_relu2_mlp_gradients_match_finite_differences():
+    X, dY, up, down = _relu2_problem()
+    Y, saved = L.relu2_mlp_fwd(X, up, down)
+    assert np.abs(saved["u"]).min() > 1e-3  # away from the kink of 2 max(u, 0) at 0
+    assert (saved["u"] > 0).any() and (saved["u"] < 0).any()
+
+    def loss():
+        Yv, _ = L.relu2_mlp_fwd(X, up, down)
+        return float(np.sum(Yv * dY))
+
+    g = L.relu2_mlp_bwd(dY, X, saved, up, down)
+    _assert_grad(g["dX"], _central_fd(loss, X), "dX")
+    for name, p in (("u", up), ("d", down)):
+        _assert_grad(g["dA_" + name], _central_fd(loss, p["A"]), "dA_" + name)
+        _assert_grad(g["dB_" + name], _central_fd(loss, p["B"]), "dB_" + name)
+
+
+def test_relu2_mlp_equals_base_mlp_on_merged_weights_and_special_values():
+    X, dY, up, down = _relu2_problem(seed=7, T=5, H=8, I=12, r=3)
+    Y, _ = L.relu2_mlp_fwd(X, up, down)
+
+    def merged(p):
+        return p["W"] + p["s"] * (p["A"] @ p["B"])
+
+    pre = X @ merged(up)
+    ref = np.where(pre > 0, pre * pre, 0.0) @ merged(down)
+    np.testing.assert_allclose(Y, ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+    x = np.array([-2.0, -1e-300, 0.0, 0.5, 3.0])
+    assert np.array_equal(L.relu2(x), [0.0, 0.0, 0.0, 0.25, 9.0])
+    assert np.array_equal(L.relu2_grad(x), [0.0, 0.0, 0.0, 1.0, 6.0])
+    # B = 0 on both projections: the base ReLU^2 MLP and zero dA
+    up0, down0 = dict(up, B=np.zeros_like(up["B"])), dict(down, B=np.zeros_like(down["B"]))
+    Y0, s0 = L.relu2_mlp_fwd(X, up0, down0)
+    base = np.where(X @ up["W"] > 0, (X @ up["W"]) ** 2, 0.0) @ down["W"]
+    np.testing.assert_allclose(Y0, base, rtol=0, atol=1e-12 * np.abs(base).max())
+    g0 = L.relu2_mlp_bwd(dY, X, s0, up0, down0)
+    assert not g0["dA_u"].any() and not g0["dA_d"].any()

@@ -1,4 +1,4 @@
-"""Seeded synthetic workloads for the fused LoRA MLP / QKV / O paths.
+"""Seeded synthetic workloads for the fused LoRA MLP (gated and ReLU^2) / QKV / O paths.
 
 This package only draws random inputs of the right shapes and distributions.
 It holds none of the method's arithmetic, so both the CPU oracle (through the
@@ -10,6 +10,8 @@ from .gen import (  # noqa: F401
     WorkloadConfig,
     bf16_round,
     make_attn_inputs,
+    make_inputs,
     make_mlp_inputs,
+    make_relu2_inputs,
     rng_for,
 )

@@ -56,7 +56,8 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
 
 @dataclass(frozen=True)
 class WorkloadConfig:
-    """One benchmark shape.  ``kind`` is ``"mlp"`` or ``"attn"``."""
+    """One benchmark shape.  ``kind`` is ``"mlp"`` (gated), ``"relu2"`` (ungated
+    ReLU^2 MLP) or ``"attn"``."""
 
     cid: int
     kind: str
@@ -89,6 +90,9 @@ class WorkloadConfig:
         if self.kind == "mlp":
             H, I = self.H, self.I
             return float(self.T) * (12 * H * I + 18 * r * (H + I))
+        if self.kind == "relu2":  # up and down: 2 forward + 2 backward GEMMs, 2 adapters
+            H, I = self.H, self.I
+            return float(self.T) * (8 * H * I + 12 * r * (H + I))
         H = self.H
         tot = 0
         for n_out in (self.Nq, self.Nk, self.Nv):
@@ -115,6 +119,8 @@ CONFIGS = {
     5: WorkloadConfig(5, "attn", T=8192, H=4096, r=16, alpha=32, dtype="bf16",
                       Nq=4096, Nk=1024, Nv=1024,
                       note="LoRA Q/K/V + O projections, Llama-3-8B attention shape"),
+    6: WorkloadConfig(6, "relu2", T=8192, H=4096, I=21504, r=16, alpha=32, dtype="bf16",
+                      note="Nemotron-H-8B-like ReLU^2 LoRA-MLP (4 x 2048 tokens)"),
 }
 
 
@@ -170,6 +176,22 @@ def make_mlp_inputs(cfg: WorkloadConfig, seed=None, T=None):
         down=make_proj(cfg, "down", cfg.I, cfg.H, seed),
     )
     return out
+
+
+def make_relu2_inputs(cfg: WorkloadConfig, seed=None, T=None):
+    """X, dY and the up/down projections of one ungated ReLU^2 LoRA MLP."""
+    T = cfg.T if T is None else T
+    return dict(
+        X=make_activation(cfg, "X", T, cfg.H, seed),
+        dY=make_activation(cfg, "dY", T, cfg.H, seed),
+        up=make_proj(cfg, "up", cfg.H, cfg.I, seed),
+        down=make_proj(cfg, "down", cfg.I, cfg.H, seed),
+    )
+
+
+def make_inputs(cfg: WorkloadConfig, seed=None, T=None):
+    """The inputs of any configuration, by its kind."""
+    return {"mlp": make_mlp_inputs, "relu2": make_relu2_inputs, "attn": make_attn_inputs}[cfg.kind](cfg, seed, T)
 
 
 def make_attn_inputs(cfg: WorkloadConfig, seed=None, T=None):
