@@ -328,6 +328,12 @@ float* partial_buf(Ws& w, const Ctx& c, int64_t T, int64_t K, int R) {
 // ---------------------------------------------------------------------------
 // MLP
 // ---------------------------------------------------------------------------
+// The bf16 backward GEMM of an MLP forms the down projection's dA in its
+// epilogue (rank <= 16): per-m-tile partials of h^T (s P_d), then a
+// fixed-order reduce; h itself is never stored in the backward.
+bool fuse_da(const Ctx& c, int64_t r) { return c.bf16 && r <= 16; }
+int64_t fused_da_floats(int64_t T, int64_t I) { return cdiv(T, gemm_tile_rows(true)) * I * 16; }
+
 struct MlpPlan {
   void *ad_f, *ad_b;  // adapter casts (fp32 LoRA-gradient mode), fwd / bwd workspace
   void *At_gu, *Us_gu, *BLt_gu, *h, *At_d, *Us_d, *BLt_d;                  // forward
@@ -356,7 +362,7 @@ MlpPlan plan_mlp(const Ctx& c, const lora_mlp_desc& d, void* ws_fwd, void* ws_bw
   p.ad_b = b.take(staged_bytes(c, ad, 3, r));
   p.Ps_d = b.take(T * RLd * c.es);
   p.BLt_dh = b.take(I * RLd * c.es);
-  p.hb = b.take(T * I * c.es);
+  p.hb = fuse_da(c, r) ? nullptr : b.take(T * I * c.es);
   p.dg = b.take(T * I * c.es);
   p.de = b.take(T * I * c.es);
   p.Ps_ug = b.take(T * RLg * c.es);
@@ -366,6 +372,7 @@ MlpPlan plan_mlp(const Ctx& c, const lora_mlp_desc& d, void* ws_fwd, void* ws_bw
     const int64_t cands[4] = {colproj_partial_floats(T, H, (int)r), colproj_partial_floats(T, I, (int)r),
                               colproj_partial_floats(T, H, (int)(2 * r)), 0};
     for (int i = 0; i < 3; ++i) pf = cands[i] > pf ? cands[i] : pf;
+    if (fuse_da(c, r) && fused_da_floats(T, I) > pf) pf = fused_da_floats(T, I);
   }
   p.partial = static_cast<float*>(b.take((size_t)pf * 4));
   p.rpartial = c.bf16 ? static_cast<float*>(b.take((size_t)rowcol_partial_floats(T, I > H ? I : H) * 4)) : nullptr;
@@ -418,7 +425,7 @@ Relu2Plan plan_relu2(const Ctx& c, const lora_relu2_mlp_desc& d, void* ws_fwd, v
   p.ad_b = b.take(staged_bytes(c, ad, 2, r));
   p.Ps_d = b.take(T * RL * c.es);
   p.BLt_dh = b.take(I * RL * c.es);
-  p.hb = b.take(T * I * c.es);
+  p.hb = fuse_da(c, r) ? nullptr : b.take(T * I * c.es);
   p.du = b.take(T * I * c.es);
   p.Ps_u = b.take(T * RL * c.es);
   p.BLt_dx = b.take(H * RL * c.es);
@@ -426,6 +433,7 @@ Relu2Plan plan_relu2(const Ctx& c, const lora_relu2_mlp_desc& d, void* ws_fwd, v
   if (c.bf16) {
     const int64_t a = colproj_partial_floats(T, H, (int)r), bb = colproj_partial_floats(T, I, (int)r);
     pf = a > bb ? a : bb;
+    if (fuse_da(c, r) && fused_da_floats(T, I) > pf) pf = fused_da_floats(T, I);
   }
   p.partial = static_cast<float*>(b.take((size_t)pf * 4));
   p.rpartial = c.bf16 ? static_cast<float*>(b.take((size_t)rowcol_partial_floats(T, I > H ? I : H) * 4)) : nullptr;
@@ -877,15 +885,28 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, 
   g.g_in = saved->g;
   g.dg_out = p.dg;
   g.de_out = p.de;
-  g.h_out = p.hb;
   g.ld_act = I;
+  const bool fda = fuse_da(c, r);
+  if (fda) {
+    g.dA_part = p.partial;
+    g.pd = p.Ps_d;
+    g.ldpd = RLd;
+  } else {
+    g.h_out = p.hb;
+  }
   LAUNCH(gemm_on(c, g, st, I));
 
-  // dA_d = s_d h^T P_d  (P_d already scaled)
+  // dA_d = s_d h^T P_d  (P_d already scaled): the reduce of the epilogue's
+  // per-m-tile partials, or a pass over the stored h
   ColProjArgs c2 = colproj_args(c, p.hb, I, T, I, p.Ps_d, RLd, (int)r, (int)r, false, p.partial);
   c2.scales[0] = 1.0f;
   c2.dest[0] = gr->dA_down;
-  LAUNCHN("colproj", st, launch_colproj(c.bf16, c2, st));
+  if (fda) {
+    c2.nchunk = (int)cdiv(T, gemm_tile_rows(true));
+    LAUNCHN("colproj", st, launch_colproj_reduce(c2, st));
+  } else {
+    LAUNCHN("colproj", st, launch_colproj(c.bf16, c2, st));
+  }
 
   // one pass over dg: P_u = dg B_u^T (formed once, into [s_u P_u | s_g P_g])
   // and dB_u = s_u U_u^T dg; the same over de for P_g and dB_g
@@ -1145,15 +1166,28 @@ lora_status lora_relu2_mlp_bwd(const lora_relu2_mlp_desc* d, const void* dY, con
   g.ldbl = RL;
   g.e_in = saved->u;
   g.dg_out = p.du;
-  g.h_out = p.hb;
   g.ld_act = I;
+  const bool fda = fuse_da(c, r);
+  if (fda) {
+    g.dA_part = p.partial;
+    g.pd = p.Ps_d;
+    g.ldpd = RL;
+  } else {
+    g.h_out = p.hb;
+  }
   LAUNCH(gemm_on(c, g, st, I));
 
-  // dA_d = s_d h^T P_d  (P_d already scaled)
+  // dA_d = s_d h^T P_d  (P_d already scaled): the reduce of the epilogue's
+  // per-m-tile partials, or a pass over the stored h
   ColProjArgs c2 = colproj_args(c, p.hb, I, T, I, p.Ps_d, RL, (int)r, (int)r, false, p.partial);
   c2.scales[0] = 1.0f;
   c2.dest[0] = gr->dA_down;
-  LAUNCHN("colproj", st, launch_colproj(c.bf16, c2, st));
+  if (fda) {
+    c2.nchunk = (int)cdiv(T, gemm_tile_rows(true));
+    LAUNCHN("colproj", st, launch_colproj_reduce(c2, st));
+  } else {
+    LAUNCHN("colproj", st, launch_colproj(c.bf16, c2, st));
+  }
 
   // one pass over du: P_u = du B_u^T (formed once) and dB_u = s_u U_u^T du
   RowProjArgs r2 = rowproj_args(p.du, I, T, I, up->B, I, (int)r, (int)RL, (int)r);

@@ -102,13 +102,13 @@ constexpr int epi_stage_bytes() {
   return EPI == EPI_STORE      ? 32 * (WN + 8) * 2
          : EPI == EPI_ACT_FWD  ? 3 * 32 * (WN / 2 + 8) * 2
          : EPI == EPI_ACT1_FWD ? 2 * 32 * (WN + 8) * 2
-                               : 32 * (WN + 4) * 4;
+                               : 32 * (WN + 4) * 4 + 32 * (WN + 8) * 2 + 32 * 16 * 2;
 }
 
 template <int WN, bool DUAL, int EPI>
 __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* wstage, const GemmArgs& args,
                                                int reg, int64_t mw, int64_t nbase, int64_t NR, int64_t M,
-                                               int lane) {
+                                               int lane, int wm) {
   constexpr int NI = WN / 32;
   if constexpr (EPI == EPI_STORE) {
     constexpr int LD = WN + 8;           // bf16 staging [32][WN], padded rows
@@ -233,12 +233,29 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
     });
   } else {
     // EPI_ACT_BWD (gated) or EPI_ACT1_BWD (ungated ReLU^2: du = dh phi'(u) into dg_out)
+    //
+    // With dA_part (fused adapter gradient of the next projection): h is
+    // staged in LDS instead of stored, and h^T Pd over this wavefront's rows
+    // is accumulated with 16x16x32 MFMAs (M = 16 columns of h, N = the 16
+    // columns of Pd, K = 32 rows per pass), both operands read with the
+    // transposing LDS read from row-major staging.  The two row groups of the
+    // block are added in LDS and written as the block's m-tile slice.
     constexpr bool GATED = EPI == EPI_ACT_BWD;
     constexpr int LD = WN + 4;           // fp32 staging [32][WN]
     constexpr int CPR = WN / 8;          // 8-float groups per row
     constexpr int RPP = 64 / CPR;
     constexpr int PASSES = 32 / RPP;
+    constexpr int HLD = WN + 8;          // bf16 h staging [32][WN] (fused dA)
+    constexpr int NCB = WN / 16;         // 16-column blocks of the fused product
     float* stg = reinterpret_cast<float*>(wstage);
+    uint16_t* hs = reinterpret_cast<uint16_t*>(wstage + 32 * LD * 4);
+    uint16_t* pds = hs + 32 * HLD;       // Pd rows of the pass [32][16]
+    const lds_char* const hs_l = (const lds_char*)hs;
+    const lds_char* const pds_l = (const lds_char*)pds;
+    const bool fuse = args.dA_part != nullptr;
+    f32x4 dacc[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) dacc[cb] = f32x4{0, 0, 0, 0};
     const char* ei = static_cast<const char*>(args.e_in);
     const char* gi = static_cast<const char*>(args.g_in);
     char* dgo = static_cast<char*>(args.dg_out);
@@ -255,6 +272,13 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
           *reinterpret_cast<f32x4*>(stg + (lane & 31) * LD + col) =
               f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
         }
+      // Pd rows of this pass: lane l loads half l & 1 of row l / 2 (rows past M read zero)
+      u32x4 pv = u32x4{0, 0, 0, 0};
+      if (fuse) {
+        const int64_t m = mw + j * 32 + (lane >> 1);
+        if (m < M) pv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(args.pd) +
+                                                          (m * args.ldpd + 8 * (lane & 1)) * 2);
+      }
       wave_sync();
       u32x4 ev[PASSES], gv[PASSES];
       f32x4 d0[PASSES], d1[PASSES];
@@ -298,11 +322,50 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
           const int64_t off = (m * ld + n) * 2;
           *reinterpret_cast<u32x4*>(dgo + off) = dgv;
           if constexpr (GATED) *reinterpret_cast<u32x4*>(deo + off) = dev;
-          *reinterpret_cast<u32x4*>(ho + off) = hv;
+          if (!fuse) *reinterpret_cast<u32x4*>(ho + off) = hv;
+        }
+        // h is zero past M and NR (e, g read as zero there)
+        if (fuse) *reinterpret_cast<u32x4*>(hs + row * HLD + c8 * 8) = hv;
+      }
+      if (fuse) {
+        *reinterpret_cast<u32x4*>(pds + (lane >> 1) * 16 + 8 * (lane & 1)) = pv;
+        wave_sync();
+        // lanes 16 g + 4 jj + q point at row 8 g + jj (+ 4), columns 4 q .. 4 q + 3 of a
+        // 16-column block: lane 16 g + i receives column i of rows 8 g .. 8 g + 7
+        const int g = lane >> 4, jj = (lane & 15) >> 2, q = lane & 3;
+        const bf16x8 pb = lds_read_tr8(pds_l + ((8 * g + jj) * 16 + 4 * q) * 2, 4 * 16 * 2);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const bf16x8 ha = lds_read_tr8(hs_l + ((8 * g + jj) * HLD + 16 * cb + 4 * q) * 2, 4 * HLD * 2);
+          dacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha, pb, dacc[cb], 0, 0, 0);
         }
       }
       wave_sync();
     });
+    if (fuse) {
+      // dacc[cb][v] = sum over this wavefront's 128 rows of h[., c] Pd[., lane % 16],
+      // c = 16 cb + 4 (lane / 16) + v.  Group 1 hands its sums to group 0 through LDS.
+      constexpr int EB = epi_stage_bytes<WN, EPI>();
+      f32x4* red = reinterpret_cast<f32x4*>(wstage);
+      if (wm == 1) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) red[cb * 64 + lane] = dacc[cb];
+      }
+      __syncthreads();
+      if (wm == 0) {
+        const f32x4* other = reinterpret_cast<const f32x4*>(wstage + 4 * EB);
+        const int64_t tm = mw / 256;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const f32x4 o = other[cb * 64 + lane];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int64_t n = nbase + 16 * cb + 4 * (lane >> 4) + v;
+            if (n < NR) args.dA_part[(tm * NR + n) * 16 + (lane & 15)] = dacc[cb][v] + o[v];
+          }
+        }
+      }
+    }
   }
 }
 
@@ -856,7 +919,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   char* const wstage = smem_raw + wave * EB;
   const int64_t mw = m0 + wm * 128;
   const int64_t nbase = DUAL ? tnl * 128 + wn * 32 : tnl * 256 + wn * 64;
-  run_epilogue_w<64, DUAL, EPI>(acc, wstage, args, reg, mw, nbase, NR, M, lane);
+  run_epilogue_w<64, DUAL, EPI>(acc, wstage, args, reg, mw, nbase, NR, M, lane, wm);
 }
 
 template <int BKIND, bool DUAL, int EPI, bool NF4>

@@ -75,6 +75,14 @@ struct GemmArgs {
   void* dg_out;
   void* de_out;
   int64_t ld_act;
+  // bf16 backward epilogues (EPI_ACT_BWD, EPI_ACT1_BWD) with dA_part set: h is
+  // not stored; instead each block adds its rows of h^T Pd (Pd [M, ldpd],
+  // columns 0..15, the scaled P of the next projection, zero past its rank)
+  // into dA_part [ntile_m, N, 16] (fp32, one slice per m-tile), which a
+  // fixed-order reduce over the m-tiles turns into dA.
+  float* dA_part;
+  const void* pd;
+  int64_t ldpd;
 };
 
 // Columns of output covered by one n-tile.
@@ -126,6 +134,9 @@ struct ColProjArgs {
 
 hipError_t launch_rowproj(bool bf16, const RowProjArgs& a, hipStream_t st);
 hipError_t launch_colproj(bool bf16, const ColProjArgs& a, hipStream_t st);
+// Only the reduce of colproj: dest = scales * sum over a.nchunk slices of
+// a.partial [nchunk, K, 16] (R <= 16), in ascending slice order.
+hipError_t launch_colproj_reduce(const ColProjArgs& a, hipStream_t st);
 // rowproj r and colproj c over the same Z [T, K] in one pass (bf16, r.R <= 16):
 // the colproj blocks also form r's product over their 256 columns; a
 // fixed-order reduce then writes r's outputs.  Other cases run the two

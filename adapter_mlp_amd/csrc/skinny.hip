@@ -470,6 +470,12 @@ hipError_t launch_rowproj(bool bf16, const RowProjArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+hipError_t launch_colproj_reduce(const ColProjArgs& a, hipStream_t st) {
+  if (a.K * a.R == 0) return hipSuccess;
+  hipLaunchKernelGGL(colproj_reduce_kernel, dim3(nblk(a.K * a.R, 256)), dim3(256), 0, st, a, 16);
+  return hipGetLastError();
+}
+
 hipError_t launch_colproj(bool bf16, const ColProjArgs& a0, hipStream_t st) {
   ColProjArgs a = a0;
   if (!bf16) {
