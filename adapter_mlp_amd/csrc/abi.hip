@@ -269,6 +269,24 @@ PackPart part(const void* src, int64_t ld, int64_t v0, int64_t nv, int k0, int w
   return p;
 }
 
+// The adapter-operand packs of one call, issued as one launch before the
+// first kernel that reads them.
+struct PackBatch {
+  PackBatchArgs b{};
+  void add(const PackLoraArgs& a) { b.job[b.njobs++] = a; }
+  // [A_0 | A_1 | ...]^T, K-contiguous: out [Rpad, K] from A_q [K, w]
+  void add_cat_t(void* out, int64_t K, int Rpad, int w, int nparts, const void* const* srcs) {
+    PackLoraArgs a{};
+    a.out = out;
+    a.vcols = K;
+    a.RL = Rpad;
+    a.nparts = nparts;
+    a.kmajor = 1;
+    for (int q = 0; q < nparts; ++q) a.part[q] = part(srcs[q], w, 0, K, q * w, w, false);
+    add(a);
+  }
+};
+
 lora_status check_ws(const void* ws, size_t have, size_t need) {
   CHECK(have >= need, LORA_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", have, need);
   CHECK(need == 0 || ws != nullptr, LORA_EWORKSPACE, "workspace is NULL");
@@ -567,15 +585,10 @@ lora_status proj_forward(const Ctx& c, int64_t T, int64_t K, int64_t N, int64_t 
   const bool lora = r > 0;
   GemmArgs g{};
   if (lora) {
+    // every adapter operand of the call, packed in one launch
+    PackBatch pb;
     const void* srcs[1] = {o->A};
-    LAUNCHN("pack", st, launch_pack_cat_t(c.bf16, p.At, K, (int)r, (int)r, 1, srcs, st));
-    RowProjArgs ra = rowproj_args(X, K, T, K, p.At, K, (int)r, (int)RL, (int)r);
-    ra.scales[0] = o->scale;
-    ra.out1 = U;
-    ra.ld1 = r;
-    ra.out2 = p.Us;
-    ra.ld2 = RL;
-    LAUNCHN("rowproj", st, launch_rowproj(c.bf16, ra, st));
+    pb.add_cat_t(p.At, K, (int)r, (int)r, 1, srcs);
     PackLoraArgs pl{};
     pl.out = p.BLt;
     pl.vcols = N;
@@ -583,7 +596,15 @@ lora_status proj_forward(const Ctx& c, int64_t T, int64_t K, int64_t N, int64_t 
     pl.nparts = 1;
     pl.part[0] = part(o->B, N, 0, N, 0, (int)r, true);
     pl.kmajor = c.bf16 ? 1 : 0;  // the bf16 NN GEMM reads [RL, vcols]
-    LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, pl, st));
+    pb.add(pl);
+    LAUNCHN("pack", st, launch_pack_batch(c.bf16, pb.b, st));
+    RowProjArgs ra = rowproj_args(X, K, T, K, p.At, K, (int)r, (int)RL, (int)r);
+    ra.scales[0] = o->scale;
+    ra.out1 = U;
+    ra.ld1 = r;
+    ra.out2 = p.Us;
+    ra.ld2 = RL;
+    LAUNCHN("rowproj", st, launch_rowproj(c.bf16, ra, st));
     g.AL = p.Us;
     g.ldal = RL;
     g.RL = (int)RL;
@@ -614,13 +635,16 @@ lora_status proj_input_grad(const Ctx& c, int64_t T, int64_t K, int64_t N, int64
   const int64_t RL = c.rl(r);
   GemmArgs g{};
   if (r > 0) {
+    // every adapter operand of the call, packed in one launch
+    PackBatch pb;
     PackLoraArgs pl{};
     pl.out = p.BLt_dx;
     pl.vcols = K;
     pl.RL = (int)RL;
     pl.nparts = 1;
     pl.part[0] = part(o->A, r, 0, K, 0, (int)r, false);
-    LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, pl, st));
+    pb.add(pl);
+    LAUNCHN("pack", st, launch_pack_batch(c.bf16, pb.b, st));
     g.AL = p.Ps;
     g.ldal = RL;
     g.RL = (int)RL;
@@ -694,6 +718,7 @@ lora_status lora_mlp_fwd(const lora_mlp_desc* d, const void* X, const lora_proj*
   TRY(check_proj(c, gate, H, I, "gate"));
   TRY(check_proj(c, up, H, I, "up"));
   TRY(check_proj(c, down, I, H, "down"));
+  CHECK((gate->nf4 != nullptr) == (up->nf4 != nullptr), LORA_EUNSUPPORTED, "gate and up must both be NF4 or both dense");
   CHECK(!overlaps(Y, T * H * c.es, X, T * H * c.es), LORA_EUNSUPPORTED, "Y aliases X");
   MlpPlan need = plan_mlp(c, *d, nullptr, nullptr);
   TRY(check_ws(ws, ws_bytes, need.fwd_bytes));
@@ -708,10 +733,32 @@ lora_status lora_mlp_fwd(const lora_mlp_desc* d, const void* X, const lora_proj*
   gate = &sp[0];
   up = &sp[1];
   down = &sp[2];
+  // every adapter operand of the call, packed in one launch
+  PackBatch pb;
+  const void* srcs_gu[2] = {gate->A, up->A};
+  pb.add_cat_t(p.At_gu, H, (int)(2 * r), (int)r, 2, srcs_gu);
+  PackLoraArgs pl{};
+  pl.out = p.BLt_gu;
+  pl.vcols = 2 * I;
+  pl.RL = (int)RLg;
+  pl.nparts = 2;
+  pl.part[0] = part(gate->B, I, 0, I, 0, (int)r, true);
+  pl.part[1] = part(up->B, I, I, I, (int)r, (int)r, true);
+  pl.kmajor = c.bf16 ? 1 : 0;  // the bf16 NN GEMM reads [RL, vcols]
+  pb.add(pl);
+  const void* srcs_d[1] = {down->A};
+  pb.add_cat_t(p.At_d, I, (int)r, (int)r, 1, srcs_d);
+  PackLoraArgs pd{};
+  pd.out = p.BLt_d;
+  pd.vcols = H;
+  pd.RL = (int)RLd;
+  pd.nparts = 1;
+  pd.part[0] = part(down->B, H, 0, H, 0, (int)r, true);
+  pd.kmajor = c.bf16 ? 1 : 0;  // the bf16 NN GEMM reads [RL, vcols]
+  pb.add(pd);
+  LAUNCHN("pack", st, launch_pack_batch(c.bf16, pb.b, st));
 
   // adapter inputs of gate and up in one pass over X: [U_g | U_u] = X [A_g | A_u]
-  const void* srcs_gu[2] = {gate->A, up->A};
-  LAUNCHN("pack", st, launch_pack_cat_t(c.bf16, p.At_gu, H, (int)(2 * r), (int)r, 2, srcs_gu, st));
   RowProjArgs ra = rowproj_args(X, H, T, H, p.At_gu, H, (int)(2 * r), (int)RLg, (int)r);
   ra.scales[0] = gate->scale;
   ra.scales[1] = up->scale;
@@ -722,16 +769,6 @@ lora_status lora_mlp_fwd(const lora_mlp_desc* d, const void* X, const lora_proj*
   ra.ld2 = RLg;
   LAUNCHN("rowproj", st, launch_rowproj(c.bf16, ra, st));
 
-  PackLoraArgs pl{};
-  pl.out = p.BLt_gu;
-  pl.vcols = 2 * I;
-  pl.RL = (int)RLg;
-  pl.nparts = 2;
-  pl.part[0] = part(gate->B, I, 0, I, 0, (int)r, true);
-  pl.part[1] = part(up->B, I, I, I, (int)r, (int)r, true);
-  pl.kmajor = c.bf16 ? 1 : 0;  // the bf16 NN GEMM reads [RL, vcols]
-  LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, pl, st));
-
   // gate/up GEMM with the activation epilogue
   GemmArgs g{};
   g.M = T;
@@ -741,7 +778,6 @@ lora_status lora_mlp_fwd(const lora_mlp_desc* d, const void* X, const lora_proj*
   g.epi = EPI_ACT_FWD;
   g.act = d->act;
   g.nf4 = gate->nf4 != nullptr;
-  CHECK((gate->nf4 != nullptr) == (up->nf4 != nullptr), LORA_EUNSUPPORTED, "gate and up must both be NF4 or both dense");
   g.bkind = B_NN;
   g.seg[0].A = X;
   g.seg[0].lda = H;
@@ -763,8 +799,6 @@ lora_status lora_mlp_fwd(const lora_mlp_desc* d, const void* X, const lora_proj*
   LAUNCH(gemm_on(c, g, st, 2 * I));
 
   // U_d = h A_d, then the down GEMM
-  const void* srcs_d[1] = {down->A};
-  LAUNCHN("pack", st, launch_pack_cat_t(c.bf16, p.At_d, I, (int)r, (int)r, 1, srcs_d, st));
   RowProjArgs rd = rowproj_args(p.h, I, T, I, p.At_d, I, (int)r, (int)RLd, (int)r);
   rd.scales[0] = down->scale;
   rd.out1 = saved->U;
@@ -773,14 +807,6 @@ lora_status lora_mlp_fwd(const lora_mlp_desc* d, const void* X, const lora_proj*
   rd.out2 = p.Us_d;
   rd.ld2 = RLd;
   LAUNCHN("rowproj", st, launch_rowproj(c.bf16, rd, st));
-  PackLoraArgs pd{};
-  pd.out = p.BLt_d;
-  pd.vcols = H;
-  pd.RL = (int)RLd;
-  pd.nparts = 1;
-  pd.part[0] = part(down->B, H, 0, H, 0, (int)r, true);
-  pd.kmajor = c.bf16 ? 1 : 0;  // the bf16 NN GEMM reads [RL, vcols]
-  LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, pd, st));
 
   GemmArgs gd{};
   gd.M = T;
@@ -829,7 +855,7 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, 
   TRY(check_proj(c, up, H, I, "up"));
   TRY(check_proj(c, down, I, H, "down"));
   CHECK((gate->nf4 != nullptr) == (up->nf4 != nullptr), LORA_EUNSUPPORTED, "gate and up must both be NF4 or both dense");
-  CHECK(!overlaps(dX, T * H * c.es, X, T * H * c.es), LORA_EUNSUPPORTED, "dX aliases X (in-place dX is not supported)");
+  CHECK(dX == X || !overlaps(dX, T * H * c.es, X, T * H * c.es), LORA_EUNSUPPORTED, "dX partly overlaps X");
   MlpPlan need = plan_mlp(c, *d, nullptr, nullptr);
   TRY(check_ws(ws, ws_bytes, need.bwd_bytes));
   MlpPlan p = plan_mlp(c, *d, nullptr, ws);
@@ -843,6 +869,24 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, 
   up = &sp[1];
   down = &sp[2];
   const void* U = saved->U;
+  // every adapter operand of the call, packed in one launch
+  PackBatch pb;
+  PackLoraArgs pl{};
+  pl.out = p.BLt_dh;
+  pl.vcols = I;
+  pl.RL = (int)RLd;
+  pl.nparts = 1;
+  pl.part[0] = part(down->A, r, 0, I, 0, (int)r, false);
+  pb.add(pl);
+  PackLoraArgs px{};
+  px.out = p.BLt_dx;
+  px.vcols = H;
+  px.RL = (int)RLg;
+  px.nparts = 2;
+  px.part[0] = part(up->A, r, 0, H, 0, (int)r, false);
+  px.part[1] = part(gate->A, r, 0, H, (int)r, (int)r, false);
+  pb.add(px);
+  LAUNCHN("pack", st, launch_pack_batch(c.bf16, pb.b, st));
 
   // one pass over dY: P_d = dY B_d^T, formed once (scaled copy feeds dA_d and
   // the dh GEMM), and dB_d = s_d U_d^T dY
@@ -856,13 +900,6 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, 
   LAUNCHN("rowcol", st, launch_rowcol(c.bf16, c1, r1, p.rpartial, st));
 
   // dh GEMM with the activation-gradient epilogue -> dg, de, h
-  PackLoraArgs pl{};
-  pl.out = p.BLt_dh;
-  pl.vcols = I;
-  pl.RL = (int)RLd;
-  pl.nparts = 1;
-  pl.part[0] = part(down->A, r, 0, I, 0, (int)r, false);
-  LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, pl, st));
   GemmArgs g{};
   g.M = T;
   g.nseg = 1;
@@ -936,14 +973,6 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, 
   LAUNCHN("colproj", st, launch_colproj(c.bf16, c5, st));
 
   // dX = dg W_u^T + de W_g^T + [s_u P_u | s_g P_g] [A_u | A_g]^T
-  PackLoraArgs px{};
-  px.out = p.BLt_dx;
-  px.vcols = H;
-  px.RL = (int)RLg;
-  px.nparts = 2;
-  px.part[0] = part(up->A, r, 0, H, 0, (int)r, false);
-  px.part[1] = part(gate->A, r, 0, H, (int)r, (int)r, false);
-  LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, px, st));
   GemmArgs gx{};
   gx.M = T;
   gx.nseg = 2;
@@ -1010,10 +1039,31 @@ lora_status lora_relu2_mlp_fwd(const lora_relu2_mlp_desc* d, const void* X, cons
   STAGE(p.ad_f, in, ad, 2, r, sp, st);
   up = &sp[0];
   down = &sp[1];
+  // every adapter operand of the call, packed in one launch
+  PackBatch pb;
+  const void* srcs_u[1] = {up->A};
+  pb.add_cat_t(p.At_u, H, (int)r, (int)r, 1, srcs_u);
+  PackLoraArgs pu{};
+  pu.out = p.BLt_u;
+  pu.vcols = I;
+  pu.RL = (int)RL;
+  pu.nparts = 1;
+  pu.part[0] = part(up->B, I, 0, I, 0, (int)r, true);
+  pu.kmajor = c.bf16 ? 1 : 0;  // the bf16 NN GEMM reads [RL, vcols]
+  pb.add(pu);
+  const void* srcs_d[1] = {down->A};
+  pb.add_cat_t(p.At_d, I, (int)r, (int)r, 1, srcs_d);
+  PackLoraArgs pd{};
+  pd.out = p.BLt_d;
+  pd.vcols = H;
+  pd.RL = (int)RL;
+  pd.nparts = 1;
+  pd.part[0] = part(down->B, H, 0, H, 0, (int)r, true);
+  pd.kmajor = c.bf16 ? 1 : 0;
+  pb.add(pd);
+  LAUNCHN("pack", st, launch_pack_batch(c.bf16, pb.b, st));
 
   // U_u = X A_u, then the up GEMM with the ReLU^2 epilogue (u, h)
-  const void* srcs_u[1] = {up->A};
-  LAUNCHN("pack", st, launch_pack_cat_t(c.bf16, p.At_u, H, (int)r, (int)r, 1, srcs_u, st));
   RowProjArgs ru = rowproj_args(X, H, T, H, p.At_u, H, (int)r, (int)RL, (int)r);
   ru.scales[0] = up->scale;
   ru.out1 = saved->U;
@@ -1022,14 +1072,6 @@ lora_status lora_relu2_mlp_fwd(const lora_relu2_mlp_desc* d, const void* X, cons
   ru.out2 = p.Us_u;
   ru.ld2 = RL;
   LAUNCHN("rowproj", st, launch_rowproj(c.bf16, ru, st));
-  PackLoraArgs pu{};
-  pu.out = p.BLt_u;
-  pu.vcols = I;
-  pu.RL = (int)RL;
-  pu.nparts = 1;
-  pu.part[0] = part(up->B, I, 0, I, 0, (int)r, true);
-  pu.kmajor = c.bf16 ? 1 : 0;  // the bf16 NN GEMM reads [RL, vcols]
-  LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, pu, st));
   GemmArgs g{};
   g.M = T;
   g.nseg = 1;
@@ -1053,8 +1095,6 @@ lora_status lora_relu2_mlp_fwd(const lora_relu2_mlp_desc* d, const void* X, cons
   LAUNCH(gemm_on(c, g, st, I));
 
   // U_d = h A_d, then the down GEMM
-  const void* srcs_d[1] = {down->A};
-  LAUNCHN("pack", st, launch_pack_cat_t(c.bf16, p.At_d, I, (int)r, (int)r, 1, srcs_d, st));
   RowProjArgs rd = rowproj_args(p.h, I, T, I, p.At_d, I, (int)r, (int)RL, (int)r);
   rd.scales[0] = down->scale;
   rd.out1 = saved->U;
@@ -1063,14 +1103,6 @@ lora_status lora_relu2_mlp_fwd(const lora_relu2_mlp_desc* d, const void* X, cons
   rd.out2 = p.Us_d;
   rd.ld2 = RL;
   LAUNCHN("rowproj", st, launch_rowproj(c.bf16, rd, st));
-  PackLoraArgs pd{};
-  pd.out = p.BLt_d;
-  pd.vcols = H;
-  pd.RL = (int)RL;
-  pd.nparts = 1;
-  pd.part[0] = part(down->B, H, 0, H, 0, (int)r, true);
-  pd.kmajor = c.bf16 ? 1 : 0;
-  LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, pd, st));
   GemmArgs gd{};
   gd.M = T;
   gd.nseg = 1;
@@ -1114,7 +1146,7 @@ lora_status lora_relu2_mlp_bwd(const lora_relu2_mlp_desc* d, const void* dY, con
   TRY(check_ptr(c, gr->dB_down, "dB_down"));
   TRY(check_proj(c, up, H, I, "up"));
   TRY(check_proj(c, down, I, H, "down"));
-  CHECK(!overlaps(dX, T * H * c.es, X, T * H * c.es), LORA_EUNSUPPORTED, "dX aliases X (in-place dX is not supported)");
+  CHECK(dX == X || !overlaps(dX, T * H * c.es, X, T * H * c.es), LORA_EUNSUPPORTED, "dX partly overlaps X");
   Relu2Plan need = plan_relu2(c, *d, nullptr, nullptr);
   TRY(check_ws(ws, ws_bytes, need.bwd_bytes));
   Relu2Plan p = plan_relu2(c, *d, nullptr, ws);
@@ -1127,6 +1159,23 @@ lora_status lora_relu2_mlp_bwd(const lora_relu2_mlp_desc* d, const void* dY, con
   up = &sp[0];
   down = &sp[1];
   const void* U = saved->U;
+  // every adapter operand of the call, packed in one launch
+  PackBatch pb;
+  PackLoraArgs pl{};
+  pl.out = p.BLt_dh;
+  pl.vcols = I;
+  pl.RL = (int)RL;
+  pl.nparts = 1;
+  pl.part[0] = part(down->A, r, 0, I, 0, (int)r, false);
+  pb.add(pl);
+  PackLoraArgs px{};
+  px.out = p.BLt_dx;
+  px.vcols = H;
+  px.RL = (int)RL;
+  px.nparts = 1;
+  px.part[0] = part(up->A, r, 0, H, 0, (int)r, false);
+  pb.add(px);
+  LAUNCHN("pack", st, launch_pack_batch(c.bf16, pb.b, st));
 
   // one pass over dY: P_d = dY B_d^T, formed once (scaled copy feeds dA_d and
   // the dh GEMM), and dB_d = s_d U_d^T dY
@@ -1140,13 +1189,6 @@ lora_status lora_relu2_mlp_bwd(const lora_relu2_mlp_desc* d, const void* dY, con
   LAUNCHN("rowcol", st, launch_rowcol(c.bf16, c1, r1, p.rpartial, st));
 
   // dh GEMM with the ReLU^2 gradient epilogue -> du, h
-  PackLoraArgs pl{};
-  pl.out = p.BLt_dh;
-  pl.vcols = I;
-  pl.RL = (int)RL;
-  pl.nparts = 1;
-  pl.part[0] = part(down->A, r, 0, I, 0, (int)r, false);
-  LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, pl, st));
   GemmArgs g{};
   g.M = T;
   g.nseg = 1;
@@ -1206,13 +1248,6 @@ lora_status lora_relu2_mlp_bwd(const lora_relu2_mlp_desc* d, const void* dY, con
   LAUNCHN("colproj", st, launch_colproj(c.bf16, c4, st));
 
   // dX = du W_u^T + (s_u P_u) A_u^T
-  PackLoraArgs px{};
-  px.out = p.BLt_dx;
-  px.vcols = H;
-  px.RL = (int)RL;
-  px.nparts = 1;
-  px.part[0] = part(up->A, r, 0, H, 0, (int)r, false);
-  LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, px, st));
   GemmArgs gx{};
   gx.M = T;
   gx.nseg = 1;
@@ -1278,18 +1313,10 @@ lora_status lora_qkv_fwd(const lora_qkv_desc* d, const void* X, const lora_proj*
   k = &sp[1];
   v = &sp[2];
 
-  // [U_q | U_k | U_v] = X [A_q | A_k | A_v] in one pass over X
+  // every adapter operand of the call, packed in one launch
+  PackBatch pb;
   const void* srcs[3] = {q->A, k->A, v->A};
-  LAUNCHN("pack", st, launch_pack_cat_t(c.bf16, p.At, H, (int)(3 * r), (int)r, 3, srcs, st));
-  RowProjArgs ra = rowproj_args(X, H, T, H, p.At, H, (int)(3 * r), (int)RL, (int)r);
-  ra.scales[0] = q->scale;
-  ra.scales[1] = k->scale;
-  ra.scales[2] = v->scale;
-  ra.out1 = U;
-  ra.ld1 = 3 * r;
-  ra.out2 = p.Us;
-  ra.ld2 = RL;
-  LAUNCHN("rowproj", st, launch_rowproj(c.bf16, ra, st));
+  pb.add_cat_t(p.At, H, (int)(3 * r), (int)r, 3, srcs);
   PackLoraArgs pl{};
   pl.out = p.BLt;
   pl.vcols = Nq + Nk + Nv;
@@ -1299,7 +1326,19 @@ lora_status lora_qkv_fwd(const lora_qkv_desc* d, const void* X, const lora_proj*
   pl.part[1] = part(k->B, Nk, Nq, Nk, (int)r, (int)r, true);
   pl.part[2] = part(v->B, Nv, Nq + Nk, Nv, (int)(2 * r), (int)r, true);
   pl.kmajor = c.bf16 ? 1 : 0;  // the bf16 NN GEMM reads [RL, vcols]
-  LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, pl, st));
+  pb.add(pl);
+  LAUNCHN("pack", st, launch_pack_batch(c.bf16, pb.b, st));
+
+  // [U_q | U_k | U_v] = X [A_q | A_k | A_v] in one pass over X
+  RowProjArgs ra = rowproj_args(X, H, T, H, p.At, H, (int)(3 * r), (int)RL, (int)r);
+  ra.scales[0] = q->scale;
+  ra.scales[1] = k->scale;
+  ra.scales[2] = v->scale;
+  ra.out1 = U;
+  ra.ld1 = 3 * r;
+  ra.out2 = p.Us;
+  ra.ld2 = RL;
+  LAUNCHN("rowproj", st, launch_rowproj(c.bf16, ra, st));
 
   GemmArgs g{};
   g.M = T;
@@ -1357,7 +1396,7 @@ lora_status lora_qkv_bwd(const lora_qkv_desc* d, const void* dQ, const void* dK,
   TRY(check_proj(c, v, H, Nv, "v"));
   CHECK(((q->nf4 != nullptr) == (k->nf4 != nullptr)) && ((k->nf4 != nullptr) == (v->nf4 != nullptr)),
         LORA_EUNSUPPORTED, "q, k, v must all be NF4 or all dense");
-  CHECK(!overlaps(dX, T * H * c.es, X, T * H * c.es), LORA_EUNSUPPORTED, "dX aliases X (in-place dX is not supported)");
+  CHECK(dX == X || !overlaps(dX, T * H * c.es, X, T * H * c.es), LORA_EUNSUPPORTED, "dX partly overlaps X");
   QkvPlan need = plan_qkv(c, *d, nullptr, nullptr);
   TRY(check_ws(ws, ws_bytes, need.bwd_bytes));
   QkvPlan p = plan_qkv(c, *d, nullptr, ws);
@@ -1402,7 +1441,9 @@ lora_status lora_qkv_bwd(const lora_qkv_desc* d, const void* dQ, const void* dK,
   pl.RL = (int)RL;
   pl.nparts = 3;
   for (int i = 0; i < 3; ++i) pl.part[i] = part(projs[i]->A, r, 0, H, (int)(i * r), (int)r, false);
-  LAUNCHN("pack", st, launch_pack_lora_b(c.bf16, pl, st));
+  PackBatch pb;
+  pb.add(pl);
+  LAUNCHN("pack", st, launch_pack_batch(c.bf16, pb.b, st));
   GemmArgs g{};
   g.M = T;
   g.nseg = 3;
@@ -1472,7 +1513,7 @@ lora_status lora_o_bwd(const lora_o_desc* d, const void* dY, const void* X, cons
   TRY(check_ptr(c, dA, "dA"));
   TRY(check_ptr(c, dB, "dB"));
   TRY(check_proj(c, o, K, N, "o"));
-  CHECK(!overlaps(dX, T * K * c.es, X, T * K * c.es), LORA_EUNSUPPORTED, "dX aliases X (in-place dX is not supported)");
+  CHECK(dX == X || !overlaps(dX, T * K * c.es, X, T * K * c.es), LORA_EUNSUPPORTED, "dX partly overlaps X");
   OPlan need = plan_o(c, T, K, N, r, false, nullptr, nullptr);
   TRY(check_ws(ws, ws_bytes, need.bwd_bytes));
   OPlan p = plan_o(c, T, K, N, r, false, nullptr, ws);

@@ -19,7 +19,7 @@ namespace lora {
 //   B_NT: B_s is [N, K_s] row-major (W used transposed, an input gradient).
 // The LoRA tail AL [M, RL] / BLt [vcols, RL] always comes K-contiguous; BLt
 // row v is the adapter column that feeds output column n of region p and
-// column group c, v = vcol0[p][c] + n (built by lora_pack_* on the host side).
+// column group c, v = vcol0[p][c] + n (built by the packing jobs below).
 // Up to 3 output regions split the N range (Q/K/V); in "dual" mode every
 // tile interleaves two column groups (gate, up) over the same output columns
 // so the activation epilogue sees e and g of one element in one lane.
@@ -148,14 +148,14 @@ int64_t colproj_partial_floats(int64_t T, int64_t K, int R);
 int colproj_nchunk(int64_t T, int64_t K);
 
 // ---------------------------------------------------------------------------
-// Small packing kernels (adapter operands in the layout the kernels read).
-// pack_cat_t:  out[j, k] = src_q[k, j - q*w] for j < nparts*w, 0 for j < Rpad
-//              (A_p [K, w] of several adapters -> one K-contiguous [Rpad, K]).
-// pack_lora_b: builds the adapter operand of the GEMM's LoRA K tile over vcols
-//              virtual columns and RL rows of K: for part descriptors (v0, nv,
-//              k0, w, src, ld, nn), value(v0 + n, k0 + i) = nn ? src[i*ld + n]
-//              : src[n*ld + i] for n < nv, i < w, everything else 0; stored
-//              [vcols, RL] (K-contiguous) or, with kmajor, [RL, vcols].
+// Packing of the adapter operands in the layout the kernels read.  A job
+// builds the operand of a LoRA K tile over vcols virtual columns and RL rows
+// of K: for part descriptors (v0, nv, k0, w, src, ld, nn),
+//   value(v0 + n, k0 + i) = nn ? src[i*ld + n] : src[n*ld + i]  (n < nv, i < w),
+// everything else 0; stored [vcols, RL] (K-contiguous) or, with kmajor,
+// [RL, vcols].  The K-contiguous concatenation [A_0 | A_1 | ...]^T of adapters
+// A_q [K, w] is the kmajor job with vcols = K and part q = (0, K, q*w, w, A_q, w, 0).
+// All jobs of a call run in one launch.
 // ---------------------------------------------------------------------------
 struct PackPart {
   const void* src;
@@ -170,9 +170,11 @@ struct PackLoraArgs {
   int32_t kmajor, pad_;
   PackPart part[6];
 };
-hipError_t launch_pack_lora_b(bool bf16, const PackLoraArgs& a, hipStream_t st);
-hipError_t launch_pack_cat_t(bool bf16, void* out, int64_t K, int Rpad, int w, int nparts,
-                             const void* const* srcs, hipStream_t st);
+struct PackBatchArgs {
+  PackLoraArgs job[6];
+  int32_t njobs;
+};
+hipError_t launch_pack_batch(bool bf16, const PackBatchArgs& b, hipStream_t st);
 hipError_t launch_zero(void* p, int64_t bytes, hipStream_t st);
 
 // fp32 -> bf16 (round to nearest even) of up to six arrays in one launch: the

@@ -390,38 +390,27 @@ __global__ void colproj_f32_kernel(const ColProjArgs a) {
 // ---------------------------------------------------------------------------
 // Packing.
 // ---------------------------------------------------------------------------
+// Every pack job of a call in one launch (blockIdx.y = job).  Threads walk
+// each output in storage order, so the stores are coalesced; the sources
+// (adapters, at most a few MB) are read from L2.
 template <typename E>
-__global__ void pack_lora_b_kernel(const PackLoraArgs a) {
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= a.vcols * a.RL) return;
-  const int64_t v = e / a.RL;
-  const int kk = (int)(e % a.RL);
-  E val = E(0);
-  for (int p = 0; p < a.nparts; ++p) {
-    const PackPart& q = a.part[p];
-    if (v >= q.v0 && v < q.v0 + q.nv && kk >= q.k0 && kk < q.k0 + q.w) {
-      const int64_t n = v - q.v0, i = kk - q.k0;
-      const E* src = static_cast<const E*>(q.src);
-      val = q.nn ? src[i * q.ld + n] : src[n * q.ld + i];
+__global__ void pack_batch_kernel(const PackBatchArgs b) {
+  const PackLoraArgs& a = b.job[blockIdx.y];
+  const int64_t n = a.vcols * a.RL;
+  for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < n; o += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t v = a.kmajor ? o % a.vcols : o / a.RL;
+    const int kk = (int)(a.kmajor ? o / a.vcols : o % a.RL);
+    E val = E(0);
+    for (int p = 0; p < a.nparts; ++p) {
+      const PackPart& q = a.part[p];
+      if (v >= q.v0 && v < q.v0 + q.nv && kk >= q.k0 && kk < q.k0 + q.w) {
+        const int64_t nn = v - q.v0, i = kk - q.k0;
+        const E* src = static_cast<const E*>(q.src);
+        val = q.nn ? src[i * q.ld + nn] : src[nn * q.ld + i];
+      }
     }
+    static_cast<E*>(a.out)[o] = val;
   }
-  const int64_t o = a.kmajor ? (int64_t)kk * a.vcols + v : e;
-  static_cast<E*>(a.out)[o] = val;
-}
-
-struct CatSrcs {
-  const void* s[4];
-};
-
-template <typename E>
-__global__ void pack_cat_t_kernel(E* out, int64_t K, int Rpad, int w, int nparts, CatSrcs srcs) {
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= (int64_t)Rpad * K) return;
-  const int j = (int)(e / K);
-  const int64_t k = e % K;
-  E val = E(0);
-  if (j < nparts * w) val = static_cast<const E*>(srcs.s[j / w])[k * w + (j % w)];
-  out[e] = val;
 }
 
 __global__ void cast_bf16_kernel(const CastArgs a) {
@@ -551,26 +540,13 @@ hipError_t launch_rowcol(bool bf16, const ColProjArgs& c0, const RowProjArgs& r,
   return hipGetLastError();
 }
 
-hipError_t launch_pack_lora_b(bool bf16, const PackLoraArgs& a, hipStream_t st) {
-  const int64_t n = a.vcols * a.RL;
-  if (n == 0) return hipSuccess;
-  if (bf16) hipLaunchKernelGGL(pack_lora_b_kernel<uint16_t>, dim3(nblk(n, 256)), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(pack_lora_b_kernel<float>, dim3(nblk(n, 256)), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_pack_cat_t(bool bf16, void* out, int64_t K, int Rpad, int w, int nparts,
-                             const void* const* srcs, hipStream_t st) {
-  CatSrcs s{};
-  for (int i = 0; i < nparts && i < 4; ++i) s.s[i] = srcs[i];
-  const int64_t n = (int64_t)Rpad * K;
-  if (n == 0) return hipSuccess;
-  if (bf16)
-    hipLaunchKernelGGL(pack_cat_t_kernel<uint16_t>, dim3(nblk(n, 256)), dim3(256), 0, st,
-                       static_cast<uint16_t*>(out), K, Rpad, w, nparts, s);
-  else
-    hipLaunchKernelGGL(pack_cat_t_kernel<float>, dim3(nblk(n, 256)), dim3(256), 0, st,
-                       static_cast<float*>(out), K, Rpad, w, nparts, s);
+hipError_t launch_pack_batch(bool bf16, const PackBatchArgs& b, hipStream_t st) {
+  int64_t nmax = 0;
+  for (int i = 0; i < b.njobs; ++i) nmax = b.job[i].vcols * b.job[i].RL > nmax ? b.job[i].vcols * b.job[i].RL : nmax;
+  if (b.njobs <= 0 || nmax == 0) return hipSuccess;
+  const unsigned bx = nblk(nmax, 256) < 2048 ? nblk(nmax, 256) : 2048u;
+  if (bf16) hipLaunchKernelGGL(pack_batch_kernel<uint16_t>, dim3(bx, (unsigned)b.njobs), dim3(256), 0, st, b);
+  else hipLaunchKernelGGL(pack_batch_kernel<float>, dim3(bx, (unsigned)b.njobs), dim3(256), 0, st, b);
   return hipGetLastError();
 }
 

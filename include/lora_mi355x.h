@@ -78,7 +78,7 @@ typedef enum lora_status {
   LORA_EDTYPE = 3,       /* unknown or mismatched dtype */
   LORA_EALIGN = 4,       /* pointer not aligned as required */
   LORA_EWORKSPACE = 5,   /* ws missing or smaller than the query's size */
-  LORA_EUNSUPPORTED = 6, /* valid but unsupported (NF4 with fp32, aliasing) */
+  LORA_EUNSUPPORTED = 6, /* valid but unsupported (NF4 with fp32, partial aliasing) */
   LORA_EDEVICE = 7       /* HIP runtime reported an error */
 } lora_status;
 
@@ -185,7 +185,9 @@ lora_status lora_mlp_fwd(const lora_mlp_desc* desc, const void* X, const lora_pr
  *   P_u = dg B_u^T, P_g = de B_g^T (each formed once and used twice),
  *   dA_u = s_u X^T P_u, dB_u = s_u U_u^T dg, dA_g = s_g X^T P_g, dB_g = s_g U_g^T de,
  *   dX = dg W_u^T + s_u P_u A_u^T + de W_g^T + s_g P_g A_g^T.
- * Outputs are overwritten (not accumulated).  dX must not alias X. */
+ * Outputs are overwritten (not accumulated).  dX may be X itself
+ * (in place: X is last read by the dA pass, which precedes the dX GEMM); a
+ * partial overlap of dX and X is rejected (LORA_EUNSUPPORTED). */
 lora_status lora_mlp_bwd(const lora_mlp_desc* desc, const void* dY, const void* X,
                          const lora_mlp_saved* saved, const lora_proj* gate,
                          const lora_proj* up, const lora_proj* down, void* dX,
@@ -237,7 +239,9 @@ lora_status lora_relu2_mlp_fwd(const lora_relu2_mlp_desc* desc, const void* X, c
  *   dA_d = s_d h^T P_d, dB_d = s_d U_d^T dY, du = dh * 2 max(u, 0),
  *   P_u = du B_u^T (formed once), dA_u = s_u X^T P_u, dB_u = s_u U_u^T du,
  *   dX = du W_u^T + s_u P_u A_u^T.
- * Outputs are overwritten.  dX must not alias X. */
+ * Outputs are overwritten.  dX may be X itself
+ * (in place: X is last read by the dA pass, which precedes the dX GEMM); a
+ * partial overlap of dX and X is rejected (LORA_EUNSUPPORTED). */
 lora_status lora_relu2_mlp_bwd(const lora_relu2_mlp_desc* desc, const void* dY, const void* X,
                                const lora_relu2_mlp_saved* saved, const lora_proj* up, const lora_proj* down,
                                void* dX, const lora_relu2_mlp_grads* grads, void* ws, size_t ws_bytes,
@@ -275,7 +279,9 @@ lora_status lora_qkv_fwd(const lora_qkv_desc* desc, const void* X, const lora_pr
                          void* U, void* ws, size_t ws_bytes, void* stream);
 
 /* dX = sum over p in {q,k,v} of (dZ_p W_p^T + s_p P_p A_p^T) with P_p = dZ_p B_p^T
- * formed once; dA_p = s_p X^T P_p; dB_p = s_p U_p^T dZ_p.  dX must not alias X. */
+ * formed once; dA_p = s_p X^T P_p; dB_p = s_p U_p^T dZ_p.  dX may be X itself
+ * (in place: X is last read by the dA pass, which precedes the dX GEMM); a
+ * partial overlap of dX and X is rejected (LORA_EUNSUPPORTED). */
 lora_status lora_qkv_bwd(const lora_qkv_desc* desc, const void* dQ, const void* dK,
                          const void* dV, const void* X, const void* U, const lora_proj* q,
                          const lora_proj* k, const lora_proj* v, void* dX,
@@ -302,7 +308,8 @@ lora_status lora_o_workspace_size(const lora_o_desc* desc, size_t* fwd_bytes,
 lora_status lora_o_fwd(const lora_o_desc* desc, const void* X, const lora_proj* o, void* Y,
                        void* U, void* ws, size_t ws_bytes, void* stream);
 
-/* P = dY B^T (once); dX = dY W^T + s P A^T; dA = s X^T P; dB = s U^T dY. */
+/* P = dY B^T (once); dX = dY W^T + s P A^T; dA = s X^T P; dB = s U^T dY.
+ * dX may be X itself (in place); a partial overlap is rejected. */
 lora_status lora_o_bwd(const lora_o_desc* desc, const void* dY, const void* X, const void* U,
                        const lora_proj* o, void* dX, void* dA, void* dB, void* ws,
                        size_t ws_bytes, void* stream);

@@ -471,7 +471,87 @@ def test_errors_enqueue_nothing(lm):
     with pytest.raises(lm.LoraError) as ei:
         lm.o_fwd(X, p, ws=torch.empty(1, dtype=torch.uint8, device="cuda:0"))
     assert ei.value.status == 5  # LORA_EWORKSPACE
+    # dX may be X itself (in place) but not a partly overlapping view of it
+    buf = torch.zeros(65 * 256, dtype=torch.bfloat16, device="cuda:0")
+    Xv, dXv = buf[:64 * 256].view(64, 256), buf[256:].view(64, 256)
     with pytest.raises(lm.LoraError) as ei:
-        lm.o_bwd(torch.zeros((64, 320), dtype=torch.bfloat16, device="cuda:0"), X,
-                 torch.zeros((64, 16), dtype=torch.bfloat16, device="cuda:0"), p, dX=X)
-    assert ei.value.status == 6  # LORA_EUNSUPPORTED (dX aliases X)
+        lm.o_bwd(torch.zeros((64, 320), dtype=torch.bfloat16, device="cuda:0"), Xv,
+                 torch.zeros((64, 16), dtype=torch.bfloat16, device="cuda:0"), p, dX=dXv)
+    assert ei.value.status == 6  # LORA_EUNSUPPORTED (dX partly overlaps X)
+
+
+# ---------------------------------------------------------------------------
+# In-place dX: every backward may write dX over X ("LoRA Optimizations",
+# "Custom autograd functions"; the unsloth backward hunks write dX into X's
+# storage once dA = s X^T P has been formed).  The result must equal the
+# out-of-place call bit for bit: same kernels, same order, and X is last read
+# by the dA pass, which precedes the dX GEMM.
+# ---------------------------------------------------------------------------
+
+def _grads_equal(a, b):
+    import torch
+
+    assert a.keys() == b.keys()
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_inplace_dx_mlp(lm, dt):
+    import torch
+
+    cfg = WorkloadConfig(95, "mlp", T=300, H=512, I=640, r=16, alpha=32, dtype=dt, act="swiglu")
+    inp = make_mlp_inputs(cfg)
+    X, dY = dev(inp["X"], dt), dev(inp["dY"], dt)
+    g, u, d = (proj_dev(inp[k], dt) for k in ("gate", "up", "down"))
+    Y, saved = lm.mlp_fwd(X, g, u, d)
+    dX, grads = lm.mlp_bwd(dY, X, saved, g, u, d)
+    Xi = X.clone()
+    dXi, gi = lm.mlp_bwd(dY, Xi, saved, g, u, d, dX=Xi)
+    torch.cuda.synchronize()
+    assert dXi.data_ptr() == Xi.data_ptr()
+    assert torch.equal(Xi, dX)
+    _grads_equal(grads, gi)
+
+
+def test_inplace_dx_relu2_mlp(lm):
+    import torch
+
+    cfg = WorkloadConfig(96, "relu2", T=300, H=512, I=640, r=16, alpha=32, dtype="bf16")
+    inp = make_relu2_inputs(cfg)
+    X, dY = dev(inp["X"], "bf16"), dev(inp["dY"], "bf16")
+    up, down = (proj_dev(inp[k], "bf16") for k in ("up", "down"))
+    Y, saved = lm.relu2_mlp_fwd(X, up, down)
+    dX, grads = lm.relu2_mlp_bwd(dY, X, saved, up, down)
+    Xi = X.clone()
+    _, gi = lm.relu2_mlp_bwd(dY, Xi, saved, up, down, dX=Xi)
+    torch.cuda.synchronize()
+    assert torch.equal(Xi, dX)
+    _grads_equal(grads, gi)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_inplace_dx_qkv_o(lm, dt):
+    import torch
+
+    cfg = WorkloadConfig(97, "attn", T=300, H=512, r=16, alpha=32, dtype=dt, Nq=512, Nk=192, Nv=128)
+    inp = make_attn_inputs(cfg)
+    X = dev(inp["X"], dt)
+    q, k, v = (proj_dev(inp[n], dt) for n in ("q", "k", "v"))
+    Q, K, V, U = lm.qkv_fwd(X, q, k, v)
+    dQ, dK, dV = (dev(inp[n], dt) for n in ("dQ", "dK", "dV"))
+    dX, grads = lm.qkv_bwd(dQ, dK, dV, X, U, q, k, v)
+    Xi = X.clone()
+    _, gi = lm.qkv_bwd(dQ, dK, dV, Xi, U, q, k, v, dX=Xi)
+    Xo = dev(inp["Xo"], dt)
+    o = proj_dev(inp["o"], dt)
+    Yo, Uo = lm.o_fwd(Xo, o)
+    dO = dev(inp["dO"], dt)
+    dXo, dAo, dBo = lm.o_bwd(dO, Xo, Uo, o)
+    Xoi = Xo.clone()
+    _, dAoi, dBoi = lm.o_bwd(dO, Xoi, Uo, o, dX=Xoi)
+    torch.cuda.synchronize()
+    assert torch.equal(Xi, dX)
+    _grads_equal(grads, gi)
+    assert torch.equal(Xoi, dXo)
+    assert torch.equal(dAoi, dAo) and torch.equal(dBoi, dBo)
