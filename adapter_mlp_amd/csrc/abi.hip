@@ -176,7 +176,37 @@ const void* coff(const void* p, int64_t elems, const Ctx& c) {
 }
 void* offw(void* p, int64_t elems, const Ctx& c) { return static_cast<char*>(p) + elems * (int64_t)c.es; }
 
-hipError_t gemm_on(const Ctx& c, GemmArgs& g, hipStream_t st, int64_t lora_vcols) {
+// Split-K factor of a bf16 store GEMM [M, N] over K (LoRA tile included): the
+// s in 1..4 that best fills the last wave of 256x256 tiles on the 256 CUs,
+// weighed against the fp32 partials it writes and reads (8 s bytes per
+// output element, about 1040 s / K of the GEMM's time at the measured GEMM
+// and HBM rates).  Each part keeps at least 16 K steps of 64.
+int gemm_ksplit(const Ctx& c, int64_t M, int64_t N, int64_t K) {
+  if (!c.bf16) return 1;
+  const int64_t tiles = cdiv(M, 256) * cdiv(N, 256);
+  if (tiles == 0) return 1;
+  double best = 0.0;
+  int bs = 1;
+  for (int s = 1; s <= 4; ++s) {
+    if (s > 1 && K / 64 / s < 16) break;
+    const int64_t units = tiles * s;
+    const double fill = (double)units / (double)(cdiv(units, 256) * 256);
+    const double score = fill / (s > 1 ? 1.0 + 1040.0 * s / (double)K : 1.0);
+    if (score > best * 1.02) {
+      best = score;
+      bs = s;
+    }
+  }
+  return bs;
+}
+// fp32 partial floats a split store GEMM needs (0 without a split)
+int64_t kpart_floats(const Ctx& c, int64_t M, int64_t N, int64_t K) {
+  const int s = gemm_ksplit(c, M, N, K);
+  return s > 1 ? s * M * N : 0;
+}
+
+// kpart: fp32 scratch of kpart_floats() for a split store GEMM (nullptr: no split)
+hipError_t gemm_on(const Ctx& c, GemmArgs& g, hipStream_t st, int64_t lora_vcols, float* kpart = nullptr) {
   g.lora_vcols = lora_vcols;
   if (c.bf16 && g.RL > 0) {
     // The bf16 kernel runs the LoRA term as one more 64-wide K segment:
@@ -212,6 +242,16 @@ hipError_t gemm_on(const Ctx& c, GemmArgs& g, hipStream_t st, int64_t lora_vcols
     tiles += cdiv(g.reg[p].N, cols);
   }
   g.ntile_n = tiles;
+  g.ksplit = 1;
+  if (kpart != nullptr && c.bf16 && !g.nf4 && g.epi == EPI_STORE && g.nreg == 1) {
+    int64_t K = 0;
+    for (int s = 0; s < g.nseg; ++s) K += g.seg[s].K;
+    const int ks = gemm_ksplit(c, g.M, g.reg[0].N, K);
+    if (ks > 1) {
+      g.ksplit = ks;
+      g.kpart = kpart;
+    }
+  }
   char name[48];
   std::snprintf(name, sizeof name, "gemm_%s_%s%s%s", g.bkind == B_NN ? "nn" : "nt",
                 g.epi == EPI_STORE      ? "store"
@@ -221,7 +261,10 @@ hipError_t gemm_on(const Ctx& c, GemmArgs& g, hipStream_t st, int64_t lora_vcols
                                         : "relu2_bwd",
                 g.nf4 ? "_nf4" : "", c.bf16 ? "" : "_f32");
   TraceScope ts(name, st);
-  return c.bf16 ? launch_gemm_bf16(g, st) : launch_gemm_f32(g, st);
+  if (!c.bf16) return launch_gemm_f32(g, st);
+  const hipError_t e = launch_gemm_bf16(g, st);
+  if (e != hipSuccess || g.ksplit <= 1) return e;
+  return launch_ksplit_reduce(g.kpart, g.ksplit, g.M, g.reg[0].N, g.reg[0].out, g.reg[0].ldo, st);
 }
 
 RowProjArgs rowproj_args(const void* Z, int64_t ldz, int64_t T, int64_t K, const void* Bt, int64_t ldb,
@@ -355,6 +398,7 @@ int64_t fused_da_floats(int64_t T, int64_t I) { return cdiv(T, gemm_tile_rows(tr
 struct MlpPlan {
   void *ad_f, *ad_b;  // adapter casts (fp32 LoRA-gradient mode), fwd / bwd workspace
   void *At_gu, *Us_gu, *BLt_gu, *h, *At_d, *Us_d, *BLt_d;                  // forward
+  float* kpart;                                                             // down GEMM split-K
   void *Ps_d, *BLt_dh, *hb, *dg, *de, *Ps_ug, *BLt_dx;                      // backward
   float* partial;
   float* rpartial;  // rowproj partials of the fused dY / dg / de passes
@@ -375,6 +419,7 @@ MlpPlan plan_mlp(const Ctx& c, const lora_mlp_desc& d, void* ws_fwd, void* ws_bw
   p.At_d = f.take(r * I * c.es);
   p.Us_d = f.take(T * RLd * c.es);
   p.BLt_d = f.take(H * RLd * c.es);
+  p.kpart = static_cast<float*>(f.take((size_t)kpart_floats(c, T, H, I + RLd) * 4));
   p.fwd_bytes = f.off;
   Ws b(ws_bwd);
   p.ad_b = b.take(staged_bytes(c, ad, 3, r));
@@ -391,6 +436,8 @@ MlpPlan plan_mlp(const Ctx& c, const lora_mlp_desc& d, void* ws_fwd, void* ws_bw
                               colproj_partial_floats(T, H, (int)(2 * r)), 0};
     for (int i = 0; i < 3; ++i) pf = cands[i] > pf ? cands[i] : pf;
     if (fuse_da(c, r) && fused_da_floats(T, I) > pf) pf = fused_da_floats(T, I);
+    // the dX GEMM's split-K partials (the partial buffer is free by then)
+    if (kpart_floats(c, T, H, 2 * I + RLg) > pf) pf = kpart_floats(c, T, H, 2 * I + RLg);
   }
   p.partial = static_cast<float*>(b.take((size_t)pf * 4));
   p.rpartial = c.bf16 ? static_cast<float*>(b.take((size_t)rowcol_partial_floats(T, I > H ? I : H) * 4)) : nullptr;
@@ -418,6 +465,7 @@ lora_status validate_mlp(const lora_mlp_desc* d, Ctx& c) {
 struct Relu2Plan {
   void *ad_f, *ad_b;                                          // adapter casts (fp32 LoRA-gradient mode)
   void *At_u, *Us_u, *BLt_u, *h, *At_d, *Us_d, *BLt_d;        // forward
+  float* kpart;                                               // down GEMM split-K
   void *Ps_d, *BLt_dh, *hb, *du, *Ps_u, *BLt_dx;              // backward
   float* partial;
   float* rpartial;  // rowproj partials of the fused dY / du passes
@@ -438,6 +486,7 @@ Relu2Plan plan_relu2(const Ctx& c, const lora_relu2_mlp_desc& d, void* ws_fwd, v
   p.At_d = f.take(r * I * c.es);
   p.Us_d = f.take(T * RL * c.es);
   p.BLt_d = f.take(H * RL * c.es);
+  p.kpart = static_cast<float*>(f.take((size_t)kpart_floats(c, T, H, I + RL) * 4));
   p.fwd_bytes = f.off;
   Ws b(ws_bwd);
   p.ad_b = b.take(staged_bytes(c, ad, 2, r));
@@ -452,6 +501,7 @@ Relu2Plan plan_relu2(const Ctx& c, const lora_relu2_mlp_desc& d, void* ws_fwd, v
     const int64_t a = colproj_partial_floats(T, H, (int)r), bb = colproj_partial_floats(T, I, (int)r);
     pf = a > bb ? a : bb;
     if (fuse_da(c, r) && fused_da_floats(T, I) > pf) pf = fused_da_floats(T, I);
+    if (kpart_floats(c, T, H, I + RL) > pf) pf = kpart_floats(c, T, H, I + RL);  // dX split-K
   }
   p.partial = static_cast<float*>(b.take((size_t)pf * 4));
   p.rpartial = c.bf16 ? static_cast<float*>(b.take((size_t)rowcol_partial_floats(T, I > H ? I : H) * 4)) : nullptr;
@@ -504,6 +554,7 @@ QkvPlan plan_qkv(const Ctx& c, const lora_qkv_desc& d, void* wf, void* wb) {
     const int64_t cand[4] = {colproj_partial_floats(T, d.Nq, (int)r), colproj_partial_floats(T, d.Nk, (int)r),
                              colproj_partial_floats(T, d.Nv, (int)r), colproj_partial_floats(T, H, (int)(3 * r))};
     for (int i = 0; i < 4; ++i) pf = cand[i] > pf ? cand[i] : pf;
+    if (kpart_floats(c, T, H, N + RL) > pf) pf = kpart_floats(c, T, H, N + RL);  // dX split-K
   }
   p.partial = static_cast<float*>(b.take((size_t)pf * 4));
   int64_t nmax = d.Nq > d.Nk ? d.Nq : d.Nk;
@@ -532,6 +583,7 @@ lora_status validate_qkv(const lora_qkv_desc* d, Ctx& c) {
 struct OPlan {
   void *ad_f, *ad_b;  // adapter casts (fp32 LoRA-gradient mode)
   void *At, *Us, *BLt, *U_tmp;
+  float* kpart;  // forward GEMM split-K
   void *Ps, *BLt_dx;
   float* partial;
   float* rpartial;  // rowproj partials of the fused dY pass
@@ -549,6 +601,7 @@ OPlan plan_o(const Ctx& c, int64_t T, int64_t K, int64_t N, int64_t r, bool tmp_
   p.Us = f.take(T * RL * c.es);
   p.BLt = f.take(N * RL * c.es);
   p.U_tmp = tmp_u ? f.take(T * r * c.es) : nullptr;
+  p.kpart = static_cast<float*>(f.take((size_t)kpart_floats(c, T, N, K + (r > 0 ? RL : 0)) * 4));
   p.fwd_bytes = f.off;
   Ws b(wb);
   p.ad_b = b.take(staged_bytes(c, ad, 1, r));
@@ -558,6 +611,8 @@ OPlan plan_o(const Ctx& c, int64_t T, int64_t K, int64_t N, int64_t r, bool tmp_
   if (c.bf16) {
     const int64_t a = colproj_partial_floats(T, N, (int)r), bb = colproj_partial_floats(T, K, (int)r);
     pf = a > bb ? a : bb;
+    const int64_t kp = kpart_floats(c, T, K, N + (r > 0 ? RL : 0));  // input-gradient GEMM split-K
+    pf = kp > pf ? kp : pf;
   }
   p.partial = static_cast<float*>(b.take((size_t)pf * 4));
   p.rpartial = c.bf16 ? static_cast<float*>(b.take((size_t)rowcol_partial_floats(T, N) * 4)) : nullptr;
@@ -624,7 +679,7 @@ lora_status proj_forward(const Ctx& c, int64_t T, int64_t K, int64_t N, int64_t 
   g.reg[0].N = N;
   g.reg[0].out = Y;
   g.reg[0].ldo = N;
-  LAUNCH(gemm_on(c, g, st, N));
+  LAUNCH(gemm_on(c, g, st, N, p.kpart));
   return LORA_OK;
 }
 
@@ -664,7 +719,7 @@ lora_status proj_input_grad(const Ctx& c, int64_t T, int64_t K, int64_t N, int64
   g.reg[0].N = K;
   g.reg[0].out = dX;
   g.reg[0].ldo = K;
-  LAUNCH(gemm_on(c, g, st, K));
+  LAUNCH(gemm_on(c, g, st, K, p.partial));
   return LORA_OK;
 }
 
@@ -827,7 +882,7 @@ lora_status lora_mlp_fwd(const lora_mlp_desc* d, const void* X, const lora_proj*
   gd.RL = (int)RLd;
   gd.BLt = p.BLt_d;
   gd.ldbl = RLd;
-  LAUNCH(gemm_on(c, gd, st, H));
+  LAUNCH(gemm_on(c, gd, st, H, p.kpart));
   return LORA_OK;
 }
 
@@ -996,7 +1051,7 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, 
   gx.RL = (int)RLg;
   gx.BLt = p.BLt_dx;
   gx.ldbl = RLg;
-  if (T > 0) LAUNCH(gemm_on(c, gx, st, H));
+  if (T > 0) LAUNCH(gemm_on(c, gx, st, H, p.partial));
   return LORA_OK;
 }
 
@@ -1122,7 +1177,7 @@ lora_status lora_relu2_mlp_fwd(const lora_relu2_mlp_desc* d, const void* X, cons
   gd.RL = (int)RL;
   gd.BLt = p.BLt_d;
   gd.ldbl = RL;
-  LAUNCH(gemm_on(c, gd, st, H));
+  LAUNCH(gemm_on(c, gd, st, H, p.kpart));
   return LORA_OK;
 }
 
@@ -1267,7 +1322,7 @@ lora_status lora_relu2_mlp_bwd(const lora_relu2_mlp_desc* d, const void* dY, con
   gx.RL = (int)RL;
   gx.BLt = p.BLt_dx;
   gx.ldbl = RL;
-  if (T > 0) LAUNCH(gemm_on(c, gx, st, H));
+  if (T > 0) LAUNCH(gemm_on(c, gx, st, H, p.partial));
   return LORA_OK;
 }
 
@@ -1465,7 +1520,7 @@ lora_status lora_qkv_bwd(const lora_qkv_desc* d, const void* dQ, const void* dK,
   g.RL = (int)RL;
   g.BLt = p.BLt_dx;
   g.ldbl = RL;
-  LAUNCH(gemm_on(c, g, st, H));
+  LAUNCH(gemm_on(c, g, st, H, p.partial));
   return LORA_OK;
 }
 

@@ -99,7 +99,7 @@ __device__ __forceinline__ void for4(F&& f) {
 // Staging bytes one wavefront needs for a WN-column epilogue.
 template <int WN, int EPI>
 constexpr int epi_stage_bytes() {
-  return EPI == EPI_STORE      ? 32 * (WN + 8) * 2
+  return EPI == EPI_STORE      ? 32 * (WN + 4) * 4
          : EPI == EPI_ACT_FWD  ? 3 * 32 * (WN / 2 + 8) * 2
          : EPI == EPI_ACT1_FWD ? 2 * 32 * (WN + 8) * 2
                                : 32 * (WN + 4) * 4 + 32 * (WN + 8) * 2 + 32 * 16 * 2;
@@ -108,9 +108,39 @@ constexpr int epi_stage_bytes() {
 template <int WN, bool DUAL, int EPI>
 __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* wstage, const GemmArgs& args,
                                                int reg, int64_t mw, int64_t nbase, int64_t NR, int64_t M,
-                                               int lane, int wm) {
+                                               int lane, int wm, int kp) {
   constexpr int NI = WN / 32;
   if constexpr (EPI == EPI_STORE) {
+    if (args.ksplit > 1) {
+      // split-K part: fp32 sums through a [32][WN] fp32 staging, 16-byte stores
+      constexpr int LD = WN + 4;
+      constexpr int CPR = WN / 4;          // 4-float chunks per row
+      constexpr int RPP = 64 / CPR;
+      float* stg = reinterpret_cast<float*>(wstage);
+      float* out = args.kpart + (int64_t)kp * M * NR;
+      for4([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int col = i * 32 + 8 * g + 4 * (lane >> 5);
+            *reinterpret_cast<f32x4*>(stg + (lane & 31) * LD + col) =
+                f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          }
+        wave_sync();
+#pragma unroll
+        for (int it = 0; it < 32 / RPP; ++it) {
+          const int row = it * RPP + lane / CPR, c4 = lane % CPR;
+          const f32x4 v = *reinterpret_cast<const f32x4*>(stg + row * LD + c4 * 4);
+          const int64_t m = mw + j * 32 + row;
+          const int64_t n = nbase + c4 * 4;
+          if (m < M && n < NR) *reinterpret_cast<f32x4*>(out + m * NR + n) = v;
+        }
+        wave_sync();
+      });
+      return;
+    }
     constexpr int LD = WN + 8;           // bf16 staging [32][WN], padded rows
     constexpr int CPR = WN / 8;          // 16-byte chunks per row
     constexpr int RPP = 64 / CPR;        // rows per pass
@@ -475,7 +505,10 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   const int wm = wave >> 2, wn = wave & 3;                    // wm: the group
 
   int tm, tn;
-  tile_coords((int)blockIdx.x, (int)gridDim.x, (int)args.ntile_m, (int)args.ntile_n, tm, tn);
+  // split-K: block u works on K part u / ntiles of tile u % ntiles
+  const int ntiles = (int)(args.ntile_m * args.ntile_n);
+  const int kp = args.ksplit > 1 ? (int)blockIdx.x / ntiles : 0;
+  tile_coords((int)blockIdx.x - kp * ntiles, ntiles, (int)args.ntile_m, (int)args.ntile_n, tm, tn);
   tm = __builtin_amdgcn_readfirstlane(tm);
   tn = __builtin_amdgcn_readfirstlane(tn);
   int reg = 0;
@@ -497,6 +530,13 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
       KN += k;
       ++nseg_nf4;
     }
+  }
+  // this block's K steps [k_begin, k_begin + KT) (dense split-K only)
+  int k_begin = 0;
+  if (!NF4 && args.ksplit > 1) {
+    const int kall = KT;
+    k_begin = (int)((int64_t)kp * kall / args.ksplit);
+    KT = (int)((int64_t)(kp + 1) * kall / args.ksplit) - k_begin;
   }
 
   // ---- loads: 8 blocks of 1 KB per wavefront and step ----
@@ -557,6 +597,19 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
     }
   };
   cur_begin();
+  // skip to this block's first K step (split-K)
+  for (int sk = k_begin; sk > 0;) {
+    const int n = sk < lsteps ? sk : lsteps;
+    lp += n * lstep;
+    ln -= n * lstep;
+    lk0 += n * BK;
+    lsteps -= n;
+    sk -= n;
+    if (lsteps == 0 && lseg + 1 < args.nseg) {
+      ++lseg;
+      cur_begin();
+    }
+  }
   auto advance = [&]() {
     lp += lstep;
     ln -= lstep;
@@ -919,12 +972,25 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   char* const wstage = smem_raw + wave * EB;
   const int64_t mw = m0 + wm * 128;
   const int64_t nbase = DUAL ? tnl * 128 + wn * 32 : tnl * 256 + wn * 64;
-  run_epilogue_w<64, DUAL, EPI>(acc, wstage, args, reg, mw, nbase, NR, M, lane, wm);
+  run_epilogue_w<64, DUAL, EPI>(acc, wstage, args, reg, mw, nbase, NR, M, lane, wm, kp);
+}
+
+__global__ void ksplit_reduce_kernel(const float* part, int ks, int64_t M, int64_t N, uint16_t* out, int64_t ldo) {
+  const int64_t e = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (e >= M * N) return;
+  const int64_t m = e / N, n = e % N;
+  f32x4 a = *reinterpret_cast<const f32x4*>(part + e), b = *reinterpret_cast<const f32x4*>(part + e + 4);
+  for (int k = 1; k < ks; ++k) {
+    a += *reinterpret_cast<const f32x4*>(part + (int64_t)k * M * N + e);
+    b += *reinterpret_cast<const f32x4*>(part + (int64_t)k * M * N + e + 4);
+  }
+  const u32x4 v = {pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]), pack_bf2(b[0], b[1]), pack_bf2(b[2], b[3])};
+  *reinterpret_cast<u32x4*>(out + m * ldo + n) = v;
 }
 
 template <int BKIND, bool DUAL, int EPI, bool NF4>
 hipError_t launch(const GemmArgs& a, hipStream_t st) {
-  const int64_t nb = a.ntile_m * a.ntile_n;
+  const int64_t nb = a.ntile_m * a.ntile_n * (a.ksplit > 1 && !NF4 ? a.ksplit : 1);
   if (nb == 0) return hipSuccess;
   hipLaunchKernelGGL((gemm_kernel<BKIND, DUAL, EPI, NF4>), dim3((unsigned)nb), dim3(NTH8), 0, st, a);
   return hipGetLastError();
@@ -949,6 +1015,15 @@ int64_t gemm_tile_cols(bool bf16, bool dual) {
   return dual ? 32 : 64;
 }
 int64_t gemm_tile_rows(bool bf16) { return bf16 ? 256 : 64; }
+
+hipError_t launch_ksplit_reduce(const float* part, int ks, int64_t M, int64_t N, void* out, int64_t ldo,
+                                hipStream_t st) {
+  const int64_t n8 = M * N / 8;
+  if (n8 == 0) return hipSuccess;
+  hipLaunchKernelGGL(ksplit_reduce_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, part, ks, M, N,
+                     static_cast<uint16_t*>(out), ldo);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   return a.nf4 ? launch_family<true>(a, st) : launch_family<false>(a, st);

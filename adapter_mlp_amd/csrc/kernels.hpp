@@ -83,12 +83,21 @@ struct GemmArgs {
   float* dA_part;
   const void* pd;
   int64_t ldpd;
+  // EPI_STORE, bf16, dense, one region: split-K.  Block u works on K part
+  // u / (ntile_m * ntile_n) (parts split the K steps evenly, in order) and
+  // writes its fp32 sums to kpart [ksplit, M, N]; launch_ksplit_reduce adds
+  // the parts in ascending order and stores bf16.  ksplit <= 1: no split.
+  int32_t ksplit, pad3_;
+  float* kpart;
 };
 
 // Columns of output covered by one n-tile.
 int64_t gemm_tile_cols(bool bf16, bool dual);
 int64_t gemm_tile_rows(bool bf16);
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st);
+// out[m, n] (bf16, row pitch ldo) = sum over k < ks, ascending, of part[k][m][n] ([ks, M, N] fp32)
+hipError_t launch_ksplit_reduce(const float* part, int ks, int64_t M, int64_t N, void* out, int64_t ldo,
+                                hipStream_t st);
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t st);
 
 // ---------------------------------------------------------------------------
