@@ -365,14 +365,34 @@ __device__ __forceinline__ void colproj_store(const ColProjArgs& a, bool bf16, i
   else static_cast<float*>(a.dest[q])[idx] = o;
 }
 
+// dest = scales * (sum over the a.nchunk slices of partial [nchunk, K, Rp]),
+// slices added in ascending order.  One thread per 4 consecutive columns j
+// of one k (R is a multiple of 4 in the bf16 path; the 4 never straddle two
+// adapters since seg_w is a multiple of 8): 16-byte loads, consecutive
+// threads on consecutive addresses.
 __global__ void colproj_reduce_kernel(const ColProjArgs a, int Rp) {
+  const int RQ = a.R / 4;
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= a.K * a.R) return;
-  const int64_t k = e / a.R;
-  const int j = (int)(e % a.R);
-  float v = 0.0f;
-  for (int c = 0; c < a.nchunk; ++c) v += a.partial[(c * a.K + k) * Rp + j];
-  colproj_store(a, a.out_f32 == 0, k, j, v);
+  if (e >= a.K * RQ) return;
+  const int64_t k = e / RQ;
+  const int j0 = (int)(e % RQ) * 4;
+  const float* src = a.partial + k * Rp + j0;
+  const int64_t cstride = a.K * Rp;
+  f32x4 v = f32x4{0, 0, 0, 0};
+  int c = 0;
+  for (; c + 4 <= a.nchunk; c += 4) {
+    const f32x4 p0 = *reinterpret_cast<const f32x4*>(src + (c + 0) * cstride);
+    const f32x4 p1 = *reinterpret_cast<const f32x4*>(src + (c + 1) * cstride);
+    const f32x4 p2 = *reinterpret_cast<const f32x4*>(src + (c + 2) * cstride);
+    const f32x4 p3 = *reinterpret_cast<const f32x4*>(src + (c + 3) * cstride);
+    v += p0;
+    v += p1;
+    v += p2;
+    v += p3;
+  }
+  for (; c < a.nchunk; ++c) v += *reinterpret_cast<const f32x4*>(src + c * cstride);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) colproj_store(a, a.out_f32 == 0, k, j0 + q, v[q]);
 }
 
 __global__ void colproj_f32_kernel(const ColProjArgs a) {
@@ -461,7 +481,7 @@ hipError_t launch_rowproj(bool bf16, const RowProjArgs& a, hipStream_t st) {
 
 hipError_t launch_colproj_reduce(const ColProjArgs& a, hipStream_t st) {
   if (a.K * a.R == 0) return hipSuccess;
-  hipLaunchKernelGGL(colproj_reduce_kernel, dim3(nblk(a.K * a.R, 256)), dim3(256), 0, st, a, 16);
+  hipLaunchKernelGGL(colproj_reduce_kernel, dim3(nblk(a.K * (a.R / 4), 256)), dim3(256), 0, st, a, 16);
   return hipGetLastError();
 }
 
@@ -493,27 +513,51 @@ hipError_t launch_colproj(bool bf16, const ColProjArgs& a0, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(colproj_reduce_kernel, dim3(nblk(a.K * a.R, 256)), dim3(256), 0, st, a, NJ * 16);
+  hipLaunchKernelGGL(colproj_reduce_kernel, dim3(nblk(a.K * (a.R / 4), 256)), dim3(256), 0, st, a, NJ * 16);
   return hipGetLastError();
 }
 
 namespace {
-// Out[t, j] of a fused rowproj: the column blocks' partials summed in
-// ascending block order, then written as the rowproj kernel writes it.
+// Out[t, j] of a fused rowproj: the column blocks' partials [nb, T, 16]
+// summed in ascending block order, then written as the rowproj kernel writes
+// it.  One thread per 4 consecutive j (< 16) of one row t: 16-byte loads;
+// the threads of quad 0 also write the zero padding of out2 past 16.
 __global__ void rowproj_reduce_kernel(const RowProjArgs a, const float* rpartial, int nb) {
   const int R2 = a.R2 > a.R ? a.R2 : a.R;
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= a.T * R2) return;
-  const int64_t t = e / R2;
-  const int j = (int)(e % R2);
-  float v = 0.0f;
-  if (j < a.R)
-    for (int b = 0; b < nb; ++b) v += rpartial[((int64_t)b * a.T + t) * 16 + j];
-  if (a.out1 && j < a.R) static_cast<uint16_t*>(a.out1)[t * a.ld1 + a.off1 + j] = (uint16_t)f2bf(v);
-  if (a.out2) {
-    const float sc = j < a.R ? a.scales[j / a.seg_w] : 0.0f;
-    static_cast<uint16_t*>(a.out2)[t * a.ld2 + j] = (uint16_t)f2bf(sc * v);
+  if (e >= a.T * 4) return;
+  const int64_t t = e >> 2;
+  const int j0 = (int)(e & 3) * 4;
+  f32x4 v = f32x4{0, 0, 0, 0};
+  if (j0 < a.R) {
+    const float* src = rpartial + t * 16 + j0;
+    const int64_t bstride = a.T * 16;
+    int b = 0;
+    for (; b + 4 <= nb; b += 4) {
+      const f32x4 p0 = *reinterpret_cast<const f32x4*>(src + (b + 0) * bstride);
+      const f32x4 p1 = *reinterpret_cast<const f32x4*>(src + (b + 1) * bstride);
+      const f32x4 p2 = *reinterpret_cast<const f32x4*>(src + (b + 2) * bstride);
+      const f32x4 p3 = *reinterpret_cast<const f32x4*>(src + (b + 3) * bstride);
+      v += p0;
+      v += p1;
+      v += p2;
+      v += p3;
+    }
+    for (; b < nb; ++b) v += *reinterpret_cast<const f32x4*>(src + b * bstride);
   }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int j = j0 + q;
+    if (j >= R2) break;
+    const float x = j < a.R ? v[q] : 0.0f;
+    if (a.out1 && j < a.R) static_cast<uint16_t*>(a.out1)[t * a.ld1 + a.off1 + j] = (uint16_t)f2bf(x);
+    if (a.out2) {
+      const float sc = j < a.R ? a.scales[j / a.seg_w] : 0.0f;
+      static_cast<uint16_t*>(a.out2)[t * a.ld2 + j] = (uint16_t)f2bf(sc * x);
+    }
+  }
+  if (a.out2 && j0 == 0)
+    for (int j = 16; j < R2; ++j) static_cast<uint16_t*>(a.out2)[t * a.ld2 + j] = 0;
 }
 }  // namespace
 
@@ -535,7 +579,8 @@ hipError_t launch_rowcol(bool bf16, const ColProjArgs& c0, const RowProjArgs& r,
   hipError_t e = launch_colproj(true, c, st);
   if (e != hipSuccess) return e;
   const int R2 = r.R2 > r.R ? r.R2 : r.R;
-  hipLaunchKernelGGL(rowproj_reduce_kernel, dim3(nblk(r.T * R2, 256)), dim3(256), 0, st, r, rpartial,
+  (void)R2;
+  hipLaunchKernelGGL(rowproj_reduce_kernel, dim3(nblk(r.T * 4, 256)), dim3(256), 0, st, r, rpartial,
                      (int)((r.K + 255) / 256));
   return hipGetLastError();
 }
