@@ -399,6 +399,7 @@ struct MlpPlan {
   void *ad_f, *ad_b;  // adapter casts (fp32 LoRA-gradient mode), fwd / bwd workspace
   void *At_gu, *Us_gu, *BLt_gu, *h, *At_d, *Us_d, *BLt_d;                  // forward
   float* kpart;                                                             // down GEMM split-K
+  float* upart;  // h A_d partials of the gate/up epilogue [I/128, T, 16] (fused, bf16, r <= 16)
   void *Ps_d, *BLt_dh, *hb, *dg, *de, *Ps_ug, *BLt_dx;                      // backward
   float* partial;
   float* rpartial;  // rowproj partials of the fused dY / dg / de passes
@@ -420,6 +421,8 @@ MlpPlan plan_mlp(const Ctx& c, const lora_mlp_desc& d, void* ws_fwd, void* ws_bw
   p.Us_d = f.take(T * RLd * c.es);
   p.BLt_d = f.take(H * RLd * c.es);
   p.kpart = static_cast<float*>(f.take((size_t)kpart_floats(c, T, H, I + RLd) * 4));
+  p.upart = fuse_da(c, r) ? static_cast<float*>(f.take((size_t)(cdiv(I, gemm_tile_cols(true, true)) * T * 16 * 4)))
+                          : nullptr;
   p.fwd_bytes = f.off;
   Ws b(ws_bwd);
   p.ad_b = b.take(staged_bytes(c, ad, 3, r));
@@ -851,6 +854,13 @@ lora_status lora_mlp_fwd(const lora_mlp_desc* d, const void* X, const lora_proj*
   g.g_out = saved->g;
   g.h_out = p.h;
   g.ld_act = I;
+  const bool fu = fuse_da(c, r);  // U_d = h A_d formed in the gate/up epilogue
+  if (fu) {
+    g.u_part = p.upart;
+    g.ad_t = p.At_d;
+    g.ld_adt = I;
+    g.u_R = (int)r;
+  }
   LAUNCH(gemm_on(c, g, st, 2 * I));
 
   // U_d = h A_d, then the down GEMM
@@ -861,7 +871,11 @@ lora_status lora_mlp_fwd(const lora_mlp_desc* d, const void* X, const lora_proj*
   rd.off1 = 2 * r;
   rd.out2 = p.Us_d;
   rd.ld2 = RLd;
-  LAUNCHN("rowproj", st, launch_rowproj(c.bf16, rd, st));
+  if (fu) {
+    LAUNCHN("rowproj", st, launch_rowproj_reduce(rd, p.upart, (int)cdiv(I, gemm_tile_cols(true, true)), st));
+  } else {
+    LAUNCHN("rowproj", st, launch_rowproj(c.bf16, rd, st));
+  }
 
   GemmArgs gd{};
   gd.M = T;

@@ -100,7 +100,7 @@ __device__ __forceinline__ void for4(F&& f) {
 template <int WN, int EPI>
 constexpr int epi_stage_bytes() {
   return EPI == EPI_STORE      ? 32 * (WN + 4) * 4
-         : EPI == EPI_ACT_FWD  ? 3 * 32 * (WN / 2 + 8) * 2
+         : EPI == EPI_ACT_FWD  ? (3 * 32 * (WN / 2 + 8) * 2 > 8 * 64 * 16 ? 3 * 32 * (WN / 2 + 8) * 2 : 8 * 64 * 16)
          : EPI == EPI_ACT1_FWD ? 2 * 32 * (WN + 8) * 2
                                : 32 * (WN + 4) * 4 + 32 * (WN + 8) * 2 + 32 * 16 * 2;
 }
@@ -108,7 +108,7 @@ constexpr int epi_stage_bytes() {
 template <int WN, bool DUAL, int EPI>
 __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* wstage, const GemmArgs& args,
                                                int reg, int64_t mw, int64_t nbase, int64_t NR, int64_t M,
-                                               int lane, int wm, int kp) {
+                                               int lane, int wm, int wn, int kp) {
   constexpr int NI = WN / 32;
   if constexpr (EPI == EPI_STORE) {
     if (args.ksplit > 1) {
@@ -182,6 +182,20 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
     char* go = static_cast<char*>(args.g_out);
     char* ho = static_cast<char*>(args.h_out);
     const int64_t ld = args.ld_act;
+    // With u_part (the next projection's adapter input U_d = h Ad): h of each
+    // 32-row pass is already staged row-major; two 16x16x32 MFMAs per pass
+    // (M = 16 rows, N = the 16 adapter columns, K = this wavefront's 32 h
+    // columns) add h Ad over its columns.  Lane l holds the Ad^T fragment of
+    // adapter column l % 16, h columns 8 (l / 16) .. + 7 (zero past u_R, NR).
+    const bool fuse_u = args.u_part != nullptr;
+    bf16x8 adf = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+    if (fuse_u) {
+      const int jr = lane & 15;
+      const int64_t n = nbase + 8 * (lane >> 4);
+      if (jr < args.u_R && n < NR)
+        adf = *reinterpret_cast<const bf16x8*>(static_cast<const char*>(args.ad_t) + (jr * args.ld_adt + n) * 2);
+    }
+    f32x4 uacc[4][2];
     for4([&](auto jc) {
       constexpr int j = decltype(jc)::value;
 #pragma unroll
@@ -218,8 +232,42 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
           *reinterpret_cast<u32x4*>(ho + off) = *reinterpret_cast<const u32x4*>(stg + 2 * ARR + o);
         }
       }
+      if (fuse_u) {
+        const lds_char* hs = (const lds_char*)(stg + 2 * ARR);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const bf16x8 hf = __builtin_bit_cast(bf16x8, lds_read16(hs + ((mb * 16 + (lane & 15)) * LD + 8 * (lane >> 4)) * 2));
+          uacc[j][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hf, adf, f32x4{0, 0, 0, 0}, 0, 0, 0);
+        }
+      }
       wave_sync();
     });
+    if (fuse_u) {
+      // uacc[j][mb][v] = sum over this wavefront's h columns for row
+      // mw + 32 j + 16 mb + 4 (lane / 16) + v, adapter column lane % 16.  The
+      // four wavefronts of the row group (same rows) are added in fixed order
+      // in LDS; wavefront wn writes the sums of pass j = wn.
+      constexpr int EB = epi_stage_bytes<WN, EPI>();
+      f32x4* red = reinterpret_cast<f32x4*>(wstage);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) red[(jj * 2 + mb) * 64 + lane] = uacc[jj][mb];
+      __syncthreads();
+      const char* g0 = wstage - wn * EB;
+      const int64_t tnb = (nbase - 32 * wn) / 128;  // this tile's n index
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        f32x4 sum = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sum += reinterpret_cast<const f32x4*>(g0 + q * EB)[(wn * 2 + mb) * 64 + lane];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int64_t m = mw + 32 * wn + 16 * mb + 4 * (lane >> 4) + v;
+          if (m < M) args.u_part[(tnb * M + m) * 16 + (lane & 15)] = sum[v];
+        }
+      }
+    }
   } else if constexpr (EPI == EPI_ACT1_FWD) {
     constexpr int LD = WN + 8;           // bf16 staging [2][32][WN]: u, h
     constexpr int ARR = 32 * LD;
@@ -972,7 +1020,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   char* const wstage = smem_raw + wave * EB;
   const int64_t mw = m0 + wm * 128;
   const int64_t nbase = DUAL ? tnl * 128 + wn * 32 : tnl * 256 + wn * 64;
-  run_epilogue_w<64, DUAL, EPI>(acc, wstage, args, reg, mw, nbase, NR, M, lane, wm, kp);
+  run_epilogue_w<64, DUAL, EPI>(acc, wstage, args, reg, mw, nbase, NR, M, lane, wm, wn, kp);
 }
 
 __global__ void ksplit_reduce_kernel(const float* part, int ks, int64_t M, int64_t N, uint16_t* out, int64_t ldo) {

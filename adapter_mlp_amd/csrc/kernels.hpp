@@ -89,6 +89,14 @@ struct GemmArgs {
   // the parts in ascending order and stores bf16.  ksplit <= 1: no split.
   int32_t ksplit, pad3_;
   float* kpart;
+  // EPI_ACT_FWD (bf16) with u_part set: each block also forms h Ad over its
+  // h columns (ad_t = Ad^T [u_R, N], row pitch ld_adt, u_R <= 16) and writes
+  // the tile's sums to u_part [ntile_n, M, 16] (fp32); the rowproj reduce
+  // adds the n-tile slices in ascending order.
+  float* u_part;
+  const void* ad_t;
+  int64_t ld_adt;
+  int32_t u_R, pad4_;
 };
 
 // Columns of output covered by one n-tile.
@@ -151,6 +159,8 @@ hipError_t launch_colproj_reduce(const ColProjArgs& a, hipStream_t st);
 // fixed-order reduce then writes r's outputs.  Other cases run the two
 // kernels one after the other.  rpartial: rowcol_partial_floats(T, K) floats.
 hipError_t launch_rowcol(bool bf16, const ColProjArgs& c, const RowProjArgs& r, float* rpartial, hipStream_t st);
+// Only the reduce of a fused rowproj: r's outputs from nb column-block partials [nb, T, 16].
+hipError_t launch_rowproj_reduce(const RowProjArgs& r, const float* rpartial, int nb, hipStream_t st);
 int64_t rowcol_partial_floats(int64_t T, int64_t K);
 // partial-buffer floats the bf16 colproj needs for (T, K, R)
 int64_t colproj_partial_floats(int64_t T, int64_t K, int R);

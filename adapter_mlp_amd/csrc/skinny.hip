@@ -585,6 +585,12 @@ hipError_t launch_rowcol(bool bf16, const ColProjArgs& c0, const RowProjArgs& r,
   return hipGetLastError();
 }
 
+hipError_t launch_rowproj_reduce(const RowProjArgs& r, const float* rpartial, int nb, hipStream_t st) {
+  if (r.T == 0) return hipSuccess;
+  hipLaunchKernelGGL(rowproj_reduce_kernel, dim3(nblk(r.T * 4, 256)), dim3(256), 0, st, r, rpartial, nb);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack_batch(bool bf16, const PackBatchArgs& b, hipStream_t st) {
   int64_t nmax = 0;
   for (int i = 0; i < b.njobs; ++i) nmax = b.job[i].vcols * b.job[i].RL > nmax ? b.job[i].vcols * b.job[i].RL : nmax;
