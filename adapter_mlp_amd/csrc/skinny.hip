@@ -365,32 +365,47 @@ __device__ __forceinline__ void colproj_store(const ColProjArgs& a, bool bf16, i
   else static_cast<float*>(a.dest[q])[idx] = o;
 }
 
-// dest = scales * (sum over the a.nchunk slices of partial [nchunk, K, Rp]),
-// slices added in ascending order.  One thread per 4 consecutive columns j
-// of one k (R is a multiple of 4 in the bf16 path; the 4 never straddle two
-// adapters since seg_w is a multiple of 8): 16-byte loads, consecutive
-// threads on consecutive addresses.
-__global__ void colproj_reduce_kernel(const ColProjArgs a, int Rp) {
-  const int RQ = a.R / 4;
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= a.K * RQ) return;
-  const int64_t k = e / RQ;
-  const int j0 = (int)(e % RQ) * 4;
-  const float* src = a.partial + k * Rp + j0;
-  const int64_t cstride = a.K * Rp;
+// dest = scales * (sum over the a.nchunk slices of partial [nchunk, K, Rp]).
+// A block takes 64 outputs of 4 consecutive columns j of one k (R is a
+// multiple of 4 in the bf16 path; the 4 never straddle two adapters since
+// seg_w is a multiple of 8) and splits the slices into 4 contiguous ranges,
+// one per group of 64 threads: 16-byte loads on consecutive addresses.  Each
+// range is summed in ascending order and the 4 range sums are added in
+// ascending order, so the result does not depend on the launch.
+constexpr int RED_PARTS = 4;
+__device__ __forceinline__ f32x4 sum_slices(const float* src, int64_t stride, int b0, int b1) {
   f32x4 v = f32x4{0, 0, 0, 0};
-  int c = 0;
-  for (; c + 4 <= a.nchunk; c += 4) {
-    const f32x4 p0 = *reinterpret_cast<const f32x4*>(src + (c + 0) * cstride);
-    const f32x4 p1 = *reinterpret_cast<const f32x4*>(src + (c + 1) * cstride);
-    const f32x4 p2 = *reinterpret_cast<const f32x4*>(src + (c + 2) * cstride);
-    const f32x4 p3 = *reinterpret_cast<const f32x4*>(src + (c + 3) * cstride);
+  int b = b0;
+  for (; b + 4 <= b1; b += 4) {
+    const f32x4 p0 = *reinterpret_cast<const f32x4*>(src + (b + 0) * stride);
+    const f32x4 p1 = *reinterpret_cast<const f32x4*>(src + (b + 1) * stride);
+    const f32x4 p2 = *reinterpret_cast<const f32x4*>(src + (b + 2) * stride);
+    const f32x4 p3 = *reinterpret_cast<const f32x4*>(src + (b + 3) * stride);
     v += p0;
     v += p1;
     v += p2;
     v += p3;
   }
-  for (; c < a.nchunk; ++c) v += *reinterpret_cast<const f32x4*>(src + c * cstride);
+  for (; b < b1; ++b) v += *reinterpret_cast<const f32x4*>(src + b * stride);
+  return v;
+}
+
+__global__ __launch_bounds__(256) void colproj_reduce_kernel(const ColProjArgs a, int Rp) {
+  __shared__ f32x4 part[RED_PARTS][64];
+  const int RQ = a.R / 4;
+  const int pq = threadIdx.x >> 6, o = threadIdx.x & 63;
+  const int64_t e = (int64_t)blockIdx.x * 64 + o;
+  const bool live = e < a.K * RQ;
+  const int64_t k = live ? e / RQ : 0;
+  const int j0 = live ? (int)(e % RQ) * 4 : 0;
+  if (live)
+    part[pq][o] = sum_slices(a.partial + k * Rp + j0, a.K * Rp, (int)((int64_t)pq * a.nchunk / RED_PARTS),
+                             (int)((int64_t)(pq + 1) * a.nchunk / RED_PARTS));
+  __syncthreads();
+  if (pq != 0 || !live) return;
+  f32x4 v = part[0][o];
+#pragma unroll
+  for (int q = 1; q < RED_PARTS; ++q) v += part[q][o];
 #pragma unroll
   for (int q = 0; q < 4; ++q) colproj_store(a, a.out_f32 == 0, k, j0 + q, v[q]);
 }
@@ -481,7 +496,7 @@ hipError_t launch_rowproj(bool bf16, const RowProjArgs& a, hipStream_t st) {
 
 hipError_t launch_colproj_reduce(const ColProjArgs& a, hipStream_t st) {
   if (a.K * a.R == 0) return hipSuccess;
-  hipLaunchKernelGGL(colproj_reduce_kernel, dim3(nblk(a.K * (a.R / 4), 256)), dim3(256), 0, st, a, 16);
+  hipLaunchKernelGGL(colproj_reduce_kernel, dim3(nblk(a.K * (a.R / 4), 64)), dim3(256), 0, st, a, 16);
   return hipGetLastError();
 }
 
@@ -513,38 +528,34 @@ hipError_t launch_colproj(bool bf16, const ColProjArgs& a0, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(colproj_reduce_kernel, dim3(nblk(a.K * (a.R / 4), 256)), dim3(256), 0, st, a, NJ * 16);
+  hipLaunchKernelGGL(colproj_reduce_kernel, dim3(nblk(a.K * (a.R / 4), 64)), dim3(256), 0, st, a, NJ * 16);
   return hipGetLastError();
 }
 
 namespace {
 // Out[t, j] of a fused rowproj: the column blocks' partials [nb, T, 16]
-// summed in ascending block order, then written as the rowproj kernel writes
-// it.  One thread per 4 consecutive j (< 16) of one row t: 16-byte loads;
-// the threads of quad 0 also write the zero padding of out2 past 16.
-__global__ void rowproj_reduce_kernel(const RowProjArgs a, const float* rpartial, int nb) {
+// summed, then written as the rowproj kernel writes it.  A block takes 16
+// rows x 4 quads of columns (j < 16) and splits the blocks into 4 contiguous
+// ranges as in colproj_reduce_kernel (ascending within a range, ranges added
+// in ascending order); the quad-0 threads also write the zero padding of
+// out2 past 16.
+__global__ __launch_bounds__(256) void rowproj_reduce_kernel(const RowProjArgs a, const float* rpartial, int nb) {
+  __shared__ f32x4 part[RED_PARTS][64];
   const int R2 = a.R2 > a.R ? a.R2 : a.R;
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= a.T * 4) return;
+  const int pq = threadIdx.x >> 6, o = threadIdx.x & 63;
+  const int64_t e = (int64_t)blockIdx.x * 64 + o;
+  const bool live = e < a.T * 4;
   const int64_t t = e >> 2;
-  const int j0 = (int)(e & 3) * 4;
-  f32x4 v = f32x4{0, 0, 0, 0};
-  if (j0 < a.R) {
-    const float* src = rpartial + t * 16 + j0;
-    const int64_t bstride = a.T * 16;
-    int b = 0;
-    for (; b + 4 <= nb; b += 4) {
-      const f32x4 p0 = *reinterpret_cast<const f32x4*>(src + (b + 0) * bstride);
-      const f32x4 p1 = *reinterpret_cast<const f32x4*>(src + (b + 1) * bstride);
-      const f32x4 p2 = *reinterpret_cast<const f32x4*>(src + (b + 2) * bstride);
-      const f32x4 p3 = *reinterpret_cast<const f32x4*>(src + (b + 3) * bstride);
-      v += p0;
-      v += p1;
-      v += p2;
-      v += p3;
-    }
-    for (; b < nb; ++b) v += *reinterpret_cast<const f32x4*>(src + b * bstride);
-  }
+  const int j0 = (o & 3) * 4;
+  if (live)
+    part[pq][o] = j0 < a.R ? sum_slices(rpartial + t * 16 + j0, a.T * 16, (int)((int64_t)pq * nb / RED_PARTS),
+                                        (int)((int64_t)(pq + 1) * nb / RED_PARTS))
+                           : f32x4{0, 0, 0, 0};
+  __syncthreads();
+  if (pq != 0 || !live) return;
+  f32x4 v = part[0][o];
+#pragma unroll
+  for (int q = 1; q < RED_PARTS; ++q) v += part[q][o];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int j = j0 + q;
@@ -580,14 +591,14 @@ hipError_t launch_rowcol(bool bf16, const ColProjArgs& c0, const RowProjArgs& r,
   if (e != hipSuccess) return e;
   const int R2 = r.R2 > r.R ? r.R2 : r.R;
   (void)R2;
-  hipLaunchKernelGGL(rowproj_reduce_kernel, dim3(nblk(r.T * 4, 256)), dim3(256), 0, st, r, rpartial,
+  hipLaunchKernelGGL(rowproj_reduce_kernel, dim3(nblk(r.T * 4, 64)), dim3(256), 0, st, r, rpartial,
                      (int)((r.K + 255) / 256));
   return hipGetLastError();
 }
 
 hipError_t launch_rowproj_reduce(const RowProjArgs& r, const float* rpartial, int nb, hipStream_t st) {
   if (r.T == 0) return hipSuccess;
-  hipLaunchKernelGGL(rowproj_reduce_kernel, dim3(nblk(r.T * 4, 256)), dim3(256), 0, st, r, rpartial, nb);
+  hipLaunchKernelGGL(rowproj_reduce_kernel, dim3(nblk(r.T * 4, 64)), dim3(256), 0, st, r, rpartial, nb);
   return hipGetLastError();
 }
 
