@@ -404,11 +404,22 @@ def cpu_baseline(cfg, inp, seconds):
     t0 = time.perf_counter()
     run(ts)
     dt = time.perf_counter() - t0
+    reps = 1
+    # when the whole workload takes less than the target, pass over it again
+    # (at most 10 passes) so the timed CPU work still lasts about `seconds`
+    if ts >= cfg.T and dt < 0.75 * seconds:
+        extra = min(9, int(round(seconds / max(dt, 1e-3))) - 1)
+        t1 = time.perf_counter()
+        for _ in range(extra):
+            run(ts)
+        dt += time.perf_counter() - t1
+        reps += extra
     threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("internal_api") == "openblas"]
                   or [1])
-    return {"value": ts / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {ts} of {cfg.T} tokens, full-size weights, fp32 numpy oracle fwd+bwd "
-                      f"({dt:.1f} s)", "seconds": round(dt, 2), "cpu_count": len(os.sched_getaffinity(0))}
+    what = f"{reps} passes over all {cfg.T} tokens" if reps > 1 else f"first {ts} of {cfg.T} tokens"
+    return {"value": reps * ts / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{what}, full-size weights, fp32 numpy oracle fwd+bwd ({dt:.1f} s)",
+            "seconds": round(dt, 2), "cpu_count": len(os.sched_getaffinity(0))}
 
 
 def main():
