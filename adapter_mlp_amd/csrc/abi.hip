@@ -469,6 +469,7 @@ struct Relu2Plan {
   void *ad_f, *ad_b;                                          // adapter casts (fp32 LoRA-gradient mode)
   void *At_u, *Us_u, *BLt_u, *h, *At_d, *Us_d, *BLt_d;        // forward
   float* kpart;                                               // down GEMM split-K
+  float* upart;  // h A_d partials of the up GEMM's epilogue [I/256, T, 16] (fused, bf16, r <= 16)
   void *Ps_d, *BLt_dh, *hb, *du, *Ps_u, *BLt_dx;              // backward
   float* partial;
   float* rpartial;  // rowproj partials of the fused dY / du passes
@@ -490,6 +491,8 @@ Relu2Plan plan_relu2(const Ctx& c, const lora_relu2_mlp_desc& d, void* ws_fwd, v
   p.Us_d = f.take(T * RL * c.es);
   p.BLt_d = f.take(H * RL * c.es);
   p.kpart = static_cast<float*>(f.take((size_t)kpart_floats(c, T, H, I + RL) * 4));
+  p.upart = fuse_da(c, r) ? static_cast<float*>(f.take((size_t)(cdiv(I, gemm_tile_cols(true, false)) * T * 16 * 4)))
+                          : nullptr;
   p.fwd_bytes = f.off;
   Ws b(ws_bwd);
   p.ad_b = b.take(staged_bytes(c, ad, 2, r));
@@ -1161,6 +1164,13 @@ lora_status lora_relu2_mlp_fwd(const lora_relu2_mlp_desc* d, const void* X, cons
   g.e_out = saved->u;
   g.h_out = p.h;
   g.ld_act = I;
+  const bool fu = fuse_da(c, r);  // U_d = h A_d formed in the up GEMM's epilogue
+  if (fu) {
+    g.u_part = p.upart;
+    g.ad_t = p.At_d;
+    g.ld_adt = I;
+    g.u_R = (int)r;
+  }
   LAUNCH(gemm_on(c, g, st, I));
 
   // U_d = h A_d, then the down GEMM
@@ -1171,7 +1181,11 @@ lora_status lora_relu2_mlp_fwd(const lora_relu2_mlp_desc* d, const void* X, cons
   rd.off1 = r;
   rd.out2 = p.Us_d;
   rd.ld2 = RL;
-  LAUNCHN("rowproj", st, launch_rowproj(c.bf16, rd, st));
+  if (fu) {
+    LAUNCHN("rowproj", st, launch_rowproj_reduce(rd, p.upart, (int)cdiv(I, gemm_tile_cols(true, false)), st));
+  } else {
+    LAUNCHN("rowproj", st, launch_rowproj(c.bf16, rd, st));
+  }
   GemmArgs gd{};
   gd.M = T;
   gd.nseg = 1;

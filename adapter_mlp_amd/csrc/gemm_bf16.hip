@@ -105,6 +105,69 @@ constexpr int epi_stage_bytes() {
                                : 32 * (WN + 4) * 4 + 32 * (WN + 8) * 2 + 32 * 16 * 2;
 }
 
+// U = h Ad formed by a forward activation epilogue (u_part set): HC h columns
+// per wavefront (32 in gate/up tiles, 64 in ReLU^2 tiles), K blocks of 32.
+// Per 32-row pass, the staged h rows (row-major, pitch LD) feed 16x16x32
+// MFMAs: M = 16 rows, N = the 16 adapter columns, K = 32 h columns; lane l
+// holds the Ad^T fragment of adapter column l % 16, h columns 8 (l / 16) ..
+// + 7 of each K block (zero past u_R and NR).  At the end the four
+// wavefronts of a row group (same rows) are added in fixed order in LDS and
+// wavefront wn writes the sums of pass wn into the tile's slice of u_part.
+template <int HC>
+struct FusedU {
+  static constexpr int KB = HC / 32;
+  bf16x8 adf[KB];
+  f32x4 acc[4][2];
+  __device__ __forceinline__ void init(const GemmArgs& args, int64_t nbase, int64_t NR, int lane) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      adf[kb] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+      const int jr = lane & 15;
+      const int64_t n = nbase + 32 * kb + 8 * (lane >> 4);
+      if (jr < args.u_R && n < NR)
+        adf[kb] = *reinterpret_cast<const bf16x8*>(static_cast<const char*>(args.ad_t) + (jr * args.ld_adt + n) * 2);
+    }
+  }
+  template <int J, int LD>
+  __device__ __forceinline__ void pass(const uint16_t* hstage, int lane) {
+    const lds_char* hs = (const lds_char*)hstage;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      f32x4 a = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 hf = __builtin_bit_cast(
+            bf16x8, lds_read16(hs + ((mb * 16 + (lane & 15)) * LD + 32 * kb + 8 * (lane >> 4)) * 2));
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hf, adf[kb], a, 0, 0, 0);
+      }
+      acc[J][mb] = a;
+    }
+  }
+  // wstage: this wavefront's staging (EB bytes per wavefront, wavefront wn of its group)
+  template <int EB>
+  __device__ __forceinline__ void finish(const GemmArgs& args, char* wstage, int64_t mw, int64_t tnb, int64_t M,
+                                         int wn, int lane) {
+    f32x4* red = reinterpret_cast<f32x4*>(wstage);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) red[(jj * 2 + mb) * 64 + lane] = acc[jj][mb];
+    __syncthreads();
+    const char* g0 = wstage - wn * EB;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      f32x4 sum = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sum += reinterpret_cast<const f32x4*>(g0 + q * EB)[(wn * 2 + mb) * 64 + lane];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t m = mw + 32 * wn + 16 * mb + 4 * (lane >> 4) + v;
+        if (m < M) args.u_part[(tnb * M + m) * 16 + (lane & 15)] = sum[v];
+      }
+    }
+  }
+};
+
 template <int WN, bool DUAL, int EPI>
 __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* wstage, const GemmArgs& args,
                                                int reg, int64_t mw, int64_t nbase, int64_t NR, int64_t M,
@@ -182,20 +245,10 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
     char* go = static_cast<char*>(args.g_out);
     char* ho = static_cast<char*>(args.h_out);
     const int64_t ld = args.ld_act;
-    // With u_part (the next projection's adapter input U_d = h Ad): h of each
-    // 32-row pass is already staged row-major; two 16x16x32 MFMAs per pass
-    // (M = 16 rows, N = the 16 adapter columns, K = this wavefront's 32 h
-    // columns) add h Ad over its columns.  Lane l holds the Ad^T fragment of
-    // adapter column l % 16, h columns 8 (l / 16) .. + 7 (zero past u_R, NR).
+    // with u_part: U_d = h Ad over this wavefront's 32 h columns (FusedU)
     const bool fuse_u = args.u_part != nullptr;
-    bf16x8 adf = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-    if (fuse_u) {
-      const int jr = lane & 15;
-      const int64_t n = nbase + 8 * (lane >> 4);
-      if (jr < args.u_R && n < NR)
-        adf = *reinterpret_cast<const bf16x8*>(static_cast<const char*>(args.ad_t) + (jr * args.ld_adt + n) * 2);
-    }
-    f32x4 uacc[4][2];
+    FusedU<W2> fu;
+    if (fuse_u) fu.init(args, nbase, NR, lane);
     for4([&](auto jc) {
       constexpr int j = decltype(jc)::value;
 #pragma unroll
@@ -232,42 +285,11 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
           *reinterpret_cast<u32x4*>(ho + off) = *reinterpret_cast<const u32x4*>(stg + 2 * ARR + o);
         }
       }
-      if (fuse_u) {
-        const lds_char* hs = (const lds_char*)(stg + 2 * ARR);
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const bf16x8 hf = __builtin_bit_cast(bf16x8, lds_read16(hs + ((mb * 16 + (lane & 15)) * LD + 8 * (lane >> 4)) * 2));
-          uacc[j][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hf, adf, f32x4{0, 0, 0, 0}, 0, 0, 0);
-        }
-      }
+      if (fuse_u) fu.template pass<j, LD>(stg + 2 * ARR, lane);
       wave_sync();
     });
-    if (fuse_u) {
-      // uacc[j][mb][v] = sum over this wavefront's h columns for row
-      // mw + 32 j + 16 mb + 4 (lane / 16) + v, adapter column lane % 16.  The
-      // four wavefronts of the row group (same rows) are added in fixed order
-      // in LDS; wavefront wn writes the sums of pass j = wn.
-      constexpr int EB = epi_stage_bytes<WN, EPI>();
-      f32x4* red = reinterpret_cast<f32x4*>(wstage);
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) red[(jj * 2 + mb) * 64 + lane] = uacc[jj][mb];
-      __syncthreads();
-      const char* g0 = wstage - wn * EB;
-      const int64_t tnb = (nbase - 32 * wn) / 128;  // this tile's n index
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        f32x4 sum = f32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) sum += reinterpret_cast<const f32x4*>(g0 + q * EB)[(wn * 2 + mb) * 64 + lane];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int64_t m = mw + 32 * wn + 16 * mb + 4 * (lane >> 4) + v;
-          if (m < M) args.u_part[(tnb * M + m) * 16 + (lane & 15)] = sum[v];
-        }
-      }
-    }
+    // this tile's n index: 128 output columns per gate/up tile
+    if (fuse_u) fu.template finish<epi_stage_bytes<WN, EPI>()>(args, wstage, mw, (nbase - 32 * wn) / 128, M, wn, lane);
   } else if constexpr (EPI == EPI_ACT1_FWD) {
     constexpr int LD = WN + 8;           // bf16 staging [2][32][WN]: u, h
     constexpr int ARR = 32 * LD;
@@ -277,6 +299,10 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
     char* uo = static_cast<char*>(args.e_out);
     char* ho = static_cast<char*>(args.h_out);
     const int64_t ld = args.ld_act;
+    // with u_part: U_d = h Ad over this wavefront's WN h columns (FusedU)
+    const bool fuse_u = args.u_part != nullptr;
+    FusedU<WN> fu;
+    if (fuse_u) fu.init(args, nbase, NR, lane);
     for4([&](auto jc) {
       constexpr int j = decltype(jc)::value;
 #pragma unroll
@@ -307,8 +333,11 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
           *reinterpret_cast<u32x4*>(ho + off) = *reinterpret_cast<const u32x4*>(stg + ARR + o);
         }
       }
+      if (fuse_u) fu.template pass<j, LD>(stg + ARR, lane);
       wave_sync();
     });
+    // this tile's n index: 256 output columns per tile
+    if (fuse_u) fu.template finish<epi_stage_bytes<WN, EPI>()>(args, wstage, mw, (nbase - (int64_t)WN * wn) / 256, M, wn, lane);
   } else {
     // EPI_ACT_BWD (gated) or EPI_ACT1_BWD (ungated ReLU^2: du = dh phi'(u) into dg_out)
     //
