@@ -49,23 +49,33 @@ __device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 
 //               phi'(x) = (1 + tanh u)/2 + x/2 (1 - tanh^2 u) sqrt(2/pi) (1 + 3*0.044715 x^2)
 // tanh is formed from exp so both ends saturate cleanly: tanh u = 1 - 2/(e^{2u}+1).
 // ---------------------------------------------------------------------------
+// The bf16 epilogues (ACCURATE = false) round phi and phi' to bf16, so they
+// take the hardware exponential and reciprocal (v_exp_f32, v_rcp_f32, about
+// 1 ulp of fp32 each) instead of a correctly rounded division, which expands
+// to some ten instructions.  1 / inf = 0 keeps both ends of the sigmoid and
+// of tanh finite.
 template <bool ACCURATE>
 __device__ __forceinline__ float dev_exp(float x) {
   if constexpr (ACCURATE) return expf(x);
   else return __expf(x);
 }
+template <bool ACCURATE>
+__device__ __forceinline__ float dev_rcp(float x) {
+  if constexpr (ACCURATE) return 1.0f / x;
+  else return __builtin_amdgcn_rcpf(x);
+}
 
 template <bool ACCURATE>
 __device__ __forceinline__ void act_fwd(int act, float x, float& phi) {
   if (act == LORA_ACT_SWIGLU) {
-    float s = 1.0f / (1.0f + dev_exp<ACCURATE>(-x));
+    float s = dev_rcp<ACCURATE>(1.0f + dev_exp<ACCURATE>(-x));
     phi = x * s;
   } else {
     const float c = 0.7978845608028654f, k = 0.044715f;
     float u = c * (x + k * x * x * x);
     float t;
     if constexpr (ACCURATE) t = tanhf(u);
-    else t = 1.0f - 2.0f / (dev_exp<ACCURATE>(2.0f * u) + 1.0f);
+    else t = 1.0f - 2.0f * dev_rcp<ACCURATE>(dev_exp<ACCURATE>(2.0f * u) + 1.0f);
     phi = 0.5f * x * (1.0f + t);
   }
 }
@@ -73,7 +83,7 @@ __device__ __forceinline__ void act_fwd(int act, float x, float& phi) {
 template <bool ACCURATE>
 __device__ __forceinline__ void act_fwd_bwd(int act, float x, float& phi, float& dphi) {
   if (act == LORA_ACT_SWIGLU) {
-    float s = 1.0f / (1.0f + dev_exp<ACCURATE>(-x));
+    float s = dev_rcp<ACCURATE>(1.0f + dev_exp<ACCURATE>(-x));
     phi = x * s;
     dphi = s * (1.0f + x * (1.0f - s));
   } else {
@@ -81,7 +91,7 @@ __device__ __forceinline__ void act_fwd_bwd(int act, float x, float& phi, float&
     float u = c * (x + k * x * x * x);
     float t;
     if constexpr (ACCURATE) t = tanhf(u);
-    else t = 1.0f - 2.0f / (dev_exp<ACCURATE>(2.0f * u) + 1.0f);
+    else t = 1.0f - 2.0f * dev_rcp<ACCURATE>(dev_exp<ACCURATE>(2.0f * u) + 1.0f);
     phi = 0.5f * x * (1.0f + t);
     dphi = 0.5f * (1.0f + t) + 0.5f * x * (1.0f - t * t) * c * (1.0f + 3.0f * k * x * x);
   }
