@@ -467,7 +467,9 @@ int colproj_nchunk(int64_t T, int64_t K) {
   const int64_t steps = (T + 31) / 32;
   if (steps == 0) return 0;
   const int64_t kblocks = (K + 255) / 256;
-  int64_t want = (512 + kblocks - 1) / kblocks;  // about two blocks per CU
+  // at most one round of two blocks per CU: a partial second round would run
+  // its few blocks while most CUs idle
+  int64_t want = 512 / kblocks;
   if (want < 1) want = 1;
   return (int)(want < steps ? want : steps);
 }
