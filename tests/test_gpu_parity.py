@@ -1,8 +1,8 @@
 """GPU parity of the HIP path against the CPU oracle on the same seeded inputs.
 
 Shapes here span several 256-row / 256-column tiles with ragged tails and
-run in seconds on the oracle; the five benchmark shapes are in
-test_gpu_configs.py.  Bar: max|err|/max|ref| <= 2e-2 per output tensor in
+run in seconds on the oracle, up to operands at the kernels' 2 GiB limit;
+the benchmark shapes are in test_gpu_configs.py.  Bar: max|err|/max|ref| <= 2e-2 per output tensor in
 bf16 (fp32 accumulation), <= 1e-5 in fp32; NF4 codes and dequantized weights
 bit-exact.
 """
@@ -161,6 +161,46 @@ def _relu2_case(lm, cfg, nf4=False):
 def test_relu2_mlp_bf16_ragged(lm):
     cfg = WorkloadConfig(97, "relu2", T=300, H=512, I=1088, r=16, alpha=32, dtype="bf16")
     _relu2_case(lm, cfg)
+
+
+@pytest.mark.slow
+def test_relu2_mlp_bf16_maximum_extent(lm):
+    # u, h and du of T x I bf16 just under 2 GiB (T = 65535, a 255-row tail);
+    # the oracle runs on row chunks and the adapter gradients, sums over
+    # tokens, are added in fp64 over the chunks
+    import torch
+
+    T, H, I = 65535, 64, 16384
+    cfg = WorkloadConfig(93, "relu2", T=T, H=H, I=I, r=16, alpha=32, dtype="bf16")
+    inp = make_relu2_inputs(cfg)
+    X, dY = dev(inp["X"]), dev(inp["dY"])
+    up, down = (proj_dev(inp[k]) for k in ("up", "down"))
+    Y, saved = lm.relu2_mlp_fwd(X, up, down)
+    dX, grads = lm.relu2_mlp_bwd(dY, X, saved, up, down)
+    torch.cuda.synchronize()
+    gkeys = (("dA_up", "dA_u"), ("dB_up", "dB_u"), ("dA_down", "dA_d"), ("dB_down", "dB_d"))
+    Yr, dXr = np.zeros((T, H)), np.zeros((T, H))
+    sums = {k: 0.0 for _, k in gkeys}
+    u_err, u_ref = 0.0, 0.0
+    CH = 8192
+    for t0 in range(0, T, CH):
+        sl = slice(t0, min(T, t0 + CH))
+        Yc, sc = OL.relu2_mlp_fwd(inp["X"][sl], inp["up"], inp["down"])
+        gc = OL.relu2_mlp_bwd(inp["dY"][sl], inp["X"][sl], sc, inp["up"], inp["down"])
+        Yr[sl], dXr[sl] = Yc, gc["dX"]
+        for _, k in gkeys:
+            sums[k] = sums[k] + gc[k].astype(np.float64)
+        got = host(saved["u"][sl])
+        assert np.all(np.isfinite(got)), f"u: non-finite values in rows {t0}.."
+        u_err = max(u_err, float(np.abs(got - sc["u"]).max()))
+        u_ref = max(u_ref, float(np.abs(sc["u"]).max()))
+    tol = TOL["bf16"]
+    print(f"  u        max|err|/max|ref| = {u_err / u_ref:.3e} (tol {tol:g})", flush=True)
+    assert u_err <= tol * u_ref
+    assert_close("Y", host(Y), Yr, tol)
+    assert_close("dX", host(dX), dXr, tol)
+    for k_dev, k_ref in gkeys:
+        assert_close(k_dev, host(grads[k_dev]), sums[k_ref], tol)
 
 
 def test_relu2_mlp_bf16_rank32(lm):
@@ -423,6 +463,51 @@ def test_mlp_edge_token_counts(lm, T):
     assert_close("dX", host(dX), gr["dX"], TOL["bf16"])
     assert_close("dA_gate", host(grads["dA_gate"]), gr["dA_g"], TOL["bf16"])
     assert_close("dB_down", host(grads["dB_down"]), gr["dB_d"], TOL["bf16"])
+
+
+@pytest.mark.slow
+def test_mlp_bf16_maximum_extent(lm):
+    # The largest activation the kernels' 32-bit operand offsets accept: T x I
+    # bf16 just under 2 GiB (T = 65535: 255 whole 256-row tiles and a 255-row
+    # tail).  H = 64 keeps the oracle's products small; it runs on row chunks
+    # (Y, e, g and dX rows are per token; every dA and dB is a sum over
+    # tokens, added here in fp64 over the chunks).
+    import torch
+
+    T, H, I = 65535, 64, 16384
+    cfg = WorkloadConfig(94, "mlp", T=T, H=H, I=I, r=16, alpha=32, dtype="bf16", act="swiglu")
+    inp = make_mlp_inputs(cfg)
+    X, dY = dev(inp["X"]), dev(inp["dY"])
+    g, u, d = (proj_dev(inp[k]) for k in ("gate", "up", "down"))
+    Y, saved = lm.mlp_fwd(X, g, u, d, "swiglu")
+    dX, grads = lm.mlp_bwd(dY, X, saved, g, u, d, "swiglu")
+    torch.cuda.synchronize()
+    gkeys = (("dA_gate", "dA_g"), ("dB_gate", "dB_g"), ("dA_up", "dA_u"), ("dB_up", "dB_u"),
+             ("dA_down", "dA_d"), ("dB_down", "dB_d"))
+    Yr, dXr = np.zeros((T, H)), np.zeros((T, H))
+    sums = {k: 0.0 for _, k in gkeys}
+    err = {"e": [0.0, 0.0], "g": [0.0, 0.0]}  # max|err|, max|ref| over the chunks
+    CH = 8192
+    for t0 in range(0, T, CH):
+        sl = slice(t0, min(T, t0 + CH))
+        Yc, sc = OL.mlp_fwd(inp["X"][sl], inp["gate"], inp["up"], inp["down"], "swiglu")
+        gc = OL.mlp_bwd(inp["dY"][sl], inp["X"][sl], sc, inp["gate"], inp["up"], inp["down"], "swiglu")
+        Yr[sl], dXr[sl] = Yc, gc["dX"]
+        for _, k in gkeys:
+            sums[k] = sums[k] + gc[k].astype(np.float64)
+        for k in ("e", "g"):
+            got = host(saved[k][sl])
+            assert np.all(np.isfinite(got)), f"{k}: non-finite values in rows {t0}.."
+            err[k][0] = max(err[k][0], float(np.abs(got - sc[k]).max()))
+            err[k][1] = max(err[k][1], float(np.abs(sc[k]).max()))
+    tol = TOL["bf16"]
+    for k, (e_max, r_max) in err.items():
+        print(f"  {k:8s} max|err|/max|ref| = {e_max / r_max:.3e} (tol {tol:g})", flush=True)
+        assert e_max <= tol * r_max, k
+    assert_close("Y", host(Y), Yr, tol)
+    assert_close("dX", host(dX), dXr, tol)
+    for k_dev, k_ref in gkeys:
+        assert_close(k_dev, host(grads[k_dev]), sums[k_ref], tol)
 
 
 def test_mlp_B_zero_gives_zero_dA_and_base_output(lm):
