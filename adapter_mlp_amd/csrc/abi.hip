@@ -402,7 +402,7 @@ struct MlpPlan {
   float* upart;  // h A_d partials of the gate/up epilogue [I/128, T, 16] (fused, bf16, r <= 16)
   void *Ps_d, *BLt_dh, *hb, *dg, *de, *Ps_ug, *BLt_dx;                      // backward
   float* partial;
-  float* rpartial;  // rowproj partials of the fused dY / dg / de passes
+  float* rpartial;  // rowproj partials of the fused dY pass, then of the batched dg and de passes
   size_t fwd_bytes, bwd_bytes;
 };
 
@@ -439,11 +439,18 @@ MlpPlan plan_mlp(const Ctx& c, const lora_mlp_desc& d, void* ws_fwd, void* ws_bw
                               colproj_partial_floats(T, H, (int)(2 * r)), 0};
     for (int i = 0; i < 3; ++i) pf = cands[i] > pf ? cands[i] : pf;
     if (fuse_da(c, r) && fused_da_floats(T, I) > pf) pf = fused_da_floats(T, I);
+    // the batched dg / de passes: one colproj partial per gradient
+    const int64_t Kb[2] = {I, I};
+    const int64_t bp = 2 * rowcol_batch_partial_floats(T, Kb, 2, 0);
+    if (bp > pf) pf = bp;
     // the dX GEMM's split-K partials (the partial buffer is free by then)
     if (kpart_floats(c, T, H, 2 * I + RLg) > pf) pf = kpart_floats(c, T, H, 2 * I + RLg);
   }
   p.partial = static_cast<float*>(b.take((size_t)pf * 4));
-  p.rpartial = c.bf16 ? static_cast<float*>(b.take((size_t)rowcol_partial_floats(T, I > H ? I : H) * 4)) : nullptr;
+  {
+    const int64_t rp_dy = rowcol_partial_floats(T, H), rp_gu = 2 * rowcol_partial_floats(T, I);
+    p.rpartial = c.bf16 ? static_cast<float*>(b.take((size_t)(rp_dy > rp_gu ? rp_dy : rp_gu) * 4)) : nullptr;
+  }
   p.bwd_bytes = b.off;
   return p;
 }
@@ -536,7 +543,7 @@ struct QkvPlan {
   void *At, *Us, *BLt;     // forward
   void *Ps, *BLt_dx;       // backward
   float* partial;
-  float* rpartial;         // rowproj partials of the fused dQ / dK / dV passes
+  float* rpartial;         // rowproj partials of the batched dQ / dK / dV passes, one region each
   size_t fwd_bytes, bwd_bytes;
 };
 
@@ -557,15 +564,19 @@ QkvPlan plan_qkv(const Ctx& c, const lora_qkv_desc& d, void* wf, void* wb) {
   p.BLt_dx = b.take(H * RL * c.es);
   int64_t pf = 0;
   if (c.bf16) {
-    const int64_t cand[4] = {colproj_partial_floats(T, d.Nq, (int)r), colproj_partial_floats(T, d.Nk, (int)r),
-                             colproj_partial_floats(T, d.Nv, (int)r), colproj_partial_floats(T, H, (int)(3 * r))};
-    for (int i = 0; i < 4; ++i) pf = cand[i] > pf ? cand[i] : pf;
+    // the batched dQ / dK / dV passes (one colproj partial each), the dA pass over X
+    const int64_t Kb[3] = {d.Nq, d.Nk, d.Nv};
+    const int64_t cand[2] = {rowcol_batch_partial_floats(T, Kb, 3, 0) + rowcol_batch_partial_floats(T, Kb, 3, 1) +
+                                 rowcol_batch_partial_floats(T, Kb, 3, 2),
+                             colproj_partial_floats(T, H, (int)(3 * r))};
+    for (int i = 0; i < 2; ++i) pf = cand[i] > pf ? cand[i] : pf;
     if (kpart_floats(c, T, H, N + RL) > pf) pf = kpart_floats(c, T, H, N + RL);  // dX split-K
   }
   p.partial = static_cast<float*>(b.take((size_t)pf * 4));
-  int64_t nmax = d.Nq > d.Nk ? d.Nq : d.Nk;
-  nmax = nmax > d.Nv ? nmax : d.Nv;
-  p.rpartial = c.bf16 ? static_cast<float*>(b.take((size_t)rowcol_partial_floats(T, nmax) * 4)) : nullptr;
+  p.rpartial = c.bf16 ? static_cast<float*>(b.take(
+                            (size_t)(rowcol_partial_floats(T, d.Nq) + rowcol_partial_floats(T, d.Nk) +
+                                     rowcol_partial_floats(T, d.Nv)) * 4))
+                      : nullptr;
   p.bwd_bytes = b.off;
   return p;
 }
@@ -1023,18 +1034,26 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, 
   r2.scales[0] = up->scale;
   r2.out2 = p.Ps_ug;
   r2.ld2 = RLg;
+  // both passes in one launch, each with scratch of its own (a batch that
+  // does not fuse, r > 16, runs them one after the other on the same scratch)
+  const int64_t Kb[2] = {I, I};
+  const bool rc_fused = c.bf16 && r <= 16;
+  float* const part_de = p.partial + (rc_fused ? rowcol_batch_partial_floats(T, Kb, 2, 0) : 0);
   ColProjArgs c3 = colproj_args(c, p.dg, I, T, I, coff(U, r, c), 3 * r, (int)r, (int)r, true, p.partial);
   c3.scales[0] = up->scale;
   c3.dest[0] = gr->dB_up;
-  LAUNCHN("rowcol", st, launch_rowcol(c.bf16, c3, r2, p.rpartial, st));
+  c3.rpartial = p.rpartial;
   RowProjArgs r3 = rowproj_args(p.de, I, T, I, gate->B, I, (int)r, (int)(RLg - r), (int)r);
   r3.scales[0] = gate->scale;
   r3.out2 = offw(p.Ps_ug, r, c);
   r3.ld2 = RLg;
-  ColProjArgs c4 = colproj_args(c, p.de, I, T, I, U, 3 * r, (int)r, (int)r, true, p.partial);
+  ColProjArgs c4 = colproj_args(c, p.de, I, T, I, U, 3 * r, (int)r, (int)r, true, part_de);
   c4.scales[0] = gate->scale;
   c4.dest[0] = gr->dB_gate;
-  LAUNCHN("rowcol", st, launch_rowcol(c.bf16, c4, r3, p.rpartial, st));
+  c4.rpartial = rc_fused ? p.rpartial + rowcol_partial_floats(T, I) : p.rpartial;
+  const ColProjArgs cb[2] = {c3, c4};
+  const RowProjArgs rb[2] = {r2, r3};
+  LAUNCHN("rowcol", st, launch_rowcol_batch(c.bf16, cb, rb, 2, st));
 
   // [dA_u | dA_g] = X^T [s_u P_u | s_g P_g] in one pass over X
   ColProjArgs c5 = colproj_args(c, X, H, T, H, p.Ps_ug, RLg, (int)(2 * r), (int)r, false, p.partial);
@@ -1499,17 +1518,29 @@ lora_status lora_qkv_bwd(const lora_qkv_desc* d, const void* dQ, const void* dK,
 
   // one pass over each dZ_p: P_p = dZ_p B_p^T, formed once into
   // [s_q P_q | s_k P_k | s_v P_v], and dB_p = s_p U_p^T dZ_p
+  // (the three passes in one launch, each with scratch of its own)
+  RowProjArgs rb[3];
+  ColProjArgs cb[3];
+  float* cpart = p.partial;
+  float* rpart = p.rpartial;
   for (int i = 0; i < 3; ++i) {
     const int R2 = (i == 2) ? (int)(RL - 2 * r) : (int)r;
     RowProjArgs ra = rowproj_args(dZ[i], Ns[i], T, Ns[i], projs[i]->B, Ns[i], (int)r, R2, (int)r);
     ra.scales[0] = projs[i]->scale;
     ra.out2 = offw(p.Ps, i * r, c);
     ra.ld2 = RL;
-    ColProjArgs ca = colproj_args(c, dZ[i], Ns[i], T, Ns[i], coff(U, i * r, c), 3 * r, (int)r, (int)r, true, p.partial);
+    ColProjArgs ca = colproj_args(c, dZ[i], Ns[i], T, Ns[i], coff(U, i * r, c), 3 * r, (int)r, (int)r, true, cpart);
     ca.scales[0] = projs[i]->scale;
     ca.dest[0] = dBs[i];
-    LAUNCHN("rowcol", st, launch_rowcol(c.bf16, ca, ra, p.rpartial, st));
+    ca.rpartial = rpart;
+    rb[i] = ra;
+    cb[i] = ca;
+    if (c.bf16) {
+      cpart += rowcol_batch_partial_floats(T, Ns, 3, i);
+      rpart += rowcol_partial_floats(T, Ns[i]);
+    }
   }
+  LAUNCHN("rowcol", st, launch_rowcol_batch(c.bf16, cb, rb, 3, st));
   // [dA_q | dA_k | dA_v] = X^T [s P] in one pass over X
   ColProjArgs cx = colproj_args(c, X, H, T, H, p.Ps, RL, (int)(3 * r), (int)r, false, p.partial);
   cx.scales[0] = cx.scales[1] = cx.scales[2] = 1.0f;

@@ -166,6 +166,23 @@ int64_t rowcol_partial_floats(int64_t T, int64_t K);
 int64_t colproj_partial_floats(int64_t T, int64_t K, int R);
 int colproj_nchunk(int64_t T, int64_t K);
 
+// Up to three rowcol passes (gradients of the same T, e.g. dQ, dK, dV) in
+// one launch plus one launch of both reduces.  Segment s has its own
+// scratch: c[s].rpartial [ceil(K_s / 256), T, 16] and c[s].partial
+// [nchunk, K_s, 16] fp32, nchunk = rowcol_batch_nchunk(T, K, n) for all
+// segments.  Cases launch_rowcol would not fuse, or T = 0, run launch_rowcol
+// per segment with the same scratch.
+struct RowColBatch {
+  ColProjArgs c[3];
+  RowProjArgs r[3];
+  int32_t kb0[4];  // first column block of each segment; kb0[n] = all blocks
+  int32_t n, pad_;
+};
+hipError_t launch_rowcol_batch(bool bf16, const ColProjArgs* c, const RowProjArgs* r, int n, hipStream_t st);
+int rowcol_batch_nchunk(int64_t T, const int64_t* K, int n);
+// floats of segment s's colproj partial in a batch
+int64_t rowcol_batch_partial_floats(int64_t T, const int64_t* K, int n, int s);
+
 // ---------------------------------------------------------------------------
 // Packing of the adapter operands in the layout the kernels read.  A job
 // builds the operand of a LoRA K tile over vcols virtual columns and RL rows

@@ -214,15 +214,16 @@ struct ColProjCfg {
 // 512 bytes, chunk c of row j at c ^ j) and from there into registers; per
 // step, wavefronts 0, 1 (even steps) or 2, 3 (odd steps) each take one
 // 16-row half with 8 16x16x32 MFMAs, reading Z K-contiguously from the slot.
+// Column block kb of a (the block's 256 columns of Z), row chunk blockIdx.y.
 template <int NJ, bool ROW>
-__global__ __launch_bounds__(256) void colproj_bf16_kernel(const ColProjArgs a, int64_t rows_per_chunk) {
+__device__ __forceinline__ void colproj_body(const ColProjArgs& a, int64_t rows_per_chunk, int64_t kb) {
   using C = ColProjCfg<NJ>;
   constexpr int BTB = ROW ? 8192 : 0;  // Bt slice after the ring
   __shared__ __attribute__((aligned(1024))) char ring[C::NST * C::SB + BTB];
   lds_char* const lds = (lds_char*)ring;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t k0 = (int64_t)blockIdx.x * 256;
+  const int64_t k0 = kb * 256;
   const int64_t c = blockIdx.y;
   const int64_t tbeg = c * rows_per_chunk;
   const int64_t tend = tbeg + rows_per_chunk < a.T ? tbeg + rows_per_chunk : a.T;
@@ -303,7 +304,7 @@ __global__ __launch_bounds__(256) void colproj_bf16_kernel(const ColProjArgs a, 
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int64_t t = tbeg + 32 * (int64_t)s + rb * 16 + 4 * (lane >> 4) + v;
-        if (t < tend) a.rpartial[((int64_t)blockIdx.x * a.T + t) * 16 + (lane & 15)] = acc_r[v];
+        if (t < tend) a.rpartial[(kb * a.T + t) * 16 + (lane & 15)] = acc_r[v];
       }
     }
   };
@@ -357,6 +358,20 @@ __global__ __launch_bounds__(256) void colproj_bf16_kernel(const ColProjArgs a, 
       }
 }
 
+template <int NJ, bool ROW>
+__global__ __launch_bounds__(256) void colproj_bf16_kernel(const ColProjArgs a, int64_t rows_per_chunk) {
+  colproj_body<NJ, ROW>(a, rows_per_chunk, blockIdx.x);
+}
+
+// Fused rank-r passes over up to three gradients of the same T in one launch:
+// the column blocks of segment s are kb0[s] .. kb0[s + 1] - 1.
+__global__ __launch_bounds__(256) void rowcol_batch_kernel(const RowColBatch b, int64_t rows_per_chunk) {
+  int s = 0;
+  for (int i = 1; i < b.n; ++i)
+    if ((int)blockIdx.x >= b.kb0[i]) s = i;
+  colproj_body<1, true>(b.c[s], rows_per_chunk, (int64_t)blockIdx.x - b.kb0[s]);
+}
+
 __device__ __forceinline__ void colproj_store(const ColProjArgs& a, bool bf16, int64_t k, int j, float v) {
   const int q = j / a.seg_w, jj = j % a.seg_w;
   const float o = a.scales[q] * v;
@@ -390,11 +405,11 @@ __device__ __forceinline__ f32x4 sum_slices(const float* src, int64_t stride, in
   return v;
 }
 
-__global__ __launch_bounds__(256) void colproj_reduce_kernel(const ColProjArgs a, int Rp) {
+__device__ __forceinline__ void colproj_reduce_body(const ColProjArgs& a, int Rp, int64_t bx) {
   __shared__ f32x4 part[RED_PARTS][64];
   const int RQ = a.R / 4;
   const int pq = threadIdx.x >> 6, o = threadIdx.x & 63;
-  const int64_t e = (int64_t)blockIdx.x * 64 + o;
+  const int64_t e = bx * 64 + o;
   const bool live = e < a.K * RQ;
   const int64_t k = live ? e / RQ : 0;
   const int j0 = live ? (int)(e % RQ) * 4 : 0;
@@ -408,6 +423,9 @@ __global__ __launch_bounds__(256) void colproj_reduce_kernel(const ColProjArgs a
   for (int q = 1; q < RED_PARTS; ++q) v += part[q][o];
 #pragma unroll
   for (int q = 0; q < 4; ++q) colproj_store(a, a.out_f32 == 0, k, j0 + q, v[q]);
+}
+__global__ __launch_bounds__(256) void colproj_reduce_kernel(const ColProjArgs a, int Rp) {
+  colproj_reduce_body(a, Rp, blockIdx.x);
 }
 
 __global__ void colproj_f32_kernel(const ColProjArgs a) {
@@ -463,15 +481,35 @@ inline unsigned nblk(int64_t n, int b) { return (unsigned)((n + b - 1) / b); }
 
 }  // namespace
 
-int colproj_nchunk(int64_t T, int64_t K) {
+namespace {
+// chunks of T for a colproj grid of kblocks column blocks
+int nchunk_for(int64_t T, int64_t kblocks) {
   const int64_t steps = (T + 31) / 32;
   if (steps == 0) return 0;
-  const int64_t kblocks = (K + 255) / 256;
   // at most one round of two blocks per CU: a partial second round would run
   // its few blocks while most CUs idle
   int64_t want = 512 / kblocks;
   if (want < 1) want = 1;
   return (int)(want < steps ? want : steps);
+}
+// the chunk count after rounding the chunk to whole 32-row steps
+int nchunk_rounded(int64_t T, int nchunk, int64_t* rows_per_chunk) {
+  const int64_t steps = (T + 31) / 32;
+  const int64_t spc = (steps + nchunk - 1) / nchunk;
+  *rows_per_chunk = spc * 32;
+  return (int)((T + *rows_per_chunk - 1) / *rows_per_chunk);
+}
+}  // namespace
+
+int colproj_nchunk(int64_t T, int64_t K) { return nchunk_for(T, (K + 255) / 256); }
+
+int rowcol_batch_nchunk(int64_t T, const int64_t* K, int n) {
+  int64_t kb = 0;
+  for (int i = 0; i < n; ++i) kb += (K[i] + 255) / 256;
+  return nchunk_for(T, kb);
+}
+int64_t rowcol_batch_partial_floats(int64_t T, const int64_t* K, int n, int s) {
+  return (int64_t)rowcol_batch_nchunk(T, K, n) * K[s] * 16;
 }
 
 int64_t colproj_partial_floats(int64_t T, int64_t K, int R) {
@@ -541,11 +579,11 @@ namespace {
 // ranges as in colproj_reduce_kernel (ascending within a range, ranges added
 // in ascending order); the quad-0 threads also write the zero padding of
 // out2 past 16.
-__global__ __launch_bounds__(256) void rowproj_reduce_kernel(const RowProjArgs a, const float* rpartial, int nb) {
+__device__ __forceinline__ void rowproj_reduce_body(const RowProjArgs& a, const float* rpartial, int nb, int64_t bx) {
   __shared__ f32x4 part[RED_PARTS][64];
   const int R2 = a.R2 > a.R ? a.R2 : a.R;
   const int pq = threadIdx.x >> 6, o = threadIdx.x & 63;
-  const int64_t e = (int64_t)blockIdx.x * 64 + o;
+  const int64_t e = bx * 64 + o;
   const bool live = e < a.T * 4;
   const int64_t t = e >> 2;
   const int j0 = (o & 3) * 4;
@@ -572,6 +610,20 @@ __global__ __launch_bounds__(256) void rowproj_reduce_kernel(const RowProjArgs a
   if (a.out2 && j0 == 0)
     for (int j = 16; j < R2; ++j) static_cast<uint16_t*>(a.out2)[t * a.ld2 + j] = 0;
 }
+__global__ __launch_bounds__(256) void rowproj_reduce_kernel(const RowProjArgs a, const float* rpartial, int nb) {
+  rowproj_reduce_body(a, rpartial, nb, blockIdx.x);
+}
+// Both reduces of a rowcol batch: blockIdx.y < n the colproj reduce (dB) of
+// segment y, else the rowproj reduce (P) of segment y - n.
+__global__ __launch_bounds__(256) void rowcol_batch_reduce_kernel(const RowColBatch b) {
+  const int y = blockIdx.y;
+  if (y < b.n) {
+    colproj_reduce_body(b.c[y], 16, blockIdx.x);
+  } else {
+    const int s = y - b.n;
+    rowproj_reduce_body(b.r[s], b.c[s].rpartial, b.kb0[s + 1] - b.kb0[s], blockIdx.x);
+  }
+}
 }  // namespace
 
 int64_t rowcol_partial_floats(int64_t T, int64_t K) { return ((K + 255) / 256) * T * 16; }
@@ -595,6 +647,47 @@ hipError_t launch_rowcol(bool bf16, const ColProjArgs& c0, const RowProjArgs& r,
   (void)R2;
   hipLaunchKernelGGL(rowproj_reduce_kernel, dim3(nblk(r.T * 4, 64)), dim3(256), 0, st, r, rpartial,
                      (int)((r.K + 255) / 256));
+  return hipGetLastError();
+}
+
+hipError_t launch_rowcol_batch(bool bf16, const ColProjArgs* c, const RowProjArgs* r, int n, hipStream_t st) {
+  if (n < 1 || n > 3) return hipErrorInvalidValue;
+  bool fused = bf16 && c[0].T > 0;
+  for (int i = 0; i < n && fused; ++i)
+    fused = c[i].rpartial != nullptr && r[i].R <= 16 && r[i].Z == c[i].Z && r[i].ldz == c[i].ldz &&
+            r[i].T == c[i].T && r[i].K == c[i].K && r[i].K % 8 == 0 && c[i].R <= 16 && c[i].T == c[0].T;
+  if (!fused) {
+    for (int i = 0; i < n; ++i) {
+      const hipError_t e = launch_rowcol(bf16, c[i], r[i], c[i].rpartial, st);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  RowColBatch b{};
+  b.n = n;
+  int64_t K[3];
+  unsigned rx = nblk(c[0].T * 4, 64);  // reduce blocks: the rowproj side
+  for (int i = 0; i < n; ++i) {
+    K[i] = c[i].K;
+    b.kb0[i + 1] = b.kb0[i] + (int32_t)((c[i].K + 255) / 256);
+    const unsigned cx = nblk(c[i].K * (c[i].R / 4), 64);
+    rx = cx > rx ? cx : rx;
+  }
+  int64_t rows_per_chunk = 0;
+  const int nchunk = nchunk_rounded(c[0].T, rowcol_batch_nchunk(c[0].T, K, n), &rows_per_chunk);
+  for (int i = 0; i < n; ++i) {
+    b.c[i] = c[i];
+    b.c[i].Bt = r[i].Bt;
+    b.c[i].ldb = r[i].ldb;
+    b.c[i].R1 = r[i].R;
+    b.c[i].nchunk = nchunk;
+    b.r[i] = r[i];
+  }
+  hipLaunchKernelGGL(rowcol_batch_kernel, dim3((unsigned)b.kb0[n], (unsigned)nchunk), dim3(256), 0, st, b,
+                     rows_per_chunk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(rowcol_batch_reduce_kernel, dim3(rx, (unsigned)(2 * n)), dim3(256), 0, st, b);
   return hipGetLastError();
 }
 
