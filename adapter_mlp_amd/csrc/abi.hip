@@ -591,9 +591,11 @@ lora_status validate_qkv(const lora_qkv_desc* d, Ctx& c) {
   TRY(check_dim(c, d->Nk, "Nk"));
   TRY(check_dim(c, d->Nv, "Nv"));
   TRY(check_rank(c, d->r, 3));
-  const int64_t nmax = d->H > d->Nq ? d->H : d->Nq;
-  TRY(check_extent(c, d->T, nmax, "an activation"));
-  TRY(check_extent(c, d->H, d->Nq, "a weight"));
+  // the widest of X, dX and the three outputs / their gradients, and the widest weight
+  int64_t nout = d->Nq > d->Nk ? d->Nq : d->Nk;
+  nout = nout > d->Nv ? nout : d->Nv;
+  TRY(check_extent(c, d->T, d->H > nout ? d->H : nout, "an activation"));
+  TRY(check_extent(c, d->H, nout, "a weight"));
   return LORA_OK;
 }
 

@@ -57,6 +57,9 @@
  *   the concatenated adapter width of a shared-input group (2r for gate/up,
  *   3r for Q/K/V) at most 64.  Pointers must be 16-byte aligned.
  * Shapes (fp32).  Any positive widths, 1 <= r <= 64; 4-byte aligned pointers.
+ * Extent (all dtypes).  The kernels address each operand with 32-bit byte
+ *   offsets: every activation [T, width] and every weight must be smaller
+ *   than 2 GiB - 4 KiB, else the call returns LORA_ESHAPE.
  * No dropout and no bias on the adapters ([LO] "Requirements").
  */
 #ifndef LORA_MI355X_H

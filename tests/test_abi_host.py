@@ -151,6 +151,13 @@ def test_qkv_o_validation(L):
     assert _status(L, "lora_qkv_workspace_size", C.byref(d), C.byref(f), C.byref(b)) == L.LORA_EINVAL
     d = L.lora_o_desc(0, 4096, 4096, 16, L.LORA_BF16, 0)
     assert _status(L, "lora_o_workspace_size", C.byref(d), C.byref(f), C.byref(b)) == L.LORA_OK
+    # every operand below 2 GiB: V [T, Nv] with Nv the widest width decides it
+    d = L.lora_qkv_desc(65536, 4096, 4096, 1024, 16384, 16, L.LORA_BF16, 0)  # V: 2 GiB
+    assert _status(L, "lora_qkv_workspace_size", C.byref(d), C.byref(f), C.byref(b)) == L.LORA_ESHAPE
+    d = L.lora_qkv_desc(65535, 4096, 4096, 1024, 16384, 16, L.LORA_BF16, 0)
+    assert _status(L, "lora_qkv_workspace_size", C.byref(d), C.byref(f), C.byref(b)) == L.LORA_OK
+    d = L.lora_qkv_desc(64, 4096, 64, 64, 262144, 16, L.LORA_BF16, 0)  # W_v [4096, 262144]: 2 GiB
+    assert _status(L, "lora_qkv_workspace_size", C.byref(d), C.byref(f), C.byref(b)) == L.LORA_ESHAPE
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
