@@ -114,6 +114,33 @@ def test_qkv_o_bf16_ragged(lm):
     _qkv_case(lm, cfg)
 
 
+@pytest.mark.parametrize("T", [0, 1, 257])
+def test_qkv_o_edge_token_counts(lm, T):
+    # one token, a ragged 257, and T = 0, which must still overwrite every
+    # adapter gradient with zeros (the three rank-r passes run batched)
+    import torch
+
+    cfg = WorkloadConfig(92, "attn", T=T, H=256, r=16, alpha=32, dtype="bf16", Nq=256, Nk=128, Nv=64)
+    if T > 0:
+        _qkv_case(lm, cfg)
+        return
+    inp = make_attn_inputs(cfg)
+    X = dev(inp["X"])
+    q, k, v = (proj_dev(inp[n]) for n in ("q", "k", "v"))
+    Q, K, V, U = lm.qkv_fwd(X, q, k, v)
+    grads = {f"d{ab}_{n}": torch.full_like(getattr(p, ab), 7.0) for n, p in (("q", q), ("k", k), ("v", v))
+             for ab in ("A", "B")}
+    dX, grads = lm.qkv_bwd(*(dev(inp[n]) for n in ("dQ", "dK", "dV")), X, U, q, k, v, grads=grads)
+    o = proj_dev(inp["o"])
+    Xo = dev(inp["Xo"])
+    Yo, Uo = lm.o_fwd(Xo, o)
+    dA, dB = torch.full_like(o.A, 7.0), torch.full_like(o.B, 7.0)
+    lm.o_bwd(dev(inp["dO"]), Xo, Uo, o, dA=dA, dB=dB)
+    torch.cuda.synchronize()
+    for name, t in list(grads.items()) + [("dA_o", dA), ("dB_o", dB)]:
+        assert torch.all(t == 0), name
+
+
 def test_qkv_o_fp32(lm):
     cfg = WorkloadConfig(94, "attn", T=50, H=96, r=4, alpha=8, dtype="f32", Nq=96, Nk=32, Nv=40)
     _qkv_case(lm, cfg)
