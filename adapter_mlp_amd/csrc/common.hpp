@@ -65,35 +65,46 @@ __device__ __forceinline__ float dev_rcp(float x) {
   else return __builtin_amdgcn_rcpf(x);
 }
 
+// GeGLU-tanh terms shared by the forward and the backward, so that both form
+// phi(x) with the same operations: c x, u = c x (1 + k x^2), t = tanh u and
+// a = (1 + t) / 2 (phi = x a).
 template <bool ACCURATE>
-__device__ __forceinline__ void act_fwd(int act, float x, float& phi) {
-  if (act == LORA_ACT_SWIGLU) {
-    float s = dev_rcp<ACCURATE>(1.0f + dev_exp<ACCURATE>(-x));
-    phi = x * s;
-  } else {
-    const float c = 0.7978845608028654f, k = 0.044715f;
-    float u = c * (x + k * x * x * x);
-    float t;
-    if constexpr (ACCURATE) t = tanhf(u);
-    else t = 1.0f - 2.0f * dev_rcp<ACCURATE>(dev_exp<ACCURATE>(2.0f * u) + 1.0f);
-    phi = 0.5f * x * (1.0f + t);
-  }
+__device__ __forceinline__ void geglu_terms(float x, float& x2, float& cx, float& t, float& a) {
+  const float c = 0.7978845608028654f, k = 0.044715f;
+  x2 = x * x;
+  cx = c * x;
+  const float u = cx * fmaf(k, x2, 1.0f);
+  if constexpr (ACCURATE) t = tanhf(u);
+  else t = fmaf(-2.0f, dev_rcp<ACCURATE>(dev_exp<ACCURATE>(2.0f * u) + 1.0f), 1.0f);
+  a = fmaf(0.5f, t, 0.5f);
 }
 
 template <bool ACCURATE>
+__device__ __forceinline__ void act_fwd(int act, float x, float& phi) {
+  if (act == LORA_ACT_SWIGLU) {
+    const float s = dev_rcp<ACCURATE>(1.0f + dev_exp<ACCURATE>(-x));
+    phi = x * s;
+  } else {
+    float x2, cx, t, a;
+    geglu_terms<ACCURATE>(x, x2, cx, t, a);
+    phi = x * a;
+  }
+}
+
+// phi' as phi + (its derivative's remaining term): SwiGLU s (1 + x (1 - s)) =
+// s + phi (1 - s); GeGLU a + x (1 - t^2)/2 c (1 + 3 k x^2) = a + c x (1 - t) a (1 + 3 k x^2).
+template <bool ACCURATE>
 __device__ __forceinline__ void act_fwd_bwd(int act, float x, float& phi, float& dphi) {
   if (act == LORA_ACT_SWIGLU) {
-    float s = dev_rcp<ACCURATE>(1.0f + dev_exp<ACCURATE>(-x));
+    const float s = dev_rcp<ACCURATE>(1.0f + dev_exp<ACCURATE>(-x));
     phi = x * s;
-    dphi = s * (1.0f + x * (1.0f - s));
+    dphi = fmaf(phi, 1.0f - s, s);
   } else {
-    const float c = 0.7978845608028654f, k = 0.044715f;
-    float u = c * (x + k * x * x * x);
-    float t;
-    if constexpr (ACCURATE) t = tanhf(u);
-    else t = 1.0f - 2.0f * dev_rcp<ACCURATE>(dev_exp<ACCURATE>(2.0f * u) + 1.0f);
-    phi = 0.5f * x * (1.0f + t);
-    dphi = 0.5f * (1.0f + t) + 0.5f * x * (1.0f - t * t) * c * (1.0f + 3.0f * k * x * x);
+    const float k = 0.044715f;
+    float x2, cx, t, a;
+    geglu_terms<ACCURATE>(x, x2, cx, t, a);
+    phi = x * a;
+    dphi = fmaf(cx * (1.0f - t) * a, fmaf(3.0f * k, x2, 1.0f), a);
   }
 }
 
