@@ -555,6 +555,63 @@ def test_mlp_B_zero_gives_zero_dA_and_base_output(lm):
     assert_close("Y", host(Y), Yr, TOL["bf16"])
 
 
+@pytest.mark.parametrize("case", ["A_zero", "s_zero"])
+def test_mlp_A_zero_or_scale_zero(lm, case):
+    # A = 0: U = 0, so every dB is exactly zero while dA = s X^T (dZ B^T) is not;
+    # s = 0: the adapter term, every dA and every dB vanish exactly.  The rest
+    # is compared with the oracle.
+    import torch
+
+    cfg = WorkloadConfig(101, "mlp", T=300, H=256, I=384, r=16, alpha=32, dtype="bf16")
+    inp = make_mlp_inputs(cfg)
+    for k in ("gate", "up", "down"):
+        if case == "A_zero":
+            inp[k]["A"] = np.zeros_like(inp[k]["A"])
+        else:
+            inp[k]["s"] = 0.0
+    X, dY = dev(inp["X"]), dev(inp["dY"])
+    g, u, d = (proj_dev(inp[k]) for k in ("gate", "up", "down"))
+    Y, saved = lm.mlp_fwd(X, g, u, d)
+    dX, grads = lm.mlp_bwd(dY, X, saved, g, u, d)
+    torch.cuda.synchronize()
+    zero = ("dB_gate", "dB_up", "dB_down") + (("dA_gate", "dA_up", "dA_down") if case == "s_zero" else ())
+    for kk in zero:
+        assert torch.all(grads[kk] == 0), kk
+    Yr, sr = OL.mlp_fwd(inp["X"], inp["gate"], inp["up"], inp["down"])
+    gr = OL.mlp_bwd(inp["dY"], inp["X"], sr, inp["gate"], inp["up"], inp["down"])
+    assert_close("Y", host(Y), Yr, TOL["bf16"])
+    assert_close("dX", host(dX), gr["dX"], TOL["bf16"])
+    if case == "A_zero":
+        for k_dev, k_ref in (("dA_gate", "dA_g"), ("dA_up", "dA_u"), ("dA_down", "dA_d")):
+            assert_close(k_dev, host(grads[k_dev]), gr[k_ref], TOL["bf16"])
+
+
+def test_mlp_token_permutation(lm):
+    # Rows are independent: permuting the tokens permutes the rows of Y, e, g
+    # and dX bit for bit; dA and dB change only by their summation order.
+    import torch
+
+    cfg = WorkloadConfig(102, "mlp", T=700, H=256, I=640, r=16, alpha=32, dtype="bf16")
+    inp = make_mlp_inputs(cfg)
+    perm = np.random.default_rng(7).permutation(cfg.T)
+    g, u, d = (proj_dev(inp[k]) for k in ("gate", "up", "down"))
+    out = []
+    for rows in (np.arange(cfg.T), perm):
+        X, dY = dev(inp["X"][rows]), dev(inp["dY"][rows])
+        Y, saved = lm.mlp_fwd(X, g, u, d)
+        dX, grads = lm.mlp_bwd(dY, X, saved, g, u, d)
+        torch.cuda.synchronize()
+        out.append((Y, saved, dX, grads))
+    (Y0, s0, dX0, g0), (Y1, s1, dX1, g1) = out
+    idx = torch.from_numpy(perm).to("cuda:0")
+    assert torch.equal(Y0[idx], Y1)
+    assert torch.equal(s0["e"][idx], s1["e"])
+    assert torch.equal(s0["g"][idx], s1["g"])
+    assert torch.equal(dX0[idx], dX1)
+    for kk in g0:
+        assert_close(kk, host(g1[kk]), host(g0[kk]), TOL["bf16"])
+
+
 def test_deterministic_repeat(lm):
     import torch
 
