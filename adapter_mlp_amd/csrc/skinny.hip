@@ -643,8 +643,6 @@ hipError_t launch_rowcol(bool bf16, const ColProjArgs& c0, const RowProjArgs& r,
   c.rpartial = rpartial;
   hipError_t e = launch_colproj(true, c, st);
   if (e != hipSuccess) return e;
-  const int R2 = r.R2 > r.R ? r.R2 : r.R;
-  (void)R2;
   hipLaunchKernelGGL(rowproj_reduce_kernel, dim3(nblk(r.T * 4, 64)), dim3(256), 0, st, r, rpartial,
                      (int)((r.K + 255) / 256));
   return hipGetLastError();
