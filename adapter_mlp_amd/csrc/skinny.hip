@@ -634,7 +634,10 @@ hipError_t launch_rowcol(bool bf16, const ColProjArgs& c0, const RowProjArgs& r,
   if (!fused) {
     hipError_t e = launch_rowproj(bf16, r, st);
     if (e != hipSuccess) return e;
-    return launch_colproj(bf16, c0, st);
+    // the plain colproj: a set rpartial would select the fused (R <= 16) kernel
+    ColProjArgs c = c0;
+    c.rpartial = nullptr;
+    return launch_colproj(bf16, c, st);
   }
   ColProjArgs c = c0;
   c.Bt = r.Bt;

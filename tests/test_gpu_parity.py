@@ -60,6 +60,13 @@ def test_mlp_bf16_ragged(lm, act):
     _mlp_case(lm, cfg, act)
 
 
+def test_mlp_bf16_rank32(lm):
+    # r = 32 (2r = 64, the widest gate/up adapter group): the dg / de rank-r
+    # passes do not fuse and run one after the other on shared scratch
+    cfg = WorkloadConfig(89, "mlp", T=300, H=512, I=1088, r=32, alpha=16, dtype="bf16", act="swiglu")
+    _mlp_case(lm, cfg, "swiglu")
+
+
 def test_mlp_bf16_rank8_scale_not_power_of_two(lm):
     cfg = WorkloadConfig(91, "mlp", T=200, H=256, I=640, r=8, alpha=12, dtype="bf16", act="swiglu")
     _mlp_case(lm, cfg, "swiglu")
