@@ -67,6 +67,13 @@ def test_mlp_bf16_rank32(lm):
     _mlp_case(lm, cfg, "swiglu")
 
 
+def test_mlp_bf16_rank24(lm):
+    # a rank that is not a multiple of 16: partial 16-column blocks in the
+    # unfused rank-r products
+    cfg = WorkloadConfig(88, "mlp", T=200, H=256, I=640, r=24, alpha=24, dtype="bf16", act="geglu_tanh")
+    _mlp_case(lm, cfg, "geglu_tanh")
+
+
 def test_mlp_bf16_rank8_scale_not_power_of_two(lm):
     cfg = WorkloadConfig(91, "mlp", T=200, H=256, I=640, r=8, alpha=12, dtype="bf16", act="swiglu")
     _mlp_case(lm, cfg, "swiglu")
@@ -146,6 +153,28 @@ def test_qkv_o_edge_token_counts(lm, T):
     torch.cuda.synchronize()
     for name, t in list(grads.items()) + [("dA_o", dA), ("dB_o", dB)]:
         assert torch.all(t == 0), name
+
+
+@pytest.mark.parametrize("r", [40, 64])
+def test_o_bf16_wide_rank(lm, r):
+    # the single projection takes ranks up to 64 (three and four 16-column blocks)
+    import torch
+
+    cfg = WorkloadConfig(91, "attn", T=300, H=512, r=r, alpha=32, dtype="bf16", Nq=384, Nk=64, Nv=64)
+    inp = make_attn_inputs(cfg)
+    Xo = dev(inp["Xo"])
+    o = proj_dev(inp["o"])
+    Yo, Uo = lm.o_fwd(Xo, o)
+    dXo, dAo, dBo = lm.o_bwd(dev(inp["dO"]), Xo, Uo, o)
+    torch.cuda.synchronize()
+    Yr, so = OL.o_fwd(inp["Xo"], inp["o"])
+    go = OL.o_bwd(inp["dO"], inp["Xo"], so, inp["o"])
+    tol = TOL["bf16"]
+    assert_close("O", host(Yo), Yr, tol)
+    assert_close("U_o", host(Uo), so["U"], tol)
+    assert_close("dX_o", host(dXo), go["dX"], tol)
+    assert_close("dA_o", host(dAo), go["dA"], tol)
+    assert_close("dB_o", host(dBo), go["dB"], tol)
 
 
 def test_qkv_o_fp32(lm):
@@ -235,6 +264,12 @@ def test_relu2_mlp_bf16_maximum_extent(lm):
     assert_close("dX", host(dX), dXr, tol)
     for k_dev, k_ref in gkeys:
         assert_close(k_dev, host(grads[k_dev]), sums[k_ref], tol)
+
+
+def test_relu2_mlp_bf16_rank64(lm):
+    # the widest adapter: four 16-column blocks in every rank-r product
+    cfg = WorkloadConfig(87, "relu2", T=260, H=256, I=512, r=64, alpha=64, dtype="bf16")
+    _relu2_case(lm, cfg)
 
 
 def test_relu2_mlp_bf16_rank32(lm):
