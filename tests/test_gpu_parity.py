@@ -318,13 +318,14 @@ def test_relu2_mlp_edge_token_counts(lm, T):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("act", ["swiglu", "geglu_tanh"])
-def test_fp32_lora_mode_mlp(lm, act):
+@pytest.mark.parametrize("r", [16, 32])
+def test_fp32_lora_mode_mlp(lm, act, r):
     """Against the oracle fed the adapters as the mode casts them (bf16), and
     against the bf16 mode on the same casts: the forward outputs must agree
     bit for bit and the mode's fp32 gradients must round to the bf16 mode's."""
     import torch
 
-    cfg = WorkloadConfig(95, "mlp", T=300, H=512, I=1088, r=16, alpha=32, dtype="bf16", act=act,
+    cfg = WorkloadConfig(95, "mlp", T=300, H=512, I=1088, r=r, alpha=32, dtype="bf16", act=act,
                          lora_dtype="f32")
     inp = make_mlp_inputs(cfg)
     X, dY = dev(inp["X"]), dev(inp["dY"])
