@@ -456,10 +456,11 @@ def test_nf4_quantize_fp32_input_bitexact(lm):
 
 
 @pytest.mark.parametrize("act", ["swiglu", "geglu_tanh"])
-def test_qlora_mlp_bf16(lm, act):
+@pytest.mark.parametrize("r", [16, 32])
+def test_qlora_mlp_bf16(lm, act, r):
     import torch
 
-    cfg = WorkloadConfig(97, "mlp", T=300, H=512, I=1024, r=16, alpha=32, dtype="bf16", act=act, nf4=True)
+    cfg = WorkloadConfig(97, "mlp", T=300, H=512, I=1024, r=r, alpha=32, dtype="bf16", act=act, nf4=True)
     inp = make_mlp_inputs(cfg)
     nf4 = {k: _nf4_dev(lm, inp[k]["W"]) for k in ("gate", "up", "down")}
     for k in nf4:
