@@ -123,8 +123,9 @@ def _qkv_case(lm, cfg):
     assert_close("dB_o", host(dBo), go["dB"], tol)
 
 
-def test_qkv_o_bf16_ragged(lm):
-    cfg = WorkloadConfig(93, "attn", T=300, H=512, r=16, alpha=32, dtype="bf16", Nq=512, Nk=192, Nv=128)
+@pytest.mark.parametrize("r", [8, 16])
+def test_qkv_o_bf16_ragged(lm, r):
+    cfg = WorkloadConfig(93, "attn", T=300, H=512, r=r, alpha=32, dtype="bf16", Nq=512, Nk=192, Nv=128)
     _qkv_case(lm, cfg)
 
 
