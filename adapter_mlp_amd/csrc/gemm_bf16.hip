@@ -63,13 +63,15 @@ __device__ __forceinline__ void wave_sync() {
 
 // Block -> tile.  Workgroups are dispatched round-robin over the 8 XCDs, so
 // block b runs on XCD b % 8.  Re-number blocks so that each XCD receives a
-// contiguous run of logical tiles, and walk logical tiles in groups of 8
-// m-tiles (n-major inside a group) so the 32 tiles an XCD holds at once share
-// 8 activation panels and 4 weight panels in its L2.
+// contiguous run of logical tiles, and walk logical tiles in groups of G
+// m-tiles (n-major inside a group): the 32 tiles an XCD holds at once then
+// share G activation panels and 32 / G weight panels in its L2 (8 x 4 or
+// 4 x 8 panels fetch the same bytes; measured, groups of 4 suit the
+// activation-epilogue GEMMs and groups of 8 the store GEMMs).
+template <int G>
 __device__ __forceinline__ void tile_coords(int bid, int nb, int ntm, int ntn, int& tm, int& tn) {
   const int q = nb >> 3, rem = nb & 7, x = bid & 7, j = bid >> 3;
   const int lid = (x < rem) ? x * (q + 1) + j : rem * (q + 1) + (x - rem) * q + j;
-  const int G = 8;
   const int per_group = G * ntn;
   const int grp = lid / per_group;
   const int first_m = grp * G;
@@ -585,7 +587,8 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   // split-K: block u works on K part u / ntiles of tile u % ntiles
   const int ntiles = (int)(args.ntile_m * args.ntile_n);
   const int kp = args.ksplit > 1 ? (int)blockIdx.x / ntiles : 0;
-  tile_coords((int)blockIdx.x - kp * ntiles, ntiles, (int)args.ntile_m, (int)args.ntile_n, tm, tn);
+  tile_coords<EPI == EPI_STORE ? 8 : 4>((int)blockIdx.x - kp * ntiles, ntiles, (int)args.ntile_m,
+                                         (int)args.ntile_n, tm, tn);
   tm = __builtin_amdgcn_readfirstlane(tm);
   tn = __builtin_amdgcn_readfirstlane(tn);
   int reg = 0;
