@@ -1712,6 +1712,10 @@ lora_status lora_nf4_gemm_workspace_size(int64_t T, int64_t rows, int64_t cols, 
   TRY(check_dim(c, rows, "rows"));
   TRY(check_dim(c, cols, "cols"));
   if (r != 0) TRY(check_rank(c, r, 1));
+  // 32-bit operand offsets: the activations [T, rows | cols] and the weight
+  // (its dequantized bf16 extent bounds every NF4 array and element index)
+  TRY(check_extent(c, T, rows > cols ? rows : cols, "an activation"));
+  TRY(check_extent(c, rows, cols, "the weight"));
   OPlan p = plan_o(c, T, rows, cols, r, trans == 0, nullptr, nullptr);
   if (bytes) *bytes = trans ? p.bwd_bytes : p.fwd_bytes;
   return LORA_OK;

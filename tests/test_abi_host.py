@@ -139,6 +139,18 @@ def test_nf4_validation(L):
     assert st == L.LORA_ESHAPE
     st = _status(L, "lora_nf4_gemm_workspace_size", 64, 256, 768, 16, 2, C.byref(nbytes))
     assert st == L.LORA_EINVAL  # trans must be 0/1
+    # operands of 2 GiB or more (32-bit offsets): the activation [T, max(rows, cols)]
+    # and the weight, in the query and in the call itself
+    for trans in (0, 1):
+        st = _status(L, "lora_nf4_gemm_workspace_size", 1 << 20, 256, 1024, 16, trans, C.byref(nbytes))
+        assert st == L.LORA_ESHAPE
+        assert _status(L, "lora_nf4_gemm_workspace_size", 64, 1 << 15, 1 << 15, 0, trans, C.byref(nbytes)) == L.LORA_ESHAPE
+        assert _status(L, "lora_nf4_gemm_workspace_size", (1 << 20) - 16, 256, 1024, 16, trans,
+                       C.byref(nbytes)) == L.LORA_OK
+    qbig = L.lora_nf4(FAKE, FAKE, FAKE, FAKE, 256, 1024)
+    st = _status(L, "lora_nf4_gemm", 1 << 20, 0, FAKE, C.byref(qbig), None, None, 0, C.c_float(0.0), FAKE * 2,
+                 FAKE * 3, 1 << 40, None)
+    assert st == L.LORA_ESHAPE
 
 
 def test_qkv_o_validation(L):
@@ -216,9 +228,9 @@ def test_binding_picks_fp32_lora_mode_from_adapter_dtype():
                   W=torch.zeros(64, 64, dtype=torch.bfloat16))
     assert lm._call_dtype(X, (p32,)) == _lib.LORA_BF16_F32LORA
     assert lm._call_dtype(X, (p16,)) == _lib.LORA_BF16
-    with pytest.raises(TypeError):
+    with pytest.raises(ValueError):
         lm._call_dtype(X, (p32, p16))  # mixed adapter dtypes
-    with pytest.raises(TypeError):
+    with pytest.raises(ValueError):
         lm._call_dtype(X.float(), (p16,))  # bf16 adapters with fp32 inputs
 
 

@@ -29,16 +29,31 @@ def lm():
 
 
 def _mlp_case(lm, cfg, act, seed=None):
+    """Forward + backward of one gated MLP against the oracle.  With cfg.nf4
+    the three bases are NF4-quantized on the GPU (checked bit for bit against
+    the oracle quantizer) and the oracle runs on the dequantized weights; with
+    cfg.lora_dtype == "f32" the adapters are fp32 and the oracle multiplies
+    with them as the mode casts them."""
+    import torch
+
     inp = make_mlp_inputs(cfg, seed=seed)
     dt = cfg.dtype
     tol = TOL[dt]
+    nf = {}
+    if cfg.nf4:
+        for k in ("gate", "up", "down"):
+            nf[k] = _nf4_dev(lm, inp[k]["W"])
+            q = _check_nf4_bitexact(lm, inp[k]["W"], nf[k])
+            inp[k] = dict(inp[k], W=ON.dequantize(q, "bf16"))
+    ad = cfg.lora_dtype or None
     X, dY = dev(inp["X"], dt), dev(inp["dY"], dt)
-    g, u, d = (proj_dev(inp[k], dt) for k in ("gate", "up", "down"))
+    g, u, d = (proj_dev(inp[k], dt, nf4=nf.get(k), adapters=ad) for k in ("gate", "up", "down"))
     Y, saved = lm.mlp_fwd(X, g, u, d, act)
     dX, grads = lm.mlp_bwd(dY, X, saved, g, u, d, act)
-    import torch
-
     torch.cuda.synchronize()
+    if ad:
+        assert all(t.dtype == torch.float32 for t in grads.values())
+        inp = dict(inp, **{k: OL.to_compute_adapters(inp[k]) for k in ("gate", "up", "down")})
     Yr, sr = OL.mlp_fwd(inp["X"], inp["gate"], inp["up"], inp["down"], act)
     gr = OL.mlp_bwd(inp["dY"], inp["X"], sr, inp["gate"], inp["up"], inp["down"], act)
     assert_close("Y", host(Y), Yr, tol)
@@ -92,21 +107,35 @@ def test_mlp_fp32_odd_shapes(lm):
 
 
 def _qkv_case(lm, cfg):
+    """Q/K/V and O forward + backward against the oracle.  With cfg.nf4 every
+    base (q, k, v, o) is NF4-quantized on the GPU, checked bit for bit, and
+    the oracle runs on the dequantized weights; cfg.lora_dtype == "f32" selects
+    fp32 adapters (the oracle takes them as the mode casts them)."""
     import torch
 
     inp = make_attn_inputs(cfg)
     dt = cfg.dtype
     tol = TOL[dt]
+    nf = {}
+    if cfg.nf4:
+        for n in ("q", "k", "v", "o"):
+            nf[n] = _nf4_dev(lm, inp[n]["W"])
+            qz = _check_nf4_bitexact(lm, inp[n]["W"], nf[n])
+            inp[n] = dict(inp[n], W=ON.dequantize(qz, "bf16"))
+    ad = cfg.lora_dtype or None
     X = dev(inp["X"], dt)
-    q, k, v = (proj_dev(inp[n], dt) for n in ("q", "k", "v"))
+    q, k, v = (proj_dev(inp[n], dt, nf4=nf.get(n), adapters=ad) for n in ("q", "k", "v"))
     Q, K, V, U = lm.qkv_fwd(X, q, k, v)
     dQ, dK, dV = (dev(inp[n], dt) for n in ("dQ", "dK", "dV"))
     dX, grads = lm.qkv_bwd(dQ, dK, dV, X, U, q, k, v)
     Xo = dev(inp["Xo"], dt)
-    o = proj_dev(inp["o"], dt)
+    o = proj_dev(inp["o"], dt, nf4=nf.get("o"), adapters=ad)
     Yo, Uo = lm.o_fwd(Xo, o)
     dXo, dAo, dBo = lm.o_bwd(dev(inp["dO"], dt), Xo, Uo, o)
     torch.cuda.synchronize()
+    if ad:
+        assert all(t.dtype == torch.float32 for t in list(grads.values()) + [dAo, dBo])
+        inp = dict(inp, **{n: OL.to_compute_adapters(inp[n]) for n in ("q", "k", "v", "o")})
     (Qr, Kr, Vr), sr = OL.qkv_fwd(inp["X"], inp["q"], inp["k"], inp["v"])
     gr = OL.qkv_bwd(inp["dQ"], inp["dK"], inp["dV"], inp["X"], sr, inp["q"], inp["k"], inp["v"])
     for name, a, b in (("Q", Q, Qr), ("K", K, Kr), ("V", V, Vr)):
@@ -180,6 +209,22 @@ def test_o_bf16_wide_rank(lm, r):
 
 def test_qkv_o_fp32(lm):
     cfg = WorkloadConfig(94, "attn", T=50, H=96, r=4, alpha=8, dtype="f32", Nq=96, Nk=32, Nv=40)
+    _qkv_case(lm, cfg)
+
+
+# QLoRA on the attention projections ("loralei" README, section "Use": the
+# QLoRA example quantizes q, k, v and o).  The Q/K/V forward walks three NF4
+# regions across N (a ragged 192- and 128-column region after the first), the
+# Q/K/V input gradient three NF4 K segments, and O one NF4 weight each way.
+@pytest.mark.parametrize("T", [1, 257, 300])
+def test_qkv_o_nf4_base(lm, T):
+    cfg = WorkloadConfig(103, "attn", T=T, H=512, r=16, alpha=32, dtype="bf16", Nq=512, Nk=192, Nv=128, nf4=True)
+    _qkv_case(lm, cfg)
+
+
+def test_qkv_o_nf4_base_fp32_adapters(lm):
+    cfg = WorkloadConfig(104, "attn", T=300, H=512, r=16, alpha=32, dtype="bf16", Nq=512, Nk=192, Nv=128, nf4=True,
+                         lora_dtype="f32")
     _qkv_case(lm, cfg)
 
 
@@ -481,6 +526,21 @@ def test_qlora_mlp_bf16(lm, act, r):
         assert_close(k_dev, host(grads[k_dev]), gr[k_ref], TOL["bf16"])
 
 
+# I = 1088 = 8 x 128 + 64: the last gate/up tile holds 64 gate and 64 up
+# columns, so half of every NF4 column pair it unpacks lies past I.
+@pytest.mark.parametrize("act", ["swiglu", "geglu_tanh"])
+def test_qlora_mlp_ragged_dual_tile(lm, act):
+    cfg = WorkloadConfig(105, "mlp", T=300, H=512, I=1088, r=16, alpha=32, dtype="bf16", act=act, nf4=True)
+    _mlp_case(lm, cfg, act)
+
+
+@pytest.mark.parametrize("act", ["swiglu", "geglu_tanh"])
+def test_qlora_mlp_fp32_adapters(lm, act):
+    cfg = WorkloadConfig(106, "mlp", T=300, H=512, I=1088, r=16, alpha=32, dtype="bf16", act=act, nf4=True,
+                         lora_dtype="f32")
+    _mlp_case(lm, cfg, act)
+
+
 # (rows, cols) of the NF4 weight: K = rows (forward) or cols (transposed) is
 # 1, 2, 3 or more K steps of 64, and N leaves ragged tiles of 64 or 128.
 @pytest.mark.parametrize("shape", [(512, 768), (64, 512), (128, 384), (192, 256)])
@@ -500,10 +560,16 @@ def test_nf4_gemm(lm, shape, trans, with_lora):
     Wd = ON.dequantize(q, "bf16")
     Y = lm.nf4_gemm(dev(X), w, dev(A) if with_lora else None, dev(B) if with_lora else None, s, trans)
     torch.cuda.synchronize()
+    # the oracle's projection on the dequantized weight: its forward for
+    # trans = 0, and for trans = 1 the input gradient of its backward with
+    # dZ = X (Y = X deq(W)^T + s (X B^T) A^T); without adapters A = B = 0
+    if not with_lora:
+        A, B = np.zeros_like(A), np.zeros_like(B)
     if not trans:
-        ref = X @ Wd + (s * ((X @ A) @ B) if with_lora else 0)
+        ref, _ = OL.proj_fwd(X, Wd, A, B, s)
     else:
-        ref = X @ Wd.T + (s * ((X @ B.T) @ A.T) if with_lora else 0)
+        X_in, U = np.zeros((T, rows), np.float32), np.zeros((T, r), np.float32)
+        ref, _, _ = OL.proj_bwd(X, X_in, Wd, A, B, s, U)
     assert_close("Y", host(Y), ref, TOL["bf16"])
 
 
@@ -697,9 +763,10 @@ def test_errors_enqueue_nothing(lm):
 # ---------------------------------------------------------------------------
 # In-place dX: every backward may write dX over X ("LoRA Optimizations",
 # "Custom autograd functions"; the unsloth backward hunks write dX into X's
-# storage once dA = s X^T P has been formed).  The result must equal the
-# out-of-place call bit for bit: same kernels, same order, and X is last read
-# by the dA pass, which precedes the dX GEMM.
+# storage once dA = s X^T P has been formed).  The in-place dX and gradients
+# are compared with the oracle, and with the out-of-place call bit for bit
+# (same kernels, same order; X is last read by the dA pass, which precedes
+# the dX GEMM).
 # ---------------------------------------------------------------------------
 
 def _grads_equal(a, b):
@@ -708,6 +775,10 @@ def _grads_equal(a, b):
     assert a.keys() == b.keys()
     for k in a:
         assert torch.equal(a[k], b[k]), k
+
+
+_MLP_GRADS = (("dA_gate", "dA_g"), ("dB_gate", "dB_g"), ("dA_up", "dA_u"), ("dB_up", "dB_u"),
+              ("dA_down", "dA_d"), ("dB_down", "dB_d"))
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
@@ -724,6 +795,12 @@ def test_inplace_dx_mlp(lm, dt):
     dXi, gi = lm.mlp_bwd(dY, Xi, saved, g, u, d, dX=Xi)
     torch.cuda.synchronize()
     assert dXi.data_ptr() == Xi.data_ptr()
+    _, sr = OL.mlp_fwd(inp["X"], inp["gate"], inp["up"], inp["down"])
+    gr = OL.mlp_bwd(inp["dY"], inp["X"], sr, inp["gate"], inp["up"], inp["down"])
+    tol = TOL[dt]
+    assert_close("dX (in place)", host(Xi), gr["dX"], tol)
+    for k_dev, k_ref in _MLP_GRADS:
+        assert_close(k_dev, host(gi[k_dev]), gr[k_ref], tol)
     assert torch.equal(Xi, dX)
     _grads_equal(grads, gi)
 
@@ -740,6 +817,12 @@ def test_inplace_dx_relu2_mlp(lm):
     Xi = X.clone()
     _, gi = lm.relu2_mlp_bwd(dY, Xi, saved, up, down, dX=Xi)
     torch.cuda.synchronize()
+    _, sr = OL.relu2_mlp_fwd(inp["X"], inp["up"], inp["down"])
+    gr = OL.relu2_mlp_bwd(inp["dY"], inp["X"], sr, inp["up"], inp["down"])
+    tol = TOL["bf16"]
+    assert_close("dX (in place)", host(Xi), gr["dX"], tol)
+    for k_dev, k_ref in (("dA_up", "dA_u"), ("dB_up", "dB_u"), ("dA_down", "dA_d"), ("dB_down", "dB_d")):
+        assert_close(k_dev, host(gi[k_dev]), gr[k_ref], tol)
     assert torch.equal(Xi, dX)
     _grads_equal(grads, gi)
 
@@ -765,7 +848,46 @@ def test_inplace_dx_qkv_o(lm, dt):
     Xoi = Xo.clone()
     _, dAoi, dBoi = lm.o_bwd(dO, Xoi, Uo, o, dX=Xoi)
     torch.cuda.synchronize()
+    _, sr = OL.qkv_fwd(inp["X"], inp["q"], inp["k"], inp["v"])
+    gr = OL.qkv_bwd(inp["dQ"], inp["dK"], inp["dV"], inp["X"], sr, inp["q"], inp["k"], inp["v"])
+    _, so = OL.o_fwd(inp["Xo"], inp["o"])
+    go = OL.o_bwd(inp["dO"], inp["Xo"], so, inp["o"])
+    tol = TOL[dt]
+    assert_close("dX (in place)", host(Xi), gr["dX"], tol)
+    for n in ("dA_q", "dB_q", "dA_k", "dB_k", "dA_v", "dB_v"):
+        assert_close(n, host(gi[n]), gr[n], tol)
+    assert_close("dX_o (in place)", host(Xoi), go["dX"], tol)
+    assert_close("dA_o", host(dAoi), go["dA"], tol)
+    assert_close("dB_o", host(dBoi), go["dB"], tol)
     assert torch.equal(Xi, dX)
     _grads_equal(grads, gi)
     assert torch.equal(Xoi, dXo)
     assert torch.equal(dAoi, dAo) and torch.equal(dBoi, dBo)
+
+
+def test_non_default_stream(lm):
+    """A call on a caller's stream: outputs and workspace are allocated on that
+    stream, so memory the current stream allocates and overwrites right after
+    the call (while the call's kernels may still run) cannot be a buffer the
+    call uses.  Results are checked against the oracle after the stream ends."""
+    import torch
+
+    cfg = WorkloadConfig(107, "mlp", T=300, H=512, I=1088, r=16, alpha=32, dtype="bf16", act="swiglu")
+    inp = make_mlp_inputs(cfg)
+    X, dY = dev(inp["X"]), dev(inp["dY"])
+    g, u, d = (proj_dev(inp[k]) for k in ("gate", "up", "down"))
+    s = torch.cuda.Stream()  # default priority
+    s.wait_stream(torch.cuda.current_stream())
+    Y, saved = lm.mlp_fwd(X, g, u, d, stream=s)
+    dX, grads = lm.mlp_bwd(dY, X, saved, g, u, d, stream=s)
+    junk = [torch.full((1 << 22,), float("nan"), dtype=torch.float32, device="cuda:0") for _ in range(16)]
+    s.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    Yr, sr = OL.mlp_fwd(inp["X"], inp["gate"], inp["up"], inp["down"])
+    gr = OL.mlp_bwd(inp["dY"], inp["X"], sr, inp["gate"], inp["up"], inp["down"])
+    tol = TOL["bf16"]
+    assert_close("Y", host(Y), Yr, tol)
+    assert_close("dX", host(dX), gr["dX"], tol)
+    for k_dev, k_ref in _MLP_GRADS:
+        assert_close(k_dev, host(grads[k_dev]), gr[k_ref], tol)
