@@ -565,7 +565,7 @@ def nf4_quantize(W, *, stream=None) -> NF4Weight:
                       mu=torch.empty(1, dtype=torch.float32, device=dev), rows=rows, cols=cols)
         ws = _ws(nbytes.value, dev)
     L.call("lora_nf4_quantize", _ptr(W), rows, cols, _dtype_code(W), _ptr(w.codes), _ptr(w.q8), _ptr(w.s2),
-           _ptr(w.mu), _ptr(ws), _nbytes(ws, X.device), _stream(stream))
+           _ptr(w.mu), _ptr(ws), _nbytes(ws, dev), _stream(stream))
     return w
 
 
