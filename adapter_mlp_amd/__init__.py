@@ -21,7 +21,7 @@ __all__ = [
     "Proj", "NF4Weight", "load", "LoraError",
     "mlp_fwd", "mlp_bwd", "mlp_workspace_size",
     "relu2_mlp_fwd", "relu2_mlp_bwd", "relu2_mlp_workspace_size",
-    "qkv_fwd", "qkv_bwd", "o_fwd", "o_bwd",
+    "qkv_fwd", "qkv_bwd", "o_fwd", "o_bwd", "o_fwd_noalloc",
     "nf4_quantize", "nf4_dequant", "nf4_unpack_codes", "nf4_gemm", "nf4_codebook",
     "trace_begin", "trace_end",
 ]
@@ -507,6 +507,25 @@ def o_fwd(X, o: Proj, *, Y=None, U=None, ws=None, stream=None):
     L.call("lora_o_fwd", C.byref(d), _ptr(X), C.byref(o.c_struct(keep)), _ptr(Y), _ptr(U), _ptr(ws), _nbytes(ws, X.device),
            _stream(stream))
     return Y, U
+
+
+def o_fwd_noalloc(X, o: Proj, *, Y, U, stream=None):
+    """o_fwd for callers that cannot allocate: the library takes its scratch
+    from a static per-GPU array (at most NOALLOC_SCRATCH_BYTES, shared by all
+    such calls on that GPU) and allocates nothing; the caller passes the
+    outputs Y [T, N] and U [T, r].  Returns (Y, U)."""
+    T, K, N, r, dt = _o_dims(X, o)
+    _need("Y", Y, (T, N), X.dtype, X.device)
+    _need("U", U, (T, r), X.dtype, X.device)
+    _on_gpu(X)
+    d = L.lora_o_desc(T, K, N, r, dt, 0)
+    keep = []
+    L.call("lora_o_fwd_noalloc", C.byref(d), _ptr(X), C.byref(o.c_struct(keep)), _ptr(Y), _ptr(U),
+           _stream(stream))
+    return Y, U
+
+
+NOALLOC_SCRATCH_BYTES = L.NOALLOC_SCRATCH_BYTES
 
 
 def o_bwd(dY, X, U, o: Proj, *, dX=None, dA=None, dB=None, ws=None, stream=None):

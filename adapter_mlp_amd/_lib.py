@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblora_mi3
 
 LORA_OK, LORA_EINVAL, LORA_ESHAPE, LORA_EDTYPE, LORA_EALIGN, LORA_EWORKSPACE, LORA_EUNSUPPORTED, LORA_EDEVICE = range(8)
 LORA_F32, LORA_BF16, LORA_BF16_F32LORA = 0, 1, 2
+NOALLOC_SCRATCH_BYTES = 32 << 20  # LORA_NOALLOC_SCRATCH_BYTES
 LORA_ACT_SWIGLU, LORA_ACT_GEGLU_TANH = 0, 1
 ACT_CODES = {"swiglu": LORA_ACT_SWIGLU, "geglu_tanh": LORA_ACT_GEGLU_TANH}
 STATUS_NAMES = {0: "LORA_OK", 1: "LORA_EINVAL", 2: "LORA_ESHAPE", 3: "LORA_EDTYPE", 4: "LORA_EALIGN",
@@ -97,6 +98,7 @@ SIGNATURES = {
     "lora_o_workspace_size": (i32, [P(lora_o_desc), P(sz), P(sz)]),
     "lora_o_fwd": (i32, [P(lora_o_desc), vp, P(lora_proj), vp, vp, vp, sz, vp]),
     "lora_o_bwd": (i32, [P(lora_o_desc), vp, vp, vp, P(lora_proj), vp, vp, vp, vp, sz, vp]),
+    "lora_o_fwd_noalloc": (i32, [P(lora_o_desc), vp, P(lora_proj), vp, vp, vp]),
     "lora_nf4_quantize_workspace_size": (i32, [i64, i64, P(sz)]),
     "lora_nf4_quantize": (i32, [vp, i64, i64, i32, vp, vp, vp, vp, vp, sz, vp]),
     "lora_nf4_dequant": (i32, [P(lora_nf4), vp, i32, vp]),

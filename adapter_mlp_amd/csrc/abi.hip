@@ -4,7 +4,9 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <atomic>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "common.hpp"
@@ -12,6 +14,10 @@
 #include "trace.hpp"
 
 using namespace lora;
+
+// Static scratch of lora_o_fwd_noalloc (see static_scratch below).
+constexpr size_t kScratchBytes = LORA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
 
 namespace {
 
@@ -609,8 +615,10 @@ struct OPlan {
   size_t fwd_bytes, bwd_bytes;
 };
 
-// Shared by lora_o_* and lora_nf4_gemm: n_in = K, n_out = N.
-OPlan plan_o(const Ctx& c, int64_t T, int64_t K, int64_t N, int64_t r, bool tmp_u, void* wf, void* wb) {
+// Shared by lora_o_* and lora_nf4_gemm: n_in = K, n_out = N.  split = false
+// plans the forward without split-K partials (the GEMM then runs unsplit).
+OPlan plan_o(const Ctx& c, int64_t T, int64_t K, int64_t N, int64_t r, bool tmp_u, void* wf, void* wb,
+             bool split = true) {
   OPlan p{};
   const int64_t RL = c.rl(r);
   const AdapterDims ad[1] = {{K, N}};
@@ -620,7 +628,7 @@ OPlan plan_o(const Ctx& c, int64_t T, int64_t K, int64_t N, int64_t r, bool tmp_
   p.Us = f.take(T * RL * c.es);
   p.BLt = f.take(N * RL * c.es);
   p.U_tmp = tmp_u ? f.take(T * r * c.es) : nullptr;
-  p.kpart = static_cast<float*>(f.take((size_t)kpart_floats(c, T, N, K + (r > 0 ? RL : 0)) * 4));
+  p.kpart = split ? static_cast<float*>(f.take((size_t)kpart_floats(c, T, N, K + (r > 0 ? RL : 0)) * 4)) : nullptr;
   p.fwd_bytes = f.off;
   Ws b(wb);
   p.ad_b = b.take(staged_bytes(c, ad, 1, r));
@@ -739,6 +747,38 @@ lora_status proj_input_grad(const Ctx& c, int64_t T, int64_t K, int64_t N, int64
   g.reg[0].out = dX;
   g.reg[0].ldo = K;
   LAUNCH(gemm_on(c, g, st, K, p.partial));
+  return LORA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch of lora_o_fwd_noalloc: one array per device, allocated with
+// the code object when the library is loaded on that device and held until
+// the process ends.  In host code `scratch` is a host-side stand-in, not a
+// device address: every use goes through the address hipGetSymbolAddress
+// returns for the current device, looked up once per device at that
+// device's first call.  Every call on a device shares its array.
+// ---------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+lora_status static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  CHECK(e == hipSuccess, LORA_EDEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  CHECK(dev >= 0 && dev < kMaxDevices, LORA_EDEVICE, "device %d is beyond the %d the library tracks", dev, kMaxDevices);
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      CHECK(e == hipSuccess && p != nullptr, LORA_EDEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+            hipGetErrorString(e));
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
   return LORA_OK;
 }
 
@@ -1610,6 +1650,31 @@ lora_status lora_o_fwd(const lora_o_desc* d, const void* X, const lora_proj* o, 
   TRY(check_ws(ws, ws_bytes, need.fwd_bytes));
   if (d->T == 0) return LORA_OK;
   OPlan p = plan_o(c, d->T, d->K, d->N, d->r, false, ws, nullptr);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const AdapterDims ad[1] = {{d->K, d->N}};
+  lora_proj sp[1];
+  STAGE(p.ad_f, &o, ad, 1, d->r, sp, st);
+  return proj_forward(c, d->T, d->K, d->N, d->r, X, &sp[0], Y, U, p, st);
+}
+
+lora_status lora_o_fwd_noalloc(const lora_o_desc* d, const void* X, const lora_proj* o, void* Y, void* U,
+                               void* stream) {
+  Ctx c{};
+  TRY(validate_o(d, c));
+  const int64_t T = d->T;
+  TRY(check_tptr(c, X, T, "X"));
+  TRY(check_tptr(c, Y, T, "Y"));
+  TRY(check_tptr(c, U, T, "U"));
+  TRY(check_proj(c, o, d->K, d->N, "o"));
+  // the GEMM runs unsplit here: no fp32 split-K partials in the scratch
+  OPlan need = plan_o(c, d->T, d->K, d->N, d->r, false, nullptr, nullptr, false);
+  CHECK(need.fwd_bytes <= kScratchBytes, LORA_EWORKSPACE,
+        "this call needs %zu bytes of scratch; the static scratch holds %zu (fewer tokens per call fit)",
+        need.fwd_bytes, kScratchBytes);
+  void* ws = nullptr;
+  TRY(static_scratch(&ws));
+  if (d->T == 0) return LORA_OK;
+  OPlan p = plan_o(c, d->T, d->K, d->N, d->r, false, ws, nullptr, false);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const AdapterDims ad[1] = {{d->K, d->N}};
   lora_proj sp[1];

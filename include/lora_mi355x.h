@@ -311,6 +311,26 @@ lora_status lora_o_workspace_size(const lora_o_desc* desc, size_t* fwd_bytes,
 lora_status lora_o_fwd(const lora_o_desc* desc, const void* X, const lora_proj* o, void* Y,
                        void* U, void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the forward
+ * of lora_o_fwd with no workspace argument.  The call allocates nothing; its
+ * scratch is a static device array of LORA_NOALLOC_SCRATCH_BYTES per GPU,
+ * part of the library's code object, held until the process ends, and looked
+ * up on the calling thread's current device (which must be the device of the
+ * buffers and of `stream`) at that device's first call.  The caller passes
+ * inputs and outputs as for lora_o_fwd, with the same results; the GEMM never
+ * uses split-K here.  A call whose scratch need exceeds the limit (about
+ * 128 bytes per token plus 128 bytes per output column and 2 r K bytes in
+ * bf16; the fp32 adapter casts add 2 r (K + N) bytes under LORA_BF16_F32LORA;
+ * 4 r (T + N + K) bytes in fp32)
+ * returns LORA_EWORKSPACE and enqueues nothing.  Every call on one GPU uses
+ * the same array: calls that can overlap on one GPU (on different streams,
+ * or from different threads) race and must be ordered by the caller.
+ * LORA_EDEVICE if the array's address cannot be obtained. */
+#define LORA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+lora_status lora_o_fwd_noalloc(const lora_o_desc* desc, const void* X, const lora_proj* o, void* Y, void* U,
+                               void* stream);
+
 /* P = dY B^T (once); dX = dY W^T + s P A^T; dA = s X^T P; dB = s U^T dY.
  * dX may be X itself (in place); a partial overlap is rejected. */
 lora_status lora_o_bwd(const lora_o_desc* desc, const void* dY, const void* X, const void* U,
