@@ -189,6 +189,8 @@ void* offw(void* p, int64_t elems, const Ctx& c) { return static_cast<char*>(p) 
 // and HBM rates).  Each part keeps at least 16 K steps of 64.
 int gemm_ksplit(const Ctx& c, int64_t M, int64_t N, int64_t K) {
   if (!c.bf16) return 1;
+  // each fp32 part [M, N] must stay below 2 GiB (32-bit offsets of its stores)
+  if (M * N * 4 >= ((int64_t)1 << 31) - 4096) return 1;
   const int64_t tiles = cdiv(M, 256) * cdiv(N, 256);
   if (tiles == 0) return 1;
   double best = 0.0;

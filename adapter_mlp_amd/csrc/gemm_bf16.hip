@@ -121,6 +121,11 @@ struct FusedU {
   bf16x8 adf[KB];
   f32x4 acc[4][2];
   __device__ __forceinline__ void init(const GemmArgs& args, int64_t nbase, int64_t NR, int lane) {
+    // zero sums for a wavefront whose columns lie past NR (it runs no pass)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) acc[jj][mb] = f32x4{0, 0, 0, 0};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       adf[kb] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
@@ -170,11 +175,17 @@ struct FusedU {
   }
 };
 
-template <int WN, bool DUAL, int EPI>
+// Every feature width of a bf16 call is a multiple of 64, so the WN / 2 (gate/up
+// tiles) or WN (other tiles) output columns of a wavefront lie wholly inside or
+// wholly past the region: the column check is uniform across the wavefront.
+// Rows past M are handled by the range-checked buffer accesses (loads read
+// zero, stores are dropped), so the epilogues carry no per-lane branch.
+template <int WN, bool DUAL, int EPI, int ACT>
 __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* wstage, const GemmArgs& args,
                                                int reg, int64_t mw, int64_t nbase, int64_t NR, int64_t M,
                                                int lane, int wm, int wn, int kp) {
   constexpr int NI = WN / 32;
+  const bool cols_ok = nbase < NR;  // uniform
   if constexpr (EPI == EPI_STORE) {
     if (args.ksplit > 1) {
       // split-K part: fp32 sums through a [32][WN] fp32 staging, 16-byte stores
@@ -182,7 +193,8 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
       constexpr int CPR = WN / 4;          // 4-float chunks per row
       constexpr int RPP = 64 / CPR;
       float* stg = reinterpret_cast<float*>(wstage);
-      float* out = args.kpart + (int64_t)kp * M * NR;
+      const brsrc ro = make_rsrc(args.kpart + (int64_t)kp * M * NR, M * NR * 4);
+      if (!cols_ok) return;
       for4([&](auto jc) {
         constexpr int j = decltype(jc)::value;
 #pragma unroll
@@ -200,7 +212,7 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
           const f32x4 v = *reinterpret_cast<const f32x4*>(stg + row * LD + c4 * 4);
           const int64_t m = mw + j * 32 + row;
           const int64_t n = nbase + c4 * 4;
-          if (m < M && n < NR) *reinterpret_cast<f32x4*>(out + m * NR + n) = v;
+          buf_store16f(ro, row_off(m, M, NR, n, 4), v);
         }
         wave_sync();
       });
@@ -210,8 +222,9 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
     constexpr int CPR = WN / 8;          // 16-byte chunks per row
     constexpr int RPP = 64 / CPR;        // rows per pass
     uint16_t* stg = reinterpret_cast<uint16_t*>(wstage);
-    char* out = static_cast<char*>(args.reg[reg].out);
     const int64_t ldo = args.reg[reg].ldo;
+    const brsrc ro = make_rsrc(args.reg[reg].out, M * ldo * 2);
+    if (!cols_ok) return;
     for4([&](auto jc) {
       constexpr int j = decltype(jc)::value;
 #pragma unroll
@@ -231,7 +244,7 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
         const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * LD + c8 * 8);
         const int64_t m = mw + j * 32 + row;
         const int64_t n = nbase + c8 * 8;
-        if (m < M && n < NR) *reinterpret_cast<u32x4*>(out + (m * ldo + n) * 2) = v;
+        buf_store16(ro, row_off(m, M, ldo, n, 2), v);
       }
       wave_sync();
     });
@@ -243,54 +256,55 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
     constexpr int CPR = W2 / 8;
     constexpr int RPP = 64 / CPR;
     uint16_t* stg = reinterpret_cast<uint16_t*>(wstage);
-    char* eo = static_cast<char*>(args.e_out);
-    char* go = static_cast<char*>(args.g_out);
-    char* ho = static_cast<char*>(args.h_out);
     const int64_t ld = args.ld_act;
+    const brsrc eo = make_rsrc(args.e_out, M * ld * 2);
+    const brsrc go = make_rsrc(args.g_out, M * ld * 2);
+    const brsrc ho = make_rsrc(args.h_out, M * ld * 2);
     // with u_part: U_d = h Ad over this wavefront's 32 h columns (FusedU)
     const bool fuse_u = args.u_part != nullptr;
     FusedU<W2> fu;
     if (fuse_u) fu.init(args, nbase, NR, lane);
-    for4([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
+    if (cols_ok) {
+      for4([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
 #pragma unroll
-      for (int i = 0; i < NI / 2; ++i)
+        for (int i = 0; i < NI / 2; ++i)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = i * 32 + 8 * g + 4 * (lane >> 5);
-          u32x2 ev, gv, hv;
+          for (int g = 0; g < 4; ++g) {
+            const int col = i * 32 + 8 * g + 4 * (lane >> 5);
+            u32x2 ev, gv, hv;
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            ev[h] = pack_bf2(acc[i][j][4 * g + 2 * h], acc[i][j][4 * g + 2 * h + 1]);
-            gv[h] = pack_bf2(acc[i + NI / 2][j][4 * g + 2 * h], acc[i + NI / 2][j][4 * g + 2 * h + 1]);
-            float p0, p1;
-            act_fwd<false>(args.act, lo_bf(ev[h]), p0);
-            act_fwd<false>(args.act, hi_bf(ev[h]), p1);
-            hv[h] = pack_bf2(p0 * lo_bf(gv[h]), p1 * hi_bf(gv[h]));
+            for (int h = 0; h < 2; ++h) {
+              ev[h] = pack_bf2(acc[i][j][4 * g + 2 * h], acc[i][j][4 * g + 2 * h + 1]);
+              gv[h] = pack_bf2(acc[i + NI / 2][j][4 * g + 2 * h], acc[i + NI / 2][j][4 * g + 2 * h + 1]);
+              float p0, p1;
+              act_fwd<false>(ACT, lo_bf(ev[h]), p0);
+              act_fwd<false>(ACT, hi_bf(ev[h]), p1);
+              hv[h] = pack_bf2(p0 * lo_bf(gv[h]), p1 * hi_bf(gv[h]));
+            }
+            const int o = (lane & 31) * LD + col;
+            *reinterpret_cast<u32x2*>(stg + o) = ev;
+            *reinterpret_cast<u32x2*>(stg + ARR + o) = gv;
+            *reinterpret_cast<u32x2*>(stg + 2 * ARR + o) = hv;
           }
-          const int o = (lane & 31) * LD + col;
-          *reinterpret_cast<u32x2*>(stg + o) = ev;
-          *reinterpret_cast<u32x2*>(stg + ARR + o) = gv;
-          *reinterpret_cast<u32x2*>(stg + 2 * ARR + o) = hv;
-        }
-      wave_sync();
+        wave_sync();
 #pragma unroll
-      for (int it = 0; it < 32 / RPP; ++it) {
-        const int row = it * RPP + lane / CPR, c8 = lane % CPR;
-        const int64_t m = mw + j * 32 + row;
-        const int64_t n = nbase + c8 * 8;
-        if (m < M && n < NR) {
+        for (int it = 0; it < 32 / RPP; ++it) {
+          const int row = it * RPP + lane / CPR, c8 = lane % CPR;
+          const int64_t m = mw + j * 32 + row;
+          const int64_t n = nbase + c8 * 8;
           const int o = row * LD + c8 * 8;
-          const int64_t off = (m * ld + n) * 2;
-          *reinterpret_cast<u32x4*>(eo + off) = *reinterpret_cast<const u32x4*>(stg + o);
-          *reinterpret_cast<u32x4*>(go + off) = *reinterpret_cast<const u32x4*>(stg + ARR + o);
-          *reinterpret_cast<u32x4*>(ho + off) = *reinterpret_cast<const u32x4*>(stg + 2 * ARR + o);
+          const uint32_t off = row_off(m, M, ld, n, 2);
+          buf_store16(eo, off, *reinterpret_cast<const u32x4*>(stg + o));
+          buf_store16(go, off, *reinterpret_cast<const u32x4*>(stg + ARR + o));
+          buf_store16(ho, off, *reinterpret_cast<const u32x4*>(stg + 2 * ARR + o));
         }
-      }
-      if (fuse_u) fu.template pass<j, LD>(stg + 2 * ARR, lane);
-      wave_sync();
-    });
-    // this tile's n index: 128 output columns per gate/up tile
+        if (fuse_u) fu.template pass<j, LD>(stg + 2 * ARR, lane);
+        wave_sync();
+      });
+    }
+    // this tile's n index: 128 output columns per gate/up tile (a wavefront
+    // past NR contributes zero sums: its h columns meet zero Ad^T rows)
     if (fuse_u) fu.template finish<epi_stage_bytes<WN, EPI>()>(args, wstage, mw, (nbase - 32 * wn) / 128, M, wn, lane);
   } else if constexpr (EPI == EPI_ACT1_FWD) {
     constexpr int LD = WN + 8;           // bf16 staging [2][32][WN]: u, h
@@ -298,46 +312,46 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
     constexpr int CPR = WN / 8;
     constexpr int RPP = 64 / CPR;
     uint16_t* stg = reinterpret_cast<uint16_t*>(wstage);
-    char* uo = static_cast<char*>(args.e_out);
-    char* ho = static_cast<char*>(args.h_out);
     const int64_t ld = args.ld_act;
+    const brsrc uo = make_rsrc(args.e_out, M * ld * 2);
+    const brsrc ho = make_rsrc(args.h_out, M * ld * 2);
     // with u_part: U_d = h Ad over this wavefront's WN h columns (FusedU)
     const bool fuse_u = args.u_part != nullptr;
     FusedU<WN> fu;
     if (fuse_u) fu.init(args, nbase, NR, lane);
-    for4([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
+    if (cols_ok) {
+      for4([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
+        for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = i * 32 + 8 * g + 4 * (lane >> 5);
-          u32x2 uv, hv;
+          for (int g = 0; g < 4; ++g) {
+            const int col = i * 32 + 8 * g + 4 * (lane >> 5);
+            u32x2 uv, hv;
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            uv[h] = pack_bf2(acc[i][j][4 * g + 2 * h], acc[i][j][4 * g + 2 * h + 1]);
-            hv[h] = pack_bf2(relu2(lo_bf(uv[h])), relu2(hi_bf(uv[h])));
+            for (int h = 0; h < 2; ++h) {
+              uv[h] = pack_bf2(acc[i][j][4 * g + 2 * h], acc[i][j][4 * g + 2 * h + 1]);
+              hv[h] = pack_bf2(relu2(lo_bf(uv[h])), relu2(hi_bf(uv[h])));
+            }
+            const int o = (lane & 31) * LD + col;
+            *reinterpret_cast<u32x2*>(stg + o) = uv;
+            *reinterpret_cast<u32x2*>(stg + ARR + o) = hv;
           }
-          const int o = (lane & 31) * LD + col;
-          *reinterpret_cast<u32x2*>(stg + o) = uv;
-          *reinterpret_cast<u32x2*>(stg + ARR + o) = hv;
-        }
-      wave_sync();
+        wave_sync();
 #pragma unroll
-      for (int it = 0; it < 32 / RPP; ++it) {
-        const int row = it * RPP + lane / CPR, c8 = lane % CPR;
-        const int64_t m = mw + j * 32 + row;
-        const int64_t n = nbase + c8 * 8;
-        if (m < M && n < NR) {
+        for (int it = 0; it < 32 / RPP; ++it) {
+          const int row = it * RPP + lane / CPR, c8 = lane % CPR;
+          const int64_t m = mw + j * 32 + row;
+          const int64_t n = nbase + c8 * 8;
           const int o = row * LD + c8 * 8;
-          const int64_t off = (m * ld + n) * 2;
-          *reinterpret_cast<u32x4*>(uo + off) = *reinterpret_cast<const u32x4*>(stg + o);
-          *reinterpret_cast<u32x4*>(ho + off) = *reinterpret_cast<const u32x4*>(stg + ARR + o);
+          const uint32_t off = row_off(m, M, ld, n, 2);
+          buf_store16(uo, off, *reinterpret_cast<const u32x4*>(stg + o));
+          buf_store16(ho, off, *reinterpret_cast<const u32x4*>(stg + ARR + o));
         }
-      }
-      if (fuse_u) fu.template pass<j, LD>(stg + ARR, lane);
-      wave_sync();
-    });
+        if (fuse_u) fu.template pass<j, LD>(stg + ARR, lane);
+        wave_sync();
+      });
+    }
     // this tile's n index: 256 output columns per tile
     if (fuse_u) fu.template finish<epi_stage_bytes<WN, EPI>()>(args, wstage, mw, (nbase - (int64_t)WN * wn) / 256, M, wn, lane);
   } else {
@@ -365,92 +379,96 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
     f32x4 dacc[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) dacc[cb] = f32x4{0, 0, 0, 0};
-    const char* ei = static_cast<const char*>(args.e_in);
-    const char* gi = static_cast<const char*>(args.g_in);
-    char* dgo = static_cast<char*>(args.dg_out);
-    char* deo = static_cast<char*>(args.de_out);
-    char* ho = static_cast<char*>(args.h_out);
     const int64_t ld = args.ld_act;
-    for4([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
+    const brsrc ei = make_rsrc(args.e_in, M * ld * 2);
+    const brsrc gi = make_rsrc(args.g_in, M * ld * 2);
+    const brsrc dgo = make_rsrc(args.dg_out, M * ld * 2);
+    const brsrc deo = make_rsrc(args.de_out, M * ld * 2);
+    const brsrc ho = make_rsrc(args.h_out, M * ld * 2);
+    const brsrc pdr = make_rsrc(args.pd, M * args.ldpd * 2);
+    // a wavefront past NR leaves dacc zero (those dA rows are not written)
+    if (cols_ok) {
+      for4([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
+        for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = i * 32 + 8 * g + 4 * (lane >> 5);
-          *reinterpret_cast<f32x4*>(stg + (lane & 31) * LD + col) =
-              f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          for (int g = 0; g < 4; ++g) {
+            const int col = i * 32 + 8 * g + 4 * (lane >> 5);
+            *reinterpret_cast<f32x4*>(stg + (lane & 31) * LD + col) =
+                f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          }
+        // Pd rows of this pass: lane l loads half l & 1 of row l / 2 (rows past M read zero)
+        u32x4 pv = u32x4{0, 0, 0, 0};
+        if (fuse) {
+          const int64_t m = mw + j * 32 + (lane >> 1);
+          pv = buf_load16(pdr, row_off(m, M, args.ldpd, 8 * (lane & 1), 2));
         }
-      // Pd rows of this pass: lane l loads half l & 1 of row l / 2 (rows past M read zero)
-      u32x4 pv = u32x4{0, 0, 0, 0};
-      if (fuse) {
-        const int64_t m = mw + j * 32 + (lane >> 1);
-        if (m < M) pv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(args.pd) +
-                                                          (m * args.ldpd + 8 * (lane & 1)) * 2);
-      }
-      wave_sync();
-      u32x4 ev[PASSES], gv[PASSES];
-      f32x4 d0[PASSES], d1[PASSES];
+        // e, g of the pass (rows past M read zero, so h is zero there)
+        u32x4 ev[PASSES], gv[PASSES];
 #pragma unroll
-      for (int it = 0; it < PASSES; ++it) {
-        const int row = it * RPP + lane / CPR, c8 = lane % CPR;
-        const int64_t m = mw + j * 32 + row;
-        const int64_t n = nbase + c8 * 8;
-        const bool ok = m < M && n < NR;
-        const int64_t off = ok ? (m * ld + n) * 2 : 0;
-        ev[it] = ok ? *reinterpret_cast<const u32x4*>(ei + off) : u32x4{0, 0, 0, 0};
-        if constexpr (GATED) gv[it] = ok ? *reinterpret_cast<const u32x4*>(gi + off) : u32x4{0, 0, 0, 0};
-        d0[it] = *reinterpret_cast<const f32x4*>(stg + row * LD + c8 * 8);
-        d1[it] = *reinterpret_cast<const f32x4*>(stg + row * LD + c8 * 8 + 4);
-      }
+        for (int it = 0; it < PASSES; ++it) {
+          const int row = it * RPP + lane / CPR, c8 = lane % CPR;
+          const int64_t m = mw + j * 32 + row;
+          const int64_t n = nbase + c8 * 8;
+          const uint32_t off = row_off(m, M, ld, n, 2);
+          ev[it] = buf_load16(ei, off);
+          if constexpr (GATED) gv[it] = buf_load16(gi, off);
+        }
+        wave_sync();
+        f32x4 d0[PASSES], d1[PASSES];
 #pragma unroll
-      for (int it = 0; it < PASSES; ++it) {
-        const int row = it * RPP + lane / CPR, c8 = lane % CPR;
-        const int64_t m = mw + j * 32 + row;
-        const int64_t n = nbase + c8 * 8;
-        u32x4 dgv, dev, hv;
+        for (int it = 0; it < PASSES; ++it) {
+          const int row = it * RPP + lane / CPR, c8 = lane % CPR;
+          d0[it] = *reinterpret_cast<const f32x4*>(stg + row * LD + c8 * 8);
+          d1[it] = *reinterpret_cast<const f32x4*>(stg + row * LD + c8 * 8 + 4);
+        }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float dha = q < 2 ? d0[it][2 * q] : d1[it][2 * q - 4];
-          const float dhb = q < 2 ? d0[it][2 * q + 1] : d1[it][2 * q - 3];
-          const float e0 = lo_bf(ev[it][q]), e1 = hi_bf(ev[it][q]);
-          if constexpr (GATED) {
-            const float g0 = lo_bf(gv[it][q]), g1 = hi_bf(gv[it][q]);
-            float p0, s0, p1, s1;
-            act_fwd_bwd<false>(args.act, e0, p0, s0);
-            act_fwd_bwd<false>(args.act, e1, p1, s1);
-            hv[q] = pack_bf2(p0 * g0, p1 * g1);
-            dgv[q] = pack_bf2(dha * p0, dhb * p1);
-            dev[q] = pack_bf2(dha * g0 * s0, dhb * g1 * s1);
-          } else {
-            hv[q] = pack_bf2(relu2(e0), relu2(e1));
-            dgv[q] = pack_bf2(dha * relu2_grad(e0), dhb * relu2_grad(e1));
+        for (int it = 0; it < PASSES; ++it) {
+          const int row = it * RPP + lane / CPR, c8 = lane % CPR;
+          const int64_t m = mw + j * 32 + row;
+          const int64_t n = nbase + c8 * 8;
+          u32x4 dgv, dev, hv;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float dha = q < 2 ? d0[it][2 * q] : d1[it][2 * q - 4];
+            const float dhb = q < 2 ? d0[it][2 * q + 1] : d1[it][2 * q - 3];
+            const float e0 = lo_bf(ev[it][q]), e1 = hi_bf(ev[it][q]);
+            if constexpr (GATED) {
+              const float g0 = lo_bf(gv[it][q]), g1 = hi_bf(gv[it][q]);
+              float p0, s0, p1, s1;
+              act_fwd_bwd<false>(ACT, e0, p0, s0);
+              act_fwd_bwd<false>(ACT, e1, p1, s1);
+              hv[q] = pack_bf2(p0 * g0, p1 * g1);
+              dgv[q] = pack_bf2(dha * p0, dhb * p1);
+              dev[q] = pack_bf2(dha * g0 * s0, dhb * g1 * s1);
+            } else {
+              hv[q] = pack_bf2(relu2(e0), relu2(e1));
+              dgv[q] = pack_bf2(dha * relu2_grad(e0), dhb * relu2_grad(e1));
+            }
+          }
+          const uint32_t off = row_off(m, M, ld, n, 2);
+          buf_store16(dgo, off, dgv);
+          if constexpr (GATED) buf_store16(deo, off, dev);
+          if (!fuse) buf_store16(ho, off, hv);
+          else *reinterpret_cast<u32x4*>(hs + row * HLD + c8 * 8) = hv;
+        }
+        if (fuse) {
+          *reinterpret_cast<u32x4*>(pds + (lane >> 1) * 16 + 8 * (lane & 1)) = pv;
+          wave_sync();
+          // lanes 16 g + 4 jj + q point at row 8 g + jj (+ 4), columns 4 q .. 4 q + 3 of a
+          // 16-column block: lane 16 g + i receives column i of rows 8 g .. 8 g + 7
+          const int g = lane >> 4, jj = (lane & 15) >> 2, q = lane & 3;
+          const bf16x8 pb = lds_read_tr8(pds_l + ((8 * g + jj) * 16 + 4 * q) * 2, 4 * 16 * 2);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            const bf16x8 ha = lds_read_tr8(hs_l + ((8 * g + jj) * HLD + 16 * cb + 4 * q) * 2, 4 * HLD * 2);
+            dacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha, pb, dacc[cb], 0, 0, 0);
           }
         }
-        if (m < M && n < NR) {
-          const int64_t off = (m * ld + n) * 2;
-          *reinterpret_cast<u32x4*>(dgo + off) = dgv;
-          if constexpr (GATED) *reinterpret_cast<u32x4*>(deo + off) = dev;
-          if (!fuse) *reinterpret_cast<u32x4*>(ho + off) = hv;
-        }
-        // h is zero past M and NR (e, g read as zero there)
-        if (fuse) *reinterpret_cast<u32x4*>(hs + row * HLD + c8 * 8) = hv;
-      }
-      if (fuse) {
-        *reinterpret_cast<u32x4*>(pds + (lane >> 1) * 16 + 8 * (lane & 1)) = pv;
         wave_sync();
-        // lanes 16 g + 4 jj + q point at row 8 g + jj (+ 4), columns 4 q .. 4 q + 3 of a
-        // 16-column block: lane 16 g + i receives column i of rows 8 g .. 8 g + 7
-        const int g = lane >> 4, jj = (lane & 15) >> 2, q = lane & 3;
-        const bf16x8 pb = lds_read_tr8(pds_l + ((8 * g + jj) * 16 + 4 * q) * 2, 4 * 16 * 2);
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const bf16x8 ha = lds_read_tr8(hs_l + ((8 * g + jj) * HLD + 16 * cb + 4 * q) * 2, 4 * HLD * 2);
-          dacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha, pb, dacc[cb], 0, 0, 0);
-        }
-      }
-      wave_sync();
-    });
+      });
+    }
     if (fuse) {
       // dacc[cb][v] = sum over this wavefront's 128 rows of h[., c] Pd[., lane % 16],
       // c = 16 cb + 4 (lane / 16) + v.  Group 1 hands its sums to group 0 through LDS.
@@ -461,7 +479,7 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
         for (int cb = 0; cb < NCB; ++cb) red[cb * 64 + lane] = dacc[cb];
       }
       __syncthreads();
-      if (wm == 0) {
+      if (wm == 0 && cols_ok) {
         const f32x4* other = reinterpret_cast<const f32x4*>(wstage + 4 * EB);
         const int64_t tm = mw / 256;
 #pragma unroll
@@ -470,7 +488,7 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int64_t n = nbase + 16 * cb + 4 * (lane >> 4) + v;
-            if (n < NR) args.dA_part[(tm * NR + n) * 16 + (lane & 15)] = dacc[cb][v] + o[v];
+            args.dA_part[(tm * NR + n) * 16 + (lane & 15)] = dacc[cb][v] + o[v];
           }
         }
       }
@@ -571,7 +589,7 @@ constexpr int SPARE = CODE_RING + 3 * CODE_SLOT;  // target of the stores of an 
 constexpr int SPARE_BYTES = 2048;
 static_assert(SPARE + SPARE_BYTES <= LDS_BYTES, "NF4 code ring exceeds LDS");
 
-template <int BKIND, bool DUAL, int EPI, bool NF4>
+template <int BKIND, bool DUAL, int EPI, bool NF4, int ACT>
 __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   static_assert(!(DUAL && BKIND == B_NT), "gate/up tiles read forward (NN) weights");
   __shared__ __attribute__((aligned(1024))) char smem_raw[LDS_BYTES];
@@ -1052,7 +1070,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   char* const wstage = smem_raw + wave * EB;
   const int64_t mw = m0 + wm * 128;
   const int64_t nbase = DUAL ? tnl * 128 + wn * 32 : tnl * 256 + wn * 64;
-  run_epilogue_w<64, DUAL, EPI>(acc, wstage, args, reg, mw, nbase, NR, M, lane, wm, wn, kp);
+  run_epilogue_w<64, DUAL, EPI, ACT>(acc, wstage, args, reg, mw, nbase, NR, M, lane, wm, wn, kp);
 }
 
 __global__ void ksplit_reduce_kernel(const float* part, int ks, int64_t M, int64_t N, uint16_t* out, int64_t ldo) {
@@ -1068,22 +1086,26 @@ __global__ void ksplit_reduce_kernel(const float* part, int ks, int64_t M, int64
   *reinterpret_cast<u32x4*>(out + m * ldo + n) = v;
 }
 
-template <int BKIND, bool DUAL, int EPI, bool NF4>
+template <int BKIND, bool DUAL, int EPI, bool NF4, int ACT = 0>
 hipError_t launch(const GemmArgs& a, hipStream_t st) {
   const int64_t nb = a.ntile_m * a.ntile_n * (a.ksplit > 1 && !NF4 ? a.ksplit : 1);
   if (nb == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_kernel<BKIND, DUAL, EPI, NF4>), dim3((unsigned)nb), dim3(NTH8), 0, st, a);
+  hipLaunchKernelGGL((gemm_kernel<BKIND, DUAL, EPI, NF4, ACT>), dim3((unsigned)nb), dim3(NTH8), 0, st, a);
   return hipGetLastError();
 }
 
 template <bool NF4>
 hipError_t launch_family(const GemmArgs& a, hipStream_t st) {
   if (a.bkind == B_NN) {
-    if (a.epi == EPI_ACT_FWD) return launch<B_NN, true, EPI_ACT_FWD, NF4>(a, st);
+    if (a.epi == EPI_ACT_FWD)
+      return a.act == LORA_ACT_SWIGLU ? launch<B_NN, true, EPI_ACT_FWD, NF4, LORA_ACT_SWIGLU>(a, st)
+                                      : launch<B_NN, true, EPI_ACT_FWD, NF4, LORA_ACT_GEGLU_TANH>(a, st);
     if (a.epi == EPI_ACT1_FWD) return launch<B_NN, false, EPI_ACT1_FWD, NF4>(a, st);
     return launch<B_NN, false, EPI_STORE, NF4>(a, st);
   }
-  if (a.epi == EPI_ACT_BWD) return launch<B_NT, false, EPI_ACT_BWD, NF4>(a, st);
+  if (a.epi == EPI_ACT_BWD)
+    return a.act == LORA_ACT_SWIGLU ? launch<B_NT, false, EPI_ACT_BWD, NF4, LORA_ACT_SWIGLU>(a, st)
+                                    : launch<B_NT, false, EPI_ACT_BWD, NF4, LORA_ACT_GEGLU_TANH>(a, st);
   if (a.epi == EPI_ACT1_BWD) return launch<B_NT, false, EPI_ACT1_BWD, NF4>(a, st);
   return launch<B_NT, false, EPI_STORE, NF4>(a, st);
 }

@@ -28,6 +28,34 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* p, int64_t bytes) {
   return i32x4{(int)(uint32_t)base, (int)((base >> 32) & 0xffff), n, 0x00020000};
 }
 
+// Range-checked buffer access to a row-major [rows, ld] operand (raw buffer,
+// stride 0): a 16-byte access at a byte offset at or past the descriptor's
+// size loads zeros, and a store there is dropped.  Epilogues address rows
+// past the last one this way without per-lane branches.  bytes is clamped
+// to [0, 2^31 - 1].
+typedef __amdgpu_buffer_rsrc_t brsrc;
+__device__ __forceinline__ brsrc make_rsrc(const void* p, int64_t bytes) {
+  if (bytes < 0) bytes = 0;
+  if (bytes > 0x7fffffff) bytes = 0x7fffffff;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+// Byte offset of element (m, n) of a row-major [M, ld] operand of es-byte
+// elements; rows at or past M get an offset past every descriptor (2^31), so
+// their accesses read zero or are dropped.  For m < M the offset is below
+// 2^31 because every operand is smaller than 2 GiB.
+__device__ __forceinline__ uint32_t row_off(int64_t m, int64_t M, int64_t ld, int64_t n, int es) {
+  return m < M ? (uint32_t)((m * ld + n) * es) : 0x80000000u;
+}
+__device__ __forceinline__ u32x4 buf_load16(brsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store16(brsrc r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store16f(brsrc r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
+}
+
 // 16 bytes per lane from global memory into LDS: lane i writes bytes
 // lds_addr + 16 i .. + 15 with the bytes at voff + soff of the descriptor;
 // offsets past the descriptor's size read zero.

@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the fused LoRA-MLP forward + backward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2|3|4|5]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1|2|3|4|5|6]
 
 A step is one forward and one backward of the whole path on one batch of
 synthetic, seeded inputs already resident in HBM: for the MLP shapes
@@ -29,6 +29,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 flop/clk x 2.4 GHz (dense)
+PEAK_F32_VALU_TFLOPS = 157.3  # 256 CU x 4 SIMD x 64 lanes x 2 flop (FMA) x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 
 
@@ -67,25 +68,26 @@ def kernel_flops(cfg, name):
         qkv_b = 2 * T * N * H + 2 * T * (3 * r) * H
         o_b = 2 * T * H * cfg.Nq + 2 * T * r * cfg.Nq
         table["gemm_nt_store"] = (qkv_b + o_b) / 2
-    base = name.replace("_nf4", "")
+    base = name.replace("_nf4", "").replace("_f32", "")
     return table.get(base)
 
 
-# Kernel names (as rocprofv3 prints them) of each GEMM family: the dense
-# kernel's template arguments are <B orientation, gate/up tiles, epilogue, NF4 weights>.
+# Kernel names (as rocprofv3 prints them) of each GEMM family: the kernel's
+# template arguments are <B orientation, gate/up tiles, epilogue, NF4 weights,
+# activation>; a family covers both activations.
 FAMILY_KERNEL = {
-    "gemm_nn_act_fwd": "gemm_kernel<0, true, 1, false>",
-    "gemm_nn_act_fwd_nf4": "gemm_kernel<0, true, 1, true>",
-    "gemm_nn_store": "gemm_kernel<0, false, 0, false>",
-    "gemm_nn_store_nf4": "gemm_kernel<0, false, 0, true>",
-    "gemm_nt_act_bwd": "gemm_kernel<1, false, 2, false>",
-    "gemm_nt_act_bwd_nf4": "gemm_kernel<1, false, 2, true>",
-    "gemm_nt_store": "gemm_kernel<1, false, 0, false>",
-    "gemm_nt_store_nf4": "gemm_kernel<1, false, 0, true>",
-    "gemm_nn_relu2_fwd": "gemm_kernel<0, false, 3, false>",
-    "gemm_nn_relu2_fwd_nf4": "gemm_kernel<0, false, 3, true>",
-    "gemm_nt_relu2_bwd": "gemm_kernel<1, false, 4, false>",
-    "gemm_nt_relu2_bwd_nf4": "gemm_kernel<1, false, 4, true>",
+    "gemm_nn_act_fwd": "gemm_kernel<0, true, 1, false, ",
+    "gemm_nn_act_fwd_nf4": "gemm_kernel<0, true, 1, true, ",
+    "gemm_nn_store": "gemm_kernel<0, false, 0, false, ",
+    "gemm_nn_store_nf4": "gemm_kernel<0, false, 0, true, ",
+    "gemm_nt_act_bwd": "gemm_kernel<1, false, 2, false, ",
+    "gemm_nt_act_bwd_nf4": "gemm_kernel<1, false, 2, true, ",
+    "gemm_nt_store": "gemm_kernel<1, false, 0, false, ",
+    "gemm_nt_store_nf4": "gemm_kernel<1, false, 0, true, ",
+    "gemm_nn_relu2_fwd": "gemm_kernel<0, false, 3, false, ",
+    "gemm_nn_relu2_fwd_nf4": "gemm_kernel<0, false, 3, true, ",
+    "gemm_nt_relu2_bwd": "gemm_kernel<1, false, 4, false, ",
+    "gemm_nt_relu2_bwd_nf4": "gemm_kernel<1, false, 4, true, ",
 }
 COPY_KERNEL = "neg_kernel"  # the --copy-calibration kernel
 
@@ -151,6 +153,99 @@ def pmc_summary(fetch_csv, write_csv, config_id):
     print(f"calibration: FETCH x{kf:.4f}, WRITE x{kw:.4f}")
 
 
+# Counter passes of --counter-summary (each within one rocprofv3 --pmc run's
+# limits: at most 8 SQ and 2 GRBM counters).
+PMC_PASSES = {
+    "mfma": ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_MFMA", "SQ_INSTS_VALU",
+             "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"],
+    "lds": ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "SQ_LDS_ADDR_CONFLICT",
+            "SQ_ACTIVE_INST_LDS", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE"],
+}
+N_SIMD, N_CU, N_XCD = 1024, 256, 8  # MI355X: 256 CUs x 4 SIMDs in 8 XCDs
+
+
+def counter_summary(csvs, config_id):
+    """MFMA and LDS counters of every GEMM family from rocprofv3 --pmc runs of
+    the PMC_PASSES sets over bench.py.  Per family: the MFMA pipe's busy share
+    of the SIMD cycles, the executed bf16 MFMA flops against the algorithmic
+    flops, VALU instructions per MFMA, LDS bank-conflict cycles against LDS
+    active cycles, and the shader clock (GRBM_GUI_ACTIVE over the dispatch
+    time).  Writes profiles/<family>_<workload>_counters.txt."""
+    import csv
+
+    from workload import CONFIGS
+    cfg = CONFIGS[config_id]
+    vals, dur = {}, {}
+    for path in csvs:
+        for row in csv.DictReader(open(path)):
+            k = row["Kernel_Name"]
+            vals.setdefault(k, {}).setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+            d = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) * 1e-9
+            dur.setdefault(k, {}).setdefault(row["Dispatch_Id"] + path, d)
+    tag = workload_tag(cfg)
+    lines = []
+    for fam, kname in FAMILY_KERNEL.items():
+        keys = [k for k in vals if kname in k]
+        if not keys:
+            continue
+        avg = {}
+        for k in keys:
+            for cn, v in vals[k].items():
+                avg.setdefault(cn, []).extend(v)
+        avg = {cn: sum(v) / len(v) for cn, v in avg.items()}
+        ds = [d for k in keys for d in dur[k].values()]
+        t = sum(ds) / len(ds)
+        fl = kernel_flops(cfg, fam)
+        # rocprofv3 sums GRBM_GUI_ACTIVE over the 8 XCDs' GRBM instances
+        gui = avg["GRBM_GUI_ACTIVE"] / N_XCD if "GRBM_GUI_ACTIVE" in avg else None
+        m = {"dispatch_s": t}
+        if gui:
+            m["clock_GHz"] = gui / t / 1e9
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and gui:
+            m["mfma_busy_frac"] = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * N_SIMD)
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in avg:
+            ex = avg["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+            m["mfma_flops_executed"] = ex
+            if fl:
+                m["mfma_flops_algorithmic"] = fl
+                m["executed_over_algorithmic"] = ex / fl
+        if "SQ_INSTS_MFMA" in avg and "SQ_INSTS_VALU" in avg and avg["SQ_INSTS_MFMA"]:
+            m["valu_non_mfma_per_mfma"] = (avg["SQ_INSTS_VALU"] - avg["SQ_INSTS_MFMA"]) / avg["SQ_INSTS_MFMA"]
+        if "SQ_LDS_IDX_ACTIVE" in avg and gui:
+            m["lds_active_frac"] = avg["SQ_LDS_IDX_ACTIVE"] / (gui * N_CU)
+        if "SQ_LDS_BANK_CONFLICT" in avg and avg.get("SQ_LDS_IDX_ACTIVE"):
+            m["lds_bank_conflict_over_active"] = avg["SQ_LDS_BANK_CONFLICT"] / avg["SQ_LDS_IDX_ACTIVE"]
+        if fl:
+            m["tflops_under_profiler"] = fl / t / 1e12
+            m["frac_of_nominal_peak"] = fl / t / 1e12 / PEAK_BF16_TFLOPS
+            if gui:
+                m["frac_of_peak_at_measured_clock"] = fl / (gui * N_CU * 4096)
+        path = os.path.join(ROOT, "profiles", f"{fam}_{tag}_counters.txt")
+        with open(path, "w") as fh:
+            fh.write(f"# MFMA and LDS counters per launch of {kname} ({fam}), workload {cfg.note}\n")
+            fh.write("# from rocprofv3 --pmc runs over bench.py, one per counter set (averages over the dispatches):\n")
+            fh.write("#   cd /tmp && export TMPDIR=/tmp\n")
+            for name, cs in PMC_PASSES.items():
+                fh.write(f"#   rocprofv3 --pmc {' '.join(cs)} --output-format csv -d <dir> -o {name} -- python3 "
+                         f"<repo>/bench.py --config {config_id} --steps 2 --warmup 1 --no-cpu-baseline\n")
+            fh.write(f"#   python3 bench.py --config {config_id} --counter-summary "
+                     f"{' '.join(n + '_counter_collection.csv' for n in PMC_PASSES)}\n")
+            fh.write("# GRBM_GUI_ACTIVE below is per XCD (the counter's sum over the 8 XCDs / 8);\n")
+            fh.write("# mfma_busy_frac = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs);\n")
+            fh.write("# mfma_flops_executed = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; clock = GRBM_GUI_ACTIVE / dispatch time;\n")
+            fh.write("# frac_of_peak_at_measured_clock = algorithmic flops / (GRBM_GUI_ACTIVE x 256 CU x 4096 flop/clk)\n")
+            fh.write(f"source_digest = {source_digest()}\n")
+            for cn in sorted(avg):
+                fh.write(f"raw.{cn} = {avg[cn]:.6g}\n")
+            for k2, v in m.items():
+                fh.write(f"{k2} = {v:.6g}\n")
+        lines.append((fam, m))
+    for fam, m in lines:
+        print(f"{fam:24s} " + "  ".join(f"{k}={v:.4g}" for k, v in m.items() if k in (
+            "clock_GHz", "mfma_busy_frac", "executed_over_algorithmic", "valu_non_mfma_per_mfma",
+            "lds_active_frac", "lds_bank_conflict_over_active", "frac_of_nominal_peak")))
+
+
 def trace_summary(stats_csv, bench_log, config_id):
     """Per-kernel durations from a rocprofv3 --kernel-trace --stats run over
     bench.py (its *_kernel_stats.csv) next to the bench line the same run
@@ -193,7 +288,7 @@ def trace_summary(stats_csv, bench_log, config_id):
 
 
 def workload_tag(cfg):
-    return {2: "llama3_8b_mlp", 3: "gemma_geglu_mlp", 4: "llama3_8b_qlora_mlp", 5: "llama3_8b_qkvo",
+    return {1: "tiny_fp32_mlp", 2: "llama3_8b_mlp", 3: "gemma_geglu_mlp", 4: "llama3_8b_qlora_mlp", 5: "llama3_8b_qkvo",
             6: "nemotron_h_relu2_mlp"}[cfg.cid]
 
 
@@ -274,8 +369,9 @@ def nf4_report(cfg, step, lm, torch, reps=5):
 class MlpStep:
     def __init__(self, cfg, inp, lm, torch):
         self.cfg, self.lm = cfg, lm
-        dev = lambda a: torch.from_numpy(a).to("cuda:0").to(torch.bfloat16)  # noqa: E731
-        adt = torch.float32 if cfg.lora_dtype == "f32" else torch.bfloat16
+        cdt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+        dev = lambda a: torch.from_numpy(a).to("cuda:0").to(cdt)  # noqa: E731
+        adt = torch.float32 if cfg.lora_dtype == "f32" else cdt
         adev = lambda a: torch.from_numpy(a).to("cuda:0").to(adt)  # noqa: E731
         self.X, self.dY = dev(inp["X"]), dev(inp["dY"])
         self.p = {}
@@ -287,7 +383,7 @@ class MlpStep:
                                 W=None if cfg.nf4 else dev(inp[k]["W"]), nf4=nf4)
         T, H, I, r = cfg.T, cfg.H, cfg.I, cfg.r
         fb, bb = lm.mlp_workspace_size(T, H, I, r, cfg.act, lm._call_dtype(self.X, list(self.p.values())))
-        bf = torch.bfloat16
+        bf = cdt
         self.Y = torch.empty((T, H), dtype=bf, device="cuda:0")
         self.saved = dict(e=torch.empty((T, I), dtype=bf, device="cuda:0"),
                           g=torch.empty((T, I), dtype=bf, device="cuda:0"),
@@ -419,7 +515,19 @@ def cpu_baseline(cfg, inp, seconds):
     what = f"{reps} passes over all {cfg.T} tokens" if reps > 1 else f"first {ts} of {cfg.T} tokens"
     return {"value": reps * ts / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{what}, full-size weights, fp32 numpy oracle fwd+bwd ({dt:.1f} s)",
-            "seconds": round(dt, 2), "cpu_count": len(os.sched_getaffinity(0))}
+            "seconds": round(dt, 2), "cpu_count": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    """The host CPU's model name as /proc/cpuinfo gives it."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -427,13 +535,16 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5, 6])
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--lora-dtype", default="bf16", choices=["bf16", "f32"],
                     help="f32: fp32 adapters and adapter gradients with bf16 inputs (fp32 LoRA-gradient mode)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU run: turn two rocprofv3 --pmc counter files into profiles/*_traffic.txt")
+    ap.add_argument("--counter-summary", nargs="+", metavar="CSV",
+                    help="no GPU run: turn rocprofv3 --pmc runs of the MFMA and LDS counter sets into "
+                         "profiles/*_counters.txt")
     ap.add_argument("--trace-summary", nargs=2, metavar=("STATS_CSV", "BENCH_LOG"),
                     help="no GPU run: turn a rocprofv3 --kernel-trace --stats run into profiles/*_kernel_trace.txt")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -445,6 +556,9 @@ def main():
         return
     if args.trace_summary:
         trace_summary(args.trace_summary[0], args.trace_summary[1], args.config)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary, args.config)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the fused LoRA path runs on a single MI355X here and "
@@ -516,6 +630,8 @@ def main():
         del src, dst
 
     nf4 = nf4_report(cfg, step, lm, torch) if cfg.nf4 else None
+    f32 = cfg.dtype == "f32"
+    peak = PEAK_F32_VALU_TFLOPS if f32 else PEAK_BF16_TFLOPS
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -536,7 +652,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32" if cfg.dtype == "f32" else "bf16",
         "data": "synthetic (seeded; random-init weights and adapters of the named shapes)",
         "config": {"workload": cfg.note, "tokens": cfg.T, "hidden": cfg.H,
                    **({"intermediate": cfg.I, "activation": cfg.act} if cfg.kind == "mlp"
@@ -547,8 +663,9 @@ def main():
                    "parallelism": "single GPU"},
         "tflops": tflops,
         "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
-        "roofline": {"bound": "mfma", "kernel": dominant, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": (achieved / PEAK_BF16_TFLOPS) if achieved else None,
+        # the fp32 path runs on fp32 FMAs (no MFMA): its bound is the vector ALU peak
+        "roofline": {"bound": "alu" if f32 else "mfma", "kernel": dominant, "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": (achieved / peak) if achieved else None,
                      "traffic": traffic, "flops_per_launch": fl, "avg_launch_ms": avg_ms,
                      "launches_timed": launches},
         "cpu_baseline": cpu,
