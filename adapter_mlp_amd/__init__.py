@@ -88,6 +88,24 @@ def _nbytes(ws, device) -> int:
     return ws.numel() * ws.element_size()
 
 
+def _set_plan(desc, plan):
+    """Put an optional GEMM launch plan into a call descriptor: a sequence of
+    up to two (group, ksplit) pairs, the call's GEMMs in launch order (see
+    lora_plan in the C header); None keeps the library's defaults.  The
+    ctypes pointer keeps the struct alive as long as the descriptor."""
+    if plan is None:
+        return desc
+    entries = list(plan)
+    if len(entries) > 2:
+        raise ValueError(f"a plan has at most two GEMM entries, got {len(entries)}")
+    p = L.lora_plan()
+    for i, e in enumerate(entries):
+        g, k = (int(x) for x in e)
+        p.gemm[i].group, p.gemm[i].ksplit = g, k
+    desc.plan = C.pointer(p)
+    return desc
+
+
 def _on(stream):
     """Allocation context of a call: PyTorch's caching allocator ties every
     tensor allocated inside it (outputs, workspace) to the stream the library
@@ -202,8 +220,8 @@ class Proj:
 # MLP
 # ---------------------------------------------------------------------------
 
-def mlp_workspace_size(T, H, I, r, act="swiglu", dtype=L.LORA_BF16):
-    d = L.lora_mlp_desc(T, H, I, r, L.ACT_CODES[act], dtype)
+def mlp_workspace_size(T, H, I, r, act="swiglu", dtype=L.LORA_BF16, plan=None):
+    d = _set_plan(L.lora_mlp_desc(T, H, I, r, L.ACT_CODES[act], dtype), plan)
     f, b = C.c_size_t(), C.c_size_t()
     L.call("lora_mlp_workspace_size", C.byref(d), C.byref(f), C.byref(b))
     return f.value, b.value
@@ -227,7 +245,8 @@ def _check_saved(saved, names_shapes, X):
         _need(f"saved[{k!r}]", saved.get(k), shape, X.dtype, X.device)
 
 
-def mlp_fwd(X, gate: Proj, up: Proj, down: Proj, act="swiglu", *, Y=None, saved=None, ws=None, stream=None):
+def mlp_fwd(X, gate: Proj, up: Proj, down: Proj, act="swiglu", *, Y=None, saved=None, ws=None, stream=None,
+            plan=None):
     """Y = down(phi(gate(X)) * up(X)).  Returns (Y, saved) with saved = dict(e, g, U).
 
     Outputs and workspace the caller does not pass are allocated on ``stream``
@@ -241,8 +260,8 @@ def mlp_fwd(X, gate: Proj, up: Proj, down: Proj, act="swiglu", *, Y=None, saved=
     if saved is not None:
         _check_saved(saved, (("e", (T, I)), ("g", (T, I)), ("U", (T, 3 * r))), X)
     _on_gpu(X, ws)
-    d = L.lora_mlp_desc(T, H, I, r, L.ACT_CODES[act], dt)
-    fb, _ = mlp_workspace_size(T, H, I, r, act, dt)
+    d = _set_plan(L.lora_mlp_desc(T, H, I, r, L.ACT_CODES[act], dt), plan)
+    fb, _ = mlp_workspace_size(T, H, I, r, act, dt, plan)
     with _on(stream):
         if Y is None:
             Y = torch.empty((T, H), dtype=X.dtype, device=X.device)
@@ -263,7 +282,7 @@ _MLP_GRAD_KEYS = ("dA_gate", "dB_gate", "dA_up", "dB_up", "dA_down", "dB_down")
 
 
 def mlp_bwd(dY, X, saved, gate: Proj, up: Proj, down: Proj, act="swiglu", *, dX=None, grads=None, ws=None,
-            stream=None):
+            stream=None, plan=None):
     """Returns (dX, grads) with grads = dict(dA_gate, dB_gate, dA_up, dB_up, dA_down, dB_down).
     ``dX=X`` writes the input gradient over X."""
     torch = _torch()
@@ -279,8 +298,8 @@ def mlp_bwd(dY, X, saved, gate: Proj, up: Proj, down: Proj, act="swiglu", *, dX=
             ref = getattr(p, ab)
             _need(f"grads[{k!r}]", grads.get(k), ref.shape, ref.dtype, X.device)
     _on_gpu(X, ws)
-    d = L.lora_mlp_desc(T, H, I, r, L.ACT_CODES[act], dt)
-    _, bb = mlp_workspace_size(T, H, I, r, act, dt)
+    d = _set_plan(L.lora_mlp_desc(T, H, I, r, L.ACT_CODES[act], dt), plan)
+    _, bb = mlp_workspace_size(T, H, I, r, act, dt, plan)
     with _on(stream):
         if dX is None:
             dX = torch.empty_like(X)
@@ -303,8 +322,8 @@ def mlp_bwd(dY, X, saved, gate: Proj, up: Proj, down: Proj, act="swiglu", *, dX=
 # Ungated ReLU^2 MLP
 # ---------------------------------------------------------------------------
 
-def relu2_mlp_workspace_size(T, H, I, r, dtype=L.LORA_BF16):
-    d = L.lora_relu2_mlp_desc(T, H, I, r, dtype, 0)
+def relu2_mlp_workspace_size(T, H, I, r, dtype=L.LORA_BF16, plan=None):
+    d = _set_plan(L.lora_relu2_mlp_desc(T, H, I, r, dtype, 0), plan)
     f, b = C.c_size_t(), C.c_size_t()
     L.call("lora_relu2_mlp_workspace_size", C.byref(d), C.byref(f), C.byref(b))
     return f.value, b.value
@@ -321,7 +340,7 @@ def _relu2_dims(X, up, down):
     return T, H, I, r, dt
 
 
-def relu2_mlp_fwd(X, up: Proj, down: Proj, *, Y=None, saved=None, ws=None, stream=None):
+def relu2_mlp_fwd(X, up: Proj, down: Proj, *, Y=None, saved=None, ws=None, stream=None, plan=None):
     """Y = down(relu(up(X))^2).  Returns (Y, saved) with saved = dict(u, U)."""
     torch = _torch()
     T, H, I, r, dt = _relu2_dims(X, up, down)
@@ -330,8 +349,8 @@ def relu2_mlp_fwd(X, up: Proj, down: Proj, *, Y=None, saved=None, ws=None, strea
     if saved is not None:
         _check_saved(saved, (("u", (T, I)), ("U", (T, 2 * r))), X)
     _on_gpu(X, ws)
-    d = L.lora_relu2_mlp_desc(T, H, I, r, dt, 0)
-    fb, _ = relu2_mlp_workspace_size(T, H, I, r, dt)
+    d = _set_plan(L.lora_relu2_mlp_desc(T, H, I, r, dt, 0), plan)
+    fb, _ = relu2_mlp_workspace_size(T, H, I, r, dt, plan)
     with _on(stream):
         if Y is None:
             Y = torch.empty((T, H), dtype=X.dtype, device=X.device)
@@ -350,7 +369,7 @@ def relu2_mlp_fwd(X, up: Proj, down: Proj, *, Y=None, saved=None, ws=None, strea
 _RELU2_GRAD_KEYS = ("dA_up", "dB_up", "dA_down", "dB_down")
 
 
-def relu2_mlp_bwd(dY, X, saved, up: Proj, down: Proj, *, dX=None, grads=None, ws=None, stream=None):
+def relu2_mlp_bwd(dY, X, saved, up: Proj, down: Proj, *, dX=None, grads=None, ws=None, stream=None, plan=None):
     """Returns (dX, grads) with grads = dict(dA_up, dB_up, dA_down, dB_down)."""
     torch = _torch()
     T, H, I, r, dt = _relu2_dims(X, up, down)
@@ -363,8 +382,8 @@ def relu2_mlp_bwd(dY, X, saved, up: Proj, down: Proj, *, dX=None, grads=None, ws
             ref = getattr(p, ab)
             _need(f"grads[{k!r}]", grads.get(k), ref.shape, ref.dtype, X.device)
     _on_gpu(X, ws)
-    d = L.lora_relu2_mlp_desc(T, H, I, r, dt, 0)
-    _, bb = relu2_mlp_workspace_size(T, H, I, r, dt)
+    d = _set_plan(L.lora_relu2_mlp_desc(T, H, I, r, dt, 0), plan)
+    _, bb = relu2_mlp_workspace_size(T, H, I, r, dt, plan)
     with _on(stream):
         if dX is None:
             dX = torch.empty_like(X)
@@ -385,8 +404,8 @@ def relu2_mlp_bwd(dY, X, saved, up: Proj, down: Proj, *, dX=None, grads=None, ws
 # Q/K/V and O
 # ---------------------------------------------------------------------------
 
-def qkv_workspace_size(T, H, Nq, Nk, Nv, r, dtype=L.LORA_BF16):
-    d = L.lora_qkv_desc(T, H, Nq, Nk, Nv, r, dtype, 0)
+def qkv_workspace_size(T, H, Nq, Nk, Nv, r, dtype=L.LORA_BF16, plan=None):
+    d = _set_plan(L.lora_qkv_desc(T, H, Nq, Nk, Nv, r, dtype, 0), plan)
     f, b = C.c_size_t(), C.c_size_t()
     L.call("lora_qkv_workspace_size", C.byref(d), C.byref(f), C.byref(b))
     return f.value, b.value
@@ -407,7 +426,7 @@ def _qkv_dims(X, q, k, v):
 _QKV_GRAD_KEYS = ("dA_q", "dB_q", "dA_k", "dB_k", "dA_v", "dB_v")
 
 
-def qkv_fwd(X, q: Proj, k: Proj, v: Proj, *, out=None, U=None, ws=None, stream=None):
+def qkv_fwd(X, q: Proj, k: Proj, v: Proj, *, out=None, U=None, ws=None, stream=None, plan=None):
     """Returns (Q, K, V, U) with U = [X A_q | X A_k | X A_v]."""
     torch = _torch()
     T, H, Ns, r, dt = _qkv_dims(X, q, k, v)
@@ -419,8 +438,8 @@ def qkv_fwd(X, q: Proj, k: Proj, v: Proj, *, out=None, U=None, ws=None, stream=N
     if U is not None:
         _need("U", U, (T, 3 * r), X.dtype, X.device)
     _on_gpu(X, ws)
-    d = L.lora_qkv_desc(T, H, Ns[0], Ns[1], Ns[2], r, dt, 0)
-    fb, _ = qkv_workspace_size(T, H, *Ns, r, dt)
+    d = _set_plan(L.lora_qkv_desc(T, H, Ns[0], Ns[1], Ns[2], r, dt, 0), plan)
+    fb, _ = qkv_workspace_size(T, H, *Ns, r, dt, plan)
     with _on(stream):
         if out is None:
             out = [torch.empty((T, n), dtype=X.dtype, device=X.device) for n in Ns]
@@ -435,7 +454,8 @@ def qkv_fwd(X, q: Proj, k: Proj, v: Proj, *, out=None, U=None, ws=None, stream=N
     return out[0], out[1], out[2], U
 
 
-def qkv_bwd(dQ, dK, dV, X, U, q: Proj, k: Proj, v: Proj, *, dX=None, grads=None, ws=None, stream=None):
+def qkv_bwd(dQ, dK, dV, X, U, q: Proj, k: Proj, v: Proj, *, dX=None, grads=None, ws=None, stream=None,
+            plan=None):
     """Returns (dX, grads) with grads = dict(dA_q, dB_q, dA_k, dB_k, dA_v, dB_v).
     ``dX=X`` writes the input gradient over X."""
     torch = _torch()
@@ -450,8 +470,8 @@ def qkv_bwd(dQ, dK, dV, X, U, q: Proj, k: Proj, v: Proj, *, dX=None, grads=None,
             ref = getattr(p, ab)
             _need(f"grads[{key!r}]", grads.get(key), ref.shape, ref.dtype, X.device)
     _on_gpu(X, ws)
-    d = L.lora_qkv_desc(T, H, Ns[0], Ns[1], Ns[2], r, dt, 0)
-    _, bb = qkv_workspace_size(T, H, *Ns, r, dt)
+    d = _set_plan(L.lora_qkv_desc(T, H, Ns[0], Ns[1], Ns[2], r, dt, 0), plan)
+    _, bb = qkv_workspace_size(T, H, *Ns, r, dt, plan)
     with _on(stream):
         if dX is None:
             dX = torch.empty_like(X)
@@ -468,8 +488,8 @@ def qkv_bwd(dQ, dK, dV, X, U, q: Proj, k: Proj, v: Proj, *, dX=None, grads=None,
     return dX, grads
 
 
-def o_workspace_size(T, K, N, r, dtype=L.LORA_BF16):
-    d = L.lora_o_desc(T, K, N, r, dtype, 0)
+def o_workspace_size(T, K, N, r, dtype=L.LORA_BF16, plan=None):
+    d = _set_plan(L.lora_o_desc(T, K, N, r, dtype, 0), plan)
     f, b = C.c_size_t(), C.c_size_t()
     L.call("lora_o_workspace_size", C.byref(d), C.byref(f), C.byref(b))
     return f.value, b.value
@@ -485,7 +505,7 @@ def _o_dims(X, o):
     return T, K, N, r, dt
 
 
-def o_fwd(X, o: Proj, *, Y=None, U=None, ws=None, stream=None):
+def o_fwd(X, o: Proj, *, Y=None, U=None, ws=None, stream=None, plan=None):
     """Returns (Y, U)."""
     torch = _torch()
     T, K, N, r, dt = _o_dims(X, o)
@@ -494,8 +514,8 @@ def o_fwd(X, o: Proj, *, Y=None, U=None, ws=None, stream=None):
     if U is not None:
         _need("U", U, (T, r), X.dtype, X.device)
     _on_gpu(X, ws)
-    d = L.lora_o_desc(T, K, N, r, dt, 0)
-    fb, _ = o_workspace_size(T, K, N, r, dt)
+    d = _set_plan(L.lora_o_desc(T, K, N, r, dt, 0), plan)
+    fb, _ = o_workspace_size(T, K, N, r, dt, plan)
     with _on(stream):
         if Y is None:
             Y = torch.empty((T, N), dtype=X.dtype, device=X.device)
@@ -509,7 +529,7 @@ def o_fwd(X, o: Proj, *, Y=None, U=None, ws=None, stream=None):
     return Y, U
 
 
-def o_fwd_noalloc(X, o: Proj, *, Y, U, stream=None):
+def o_fwd_noalloc(X, o: Proj, *, Y, U, stream=None, plan=None):
     """o_fwd for callers that cannot allocate: the library takes its scratch
     from a static per-GPU array (at most NOALLOC_SCRATCH_BYTES, shared by all
     such calls on that GPU) and allocates nothing; the caller passes the
@@ -518,7 +538,7 @@ def o_fwd_noalloc(X, o: Proj, *, Y, U, stream=None):
     _need("Y", Y, (T, N), X.dtype, X.device)
     _need("U", U, (T, r), X.dtype, X.device)
     _on_gpu(X)
-    d = L.lora_o_desc(T, K, N, r, dt, 0)
+    d = _set_plan(L.lora_o_desc(T, K, N, r, dt, 0), plan)
     keep = []
     L.call("lora_o_fwd_noalloc", C.byref(d), _ptr(X), C.byref(o.c_struct(keep)), _ptr(Y), _ptr(U),
            _stream(stream))
@@ -528,7 +548,7 @@ def o_fwd_noalloc(X, o: Proj, *, Y, U, stream=None):
 NOALLOC_SCRATCH_BYTES = L.NOALLOC_SCRATCH_BYTES
 
 
-def o_bwd(dY, X, U, o: Proj, *, dX=None, dA=None, dB=None, ws=None, stream=None):
+def o_bwd(dY, X, U, o: Proj, *, dX=None, dA=None, dB=None, ws=None, stream=None, plan=None):
     """Returns (dX, dA, dB).  ``dX=X`` writes the input gradient over X."""
     torch = _torch()
     T, K, N, r, dt = _o_dims(X, o)
@@ -541,8 +561,8 @@ def o_bwd(dY, X, U, o: Proj, *, dX=None, dA=None, dB=None, ws=None, stream=None)
     if dB is not None:
         _need("dB", dB, o.B.shape, o.B.dtype, X.device)
     _on_gpu(X, ws)
-    d = L.lora_o_desc(T, K, N, r, dt, 0)
-    _, bb = o_workspace_size(T, K, N, r, dt)
+    d = _set_plan(L.lora_o_desc(T, K, N, r, dt, 0), plan)
+    _, bb = o_workspace_size(T, K, N, r, dt, plan)
     with _on(stream):
         dX = torch.empty_like(X) if dX is None else dX
         dA = torch.empty_like(o.A) if dA is None else dA

@@ -33,8 +33,17 @@ class lora_proj(C.Structure):
     _fields_ = [("W", vp), ("nf4", C.POINTER(lora_nf4)), ("A", vp), ("B", vp), ("scale", C.c_float)]
 
 
+class lora_gemm_plan(C.Structure):
+    _fields_ = [("group", i32), ("ksplit", i32)]
+
+
+class lora_plan(C.Structure):
+    _fields_ = [("gemm", lora_gemm_plan * 2)]
+
+
 class lora_mlp_desc(C.Structure):
-    _fields_ = [("T", i64), ("H", i64), ("I", i64), ("r", i64), ("act", i32), ("dtype", i32)]
+    _fields_ = [("T", i64), ("H", i64), ("I", i64), ("r", i64), ("act", i32), ("dtype", i32),
+                ("plan", C.POINTER(lora_plan))]
 
 
 class lora_mlp_saved(C.Structure):
@@ -46,7 +55,8 @@ class lora_mlp_grads(C.Structure):
 
 
 class lora_relu2_mlp_desc(C.Structure):
-    _fields_ = [("T", i64), ("H", i64), ("I", i64), ("r", i64), ("dtype", i32), ("reserved", i32)]
+    _fields_ = [("T", i64), ("H", i64), ("I", i64), ("r", i64), ("dtype", i32), ("reserved", i32),
+                ("plan", C.POINTER(lora_plan))]
 
 
 class lora_relu2_mlp_saved(C.Structure):
@@ -59,7 +69,7 @@ class lora_relu2_mlp_grads(C.Structure):
 
 class lora_qkv_desc(C.Structure):
     _fields_ = [("T", i64), ("H", i64), ("Nq", i64), ("Nk", i64), ("Nv", i64), ("r", i64),
-                ("dtype", i32), ("reserved", i32)]
+                ("dtype", i32), ("reserved", i32), ("plan", C.POINTER(lora_plan))]
 
 
 class lora_qkv_grads(C.Structure):
@@ -71,7 +81,8 @@ class lora_trace_entry(C.Structure):
 
 
 class lora_o_desc(C.Structure):
-    _fields_ = [("T", i64), ("K", i64), ("N", i64), ("r", i64), ("dtype", i32), ("reserved", i32)]
+    _fields_ = [("T", i64), ("K", i64), ("N", i64), ("r", i64), ("dtype", i32), ("reserved", i32),
+                ("plan", C.POINTER(lora_plan))]
 
 
 P = C.POINTER

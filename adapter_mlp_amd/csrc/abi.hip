@@ -59,6 +59,7 @@ struct Ctx {
   bool bf16;
   bool f32lora;  // LORA_BF16_F32LORA: fp32 adapters and adapter gradients
   size_t es;     // element size of the activations and the base
+  const lora_plan* plan = nullptr;  // the call's GEMM launch plan (bf16 only)
   // Width of the GEMM's LoRA K tile: one full 64-wide tile (zero-padded) in bf16.
   int64_t rl(int64_t w) const { return bf16 ? 64 : w; }
 };
@@ -182,6 +183,12 @@ const void* coff(const void* p, int64_t elems, const Ctx& c) {
 }
 void* offw(void* p, int64_t elems, const Ctx& c) { return static_cast<char*>(p) + elems * (int64_t)c.es; }
 
+// Plan entry i of the call (zeros: the library's defaults; always zeros in fp32).
+lora_gemm_plan gemm_plan(const Ctx& c, int i) {
+  if (!c.bf16 || c.plan == nullptr) return lora_gemm_plan{0, 0};
+  return c.plan->gemm[i];
+}
+
 // Split-K factor of a bf16 store GEMM [M, N] over K (LoRA tile included): the
 // s in 1..4 that best fills the last wave of 256x256 tiles on the 256 CUs,
 // weighed against the fp32 partials it writes and reads (8 s bytes per
@@ -207,14 +214,52 @@ int gemm_ksplit(const Ctx& c, int64_t M, int64_t N, int64_t K) {
   }
   return bs;
 }
-// fp32 partial floats a split store GEMM needs (0 without a split)
-int64_t kpart_floats(const Ctx& c, int64_t M, int64_t N, int64_t K) {
-  const int s = gemm_ksplit(c, M, N, K);
+// fp32 partial floats a split store GEMM needs (0 without a split); `forced`
+// is the plan's ksplit (0: the model above).
+int64_t kpart_floats(const Ctx& c, int64_t M, int64_t N, int64_t K, int forced = 0) {
+  if (!c.bf16) return 0;
+  const int s = forced > 0 ? forced : gemm_ksplit(c, M, N, K);
   return s > 1 ? s * M * N : 0;
 }
 
-// kpart: fp32 scratch of kpart_floats() for a split store GEMM (nullptr: no split)
-hipError_t gemm_on(const Ctx& c, GemmArgs& g, hipStream_t st, int64_t lora_vcols, float* kpart = nullptr) {
+// The plan's value ranges (every call and workspace query; ngemm: GEMMs in
+// the call).
+lora_status plan_ranges(const Ctx& c, int ngemm) {
+  if (c.plan == nullptr || !c.bf16) return LORA_OK;
+  for (int i = 0; i < 2; ++i) {
+    const lora_gemm_plan& g = c.plan->gemm[i];
+    if (i >= ngemm) {
+      CHECK(g.group == 0 && g.ksplit == 0, LORA_EINVAL, "plan.gemm[%d] must be zero: the call has %d GEMM", i, ngemm);
+      continue;
+    }
+    const int gr = g.group;
+    CHECK(gr == 0 || gr == 1 || gr == 2 || gr == 4 || gr == 8 || gr == 16 || gr == 32, LORA_EINVAL,
+          "plan.gemm[%d].group = %d is not 0, 1, 2, 4, 8, 16 or 32", i, gr);
+    CHECK(g.ksplit >= 0 && g.ksplit <= 4, LORA_EINVAL, "plan.gemm[%d].ksplit = %d is not in [0, 4]", i, g.ksplit);
+  }
+  return LORA_OK;
+}
+
+// Split-K entry of plan GEMM i of a call (before anything is enqueued):
+// splittable = a dense bf16 plain-store GEMM with one output region, of
+// [M, N] over K (LoRA tile included).
+lora_status plan_split(const Ctx& c, int i, bool splittable, int64_t M, int64_t N, int64_t K) {
+  const lora_gemm_plan g = gemm_plan(c, i);
+  if (g.ksplit <= 1) return LORA_OK;
+  CHECK(splittable, LORA_EINVAL,
+        "plan.gemm[%d].ksplit = %d: only a dense plain-store GEMM with one output region can split K", i, g.ksplit);
+  CHECK(K / 64 >= g.ksplit, LORA_EINVAL, "plan.gemm[%d].ksplit = %d exceeds the %lld K steps", i, g.ksplit,
+        (long long)(K / 64));
+  CHECK(M * N * 4 < ((int64_t)1 << 31) - 4096, LORA_EINVAL,
+        "plan.gemm[%d]: the fp32 split-K part [%lld, %lld] would exceed 2 GiB", i, (long long)M, (long long)N);
+  return LORA_OK;
+}
+
+// kpart: fp32 scratch of kpart_floats() for a split store GEMM (nullptr: no
+// split); gi: the GEMM's index in the call's plan.
+hipError_t gemm_on(const Ctx& c, GemmArgs& g, hipStream_t st, int64_t lora_vcols, int gi, float* kpart = nullptr) {
+  const lora_gemm_plan gp = gemm_plan(c, gi);
+  g.group = gp.group > 0 ? gp.group : (g.epi == EPI_STORE ? 8 : 4);
   g.lora_vcols = lora_vcols;
   if (c.bf16 && g.RL > 0) {
     // The bf16 kernel runs the LoRA term as one more 64-wide K segment:
@@ -254,7 +299,7 @@ hipError_t gemm_on(const Ctx& c, GemmArgs& g, hipStream_t st, int64_t lora_vcols
   if (kpart != nullptr && c.bf16 && !g.nf4 && g.epi == EPI_STORE && g.nreg == 1) {
     int64_t K = 0;
     for (int s = 0; s < g.nseg; ++s) K += g.seg[s].K;
-    const int ks = gemm_ksplit(c, g.M, g.reg[0].N, K);
+    const int ks = gp.ksplit > 0 ? gp.ksplit : gemm_ksplit(c, g.M, g.reg[0].N, K);
     if (ks > 1) {
       g.ksplit = ks;
       g.kpart = kpart;
@@ -428,7 +473,7 @@ MlpPlan plan_mlp(const Ctx& c, const lora_mlp_desc& d, void* ws_fwd, void* ws_bw
   p.At_d = f.take(r * I * c.es);
   p.Us_d = f.take(T * RLd * c.es);
   p.BLt_d = f.take(H * RLd * c.es);
-  p.kpart = static_cast<float*>(f.take((size_t)kpart_floats(c, T, H, I + RLd) * 4));
+  p.kpart = static_cast<float*>(f.take((size_t)kpart_floats(c, T, H, I + RLd, gemm_plan(c, 1).ksplit) * 4));
   p.upart = fuse_da(c, r) ? static_cast<float*>(f.take((size_t)(cdiv(I, gemm_tile_cols(true, true)) * T * 16 * 4)))
                           : nullptr;
   p.fwd_bytes = f.off;
@@ -452,7 +497,8 @@ MlpPlan plan_mlp(const Ctx& c, const lora_mlp_desc& d, void* ws_fwd, void* ws_bw
     const int64_t bp = 2 * rowcol_batch_partial_floats(T, Kb, 2, 0);
     if (bp > pf) pf = bp;
     // the dX GEMM's split-K partials (the partial buffer is free by then)
-    if (kpart_floats(c, T, H, 2 * I + RLg) > pf) pf = kpart_floats(c, T, H, 2 * I + RLg);
+    const int64_t kx = kpart_floats(c, T, H, 2 * I + RLg, gemm_plan(c, 1).ksplit);
+    if (kx > pf) pf = kx;
   }
   p.partial = static_cast<float*>(b.take((size_t)pf * 4));
   {
@@ -466,6 +512,8 @@ MlpPlan plan_mlp(const Ctx& c, const lora_mlp_desc& d, void* ws_fwd, void* ws_bw
 lora_status validate_mlp(const lora_mlp_desc* d, Ctx& c) {
   CHECK(d != nullptr, LORA_EINVAL, "desc is NULL");
   TRY(check_dtype(d->dtype, c, true));
+  c.plan = d->plan;
+  TRY(plan_ranges(c, 2));
   CHECK(d->act == LORA_ACT_SWIGLU || d->act == LORA_ACT_GEGLU_TANH, LORA_EINVAL, "unknown activation %d", d->act);
   CHECK(d->T >= 0, LORA_ESHAPE, "T = %lld is negative", (long long)d->T);
   TRY(check_dim(c, d->H, "H"));
@@ -505,7 +553,7 @@ Relu2Plan plan_relu2(const Ctx& c, const lora_relu2_mlp_desc& d, void* ws_fwd, v
   p.At_d = f.take(r * I * c.es);
   p.Us_d = f.take(T * RL * c.es);
   p.BLt_d = f.take(H * RL * c.es);
-  p.kpart = static_cast<float*>(f.take((size_t)kpart_floats(c, T, H, I + RL) * 4));
+  p.kpart = static_cast<float*>(f.take((size_t)kpart_floats(c, T, H, I + RL, gemm_plan(c, 1).ksplit) * 4));
   p.upart = fuse_da(c, r) ? static_cast<float*>(f.take((size_t)(cdiv(I, gemm_tile_cols(true, false)) * T * 16 * 4)))
                           : nullptr;
   p.fwd_bytes = f.off;
@@ -522,7 +570,8 @@ Relu2Plan plan_relu2(const Ctx& c, const lora_relu2_mlp_desc& d, void* ws_fwd, v
     const int64_t a = colproj_partial_floats(T, H, (int)r), bb = colproj_partial_floats(T, I, (int)r);
     pf = a > bb ? a : bb;
     if (fuse_da(c, r) && fused_da_floats(T, I) > pf) pf = fused_da_floats(T, I);
-    if (kpart_floats(c, T, H, I + RL) > pf) pf = kpart_floats(c, T, H, I + RL);  // dX split-K
+    const int64_t kx = kpart_floats(c, T, H, I + RL, gemm_plan(c, 1).ksplit);  // dX split-K
+    if (kx > pf) pf = kx;
   }
   p.partial = static_cast<float*>(b.take((size_t)pf * 4));
   p.rpartial = c.bf16 ? static_cast<float*>(b.take((size_t)rowcol_partial_floats(T, I > H ? I : H) * 4)) : nullptr;
@@ -533,6 +582,8 @@ Relu2Plan plan_relu2(const Ctx& c, const lora_relu2_mlp_desc& d, void* ws_fwd, v
 lora_status validate_relu2(const lora_relu2_mlp_desc* d, Ctx& c) {
   CHECK(d != nullptr, LORA_EINVAL, "desc is NULL");
   TRY(check_dtype(d->dtype, c, true));
+  c.plan = d->plan;
+  TRY(plan_ranges(c, 2));
   CHECK(d->reserved == 0, LORA_EINVAL, "reserved field must be 0");
   CHECK(d->T >= 0, LORA_ESHAPE, "T = %lld is negative", (long long)d->T);
   TRY(check_dim(c, d->H, "H"));
@@ -578,7 +629,8 @@ QkvPlan plan_qkv(const Ctx& c, const lora_qkv_desc& d, void* wf, void* wb) {
                                  rowcol_batch_partial_floats(T, Kb, 3, 2),
                              colproj_partial_floats(T, H, (int)(3 * r))};
     for (int i = 0; i < 2; ++i) pf = cand[i] > pf ? cand[i] : pf;
-    if (kpart_floats(c, T, H, N + RL) > pf) pf = kpart_floats(c, T, H, N + RL);  // dX split-K
+    const int64_t kx = kpart_floats(c, T, H, N + RL, gemm_plan(c, 0).ksplit);  // dX split-K
+    if (kx > pf) pf = kx;
   }
   p.partial = static_cast<float*>(b.take((size_t)pf * 4));
   p.rpartial = c.bf16 ? static_cast<float*>(b.take(
@@ -592,6 +644,8 @@ QkvPlan plan_qkv(const Ctx& c, const lora_qkv_desc& d, void* wf, void* wb) {
 lora_status validate_qkv(const lora_qkv_desc* d, Ctx& c) {
   CHECK(d != nullptr, LORA_EINVAL, "desc is NULL");
   TRY(check_dtype(d->dtype, c, true));
+  c.plan = d->plan;
+  TRY(plan_ranges(c, 1));
   CHECK(d->reserved == 0, LORA_EINVAL, "reserved field must be 0");
   CHECK(d->T >= 0, LORA_ESHAPE, "T = %lld is negative", (long long)d->T);
   TRY(check_dim(c, d->H, "H"));
@@ -630,7 +684,7 @@ OPlan plan_o(const Ctx& c, int64_t T, int64_t K, int64_t N, int64_t r, bool tmp_
   p.Us = f.take(T * RL * c.es);
   p.BLt = f.take(N * RL * c.es);
   p.U_tmp = tmp_u ? f.take(T * r * c.es) : nullptr;
-  p.kpart = split ? static_cast<float*>(f.take((size_t)kpart_floats(c, T, N, K + (r > 0 ? RL : 0)) * 4)) : nullptr;
+  p.kpart = split ? static_cast<float*>(f.take((size_t)kpart_floats(c, T, N, K + (r > 0 ? RL : 0), gemm_plan(c, 0).ksplit) * 4)) : nullptr;
   p.fwd_bytes = f.off;
   Ws b(wb);
   p.ad_b = b.take(staged_bytes(c, ad, 1, r));
@@ -640,7 +694,7 @@ OPlan plan_o(const Ctx& c, int64_t T, int64_t K, int64_t N, int64_t r, bool tmp_
   if (c.bf16) {
     const int64_t a = colproj_partial_floats(T, N, (int)r), bb = colproj_partial_floats(T, K, (int)r);
     pf = a > bb ? a : bb;
-    const int64_t kp = kpart_floats(c, T, K, N + (r > 0 ? RL : 0));  // input-gradient GEMM split-K
+    const int64_t kp = kpart_floats(c, T, K, N + (r > 0 ? RL : 0), gemm_plan(c, 0).ksplit);  // input-gradient split-K
     pf = kp > pf ? kp : pf;
   }
   p.partial = static_cast<float*>(b.take((size_t)pf * 4));
@@ -652,6 +706,8 @@ OPlan plan_o(const Ctx& c, int64_t T, int64_t K, int64_t N, int64_t r, bool tmp_
 lora_status validate_o(const lora_o_desc* d, Ctx& c) {
   CHECK(d != nullptr, LORA_EINVAL, "desc is NULL");
   TRY(check_dtype(d->dtype, c, true));
+  c.plan = d->plan;
+  TRY(plan_ranges(c, 1));
   CHECK(d->reserved == 0, LORA_EINVAL, "reserved field must be 0");
   CHECK(d->T >= 0, LORA_ESHAPE, "T = %lld is negative", (long long)d->T);
   TRY(check_dim(c, d->K, "K"));
@@ -708,7 +764,7 @@ lora_status proj_forward(const Ctx& c, int64_t T, int64_t K, int64_t N, int64_t 
   g.reg[0].N = N;
   g.reg[0].out = Y;
   g.reg[0].ldo = N;
-  LAUNCH(gemm_on(c, g, st, N, p.kpart));
+  LAUNCH(gemm_on(c, g, st, N, 0, p.kpart));
   return LORA_OK;
 }
 
@@ -748,7 +804,7 @@ lora_status proj_input_grad(const Ctx& c, int64_t T, int64_t K, int64_t N, int64
   g.reg[0].N = K;
   g.reg[0].out = dX;
   g.reg[0].ldo = K;
-  LAUNCH(gemm_on(c, g, st, K, p.partial));
+  LAUNCH(gemm_on(c, g, st, K, 0, p.partial));
   return LORA_OK;
 }
 
@@ -836,6 +892,8 @@ lora_status lora_mlp_fwd(const lora_mlp_desc* d, const void* X, const lora_proj*
   TRY(check_proj(c, down, I, H, "down"));
   CHECK((gate->nf4 != nullptr) == (up->nf4 != nullptr), LORA_EUNSUPPORTED, "gate and up must both be NF4 or both dense");
   CHECK(!overlaps(Y, T * H * c.es, X, T * H * c.es), LORA_EUNSUPPORTED, "Y aliases X");
+  TRY(plan_split(c, 0, false, 0, 0, 0));
+  TRY(plan_split(c, 1, down->nf4 == nullptr, T, H, I + c.rl(r)));
   MlpPlan need = plan_mlp(c, *d, nullptr, nullptr);
   TRY(check_ws(ws, ws_bytes, need.fwd_bytes));
   if (T == 0) return LORA_OK;
@@ -919,7 +977,7 @@ lora_status lora_mlp_fwd(const lora_mlp_desc* d, const void* X, const lora_proj*
     g.ld_adt = I;
     g.u_R = (int)r;
   }
-  LAUNCH(gemm_on(c, g, st, 2 * I));
+  LAUNCH(gemm_on(c, g, st, 2 * I, 0));
 
   // U_d = h A_d, then the down GEMM
   RowProjArgs rd = rowproj_args(p.h, I, T, I, p.At_d, I, (int)r, (int)RLd, (int)r);
@@ -954,7 +1012,7 @@ lora_status lora_mlp_fwd(const lora_mlp_desc* d, const void* X, const lora_proj*
   gd.RL = (int)RLd;
   gd.BLt = p.BLt_d;
   gd.ldbl = RLd;
-  LAUNCH(gemm_on(c, gd, st, H, p.kpart));
+  LAUNCH(gemm_on(c, gd, st, H, 1, p.kpart));
   return LORA_OK;
 }
 
@@ -983,6 +1041,8 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, 
   TRY(check_proj(c, down, I, H, "down"));
   CHECK((gate->nf4 != nullptr) == (up->nf4 != nullptr), LORA_EUNSUPPORTED, "gate and up must both be NF4 or both dense");
   CHECK(dX == X || !overlaps(dX, T * H * c.es, X, T * H * c.es), LORA_EUNSUPPORTED, "dX partly overlaps X");
+  TRY(plan_split(c, 0, false, 0, 0, 0));
+  TRY(plan_split(c, 1, gate->nf4 == nullptr, T, H, 2 * I + c.rl(2 * r)));
   MlpPlan need = plan_mlp(c, *d, nullptr, nullptr);
   TRY(check_ws(ws, ws_bytes, need.bwd_bytes));
   MlpPlan p = plan_mlp(c, *d, nullptr, ws);
@@ -1058,7 +1118,7 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, 
   } else {
     g.h_out = p.hb;
   }
-  LAUNCH(gemm_on(c, g, st, I));
+  LAUNCH(gemm_on(c, g, st, I, 0));
 
   // dA_d = s_d h^T P_d  (P_d already scaled): the reduce of the epilogue's
   // per-m-tile partials, or a pass over the stored h
@@ -1131,7 +1191,7 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, 
   gx.RL = (int)RLg;
   gx.BLt = p.BLt_dx;
   gx.ldbl = RLg;
-  if (T > 0) LAUNCH(gemm_on(c, gx, st, H, p.partial));
+  if (T > 0) LAUNCH(gemm_on(c, gx, st, H, 1, p.partial));
   return LORA_OK;
 }
 
@@ -1162,6 +1222,8 @@ lora_status lora_relu2_mlp_fwd(const lora_relu2_mlp_desc* d, const void* X, cons
   TRY(check_proj(c, up, H, I, "up"));
   TRY(check_proj(c, down, I, H, "down"));
   CHECK(!overlaps(Y, T * H * c.es, X, T * H * c.es), LORA_EUNSUPPORTED, "Y aliases X");
+  TRY(plan_split(c, 0, false, 0, 0, 0));
+  TRY(plan_split(c, 1, down->nf4 == nullptr, d->T, d->H, d->I + c.rl(d->r)));
   Relu2Plan need = plan_relu2(c, *d, nullptr, nullptr);
   TRY(check_ws(ws, ws_bytes, need.fwd_bytes));
   if (T == 0) return LORA_OK;
@@ -1234,7 +1296,7 @@ lora_status lora_relu2_mlp_fwd(const lora_relu2_mlp_desc* d, const void* X, cons
     g.ld_adt = I;
     g.u_R = (int)r;
   }
-  LAUNCH(gemm_on(c, g, st, I));
+  LAUNCH(gemm_on(c, g, st, I, 0));
 
   // U_d = h A_d, then the down GEMM
   RowProjArgs rd = rowproj_args(p.h, I, T, I, p.At_d, I, (int)r, (int)RL, (int)r);
@@ -1268,7 +1330,7 @@ lora_status lora_relu2_mlp_fwd(const lora_relu2_mlp_desc* d, const void* X, cons
   gd.RL = (int)RL;
   gd.BLt = p.BLt_d;
   gd.ldbl = RL;
-  LAUNCH(gemm_on(c, gd, st, H, p.kpart));
+  LAUNCH(gemm_on(c, gd, st, H, 1, p.kpart));
   return LORA_OK;
 }
 
@@ -1293,6 +1355,8 @@ lora_status lora_relu2_mlp_bwd(const lora_relu2_mlp_desc* d, const void* dY, con
   TRY(check_proj(c, up, H, I, "up"));
   TRY(check_proj(c, down, I, H, "down"));
   CHECK(dX == X || !overlaps(dX, T * H * c.es, X, T * H * c.es), LORA_EUNSUPPORTED, "dX partly overlaps X");
+  TRY(plan_split(c, 0, false, 0, 0, 0));
+  TRY(plan_split(c, 1, up->nf4 == nullptr, d->T, d->H, d->I + c.rl(d->r)));
   Relu2Plan need = plan_relu2(c, *d, nullptr, nullptr);
   TRY(check_ws(ws, ws_bytes, need.bwd_bytes));
   Relu2Plan p = plan_relu2(c, *d, nullptr, ws);
@@ -1363,7 +1427,7 @@ lora_status lora_relu2_mlp_bwd(const lora_relu2_mlp_desc* d, const void* dY, con
   } else {
     g.h_out = p.hb;
   }
-  LAUNCH(gemm_on(c, g, st, I));
+  LAUNCH(gemm_on(c, g, st, I, 0));
 
   // dA_d = s_d h^T P_d  (P_d already scaled): the reduce of the epilogue's
   // per-m-tile partials, or a pass over the stored h
@@ -1413,7 +1477,7 @@ lora_status lora_relu2_mlp_bwd(const lora_relu2_mlp_desc* d, const void* dY, con
   gx.RL = (int)RL;
   gx.BLt = p.BLt_dx;
   gx.ldbl = RL;
-  if (T > 0) LAUNCH(gemm_on(c, gx, st, H, p.partial));
+  if (T > 0) LAUNCH(gemm_on(c, gx, st, H, 1, p.partial));
   return LORA_OK;
 }
 
@@ -1445,6 +1509,7 @@ lora_status lora_qkv_fwd(const lora_qkv_desc* d, const void* X, const lora_proj*
   TRY(check_proj(c, v, H, Nv, "v"));
   CHECK(((q->nf4 != nullptr) == (k->nf4 != nullptr)) && ((k->nf4 != nullptr) == (v->nf4 != nullptr)),
         LORA_EUNSUPPORTED, "q, k, v must all be NF4 or all dense");
+  TRY(plan_split(c, 0, false, 0, 0, 0));
   QkvPlan need = plan_qkv(c, *d, nullptr, nullptr);
   TRY(check_ws(ws, ws_bytes, need.fwd_bytes));
   if (T == 0) return LORA_OK;
@@ -1514,7 +1579,7 @@ lora_status lora_qkv_fwd(const lora_qkv_desc* d, const void* X, const lora_proj*
   g.RL = (int)RL;
   g.BLt = p.BLt;
   g.ldbl = RL;
-  LAUNCH(gemm_on(c, g, st, Nq + Nk + Nv));
+  LAUNCH(gemm_on(c, g, st, Nq + Nk + Nv, 0));
   return LORA_OK;
 }
 
@@ -1543,6 +1608,7 @@ lora_status lora_qkv_bwd(const lora_qkv_desc* d, const void* dQ, const void* dK,
   CHECK(((q->nf4 != nullptr) == (k->nf4 != nullptr)) && ((k->nf4 != nullptr) == (v->nf4 != nullptr)),
         LORA_EUNSUPPORTED, "q, k, v must all be NF4 or all dense");
   CHECK(dX == X || !overlaps(dX, T * H * c.es, X, T * H * c.es), LORA_EUNSUPPORTED, "dX partly overlaps X");
+  TRY(plan_split(c, 0, q->nf4 == nullptr, T, H, Nq + Nk + Nv + c.rl(3 * r)));
   QkvPlan need = plan_qkv(c, *d, nullptr, nullptr);
   TRY(check_ws(ws, ws_bytes, need.bwd_bytes));
   QkvPlan p = plan_qkv(c, *d, nullptr, ws);
@@ -1623,7 +1689,7 @@ lora_status lora_qkv_bwd(const lora_qkv_desc* d, const void* dQ, const void* dK,
   g.RL = (int)RL;
   g.BLt = p.BLt_dx;
   g.ldbl = RL;
-  LAUNCH(gemm_on(c, g, st, H, p.partial));
+  LAUNCH(gemm_on(c, g, st, H, 0, p.partial));
   return LORA_OK;
 }
 
@@ -1648,6 +1714,7 @@ lora_status lora_o_fwd(const lora_o_desc* d, const void* X, const lora_proj* o, 
   TRY(check_tptr(c, Y, T, "Y"));
   TRY(check_tptr(c, U, T, "U"));
   TRY(check_proj(c, o, d->K, d->N, "o"));
+  TRY(plan_split(c, 0, o->nf4 == nullptr, d->T, d->N, d->K + c.rl(d->r)));
   OPlan need = plan_o(c, d->T, d->K, d->N, d->r, false, nullptr, nullptr);
   TRY(check_ws(ws, ws_bytes, need.fwd_bytes));
   if (d->T == 0) return LORA_OK;
@@ -1669,6 +1736,7 @@ lora_status lora_o_fwd_noalloc(const lora_o_desc* d, const void* X, const lora_p
   TRY(check_tptr(c, U, T, "U"));
   TRY(check_proj(c, o, d->K, d->N, "o"));
   // the GEMM runs unsplit here: no fp32 split-K partials in the scratch
+  TRY(plan_split(c, 0, false, 0, 0, 0));
   OPlan need = plan_o(c, d->T, d->K, d->N, d->r, false, nullptr, nullptr, false);
   CHECK(need.fwd_bytes <= kScratchBytes, LORA_EWORKSPACE,
         "this call needs %zu bytes of scratch; the static scratch holds %zu (fewer tokens per call fit)",
@@ -1697,6 +1765,7 @@ lora_status lora_o_bwd(const lora_o_desc* d, const void* dY, const void* X, cons
   TRY(check_ptr(c, dB, "dB"));
   TRY(check_proj(c, o, K, N, "o"));
   CHECK(dX == X || !overlaps(dX, T * K * c.es, X, T * K * c.es), LORA_EUNSUPPORTED, "dX partly overlaps X");
+  TRY(plan_split(c, 0, o->nf4 == nullptr, T, K, N + c.rl(r)));
   OPlan need = plan_o(c, T, K, N, r, false, nullptr, nullptr);
   TRY(check_ws(ws, ws_bytes, need.bwd_bytes));
   OPlan p = plan_o(c, T, K, N, r, false, nullptr, ws);

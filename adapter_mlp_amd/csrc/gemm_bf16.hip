@@ -67,9 +67,9 @@ __device__ __forceinline__ void wave_sync() {
 // m-tiles (n-major inside a group): the 32 tiles an XCD holds at once then
 // share G activation panels and 32 / G weight panels in its L2 (8 x 4 or
 // 4 x 8 panels fetch the same bytes; measured, groups of 4 suit the
-// activation-epilogue GEMMs and groups of 8 the store GEMMs).
-template <int G>
-__device__ __forceinline__ void tile_coords(int bid, int nb, int ntm, int ntn, int& tm, int& tn) {
+// activation-epilogue GEMMs and groups of 8 the store GEMMs, the defaults; a
+// call's plan may choose another G).  All arguments are uniform.
+__device__ __forceinline__ void tile_coords(int bid, int nb, int ntm, int ntn, int G, int& tm, int& tn) {
   const int q = nb >> 3, rem = nb & 7, x = bid & 7, j = bid >> 3;
   const int lid = (x < rem) ? x * (q + 1) + j : rem * (q + 1) + (x - rem) * q + j;
   const int per_group = G * ntn;
@@ -605,8 +605,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   // split-K: block u works on K part u / ntiles of tile u % ntiles
   const int ntiles = (int)(args.ntile_m * args.ntile_n);
   const int kp = args.ksplit > 1 ? (int)blockIdx.x / ntiles : 0;
-  tile_coords<EPI == EPI_STORE ? 8 : 4>((int)blockIdx.x - kp * ntiles, ntiles, (int)args.ntile_m,
-                                         (int)args.ntile_n, tm, tn);
+  tile_coords((int)blockIdx.x - kp * ntiles, ntiles, (int)args.ntile_m, (int)args.ntile_n, args.group, tm, tn);
   tm = __builtin_amdgcn_readfirstlane(tm);
   tn = __builtin_amdgcn_readfirstlane(tn);
   int reg = 0;

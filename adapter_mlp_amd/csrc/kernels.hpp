@@ -55,7 +55,8 @@ struct GemmRegion {
 struct GemmArgs {
   int64_t M;
   int32_t nseg, nreg;
-  int32_t dual, epi, act, nf4, bkind, pad_;
+  int32_t dual, epi, act, nf4, bkind;
+  int32_t group;  // m-tiles per group of the XCD-aware tile order (bf16)
   GemmSeg seg[4];  // up to 3 main segments + the LoRA tail as a segment
   GemmRegion reg[3];
   int64_t ntile_m, ntile_n;

@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define LORA_MI355X_VERSION 1
+#define LORA_MI355X_VERSION 2
 
 typedef enum lora_status {
   LORA_OK = 0,
@@ -124,6 +124,35 @@ typedef struct lora_proj {
   float scale;
 } lora_proj;
 
+/* Optional launch plan of a call's GEMMs ("loralei" README, section "Use":
+ * per GPU and shape, a few valid tile configurations are timed and the
+ * fastest is kept in a cache, with a conservative default on a miss).  The
+ * library keeps no such cache: a caller (the Python tuner in
+ * adapter_mlp_amd.tune) times candidates, stores the winners, and passes the
+ * plan for a shape in the call's descriptor; NULL, or an all-zero entry,
+ * keeps the library's defaults.  Plans change only the order of work and
+ * how K is split, never what is computed; they are ignored in fp32.
+ *   group:  m-tiles per group of the XCD-aware tile order (the tiles an XCD
+ *           holds at once share group activation panels): 0 = default (4 for
+ *           activation epilogues, 8 for plain stores), or 1, 2, 4, 8, 16, 32;
+ *   ksplit: 0 = the library's split-K model, 1 = no split, 2..4 = that many
+ *           K parts (fp32 partials in the workspace, added in a fixed order).
+ *           Only a dense plain-store GEMM with one output region can split;
+ *           elsewhere ksplit must be 0 or 1.  Each part needs at least one
+ *           K step of 64.
+ * gemm[] lists the call's GEMMs in launch order: gated / ReLU^2 MLP forward:
+ * [0] gate/up (or up), [1] down; MLP backward: [0] dh, [1] dX; Q/K/V and O,
+ * forward or backward: [0] (gemm[1] must be zero).  An invalid entry returns
+ * LORA_EINVAL.  The workspace queries take the plan into account. */
+typedef struct lora_gemm_plan {
+  int32_t group;
+  int32_t ksplit;
+} lora_gemm_plan;
+
+typedef struct lora_plan {
+  lora_gemm_plan gemm[2];
+} lora_plan;
+
 /* ------------------------------------------------------------------------ */
 /* Library information                                                       */
 /* ------------------------------------------------------------------------ */
@@ -146,6 +175,7 @@ typedef struct lora_mlp_desc {
   int64_t r;     /* adapter rank, shared by gate, up and down */
   int32_t act;   /* lora_act */
   int32_t dtype; /* lora_dtype */
+  const lora_plan* plan; /* optional GEMM launch plan (NULL: defaults) */
 } lora_mlp_desc;
 
 /* Tensors the forward saves for the backward (caller-owned, compute dtype):
@@ -210,6 +240,7 @@ typedef struct lora_relu2_mlp_desc {
   int64_t r;        /* adapter rank, shared by up and down */
   int32_t dtype;    /* lora_dtype */
   int32_t reserved; /* must be 0 */
+  const lora_plan* plan; /* optional GEMM launch plan (NULL: defaults) */
 } lora_relu2_mlp_desc;
 
 /* Saved by the forward (caller-owned, compute dtype): u [T, I] = the up
@@ -261,6 +292,7 @@ typedef struct lora_qkv_desc {
   int64_t r;          /* adapter rank shared by q, k, v */
   int32_t dtype;
   int32_t reserved;   /* must be 0 */
+  const lora_plan* plan; /* optional GEMM launch plan (NULL: defaults) */
 } lora_qkv_desc;
 
 typedef struct lora_qkv_grads {
@@ -302,6 +334,7 @@ typedef struct lora_o_desc {
   int64_t r;
   int32_t dtype;
   int32_t reserved; /* must be 0 */
+  const lora_plan* plan; /* optional GEMM launch plan (NULL: defaults) */
 } lora_o_desc;
 
 lora_status lora_o_workspace_size(const lora_o_desc* desc, size_t* fwd_bytes,

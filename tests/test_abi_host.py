@@ -40,7 +40,7 @@ def test_exports_every_declared_function(L):
 
 def test_version_and_strerror(L):
     lib = L.load()
-    assert lib.lora_version() == 1
+    assert lib.lora_version() == 2
     for s in range(8):
         assert lib.lora_strerror(s)
     assert lib.lora_strerror(0) == b"success"
@@ -263,3 +263,74 @@ def test_relu2_mlp_validation(L):
     assert fwd(nbytes=f.value - 1) == L.LORA_EWORKSPACE
     assert fwd(saved=L.lora_relu2_mlp_saved(FAKE, None)) == L.LORA_EINVAL
     assert fwd(Y=FAKE) == L.LORA_EUNSUPPORTED  # Y aliases X
+
+
+def test_plan_validation(L):
+    """Per-call GEMM plans: value ranges, split-K only where a GEMM can split,
+    unused entries zero; the workspace query sizes a forced split."""
+    f, b = C.c_size_t(), C.c_size_t()
+
+    def plan(g0=(0, 0), g1=(0, 0)):
+        p = L.lora_plan()
+        p.gemm[0].group, p.gemm[0].ksplit = g0
+        p.gemm[1].group, p.gemm[1].ksplit = g1
+        return p
+
+    def mlp_ws(p):
+        d = L.lora_mlp_desc(8192, 4096, 1024, 16, 0, L.LORA_BF16, C.pointer(p))
+        st = _status(L, "lora_mlp_workspace_size", C.byref(d), C.byref(f), C.byref(b))
+        return st, f.value, b.value
+
+    st, f0, b0 = mlp_ws(plan())
+    assert st == L.LORA_OK
+    assert mlp_ws(plan(g0=(3, 0)))[0] == L.LORA_EINVAL        # group not a power of two
+    assert mlp_ws(plan(g0=(64, 0)))[0] == L.LORA_EINVAL       # group too large
+    assert mlp_ws(plan(g1=(8, 5)))[0] == L.LORA_EINVAL        # ksplit > 4
+    assert mlp_ws(plan(g1=(8, -1)))[0] == L.LORA_EINVAL
+    st, f4, b4 = mlp_ws(plan(g0=(16, 1), g1=(2, 4)))          # forced 4-way split of down and dX
+    assert st == L.LORA_OK
+    assert f4 - f0 >= 4 * 8192 * 4096 * 4 - 4096              # the down GEMM's fp32 parts
+    assert b4 >= b0
+    # the call rejects a split of an activation-epilogue GEMM before anything is enqueued
+    sv = L.lora_mlp_saved(FAKE, FAKE, FAKE)
+    g, u, dn = _proj(L), _proj(L), _proj(L)
+    p = plan(g0=(4, 2))
+    d = L.lora_mlp_desc(128, 256, 768, 16, 0, L.LORA_BF16, C.pointer(p))
+    _status(L, "lora_mlp_workspace_size", C.byref(d), C.byref(f), C.byref(b))
+    st = _status(L, "lora_mlp_fwd", C.byref(d), FAKE, C.byref(g), C.byref(u), C.byref(dn), FAKE * 2, C.byref(sv),
+                 FAKE * 3, f.value, None)
+    assert st == L.LORA_EINVAL and b"only a dense plain-store GEMM" in L.load().lora_last_error()
+    # an NF4 base cannot split either
+    q = L.lora_nf4(FAKE, FAKE, FAKE, FAKE, 256, 768)
+    p = plan(g0=(4, 2))
+    do = L.lora_o_desc(64, 256, 768, 16, L.LORA_BF16, 0, C.pointer(p))
+    _status(L, "lora_o_workspace_size", C.byref(do), C.byref(f), C.byref(b))
+    st = _status(L, "lora_o_fwd", C.byref(do), FAKE, C.byref(_proj(L, W=None, nf4=q)), FAKE * 2, FAKE * 3, FAKE * 4,
+                 f.value, None)
+    assert st == L.LORA_EINVAL
+    # a one-GEMM call takes no second entry; more parts than K steps are refused
+    p = plan(g1=(4, 0))
+    do = L.lora_o_desc(64, 256, 768, 16, L.LORA_BF16, 0, C.pointer(p))
+    assert _status(L, "lora_o_workspace_size", C.byref(do), C.byref(f), C.byref(b)) == L.LORA_EINVAL
+    p = plan(g0=(4, 4))
+    do = L.lora_o_desc(64, 64, 768, 16, L.LORA_BF16, 0, C.pointer(p))  # K = 64 + the LoRA tile: 2 steps
+    _status(L, "lora_o_workspace_size", C.byref(do), C.byref(f), C.byref(b))
+    st = _status(L, "lora_o_fwd", C.byref(do), FAKE, C.byref(_proj(L)), FAKE * 2, FAKE * 3, FAKE * 4, f.value, None)
+    assert st == L.LORA_EINVAL and b"exceeds the 2 K steps" in L.load().lora_last_error()
+
+
+def test_plan_cache_round_trip(tmp_path, monkeypatch):
+    """The tuner's JSON cache: entries are stored per device and shape, survive
+    a reload, and a miss returns None (the library's defaults)."""
+    from adapter_mlp_amd import tune
+
+    monkeypatch.setattr(tune, "device_key", lambda device=None: "gfx950:256cu:test")
+    path = str(tmp_path / "plans.json")
+    c = tune.PlanCache(path)
+    key = tune.mlp_key(3000, 2560, 9728, 16, "swiglu", 1, False)
+    assert tune.cached(c, key) is None
+    c.put(key, {"fwd": [[4, 0], [16, 2]], "bwd": [[2, 0], [8, 1]], "ms": {}})
+    c2 = tune.PlanCache(path)
+    assert tune.cached(c2, key) == {"fwd": [(4, 0), (16, 2)], "bwd": [(2, 0), (8, 1)]}
+    monkeypatch.setattr(tune, "device_key", lambda device=None: "gfx942:304cu:other")
+    assert tune.cached(c2, key) is None  # plans are per GPU
