@@ -847,7 +847,11 @@ extern "C" {
 int lora_version(void) { return LORA_MI355X_VERSION; }
 
 const char* lora_strerror(lora_status s) {
-  switch (s) {
+  // a C caller may pass any integer: read it as one (loading an enum value
+  // outside the enumerators is undefined in C++)
+  int v;
+  std::memcpy(&v, &s, sizeof v);
+  switch (v) {
     case LORA_OK: return "success";
     case LORA_EINVAL: return "invalid argument";
     case LORA_ESHAPE: return "unsupported shape";

@@ -24,11 +24,11 @@ namespace {
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 // ---------------------------------------------------------------------------
-// rowproj, bf16.  Block = 32 rows of Z over all of K, 4 wavefronts.  Per
+// rowproj, bf16.  Block = 32 rows of Z over all of K, 8 wavefronts.  Per
 // 256-column chunk, Z [32 x 256] and Bt [16 NJ x 256] land in one ring slot;
-// wavefront w multiplies the chunk's K steps 2w and 2w+1 (32 columns each)
-// into acc[row block][column block]; the four partial sums are added in
-// fixed order at the end.  Slot rows are 512 bytes; 16-byte chunk c of row r
+// wavefront w multiplies the chunk's K step w (32 columns) into
+// acc[row block][column block]; the eight partial sums are added in fixed
+// order at the end.  Slot rows are 512 bytes; 16-byte chunk c of row r
 // is stored at c ^ (r & 15), so the 16 rows of a fragment read hit 16
 // different bank groups.
 // ---------------------------------------------------------------------------

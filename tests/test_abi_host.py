@@ -334,3 +334,39 @@ def test_plan_cache_round_trip(tmp_path, monkeypatch):
     assert tune.cached(c2, key) == {"fwd": [(4, 0), (16, 2)], "bwd": [(2, 0), (8, 1)]}
     monkeypatch.setattr(tune, "device_key", lambda device=None: "gfx942:304cu:other")
     assert tune.cached(c2, key) is None  # plans are per GPU
+
+
+def test_validator_under_asan_ubsan(tmp_path):
+    """The host code of csrc/abi.hip (validation, workspace planning, plans)
+    built with AddressSanitizer and UndefinedBehaviorSanitizer, driven by
+    tests/abi_sanitize_driver.cpp through failing calls and workspace
+    queries only (no GPU needed); the other translation units are the
+    regular build's objects.  Any sanitizer report aborts the driver."""
+    import subprocess
+
+    hipcc, clang = "/opt/rocm/bin/hipcc", "/opt/rocm/llvm/bin/clang++"
+    build = os.path.join(ROOT, "adapter_mlp_amd", "_build")
+    others = [os.path.join(build, f + ".o") for f in ("gemm_bf16", "gemm_f32", "nf4", "skinny", "trace")]
+    if not (os.path.exists(hipcc) and os.path.exists(clang) and all(map(os.path.exists, others))):
+        pytest.skip("needs hipcc and the regular build's objects (python -m adapter_mlp_amd.build)")
+    inc = ["-I" + os.path.join(ROOT, "include"), "-I" + os.path.join(ROOT, "adapter_mlp_amd", "csrc")]
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+    abi_o, drv_o, exe = (str(tmp_path / n) for n in ("abi_san.o", "driver.o", "driver"))
+
+    def run(cmd):
+        p = subprocess.run(cmd, capture_output=True, text=True)
+        assert p.returncode == 0, " ".join(cmd) + "\n" + p.stdout[-3000:] + p.stderr[-3000:]
+
+    run([hipcc, "-O1", "-g", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Xclang", "-target-feature",
+         "-Xclang", "-packed-fp32-ops"] + san + inc +
+        ["-c", os.path.join(ROOT, "adapter_mlp_amd", "csrc", "abi.hip"), "-o", abi_o])
+    run([clang, "-O1", "-g", "-std=c++17", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined"] + inc +
+        ["-c", os.path.join(ROOT, "tests", "abi_sanitize_driver.cpp"), "-o", drv_o])
+    run([hipcc, "--offload-arch=gfx950", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+         drv_o, abi_o] + others + ["-o", exe])
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:verify_asan_link_order=0:abort_on_error=1",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    p = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=120)
+    assert p.returncode == 0, p.stdout[-3000:] + p.stderr[-3000:]
+    assert "0 unexpected statuses" in p.stdout
