@@ -361,7 +361,10 @@ def test_validator_under_asan_ubsan(tmp_path):
     run([hipcc, "-O1", "-g", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Xclang", "-target-feature",
          "-Xclang", "-packed-fp32-ops"] + san + inc +
         ["-c", os.path.join(ROOT, "adapter_mlp_amd", "csrc", "abi.hip"), "-o", abi_o])
-    run([clang, "-O1", "-g", "-std=c++17", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined"] + inc +
+    # the driver passes an out-of-range status on purpose (as a C caller may):
+    # only its own enum loads go unchecked; the library's are checked
+    run([clang, "-O1", "-g", "-std=c++17", "-fsanitize=address,undefined", "-fno-sanitize=enum",
+         "-fno-sanitize-recover=undefined"] + inc +
         ["-c", os.path.join(ROOT, "tests", "abi_sanitize_driver.cpp"), "-o", drv_o])
     run([hipcc, "--offload-arch=gfx950", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
          drv_o, abi_o] + others + ["-o", exe])
