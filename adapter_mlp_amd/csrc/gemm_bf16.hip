@@ -53,6 +53,19 @@ constexpr int BM = 256, BK = 64;
 // together land in different banks.
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
+// NN weight tiles (256-byte rows of 16 chunks): chunk c of K row k sits at
+// c ^ nn_swz(k).  A dense tile is written by global -> LDS loads that fill
+// whole rows, so only the transposing fragment reads (4 rows x 4 chunks at a
+// time) need spreading over the banks: 4 (k & 3).  An NF4 tile is written by
+// the unpack, 16 lanes at a time over 8 rows and 2 chunks 8 apart, so its
+// swizzle also spreads 8 consecutive rows: 4 (k & 3) + ((k >> 1) & 3) keeps
+// any 4 aligned rows x 4 aligned chunks and any 8 aligned rows x {c, c + 8}
+// on distinct chunk positions.
+template <bool NF4>
+__device__ __forceinline__ int nn_swz(int k) {
+  return NF4 ? (((k & 3) << 2) | ((k >> 1) & 3)) : ((k & 3) << 2);
+}
+
 // Wavefront-local LDS hand-off between lanes (each wavefront stages into its
 // own LDS region in the epilogue, so no block barrier is needed).
 __device__ __forceinline__ void wave_sync() {
@@ -738,13 +751,23 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
       const uint32_t dst = wslot + wn * 8 * 1024;
 #pragma unroll
       for (int i = 0; i < 8; ++i) dma16(rb, base + (uint32_t)((x ^ i) << 4), dst + i * 1024, (uint32_t)(8 * i) * lld2);
-    } else {
+    } else if constexpr (!NF4) {
       int nr = nn_row, nc = nn_chunk;
       asm volatile("" : "+v"(nr), "+v"(nc));
       const uint32_t base = (uint32_t)nr * lld2 + (uint32_t)(nc << 4);
       const uint32_t dst = wslot + (wn >> 1) * HALF_BYTES + (wn & 1) * 8 * 1024;
 #pragma unroll
       for (int i = 0; i < 8; ++i) dma16(rb, base, dst + i * 1024, (uint32_t)(4 * i) * lld2);
+    } else {
+      // the dense adapter tile of an NF4 GEMM, in the NF4 swizzle: load i
+      // covers rows nn_row + 4 i, whose swizzle alternates with i & 1
+      int nr = nn_row, nc = lane & 15;
+      asm volatile("" : "+v"(nr), "+v"(nc));
+      const uint32_t b0 = (uint32_t)nr * lld2 + (uint32_t)((nc ^ nn_swz<true>(nr)) << 4);
+      const uint32_t b1 = (uint32_t)nr * lld2 + (uint32_t)((nc ^ nn_swz<true>(nr + 4)) << 4);
+      const uint32_t dst = wslot + (wn >> 1) * HALF_BYTES + (wn & 1) * 8 * 1024;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dma16(rb, (i & 1) ? b1 : b0, dst + i * 1024, (uint32_t)(4 * i) * lld2);
     }
     advance();
   };
@@ -794,7 +817,17 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   // unpack) the same work runs on stale codes and its stores go to 2 KB of
   // otherwise unused LDS, so the call has no branch and shares one
   // scheduling region with the MFMA cluster it is interleaved with.
-  auto unpack = [&](int cslot, int wslot, int h, bool live) {
+  // The unpack is split in two.  unpack_fetch (in a read phase, where the
+  // wavefront waits for LDS at the barrier anyway) reads the block's 32 codes
+  // from the code ring and rebuilds its absmax from the scale code, the
+  // second-level scale and the mean; unpack_store (interleaved with an MFMA
+  // cluster) builds the level table, decodes and stores into the weight ring,
+  // with no load, so no wait for LDS or scalar memory stalls the MFMAs.
+  struct UnpackIn {
+    u32x4 w;       // 32 codes
+    float absmax;  // the block's reconstructed absmax
+  };
+  auto unpack_fetch = [&](int cslot, int h, bool live) -> UnpackIn {
     const GemmSeg& S = args.seg[dseg < nseg_nf4 ? dseg : nseg_nf4 - 1];
     const BSrc& B = nf4_src(S);
     // uniform: a scalar load (a vector load would make the compiler wait for
@@ -806,7 +839,8 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
     int lane = lane_id;
     asm volatile("" : "+v"(lane));
     const int b = 64 * wn + lane;
-    const u32x4 w = lds_read16(cs + 32 * b + 16 * h);
+    UnpackIn in;
+    in.w = lds_read16(cs + 32 * b + 16 * h);
     const uint32_t q8w = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(cs + 8192 + 4 * b);
     const float s2 = *reinterpret_cast<const __attribute__((address_space(3))) float*>(cs + 9216 + 4 * b);
     // byte of the scale code inside its aligned dword: block index mod 4
@@ -820,41 +854,53 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
       qb = (uint32_t)((int)tnl * 256 + 64 * wn + lane) * (uint32_t)(B.wcols >> 6) + (uint32_t)(dk0 >> 6);
     }
     const int8_t q8 = (int8_t)(q8w >> (8 * (qb & 3)));
-    const Nf4Planes pl = nf4_planes(nf4_absmax(q8, s2, mu));
+    in.absmax = nf4_absmax(q8, s2, mu);
+    const int nk0 = dk0 + BK;
+    const bool wrap = nk0 >= (int)S.K;
+    dseg = live && wrap ? dseg + 1 : dseg;
+    dk0 = live ? (wrap ? 0 : nk0) : dk0;
+    return in;
+  };
+  // Without `live` (no step left to unpack) the same work runs on stale codes
+  // and its stores go to 2 KB of otherwise unused LDS, so the call has no
+  // branch and shares one scheduling region with the MFMA cluster.
+  auto unpack_store = [&](const UnpackIn& in, int wslot, int h, bool live) {
+    int lane = lane_id;
+    asm volatile("" : "+v"(lane));
+    const int b = 64 * wn + lane;
+    const Nf4Planes pl = nf4_planes(in.absmax);
     lds_char* const wt = lds + (live ? W_RING + wslot * SLOT_BYTES : SPARE);
     const int omask = live ? 0x7fffffff : SPARE_BYTES - 1;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const u32x4 v = nf4_decode8(w[d], pl);
+      const u32x4 v = nf4_decode8(in.w[d], pl);
       int off;
       if constexpr (BKIND == B_NN) {
         const int k = 32 * (wn & 1) + (lane >> 1);
         const int c = 8 * (lane & 1) + 4 * h + d;
-        off = (wn >> 1) * HALF_BYTES + k * 256 + ((c ^ (4 * (k & 3))) << 4);
+        off = (wn >> 1) * HALF_BYTES + k * 256 + ((c ^ nn_swz<true>(k)) << 4);
       } else {
         const int c = 4 * h + d;
         off = b * 128 + ((c ^ swz(b)) << 4);
       }
       *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(wt + (off & omask)) = v;
     }
-    const int nk0 = dk0 + BK;
-    const bool wrap = nk0 >= (int)S.K;
-    dseg = live && wrap ? dseg + 1 : dseg;
-    dk0 = live ? (wrap ? 0 : nk0) : dk0;
   };
 
   // ---- fragment reads ----
   // NN weights: lane s of read h (0, 1) of K slice ks points at K row
   //   16 ks + 8 (g >> 1) + 4 h + (s & 15) / 4 and columns nb + 16 (g & 1) + 4 (s & 3), g = s / 16
-  int fa_nn[2];
+  // (rows 4 h apart; in the NF4 swizzle the two reads' chunk positions differ)
+  int fa_nn[2], fa_nn4[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int half = DUAL ? i : (wn >> 1);
     const int nb = DUAL ? wn * 32 : (wn & 1) * 64 + 32 * i;
     const int g = lane >> 4;
     const int n = nb + 16 * (g & 1) + 4 * (lane & 3);
-    const int kr = (lane & 15) >> 2;  // K row & 3 of every read of this lane
-    fa_nn[i] = half * HALF_BYTES + (8 * (g >> 1) + kr) * 256 + (((n >> 3) ^ (4 * kr)) * 16) + (lane & 1) * 8;
+    const int k0 = 8 * (g >> 1) + ((lane & 15) >> 2);  // K row of read h = 0 in slice 0
+    fa_nn[i] = half * HALF_BYTES + k0 * 256 + (((n >> 3) ^ nn_swz<NF4>(k0)) * 16) + (lane & 1) * 8;
+    fa_nn4[i] = half * HALF_BYTES + (k0 + 4) * 256 + (((n >> 3) ^ nn_swz<NF4>(k0 + 4)) * 16) + (lane & 1) * 8;
   }
   // K-contiguous tiles: row r0 + 32 j (r0 = first row of the sub-tile + lane % 32)
   // has swz = swz(r0) ^ 4 (j & 1), so chunk 2 ks + lane / 32 sits at
@@ -879,7 +925,10 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         if constexpr (BKIND == B_NN) {
-          fa[ks][i] = lds_read_tr8(wt + fa_nn[i] + (16 * ks) * 256, 4 * 256);
+          if constexpr (NF4)
+            fa[ks][i] = lds_read_tr8(wt + fa_nn[i] + (16 * ks) * 256, wt + fa_nn4[i] + (16 * ks) * 256);
+          else
+            fa[ks][i] = lds_read_tr8(wt + fa_nn[i] + (16 * ks) * 256, 4 * 256);
         } else {
           const int y = ((2 * ks) ^ (4 * (i & 1))) >> 1;
           fa[ks][i] = __builtin_bit_cast(bf16x8, lds_read16(wt + bo[y] + i * 32 * 128));
@@ -914,14 +963,12 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
     mma_body();
     __builtin_amdgcn_s_setprio(0);
   };
-  // MFMA cluster with an unpack interleaved: its LDS reads first, then about
-  // five of its vector instructions after each MFMA
-  auto mma_unpack = [&](int cslot, int wslot, int h, bool live) {
+  // MFMA cluster with the store half of an unpack interleaved: about five of
+  // its vector instructions after each MFMA (its inputs are in registers)
+  auto mma_unpack = [&](const UnpackIn& in, int wslot, int h, bool live) {
     __builtin_amdgcn_s_setprio(1);
     mma_body();
-    unpack(cslot, wslot, h, live);
-    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // their addresses
-    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    unpack_store(in, wslot, h, live);
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -997,32 +1044,40 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
     //   P1  g0 loads A 0, 1             g1 loads codes 0, 1, 2, waits for codes 0   | barrier
     //   P2  g0 unpacks W 0 (lower half)  g1 unpacks W 0 (upper), waits for codes 1
     //       g0 waits for A 0                                                         | barrier
-    //   P3  g0 reads step 0              g1 unpacks W 1 (upper) or loads the adapter W 1 | barrier
-    //   X(t)  g0 MFMA t, unpacks W t+1 (lower), waits for A t+1
-    //         g1 reads step t, loads codes t+3, waits for codes t+2 (and adapter W)  | barrier
-    //   Y(t)  g0 reads step t+1, loads A t+2
-    //         g1 MFMA t, unpacks W t+2 (upper) or loads the adapter W t+2           | barrier
-    // Weight slot of step t: t & 1; code slot: t % 3.
+    //   P3  g0 reads step 0, fetches W 1 (lower)
+    //       g1 unpacks W 1 (upper) or loads the adapter W 1                          | barrier
+    //   X(t)  g0 MFMA t, stores W t+1 (lower), waits for A t+1
+    //         g1 reads step t, loads codes t+3, waits for codes t+2 (and adapter W),
+    //         fetches W t+2 (upper)                                                  | barrier
+    //   Y(t)  g0 reads step t+1, loads A t+2, fetches W t+2 (lower)
+    //         g1 MFMA t, stores W t+2 (upper) or loads the adapter W t+2            | barrier
+    // Weight slot of step t: t & 1; code slot: t % 3.  A fetch reads codes that
+    // its own wavefront waited for (g1) or that a barrier has published (g0).
     const bool lora_step = KT > KN;  // the last step is the dense adapter tile
     if (wm == 0) {
       issue_a(0);
       if (KT > 1) issue_a(1);
       phase_end();
-      unpack(0, 0, 0, true);
+      {
+        const UnpackIn u = unpack_fetch(0, 0, true);
+        unpack_store(u, 0, 0, true);
+      }
       if (KT > 1) wait_vmcnt<8>();
       else wait_vmcnt<0>();
       phase_end();
       read(0, 0);
+      UnpackIn nx = unpack_fetch(1, 0, 1 < KN);  // W 1 (lower): code slot 1
       phase_end();
-      int cs1 = 1;  // code slot of step t + 1
+      int cs2 = 2;  // code slot of step t + 2
       for (int t = 0; t < KT; ++t) {
-        mma_unpack(cs1, (t + 1) & 1, 0, t + 1 < KN);
+        mma_unpack(nx, (t + 1) & 1, 0, t + 1 < KN);
         wait_vmcnt<0>();  // A t+1 is in
         phase_end();
         if (t + 1 < KT) read((t + 1) & 1, (t + 1) & 1);
         if (t + 2 < KT) issue_a(t & 1);
+        nx = unpack_fetch(cs2, 0, t + 2 < KN);
         phase_end();
-        cs1 = cs1 == 2 ? 0 : cs1 + 1;
+        cs2 = cs2 == 2 ? 0 : cs2 + 1;
       }
     } else {
       issue_codes(0);
@@ -1036,12 +1091,19 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
         wait_vmcnt<0>();
       }
       phase_end();
-      unpack(0, 0, 1, true);
+      {
+        const UnpackIn u = unpack_fetch(0, 1, true);
+        unpack_store(u, 0, 1, true);
+      }
       if (KN > 2) wait_vmcnt<4>();
       else wait_vmcnt<0>();
       phase_end();
-      if (KN > 1) unpack(1, 1, 1, true);
-      else if (lora_step) issue_w(1);
+      if (KN > 1) {
+        const UnpackIn u = unpack_fetch(1, 1, true);
+        unpack_store(u, 1, 1, true);
+      } else if (lora_step) {
+        issue_w(1);
+      }
       phase_end();
       int cs0 = 0;  // code slot of step t (= that of step t + 3)
       for (int t = 0; t < KT; ++t) {
@@ -1054,8 +1116,9 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
           read(t & 1, t & 1);
           wait_vmcnt<0>();
         }
+        const UnpackIn nx = unpack_fetch(cs2, 1, t + 2 < KN);
         phase_end();
-        mma_unpack(cs2, t & 1, 1, t + 2 < KN);
+        mma_unpack(nx, t & 1, 1, t + 2 < KN);
         if (lora_step && t + 2 == KN) issue_w(t & 1);
         phase_end();
         cs0 = cs0 == 2 ? 0 : cs0 + 1;

@@ -112,5 +112,16 @@ __device__ __forceinline__ bf16x8 lds_read_tr8(const lds_char* p, int second_off
   v[3] = (uint32_t)(hi >> 32);
   return __builtin_bit_cast(bf16x8, v);
 }
+// The same with the two reads at addresses of their own.
+__device__ __forceinline__ bf16x8 lds_read_tr8(const lds_char* p, const lds_char* q) {
+  const uint64_t lo = lds_read_tr(p);
+  const uint64_t hi = lds_read_tr(q);
+  u32x4 v;
+  v[0] = (uint32_t)lo;
+  v[1] = (uint32_t)(lo >> 32);
+  v[2] = (uint32_t)hi;
+  v[3] = (uint32_t)(hi >> 32);
+  return __builtin_bit_cast(bf16x8, v);
+}
 
 }  // namespace lora
