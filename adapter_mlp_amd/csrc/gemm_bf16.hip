@@ -399,8 +399,24 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
     const brsrc deo = make_rsrc(args.de_out, M * ld * 2);
     const brsrc ho = make_rsrc(args.h_out, M * ld * 2);
     const brsrc pdr = make_rsrc(args.pd, M * args.ldpd * 2);
+    // e, g of 32-row pass j (rows past M read zero, so h is zero there); the
+    // loads of pass j + 1 are issued before pass j is computed, so each pass
+    // waits for memory only as long as the previous pass's work does not cover
+    u32x4 evn[PASSES], gvn[PASSES];
+    auto load_eg = [&](int j) {
+#pragma unroll
+      for (int it = 0; it < PASSES; ++it) {
+        const int row = it * RPP + lane / CPR, c8 = lane % CPR;
+        const int64_t m = mw + j * 32 + row;
+        const int64_t n = nbase + c8 * 8;
+        const uint32_t off = row_off(m, M, ld, n, 2);
+        evn[it] = buf_load16(ei, off);
+        if constexpr (GATED) gvn[it] = buf_load16(gi, off);
+      }
+    };
     // a wavefront past NR leaves dacc zero (those dA rows are not written)
     if (cols_ok) {
+      load_eg(0);
       for4([&](auto jc) {
         constexpr int j = decltype(jc)::value;
 #pragma unroll
@@ -417,17 +433,13 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
           const int64_t m = mw + j * 32 + (lane >> 1);
           pv = buf_load16(pdr, row_off(m, M, args.ldpd, 8 * (lane & 1), 2));
         }
-        // e, g of the pass (rows past M read zero, so h is zero there)
         u32x4 ev[PASSES], gv[PASSES];
 #pragma unroll
         for (int it = 0; it < PASSES; ++it) {
-          const int row = it * RPP + lane / CPR, c8 = lane % CPR;
-          const int64_t m = mw + j * 32 + row;
-          const int64_t n = nbase + c8 * 8;
-          const uint32_t off = row_off(m, M, ld, n, 2);
-          ev[it] = buf_load16(ei, off);
-          if constexpr (GATED) gv[it] = buf_load16(gi, off);
+          ev[it] = evn[it];
+          if constexpr (GATED) gv[it] = gvn[it];
         }
+        if constexpr (j < 3) load_eg(j + 1);
         wave_sync();
         f32x4 d0[PASSES], d1[PASSES];
 #pragma unroll
