@@ -976,9 +976,12 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
     __builtin_amdgcn_s_setprio(0);
   };
   // MFMA cluster with the store half of an unpack interleaved: about five of
-  // its vector instructions after each MFMA (its inputs are in registers)
+  // its vector instructions after each MFMA (its inputs are in registers).
+  // Unlike the dense clusters it runs at normal priority and the NF4 read
+  // phases run raised: the unpack's vector instructions would otherwise hold
+  // back the address arithmetic and loads of the SIMD's other wavefront,
+  // whose read phase then ends later (measured: config-4 step -3%).
   auto mma_unpack = [&](const UnpackIn& in, int wslot, int h, bool live) {
-    __builtin_amdgcn_s_setprio(1);
     mma_body();
     unpack_store(in, wslot, h, live);
 #pragma unroll
@@ -986,7 +989,6 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
     }
-    __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- phases.  Every wavefront passes 2 + 2 KT barriers. ----
@@ -1085,9 +1087,11 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
         mma_unpack(nx, (t + 1) & 1, 0, t + 1 < KN);
         wait_vmcnt<0>();  // A t+1 is in
         phase_end();
+        __builtin_amdgcn_s_setprio(1);
         if (t + 1 < KT) read((t + 1) & 1, (t + 1) & 1);
         if (t + 2 < KT) issue_a(t & 1);
         nx = unpack_fetch(cs2, 0, t + 2 < KN);
+        __builtin_amdgcn_s_setprio(0);
         phase_end();
         cs2 = cs2 == 2 ? 0 : cs2 + 1;
       }
@@ -1120,6 +1124,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
       int cs0 = 0;  // code slot of step t (= that of step t + 3)
       for (int t = 0; t < KT; ++t) {
         const int cs2 = cs0 == 0 ? 2 : cs0 - 1;  // (t + 2) % 3
+        __builtin_amdgcn_s_setprio(1);
         if (t + 3 < KN) {
           read(t & 1, t & 1);
           issue_codes(cs0);
@@ -1129,6 +1134,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
           wait_vmcnt<0>();
         }
         const UnpackIn nx = unpack_fetch(cs2, 1, t + 2 < KN);
+        __builtin_amdgcn_s_setprio(0);
         phase_end();
         mma_unpack(nx, t & 1, 1, t + 2 < KN);
         if (lora_step && t + 2 == KN) issue_w(t & 1);
