@@ -160,6 +160,8 @@ PMC_PASSES = {
              "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"],
     "lds": ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "SQ_LDS_ADDR_CONFLICT",
             "SQ_ACTIVE_INST_LDS", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE"],
+    "cx": ["SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_VALU2",
+           "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "GRBM_GUI_ACTIVE"],
 }
 N_SIMD, N_CU, N_XCD = 1024, 256, 8  # MI355X: 256 CUs x 4 SIMDs in 8 XCDs
 
@@ -211,6 +213,10 @@ def counter_summary(csvs, config_id):
                 m["executed_over_algorithmic"] = ex / fl
         if "SQ_INSTS_MFMA" in avg and "SQ_INSTS_VALU" in avg and avg["SQ_INSTS_MFMA"]:
             m["valu_non_mfma_per_mfma"] = (avg["SQ_INSTS_VALU"] - avg["SQ_INSTS_MFMA"]) / avg["SQ_INSTS_MFMA"]
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in avg and avg.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+            m["coexec_over_mfma_busy"] = avg["SQ_VALU_MFMA_COEXEC_CYCLES"] / avg["SQ_VALU_MFMA_BUSY_CYCLES"]
+        if "SQ_ACTIVE_INST_VALU" in avg and gui:  # quad-cycles summed over the SIMDs
+            m["valu_active_frac"] = 4 * avg["SQ_ACTIVE_INST_VALU"] / (gui * N_SIMD)
         if "SQ_LDS_IDX_ACTIVE" in avg and gui:
             m["lds_active_frac"] = avg["SQ_LDS_IDX_ACTIVE"] / (gui * N_CU)
         if "SQ_LDS_BANK_CONFLICT" in avg and avg.get("SQ_LDS_IDX_ACTIVE"):
@@ -229,7 +235,9 @@ def counter_summary(csvs, config_id):
                 fh.write(f"#   rocprofv3 --pmc {' '.join(cs)} --output-format csv -d <dir> -o {name} -- python3 "
                          f"<repo>/bench.py --config {config_id} --steps 2 --warmup 1 --no-cpu-baseline\n")
             fh.write(f"#   python3 bench.py --config {config_id} --counter-summary "
-                     f"{' '.join(n + '_counter_collection.csv' for n in PMC_PASSES)}\n")
+                     f"{' '.join(n + '_counter_collection.csv' for n in PMC_PASSES)}   (the sets that were run)\n")
+            fh.write("# coexec_over_mfma_busy = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES (a VALU issued while\n")
+            fh.write("# the matrix core works); valu_active_frac = 4 SQ_ACTIVE_INST_VALU (quad-cycles) / (GRBM_GUI_ACTIVE x 1024)\n")
             fh.write("# GRBM_GUI_ACTIVE below is per XCD (the counter's sum over the 8 XCDs / 8);\n")
             fh.write("# mfma_busy_frac = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs);\n")
             fh.write("# mfma_flops_executed = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; clock = GRBM_GUI_ACTIVE / dispatch time;\n")
@@ -243,7 +251,8 @@ def counter_summary(csvs, config_id):
     for fam, m in lines:
         print(f"{fam:24s} " + "  ".join(f"{k}={v:.4g}" for k, v in m.items() if k in (
             "clock_GHz", "mfma_busy_frac", "executed_over_algorithmic", "valu_non_mfma_per_mfma",
-            "lds_active_frac", "lds_bank_conflict_over_active", "frac_of_nominal_peak")))
+            "lds_active_frac", "lds_bank_conflict_over_active", "coexec_over_mfma_busy", "valu_active_frac",
+            "frac_of_nominal_peak")))
 
 
 def trace_summary(stats_csv, bench_log, config_id):
