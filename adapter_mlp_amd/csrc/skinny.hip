@@ -219,7 +219,8 @@ template <int NJ, bool ROW>
 __device__ __forceinline__ void colproj_body(const ColProjArgs& a, int64_t rows_per_chunk, int64_t kb) {
   using C = ColProjCfg<NJ>;
   constexpr int BTB = ROW ? 8192 : 0;  // Bt slice after the ring
-  __shared__ __attribute__((aligned(1024))) char ring[C::NST * C::SB + BTB];
+  constexpr int RSB = ROW ? 2048 : 0;  // then the rowproj output staging, 1 KB per wavefront of a step
+  __shared__ __attribute__((aligned(1024))) char ring[C::NST * C::SB + BTB + RSB];
   lds_char* const lds = (lds_char*)ring;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -300,12 +301,20 @@ __device__ __forceinline__ void colproj_body(const ColProjArgs& a, int64_t rows_
         const bf16x8 za = __builtin_bit_cast(bf16x8, lds_read16(zs + r * 512 + ((cz ^ zswz(r)) * 16)));
         acc_r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(za, btf[ks], acc_r, 0, 0, 0);
       }
-      // acc_r[v] = Out[row rb * 16 + 4 (lane >> 4) + v of the step, j = lane % 16]
+      // acc_r[v] = Out[row rb * 16 + 4 (lane >> 4) + v of the step, j = lane % 16].  The 16 x 16
+      // block is staged row-major in LDS and stored as 16-byte pieces: rows t .. t + 15 of the
+      // partial are 1 KB of consecutive floats, written by one store per lane.  (Four 4-byte
+      // stores per lane, each scattering 64-byte pieces over four rows, cost the pass about a
+      // fifth of its time.)  The other pair of wavefronts reuses this staging in the next step,
+      // after that step's barrier.
+      float* const stg = reinterpret_cast<float*>(ring + C::NST * C::SB + BTB) + rb * 256;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t t = tbeg + 32 * (int64_t)s + rb * 16 + 4 * (lane >> 4) + v;
-        if (t < tend) a.rpartial[(kb * a.T + t) * 16 + (lane & 15)] = acc_r[v];
-      }
+      for (int v = 0; v < 4; ++v) stg[(4 * (lane >> 4) + v) * 16 + (lane & 15)] = acc_r[v];
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wavefront's LDS writes are done
+      __builtin_amdgcn_wave_barrier();
+      const f32x4 o = *reinterpret_cast<const f32x4*>(stg + 4 * lane);  // row lane / 4, j = 4 (lane % 4) ..
+      const int64_t t = tbeg + 32 * (int64_t)s + rb * 16 + (lane >> 2);
+      if (t < tend) *reinterpret_cast<f32x4*>(a.rpartial + (kb * a.T + t) * 16 + 4 * (lane & 3)) = o;
     }
   };
 
