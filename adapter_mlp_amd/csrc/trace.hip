@@ -1,4 +1,5 @@
 // Kernel timing: HIP event pairs around each launch, on the launch stream.
+#include <atomic>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -14,8 +15,10 @@ struct Rec {
   hipEvent_t start, stop;
 };
 
+// g_on is read without the lock on every launch, so a launch with tracing off
+// touches no lock; the records and the event pool are guarded by g_mu.
 std::mutex g_mu;
-bool g_on = false;
+std::atomic<bool> g_on{false};
 std::string g_prefix;
 std::vector<Rec> g_recs;
 std::vector<hipEvent_t> g_pool;
@@ -33,14 +36,12 @@ hipEvent_t get_event() {
 
 }  // namespace
 
-bool trace_on() {
-  std::lock_guard<std::mutex> lk(g_mu);
-  return g_on;
-}
+bool trace_on() { return g_on.load(std::memory_order_acquire); }
 
 void* trace_start(const char* name, hipStream_t st) {
+  if (!g_on.load(std::memory_order_acquire)) return nullptr;
   std::lock_guard<std::mutex> lk(g_mu);
-  if (!g_on) return nullptr;
+  if (!g_on.load(std::memory_order_relaxed)) return nullptr;
   if (!g_prefix.empty() && std::strncmp(name, g_prefix.c_str(), g_prefix.size()) != 0) return nullptr;
   Rec r{name, get_event(), get_event()};
   if (!r.start || !r.stop) return nullptr;
@@ -70,13 +71,13 @@ lora_status lora_trace_begin(const char* prefix) {
     g_pool.push_back(r.stop);
   }
   g_recs.clear();
-  g_on = true;
+  g_on.store(true, std::memory_order_release);
   return LORA_OK;
 }
 
 lora_status lora_trace_end(lora_trace_entry* out, int32_t max, int32_t* count) {
   std::lock_guard<std::mutex> lk(g_mu);
-  g_on = false;
+  g_on.store(false, std::memory_order_release);
   std::vector<lora_trace_entry> agg;
   lora_status st = LORA_OK;
   for (auto& r : g_recs) {

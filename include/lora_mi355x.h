@@ -26,7 +26,11 @@
  *       U = X A          Z = X W + s (U B)                          ([UD] LoRA_W)
  *   Gradients dA, dB have the layout of A, B.
  * Memory.  All tensor pointers are device memory owned by the caller; the
- *   library never allocates or frees and keeps no state between calls.
+ *   library never allocates or frees device memory, and no call's result
+ *   depends on an earlier call.  The only state it holds: the calling
+ *   thread's last error text (lora_last_error), the tracing records (off by
+ *   default; see lora_trace_begin) and, for lora_o_fwd_noalloc only, the
+ *   address of each GPU's static scratch array.
  *   Scratch memory comes from the caller's workspace (ws, ws_bytes), whose
  *   minimum size the matching *_workspace_size query returns.  Descriptor
  *   structs (lora_*_desc, lora_proj, lora_nf4, lora_*_grads) live in host
@@ -415,9 +419,10 @@ lora_status lora_nf4_gemm(int64_t T, int32_t trans, const void* X, const lora_nf
 /* Per-kernel totals of the launches recorded between lora_trace_begin and
  * lora_trace_end.  While tracing is on, every kernel the library enqueues is
  * bracketed by two HIP events recorded on its launch stream; the pair's
- * elapsed time is that launch's duration.  Tracing is process-wide state (the
- * only state the library keeps) and is off by default; it adds two event
- * records per launch. */
+ * elapsed time is that launch's duration.  Tracing is process-wide state and
+ * is off by default.  While it is off a launch only reads one atomic flag;
+ * while it is on each launch adds two event records and takes one
+ * process-wide lock (a debugging and measurement aid, not for production). */
 typedef struct lora_trace_entry {
   char name[48];     /* kernel family, e.g. "gemm_nn_act_fwd" */
   int64_t launches;
