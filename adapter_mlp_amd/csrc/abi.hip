@@ -214,6 +214,19 @@ int gemm_ksplit(const Ctx& c, int64_t M, int64_t N, int64_t K) {
   }
   return bs;
 }
+// First split tile of a GEMM of `tiles` tiles split into s K parts.  With
+// R = tiles / 256 full rounds of the grid and rem tiles left, splitting only
+// the rem tiles (R whole rounds, then ceil(rem s / 256) rounds of 1/s tile)
+// takes no longer than splitting every tile whenever it fills its rounds as
+// well, and writes and reduces fp32 partials for the rem tiles only.
+int64_t ksplit_t0(int64_t tiles, int s) {
+  const int64_t R = tiles / 256, rem = tiles % 256;
+  if (s <= 1 || R == 0 || rem == 0) return 0;
+  const int64_t all = cdiv(tiles * s, 256);            // rounds of 1/s tile, every tile split
+  const int64_t tail = R * s + cdiv(rem * s, 256);     // the same, only the rem tiles split
+  return tail <= all ? R * 256 : 0;
+}
+
 // fp32 partial floats a split store GEMM needs (0 without a split); `forced`
 // is the plan's ksplit (0: the model above).
 int64_t kpart_floats(const Ctx& c, int64_t M, int64_t N, int64_t K, int forced = 0) {
@@ -302,6 +315,7 @@ hipError_t gemm_on(const Ctx& c, GemmArgs& g, hipStream_t st, int64_t lora_vcols
     const int ks = gp.ksplit > 0 ? gp.ksplit : gemm_ksplit(c, g.M, g.reg[0].N, K);
     if (ks > 1) {
       g.ksplit = ks;
+      g.ksplit_t0 = (int32_t)ksplit_t0(g.ntile_m * g.ntile_n, ks);
       g.kpart = kpart;
     }
   }
@@ -317,7 +331,7 @@ hipError_t gemm_on(const Ctx& c, GemmArgs& g, hipStream_t st, int64_t lora_vcols
   if (!c.bf16) return launch_gemm_f32(g, st);
   const hipError_t e = launch_gemm_bf16(g, st);
   if (e != hipSuccess || g.ksplit <= 1) return e;
-  return launch_ksplit_reduce(g.kpart, g.ksplit, g.M, g.reg[0].N, g.reg[0].out, g.reg[0].ldo, st);
+  return launch_ksplit_reduce(g, st);
 }
 
 RowProjArgs rowproj_args(const void* Z, int64_t ldz, int64_t T, int64_t K, const void* Bt, int64_t ldb,

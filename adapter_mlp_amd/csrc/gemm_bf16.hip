@@ -197,10 +197,11 @@ template <int WN, bool DUAL, int EPI, int ACT>
 __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* wstage, const GemmArgs& args,
                                                int reg, int64_t mw, int64_t nbase, int64_t NR, int64_t M,
                                                int lane, int wm, int wn, int kp) {
+  // kp >= 0: this block computes K part kp of a split tile (fp32 partial sums)
   constexpr int NI = WN / 32;
   const bool cols_ok = nbase < NR;  // uniform
   if constexpr (EPI == EPI_STORE) {
-    if (args.ksplit > 1) {
+    if (kp >= 0) {
       // split-K part: fp32 sums through a [32][WN] fp32 staging, 16-byte stores
       constexpr int LD = WN + 4;
       constexpr int CPR = WN / 4;          // 4-float chunks per row
@@ -627,10 +628,17 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   const int wm = wave >> 2, wn = wave & 3;                    // wm: the group
 
   int tm, tn;
-  // split-K: block u works on K part u / ntiles of tile u % ntiles
+  // split-K: blocks below ksplit_t0 compute tiles 0 .. t0-1 whole; block
+  // t0 + u computes K part u / ns of tile t0 + u % ns (ns = ntiles - t0), so
+  // only the tiles past the last full round of the grid are split
   const int ntiles = (int)(args.ntile_m * args.ntile_n);
-  const int kp = args.ksplit > 1 ? (int)blockIdx.x / ntiles : 0;
-  tile_coords((int)blockIdx.x - kp * ntiles, ntiles, (int)args.ntile_m, (int)args.ntile_n, args.group, tm, tn);
+  int tile = (int)blockIdx.x, kp = -1;
+  if (!NF4 && args.ksplit > 1 && tile >= args.ksplit_t0) {
+    const int u = tile - args.ksplit_t0, ns = ntiles - args.ksplit_t0;
+    kp = u / ns;
+    tile = args.ksplit_t0 + (u - kp * ns);
+  }
+  tile_coords(tile, ntiles, (int)args.ntile_m, (int)args.ntile_n, args.group, tm, tn);
   tm = __builtin_amdgcn_readfirstlane(tm);
   tn = __builtin_amdgcn_readfirstlane(tn);
   int reg = 0;
@@ -655,7 +663,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   }
   // this block's K steps [k_begin, k_begin + KT) (dense split-K only)
   int k_begin = 0;
-  if (!NF4 && args.ksplit > 1) {
+  if (!NF4 && kp >= 0) {
     const int kall = KT;
     k_begin = (int)((int64_t)kp * kall / args.ksplit);
     KT = (int)((int64_t)(kp + 1) * kall / args.ksplit) - k_begin;
@@ -1153,10 +1161,17 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   run_epilogue_w<64, DUAL, EPI, ACT>(acc, wstage, args, reg, mw, nbase, NR, M, lane, wm, wn, kp);
 }
 
-__global__ void ksplit_reduce_kernel(const float* part, int ks, int64_t M, int64_t N, uint16_t* out, int64_t ldo) {
-  const int64_t e = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
-  if (e >= M * N) return;
-  const int64_t m = e / N, n = e % N;
+// Sum of the K parts of the split tiles t0 .. ntiles-1 (tile order as in the
+// GEMM): 32 blocks per tile, each 8 rows of 256 columns, 8 columns per thread.
+__global__ void ksplit_reduce_kernel(const float* part, int ks, int64_t M, int64_t N, uint16_t* out, int64_t ldo,
+                                     int t0, int ntm, int ntn, int G) {
+  const int tile = t0 + (int)(blockIdx.x >> 5);
+  int tm, tn;
+  tile_coords(tile, ntm * ntn, ntm, ntn, G, tm, tn);
+  const int64_t m = (int64_t)tm * 256 + (blockIdx.x & 31) * 8 + (threadIdx.x >> 5);
+  const int64_t n = (int64_t)tn * 256 + (threadIdx.x & 31) * 8;
+  if (m >= M || n >= N) return;  // N is a multiple of 8
+  const int64_t e = m * N + n;
   f32x4 a = *reinterpret_cast<const f32x4*>(part + e), b = *reinterpret_cast<const f32x4*>(part + e + 4);
   for (int k = 1; k < ks; ++k) {
     a += *reinterpret_cast<const f32x4*>(part + (int64_t)k * M * N + e);
@@ -1168,7 +1183,8 @@ __global__ void ksplit_reduce_kernel(const float* part, int ks, int64_t M, int64
 
 template <int BKIND, bool DUAL, int EPI, bool NF4, int ACT = 0>
 hipError_t launch(const GemmArgs& a, hipStream_t st) {
-  const int64_t nb = a.ntile_m * a.ntile_n * (a.ksplit > 1 && !NF4 ? a.ksplit : 1);
+  const int64_t nt = a.ntile_m * a.ntile_n;
+  const int64_t nb = a.ksplit > 1 && !NF4 ? a.ksplit_t0 + (nt - a.ksplit_t0) * a.ksplit : nt;
   if (nb == 0) return hipSuccess;
   hipLaunchKernelGGL((gemm_kernel<BKIND, DUAL, EPI, NF4, ACT>), dim3((unsigned)nb), dim3(NTH8), 0, st, a);
   return hipGetLastError();
@@ -1198,12 +1214,12 @@ int64_t gemm_tile_cols(bool bf16, bool dual) {
 }
 int64_t gemm_tile_rows(bool bf16) { return bf16 ? 256 : 64; }
 
-hipError_t launch_ksplit_reduce(const float* part, int ks, int64_t M, int64_t N, void* out, int64_t ldo,
-                                hipStream_t st) {
-  const int64_t n8 = M * N / 8;
-  if (n8 == 0) return hipSuccess;
-  hipLaunchKernelGGL(ksplit_reduce_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, part, ks, M, N,
-                     static_cast<uint16_t*>(out), ldo);
+hipError_t launch_ksplit_reduce(const GemmArgs& a, hipStream_t st) {
+  const int64_t nsplit = a.ntile_m * a.ntile_n - a.ksplit_t0;
+  if (a.ksplit <= 1 || nsplit <= 0) return hipSuccess;
+  hipLaunchKernelGGL(ksplit_reduce_kernel, dim3((unsigned)(nsplit * 32)), dim3(256), 0, st, a.kpart, a.ksplit, a.M,
+                     a.reg[0].N, static_cast<uint16_t*>(a.reg[0].out), a.reg[0].ldo, a.ksplit_t0, (int)a.ntile_m,
+                     (int)a.ntile_n, a.group);
   return hipGetLastError();
 }
 

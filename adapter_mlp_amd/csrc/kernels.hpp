@@ -84,11 +84,14 @@ struct GemmArgs {
   float* dA_part;
   const void* pd;
   int64_t ldpd;
-  // EPI_STORE, bf16, dense, one region: split-K.  Block u works on K part
-  // u / (ntile_m * ntile_n) (parts split the K steps evenly, in order) and
-  // writes its fp32 sums to kpart [ksplit, M, N]; launch_ksplit_reduce adds
-  // the parts in ascending order and stores bf16.  ksplit <= 1: no split.
-  int32_t ksplit, pad3_;
+  // EPI_STORE, bf16, dense, one region: split-K.  Tiles 0 .. ksplit_t0-1 (in
+  // the tile order) are computed whole and stored as bf16; each later tile is
+  // split into ksplit K parts (the K steps split evenly, in order), block
+  // ksplit_t0 + u working on part u / ns of tile ksplit_t0 + u % ns (ns = the
+  // split tiles) and writing its fp32 sums to kpart [ksplit, M, N];
+  // launch_ksplit_reduce adds the parts of the split tiles in ascending order
+  // and stores bf16.  ksplit <= 1: no split.
+  int32_t ksplit, ksplit_t0;
   float* kpart;
   // EPI_ACT_FWD (bf16) with u_part set: each block also forms h Ad over its
   // h columns (ad_t = Ad^T [u_R, N], row pitch ld_adt, u_R <= 16) and writes
@@ -104,9 +107,9 @@ struct GemmArgs {
 int64_t gemm_tile_cols(bool bf16, bool dual);
 int64_t gemm_tile_rows(bool bf16);
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st);
-// out[m, n] (bf16, row pitch ldo) = sum over k < ks, ascending, of part[k][m][n] ([ks, M, N] fp32)
-hipError_t launch_ksplit_reduce(const float* part, int ks, int64_t M, int64_t N, void* out, int64_t ldo,
-                                hipStream_t st);
+// For the split tiles of a (tiles ksplit_t0 ..): out[m, n] (bf16) = sum over
+// k < ksplit, ascending, of kpart[k][m][n]
+hipError_t launch_ksplit_reduce(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t st);
 
 // ---------------------------------------------------------------------------

@@ -115,3 +115,36 @@ def test_tune_mlp_new_shape_and_cache(lm, tmp_path):
         assert_close(k_dev, host(grads[k_dev]), gr[k_ref], tol)
     assert entry["ms"]["fwd"]["tuned"] <= entry["ms"]["fwd"]["default"]
     assert entry["ms"]["bwd"]["tuned"] <= entry["ms"]["bwd"]["default"]
+
+
+def test_tail_split_o_fwd_and_qkv_dx(lm):
+    """Split-K of only the tiles past the grid's last full round: H = 7168
+    gives the O forward and the Q/K/V input-gradient GEMM 10 x 28 = 280
+    tiles, so a split of 2 runs 256 tiles whole and splits the other 24.
+    Both results (and those of every GEMM of the calls) against the oracle,
+    and against the same calls without a split."""
+    import torch
+
+    cfg = WorkloadConfig(113, "attn", T=2560, H=7168, r=16, alpha=32, dtype="bf16", Nq=512, Nk=128, Nv=128)
+    inp = make_attn_inputs(cfg)
+    X, Xo = dev(inp["X"]), dev(inp["Xo"])
+    q, k, v, o = (proj_dev(inp[n]) for n in ("q", "k", "v", "o"))
+    Yo, Uo = lm.o_fwd(Xo, o, plan=[(8, 2)])
+    Yo1, _ = lm.o_fwd(Xo, o, plan=[(8, 1)])
+    Q, K, V, U = lm.qkv_fwd(X, q, k, v)
+    dQ, dK, dV = (dev(inp[n]) for n in ("dQ", "dK", "dV"))
+    dX, grads = lm.qkv_bwd(dQ, dK, dV, X, U, q, k, v, plan=[(8, 2)])
+    dX1, _ = lm.qkv_bwd(dQ, dK, dV, X, U, q, k, v, plan=[(8, 1)])
+    torch.cuda.synchronize()
+    Yr, so = OL.o_fwd(inp["Xo"], inp["o"])
+    (Qr, Kr, Vr), sr = OL.qkv_fwd(inp["X"], inp["q"], inp["k"], inp["v"])
+    gr = OL.qkv_bwd(inp["dQ"], inp["dK"], inp["dV"], inp["X"], sr, inp["q"], inp["k"], inp["v"])
+    tol = TOL["bf16"]
+    assert_close("O", host(Yo), Yr, tol)
+    assert_close("U_o", host(Uo), so["U"], tol)
+    assert_close("dX", host(dX), gr["dX"], tol)
+    for n in ("dA_q", "dB_q", "dA_k", "dB_k", "dA_v", "dB_v"):
+        assert_close(n, host(grads[n]), gr[n], tol)
+    # the split changes only the fp32 summation order of the split tiles' K parts
+    assert_close("O split vs whole", host(Yo), host(Yo1), tol)
+    assert_close("dX split vs whole", host(dX), host(dX1), tol)
