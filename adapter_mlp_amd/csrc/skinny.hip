@@ -648,16 +648,11 @@ hipError_t launch_rowcol(bool bf16, const ColProjArgs& c0, const RowProjArgs& r,
     c.rpartial = nullptr;
     return launch_colproj(bf16, c, st);
   }
+  // a batch of one: the pass, then both reduces in one launch (the chunking
+  // is that of launch_colproj, so the sums are the same)
   ColProjArgs c = c0;
-  c.Bt = r.Bt;
-  c.ldb = r.ldb;
-  c.R1 = r.R;
   c.rpartial = rpartial;
-  hipError_t e = launch_colproj(true, c, st);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(rowproj_reduce_kernel, dim3(nblk(r.T * 4, 64)), dim3(256), 0, st, r, rpartial,
-                     (int)((r.K + 255) / 256));
-  return hipGetLastError();
+  return launch_rowcol_batch(true, &c, &r, 1, st);
 }
 
 hipError_t launch_rowcol_batch(bool bf16, const ColProjArgs* c, const RowProjArgs* r, int n, hipStream_t st) {
