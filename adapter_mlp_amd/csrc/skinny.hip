@@ -458,17 +458,19 @@ __global__ void colproj_f32_kernel(const ColProjArgs a) {
 template <typename E>
 __global__ void pack_batch_kernel(const PackBatchArgs b) {
   const PackLoraArgs& a = b.job[blockIdx.y];
-  const int64_t n = a.vcols * a.RL;
-  for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < n; o += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t v = a.kmajor ? o % a.vcols : o / a.RL;
-    const int kk = (int)(a.kmajor ? o / a.vcols : o % a.RL);
+  // 32-bit index arithmetic (a 64-bit division per element dominated the
+  // kernel); launch_pack_batch checks that every job has fewer than 2^31 elements
+  const uint32_t vc = (uint32_t)a.vcols, rl = (uint32_t)a.RL, n = vc * rl;
+  for (uint32_t o = blockIdx.x * blockDim.x + threadIdx.x; o < n; o += gridDim.x * blockDim.x) {
+    const uint32_t v = a.kmajor ? o % vc : o / rl;
+    const uint32_t kk = a.kmajor ? o / vc : o % rl;
     E val = E(0);
     for (int p = 0; p < a.nparts; ++p) {
       const PackPart& q = a.part[p];
-      if (v >= q.v0 && v < q.v0 + q.nv && kk >= q.k0 && kk < q.k0 + q.w) {
-        const int64_t nn = v - q.v0, i = kk - q.k0;
+      const uint32_t nn = v - (uint32_t)q.v0, i = kk - (uint32_t)q.k0;  // wrap past the part's range
+      if (nn < (uint32_t)q.nv && i < (uint32_t)q.w) {
         const E* src = static_cast<const E*>(q.src);
-        val = q.nn ? src[i * q.ld + nn] : src[nn * q.ld + i];
+        val = q.nn ? src[(size_t)i * q.ld + nn] : src[(size_t)nn * q.ld + i];
       }
     }
     static_cast<E*>(a.out)[o] = val;
@@ -706,6 +708,7 @@ hipError_t launch_pack_batch(bool bf16, const PackBatchArgs& b, hipStream_t st) 
   int64_t nmax = 0;
   for (int i = 0; i < b.njobs; ++i) nmax = b.job[i].vcols * b.job[i].RL > nmax ? b.job[i].vcols * b.job[i].RL : nmax;
   if (b.njobs <= 0 || nmax == 0) return hipSuccess;
+  if (nmax >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const unsigned bx = nblk(nmax, 256) < 2048 ? nblk(nmax, 256) : 2048u;
   if (bf16) hipLaunchKernelGGL(pack_batch_kernel<uint16_t>, dim3(bx, (unsigned)b.njobs), dim3(256), 0, st, b);
   else hipLaunchKernelGGL(pack_batch_kernel<float>, dim3(bx, (unsigned)b.njobs), dim3(256), 0, st, b);
