@@ -215,16 +215,13 @@ int gemm_ksplit(const Ctx& c, int64_t M, int64_t N, int64_t K) {
   return bs;
 }
 // First split tile of a GEMM of `tiles` tiles split into s K parts.  With
-// R = tiles / 256 full rounds of the grid and rem tiles left, splitting only
-// the rem tiles (R whole rounds, then ceil(rem s / 256) rounds of 1/s tile)
-// takes no longer than splitting every tile whenever it fills its rounds as
-// well, and writes and reduces fp32 partials for the rem tiles only.
+// R = tiles / 256 full rounds of the grid and rem tiles left over, splitting
+// only the rem tiles takes R s + ceil(rem s / 256) rounds of 1/s tile, exactly
+// the ceil(tiles s / 256) rounds of splitting every tile, and writes and
+// reduces fp32 partials for the rem tiles only.
 int64_t ksplit_t0(int64_t tiles, int s) {
   const int64_t R = tiles / 256, rem = tiles % 256;
-  if (s <= 1 || R == 0 || rem == 0) return 0;
-  const int64_t all = cdiv(tiles * s, 256);            // rounds of 1/s tile, every tile split
-  const int64_t tail = R * s + cdiv(rem * s, 256);     // the same, only the rem tiles split
-  return tail <= all ? R * 256 : 0;
+  return (s > 1 && R > 0 && rem > 0) ? R * 256 : 0;
 }
 
 // fp32 partial floats a split store GEMM needs (0 without a split); `forced`

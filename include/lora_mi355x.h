@@ -144,8 +144,8 @@ typedef struct lora_proj {
  *           Only a dense plain-store GEMM with one output region can split;
  *           elsewhere ksplit must be 0 or 1.  Each part needs at least one
  *           K step of 64.  When the 256x256 tiles fill one or more whole
- *           rounds of 256 CUs and splitting only the tiles left over fills
- *           the last rounds as well as splitting all, only those are split.
+ *           rounds of 256 CUs, only the tiles left over are split (the same
+ *           number of rounds as splitting all, with fewer partial sums).
  * gemm[] lists the call's GEMMs in launch order: gated / ReLU^2 MLP forward:
  * [0] gate/up (or up), [1] down; MLP backward: [0] dh, [1] dX; Q/K/V and O,
  * forward or backward: [0] (gemm[1] must be zero).  An invalid entry returns

@@ -148,3 +148,22 @@ def test_tail_split_o_fwd_and_qkv_dx(lm):
     # the split changes only the fp32 summation order of the split tiles' K parts
     assert_close("O split vs whole", host(Yo), host(Yo1), tol)
     assert_close("dX split vs whole", host(dX), host(dX1), tol)
+
+
+@pytest.mark.parametrize("ksplit", [3, 4])
+def test_tail_split_ragged(lm, ksplit):
+    """A tail split over ragged edge tiles: T = 2660 and N = 7104 give
+    11 x 28 = 308 tiles (the last m-tile 100 rows, the last n-tile 192
+    columns), 256 computed whole and 52 split into 3 or 4 K parts."""
+    import torch
+
+    cfg = WorkloadConfig(114, "attn", T=2660, H=7104, r=16, alpha=32, dtype="bf16", Nq=512, Nk=128, Nv=128)
+    inp = make_attn_inputs(cfg)
+    Xo = dev(inp["Xo"])
+    o = proj_dev(inp["o"])
+    Yo, Uo = lm.o_fwd(Xo, o, plan=[(8, ksplit)])
+    torch.cuda.synchronize()
+    Yr, so = OL.o_fwd(inp["Xo"], inp["o"])
+    tol = TOL["bf16"]
+    assert_close("O", host(Yo), Yr, tol)
+    assert_close("U_o", host(Uo), so["U"], tol)
