@@ -158,6 +158,10 @@ def _check_proj(name, p, n_in, n_out, r, X, dt):
     _need(f"{name}.B", p.B, (r, n_out), ad, X.device)
     if (p.W is None) == (p.nf4 is None):
         raise ValueError(f"{name}: exactly one of W and nf4 must be set")
+    if p.Wt is not None:
+        if p.W is None:
+            raise ValueError(f"{name}: Wt is only for a dense W")
+        _need(f"{name}.Wt", p.Wt, (n_out, n_in), X.dtype, X.device)
     if p.W is not None:
         _need(f"{name}.W", p.W, (n_in, n_out), X.dtype, X.device)
     else:
@@ -195,13 +199,17 @@ class NF4Weight:
 
 @dataclass
 class Proj:
-    """One LoRA projection: dense W or NF4 weight, adapters A, B and scale s."""
+    """One LoRA projection: dense W or NF4 weight, adapters A, B and scale s.
+    Wt (optional, dense bf16 only): the same weight stored [n_out, n_in]
+    (W.t().contiguous(), PyTorch nn.Linear's layout); the forward GEMMs read
+    it when every projection they read has one."""
 
     A: object
     B: object
     scale: float
     W: object = None
     nf4: Optional[NF4Weight] = None
+    Wt: object = None
 
     def c_struct(self, keep: list) -> L.lora_proj:
         p = L.lora_proj()
@@ -213,6 +221,7 @@ class Proj:
         p.A = _ptr(self.A)
         p.B = _ptr(self.B)
         p.scale = float(self.scale)
+        p.Wt = _ptr(self.Wt)
         return p
 
 

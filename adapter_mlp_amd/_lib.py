@@ -30,7 +30,7 @@ class lora_nf4(C.Structure):
 
 
 class lora_proj(C.Structure):
-    _fields_ = [("W", vp), ("nf4", C.POINTER(lora_nf4)), ("A", vp), ("B", vp), ("scale", C.c_float)]
+    _fields_ = [("W", vp), ("nf4", C.POINTER(lora_nf4)), ("A", vp), ("B", vp), ("scale", C.c_float), ("Wt", vp)]
 
 
 class lora_gemm_plan(C.Structure):

@@ -2,6 +2,7 @@
 // sequence of each call.  Every check runs on the host before the first
 // enqueue, so a call that returns an error has enqueued nothing.
 #include <cmath>
+#include <initializer_list>
 #include <cstdarg>
 #include <cstdio>
 #include <atomic>
@@ -151,6 +152,10 @@ lora_status check_proj(const Ctx& c, const lora_proj* p, int64_t n_in, int64_t n
   } else {
     TRY(check_ptr(c, p->W, name));
   }
+  if (p->Wt) {
+    CHECK(p->W != nullptr, LORA_EINVAL, "%s: Wt is only for a dense W", name);
+    TRY(check_ptr(c, p->Wt, name));
+  }
   TRY(check_ptr(c, p->A, name));
   TRY(check_ptr(c, p->B, name));
   CHECK(std::isfinite(p->scale), LORA_EINVAL, "%s: scale is not finite", name);
@@ -175,6 +180,21 @@ BSrc bsrc(const lora_proj* p, int64_t ld) {
     s.p = p->W;
     s.ld = ld;
   }
+  return s;
+}
+
+// A forward GEMM reads the K-contiguous copies Wt when every projection it
+// reads has one (bf16): B_NT over Wt [n_out, n_in] (row pitch n_in).
+bool fwd_t(const Ctx& c, std::initializer_list<const lora_proj*> ps) {
+  if (!c.bf16) return false;
+  for (const lora_proj* p : ps)
+    if (p->Wt == nullptr) return false;
+  return true;
+}
+BSrc bsrc_t(const lora_proj* p, int64_t n_in) {
+  BSrc s{};
+  s.p = p->Wt;
+  s.ld = n_in;
   return s;
 }
 
@@ -734,6 +754,7 @@ lora_status proj_forward(const Ctx& c, int64_t T, int64_t K, int64_t N, int64_t 
                          const lora_proj* o, void* Y, void* U, const OPlan& p, hipStream_t st) {
   const int64_t RL = c.rl(r);
   const bool lora = r > 0;
+  const bool tw = fwd_t(c, {o});
   GemmArgs g{};
   if (lora) {
     // every adapter operand of the call, packed in one launch
@@ -746,7 +767,7 @@ lora_status proj_forward(const Ctx& c, int64_t T, int64_t K, int64_t N, int64_t 
     pl.RL = (int)RL;
     pl.nparts = 1;
     pl.part[0] = part(o->B, N, 0, N, 0, (int)r, true);
-    pl.kmajor = c.bf16 ? 1 : 0;  // the bf16 NN GEMM reads [RL, vcols]
+    pl.kmajor = c.bf16 && !tw ? 1 : 0;  // the bf16 NN GEMM reads [RL, vcols], NT [vcols, RL]
     pb.add(pl);
     LAUNCHN("pack", st, launch_pack_batch(c.bf16, pb.b, st));
     RowProjArgs ra = rowproj_args(X, K, T, K, p.At, K, (int)r, (int)RL, (int)r);
@@ -767,11 +788,11 @@ lora_status proj_forward(const Ctx& c, int64_t T, int64_t K, int64_t N, int64_t 
   g.nreg = 1;
   g.epi = EPI_STORE;
   g.nf4 = o->nf4 != nullptr;
-  g.bkind = B_NN;
+  g.bkind = tw ? B_NT : B_NN;
   g.seg[0].A = X;
   g.seg[0].lda = K;
   g.seg[0].K = K;
-  g.seg[0].b[0][0] = bsrc(o, N);
+  g.seg[0].b[0][0] = tw ? bsrc_t(o, K) : bsrc(o, N);
   g.reg[0].N = N;
   g.reg[0].out = Y;
   g.reg[0].ldo = N;
@@ -922,6 +943,7 @@ lora_status lora_mlp_fwd(const lora_mlp_desc* d, const void* X, const lora_proj*
   gate = &sp[0];
   up = &sp[1];
   down = &sp[2];
+  const bool t_gu = fwd_t(c, {gate, up}), t_d = fwd_t(c, {down});
   // every adapter operand of the call, packed in one launch
   PackBatch pb;
   const void* srcs_gu[2] = {gate->A, up->A};
@@ -933,7 +955,7 @@ lora_status lora_mlp_fwd(const lora_mlp_desc* d, const void* X, const lora_proj*
   pl.nparts = 2;
   pl.part[0] = part(gate->B, I, 0, I, 0, (int)r, true);
   pl.part[1] = part(up->B, I, I, I, (int)r, (int)r, true);
-  pl.kmajor = c.bf16 ? 1 : 0;  // the bf16 NN GEMM reads [RL, vcols]
+  pl.kmajor = c.bf16 && !t_gu ? 1 : 0;  // the bf16 NN GEMM reads [RL, vcols], NT [vcols, RL]
   pb.add(pl);
   const void* srcs_d[1] = {down->A};
   pb.add_cat_t(p.At_d, I, (int)r, (int)r, 1, srcs_d);
@@ -943,7 +965,7 @@ lora_status lora_mlp_fwd(const lora_mlp_desc* d, const void* X, const lora_proj*
   pd.RL = (int)RLd;
   pd.nparts = 1;
   pd.part[0] = part(down->B, H, 0, H, 0, (int)r, true);
-  pd.kmajor = c.bf16 ? 1 : 0;  // the bf16 NN GEMM reads [RL, vcols]
+  pd.kmajor = c.bf16 && !t_d ? 1 : 0;
   pb.add(pd);
   LAUNCHN("pack", st, launch_pack_batch(c.bf16, pb.b, st));
 
@@ -967,12 +989,12 @@ lora_status lora_mlp_fwd(const lora_mlp_desc* d, const void* X, const lora_proj*
   g.epi = EPI_ACT_FWD;
   g.act = d->act;
   g.nf4 = gate->nf4 != nullptr;
-  g.bkind = B_NN;
+  g.bkind = t_gu ? B_NT : B_NN;
   g.seg[0].A = X;
   g.seg[0].lda = H;
   g.seg[0].K = H;
-  g.seg[0].b[0][0] = bsrc(gate, I);
-  g.seg[0].b[0][1] = bsrc(up, I);
+  g.seg[0].b[0][0] = t_gu ? bsrc_t(gate, H) : bsrc(gate, I);
+  g.seg[0].b[0][1] = t_gu ? bsrc_t(up, H) : bsrc(up, I);
   g.reg[0].N = I;
   g.reg[0].vcol0[0] = 0;
   g.reg[0].vcol0[1] = I;
@@ -1014,11 +1036,11 @@ lora_status lora_mlp_fwd(const lora_mlp_desc* d, const void* X, const lora_proj*
   gd.nreg = 1;
   gd.epi = EPI_STORE;
   gd.nf4 = down->nf4 != nullptr;
-  gd.bkind = B_NN;
+  gd.bkind = t_d ? B_NT : B_NN;
   gd.seg[0].A = p.h;
   gd.seg[0].lda = I;
   gd.seg[0].K = I;
-  gd.seg[0].b[0][0] = bsrc(down, H);
+  gd.seg[0].b[0][0] = t_d ? bsrc_t(down, I) : bsrc(down, H);
   gd.reg[0].N = H;
   gd.reg[0].out = Y;
   gd.reg[0].ldo = H;
@@ -1251,6 +1273,7 @@ lora_status lora_relu2_mlp_fwd(const lora_relu2_mlp_desc* d, const void* X, cons
   STAGE(p.ad_f, in, ad, 2, r, sp, st);
   up = &sp[0];
   down = &sp[1];
+  const bool t_u = fwd_t(c, {up}), t_d = fwd_t(c, {down});
   // every adapter operand of the call, packed in one launch
   PackBatch pb;
   const void* srcs_u[1] = {up->A};
@@ -1261,7 +1284,7 @@ lora_status lora_relu2_mlp_fwd(const lora_relu2_mlp_desc* d, const void* X, cons
   pu.RL = (int)RL;
   pu.nparts = 1;
   pu.part[0] = part(up->B, I, 0, I, 0, (int)r, true);
-  pu.kmajor = c.bf16 ? 1 : 0;  // the bf16 NN GEMM reads [RL, vcols]
+  pu.kmajor = c.bf16 && !t_u ? 1 : 0;  // the bf16 NN GEMM reads [RL, vcols], NT [vcols, RL]
   pb.add(pu);
   const void* srcs_d[1] = {down->A};
   pb.add_cat_t(p.At_d, I, (int)r, (int)r, 1, srcs_d);
@@ -1271,7 +1294,7 @@ lora_status lora_relu2_mlp_fwd(const lora_relu2_mlp_desc* d, const void* X, cons
   pd.RL = (int)RL;
   pd.nparts = 1;
   pd.part[0] = part(down->B, H, 0, H, 0, (int)r, true);
-  pd.kmajor = c.bf16 ? 1 : 0;
+  pd.kmajor = c.bf16 && !t_d ? 1 : 0;
   pb.add(pd);
   LAUNCHN("pack", st, launch_pack_batch(c.bf16, pb.b, st));
 
@@ -1290,11 +1313,11 @@ lora_status lora_relu2_mlp_fwd(const lora_relu2_mlp_desc* d, const void* X, cons
   g.nreg = 1;
   g.epi = EPI_ACT1_FWD;
   g.nf4 = up->nf4 != nullptr;
-  g.bkind = B_NN;
+  g.bkind = t_u ? B_NT : B_NN;
   g.seg[0].A = X;
   g.seg[0].lda = H;
   g.seg[0].K = H;
-  g.seg[0].b[0][0] = bsrc(up, I);
+  g.seg[0].b[0][0] = t_u ? bsrc_t(up, H) : bsrc(up, I);
   g.reg[0].N = I;
   g.AL = p.Us_u;
   g.ldal = RL;
@@ -1332,11 +1355,11 @@ lora_status lora_relu2_mlp_fwd(const lora_relu2_mlp_desc* d, const void* X, cons
   gd.nreg = 1;
   gd.epi = EPI_STORE;
   gd.nf4 = down->nf4 != nullptr;
-  gd.bkind = B_NN;
+  gd.bkind = t_d ? B_NT : B_NN;
   gd.seg[0].A = p.h;
   gd.seg[0].lda = I;
   gd.seg[0].K = I;
-  gd.seg[0].b[0][0] = bsrc(down, H);
+  gd.seg[0].b[0][0] = t_d ? bsrc_t(down, I) : bsrc(down, H);
   gd.reg[0].N = H;
   gd.reg[0].out = Y;
   gd.reg[0].ldo = H;
@@ -1539,6 +1562,7 @@ lora_status lora_qkv_fwd(const lora_qkv_desc* d, const void* X, const lora_proj*
   k = &sp[1];
   v = &sp[2];
 
+  const bool tw = fwd_t(c, {q, k, v});
   // every adapter operand of the call, packed in one launch
   PackBatch pb;
   const void* srcs[3] = {q->A, k->A, v->A};
@@ -1551,7 +1575,7 @@ lora_status lora_qkv_fwd(const lora_qkv_desc* d, const void* X, const lora_proj*
   pl.part[0] = part(q->B, Nq, 0, Nq, 0, (int)r, true);
   pl.part[1] = part(k->B, Nk, Nq, Nk, (int)r, (int)r, true);
   pl.part[2] = part(v->B, Nv, Nq + Nk, Nv, (int)(2 * r), (int)r, true);
-  pl.kmajor = c.bf16 ? 1 : 0;  // the bf16 NN GEMM reads [RL, vcols]
+  pl.kmajor = c.bf16 && !tw ? 1 : 0;  // the bf16 NN GEMM reads [RL, vcols], NT [vcols, RL]
   pb.add(pl);
   LAUNCHN("pack", st, launch_pack_batch(c.bf16, pb.b, st));
 
@@ -1572,13 +1596,13 @@ lora_status lora_qkv_fwd(const lora_qkv_desc* d, const void* X, const lora_proj*
   g.nreg = 3;
   g.epi = EPI_STORE;
   g.nf4 = q->nf4 != nullptr;
-  g.bkind = B_NN;
+  g.bkind = tw ? B_NT : B_NN;
   g.seg[0].A = X;
   g.seg[0].lda = H;
   g.seg[0].K = H;
-  g.seg[0].b[0][0] = bsrc(q, Nq);
-  g.seg[0].b[1][0] = bsrc(k, Nk);
-  g.seg[0].b[2][0] = bsrc(v, Nv);
+  g.seg[0].b[0][0] = tw ? bsrc_t(q, H) : bsrc(q, Nq);
+  g.seg[0].b[1][0] = tw ? bsrc_t(k, H) : bsrc(k, Nk);
+  g.seg[0].b[2][0] = tw ? bsrc_t(v, H) : bsrc(v, Nv);
   const int64_t Ns[3] = {Nq, Nk, Nv};
   void* outs[3] = {Q, K, V};
   int64_t v0 = 0;

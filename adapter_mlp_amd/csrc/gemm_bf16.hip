@@ -617,7 +617,7 @@ static_assert(SPARE + SPARE_BYTES <= LDS_BYTES, "NF4 code ring exceeds LDS");
 
 template <int BKIND, bool DUAL, int EPI, bool NF4, int ACT>
 __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
-  static_assert(!(DUAL && BKIND == B_NT), "gate/up tiles read forward (NN) weights");
+  static_assert(!(DUAL && BKIND == B_NT && NF4), "NF4 gate/up tiles read forward (NN) weights");
   __shared__ __attribute__((aligned(1024))) char smem_raw[LDS_BYTES];
   lds_char* const lds = (lds_char*)smem_raw;
 
@@ -698,14 +698,17 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   // cursor stays in scalar registers
   auto cur_begin = [&]() {
     const GemmSeg& S = args.seg[lseg];
-    const BSrc& B = S.b[reg][(BKIND == B_NN && DUAL) ? (wn >> 1) : 0];
+    const BSrc& B = S.b[reg][DUAL ? (wn >> 1) : 0];
     lsteps = (int)(S.K / BK);
     lk0 = 0;
     const char* pw;
     int64_t nw, sw;
     if constexpr (BKIND == B_NT) {
-      pw = static_cast<const char*>(B.p) + tnl * 256 * B.ld * 2;
-      nw = (NR - tnl * 256) * B.ld * 2;
+      // gate/up tiles: rows 0..127 of the tile are 128 gate columns, rows
+      // 128..255 the same up columns (column group wn / 2 of the loader)
+      const int64_t row0 = DUAL ? tnl * 128 : tnl * 256;
+      pw = static_cast<const char*>(B.p) + row0 * B.ld * 2;
+      nw = (NR - row0) * B.ld * 2;
       sw = BK * 2;
     } else {
       const int64_t ncol0 = DUAL ? tnl * 128 : tnl * 256 + (wn >> 1) * 128;
@@ -765,7 +768,9 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
     const uint32_t wslot = lds_addr(lds) + W_RING + slot * SLOT_BYTES;
     const i32x4 rb = rsrc_words(lp, ln);
     if constexpr (BKIND == B_NT) {
-      int x = kc_x, r = kc_row;
+      // source row in the loader's column group (gate/up tiles: wn & 1 picks
+      // the 64-row half); the LDS row and its swizzle are those of the tile
+      int x = kc_x, r = DUAL ? (wn & 1) * 64 + (lane >> 3) : kc_row;
       asm volatile("" : "+v"(x), "+v"(r));
       const uint32_t base = (uint32_t)r * lld2;
       const uint32_t dst = wslot + wn * 8 * 1024;
@@ -809,7 +814,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
       return row < (int)NR ? (uint32_t)row * (uint32_t)wcols + (uint32_t)k0 : 0xffffff80u;
     }
   };
-  auto nf4_src = [&](const GemmSeg& S) -> const BSrc& { return S.b[reg][(BKIND == B_NN && DUAL) ? (wn >> 1) : 0]; };
+  auto nf4_src = [&](const GemmSeg& S) -> const BSrc& { return S.b[reg][DUAL ? (wn >> 1) : 0]; };
   // group 1: codes and scales of the next NF4 step into code slot `slot`
   auto issue_codes = [&](int slot) {
     const i32x4 rc = rsrc_words(lcodes, lnumel / 2);
@@ -933,8 +938,11 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   };
   int ao[4];
   kc_offsets(wm * 128 + (lane & 31), ao);
+  // NT weights: fragment i of wavefront wn is tile row wn * 64 + 32 i + lane % 32;
+  // in gate/up tiles, gate row wn * 32 + lane % 32 (i = 0) and the up row 128
+  // below it (i = 1), whose swizzle is the same
   int bo[4];
-  if constexpr (BKIND == B_NT) kc_offsets(wn * 64 + (lane & 31), bo);
+  if constexpr (BKIND == B_NT) kc_offsets(DUAL ? wn * 32 + (lane & 31) : wn * 64 + (lane & 31), bo);
 
   bf16x8 fa[4][2], fb[4][4];
   auto read = [&](int aslot, int wslot) {
@@ -950,8 +958,8 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
           else
             fa[ks][i] = lds_read_tr8(wt + fa_nn[i] + (16 * ks) * 256, 4 * 256);
         } else {
-          const int y = ((2 * ks) ^ (4 * (i & 1))) >> 1;
-          fa[ks][i] = __builtin_bit_cast(bf16x8, lds_read16(wt + bo[y] + i * 32 * 128));
+          const int y = DUAL ? ks : ((2 * ks) ^ (4 * (i & 1))) >> 1;
+          fa[ks][i] = __builtin_bit_cast(bf16x8, lds_read16(wt + bo[y] + i * (DUAL ? 128 : 32) * 128));
         }
       }
 #pragma unroll
@@ -1198,6 +1206,14 @@ hipError_t launch_family(const GemmArgs& a, hipStream_t st) {
                                       : launch<B_NN, true, EPI_ACT_FWD, NF4, LORA_ACT_GEGLU_TANH>(a, st);
     if (a.epi == EPI_ACT1_FWD) return launch<B_NN, false, EPI_ACT1_FWD, NF4>(a, st);
     return launch<B_NN, false, EPI_STORE, NF4>(a, st);
+  }
+  if constexpr (!NF4) {  // forward GEMMs over K-contiguous weights (dense only)
+    if (a.epi == EPI_ACT_FWD)
+      return a.act == LORA_ACT_SWIGLU ? launch<B_NT, true, EPI_ACT_FWD, false, LORA_ACT_SWIGLU>(a, st)
+                                      : launch<B_NT, true, EPI_ACT_FWD, false, LORA_ACT_GEGLU_TANH>(a, st);
+    if (a.epi == EPI_ACT1_FWD) return launch<B_NT, false, EPI_ACT1_FWD, false>(a, st);
+  } else {
+    if (a.epi == EPI_ACT_FWD || a.epi == EPI_ACT1_FWD) return hipErrorInvalidValue;
   }
   if (a.epi == EPI_ACT_BWD)
     return a.act == LORA_ACT_SWIGLU ? launch<B_NT, false, EPI_ACT_BWD, NF4, LORA_ACT_SWIGLU>(a, st)

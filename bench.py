@@ -375,6 +375,16 @@ def nf4_report(cfg, step, lm, torch, reps=5):
 # Workloads
 # ---------------------------------------------------------------------------
 
+def with_wt(step):
+    """Give every dense bf16 projection of a step the K-contiguous copy of its
+    frozen weight, Wt = W^T ([n_out, n_in]); the library's forward GEMMs then
+    read Wt, the backward ones W."""
+    for p in step.p.values():
+        if p.W is not None and p.nf4 is None and p.W.element_size() == 2:
+            p.Wt = p.W.t().contiguous()
+    return step
+
+
 class MlpStep:
     def __init__(self, cfg, inp, lm, torch):
         self.cfg, self.lm = cfg, lm
@@ -549,6 +559,8 @@ def main():
                     help="f32: fp32 adapters and adapter gradients with bf16 inputs (fp32 LoRA-gradient mode)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--wt", action="store_true",
+                    help="also pass each dense bf16 base weight as W^T, so the forward GEMMs read it K-contiguous")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU run: turn two rocprofv3 --pmc counter files into profiles/*_traffic.txt")
     ap.add_argument("--counter-summary", nargs="+", metavar="CSV",
@@ -589,6 +601,8 @@ def main():
     inp = make_inputs(cfg)
     log(f"[bench] inputs ready in {time.time() - t0:.1f} s")
     step = {"mlp": MlpStep, "relu2": Relu2Step, "attn": AttnStep}[cfg.kind](cfg, inp, lm, torch)
+    if args.wt:
+        with_wt(step)
     torch.cuda.synchronize()
 
     # warm-up; the first warm-up step also finds the dominant GEMM family
@@ -668,6 +682,8 @@ def main():
                       else {"intermediate": cfg.I, "activation": "relu2"} if cfg.kind == "relu2"
                       else {"q": cfg.Nq, "k": cfg.Nk, "v": cfg.Nv, "o": [cfg.Nq, cfg.H]}),
                    "rank": cfg.r, "alpha": cfg.alpha, "base": "nf4" if cfg.nf4 else "bf16",
+                   **({"base_layout": "W [in, out] and W^T [out, in] (forward GEMMs read W^T)"} if args.wt
+                      else {}),
                    "adapters": args.lora_dtype,
                    "parallelism": "single GPU"},
         "tflops": tflops,

@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define LORA_MI355X_VERSION 2
+#define LORA_MI355X_VERSION 3
 
 typedef enum lora_status {
   LORA_OK = 0,
@@ -119,13 +119,22 @@ typedef struct lora_nf4 {
 
 /* One LoRA projection: exactly one of W (dense, compute dtype) and nf4 is
  * non-NULL.  A [n_in, r], B [r, n_out] in the compute dtype (fp32 under
- * LORA_BF16_F32LORA); scale = s. */
+ * LORA_BF16_F32LORA); scale = s.
+ * Wt (optional, dense bf16 only, else NULL): the same frozen weight stored
+ * [n_out, n_in], i.e. W^T, PyTorch nn.Linear's own layout.  The forward
+ * product X W reads the weight along n_in; from Wt that is a K-contiguous
+ * operand, which the bf16 GEMM loads and feeds to the matrix cores with
+ * fewer LDS reads than W's N-contiguous rows.  When every projection of a
+ * forward GEMM has Wt (gate and up together, q, k and v together), that GEMM
+ * reads Wt; backward GEMMs always read W.  Wt must hold exactly W^T (not
+ * checked); it is ignored in fp32. */
 typedef struct lora_proj {
   const void* W;
   const lora_nf4* nf4;
   const void* A;
   const void* B;
   float scale;
+  const void* Wt;
 } lora_proj;
 
 /* Optional launch plan of a call's GEMMs ("loralei" README, section "Use":

@@ -104,6 +104,11 @@ int main() {
   s32.dtype = LORA_F32;
   lora_mlp_workspace_size(&s32, &f, &b);
   expect("mlp nf4 fp32", lora_mlp_fwd(&s32, F, &pq, &pq, &p, F2, &sv, F3, f, nullptr), LORA_EUNSUPPORTED);
+  lora_mlp_workspace_size(&sd, &f, &b);
+  lora_proj pqt{nullptr, &q, F2, F3, 2.0f, F};
+  expect("mlp nf4 with Wt", lora_mlp_fwd(&sd, F, &pqt, &pq, &p, F2, &sv, F3, f, nullptr), LORA_EINVAL);
+  lora_proj podd{F, nullptr, F2, F3, 2.0f, ODD};
+  expect("mlp Wt odd", lora_mlp_fwd(&sd, F, &podd, &p, &p, F2, &sv, F3, f, nullptr), LORA_EALIGN);
   lora_nf4 qs{q.codes, q.q8, q.s2, q.mu, 64, 64};
   expect("nf4 dequant numel", lora_nf4_dequant(&qs, F, LORA_BF16, nullptr), LORA_ESHAPE);
   expect("nf4 unpack null", lora_nf4_unpack_codes(&q, nullptr, nullptr), LORA_EINVAL);

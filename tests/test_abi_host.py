@@ -40,7 +40,7 @@ def test_exports_every_declared_function(L):
 
 def test_version_and_strerror(L):
     lib = L.load()
-    assert lib.lora_version() == 2
+    assert lib.lora_version() == 3
     for s in range(8):
         assert lib.lora_strerror(s)
     assert lib.lora_strerror(0) == b"success"

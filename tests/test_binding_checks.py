@@ -119,3 +119,19 @@ def test_nf4_weight_arrays_checked():
                                             cols=n_out))
     with pytest.raises(ValueError, match="q8"):
         lm.o_fwd(X, p)
+
+
+def test_wt_checked():
+    """Wt is the dense weight stored [n_out, n_in]: the wrong shape, a
+    non-contiguous view, or Wt beside an NF4 weight raise before any call."""
+    X = torch.zeros(T, H, dtype=torch.bfloat16)
+    o = _proj(H, 128)
+    o.Wt = torch.zeros(H, 128, dtype=torch.bfloat16)  # [n_in, n_out]: transposed shape
+    with pytest.raises(ValueError, match="Wt"):
+        lm.o_fwd(X, o)
+    o.Wt = torch.zeros(H, 128, dtype=torch.bfloat16).t()  # right shape, not contiguous
+    with pytest.raises(ValueError, match="Wt"):
+        lm.o_fwd(X, o)
+    o2 = lm.Proj(A=o.A, B=o.B, scale=1.0, nf4=object(), Wt=torch.zeros(128, H, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="Wt"):
+        lm.o_fwd(X, o2)
