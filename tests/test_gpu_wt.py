@@ -119,3 +119,40 @@ def test_o_forward_over_wt_tail_split(lm):
     Yr, so = OL.o_fwd(inp["Xo"], inp["o"])
     assert_close("O", host(Yo), Yr, TOL["bf16"])
     assert_close("U_o", host(Uo), so["U"], TOL["bf16"])
+
+
+def test_mlp_forward_over_wt_fp32_adapters(lm):
+    """The fp32 LoRA-gradient mode stages bf16 copies of the adapters; the
+    staged projections keep Wt."""
+    cfg = WorkloadConfig(124, "mlp", T=300, H=512, I=1088, r=16, alpha=32, dtype="bf16", act="swiglu",
+                         lora_dtype="f32")
+    inp = make_mlp_inputs(cfg)
+    X = dev(inp["X"])
+    g, u, d = (_with_wt(proj_dev(inp[k], adapters="f32")) for k in ("gate", "up", "down"))
+    (Y, saved), fams = _traced(lm, lambda: lm.mlp_fwd(X, g, u, d, "swiglu"))
+    assert "gemm_nt_act_fwd" in fams, fams
+    cast = {k: OL.to_compute_adapters(inp[k]) for k in ("gate", "up", "down")}
+    Yr, sr = OL.mlp_fwd(inp["X"], cast["gate"], cast["up"], cast["down"], "swiglu")
+    assert_close("Y", host(Y), Yr, TOL["bf16"])
+    assert_close("e", host(saved["e"]), sr["e"], TOL["bf16"])
+
+
+def test_o_forward_noalloc_over_wt(lm):
+    """The no-allocation forward with Wt equals lora_o_fwd with Wt, on two calls
+    in a row, the second smaller."""
+    import torch
+
+    for T in (700, 129):
+        cfg = WorkloadConfig(125, "attn", T=T, H=512, r=16, alpha=32, dtype="bf16", Nq=512, Nk=128, Nv=128)
+        inp = make_attn_inputs(cfg)
+        Xo = dev(inp["Xo"])
+        o = _with_wt(proj_dev(inp["o"]))
+        Y1, U1 = lm.o_fwd(Xo, o)
+        Y2 = torch.empty_like(Y1)
+        U2 = torch.empty_like(U1)
+        lm.o_fwd_noalloc(Xo, o, Y=Y2, U=U2)
+        torch.cuda.synchronize()
+        Yr, so = OL.o_fwd(inp["Xo"], inp["o"])
+        assert_close("O noalloc", host(Y2), Yr, TOL["bf16"])
+        assert_close("U noalloc", host(U2), so["U"], TOL["bf16"])
+        assert_close("O noalloc vs o_fwd", host(Y2), host(Y1), TOL["bf16"])
