@@ -169,22 +169,33 @@ def tune_call(run, gemms, reps: int = 3):
 # Gated MLP
 # ---------------------------------------------------------------------------
 
-def mlp_key(T, H, I, r, act, dtype_code, nf4) -> str:
-    return f"mlp:T={T}:H={H}:I={I}:r={r}:act={act}:dtype={dtype_code}:base={'nf4' if nf4 else 'dense'}"
+def _base(nf4, wt) -> str:
+    """Base weights of a key: NF4, dense, or dense with the nn.Linear-layout
+    copies (Wt), whose forward GEMMs run other kernels."""
+    return "nf4" if nf4 else ("dense_wt" if wt else "dense")
 
 
-def _mlp_shape(X, gate, act):
+def _has_wt(projs) -> bool:
+    return all(getattr(p, "Wt", None) is not None for p in projs)
+
+
+def mlp_key(T, H, I, r, act, dtype_code, nf4, wt=False) -> str:
+    return f"mlp:T={T}:H={H}:I={I}:r={r}:act={act}:dtype={dtype_code}:base={_base(nf4, wt)}"
+
+
+def _mlp_shape(X, gate, up, down, act):
     from . import _call_dtype
 
     T, H = X.shape
     I, r = gate.B.shape[1], gate.A.shape[1]
-    return T, H, I, r, mlp_key(T, H, I, r, act, _call_dtype(X, (gate,)), gate.nf4 is not None)
+    wt = _has_wt((gate, up, down))
+    return T, H, I, r, mlp_key(T, H, I, r, act, _call_dtype(X, (gate,)), gate.nf4 is not None, wt)
 
 
 def mlp_plans(cache: PlanCache, X, gate, up, down, act="swiglu"):
     """The cached plans {"fwd": plan, "bwd": plan} of this shape on this GPU,
     or None (a miss: call with plan=None for the library's defaults)."""
-    *_, key = _mlp_shape(X, gate, act)
+    *_, key = _mlp_shape(X, gate, up, down, act)
     e = cache.get(key, X.device)
     return None if e is None else {"fwd": _as_plan(e["fwd"]), "bwd": _as_plan(e["bwd"])}
 
@@ -195,7 +206,7 @@ def tune_mlp(cache: PlanCache, X, dY, gate, up, down, act="swiglu", reps: int = 
     {"fwd": plan, "bwd": plan}."""
     from . import mlp_bwd, mlp_fwd
 
-    T, H, I, r, key = _mlp_shape(X, gate, act)
+    T, H, I, r, key = _mlp_shape(X, gate, up, down, act)
     dense_down, dense_gu = down.nf4 is None, gate.nf4 is None
     Y, saved = mlp_fwd(X, gate, up, down, act)
     fwd, tf = tune_call(lambda p: mlp_fwd(X, gate, up, down, act, Y=Y, saved=saved, plan=p),
@@ -212,8 +223,8 @@ def tune_mlp(cache: PlanCache, X, dY, gate, up, down, act="swiglu", reps: int = 
 # Q/K/V and single projections
 # ---------------------------------------------------------------------------
 
-def qkv_key(T, H, Ns, r, dtype_code, nf4) -> str:
-    return f"qkv:T={T}:H={H}:N={Ns[0]},{Ns[1]},{Ns[2]}:r={r}:dtype={dtype_code}:base={'nf4' if nf4 else 'dense'}"
+def qkv_key(T, H, Ns, r, dtype_code, nf4, wt=False) -> str:
+    return f"qkv:T={T}:H={H}:N={Ns[0]},{Ns[1]},{Ns[2]}:r={r}:dtype={dtype_code}:base={_base(nf4, wt)}"
 
 
 def tune_qkv(cache: PlanCache, X, dQ, dK, dV, q, k, v, reps: int = 3):
@@ -224,7 +235,7 @@ def tune_qkv(cache: PlanCache, X, dQ, dK, dV, q, k, v, reps: int = 3):
     T, H = X.shape
     Ns = [p.B.shape[1] for p in (q, k, v)]
     r = q.A.shape[1]
-    key = qkv_key(T, H, Ns, r, _call_dtype(X, (q,)), q.nf4 is not None)
+    key = qkv_key(T, H, Ns, r, _call_dtype(X, (q,)), q.nf4 is not None, _has_wt((q, k, v)))
     Q, K, V, U = qkv_fwd(X, q, k, v)
     fwd, tf = tune_call(lambda p: qkv_fwd(X, q, k, v, out=[Q, K, V], U=U, plan=p), [(False, H // 64 + 1)], reps)
     dX, grads = qkv_bwd(dQ, dK, dV, X, U, q, k, v)
@@ -234,8 +245,8 @@ def tune_qkv(cache: PlanCache, X, dQ, dK, dV, q, k, v, reps: int = 3):
     return {"fwd": _as_plan(fwd), "bwd": _as_plan(bwd)}
 
 
-def o_key(T, K, N, r, dtype_code, nf4) -> str:
-    return f"o:T={T}:K={K}:N={N}:r={r}:dtype={dtype_code}:base={'nf4' if nf4 else 'dense'}"
+def o_key(T, K, N, r, dtype_code, nf4, wt=False) -> str:
+    return f"o:T={T}:K={K}:N={N}:r={r}:dtype={dtype_code}:base={_base(nf4, wt)}"
 
 
 def tune_o(cache: PlanCache, X, dY, o, reps: int = 3):
@@ -245,7 +256,7 @@ def tune_o(cache: PlanCache, X, dY, o, reps: int = 3):
 
     T, K = X.shape
     N, r = o.B.shape[1], o.A.shape[1]
-    key = o_key(T, K, N, r, _call_dtype(X, (o,)), o.nf4 is not None)
+    key = o_key(T, K, N, r, _call_dtype(X, (o,)), o.nf4 is not None, _has_wt((o,)))
     Y, U = o_fwd(X, o)
     fwd, tf = tune_call(lambda p: o_fwd(X, o, Y=Y, U=U, plan=p), [(o.nf4 is None, K // 64 + 1)], reps)
     dX, dA, dB = o_bwd(dY, X, U, o)
