@@ -138,7 +138,7 @@ def pmc_summary(fetch_csv, write_csv, config_id):
             fh.write(f"# each scaled by the same counter on a {true_kib // 1024} MiB fp32 copy kernel of known size\n")
             fh.write("#   cd /tmp && export TMPDIR=/tmp\n")
             fh.write(f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o pf -- python3 <repo>/bench.py "
-                     f"--config {config_id} --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration {true_kib // 1024}\n")
+                     f"--config {config_id} --steps 2 --warmup 1 --no-cpu-baseline --no-family-times --copy-calibration {true_kib // 1024}\n")
             fh.write("#   rocprofv3 --pmc WRITE_SIZE ... (same)\n")
             fh.write(f"#   python3 bench.py --config {config_id} --pmc-summary pf_counter_collection.csv pw_counter_collection.csv\n")
             fh.write(f"source_digest = {source_digest()}\n")
@@ -233,7 +233,7 @@ def counter_summary(csvs, config_id):
             fh.write("#   cd /tmp && export TMPDIR=/tmp\n")
             for name, cs in PMC_PASSES.items():
                 fh.write(f"#   rocprofv3 --pmc {' '.join(cs)} --output-format csv -d <dir> -o {name} -- python3 "
-                         f"<repo>/bench.py --config {config_id} --steps 2 --warmup 1 --no-cpu-baseline\n")
+                         f"<repo>/bench.py --config {config_id} --steps 2 --warmup 1 --no-cpu-baseline --no-family-times\n")
             fh.write(f"#   python3 bench.py --config {config_id} --counter-summary "
                      f"{' '.join(n + '_counter_collection.csv' for n in PMC_PASSES)}   (the sets that were run)\n")
             fh.write("# coexec_over_mfma_busy = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES (a VALU issued while\n")
@@ -280,7 +280,7 @@ def trace_summary(stats_csv, bench_log, config_id):
         f.write("# command (repository root on the GPU host; 3 warm-up + 10 timed steps):\n")
         f.write("#   cd /tmp && export TMPDIR=/tmp\n")
         f.write(f"#   rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o kt -- python3 <repo>/bench.py "
-                f"--config {config_id} --steps 10 --warmup 3 --no-cpu-baseline > kt.log\n")
+                f"--config {config_id} --steps 10 --warmup 3 --no-cpu-baseline --no-family-times > kt.log\n")
         f.write(f"#   python3 bench.py --config {config_id} --trace-summary <dir>/kt_kernel_stats.csv kt.log\n")
         f.write(f"source_digest = {source_digest()}\n")
         f.write("# durations in microseconds\n\n")
@@ -559,6 +559,8 @@ def main():
                     help="f32: fp32 adapters and adapter gradients with bf16 inputs (fp32 LoRA-gradient mode)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-family-times", action="store_true",
+                    help="skip the 5 extra traced steps that time every kernel family")
     ap.add_argument("--wt", action="store_true",
                     help="also pass each dense bf16 base weight as W^T, so the forward GEMMs read it K-contiguous")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -637,9 +639,22 @@ def main():
     avg_ms = kms / max(launches, 1)
     fl = kernel_flops(cfg, dominant)
     achieved = fl / (avg_ms / 1e3) / 1e12 if fl and avg_ms > 0 else None
-    traffic = read_traffic(dominant, workload_tag(cfg))
+    # the committed traffic profiles were taken with W only
+    traffic = None if args.wt else read_traffic(dominant, workload_tag(cfg))
     log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step ({wall / args.steps * 1e3:.3f} ms wall), "
         f"{tokens_s:,.0f} tokens/s, {tflops:.1f} TFLOP/s; {dominant}: {avg_ms:.3f} ms/launch")
+
+    # every kernel family's launch time, from 5 more steps with all families
+    # traced (after the timed region, which they do not touch)
+    per_family = {}
+    if not args.no_family_times:
+        n_fam = 5
+        lm.trace_begin("")
+        for _ in range(n_fam):
+            step()
+        torch.cuda.synchronize()
+        for k, (n, t) in lm.trace_end().items():
+            per_family[k] = {"launches_per_step": n / n_fam, "avg_ms": t / max(n, 1)}
 
     if args.copy_calibration > 0:
         n = args.copy_calibration * (1 << 20) // 4
@@ -694,6 +709,7 @@ def main():
                      "traffic": traffic, "flops_per_launch": fl, "avg_launch_ms": avg_ms,
                      "launches_timed": launches},
         "cpu_baseline": cpu,
+        "kernel_families": per_family,
     }
     if nf4:
         out["nf4"] = nf4
