@@ -478,6 +478,9 @@ float* partial_buf(Ws& w, const Ctx& c, int64_t T, int64_t K, int R) {
 // fixed-order reduce; h itself is never stored in the backward.
 bool fuse_da(const Ctx& c, int64_t r) { return c.bf16 && r <= 16; }
 int64_t fused_da_floats(int64_t T, int64_t I) { return cdiv(T, gemm_tile_rows(true)) * I * 16; }
+// Under the same condition the epilogue also forms the rank-r products of the
+// gradients it writes (P = dZ B^T and U^T dZ, per-tile partials): the pass
+// over those gradients is replaced by its reduce.
 
 struct MlpPlan {
   void *ad_f, *ad_b;  // adapter casts (fp32 LoRA-gradient mode), fwd / bwd workspace
@@ -522,8 +525,9 @@ MlpPlan plan_mlp(const Ctx& c, const lora_mlp_desc& d, void* ws_fwd, void* ws_bw
     const int64_t cands[4] = {colproj_partial_floats(T, H, (int)r), colproj_partial_floats(T, I, (int)r),
                               colproj_partial_floats(T, H, (int)(2 * r)), 0};
     for (int i = 0; i < 3; ++i) pf = cands[i] > pf ? cands[i] : pf;
-    if (fuse_da(c, r) && fused_da_floats(T, I) > pf) pf = fused_da_floats(T, I);
-    // the batched dg / de passes: one colproj partial per gradient
+    // the dh epilogue's partials: dA_d, then the column products over dg and de
+    if (fuse_da(c, r) && 3 * fused_da_floats(T, I) > pf) pf = 3 * fused_da_floats(T, I);
+    // the batched dg / de passes (r > 16): one colproj partial per gradient
     const int64_t Kb[2] = {I, I};
     const int64_t bp = 2 * rowcol_batch_partial_floats(T, Kb, 2, 0);
     if (bp > pf) pf = bp;
@@ -600,7 +604,8 @@ Relu2Plan plan_relu2(const Ctx& c, const lora_relu2_mlp_desc& d, void* ws_fwd, v
   if (c.bf16) {
     const int64_t a = colproj_partial_floats(T, H, (int)r), bb = colproj_partial_floats(T, I, (int)r);
     pf = a > bb ? a : bb;
-    if (fuse_da(c, r) && fused_da_floats(T, I) > pf) pf = fused_da_floats(T, I);
+    // the dh epilogue's partials: dA_d, then the column products over du
+    if (fuse_da(c, r) && 2 * fused_da_floats(T, I) > pf) pf = 2 * fused_da_floats(T, I);
     const int64_t kx = kpart_floats(c, T, H, I + RL, gemm_plan(c, 1).ksplit);  // dX split-K
     if (kx > pf) pf = kx;
   }
@@ -1152,6 +1157,19 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, 
     g.dA_part = p.partial;
     g.pd = p.Ps_d;
     g.ldpd = RLd;
+    // rank-r products of dg (p = 0: P_u, dB_u) and de (p = 1: P_g, dB_g)
+    g.rc_part[0] = p.partial + fused_da_floats(T, I);
+    g.rc_part[1] = p.partial + 2 * fused_da_floats(T, I);
+    g.rc_rpart[0] = p.rpartial;
+    g.rc_rpart[1] = p.rpartial + rowcol_partial_floats(T, I);
+    g.rc_b[0] = up->B;
+    g.rc_b[1] = gate->B;
+    g.rc_ldb = I;
+    g.rc_R = (int)r;
+    g.rc_u = U;
+    g.rc_ldu = 3 * r;
+    g.rc_uoff[0] = (int)r;
+    g.rc_uoff[1] = 0;
   } else {
     g.h_out = p.hb;
   }
@@ -1192,9 +1210,18 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, 
   c4.scales[0] = gate->scale;
   c4.dest[0] = gr->dB_gate;
   c4.rpartial = rc_fused ? p.rpartial + rowcol_partial_floats(T, I) : p.rpartial;
+  if (fda) {
+    // the dh epilogue wrote the partials: per-m-tile column products, per-n-tile row products
+    c3.partial = g.rc_part[0];
+    c4.partial = g.rc_part[1];
+    c3.nchunk = c4.nchunk = (int)cdiv(T, gemm_tile_rows(true));
+    c3.rpartial = g.rc_rpart[0];
+    c4.rpartial = g.rc_rpart[1];
+  }
   const ColProjArgs cb[2] = {c3, c4};
   const RowProjArgs rb[2] = {r2, r3};
-  LAUNCHN("rowcol", st, launch_rowcol_batch(c.bf16, cb, rb, 2, st));
+  if (fda) LAUNCHN("rowcol_reduce", st, launch_rowcol_batch_reduce(cb, rb, 2, st));
+  else LAUNCHN("rowcol", st, launch_rowcol_batch(c.bf16, cb, rb, 2, st));
 
   // [dA_u | dA_g] = X^T [s_u P_u | s_g P_g] in one pass over X
   ColProjArgs c5 = colproj_args(c, X, H, T, H, p.Ps_ug, RLg, (int)(2 * r), (int)r, false, p.partial);
@@ -1462,6 +1489,15 @@ lora_status lora_relu2_mlp_bwd(const lora_relu2_mlp_desc* d, const void* dY, con
     g.dA_part = p.partial;
     g.pd = p.Ps_d;
     g.ldpd = RL;
+    // rank-r products of du (P_u, dB_u)
+    g.rc_part[0] = p.partial + fused_da_floats(T, I);
+    g.rc_rpart[0] = p.rpartial;
+    g.rc_b[0] = up->B;
+    g.rc_ldb = I;
+    g.rc_R = (int)r;
+    g.rc_u = U;
+    g.rc_ldu = 2 * r;
+    g.rc_uoff[0] = 0;
   } else {
     g.h_out = p.hb;
   }
@@ -1487,7 +1523,15 @@ lora_status lora_relu2_mlp_bwd(const lora_relu2_mlp_desc* d, const void* dY, con
   ColProjArgs c3 = colproj_args(c, p.du, I, T, I, U, 2 * r, (int)r, (int)r, true, p.partial);
   c3.scales[0] = up->scale;
   c3.dest[0] = gr->dB_up;
-  LAUNCHN("rowcol", st, launch_rowcol(c.bf16, c3, r2, p.rpartial, st));
+  if (fda) {
+    // the dh epilogue wrote the partials: per-m-tile column products, per-n-tile row products
+    c3.partial = g.rc_part[0];
+    c3.nchunk = (int)cdiv(T, gemm_tile_rows(true));
+    c3.rpartial = g.rc_rpart[0];
+    LAUNCHN("rowcol_reduce", st, launch_rowcol_batch_reduce(&c3, &r2, 1, st));
+  } else {
+    LAUNCHN("rowcol", st, launch_rowcol(c.bf16, c3, r2, p.rpartial, st));
+  }
 
   // dA_u = X^T (s_u P_u)
   ColProjArgs c4 = colproj_args(c, X, H, T, H, p.Ps_u, RL, (int)r, (int)r, false, p.partial);

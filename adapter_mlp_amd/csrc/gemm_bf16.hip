@@ -111,13 +111,24 @@ __device__ __forceinline__ void for4(F&& f) {
 // loop has ended -- so global loads and stores move 16-byte chunks of
 // consecutive columns.  In dual tiles blocks i < NI/2 hold gate columns and
 // blocks i + NI/2 the up columns of the same outputs.
+// Backward activation epilogues: region 0 holds the fp32 dh rows of a pass,
+// then (once read) the bf16 gradient rows [NP][32][WN + 8] of the fused
+// rank-r products; then h rows [32][WN + 8] bf16, Pd rows [32][16] bf16 and
+// U rows [NP][32][16] bf16.
+template <int WN, int EPI>
+constexpr int bwd_region0() {
+  return 32 * (WN + 4) * 4 > (EPI == EPI_ACT_BWD ? 2 : 1) * 32 * (WN + 8) * 2
+             ? 32 * (WN + 4) * 4
+             : (EPI == EPI_ACT_BWD ? 2 : 1) * 32 * (WN + 8) * 2;
+}
 // Staging bytes one wavefront needs for a WN-column epilogue.
 template <int WN, int EPI>
 constexpr int epi_stage_bytes() {
   return EPI == EPI_STORE      ? 32 * (WN + 4) * 4
          : EPI == EPI_ACT_FWD  ? (3 * 32 * (WN / 2 + 8) * 2 > 8 * 64 * 16 ? 3 * 32 * (WN / 2 + 8) * 2 : 8 * 64 * 16)
          : EPI == EPI_ACT1_FWD ? 2 * 32 * (WN + 8) * 2
-                               : 32 * (WN + 4) * 4 + 32 * (WN + 8) * 2 + 32 * 16 * 2;
+                               : bwd_region0<WN, EPI>() + 32 * (WN + 8) * 2 + 32 * 16 * 2 +
+                                     (EPI == EPI_ACT_BWD ? 2 : 1) * 32 * 16 * 2;
 }
 
 // U = h Ad formed by a forward activation epilogue (u_part set): HC h columns
@@ -377,22 +388,45 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
     // columns of Pd, K = 32 rows per pass), both operands read with the
     // transposing LDS read from row-major staging.  The two row groups of the
     // block are added in LDS and written as the block's m-tile slice.
+    //
+    // With rc_part (the rank-r products of the gradients written here): each
+    // pass also stages its bf16 gradient rows dZ_p and, with 16x16x32 MFMAs,
+    //  - adds U_p^T dZ_p over its rows the same way as h^T Pd (M = 16
+    //    columns of dZ_p, N = the 16 columns of U_p, K = 32 rows);
+    //  - forms dZ_p B_p^T over the wavefront's columns (M = 16 rows, N = the
+    //    16 rows of B_p, K = 32 columns, dZ_p read K-contiguous), which the
+    //    four wavefronts of the row group add in LDS in a fixed order (two
+    //    block barriers per pass) and write as the tile's n-slice.
     constexpr bool GATED = EPI == EPI_ACT_BWD;
+    constexpr int NP = GATED ? 2 : 1;    // gradients with fused rank-r products
     constexpr int LD = WN + 4;           // fp32 staging [32][WN]
     constexpr int CPR = WN / 8;          // 8-float groups per row
     constexpr int RPP = 64 / CPR;
     constexpr int PASSES = 32 / RPP;
-    constexpr int HLD = WN + 8;          // bf16 h staging [32][WN] (fused dA)
-    constexpr int NCB = WN / 16;         // 16-column blocks of the fused product
+    constexpr int HLD = WN + 8;          // bf16 row staging [32][WN] (h, dZ_p)
+    constexpr int NCB = WN / 16;         // 16-column blocks of the fused products
+    constexpr int EB = epi_stage_bytes<WN, EPI>();
+    constexpr int R0 = bwd_region0<WN, EPI>();
+    static_assert(WN == 64 || WN == 32, "row products take 32-column K blocks");
     float* stg = reinterpret_cast<float*>(wstage);
-    uint16_t* hs = reinterpret_cast<uint16_t*>(wstage + 32 * LD * 4);
+    uint16_t* zs = reinterpret_cast<uint16_t*>(wstage);  // dZ_p rows, once stg is read
+    uint16_t* hs = reinterpret_cast<uint16_t*>(wstage + R0);
     uint16_t* pds = hs + 32 * HLD;       // Pd rows of the pass [32][16]
+    uint16_t* us = pds + 32 * 16;        // U_p rows of the pass [NP][32][16]
     const lds_char* const hs_l = (const lds_char*)hs;
     const lds_char* const pds_l = (const lds_char*)pds;
+    const lds_char* const zs_l = (const lds_char*)zs;
+    const lds_char* const us_l = (const lds_char*)us;
     const bool fuse = args.dA_part != nullptr;
+    const bool frc = args.rc_part[0] != nullptr;  // uniform over the block
     f32x4 dacc[NCB];
+    f32x4 dbacc[NP][NCB];
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) dacc[cb] = f32x4{0, 0, 0, 0};
+    for (int cb = 0; cb < NCB; ++cb) {
+      dacc[cb] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int p = 0; p < NP; ++p) dbacc[p][cb] = f32x4{0, 0, 0, 0};
+    }
     const int64_t ld = args.ld_act;
     const brsrc ei = make_rsrc(args.e_in, M * ld * 2);
     const brsrc gi = make_rsrc(args.g_in, M * ld * 2);
@@ -400,6 +434,21 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
     const brsrc deo = make_rsrc(args.de_out, M * ld * 2);
     const brsrc ho = make_rsrc(args.h_out, M * ld * 2);
     const brsrc pdr = make_rsrc(args.pd, M * args.ldpd * 2);
+    const brsrc ur = make_rsrc(args.rc_u, M * args.rc_ldu * 2);
+    // B_p fragments of the wavefront's columns: lane l holds B_p[l % 16][n .. n + 7],
+    // n = nbase + 32 kb + 8 (l / 16) (rows past the rank read zero)
+    bf16x8 bfr[NP][WN / 32];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int kb = 0; kb < WN / 32; ++kb) {
+        u32x4 v = u32x4{0, 0, 0, 0};
+        if (frc && cols_ok) {
+          const brsrc br = make_rsrc(args.rc_b[p], (int64_t)args.rc_R * args.rc_ldb * 2);
+          v = buf_load16(br, (uint32_t)(((lane & 15) * args.rc_ldb + nbase + 32 * kb + 8 * (lane >> 4)) * 2));
+        }
+        bfr[p][kb] = __builtin_bit_cast(bf16x8, v);
+      }
     // e, g of 32-row pass j (rows past M read zero, so h is zero there); the
     // loads of pass j + 1 are issued before pass j is computed, so each pass
     // waits for memory only as long as the previous pass's work does not cover
@@ -415,106 +464,197 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
         if constexpr (GATED) gvn[it] = buf_load16(gi, off);
       }
     };
-    // a wavefront past NR leaves dacc zero (those dA rows are not written)
-    if (cols_ok) {
-      load_eg(0);
+    // a wavefront past NR leaves dacc and dbacc zero (those rows are not
+    // written) and, with rc_part, takes part in every pass's barriers with
+    // zero row products
+    if (cols_ok || frc) {
+      if (cols_ok) load_eg(0);
       for4([&](auto jc) {
         constexpr int j = decltype(jc)::value;
+        f32x4 pacc[NP][2];
 #pragma unroll
-        for (int i = 0; i < NI; ++i)
+        for (int p = 0; p < NP; ++p) pacc[p][0] = pacc[p][1] = f32x4{0, 0, 0, 0};
+        if (cols_ok) {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int col = i * 32 + 8 * g + 4 * (lane >> 5);
-            *reinterpret_cast<f32x4*>(stg + (lane & 31) * LD + col) =
-                f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int col = i * 32 + 8 * g + 4 * (lane >> 5);
+              *reinterpret_cast<f32x4*>(stg + (lane & 31) * LD + col) =
+                  f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+            }
+          // Pd and U_p rows of this pass: lane l loads half l & 1 of row l / 2 (rows past M read zero)
+          const int64_t mh = mw + j * 32 + (lane >> 1);
+          u32x4 pv = u32x4{0, 0, 0, 0};
+          if (fuse) pv = buf_load16(pdr, row_off(mh, M, args.ldpd, 8 * (lane & 1), 2));
+          u32x4 uv[NP];
+#pragma unroll
+          for (int p = 0; p < NP; ++p) {
+            uv[p] = u32x4{0, 0, 0, 0};
+            if (frc) uv[p] = buf_load16(ur, row_off(mh, M, args.rc_ldu, args.rc_uoff[p] + 8 * (lane & 1), 2));
           }
-        // Pd rows of this pass: lane l loads half l & 1 of row l / 2 (rows past M read zero)
-        u32x4 pv = u32x4{0, 0, 0, 0};
-        if (fuse) {
-          const int64_t m = mw + j * 32 + (lane >> 1);
-          pv = buf_load16(pdr, row_off(m, M, args.ldpd, 8 * (lane & 1), 2));
-        }
-        u32x4 ev[PASSES], gv[PASSES];
+          u32x4 ev[PASSES], gv[PASSES];
 #pragma unroll
-        for (int it = 0; it < PASSES; ++it) {
-          ev[it] = evn[it];
-          if constexpr (GATED) gv[it] = gvn[it];
-        }
-        if constexpr (j < 3) load_eg(j + 1);
-        wave_sync();
-        f32x4 d0[PASSES], d1[PASSES];
+          for (int it = 0; it < PASSES; ++it) {
+            ev[it] = evn[it];
+            if constexpr (GATED) gv[it] = gvn[it];
+          }
+          if constexpr (j < 3) load_eg(j + 1);
+          wave_sync();
+          f32x4 d0[PASSES], d1[PASSES];
 #pragma unroll
-        for (int it = 0; it < PASSES; ++it) {
-          const int row = it * RPP + lane / CPR, c8 = lane % CPR;
-          d0[it] = *reinterpret_cast<const f32x4*>(stg + row * LD + c8 * 8);
-          d1[it] = *reinterpret_cast<const f32x4*>(stg + row * LD + c8 * 8 + 4);
-        }
+          for (int it = 0; it < PASSES; ++it) {
+            const int row = it * RPP + lane / CPR, c8 = lane % CPR;
+            d0[it] = *reinterpret_cast<const f32x4*>(stg + row * LD + c8 * 8);
+            d1[it] = *reinterpret_cast<const f32x4*>(stg + row * LD + c8 * 8 + 4);
+          }
 #pragma unroll
-        for (int it = 0; it < PASSES; ++it) {
-          const int row = it * RPP + lane / CPR, c8 = lane % CPR;
-          const int64_t m = mw + j * 32 + row;
-          const int64_t n = nbase + c8 * 8;
-          u32x4 dgv, dev, hv;
+          for (int it = 0; it < PASSES; ++it) {
+            const int row = it * RPP + lane / CPR, c8 = lane % CPR;
+            const int64_t m = mw + j * 32 + row;
+            const int64_t n = nbase + c8 * 8;
+            u32x4 dgv, dev, hv;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float dha = q < 2 ? d0[it][2 * q] : d1[it][2 * q - 4];
-            const float dhb = q < 2 ? d0[it][2 * q + 1] : d1[it][2 * q - 3];
-            const float e0 = lo_bf(ev[it][q]), e1 = hi_bf(ev[it][q]);
-            if constexpr (GATED) {
-              const float g0 = lo_bf(gv[it][q]), g1 = hi_bf(gv[it][q]);
-              float p0, s0, p1, s1;
-              act_fwd_bwd<false>(ACT, e0, p0, s0);
-              act_fwd_bwd<false>(ACT, e1, p1, s1);
-              hv[q] = pack_bf2(p0 * g0, p1 * g1);
-              dgv[q] = pack_bf2(dha * p0, dhb * p1);
-              dev[q] = pack_bf2(dha * g0 * s0, dhb * g1 * s1);
-            } else {
-              hv[q] = pack_bf2(relu2(e0), relu2(e1));
-              dgv[q] = pack_bf2(dha * relu2_grad(e0), dhb * relu2_grad(e1));
+            for (int q = 0; q < 4; ++q) {
+              const float dha = q < 2 ? d0[it][2 * q] : d1[it][2 * q - 4];
+              const float dhb = q < 2 ? d0[it][2 * q + 1] : d1[it][2 * q - 3];
+              const float e0 = lo_bf(ev[it][q]), e1 = hi_bf(ev[it][q]);
+              if constexpr (GATED) {
+                const float g0 = lo_bf(gv[it][q]), g1 = hi_bf(gv[it][q]);
+                float p0, s0, p1, s1;
+                act_fwd_bwd<false>(ACT, e0, p0, s0);
+                act_fwd_bwd<false>(ACT, e1, p1, s1);
+                hv[q] = pack_bf2(p0 * g0, p1 * g1);
+                dgv[q] = pack_bf2(dha * p0, dhb * p1);
+                dev[q] = pack_bf2(dha * g0 * s0, dhb * g1 * s1);
+              } else {
+                hv[q] = pack_bf2(relu2(e0), relu2(e1));
+                dgv[q] = pack_bf2(dha * relu2_grad(e0), dhb * relu2_grad(e1));
+              }
+            }
+            const uint32_t off = row_off(m, M, ld, n, 2);
+            buf_store16(dgo, off, dgv);
+            if constexpr (GATED) buf_store16(deo, off, dev);
+            if (!fuse) buf_store16(ho, off, hv);
+            else *reinterpret_cast<u32x4*>(hs + row * HLD + c8 * 8) = hv;
+            // every read of stg above precedes these writes in this wavefront's LDS order
+            if (frc) {
+              *reinterpret_cast<u32x4*>(zs + row * HLD + c8 * 8) = dgv;
+              if constexpr (GATED) *reinterpret_cast<u32x4*>(zs + 32 * HLD + row * HLD + c8 * 8) = dev;
             }
           }
-          const uint32_t off = row_off(m, M, ld, n, 2);
-          buf_store16(dgo, off, dgv);
-          if constexpr (GATED) buf_store16(deo, off, dev);
-          if (!fuse) buf_store16(ho, off, hv);
-          else *reinterpret_cast<u32x4*>(hs + row * HLD + c8 * 8) = hv;
-        }
-        if (fuse) {
-          *reinterpret_cast<u32x4*>(pds + (lane >> 1) * 16 + 8 * (lane & 1)) = pv;
-          wave_sync();
-          // lanes 16 g + 4 jj + q point at row 8 g + jj (+ 4), columns 4 q .. 4 q + 3 of a
-          // 16-column block: lane 16 g + i receives column i of rows 8 g .. 8 g + 7
-          const int g = lane >> 4, jj = (lane & 15) >> 2, q = lane & 3;
-          const bf16x8 pb = lds_read_tr8(pds_l + ((8 * g + jj) * 16 + 4 * q) * 2, 4 * 16 * 2);
+          if (fuse || frc) {
+            if (fuse) *reinterpret_cast<u32x4*>(pds + (lane >> 1) * 16 + 8 * (lane & 1)) = pv;
+            if (frc) {
 #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
-            const bf16x8 ha = lds_read_tr8(hs_l + ((8 * g + jj) * HLD + 16 * cb + 4 * q) * 2, 4 * HLD * 2);
-            dacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha, pb, dacc[cb], 0, 0, 0);
+              for (int p = 0; p < NP; ++p)
+                *reinterpret_cast<u32x4*>(us + p * 512 + (lane >> 1) * 16 + 8 * (lane & 1)) = uv[p];
+            }
+            wave_sync();
+            // lanes 16 g + 4 jj + q point at row 8 g + jj (+ 4), columns 4 q .. 4 q + 3 of a
+            // 16-column block: lane 16 g + i receives column i of rows 8 g .. 8 g + 7
+            const int g = lane >> 4, jj = (lane & 15) >> 2, q = lane & 3;
+            if (fuse) {
+              const bf16x8 pb = lds_read_tr8(pds_l + ((8 * g + jj) * 16 + 4 * q) * 2, 4 * 16 * 2);
+#pragma unroll
+              for (int cb = 0; cb < NCB; ++cb) {
+                const bf16x8 ha = lds_read_tr8(hs_l + ((8 * g + jj) * HLD + 16 * cb + 4 * q) * 2, 4 * HLD * 2);
+                dacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha, pb, dacc[cb], 0, 0, 0);
+              }
+            }
+            if (frc) {
+#pragma unroll
+              for (int p = 0; p < NP; ++p) {
+                const lds_char* const zp = zs_l + p * 32 * HLD * 2;
+                const bf16x8 ub = lds_read_tr8(us_l + (p * 512 + (8 * g + jj) * 16 + 4 * q) * 2, 4 * 16 * 2);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                  const bf16x8 za = lds_read_tr8(zp + ((8 * g + jj) * HLD + 16 * cb + 4 * q) * 2, 4 * HLD * 2);
+                  dbacc[p][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(za, ub, dbacc[p][cb], 0, 0, 0);
+                }
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                  for (int kb = 0; kb < WN / 32; ++kb) {
+                    const bf16x8 zr = __builtin_bit_cast(
+                        bf16x8, lds_read16(zp + ((16 * rb + (lane & 15)) * HLD + 32 * kb + 8 * (lane >> 4)) * 2));
+                    pacc[p][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(zr, bfr[p][kb], pacc[p][rb], 0, 0, 0);
+                  }
+              }
+            }
           }
+        }
+        if (frc) {
+          // pacc[p][rb][v] = row 16 rb + 4 (lane / 16) + v, rank column lane % 16, over this
+          // wavefront's columns; staged [p][32][16] fp32 in its h region (read above)
+          float* const xs = reinterpret_cast<float*>(hs);
+#pragma unroll
+          for (int p = 0; p < NP; ++p)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+              for (int v = 0; v < 4; ++v) xs[p * 512 + (16 * rb + 4 * (lane >> 4) + v) * 16 + (lane & 15)] = pacc[p][rb][v];
+          __syncthreads();
+          // wavefront wn adds the row group's four wavefronts (ascending) for gradient wn / 2,
+          // rows 16 (wn & 1) .. + 15 (gated), or rows 8 wn .. 8 wn + 7 (ungated, lanes < 32)
+          const int p = GATED ? (wn >> 1) : 0;
+          const int row = GATED ? 16 * (wn & 1) + (lane >> 2) : 8 * wn + ((lane >> 2) & 7);
+          const int j4 = 4 * (lane & 3);
+          const char* const g0 = wstage - wn * EB + R0;
+          f32x4 s = f32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int w2 = 0; w2 < 4; ++w2) s += *reinterpret_cast<const f32x4*>(g0 + w2 * EB + (p * 512 + row * 16 + j4) * 4);
+          const int64_t m = mw + j * 32 + row;
+          const int64_t tn = (nbase - (int64_t)WN * wn) / 256;
+          if (m < M && (GATED || lane < 32)) *reinterpret_cast<f32x4*>(args.rc_rpart[p] + (tn * M + m) * 16 + j4) = s;
+          __syncthreads();  // the h regions are rewritten by the next pass
         }
         wave_sync();
       });
     }
-    if (fuse) {
-      // dacc[cb][v] = sum over this wavefront's 128 rows of h[., c] Pd[., lane % 16],
-      // c = 16 cb + 4 (lane / 16) + v.  Group 1 hands its sums to group 0 through LDS.
-      constexpr int EB = epi_stage_bytes<WN, EPI>();
+    if (fuse || frc) {
+      // dacc[cb][v] = sum over this wavefront's 128 rows of h[., c] Pd[., lane % 16] (dbacc:
+      // dZ_p[., c] U_p[., lane % 16]), c = 16 cb + 4 (lane / 16) + v.  Group 1 hands its
+      // sums to group 0 through LDS.
       f32x4* red = reinterpret_cast<f32x4*>(wstage);
       if (wm == 1) {
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) red[cb * 64 + lane] = dacc[cb];
+        for (int cb = 0; cb < NCB; ++cb) {
+          red[cb * 64 + lane] = dacc[cb];
+#pragma unroll
+          for (int p = 0; p < NP; ++p) red[((1 + p) * NCB + cb) * 64 + lane] = dbacc[p][cb];
+        }
       }
       __syncthreads();
       if (wm == 0 && cols_ok) {
+        // the block's sums, staged [WN columns][16] (row pitch 20 floats) per product in this
+        // wavefront's region 0 (its hand-off area is unused), then stored as 1 KB runs: the
+        // wavefront's WN columns of a [., N, 16] slice are contiguous
         const f32x4* other = reinterpret_cast<const f32x4*>(wstage + 4 * EB);
+        float* const tb = reinterpret_cast<float*>(wstage);
+        constexpr int TP = 20, TB = WN * TP;
+        static_assert((1 + NP) * TB * 4 <= EB, "sum staging exceeds the wavefront's region");
         const int64_t tm = mw / 256;
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const f32x4 o = other[cb * 64 + lane];
+        for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const int64_t n = nbase + 16 * cb + 4 * (lane >> 4) + v;
-            args.dA_part[(tm * NR + n) * 16 + (lane & 15)] = dacc[cb][v] + o[v];
+            const int o = (16 * cb + 4 * (lane >> 4) + v) * TP + (lane & 15);
+            tb[o] = dacc[cb][v] + other[cb * 64 + lane][v];
+#pragma unroll
+            for (int p = 0; p < NP; ++p) tb[(1 + p) * TB + o] = dbacc[p][cb][v] + other[((1 + p) * NCB + cb) * 64 + lane][v];
+          }
+        wave_sync();
+#pragma unroll
+        for (int i = 0; i < WN / 16; ++i) {
+          const int col = 16 * i + (lane >> 2), j4 = 4 * (lane & 3);
+          const int64_t off = (tm * NR + nbase + col) * 16 + j4;
+          if (fuse) *reinterpret_cast<f32x4*>(args.dA_part + off) = *reinterpret_cast<const f32x4*>(tb + col * TP + j4);
+          if (frc) {
+#pragma unroll
+            for (int p = 0; p < NP; ++p)
+              *reinterpret_cast<f32x4*>(args.rc_part[p] + off) =
+                  *reinterpret_cast<const f32x4*>(tb + (1 + p) * TB + col * TP + j4);
           }
         }
       }

@@ -101,6 +101,24 @@ struct GemmArgs {
   const void* ad_t;
   int64_t ld_adt;
   int32_t u_R, pad4_;
+  // bf16 backward epilogues with rc_part[0] set (rank rc_R <= 16): the rank-r
+  // products of the gradients the epilogue writes, dZ_0 = dg_out and (gated)
+  // dZ_1 = de_out, formed from their bf16 values:
+  //   column products U_p^T dZ_p into rc_part[p] [ntile_m, N, 16] (U_p =
+  //     columns rc_uoff[p] .. + 15 of rc_u [M, rc_ldu]; sums past the rank
+  //     are never read);
+  //   row products dZ_p B_p^T into rc_rpart[p] [ntile_n, M, 16] (B_p = rc_b[p]
+  //     [rc_R, N], row pitch rc_ldb; zero past the rank);
+  // fp32, unscaled, one slice per m-tile or n-tile, which the rowcol reduce
+  // adds in a fixed order.
+  float* rc_part[2];
+  float* rc_rpart[2];
+  const void* rc_b[2];
+  int64_t rc_ldb;
+  const void* rc_u;
+  int64_t rc_ldu;
+  int32_t rc_uoff[2];
+  int32_t rc_R, pad5_;
 };
 
 // Columns of output covered by one n-tile.
@@ -183,6 +201,11 @@ struct RowColBatch {
   int32_t n, pad_;
 };
 hipError_t launch_rowcol_batch(bool bf16, const ColProjArgs* c, const RowProjArgs* r, int n, hipStream_t st);
+// Only the reduces of a rowcol batch whose partials another kernel wrote
+// (bf16, r[s].R <= 16): segment s's colproj outputs from c[s].nchunk slices
+// c[s].partial [nchunk, K_s, 16] and its rowproj outputs from ceil(K_s / 256)
+// slices c[s].rpartial [., T, 16].
+hipError_t launch_rowcol_batch_reduce(const ColProjArgs* c, const RowProjArgs* r, int n, hipStream_t st);
 int rowcol_batch_nchunk(int64_t T, const int64_t* K, int n);
 // floats of segment s's colproj partial in a batch
 int64_t rowcol_batch_partial_floats(int64_t T, const int64_t* K, int n, int s);

@@ -698,6 +698,25 @@ hipError_t launch_rowcol_batch(bool bf16, const ColProjArgs* c, const RowProjArg
   return hipGetLastError();
 }
 
+hipError_t launch_rowcol_batch_reduce(const ColProjArgs* c, const RowProjArgs* r, int n, hipStream_t st) {
+  if (n < 1 || n > 3) return hipErrorInvalidValue;
+  RowColBatch b{};
+  b.n = n;
+  unsigned rx = nblk(c[0].T * 4, 64);  // reduce blocks: the rowproj side
+  for (int i = 0; i < n; ++i) {
+    if (r[i].R > 16 || c[i].R > 16 || c[i].T != c[0].T || r[i].T != c[0].T) return hipErrorInvalidValue;
+    b.kb0[i + 1] = b.kb0[i] + (int32_t)((c[i].K + 255) / 256);
+    const unsigned cx = nblk(c[i].K * (c[i].R / 4), 64);
+    rx = cx > rx ? cx : rx;
+    b.c[i] = c[i];
+    b.r[i] = r[i];
+  }
+  // T = 0 still writes the colproj outputs: sums over no slices, zero
+  if (rx == 0) return hipSuccess;
+  hipLaunchKernelGGL(rowcol_batch_reduce_kernel, dim3(rx, (unsigned)(2 * n)), dim3(256), 0, st, b);
+  return hipGetLastError();
+}
+
 hipError_t launch_rowproj_reduce(const RowProjArgs& r, const float* rpartial, int nb, hipStream_t st) {
   if (r.T == 0) return hipSuccess;
   hipLaunchKernelGGL(rowproj_reduce_kernel, dim3(nblk(r.T * 4, 64)), dim3(256), 0, st, r, rpartial, nb);
