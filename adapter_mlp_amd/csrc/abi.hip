@@ -1176,13 +1176,13 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, 
   LAUNCH(gemm_on(c, g, st, I, 0));
 
   // dA_d = s_d h^T P_d  (P_d already scaled): the reduce of the epilogue's
-  // per-m-tile partials, or a pass over the stored h
+  // per-m-tile partials (in the launch of the gradients' reduces), or a pass
+  // over the stored h
   ColProjArgs c2 = colproj_args(c, p.hb, I, T, I, p.Ps_d, RLd, (int)r, (int)r, false, p.partial);
   c2.scales[0] = 1.0f;
   c2.dest[0] = gr->dA_down;
   if (fda) {
-    c2.nchunk = (int)cdiv(T, gemm_tile_rows(true));
-    LAUNCHN("colproj", st, launch_colproj_reduce(c2, st));
+    c2.nchunk = (int)cdiv(T, gemm_tile_rows(true));  // reduced in the launch of the gradients' reduces below
   } else {
     LAUNCHN("colproj", st, launch_colproj(c.bf16, c2, st));
   }
@@ -1220,7 +1220,7 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, 
   }
   const ColProjArgs cb[2] = {c3, c4};
   const RowProjArgs rb[2] = {r2, r3};
-  if (fda) LAUNCHN("rowcol_reduce", st, launch_rowcol_batch_reduce(cb, rb, 2, st));
+  if (fda) LAUNCHN("rowcol_reduce", st, launch_rowcol_batch_reduce(cb, rb, 2, &c2, 1, st));
   else LAUNCHN("rowcol", st, launch_rowcol_batch(c.bf16, cb, rb, 2, st));
 
   // [dA_u | dA_g] = X^T [s_u P_u | s_g P_g] in one pass over X
@@ -1504,13 +1504,13 @@ lora_status lora_relu2_mlp_bwd(const lora_relu2_mlp_desc* d, const void* dY, con
   LAUNCH(gemm_on(c, g, st, I, 0));
 
   // dA_d = s_d h^T P_d  (P_d already scaled): the reduce of the epilogue's
-  // per-m-tile partials, or a pass over the stored h
+  // per-m-tile partials (in the launch of the gradients' reduces), or a pass
+  // over the stored h
   ColProjArgs c2 = colproj_args(c, p.hb, I, T, I, p.Ps_d, RL, (int)r, (int)r, false, p.partial);
   c2.scales[0] = 1.0f;
   c2.dest[0] = gr->dA_down;
   if (fda) {
-    c2.nchunk = (int)cdiv(T, gemm_tile_rows(true));
-    LAUNCHN("colproj", st, launch_colproj_reduce(c2, st));
+    c2.nchunk = (int)cdiv(T, gemm_tile_rows(true));  // reduced in the launch of the gradients' reduces below
   } else {
     LAUNCHN("colproj", st, launch_colproj(c.bf16, c2, st));
   }
@@ -1528,7 +1528,7 @@ lora_status lora_relu2_mlp_bwd(const lora_relu2_mlp_desc* d, const void* dY, con
     c3.partial = g.rc_part[0];
     c3.nchunk = (int)cdiv(T, gemm_tile_rows(true));
     c3.rpartial = g.rc_rpart[0];
-    LAUNCHN("rowcol_reduce", st, launch_rowcol_batch_reduce(&c3, &r2, 1, st));
+    LAUNCHN("rowcol_reduce", st, launch_rowcol_batch_reduce(&c3, &r2, 1, &c2, 1, st));
   } else {
     LAUNCHN("rowcol", st, launch_rowcol(c.bf16, c3, r2, p.rpartial, st));
   }

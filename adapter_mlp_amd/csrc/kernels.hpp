@@ -198,14 +198,17 @@ struct RowColBatch {
   ColProjArgs c[3];
   RowProjArgs r[3];
   int32_t kb0[4];  // first column block of each segment; kb0[n] = all blocks
-  int32_t n, pad_;
+  int32_t n;
+  int32_t nx;  // reduce launch only: c[n .. n + nx - 1] are colproj reduces without a rowproj
 };
 hipError_t launch_rowcol_batch(bool bf16, const ColProjArgs* c, const RowProjArgs* r, int n, hipStream_t st);
 // Only the reduces of a rowcol batch whose partials another kernel wrote
 // (bf16, r[s].R <= 16): segment s's colproj outputs from c[s].nchunk slices
 // c[s].partial [nchunk, K_s, 16] and its rowproj outputs from ceil(K_s / 256)
-// slices c[s].rpartial [., T, 16].
-hipError_t launch_rowcol_batch_reduce(const ColProjArgs* c, const RowProjArgs* r, int n, hipStream_t st);
+// slices c[s].rpartial [., T, 16]; in the same launch, the nx colproj reduces
+// xc (as launch_colproj_reduce); n + nx <= 3.
+hipError_t launch_rowcol_batch_reduce(const ColProjArgs* c, const RowProjArgs* r, int n, const ColProjArgs* xc,
+                                      int nx, hipStream_t st);
 int rowcol_batch_nchunk(int64_t T, const int64_t* K, int n);
 // floats of segment s's colproj partial in a batch
 int64_t rowcol_batch_partial_floats(int64_t T, const int64_t* K, int n, int s);

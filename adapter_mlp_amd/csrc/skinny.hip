@@ -630,9 +630,11 @@ __global__ __launch_bounds__(256) void rowcol_batch_reduce_kernel(const RowColBa
   const int y = blockIdx.y;
   if (y < b.n) {
     colproj_reduce_body(b.c[y], 16, blockIdx.x);
-  } else {
+  } else if (y < 2 * b.n) {
     const int s = y - b.n;
     rowproj_reduce_body(b.r[s], b.c[s].rpartial, b.kb0[s + 1] - b.kb0[s], blockIdx.x);
+  } else {
+    colproj_reduce_body(b.c[y - b.n], 16, blockIdx.x);  // the extra colproj reduces
   }
 }
 }  // namespace
@@ -698,10 +700,12 @@ hipError_t launch_rowcol_batch(bool bf16, const ColProjArgs* c, const RowProjArg
   return hipGetLastError();
 }
 
-hipError_t launch_rowcol_batch_reduce(const ColProjArgs* c, const RowProjArgs* r, int n, hipStream_t st) {
-  if (n < 1 || n > 3) return hipErrorInvalidValue;
+hipError_t launch_rowcol_batch_reduce(const ColProjArgs* c, const RowProjArgs* r, int n, const ColProjArgs* xc,
+                                      int nx, hipStream_t st) {
+  if (n < 1 || nx < 0 || n + nx > 3) return hipErrorInvalidValue;
   RowColBatch b{};
   b.n = n;
+  b.nx = nx;
   unsigned rx = nblk(c[0].T * 4, 64);  // reduce blocks: the rowproj side
   for (int i = 0; i < n; ++i) {
     if (r[i].R > 16 || c[i].R > 16 || c[i].T != c[0].T || r[i].T != c[0].T) return hipErrorInvalidValue;
@@ -711,9 +715,15 @@ hipError_t launch_rowcol_batch_reduce(const ColProjArgs* c, const RowProjArgs* r
     b.c[i] = c[i];
     b.r[i] = r[i];
   }
+  for (int i = 0; i < nx; ++i) {
+    if (xc[i].R > 16) return hipErrorInvalidValue;
+    const unsigned cx = nblk(xc[i].K * (xc[i].R / 4), 64);
+    rx = cx > rx ? cx : rx;
+    b.c[n + i] = xc[i];
+  }
   // T = 0 still writes the colproj outputs: sums over no slices, zero
   if (rx == 0) return hipSuccess;
-  hipLaunchKernelGGL(rowcol_batch_reduce_kernel, dim3(rx, (unsigned)(2 * n)), dim3(256), 0, st, b);
+  hipLaunchKernelGGL(rowcol_batch_reduce_kernel, dim3(rx, (unsigned)(2 * n + nx)), dim3(256), 0, st, b);
   return hipGetLastError();
 }
 
