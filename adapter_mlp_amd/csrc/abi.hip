@@ -773,6 +773,7 @@ lora_status proj_forward(const Ctx& c, int64_t T, int64_t K, int64_t N, int64_t 
     pl.nparts = 1;
     pl.part[0] = part(o->B, N, 0, N, 0, (int)r, true);
     pl.kmajor = c.bf16 && !tw ? 1 : 0;  // the bf16 NN GEMM reads [RL, vcols], NT [vcols, RL]
+    pl.perm8 = pl.kmajor && o->nf4 != nullptr;
     pb.add(pl);
     LAUNCHN("pack", st, launch_pack_batch(c.bf16, pb.b, st));
     RowProjArgs ra = rowproj_args(X, K, T, K, p.At, K, (int)r, (int)RL, (int)r);
@@ -961,6 +962,7 @@ lora_status lora_mlp_fwd(const lora_mlp_desc* d, const void* X, const lora_proj*
   pl.part[0] = part(gate->B, I, 0, I, 0, (int)r, true);
   pl.part[1] = part(up->B, I, I, I, (int)r, (int)r, true);
   pl.kmajor = c.bf16 && !t_gu ? 1 : 0;  // the bf16 NN GEMM reads [RL, vcols], NT [vcols, RL]
+  pl.perm8 = pl.kmajor && gate->nf4 != nullptr;
   pb.add(pl);
   const void* srcs_d[1] = {down->A};
   pb.add_cat_t(p.At_d, I, (int)r, (int)r, 1, srcs_d);
@@ -971,6 +973,7 @@ lora_status lora_mlp_fwd(const lora_mlp_desc* d, const void* X, const lora_proj*
   pd.nparts = 1;
   pd.part[0] = part(down->B, H, 0, H, 0, (int)r, true);
   pd.kmajor = c.bf16 && !t_d ? 1 : 0;
+  pd.perm8 = pd.kmajor && down->nf4 != nullptr;
   pb.add(pd);
   LAUNCHN("pack", st, launch_pack_batch(c.bf16, pb.b, st));
 
@@ -1312,6 +1315,7 @@ lora_status lora_relu2_mlp_fwd(const lora_relu2_mlp_desc* d, const void* X, cons
   pu.nparts = 1;
   pu.part[0] = part(up->B, I, 0, I, 0, (int)r, true);
   pu.kmajor = c.bf16 && !t_u ? 1 : 0;  // the bf16 NN GEMM reads [RL, vcols], NT [vcols, RL]
+  pu.perm8 = pu.kmajor && up->nf4 != nullptr;
   pb.add(pu);
   const void* srcs_d[1] = {down->A};
   pb.add_cat_t(p.At_d, I, (int)r, (int)r, 1, srcs_d);
@@ -1322,6 +1326,7 @@ lora_status lora_relu2_mlp_fwd(const lora_relu2_mlp_desc* d, const void* X, cons
   pd.nparts = 1;
   pd.part[0] = part(down->B, H, 0, H, 0, (int)r, true);
   pd.kmajor = c.bf16 && !t_d ? 1 : 0;
+  pd.perm8 = pd.kmajor && down->nf4 != nullptr;
   pb.add(pd);
   LAUNCHN("pack", st, launch_pack_batch(c.bf16, pb.b, st));
 
@@ -1620,6 +1625,7 @@ lora_status lora_qkv_fwd(const lora_qkv_desc* d, const void* X, const lora_proj*
   pl.part[1] = part(k->B, Nk, Nq, Nk, (int)r, (int)r, true);
   pl.part[2] = part(v->B, Nv, Nq + Nk, Nv, (int)(2 * r), (int)r, true);
   pl.kmajor = c.bf16 && !tw ? 1 : 0;  // the bf16 NN GEMM reads [RL, vcols], NT [vcols, RL]
+  pl.perm8 = pl.kmajor && q->nf4 != nullptr;
   pb.add(pl);
   LAUNCHN("pack", st, launch_pack_batch(c.bf16, pb.b, st));
 

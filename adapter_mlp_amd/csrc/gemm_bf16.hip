@@ -66,6 +66,21 @@ __device__ __forceinline__ int nn_swz(int k) {
   return NF4 ? (((k & 3) << 2) | ((k >> 1) & 3)) : ((k & 3) << 2);
 }
 
+// v_permlane32_swap_b32: lo = (a in lanes 0-31, b of lanes 0-31 in lanes
+// 32-63), hi = (a of lanes 32-63 in lanes 0-31, b in lanes 32-63).  The
+// operands pass through empty asm statements: applied directly to elements
+// of an MFMA accumulator tuple, the swap was compiled with both operands
+// taken from one register.
+__device__ __forceinline__ void swap_lane_halves(float a, float b, float& lo, float& hi) {
+  uint32_t x = __builtin_bit_cast(uint32_t, a), y = __builtin_bit_cast(uint32_t, b);
+  asm volatile("" : "+v"(x), "+v"(y));
+  const auto s = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+  uint32_t p = s[0], q = s[1];
+  asm volatile("" : "+v"(p), "+v"(q));
+  lo = __builtin_bit_cast(float, p);
+  hi = __builtin_bit_cast(float, q);
+}
+
 // Wavefront-local LDS hand-off between lanes (each wavefront stages into its
 // own LDS region in the epilogue, so no block barrier is needed).
 __device__ __forceinline__ void wave_sync() {
@@ -688,7 +703,9 @@ __device__ __forceinline__ uint32_t nf4_lookup(const uint32_t (&pl)[4], uint32_t
   return __builtin_amdgcn_perm(b, a, fsel);
 }
 // 8 codes of one dword (element 2j in the high nibble of byte j, element
-// 2j + 1 in its low nibble) -> 8 bf16 in element order.
+// 2j + 1 in its low nibble) -> 8 bf16, in element order (NAT) or in the order
+// 0, 2, 4, 6, 1, 3, 5, 7, which saves the four final interleaving permutes.
+template <bool NAT>
 __device__ __forceinline__ u32x4 nf4_decode8(uint32_t w, const Nf4Planes& p) {
   const uint32_t se = (w >> 4) & 0x07070707u, fe = ((w >> 5) & 0x04040404u) | 0x03020100u;
   const uint32_t so = w & 0x07070707u, fo = ((w >> 1) & 0x04040404u) | 0x03020100u;
@@ -697,10 +714,17 @@ __device__ __forceinline__ u32x4 nf4_decode8(uint32_t w, const Nf4Planes& p) {
   const uint32_t e01 = __builtin_amdgcn_perm(he, le, 0x05010400u), e23 = __builtin_amdgcn_perm(he, le, 0x07030602u);
   const uint32_t o01 = __builtin_amdgcn_perm(ho, lo, 0x05010400u), o23 = __builtin_amdgcn_perm(ho, lo, 0x07030602u);
   u32x4 r;
-  r[0] = __builtin_amdgcn_perm(o01, e01, 0x05040100u);
-  r[1] = __builtin_amdgcn_perm(o01, e01, 0x07060302u);
-  r[2] = __builtin_amdgcn_perm(o23, e23, 0x05040100u);
-  r[3] = __builtin_amdgcn_perm(o23, e23, 0x07060302u);
+  if constexpr (NAT) {
+    r[0] = __builtin_amdgcn_perm(o01, e01, 0x05040100u);
+    r[1] = __builtin_amdgcn_perm(o01, e01, 0x07060302u);
+    r[2] = __builtin_amdgcn_perm(o23, e23, 0x05040100u);
+    r[3] = __builtin_amdgcn_perm(o23, e23, 0x07060302u);
+  } else {
+    r[0] = e01;
+    r[1] = e23;
+    r[2] = o01;
+    r[3] = o23;
+  }
   return r;
 }
 
@@ -1038,7 +1062,9 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
     const int omask = live ? 0x7fffffff : SPARE_BYTES - 1;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const u32x4 v = nf4_decode8(in.w[d], pl);
+      // NN tiles: the 8 columns of each chunk in the order 0, 2, 4, 6, 1, 3, 5, 7
+      // (restored in the accumulators by restore_cols); NT tiles: K order
+      const u32x4 v = nf4_decode8<BKIND != B_NN>(in.w[d], pl);
       int off;
       if constexpr (BKIND == B_NN) {
         const int k = 32 * (wn & 1) + (lane >> 1);
@@ -1130,6 +1156,30 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
     __builtin_amdgcn_s_setprio(1);
     mma_body();
     __builtin_amdgcn_s_setprio(0);
+  };
+  // NF4 NN tiles store each 8-column group of the weight tile in the order
+  // 0, 2, 4, 6, 1, 3, 5, 7, so accumulator registers 4k .. 4k + 3 hold, in lanes
+  // 0-31, columns 8k + 0, 2, 4, 6 and in lanes 32-63 columns 8k + 1, 3, 5, 7
+  // (natural: 8k + 0..3 and 8k + 4..7).  Exchanging the upper lane half of
+  // registers 4k, 4k + 1 with the lower lane half of registers 4k + 2, 4k + 3
+  // (v_permlane32_swap) and renaming restores the natural order.  It runs once,
+  // after the K loop: the dense adapter tile of these GEMMs comes packed in the
+  // same column order (the pack job's perm8).
+  auto restore_cols = [&]() {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          float n0, n1, n2, n3;
+          swap_lane_halves(acc[i][j][4 * k], acc[i][j][4 * k + 2], n0, n1);
+          swap_lane_halves(acc[i][j][4 * k + 1], acc[i][j][4 * k + 3], n2, n3);
+          acc[i][j][4 * k] = n0;
+          acc[i][j][4 * k + 1] = n1;
+          acc[i][j][4 * k + 2] = n2;
+          acc[i][j][4 * k + 3] = n3;
+        }
   };
   // MFMA cluster with the store half of an unpack interleaved: about five of
   // its vector instructions after each MFMA (its inputs are in registers).
@@ -1251,6 +1301,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
         phase_end();
         cs2 = cs2 == 2 ? 0 : cs2 + 1;
       }
+      if constexpr (BKIND == B_NN) restore_cols();
     } else {
       issue_codes(0);
       if (KN > 1) issue_codes(1);
@@ -1297,6 +1348,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
         phase_end();
         cs0 = cs0 == 2 ? 0 : cs0 + 1;
       }
+      if constexpr (BKIND == B_NN) restore_cols();
     }
   }
 

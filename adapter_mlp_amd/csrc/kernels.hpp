@@ -233,7 +233,11 @@ struct PackLoraArgs {
   void* out;
   int64_t vcols;
   int32_t RL, nparts;
-  int32_t kmajor, pad_;
+  int32_t kmajor;
+  // kmajor operands of NF4 forward (NN) GEMMs: within every 8 columns, column
+  // position q holds virtual column 2q (q < 4) or 2(q - 4) + 1, the order in
+  // which those GEMMs decode the weight tile (vcols a multiple of 8)
+  int32_t perm8;
   PackPart part[6];
 };
 struct PackBatchArgs {

@@ -462,8 +462,9 @@ __global__ void pack_batch_kernel(const PackBatchArgs b) {
   // kernel); launch_pack_batch checks that every job has fewer than 2^31 elements
   const uint32_t vc = (uint32_t)a.vcols, rl = (uint32_t)a.RL, n = vc * rl;
   for (uint32_t o = blockIdx.x * blockDim.x + threadIdx.x; o < n; o += gridDim.x * blockDim.x) {
-    const uint32_t v = a.kmajor ? o % vc : o / rl;
+    uint32_t v = a.kmajor ? o % vc : o / rl;
     const uint32_t kk = a.kmajor ? o / vc : o % rl;
+    if (a.perm8) v = (v & ~7u) | ((v & 3u) << 1) | ((v >> 2) & 1u);
     E val = E(0);
     for (int p = 0; p < a.nparts; ++p) {
       const PackPart& q = a.part[p];
