@@ -808,21 +808,29 @@ lora_status proj_forward(const Ctx& c, int64_t T, int64_t K, int64_t N, int64_t 
 
 // Input-gradient GEMM of one projection: dX = dY W^T + (s P) A^T with
 // s P = Ps [T, RL] (already formed); A rows feed the LoRA tail.
+// The adapter operand of an input-gradient GEMM: A [K, r] as the LoRA tail.
+PackBatch input_grad_pack(const Ctx& c, int64_t K, int64_t r, const lora_proj* o, const OPlan& p) {
+  PackBatch pb;
+  PackLoraArgs pl{};
+  pl.out = p.BLt_dx;
+  pl.vcols = K;
+  pl.RL = (int)c.rl(r);
+  pl.nparts = 1;
+  pl.part[0] = part(o->A, r, 0, K, 0, (int)r, false);
+  pb.add(pl);
+  return pb;
+}
+
+// packed: input_grad_pack's operand is already in place (an earlier launch ran it)
 lora_status proj_input_grad(const Ctx& c, int64_t T, int64_t K, int64_t N, int64_t r, const void* dY,
-                            const lora_proj* o, void* dX, const OPlan& p, hipStream_t st) {
+                            const lora_proj* o, void* dX, const OPlan& p, hipStream_t st, bool packed = false) {
   const int64_t RL = c.rl(r);
   GemmArgs g{};
   if (r > 0) {
-    // every adapter operand of the call, packed in one launch
-    PackBatch pb;
-    PackLoraArgs pl{};
-    pl.out = p.BLt_dx;
-    pl.vcols = K;
-    pl.RL = (int)RL;
-    pl.nparts = 1;
-    pl.part[0] = part(o->A, r, 0, K, 0, (int)r, false);
-    pb.add(pl);
-    LAUNCHN("pack", st, launch_pack_batch(c.bf16, pb.b, st));
+    if (!packed) {
+      const PackBatch pb = input_grad_pack(c, K, r, o, p);
+      LAUNCHN("pack", st, launch_pack_batch(c.bf16, pb.b, st));
+    }
     g.AL = p.Ps;
     g.ldal = RL;
     g.RL = (int)RL;
@@ -1101,7 +1109,7 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, 
   up = &sp[1];
   down = &sp[2];
   const void* U = saved->U;
-  // every adapter operand of the call, packed in one launch
+  // every adapter operand of the call, packed in one launch (with the reduce below)
   PackBatch pb;
   PackLoraArgs pl{};
   pl.out = p.BLt_dh;
@@ -1118,10 +1126,10 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, 
   px.part[0] = part(up->A, r, 0, H, 0, (int)r, false);
   px.part[1] = part(gate->A, r, 0, H, (int)r, (int)r, false);
   pb.add(px);
-  LAUNCHN("pack", st, launch_pack_batch(c.bf16, pb.b, st));
 
   // one pass over dY: P_d = dY B_d^T, formed once (scaled copy feeds dA_d and
-  // the dh GEMM), and dB_d = s_d U_d^T dY
+  // the dh GEMM), and dB_d = s_d U_d^T dY; the launch of its reduce also
+  // packs the adapter operands above, which the GEMMs read
   RowProjArgs r1 = rowproj_args(dY, H, T, H, down->B, H, (int)r, (int)RLd, (int)r);
   r1.scales[0] = down->scale;
   r1.out2 = p.Ps_d;
@@ -1129,7 +1137,7 @@ lora_status lora_mlp_bwd(const lora_mlp_desc* d, const void* dY, const void* X, 
   ColProjArgs c1 = colproj_args(c, dY, H, T, H, coff(U, 2 * r, c), 3 * r, (int)r, (int)r, true, p.partial);
   c1.scales[0] = down->scale;
   c1.dest[0] = gr->dB_down;
-  LAUNCHN("rowcol", st, launch_rowcol(c.bf16, c1, r1, p.rpartial, st));
+  LAUNCHN("rowcol", st, launch_rowcol(c.bf16, c1, r1, p.rpartial, st, &pb.b));
 
   // dh GEMM with the activation-gradient epilogue -> dg, de, h
   GemmArgs g{};
@@ -1439,7 +1447,7 @@ lora_status lora_relu2_mlp_bwd(const lora_relu2_mlp_desc* d, const void* dY, con
   up = &sp[0];
   down = &sp[1];
   const void* U = saved->U;
-  // every adapter operand of the call, packed in one launch
+  // every adapter operand of the call, packed in one launch (with the reduce below)
   PackBatch pb;
   PackLoraArgs pl{};
   pl.out = p.BLt_dh;
@@ -1455,10 +1463,10 @@ lora_status lora_relu2_mlp_bwd(const lora_relu2_mlp_desc* d, const void* dY, con
   px.nparts = 1;
   px.part[0] = part(up->A, r, 0, H, 0, (int)r, false);
   pb.add(px);
-  LAUNCHN("pack", st, launch_pack_batch(c.bf16, pb.b, st));
 
   // one pass over dY: P_d = dY B_d^T, formed once (scaled copy feeds dA_d and
-  // the dh GEMM), and dB_d = s_d U_d^T dY
+  // the dh GEMM), and dB_d = s_d U_d^T dY; the launch of its reduce also
+  // packs the adapter operands above, which the GEMMs read
   RowProjArgs r1 = rowproj_args(dY, H, T, H, down->B, H, (int)r, (int)RL, (int)r);
   r1.scales[0] = down->scale;
   r1.out2 = p.Ps_d;
@@ -1466,7 +1474,7 @@ lora_status lora_relu2_mlp_bwd(const lora_relu2_mlp_desc* d, const void* dY, con
   ColProjArgs c1 = colproj_args(c, dY, H, T, H, coff(U, r, c), 2 * r, (int)r, (int)r, true, p.partial);
   c1.scales[0] = down->scale;
   c1.dest[0] = gr->dB_down;
-  LAUNCHN("rowcol", st, launch_rowcol(c.bf16, c1, r1, p.rpartial, st));
+  LAUNCHN("rowcol", st, launch_rowcol(c.bf16, c1, r1, p.rpartial, st, &pb.b));
 
   // dh GEMM with the ReLU^2 gradient epilogue -> du, h
   GemmArgs g{};
@@ -1739,15 +1747,8 @@ lora_status lora_qkv_bwd(const lora_qkv_desc* d, const void* dQ, const void* dK,
       rpart += rowcol_partial_floats(T, Ns[i]);
     }
   }
-  LAUNCHN("rowcol", st, launch_rowcol_batch(c.bf16, cb, rb, 3, st));
-  // [dA_q | dA_k | dA_v] = X^T [s P] in one pass over X
-  ColProjArgs cx = colproj_args(c, X, H, T, H, p.Ps, RL, (int)(3 * r), (int)r, false, p.partial);
-  cx.scales[0] = cx.scales[1] = cx.scales[2] = 1.0f;
-  cx.dest[0] = gr->dA_q;
-  cx.dest[1] = gr->dA_k;
-  cx.dest[2] = gr->dA_v;
-  LAUNCHN("colproj", st, launch_colproj(c.bf16, cx, st));
-  // dX = sum_p dZ_p W_p^T + [s P] [A_q | A_k | A_v]^T
+  // the adapter operand of the dX GEMM, [A_q | A_k | A_v] as its LoRA tail,
+  // packed by the launch of the passes' reduces
   PackLoraArgs pl{};
   pl.out = p.BLt_dx;
   pl.vcols = H;
@@ -1756,7 +1757,15 @@ lora_status lora_qkv_bwd(const lora_qkv_desc* d, const void* dQ, const void* dK,
   for (int i = 0; i < 3; ++i) pl.part[i] = part(projs[i]->A, r, 0, H, (int)(i * r), (int)r, false);
   PackBatch pb;
   pb.add(pl);
-  LAUNCHN("pack", st, launch_pack_batch(c.bf16, pb.b, st));
+  LAUNCHN("rowcol", st, launch_rowcol_batch(c.bf16, cb, rb, 3, st, &pb.b));
+  // [dA_q | dA_k | dA_v] = X^T [s P] in one pass over X
+  ColProjArgs cx = colproj_args(c, X, H, T, H, p.Ps, RL, (int)(3 * r), (int)r, false, p.partial);
+  cx.scales[0] = cx.scales[1] = cx.scales[2] = 1.0f;
+  cx.dest[0] = gr->dA_q;
+  cx.dest[1] = gr->dA_k;
+  cx.dest[2] = gr->dA_v;
+  LAUNCHN("colproj", st, launch_colproj(c.bf16, cx, st));
+  // dX = sum_p dZ_p W_p^T + [s P] [A_q | A_k | A_v]^T
   GemmArgs g{};
   g.M = T;
   g.nseg = 3;
@@ -1872,14 +1881,16 @@ lora_status lora_o_bwd(const lora_o_desc* d, const void* dY, const void* X, cons
   ColProjArgs cb = colproj_args(c, dY, N, T, N, U, r, (int)r, (int)r, true, p.partial);
   cb.scales[0] = o->scale;
   cb.dest[0] = dB;
-  LAUNCHN("rowcol", st, launch_rowcol(c.bf16, cb, ra, p.rpartial, st));
+  // the launch of the pass's reduce also packs the input-gradient GEMM's adapter operand
+  const PackBatch pb = input_grad_pack(c, K, r, o, p);
+  LAUNCHN("rowcol", st, launch_rowcol(c.bf16, cb, ra, p.rpartial, st, r > 0 ? &pb.b : nullptr));
   // dA = X^T (s P)
   ColProjArgs ca = colproj_args(c, X, K, T, K, p.Ps, RL, (int)r, (int)r, false, p.partial);
   ca.scales[0] = 1.0f;
   ca.dest[0] = dA;
   LAUNCHN("colproj", st, launch_colproj(c.bf16, ca, st));
   if (T == 0) return LORA_OK;
-  return proj_input_grad(c, T, K, N, r, dY, o, dX, p, st);
+  return proj_input_grad(c, T, K, N, r, dY, o, dX, p, st, true);
 }
 
 // ---------------------------------------------------------------------------

@@ -180,7 +180,12 @@ hipError_t launch_colproj_reduce(const ColProjArgs& a, hipStream_t st);
 // the colproj blocks also form r's product over their 256 columns; a
 // fixed-order reduce then writes r's outputs.  Other cases run the two
 // kernels one after the other.  rpartial: rowcol_partial_floats(T, K) floats.
-hipError_t launch_rowcol(bool bf16, const ColProjArgs& c, const RowProjArgs& r, float* rpartial, hipStream_t st);
+// With pk (bf16 packing jobs of the same call that only later kernels read),
+// the reduce launch also runs them; without the fused pass they are
+// launched first on their own.
+struct PackBatchArgs;
+hipError_t launch_rowcol(bool bf16, const ColProjArgs& c, const RowProjArgs& r, float* rpartial, hipStream_t st,
+                         const PackBatchArgs* pk = nullptr);
 // Only the reduce of a fused rowproj: r's outputs from nb column-block partials [nb, T, 16].
 hipError_t launch_rowproj_reduce(const RowProjArgs& r, const float* rpartial, int nb, hipStream_t st);
 int64_t rowcol_partial_floats(int64_t T, int64_t K);
@@ -201,7 +206,8 @@ struct RowColBatch {
   int32_t n;
   int32_t nx;  // reduce launch only: c[n .. n + nx - 1] are colproj reduces without a rowproj
 };
-hipError_t launch_rowcol_batch(bool bf16, const ColProjArgs* c, const RowProjArgs* r, int n, hipStream_t st);
+hipError_t launch_rowcol_batch(bool bf16, const ColProjArgs* c, const RowProjArgs* r, int n, hipStream_t st,
+                               const PackBatchArgs* pk = nullptr);
 // Only the reduces of a rowcol batch whose partials another kernel wrote
 // (bf16, r[s].R <= 16): segment s's colproj outputs from c[s].nchunk slices
 // c[s].partial [nchunk, K_s, 16] and its rowproj outputs from ceil(K_s / 256)

@@ -456,12 +456,11 @@ __global__ void colproj_f32_kernel(const ColProjArgs a) {
 // each output in storage order, so the stores are coalesced; the sources
 // (adapters, at most a few MB) are read from L2.
 template <typename E>
-__global__ void pack_batch_kernel(const PackBatchArgs b) {
-  const PackLoraArgs& a = b.job[blockIdx.y];
+__device__ __forceinline__ void pack_job(const PackLoraArgs& a, uint32_t first, uint32_t stride) {
   // 32-bit index arithmetic (a 64-bit division per element dominated the
-  // kernel); launch_pack_batch checks that every job has fewer than 2^31 elements
+  // kernel); the launchers check that every job has fewer than 2^31 elements
   const uint32_t vc = (uint32_t)a.vcols, rl = (uint32_t)a.RL, n = vc * rl;
-  for (uint32_t o = blockIdx.x * blockDim.x + threadIdx.x; o < n; o += gridDim.x * blockDim.x) {
+  for (uint32_t o = first; o < n; o += stride) {
     uint32_t v = a.kmajor ? o % vc : o / rl;
     const uint32_t kk = a.kmajor ? o / vc : o % rl;
     if (a.perm8) v = (v & ~7u) | ((v & 3u) << 1) | ((v >> 2) & 1u);
@@ -476,6 +475,10 @@ __global__ void pack_batch_kernel(const PackBatchArgs b) {
     }
     static_cast<E*>(a.out)[o] = val;
   }
+}
+template <typename E>
+__global__ void pack_batch_kernel(const PackBatchArgs b) {
+  pack_job<E>(b.job[blockIdx.y], blockIdx.x * blockDim.x + threadIdx.x, gridDim.x * blockDim.x);
 }
 
 __global__ void cast_bf16_kernel(const CastArgs a) {
@@ -627,8 +630,7 @@ __global__ __launch_bounds__(256) void rowproj_reduce_kernel(const RowProjArgs a
 }
 // Both reduces of a rowcol batch: blockIdx.y < n the colproj reduce (dB) of
 // segment y, else the rowproj reduce (P) of segment y - n.
-__global__ __launch_bounds__(256) void rowcol_batch_reduce_kernel(const RowColBatch b) {
-  const int y = blockIdx.y;
+__device__ __forceinline__ void rowcol_reduce_part(const RowColBatch& b, int y) {
   if (y < b.n) {
     colproj_reduce_body(b.c[y], 16, blockIdx.x);
   } else if (y < 2 * b.n) {
@@ -638,14 +640,39 @@ __global__ __launch_bounds__(256) void rowcol_batch_reduce_kernel(const RowColBa
     colproj_reduce_body(b.c[y - b.n], 16, blockIdx.x);  // the extra colproj reduces
   }
 }
+__global__ __launch_bounds__(256) void rowcol_batch_reduce_kernel(const RowColBatch b) {
+  rowcol_reduce_part(b, blockIdx.y);
+}
+// The same reduces, and past them (blockIdx.y) the bf16 adapter-packing jobs of
+// the same call, which a later kernel reads: one launch instead of two.
+__global__ __launch_bounds__(256) void rowcol_batch_reduce_pack_kernel(const RowColBatch b, const PackBatchArgs pk) {
+  const int nr = 2 * b.n + b.nx;
+  if ((int)blockIdx.y < nr) rowcol_reduce_part(b, blockIdx.y);
+  else pack_job<uint16_t>(pk.job[blockIdx.y - nr], blockIdx.x * blockDim.x + threadIdx.x, gridDim.x * blockDim.x);
+}
+static_assert(sizeof(RowColBatch) + sizeof(PackBatchArgs) <= 4096, "kernel arguments exceed 4 KB");
 }  // namespace
 
 int64_t rowcol_partial_floats(int64_t T, int64_t K) { return ((K + 255) / 256) * T * 16; }
 
-hipError_t launch_rowcol(bool bf16, const ColProjArgs& c0, const RowProjArgs& r, float* rpartial, hipStream_t st) {
+// Blocks per job of a pack launch (0: nothing to pack; -1: a job too large).
+static int64_t pack_grid_x(const PackBatchArgs& b) {
+  int64_t nmax = 0;
+  for (int i = 0; i < b.njobs; ++i) nmax = b.job[i].vcols * b.job[i].RL > nmax ? b.job[i].vcols * b.job[i].RL : nmax;
+  if (b.njobs <= 0 || nmax == 0) return 0;
+  if (nmax >= ((int64_t)1 << 31)) return -1;
+  return nblk(nmax, 256) < 2048 ? nblk(nmax, 256) : 2048;
+}
+
+hipError_t launch_rowcol(bool bf16, const ColProjArgs& c0, const RowProjArgs& r, float* rpartial, hipStream_t st,
+                         const PackBatchArgs* pk) {
   const bool fused = bf16 && rpartial != nullptr && r.R <= 16 && r.Z == c0.Z && r.ldz == c0.ldz && r.T == c0.T &&
                      r.K == c0.K && r.K % 8 == 0 && c0.R <= 16 && c0.T > 0;
   if (!fused) {
+    if (pk != nullptr) {
+      const hipError_t e = launch_pack_batch(bf16, *pk, st);
+      if (e != hipSuccess) return e;
+    }
     hipError_t e = launch_rowproj(bf16, r, st);
     if (e != hipSuccess) return e;
     // the plain colproj: a set rpartial would select the fused (R <= 16) kernel
@@ -657,16 +684,21 @@ hipError_t launch_rowcol(bool bf16, const ColProjArgs& c0, const RowProjArgs& r,
   // is that of launch_colproj, so the sums are the same)
   ColProjArgs c = c0;
   c.rpartial = rpartial;
-  return launch_rowcol_batch(true, &c, &r, 1, st);
+  return launch_rowcol_batch(true, &c, &r, 1, st, pk);
 }
 
-hipError_t launch_rowcol_batch(bool bf16, const ColProjArgs* c, const RowProjArgs* r, int n, hipStream_t st) {
+hipError_t launch_rowcol_batch(bool bf16, const ColProjArgs* c, const RowProjArgs* r, int n, hipStream_t st,
+                               const PackBatchArgs* pk) {
   if (n < 1 || n > 3) return hipErrorInvalidValue;
   bool fused = bf16 && c[0].T > 0;
   for (int i = 0; i < n && fused; ++i)
     fused = c[i].rpartial != nullptr && r[i].R <= 16 && r[i].Z == c[i].Z && r[i].ldz == c[i].ldz &&
             r[i].T == c[i].T && r[i].K == c[i].K && r[i].K % 8 == 0 && c[i].R <= 16 && c[i].T == c[0].T;
   if (!fused) {
+    if (pk != nullptr) {
+      const hipError_t e = launch_pack_batch(bf16, *pk, st);
+      if (e != hipSuccess) return e;
+    }
     for (int i = 0; i < n; ++i) {
       const hipError_t e = launch_rowcol(bf16, c[i], r[i], c[i].rpartial, st);
       if (e != hipSuccess) return e;
@@ -693,11 +725,19 @@ hipError_t launch_rowcol_batch(bool bf16, const ColProjArgs* c, const RowProjArg
     b.c[i].nchunk = nchunk;
     b.r[i] = r[i];
   }
+  const int64_t px = pk != nullptr ? pack_grid_x(*pk) : 0;
+  if (px < 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(rowcol_batch_kernel, dim3((unsigned)b.kb0[n], (unsigned)nchunk), dim3(256), 0, st, b,
                      rows_per_chunk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(rowcol_batch_reduce_kernel, dim3(rx, (unsigned)(2 * n)), dim3(256), 0, st, b);
+  if (px > 0) {
+    const unsigned gx = (unsigned)px > rx ? (unsigned)px : rx;
+    hipLaunchKernelGGL(rowcol_batch_reduce_pack_kernel, dim3(gx, (unsigned)(2 * n + pk->njobs)), dim3(256), 0, st, b,
+                       *pk);
+  } else {
+    hipLaunchKernelGGL(rowcol_batch_reduce_kernel, dim3(rx, (unsigned)(2 * n)), dim3(256), 0, st, b);
+  }
   return hipGetLastError();
 }
 
@@ -735,11 +775,10 @@ hipError_t launch_rowproj_reduce(const RowProjArgs& r, const float* rpartial, in
 }
 
 hipError_t launch_pack_batch(bool bf16, const PackBatchArgs& b, hipStream_t st) {
-  int64_t nmax = 0;
-  for (int i = 0; i < b.njobs; ++i) nmax = b.job[i].vcols * b.job[i].RL > nmax ? b.job[i].vcols * b.job[i].RL : nmax;
-  if (b.njobs <= 0 || nmax == 0) return hipSuccess;
-  if (nmax >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  const unsigned bx = nblk(nmax, 256) < 2048 ? nblk(nmax, 256) : 2048u;
+  const int64_t px = pack_grid_x(b);
+  if (px == 0) return hipSuccess;
+  if (px < 0) return hipErrorInvalidValue;
+  const unsigned bx = (unsigned)px;
   if (bf16) hipLaunchKernelGGL(pack_batch_kernel<uint16_t>, dim3(bx, (unsigned)b.njobs), dim3(256), 0, st, b);
   else hipLaunchKernelGGL(pack_batch_kernel<float>, dim3(bx, (unsigned)b.njobs), dim3(256), 0, st, b);
   return hipGetLastError();
