@@ -607,12 +607,17 @@ def main():
         with_wt(step)
     torch.cuda.synchronize()
 
-    # warm-up; the first warm-up step also finds the dominant GEMM family
+    # W warm-up steps; the second one (the first is cold: code loading and
+    # first-touch costs can outweigh a whole small GEMM), or the only one,
+    # finds the dominant GEMM family
+    if args.warmup >= 2:
+        step()
+        torch.cuda.synchronize()
     lm.trace_begin("")
     step()
     torch.cuda.synchronize()
     fams = lm.trace_end()
-    for _ in range(max(args.warmup - 1, 0)):
+    for _ in range(max(args.warmup - 2, 0)):
         step()
     torch.cuda.synchronize()
     gemms = {k: v for k, v in fams.items() if k.startswith("gemm")}
