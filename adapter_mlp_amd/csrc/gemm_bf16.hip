@@ -916,7 +916,14 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
       cur_begin();
     }
   };
-  auto issue_a = [&](int slot) {  // group 0: activation tile of the next step
+  // The tile of one K step is 8 loads of 1 KB per wavefront; issue_a and
+  // issue_w issue loads i0 .. i1 - 1 of them (constants once the callers'
+  // loops are unrolled), and the caller advances the cursor once all 8 are
+  // out.  In the K loop the read phase issues them two at a time after each
+  // K slice's fragment reads (read's `between`), which keeps the LDS read
+  // and the vector-memory queues busy together; at the Llama-3-8B MLP shape
+  // this measured 1.2% less step time than all 8 after the reads.
+  auto issue_a = [&](int slot, int i0, int i1) {  // group 0: activation tile of the next step
     const uint32_t dst = lds_addr(lds) + slot * SLOT_BYTES + wn * 8 * 1024;
     // opaque copies: keep the per-lane terms from being expanded per block
     // and hoisted out of the K loop (8 live offsets would not fit)
@@ -925,10 +932,10 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
     const i32x4 ra = rsrc_words(lp, ln);
     const uint32_t base = (uint32_t)r * lld2;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dma16(ra, base + (uint32_t)((x ^ i) << 4), dst + i * 1024, (uint32_t)(8 * i) * lld2);
-    advance();
+    for (int i = 0; i < 8; ++i)
+      if (i >= i0 && i < i1) dma16(ra, base + (uint32_t)((x ^ i) << 4), dst + i * 1024, (uint32_t)(8 * i) * lld2);
   };
-  auto issue_w = [&](int slot) {  // group 1: (dense) weight tile of the next step
+  auto issue_w = [&](int slot, int i0, int i1) {  // group 1: (dense) weight tile of the next step
     const uint32_t wslot = lds_addr(lds) + W_RING + slot * SLOT_BYTES;
     const i32x4 rb = rsrc_words(lp, ln);
     if constexpr (BKIND == B_NT) {
@@ -939,14 +946,16 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
       const uint32_t base = (uint32_t)r * lld2;
       const uint32_t dst = wslot + wn * 8 * 1024;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dma16(rb, base + (uint32_t)((x ^ i) << 4), dst + i * 1024, (uint32_t)(8 * i) * lld2);
+      for (int i = 0; i < 8; ++i)
+        if (i >= i0 && i < i1) dma16(rb, base + (uint32_t)((x ^ i) << 4), dst + i * 1024, (uint32_t)(8 * i) * lld2);
     } else if constexpr (!NF4) {
       int nr = nn_row, nc = nn_chunk;
       asm volatile("" : "+v"(nr), "+v"(nc));
       const uint32_t base = (uint32_t)nr * lld2 + (uint32_t)(nc << 4);
       const uint32_t dst = wslot + (wn >> 1) * HALF_BYTES + (wn & 1) * 8 * 1024;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dma16(rb, base, dst + i * 1024, (uint32_t)(4 * i) * lld2);
+      for (int i = 0; i < 8; ++i)
+        if (i >= i0 && i < i1) dma16(rb, base, dst + i * 1024, (uint32_t)(4 * i) * lld2);
     } else {
       // the dense adapter tile of an NF4 GEMM, in the NF4 swizzle: load i
       // covers rows nn_row + 4 i, whose swizzle alternates with i & 1
@@ -956,8 +965,17 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
       const uint32_t b1 = (uint32_t)nr * lld2 + (uint32_t)((nc ^ nn_swz<true>(nr + 4)) << 4);
       const uint32_t dst = wslot + (wn >> 1) * HALF_BYTES + (wn & 1) * 8 * 1024;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dma16(rb, (i & 1) ? b1 : b0, dst + i * 1024, (uint32_t)(4 * i) * lld2);
+      for (int i = 0; i < 8; ++i)
+        if (i >= i0 && i < i1) dma16(rb, (i & 1) ? b1 : b0, dst + i * 1024, (uint32_t)(4 * i) * lld2);
     }
+  };
+  // a whole tile, then the cursor
+  auto load_a = [&](int slot) {
+    issue_a(slot, 0, 8);
+    advance();
+  };
+  auto load_w = [&](int slot) {
+    issue_w(slot, 0, 8);
     advance();
   };
 
@@ -1111,7 +1129,8 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   if constexpr (BKIND == B_NT) kc_offsets(DUAL ? wn * 32 + (lane & 31) : wn * 64 + (lane & 31), bo);
 
   bf16x8 fa[4][2], fb[4][4];
-  auto read = [&](int aslot, int wslot) {
+  // between(ks) runs after the fragment reads of K slice ks
+  auto read = [&](int aslot, int wslot, auto&& between) {
     const lds_char* const at = lds + aslot * SLOT_BYTES;
     const lds_char* const wt = lds + W_RING + wslot * SLOT_BYTES;
 #pragma unroll
@@ -1133,8 +1152,10 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
         const int y = ((2 * ks) ^ (4 * (j & 1))) >> 1;
         fb[ks][j] = __builtin_bit_cast(bf16x8, lds_read16(at + ao[y] + j * 32 * 128));
       }
+      between(ks);
     }
   };
+  const auto nothing = [](int) {};
 
   f32x16 acc[2][4];
 #pragma unroll
@@ -1213,29 +1234,33 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   };
   if constexpr (!NF4) {
     if (wm == 0) {
-      issue_a(0);
+      load_a(0);
       if (KT > 1) {
-        issue_a(1);
+        load_a(1);
         __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): A 0 is in
       } else {
         __builtin_amdgcn_s_waitcnt(0x0F70);
       }
       phase_end();
-      read(0, 0);
+      read(0, 0, nothing);
       phase_end();
       for (int t = 0; t < KT; ++t) {
         mma();
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): A t+1 is in
         phase_end();
-        // fragment reads first: they are the phase's critical path
-        if (t + 1 < KT) read((t + 1) & 1, (t + 1) % 3);
-        if (t + 2 < KT) issue_a(t & 1);
+        // fragment reads lead: they are the phase's critical path
+        if (t + 2 < KT) {
+          read((t + 1) & 1, (t + 1) % 3, [&](int ks) { issue_a(t & 1, 2 * ks, 2 * ks + 2); });
+          advance();
+        } else if (t + 1 < KT) {
+          read((t + 1) & 1, (t + 1) % 3, nothing);
+        }
         phase_end();
       }
     } else {
-      issue_w(0);
+      load_w(0);
       if (KT > 1) {
-        issue_w(1);
+        load_w(1);
         __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): W 0 is in
       } else {
         __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -1246,11 +1271,11 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
       for (int t = 0; t < KT; ++t) {
         const int ws2 = ws == 0 ? 2 : ws - 1;  // (t + 2) % 3
         if (t + 2 < KT) {
-          read(t & 1, ws);
-          issue_w(ws2);
+          read(t & 1, ws, [&](int ks) { issue_w(ws2, 2 * ks, 2 * ks + 2); });
+          advance();
           __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): W t+1 is in (W t+2 may still fly)
         } else {
-          read(t & 1, ws);
+          read(t & 1, ws, nothing);
           __builtin_amdgcn_s_waitcnt(0x0F70);
         }
         phase_end();
@@ -1275,8 +1300,8 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
     // its own wavefront waited for (g1) or that a barrier has published (g0).
     const bool lora_step = KT > KN;  // the last step is the dense adapter tile
     if (wm == 0) {
-      issue_a(0);
-      if (KT > 1) issue_a(1);
+      load_a(0);
+      if (KT > 1) load_a(1);
       phase_end();
       {
         const UnpackIn u = unpack_fetch(0, 0, true);
@@ -1285,7 +1310,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
       if (KT > 1) wait_vmcnt<8>();
       else wait_vmcnt<0>();
       phase_end();
-      read(0, 0);
+      read(0, 0, nothing);
       UnpackIn nx = unpack_fetch(1, 0, 1 < KN);  // W 1 (lower): code slot 1
       phase_end();
       int cs2 = 2;  // code slot of step t + 2
@@ -1294,8 +1319,8 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
         wait_vmcnt<0>();  // A t+1 is in
         phase_end();
         __builtin_amdgcn_s_setprio(1);
-        if (t + 1 < KT) read((t + 1) & 1, (t + 1) & 1);
-        if (t + 2 < KT) issue_a(t & 1);
+        if (t + 1 < KT) read((t + 1) & 1, (t + 1) & 1, nothing);
+        if (t + 2 < KT) load_a(t & 1);
         nx = unpack_fetch(cs2, 0, t + 2 < KN);
         __builtin_amdgcn_s_setprio(0);
         phase_end();
@@ -1325,7 +1350,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
         const UnpackIn u = unpack_fetch(1, 1, true);
         unpack_store(u, 1, 1, true);
       } else if (lora_step) {
-        issue_w(1);
+        load_w(1);
       }
       phase_end();
       int cs0 = 0;  // code slot of step t (= that of step t + 3)
@@ -1333,18 +1358,18 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
         const int cs2 = cs0 == 0 ? 2 : cs0 - 1;  // (t + 2) % 3
         __builtin_amdgcn_s_setprio(1);
         if (t + 3 < KN) {
-          read(t & 1, t & 1);
+          read(t & 1, t & 1, nothing);
           issue_codes(cs0);
           wait_vmcnt<4>();  // codes t+2 are in (codes t+3 may still fly)
         } else {
-          read(t & 1, t & 1);
+          read(t & 1, t & 1, nothing);
           wait_vmcnt<0>();
         }
         const UnpackIn nx = unpack_fetch(cs2, 1, t + 2 < KN);
         __builtin_amdgcn_s_setprio(0);
         phase_end();
         mma_unpack(nx, t & 1, 1, t + 2 < KN);
-        if (lora_step && t + 2 == KN) issue_w(t & 1);
+        if (lora_step && t + 2 == KN) load_w(t & 1);
         phase_end();
         cs0 = cs0 == 2 ? 0 : cs0 + 1;
       }
