@@ -44,6 +44,22 @@
 #include "lds_dma.hpp"
 
 namespace lora {
+
+// Per-block timing (a separate build, -DLORA_BLOCK_TIMING, read by
+// lora_block_times): wavefront 0 of every block records the 100 MHz real-time
+// clock at kernel entry, at the start and the end of its K loop and after the
+// epilogue, the shader clock (s_memtime) at entry and exit, its hardware ids
+// and the launch shape, in the slot of its kernel family ((NF4 ? 4 : 0) +
+// activation forward 0, activation backward 1, NT store 2, NN store 3).  A
+// family's slots hold its latest launch.  The normal build compiles none of it.
+#ifdef LORA_BLOCK_TIMING
+constexpr bool kBlockTiming = true;
+constexpr int kTimedBlocks = 8192;
+__device__ unsigned long long block_times[8][kTimedBlocks][8];
+#else
+constexpr bool kBlockTiming = false;
+#endif
+
 namespace {
 
 constexpr int BM = 256, BK = 64;
@@ -784,6 +800,13 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   static_assert(!(DUAL && BKIND == B_NT && NF4), "NF4 gate/up tiles read forward (NN) weights");
   __shared__ __attribute__((aligned(1024))) char smem_raw[LDS_BYTES];
   lds_char* const lds = (lds_char*)smem_raw;
+  // timing build only: real-time stamps (entry, K loop start, K loop end) and
+  // the shader clock at entry
+  unsigned long long tstamp[3] = {0, 0, 0}, tclock0 = 0;
+  if constexpr (kBlockTiming) {
+    tstamp[0] = __builtin_amdgcn_s_memrealtime();
+    tclock0 = __builtin_amdgcn_s_memtime();
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1244,6 +1267,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
       phase_end();
       read(0, 0, nothing);
       phase_end();
+      if constexpr (kBlockTiming) tstamp[1] = __builtin_amdgcn_s_memrealtime();
       for (int t = 0; t < KT; ++t) {
         mma();
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): A t+1 is in
@@ -1257,6 +1281,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
         }
         phase_end();
       }
+      if constexpr (kBlockTiming) tstamp[2] = __builtin_amdgcn_s_memrealtime();
     } else {
       load_w(0);
       if (KT > 1) {
@@ -1313,6 +1338,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
       read(0, 0, nothing);
       UnpackIn nx = unpack_fetch(1, 0, 1 < KN);  // W 1 (lower): code slot 1
       phase_end();
+      if constexpr (kBlockTiming) tstamp[1] = __builtin_amdgcn_s_memrealtime();
       int cs2 = 2;  // code slot of step t + 2
       for (int t = 0; t < KT; ++t) {
         mma_unpack(nx, (t + 1) & 1, 0, t + 1 < KN);
@@ -1326,6 +1352,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
         phase_end();
         cs2 = cs2 == 2 ? 0 : cs2 + 1;
       }
+      if constexpr (kBlockTiming) tstamp[2] = __builtin_amdgcn_s_memrealtime();
       if constexpr (BKIND == B_NN) restore_cols();
     } else {
       issue_codes(0);
@@ -1384,6 +1411,28 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   const int64_t mw = m0 + wm * 128;
   const int64_t nbase = DUAL ? tnl * 128 + wn * 32 : tnl * 256 + wn * 64;
   run_epilogue_w<64, DUAL, EPI, ACT>(acc, wstage, args, reg, mw, nbase, NR, M, lane, wm, wn, kp);
+#ifdef LORA_BLOCK_TIMING
+  {
+    const unsigned long long t3 = __builtin_amdgcn_s_memrealtime(), c3 = __builtin_amdgcn_s_memtime();
+    unsigned int hw, xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    constexpr int fam = (NF4 ? 4 : 0) + ((EPI == EPI_ACT_FWD || EPI == EPI_ACT1_FWD) ? 0
+                                         : (EPI == EPI_ACT_BWD || EPI == EPI_ACT1_BWD) ? 1
+                                         : BKIND == B_NT ? 2 : 3);
+    if (wave == 0 && lane == 0 && blockIdx.x < (unsigned)kTimedBlocks) {
+      unsigned long long* d = block_times[fam][blockIdx.x];
+      d[0] = tstamp[0];
+      d[1] = tstamp[1];
+      d[2] = tstamp[2];
+      d[3] = t3;
+      d[4] = tclock0;
+      d[5] = c3;
+      d[6] = (unsigned long long)hw | ((unsigned long long)xcc << 32);
+      d[7] = (unsigned long long)gridDim.x | ((unsigned long long)(unsigned)KT << 32);
+    }
+  }
+#endif
 }
 
 // Sum of the K parts of the split tiles t0 .. ntiles-1 (tile order as in the
@@ -1461,3 +1510,17 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
 }
 
 }  // namespace lora
+
+#ifdef LORA_BLOCK_TIMING
+// Timing build only: copies the per-block records ([8 families][8192 blocks][8]
+// unsigned 64-bit words, see block_times) to host memory `out` of `bytes`
+// bytes (at least their size).  Synchronises the device first.  Returns a HIP
+// error code (0 on success).
+extern "C" int lora_block_times(void* out, size_t bytes) {
+  if (out == nullptr || bytes < sizeof(lora::block_times)) return (int)hipErrorInvalidValue;
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return (int)e;
+  return (int)hipMemcpyFromSymbol(out, HIP_SYMBOL(lora::block_times), sizeof(lora::block_times), 0,
+                                  hipMemcpyDeviceToHost);
+}
+#endif

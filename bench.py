@@ -296,6 +296,124 @@ def trace_summary(stats_csv, bench_log, config_id):
     print(f"wrote {path}")
 
 
+TIMING_LIB = os.path.join(ROOT, "adapter_mlp_amd", "liblora_mi355x_timing.so")
+TIMED_BLOCKS = 8192  # block_times' second dimension in the timing build
+
+
+def timing_family_names(cfg):
+    """Family names of the timing build's 8 record slots for this workload."""
+    act = "relu2" if cfg.kind == "relu2" else "act"
+    base = [f"gemm_nn_{act}_fwd", f"gemm_nt_{act}_bwd", "gemm_nt_store", "gemm_nn_store"]
+    return base + [n + "_nf4" for n in base]
+
+
+def block_timing_report(rec, name, tile_mfma_cycles=2048):
+    """Per-launch summary of one family's block records (the latest launch).
+
+    rec: [blocks, 8] uint64 rows (real-time stamps at entry, K-loop start,
+    K-loop end and epilogue end in 10 ns units; shader clock at entry and
+    exit; hardware ids; grid size | K steps << 32).  The K loop's MFMA issue
+    fraction is the ideal cycles of one 256 x 256 x 64 step per SIMD (two
+    wavefronts x 32 MFMAs x 32 cycles) over the measured cycles per step."""
+    import numpy as np
+
+    rec = rec.astype(np.int64)
+    written = rec[:, 0] != 0
+    if not written.any():
+        return None
+    # every block of the latest launch (the one that started last) rewrote its slot
+    last = rec[written][np.argmax(rec[written, 0])]
+    grid = min(int(last[7] & 0xFFFFFFFF), len(rec))
+    rec = rec[:grid]
+    kt = (rec[:, 7] >> 32).astype(np.int64)
+    pro = (rec[:, 1] - rec[:, 0]) / 100.0
+    loop = (rec[:, 2] - rec[:, 1]) / 100.0
+    epi = (rec[:, 3] - rec[:, 2]) / 100.0
+    life = (rec[:, 3] - rec[:, 0]) / 100.0
+    ghz = (rec[:, 5] - rec[:, 4]) / np.maximum(life, 1e-3) / 1e3
+    cyc_step = loop * ghz * 1e3 / np.maximum(kt, 1)
+    hw = rec[:, 6] & 0xFFFFFFFF
+    xcc = rec[:, 6] >> 32
+    cu = xcc * 4096 + (hw >> 8)  # XCC, then cu/sh/se bits of HW_ID
+    gaps = []
+    per_cu = {}
+    for k in np.unique(cu):
+        idx = np.where(cu == k)[0]
+        idx = idx[np.argsort(rec[idx, 0])]
+        per_cu[int(k)] = len(idx)
+        gaps += [(rec[b, 0] - rec[a, 3]) / 100.0 for a, b in zip(idx[:-1], idx[1:])]
+    span = (rec[:, 3].max() - rec[:, 0].min()) / 100.0
+    tiles = float(np.median(list(per_cu.values())))
+    gap = float(np.mean(gaps)) if gaps else 0.0
+    return {
+        "family": name, "blocks": int(len(rec)), "grid": grid, "k_steps": int(np.median(kt)),
+        "span_us": float(span), "cus": len(per_cu), "tiles_per_cu": tiles,
+        "prologue_us": float(pro.mean()), "k_loop_us": float(loop.mean()), "epilogue_us": float(epi.mean()),
+        "gap_between_blocks_us": gap, "clock_GHz": float(ghz.mean()),
+        "cycles_per_k_step": float(cyc_step.mean()),
+        "k_loop_mfma_issue_frac": float(tile_mfma_cycles / cyc_step.mean()),
+        "k_loop_share_of_cu_time": float(loop.sum() / (pro.sum() + loop.sum() + epi.sum() + max(sum(gaps), 0.0))),
+    }
+
+
+def block_timing(args):
+    """Run the workload on the per-block timing build and summarise where each
+    GEMM family's time goes: prologue (entry to the first MFMA phase), K loop,
+    epilogue, the gap before the next block on the same CU, and the K loop's
+    cycles per step at the clock the blocks measured.  Writes
+    profiles/<family>_<workload>_block_timing.txt."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import adapter_mlp_amd as lm
+    from workload import CONFIGS, make_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if not os.path.exists(TIMING_LIB):
+        raise SystemExit(f"{TIMING_LIB} is missing: build it with `python -m adapter_mlp_amd.build --timing`")
+    lib = lm.load(TIMING_LIB)
+    cfg = CONFIGS[args.config]
+    inp = make_inputs(cfg)
+    step = {"mlp": MlpStep, "relu2": Relu2Step, "attn": AttnStep}[cfg.kind](cfg, inp, lm, torch)
+    for _ in range(max(args.warmup, 1) + max(args.steps, 1)):
+        step()
+    torch.cuda.synchronize()
+    buf = np.zeros((8, TIMED_BLOCKS, 8), dtype=np.uint64)
+    fetch = lib.lora_block_times
+    fetch.restype = ctypes.c_int
+    fetch.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    rc = fetch(buf.ctypes.data, buf.nbytes)
+    if rc != 0:
+        raise SystemExit(f"lora_block_times returned HIP error {rc}")
+    names = timing_family_names(cfg)
+    cmd = (f"python3 bench.py --config {cfg.cid} --block-timing --steps {args.steps} --warmup {args.warmup}")
+    for f in range(8):
+        r = block_timing_report(buf[f], names[f])
+        if r is None:
+            continue
+        lines = [f"# per-block timing of {names[f]}, workload {cfg.note}, latest launch after "
+                 f"{max(args.warmup, 1) + max(args.steps, 1)} steps",
+                 "# timing build of the library (-DLORA_BLOCK_TIMING): wavefront 0 of each block records the",
+                 "# 100 MHz real-time clock at entry, at the start and the end of its K loop and after the",
+                 "# epilogue, and the shader clock (s_memtime) at entry and exit",
+                 f"#   python -m adapter_mlp_amd.build --timing && {cmd}",
+                 "# k_loop_mfma_issue_frac = 2048 (two wavefronts x 32 MFMAs x 32 cycles per SIMD and K step)",
+                 "#   / measured shader cycles per K step",
+                 f"source_digest = {source_digest()}"]
+        lines += [f"{k} = {v:.4g}" if isinstance(v, float) else f"{k} = {v}" for k, v in r.items()]
+        text = "\n".join(lines) + "\n"
+        path = os.path.join(ROOT, "profiles", f"{names[f]}_{workload_tag(cfg)}_block_timing.txt")
+        with open(path, "w") as fh:
+            fh.write(text)
+        print(f"{names[f]:24s} span {r['span_us']:8.1f} us  tiles/CU {r['tiles_per_cu']:4.1f}  "
+              f"prologue {r['prologue_us']:6.2f}  K loop {r['k_loop_us']:8.2f}  epilogue {r['epilogue_us']:6.2f}  "
+              f"gap {r['gap_between_blocks_us']:5.2f} us  clock {r['clock_GHz']:.3f} GHz  "
+              f"{r['cycles_per_k_step']:.0f} cycles/step ({100 * r['k_loop_mfma_issue_frac']:.1f}% MFMA issue)",
+              flush=True)
+
+
 def workload_tag(cfg):
     return {1: "tiny_fp32_mlp", 2: "llama3_8b_mlp", 3: "gemma_geglu_mlp", 4: "llama3_8b_qlora_mlp", 5: "llama3_8b_qkvo",
             6: "nemotron_h_relu2_mlp"}[cfg.cid]
@@ -570,6 +688,9 @@ def main():
                          "profiles/*_counters.txt")
     ap.add_argument("--trace-summary", nargs=2, metavar=("STATS_CSV", "BENCH_LOG"),
                     help="no GPU run: turn a rocprofv3 --kernel-trace --stats run into profiles/*_kernel_trace.txt")
+    ap.add_argument("--block-timing", action="store_true",
+                    help="run on the per-block timing build (liblora_mi355x_timing.so) and write "
+                         "profiles/*_block_timing.txt: prologue, K loop, epilogue and clock per GEMM family")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run a plain fp32 elementwise copy (negation) of MIB MiB "
                          "three times, the known-size kernel that scales HBM byte counters")
@@ -582,6 +703,9 @@ def main():
         return
     if args.counter_summary:
         counter_summary(args.counter_summary, args.config)
+        return
+    if args.block_timing:
+        block_timing(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the fused LoRA path runs on a single MI355X here and "
