@@ -52,6 +52,10 @@ namespace lora {
 // and the launch shape, in the slot of its kernel family ((NF4 ? 4 : 0) +
 // activation forward 0, activation backward 1, NT store 2, NN store 3).  A
 // family's slots hold its latest launch.  The normal build compiles none of it.
+// The stamps are held in scalar registers until the exit: the dense kernels
+// compile without spills, the NF4 kernels spill 2 to 5 scalar and up to 6
+// vector registers, so their timing-build figures run slower than the normal
+// build (storing each stamp when taken, or holding 32-bit stamps, spilled more).
 #ifdef LORA_BLOCK_TIMING
 constexpr bool kBlockTiming = true;
 constexpr int kTimedBlocks = 8192;

@@ -402,6 +402,9 @@ def block_timing(args):
                  "# k_loop_mfma_issue_frac = 2048 (two wavefronts x 32 MFMAs x 32 cycles per SIMD and K step)",
                  "#   / measured shader cycles per K step",
                  f"source_digest = {source_digest()}"]
+        if names[f].endswith("_nf4"):
+            lines.insert(-1, "# NF4 kernels spill 2-5 scalar registers in the timing build (held stamps), so these figures "
+                             "run slower than the normal build's kernel trace")
         lines += [f"{k} = {v:.4g}" if isinstance(v, float) else f"{k} = {v}" for k, v in r.items()]
         text = "\n".join(lines) + "\n"
         path = os.path.join(ROOT, "profiles", f"{names[f]}_{workload_tag(cfg)}_block_timing.txt")
