@@ -9,9 +9,14 @@ and linked into adapter_mlp_amd/liblora_mi355x.so.  No GPU is needed to build.
 
 builds the same sources with -DLORA_BLOCK_TIMING into
 adapter_mlp_amd/liblora_mi355x_timing.so: the GEMM kernels then record per-block
-clock stamps, read by `bench.py --block-timing` through lora_block_times.  The
-normal library is unaffected (its GEMM code is the same instruction for
-instruction).
+clock stamps, read by `bench.py --block-timing` through lora_block_times.
+
+    python -m adapter_mlp_amd.build --phases
+
+builds them with -DLORA_PHASE_TIMING into adapter_mlp_amd/liblora_mi355x_phases.so,
+whose GEMM kernels read the shader clock at every phase boundary of one K step
+(`bench.py --phase-timing`, through lora_phase_times).  The normal library is
+unaffected by either (its GEMM code is the same instruction for instruction).
 """
 from __future__ import annotations
 
@@ -27,8 +32,13 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblora_mi355x.so")
-BUILD_TIMING = os.path.join(PKG, "_build_timing")
-LIB_TIMING = os.path.join(PKG, "liblora_mi355x_timing.so")
+# instrumented variants: name -> (macro, object folder, library)
+VARIANTS = {
+    "timing": ("LORA_BLOCK_TIMING", os.path.join(PKG, "_build_timing"), os.path.join(PKG, "liblora_mi355x_timing.so")),
+    "phases": ("LORA_PHASE_TIMING", os.path.join(PKG, "_build_phases"), os.path.join(PKG, "liblora_mi355x_phases.so")),
+}
+LIB_TIMING = VARIANTS["timing"][2]
+LIB_PHASES = VARIANTS["phases"][2]
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -43,9 +53,10 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src, timing=False):
-    obj = os.path.join(BUILD_TIMING if timing else BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC] + CFLAGS + (["-DLORA_BLOCK_TIMING"] if timing else []) + ["-c", src, "-o", obj]
+def _compile(src, variant=None):
+    folder = VARIANTS[variant][1] if variant else BUILD
+    obj = os.path.join(folder, os.path.basename(src)[:-4] + ".o")
+    cmd = [HIPCC] + CFLAGS + (["-D" + VARIANTS[variant][0]] if variant else []) + ["-c", src, "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [ln for ln in (p.stdout + p.stderr).splitlines() if "packed-fp32-ops" not in ln]
     if p.returncode != 0:
@@ -53,22 +64,27 @@ def _compile(src, timing=False):
     return obj, msgs
 
 
-def build(verbose: bool = False, timing: bool = False) -> str:
-    """Compile and link; returns the path of the shared library (the timing
-    variant with timing=True)."""
+def build(verbose: bool = False, timing: bool = False, variant: str = None) -> str:
+    """Compile and link; returns the path of the shared library (an
+    instrumented variant with variant="timing" or "phases"; timing=True is
+    variant="timing")."""
+    if timing:
+        variant = "timing"
+    if variant is not None and variant not in VARIANTS:
+        raise ValueError(f"unknown build variant {variant!r}")
     if not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
-    os.makedirs(BUILD_TIMING if timing else BUILD, exist_ok=True)
+    os.makedirs(VARIANTS[variant][1] if variant else BUILD, exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        results = list(ex.map(lambda f: _compile(f, timing), srcs))
+        results = list(ex.map(lambda f: _compile(f, variant), srcs))
     objs = []
     for obj, msgs in results:
         objs.append(obj)
         if verbose:
             for m in msgs:
                 print(m)
-    lib = LIB_TIMING if timing else LIB
+    lib = VARIANTS[variant][2] if variant else LIB
     tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     p = subprocess.run(cmd, capture_output=True, text=True)
@@ -79,4 +95,5 @@ def build(verbose: bool = False, timing: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv, timing="--timing" in sys.argv))
+    v = "timing" if "--timing" in sys.argv else "phases" if "--phases" in sys.argv else None
+    print(build(verbose="-v" in sys.argv, variant=v))

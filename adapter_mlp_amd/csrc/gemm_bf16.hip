@@ -63,6 +63,20 @@ __device__ unsigned long long block_times[8][kTimedBlocks][8];
 #else
 constexpr bool kBlockTiming = false;
 #endif
+// Per-phase timing (another build, -DLORA_PHASE_TIMING, read by
+// lora_phase_times): in blocks 0..63, lane 0 of wavefronts 0 and 4 (the first
+// of each group) reads the shader clock at every phase boundary of K step
+// kPhaseStep and at the start of the next step, and stores them with the K
+// step count after the loop, in the slot of the kernel family (as
+// block_times).  Group 0 records: MFMA cluster start, its end, after the wait
+// for its loads, read phase start (after the barrier), read phase end; group
+// 1: read phase start, its end, MFMA cluster start (after the barrier), its
+// end.  The stamps are held in scalar registers through the loop, which
+// changes the register allocation of this build.
+#ifdef LORA_PHASE_TIMING
+constexpr int kPhaseStep = 21;
+__device__ unsigned long long phase_times[8][64][2][8];
+#endif
 
 namespace {
 
@@ -1259,6 +1273,28 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
   };
+  // phase-timing build only: stamp k of K step t (see phase_times)
+#ifdef LORA_PHASE_TIMING
+  unsigned long long pst[5] = {0, 0, 0, 0, 0}, pnext = 0;
+#endif
+  auto pstamp = [&](int t, auto kc) {
+#ifdef LORA_PHASE_TIMING
+    constexpr int k = decltype(kc)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    const unsigned long long x = __builtin_amdgcn_s_memtime();
+    if (t == kPhaseStep) pst[k] = x;
+    if (k == 0 && t == kPhaseStep + 1) pnext = x;
+    __builtin_amdgcn_sched_barrier(0);
+#else
+    (void)t;
+    (void)kc;
+#endif
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
+  using P3 = std::integral_constant<int, 3>;
+  using P4 = std::integral_constant<int, 4>;
   if constexpr (!NF4) {
     if (wm == 0) {
       load_a(0);
@@ -1273,9 +1309,13 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
       phase_end();
       if constexpr (kBlockTiming) tstamp[1] = __builtin_amdgcn_s_memrealtime();
       for (int t = 0; t < KT; ++t) {
+        pstamp(t, P0{});
         mma();
+        pstamp(t, P1{});
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): A t+1 is in
+        pstamp(t, P2{});
         phase_end();
+        pstamp(t, P3{});
         // fragment reads lead: they are the phase's critical path
         if (t + 2 < KT) {
           read((t + 1) & 1, (t + 1) % 3, [&](int ks) { issue_a(t & 1, 2 * ks, 2 * ks + 2); });
@@ -1283,6 +1323,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
         } else if (t + 1 < KT) {
           read((t + 1) & 1, (t + 1) % 3, nothing);
         }
+        pstamp(t, P4{});
         phase_end();
       }
       if constexpr (kBlockTiming) tstamp[2] = __builtin_amdgcn_s_memrealtime();
@@ -1299,6 +1340,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
       int ws = 0;  // weight slot of step t
       for (int t = 0; t < KT; ++t) {
         const int ws2 = ws == 0 ? 2 : ws - 1;  // (t + 2) % 3
+        pstamp(t, P0{});
         if (t + 2 < KT) {
           read(t & 1, ws, [&](int ks) { issue_w(ws2, 2 * ks, 2 * ks + 2); });
           advance();
@@ -1307,8 +1349,11 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
           read(t & 1, ws, nothing);
           __builtin_amdgcn_s_waitcnt(0x0F70);
         }
+        pstamp(t, P1{});
         phase_end();
+        pstamp(t, P2{});
         mma();
+        pstamp(t, P3{});
         phase_end();
         ws = ws == 2 ? 0 : ws + 1;
       }
@@ -1345,14 +1390,19 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
       if constexpr (kBlockTiming) tstamp[1] = __builtin_amdgcn_s_memrealtime();
       int cs2 = 2;  // code slot of step t + 2
       for (int t = 0; t < KT; ++t) {
+        pstamp(t, P0{});
         mma_unpack(nx, (t + 1) & 1, 0, t + 1 < KN);
+        pstamp(t, P1{});
         wait_vmcnt<0>();  // A t+1 is in
+        pstamp(t, P2{});
         phase_end();
+        pstamp(t, P3{});
         __builtin_amdgcn_s_setprio(1);
         if (t + 1 < KT) read((t + 1) & 1, (t + 1) & 1, nothing);
         if (t + 2 < KT) load_a(t & 1);
         nx = unpack_fetch(cs2, 0, t + 2 < KN);
         __builtin_amdgcn_s_setprio(0);
+        pstamp(t, P4{});
         phase_end();
         cs2 = cs2 == 2 ? 0 : cs2 + 1;
       }
@@ -1387,6 +1437,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
       int cs0 = 0;  // code slot of step t (= that of step t + 3)
       for (int t = 0; t < KT; ++t) {
         const int cs2 = cs0 == 0 ? 2 : cs0 - 1;  // (t + 2) % 3
+        pstamp(t, P0{});
         __builtin_amdgcn_s_setprio(1);
         if (t + 3 < KN) {
           read(t & 1, t & 1, nothing);
@@ -1398,9 +1449,12 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
         }
         const UnpackIn nx = unpack_fetch(cs2, 1, t + 2 < KN);
         __builtin_amdgcn_s_setprio(0);
+        pstamp(t, P1{});
         phase_end();
+        pstamp(t, P2{});
         mma_unpack(nx, t & 1, 1, t + 2 < KN);
         if (lora_step && t + 2 == KN) load_w(t & 1);
+        pstamp(t, P3{});
         phase_end();
         cs0 = cs0 == 2 ? 0 : cs0 + 1;
       }
@@ -1408,6 +1462,22 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
     }
   }
 
+#ifdef LORA_PHASE_TIMING
+  if ((wave == 0 || wave == 4) && lane == 0 && blockIdx.x < 64u) {
+    constexpr int fam = (NF4 ? 4 : 0) + ((EPI == EPI_ACT_FWD || EPI == EPI_ACT1_FWD) ? 0
+                                         : (EPI == EPI_ACT_BWD || EPI == EPI_ACT1_BWD) ? 1
+                                         : BKIND == B_NT ? 2 : 3);
+    unsigned long long* d = phase_times[fam][blockIdx.x][wave >> 2];
+    d[0] = pst[0];
+    d[1] = pst[1];
+    d[2] = pst[2];
+    d[3] = pst[3];
+    d[4] = pst[4];
+    d[5] = pnext;
+    d[6] = (unsigned long long)(unsigned)KT;
+    d[7] = (unsigned long long)gridDim.x;
+  }
+#endif
   // epilogue staging: a private region per wavefront (operand slots are no longer read)
   constexpr int EB = epi_stage_bytes<64, EPI>();
   static_assert(8 * EB <= LDS_BYTES, "epilogue staging exceeds LDS");
@@ -1514,6 +1584,20 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
 }
 
 }  // namespace lora
+
+#ifdef LORA_PHASE_TIMING
+// Phase-timing build only: copies the phase records ([8 families][64 blocks]
+// [2 groups][8] unsigned 64-bit words, see phase_times) to host memory `out`
+// of `bytes` bytes (at least their size).  Synchronises the device first.
+// Returns a HIP error code (0 on success).
+extern "C" int lora_phase_times(void* out, size_t bytes) {
+  if (out == nullptr || bytes < sizeof(lora::phase_times)) return (int)hipErrorInvalidValue;
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return (int)e;
+  return (int)hipMemcpyFromSymbol(out, HIP_SYMBOL(lora::phase_times), sizeof(lora::phase_times), 0,
+                                  hipMemcpyDeviceToHost);
+}
+#endif
 
 #ifdef LORA_BLOCK_TIMING
 // Timing build only: copies the per-block records ([8 families][8192 blocks][8]

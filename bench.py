@@ -297,6 +297,7 @@ def trace_summary(stats_csv, bench_log, config_id):
 
 
 TIMING_LIB = os.path.join(ROOT, "adapter_mlp_amd", "liblora_mi355x_timing.so")
+PHASES_LIB = os.path.join(ROOT, "adapter_mlp_amd", "liblora_mi355x_phases.so")
 TIMED_BLOCKS = 8192  # block_times' second dimension in the timing build
 
 
@@ -414,6 +415,82 @@ def block_timing(args):
               f"prologue {r['prologue_us']:6.2f}  K loop {r['k_loop_us']:8.2f}  epilogue {r['epilogue_us']:6.2f}  "
               f"gap {r['gap_between_blocks_us']:5.2f} us  clock {r['clock_GHz']:.3f} GHz  "
               f"{r['cycles_per_k_step']:.0f} cycles/step ({100 * r['k_loop_mfma_issue_frac']:.1f}% MFMA issue)",
+              flush=True)
+
+
+def phase_timing_report(rec, name):
+    """Summary of one family's phase records ([64 blocks, 2 groups, 8] uint64,
+    shader-clock stamps of one K step: group 0 = MFMA start, MFMA end, after its
+    load wait, read start, read end; group 1 = read start, read end, MFMA
+    start, MFMA end; word 5 = the next step's start, 6 = K steps)."""
+    import numpy as np
+
+    rec = rec.astype(np.int64)
+    ok = (rec[:, 0, 0] != 0) & (rec[:, 1, 0] != 0) & (rec[:, 0, 5] > rec[:, 0, 0]) & (rec[:, 1, 5] > rec[:, 1, 0])
+    if not ok.any():
+        return None
+    g0, g1 = rec[ok, 0], rec[ok, 1]
+    m = lambda a: float(np.mean(a))  # noqa: E731
+    return {
+        "family": name, "blocks": int(ok.sum()), "k_steps": int(np.median(g0[:, 6])),
+        "cycles_per_k_step": m(g0[:, 5] - g0[:, 0]),
+        "g0_mfma": m(g0[:, 1] - g0[:, 0]), "g0_load_wait": m(g0[:, 2] - g0[:, 1]),
+        "g0_barrier_after_mfma": m(g0[:, 3] - g0[:, 2]), "g0_read": m(g0[:, 4] - g0[:, 3]),
+        "g0_barrier_after_read": m(g0[:, 5] - g0[:, 4]),
+        "g1_read": m(g1[:, 1] - g1[:, 0]), "g1_barrier_after_read": m(g1[:, 2] - g1[:, 1]),
+        "g1_mfma": m(g1[:, 3] - g1[:, 2]), "g1_barrier_after_mfma": m(g1[:, 5] - g1[:, 3]),
+    }
+
+
+def phase_timing(args):
+    """Run the workload on the phase-timing build and summarise one K step of
+    the first 64 blocks of each GEMM family: how long each group's MFMA
+    cluster and read phase take and how long each waits at the barriers, in
+    shader cycles.  Writes profiles/<family>_<workload>_phase_timing.txt."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import adapter_mlp_amd as lm
+    from workload import CONFIGS, make_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if not os.path.exists(PHASES_LIB):
+        raise SystemExit(f"{PHASES_LIB} is missing: build it with `python -m adapter_mlp_amd.build --phases`")
+    lib = lm.load(PHASES_LIB)
+    cfg = CONFIGS[args.config]
+    step = {"mlp": MlpStep, "relu2": Relu2Step, "attn": AttnStep}[cfg.kind](cfg, make_inputs(cfg), lm, torch)
+    for _ in range(max(args.warmup, 1) + max(args.steps, 1)):
+        step()
+    torch.cuda.synchronize()
+    buf = np.zeros((8, 64, 2, 8), dtype=np.uint64)
+    fetch = lib.lora_phase_times
+    fetch.restype = ctypes.c_int
+    fetch.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    rc = fetch(buf.ctypes.data, buf.nbytes)
+    if rc != 0:
+        raise SystemExit(f"lora_phase_times returned HIP error {rc}")
+    names = timing_family_names(cfg)
+    cmd = f"python3 bench.py --config {cfg.cid} --phase-timing --steps {args.steps} --warmup {args.warmup}"
+    for f in range(8):
+        r = phase_timing_report(buf[f], names[f])
+        if r is None:
+            continue
+        lines = [f"# per-phase timing of {names[f]}, workload {cfg.note}: K step 21 of blocks 0-63 of the latest launch",
+                 "# phase-timing build of the library (-DLORA_PHASE_TIMING): lane 0 of the first wavefront of each",
+                 "# group reads the shader clock (s_memtime) at every phase boundary; its stamps change that build's",
+                 "# register allocation (scratch and spilled registers), so its K steps run a little slower",
+                 f"#   python -m adapter_mlp_amd.build --phases && {cmd}",
+                 "# cycles; an MFMA cluster issues 32 MFMAs (1024 cycles at full rate)",
+                 f"source_digest = {source_digest()}"]
+        lines += [f"{k} = {v:.1f}" if isinstance(v, float) else f"{k} = {v}" for k, v in r.items()]
+        with open(os.path.join(ROOT, "profiles", f"{names[f]}_{workload_tag(cfg)}_phase_timing.txt"), "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+        print(f"{names[f]:24s} {r['cycles_per_k_step']:6.0f} cycles/step  g0: MFMA {r['g0_mfma']:5.0f} "
+              f"wait {r['g0_load_wait']:4.0f} barrier {r['g0_barrier_after_mfma']:4.0f} read {r['g0_read']:5.0f} "
+              f"barrier {r['g0_barrier_after_read']:4.0f} | g1: read {r['g1_read']:5.0f} barrier "
+              f"{r['g1_barrier_after_read']:4.0f} MFMA {r['g1_mfma']:5.0f} barrier {r['g1_barrier_after_mfma']:4.0f}",
               flush=True)
 
 
@@ -694,6 +771,9 @@ def main():
     ap.add_argument("--block-timing", action="store_true",
                     help="run on the per-block timing build (liblora_mi355x_timing.so) and write "
                          "profiles/*_block_timing.txt: prologue, K loop, epilogue and clock per GEMM family")
+    ap.add_argument("--phase-timing", action="store_true",
+                    help="run on the per-phase timing build (liblora_mi355x_phases.so) and write "
+                         "profiles/*_phase_timing.txt: MFMA cluster, read phase and barrier waits of one K step")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run a plain fp32 elementwise copy (negation) of MIB MiB "
                          "three times, the known-size kernel that scales HBM byte counters")
@@ -709,6 +789,9 @@ def main():
         return
     if args.block_timing:
         block_timing(args)
+        return
+    if args.phase_timing:
+        phase_timing(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the fused LoRA path runs on a single MI355X here and "

@@ -72,3 +72,20 @@ def test_only_the_timing_build_exports_block_times():
         pytest.skip("libraries not built")
     assert hasattr(ctypes.CDLL(timing), "lora_block_times")
     assert not hasattr(ctypes.CDLL(normal), "lora_block_times")
+
+
+def test_phase_timing_report():
+    rec = np.zeros((64, 2, 8), dtype=np.uint64)
+    for b in range(64):
+        base = 10_000 + 50 * b
+        # group 0: MFMA 1100, wait 10, barrier 80, read 900, barrier 200 (step 2290)
+        rec[b, 0, :7] = [base, base + 1100, base + 1110, base + 1190, base + 2090, base + 2290, 65]
+        # group 1: read 1000, barrier 190, MFMA 1000, then the next step at +2290
+        rec[b, 1, :7] = [base + 1190 - 2290 + 2290, base + 2190, base + 2380, base + 3380, 0, base + 3480, 65]
+    r = bench.phase_timing_report(rec, "gemm_nn_store")
+    assert r["blocks"] == 64 and r["k_steps"] == 65
+    assert r["cycles_per_k_step"] == 2290.0
+    assert (r["g0_mfma"], r["g0_load_wait"], r["g0_barrier_after_mfma"], r["g0_read"], r["g0_barrier_after_read"]) == \
+        (1100.0, 10.0, 80.0, 900.0, 200.0)
+    assert (r["g1_read"], r["g1_barrier_after_read"], r["g1_mfma"], r["g1_barrier_after_mfma"]) == (1000.0, 190.0, 1000.0, 100.0)
+    assert bench.phase_timing_report(np.zeros((64, 2, 8), dtype=np.uint64), "x") is None
