@@ -1,7 +1,8 @@
 // bf16 GEMM core for gfx950: 256x256x64 block tiles, 8 wavefronts in two
 // groups that alternate between MFMA clusters and LDS fragment reads,
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulation, operands moved from global
-// memory into LDS without passing through registers.
+// v_mfma_f32_16x16x32_bf16 (dense weights) or v_mfma_f32_32x32x16_bf16 (NF4
+// weights) with fp32 accumulation, operands moved from global memory into LDS
+// without passing through registers.
 //
 // What it computes (the base projections and the adapter term of the LoRA
 // projections, "LoRA Optimizations" section "Custom autograd functions"; the
@@ -22,10 +23,20 @@
 // Each wavefront stages its results through a private LDS region so global
 // loads and stores move whole 16-byte chunks of consecutive columns.
 //
-// MFMA roles.  The weight tile is the MFMA "A" source (32 rows = output
-// columns n) and the activation tile the "B" source (32 columns = rows m), so
-// each lane ends with 4 consecutive output columns of one row, and the gated
-// activation finds e and g of the same element in the same lane.
+// MFMA roles.  The weight tile is the MFMA "A" source (rows = output columns
+// n) and the activation tile the "B" source (columns = rows m), so each lane
+// ends with 4 consecutive output columns of one row, and the gated activation
+// finds e and g of the same element in the same lane.
+//
+// MFMA shape.  Under a sustained MFMA load the chip is power-limited, and the
+// 16x16x32 instruction, which accumulates over twice the K of 32x32x16 and so
+// reads and writes half the accumulator bytes per flop, holds a higher clock:
+// in a loop of nothing but MFMAs on one block per CU (same operand and
+// accumulator registers) 1.98 against 1.74 GHz.  The dense kernels therefore
+// use 16x16x32 blocks.  The NF4 kernels keep 32x32x16: their unpack is
+// interleaved with the MFMA cluster at about five vector instructions per
+// MFMA, and their matrix cores are busy less than half the time, so the power
+// limit binds less.
 //
 // Operands are read with buffer loads: rows past the end of a matrix read as
 // zero, which covers ragged M and N tiles without clamping.
@@ -154,12 +165,32 @@ __device__ __forceinline__ void for4(F&& f) {
   f(std::integral_constant<int, 3>{});
 }
 
+// A wavefront's accumulators (its 64 output columns x 128 rows) as 32x32 MFMA
+// blocks, f32x16 [2][4] (block i: columns 32 i.., block j: rows 32 j..; lane l
+// holds row 32 j + l % 32, columns 32 i + 8 g + 4 (l / 32) + v in registers
+// 4 g + v), or as 16x16 blocks, f32x4 [4][8] (block i: columns 16 i.., block
+// j: rows 16 j..; lane l holds row 16 j + l % 16, columns 16 i + 4 (l / 16) + v).
+// The epilogues read either as quads: quad q (0..7) of 32-row pass j is four
+// consecutive columns qcol .. qcol + 3 of row qrow of the pass, in one lane.
+// In gate/up tiles quads q < 4 hold gate columns and quad q + 4 the up columns
+// of the same outputs.
+__device__ __forceinline__ f32x4 quad(const f32x16 (&acc)[2][4], int q, int j) {
+  const int i = q >> 2, g = q & 3;
+  return f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+}
+__device__ __forceinline__ int qcol(const f32x16 (&)[2][4], int q, int lane) {
+  return 32 * (q >> 2) + 8 * (q & 3) + 4 * (lane >> 5);
+}
+__device__ __forceinline__ int qrow(const f32x16 (&)[2][4], int, int lane) { return lane & 31; }
+__device__ __forceinline__ f32x4 quad(const f32x4 (&acc)[4][8], int q, int j) { return acc[q >> 1][2 * j + (q & 1)]; }
+__device__ __forceinline__ int qcol(const f32x4 (&)[4][8], int q, int lane) { return 16 * (q >> 1) + 4 * (lane >> 4); }
+__device__ __forceinline__ int qrow(const f32x4 (&)[4][8], int q, int lane) { return 16 * (q & 1) + (lane & 15); }
+
 // Epilogue: each wavefront stages its results (WN output tile columns x 128
-// rows; accumulator block i covers tile columns 32 i.., block j rows 32 j..)
+// rows, read from the accumulators as quads, one 32-row pass at a time)
 // through a private LDS region -- the operand buffers are free once the K
 // loop has ended -- so global loads and stores move 16-byte chunks of
-// consecutive columns.  In dual tiles blocks i < NI/2 hold gate columns and
-// blocks i + NI/2 the up columns of the same outputs.
+// consecutive columns.
 // Backward activation epilogues: region 0 holds the fp32 dh rows of a pass,
 // then (once read) the bf16 gradient rows [NP][32][WN + 8] of the fused
 // rank-r products; then h rows [32][WN + 8] bf16, Pd rows [32][16] bf16 and
@@ -253,12 +284,13 @@ struct FusedU {
 // wholly past the region: the column check is uniform across the wavefront.
 // Rows past M are handled by the range-checked buffer accesses (loads read
 // zero, stores are dropped), so the epilogues carry no per-lane branch.
-template <int WN, bool DUAL, int EPI, int ACT>
-__device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* wstage, const GemmArgs& args,
+template <int WN, bool DUAL, int EPI, int ACT, typename ACC>
+__device__ __forceinline__ void run_epilogue_w(const ACC& acc, char* wstage, const GemmArgs& args,
                                                int reg, int64_t mw, int64_t nbase, int64_t NR, int64_t M,
                                                int lane, int wm, int wn, int kp) {
   // kp >= 0: this block computes K part kp of a split tile (fp32 partial sums)
-  constexpr int NI = WN / 32;
+  static_assert(WN == 64, "the quads cover 64 columns per wavefront");
+  constexpr int NQ = WN / 8;             // quads per 32-row pass
   const bool cols_ok = nbase < NR;  // uniform
   if constexpr (EPI == EPI_STORE) {
     if (kp >= 0) {
@@ -272,13 +304,8 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
       for4([&](auto jc) {
         constexpr int j = decltype(jc)::value;
 #pragma unroll
-        for (int i = 0; i < NI; ++i)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int col = i * 32 + 8 * g + 4 * (lane >> 5);
-            *reinterpret_cast<f32x4*>(stg + (lane & 31) * LD + col) =
-                f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-          }
+        for (int q = 0; q < NQ; ++q)
+          *reinterpret_cast<f32x4*>(stg + qrow(acc, q, lane) * LD + qcol(acc, q, lane)) = quad(acc, q, j);
         wave_sync();
 #pragma unroll
         for (int it = 0; it < 32 / RPP; ++it) {
@@ -302,15 +329,13 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
     for4([&](auto jc) {
       constexpr int j = decltype(jc)::value;
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = i * 32 + 8 * g + 4 * (lane >> 5);
-          u32x2 v;
-          v[0] = pack_bf2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
-          v[1] = pack_bf2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-          *reinterpret_cast<u32x2*>(stg + (lane & 31) * LD + col) = v;
-        }
+      for (int q = 0; q < NQ; ++q) {
+        const f32x4 a = quad(acc, q, j);
+        u32x2 v;
+        v[0] = pack_bf2(a[0], a[1]);
+        v[1] = pack_bf2(a[2], a[3]);
+        *reinterpret_cast<u32x2*>(stg + qrow(acc, q, lane) * LD + qcol(acc, q, lane)) = v;
+      }
       wave_sync();
 #pragma unroll
       for (int it = 0; it < 32 / RPP; ++it) {
@@ -342,25 +367,23 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
       for4([&](auto jc) {
         constexpr int j = decltype(jc)::value;
 #pragma unroll
-        for (int i = 0; i < NI / 2; ++i)
+        for (int q = 0; q < NQ / 2; ++q) {
+          const f32x4 a = quad(acc, q, j), b = quad(acc, q + NQ / 2, j);  // gate, up
+          u32x2 ev, gv, hv;
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int col = i * 32 + 8 * g + 4 * (lane >> 5);
-            u32x2 ev, gv, hv;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              ev[h] = pack_bf2(acc[i][j][4 * g + 2 * h], acc[i][j][4 * g + 2 * h + 1]);
-              gv[h] = pack_bf2(acc[i + NI / 2][j][4 * g + 2 * h], acc[i + NI / 2][j][4 * g + 2 * h + 1]);
-              float p0, p1;
-              act_fwd<false>(ACT, lo_bf(ev[h]), p0);
-              act_fwd<false>(ACT, hi_bf(ev[h]), p1);
-              hv[h] = pack_bf2(p0 * lo_bf(gv[h]), p1 * hi_bf(gv[h]));
-            }
-            const int o = (lane & 31) * LD + col;
-            *reinterpret_cast<u32x2*>(stg + o) = ev;
-            *reinterpret_cast<u32x2*>(stg + ARR + o) = gv;
-            *reinterpret_cast<u32x2*>(stg + 2 * ARR + o) = hv;
+          for (int h = 0; h < 2; ++h) {
+            ev[h] = pack_bf2(a[2 * h], a[2 * h + 1]);
+            gv[h] = pack_bf2(b[2 * h], b[2 * h + 1]);
+            float p0, p1;
+            act_fwd<false>(ACT, lo_bf(ev[h]), p0);
+            act_fwd<false>(ACT, hi_bf(ev[h]), p1);
+            hv[h] = pack_bf2(p0 * lo_bf(gv[h]), p1 * hi_bf(gv[h]));
           }
+          const int o = qrow(acc, q, lane) * LD + qcol(acc, q, lane);
+          *reinterpret_cast<u32x2*>(stg + o) = ev;
+          *reinterpret_cast<u32x2*>(stg + ARR + o) = gv;
+          *reinterpret_cast<u32x2*>(stg + 2 * ARR + o) = hv;
+        }
         wave_sync();
 #pragma unroll
         for (int it = 0; it < 32 / RPP; ++it) {
@@ -397,20 +420,18 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
       for4([&](auto jc) {
         constexpr int j = decltype(jc)::value;
 #pragma unroll
-        for (int i = 0; i < NI; ++i)
+        for (int q = 0; q < NQ; ++q) {
+          const f32x4 a = quad(acc, q, j);
+          u32x2 uv, hv;
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int col = i * 32 + 8 * g + 4 * (lane >> 5);
-            u32x2 uv, hv;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              uv[h] = pack_bf2(acc[i][j][4 * g + 2 * h], acc[i][j][4 * g + 2 * h + 1]);
-              hv[h] = pack_bf2(relu2(lo_bf(uv[h])), relu2(hi_bf(uv[h])));
-            }
-            const int o = (lane & 31) * LD + col;
-            *reinterpret_cast<u32x2*>(stg + o) = uv;
-            *reinterpret_cast<u32x2*>(stg + ARR + o) = hv;
+          for (int h = 0; h < 2; ++h) {
+            uv[h] = pack_bf2(a[2 * h], a[2 * h + 1]);
+            hv[h] = pack_bf2(relu2(lo_bf(uv[h])), relu2(hi_bf(uv[h])));
           }
+          const int o = qrow(acc, q, lane) * LD + qcol(acc, q, lane);
+          *reinterpret_cast<u32x2*>(stg + o) = uv;
+          *reinterpret_cast<u32x2*>(stg + ARR + o) = hv;
+        }
         wave_sync();
 #pragma unroll
         for (int it = 0; it < 32 / RPP; ++it) {
@@ -525,13 +546,8 @@ __device__ __forceinline__ void run_epilogue_w(f32x16 (&acc)[WN / 32][4], char* 
         for (int p = 0; p < NP; ++p) pacc[p][0] = pacc[p][1] = f32x4{0, 0, 0, 0};
         if (cols_ok) {
 #pragma unroll
-          for (int i = 0; i < NI; ++i)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int col = i * 32 + 8 * g + 4 * (lane >> 5);
-              *reinterpret_cast<f32x4*>(stg + (lane & 31) * LD + col) =
-                  f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-            }
+          for (int q = 0; q < NQ; ++q)
+            *reinterpret_cast<f32x4*>(stg + qrow(acc, q, lane) * LD + qcol(acc, q, lane)) = quad(acc, q, j);
           // Pd and U_p rows of this pass: lane l loads half l & 1 of row l / 2 (rows past M read zero)
           const int64_t mh = mw + j * 32 + (lane >> 1);
           u32x4 pv = u32x4{0, 0, 0, 0};
@@ -765,12 +781,13 @@ __device__ __forceinline__ u32x4 nf4_decode8(uint32_t w, const Nf4Planes& p) {
 // ---------------------------------------------------------------------------
 // Dense weights.  8 wavefronts in two groups of 4, one wavefront of each
 // group on every SIMD, working in alternating phases separated by barriers:
-// while group 0 runs a cluster of 32 MFMAs on fragments already in its
-// registers, group 1 reads the fragments of its next cluster from LDS, and
-// then the roles swap -- the SIMD's matrix unit always has one wavefront
-// feeding it and LDS latency never sits between two MFMAs.  Each wavefront
-// owns a 128x64 sub-tile (8 accumulators of 32x32); group g covers tile rows
-// 128 g .. 128 g + 127.
+// while group 0 runs a cluster of MFMAs (one K step: 64 of 16x16x32, or 32
+// of 32x32x16 in the NF4 kernels) on fragments already in its registers,
+// group 1 reads the fragments of its next cluster from LDS, and then the
+// roles swap -- the SIMD's matrix unit always has one wavefront feeding it and
+// LDS latency never sits between two MFMAs.  Each wavefront owns a 128x64
+// sub-tile (32 accumulators of 16x16, or 8 of 32x32); group g covers tile
+// rows 128 g .. 128 g + 127.
 //
 // Operands go from global memory straight into LDS (buffer_load_dwordx4 ...
 // lds: lane i of a load writes bytes 16 i .. 16 i + 15 of a 1 KB LDS block
@@ -1138,21 +1155,40 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   };
 
   // ---- fragment reads ----
-  // NN weights: lane s of read h (0, 1) of K slice ks points at K row
+  // Dense kernels run 16x16x32 MFMA blocks, NF4 kernels 32x32x16 (file
+  // header).  fa holds the weight (A) fragments of one K step and fb the
+  // activation (B) fragments: fa[4 ks + i], fb[8 ks + j] over two K slices ks
+  // of 32 (16x16x32), fa[2 ks + i], fb[4 ks + j] over four K slices of 16
+  // (32x32x16).
+  constexpr bool M16 = !NF4;
+  // NN weights, 32x32x16: lane s of read h (0, 1) of K slice ks points at K row
   //   16 ks + 8 (g >> 1) + 4 h + (s & 15) / 4 and columns nb + 16 (g & 1) + 4 (s & 3), g = s / 16
-  // (rows 4 h apart; in the NF4 swizzle the two reads' chunk positions differ)
+  // (rows 4 h apart; in the NF4 swizzle the two reads' chunk positions differ).
+  // NN weights, 16x16x32: lane s of read h of K slice ks points at K row
+  //   32 ks + 8 (s / 16) + 4 h + (s & 15) / 4 and columns nb + 4 (s & 3) of its 16-column
+  // fragment.  Fragment i = 2 p + e starts at column nb_p + 16 e, whose chunk index is that
+  // of nb_p plus 2 e; bit 1 of the chunk index is clear in nb_p's and in the dense swizzle,
+  // so e adds 32 bytes to fa_nn[p].
   int fa_nn[2], fa_nn4[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int half = DUAL ? i : (wn >> 1);
-    const int nb = DUAL ? wn * 32 : (wn & 1) * 64 + 32 * i;
-    const int g = lane >> 4;
-    const int n = nb + 16 * (g & 1) + 4 * (lane & 3);
-    const int k0 = 8 * (g >> 1) + ((lane & 15) >> 2);  // K row of read h = 0 in slice 0
-    fa_nn[i] = half * HALF_BYTES + k0 * 256 + (((n >> 3) ^ nn_swz<NF4>(k0)) * 16) + (lane & 1) * 8;
-    fa_nn4[i] = half * HALF_BYTES + (k0 + 4) * 256 + (((n >> 3) ^ nn_swz<NF4>(k0 + 4)) * 16) + (lane & 1) * 8;
+    if constexpr (M16) {
+      const int nb = DUAL ? wn * 32 : (wn & 1) * 64 + 32 * i;
+      const int n = nb + 4 * (lane & 3);
+      const int k0 = 8 * (lane >> 4) + ((lane & 15) >> 2);  // K row of read h = 0 in slice 0
+      fa_nn[i] = half * HALF_BYTES + k0 * 256 + (((n >> 3) ^ nn_swz<false>(k0)) * 16) + (lane & 1) * 8;
+      fa_nn4[i] = 0;
+    } else {
+      const int nb = DUAL ? wn * 32 : (wn & 1) * 64 + 32 * i;
+      const int g = lane >> 4;
+      const int n = nb + 16 * (g & 1) + 4 * (lane & 3);
+      const int k0 = 8 * (g >> 1) + ((lane & 15) >> 2);  // K row of read h = 0 in slice 0
+      fa_nn[i] = half * HALF_BYTES + k0 * 256 + (((n >> 3) ^ nn_swz<NF4>(k0)) * 16) + (lane & 1) * 8;
+      fa_nn4[i] = half * HALF_BYTES + (k0 + 4) * 256 + (((n >> 3) ^ nn_swz<NF4>(k0 + 4)) * 16) + (lane & 1) * 8;
+    }
   }
-  // K-contiguous tiles: row r0 + 32 j (r0 = first row of the sub-tile + lane % 32)
+  // K-contiguous tiles, 32x32x16: row r0 + 32 j (r0 = first row of the sub-tile + lane % 32)
   // has swz = swz(r0) ^ 4 (j & 1), so chunk 2 ks + lane / 32 sits at
   // (2 ks ^ 4 (j & 1)) ^ x with x = (lane / 32) ^ swz(r0): four per-lane offsets
   // cover every (ks, j); the row term is an immediate.
@@ -1161,58 +1197,123 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
 #pragma unroll
     for (int y = 0; y < 4; ++y) o[y] = r0 * 128 + (((2 * y) ^ x) * 16);
   };
+  // K-contiguous tiles, 16x16x32: lane l reads row r0 + 16 b + l % 16 (r0 a multiple of 16),
+  // chunk 4 ks + l / 16, stored at that chunk ^ swz(row).  There swz(row) =
+  // (l % 16 & 7) ^ (l % 16 >> 3) ^ z(b) with z(b) = ((r0 >> 3) + 2 b) & 7, and
+  // z(b + 2) = z(b) ^ 4, so the chunk sits at (x ^ z(b & 1)) ^ 4 (ks ^ (b >> 1 & 1)),
+  // x = (l / 16) ^ (l % 16 & 7) ^ (l % 16 >> 3): four per-lane offsets o[kc16_at(ks, b)]
+  // cover every (ks, b); the row term 16 b is an immediate.
+  auto kc16_offsets = [&](int r0, int (&o)[4]) {
+    const int l16 = lane & 15;
+    const int x = (lane >> 4) ^ (l16 & 7) ^ (l16 >> 3);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int u = x ^ (((r0 >> 3) + 2 * e) & 7);
+#pragma unroll
+      for (int f = 0; f < 2; ++f) o[2 * e + f] = (r0 + l16) * 128 + ((u ^ (4 * f)) * 16);
+    }
+  };
+  const auto kc16_at = [](int ks, int b) { return 2 * (b & 1) + (ks ^ ((b >> 1) & 1)); };
   int ao[4];
-  kc_offsets(wm * 128 + (lane & 31), ao);
-  // NT weights: fragment i of wavefront wn is tile row wn * 64 + 32 i + lane % 32;
-  // in gate/up tiles, gate row wn * 32 + lane % 32 (i = 0) and the up row 128
-  // below it (i = 1), whose swizzle is the same
+  if constexpr (M16) kc16_offsets(wm * 128, ao);
+  else kc_offsets(wm * 128 + (lane & 31), ao);
+  // NT weights: the wavefront's 64 tile rows from wn * 64; in gate/up tiles the
+  // 32 gate rows from wn * 32 and the up rows 128 below them, whose swizzle is
+  // the same
   int bo[4];
-  if constexpr (BKIND == B_NT) kc_offsets(DUAL ? wn * 32 + (lane & 31) : wn * 64 + (lane & 31), bo);
+  if constexpr (BKIND == B_NT) {
+    if constexpr (M16) kc16_offsets(DUAL ? wn * 32 : wn * 64, bo);
+    else kc_offsets(DUAL ? wn * 32 + (lane & 31) : wn * 64 + (lane & 31), bo);
+  }
 
-  bf16x8 fa[4][2], fb[4][4];
-  // between(ks) runs after the fragment reads of K slice ks
+  bf16x8 fa[8], fb[16];
+  // between(c) runs after each quarter c (0..3) of the step's fragment reads
   auto read = [&](int aslot, int wslot, auto&& between) {
     const lds_char* const at = lds + aslot * SLOT_BYTES;
     const lds_char* const wt = lds + W_RING + wslot * SLOT_BYTES;
+    if constexpr (M16) {
+      // quarter 2 ks + h: weight fragments 2 h, 2 h + 1 and activation
+      // fragments 4 h .. 4 h + 3 of K slice ks
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        if constexpr (BKIND == B_NN) {
-          if constexpr (NF4)
-            fa[ks][i] = lds_read_tr8(wt + fa_nn[i] + (16 * ks) * 256, wt + fa_nn4[i] + (16 * ks) * 256);
-          else
-            fa[ks][i] = lds_read_tr8(wt + fa_nn[i] + (16 * ks) * 256, 4 * 256);
-        } else {
-          const int y = DUAL ? ks : ((2 * ks) ^ (4 * (i & 1))) >> 1;
-          fa[ks][i] = __builtin_bit_cast(bf16x8, lds_read16(wt + bo[y] + i * (DUAL ? 128 : 32) * 128));
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int i = 2 * h + e;
+            if constexpr (BKIND == B_NN)
+              fa[4 * ks + i] = lds_read_tr8(wt + fa_nn[h] + 32 * e + (32 * ks) * 256, 4 * 256);
+            else if constexpr (DUAL)
+              fa[4 * ks + i] =
+                  __builtin_bit_cast(bf16x8, lds_read16(wt + bo[kc16_at(ks, e)] + 2048 * e + 16384 * h));
+            else
+              fa[4 * ks + i] = __builtin_bit_cast(bf16x8, lds_read16(wt + bo[kc16_at(ks, i)] + 2048 * i));
+          }
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int j = 4 * h + jj;
+            fb[8 * ks + j] = __builtin_bit_cast(bf16x8, lds_read16(at + ao[kc16_at(ks, j)] + 2048 * j));
+          }
+          between(2 * ks + h);
         }
-      }
+    } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int y = ((2 * ks) ^ (4 * (j & 1))) >> 1;
-        fb[ks][j] = __builtin_bit_cast(bf16x8, lds_read16(at + ao[y] + j * 32 * 128));
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          if constexpr (BKIND == B_NN) {
+            if constexpr (NF4)
+              fa[2 * ks + i] = lds_read_tr8(wt + fa_nn[i] + (16 * ks) * 256, wt + fa_nn4[i] + (16 * ks) * 256);
+            else
+              fa[2 * ks + i] = lds_read_tr8(wt + fa_nn[i] + (16 * ks) * 256, 4 * 256);
+          } else {
+            const int y = DUAL ? ks : ((2 * ks) ^ (4 * (i & 1))) >> 1;
+            fa[2 * ks + i] = __builtin_bit_cast(bf16x8, lds_read16(wt + bo[y] + i * (DUAL ? 128 : 32) * 128));
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int y = ((2 * ks) ^ (4 * (j & 1))) >> 1;
+          fb[4 * ks + j] = __builtin_bit_cast(bf16x8, lds_read16(at + ao[y] + j * 32 * 128));
+        }
+        between(ks);
       }
-      between(ks);
     }
   };
   const auto nothing = [](int) {};
 
-  f32x16 acc[2][4];
+  std::conditional_t<M16, f32x4[4][8], f32x16[2][4]> acc;
+  if constexpr (M16) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+      for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  }
   // the MFMA phase runs at raised wavefront priority, so the SIMD's other
   // wavefront (in its read phase) cannot delay the MFMA issue
   auto mma_body = [&]() {
+    if constexpr (M16) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < 8; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[4 * ks + i], fb[8 * ks + j], acc[i][j], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[2 * ks + i], fb[4 * ks + j], acc[i][j], 0, 0, 0);
+    }
   };
   auto mma = [&]() {
     __builtin_amdgcn_s_setprio(1);
@@ -1228,20 +1329,22 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   // after the K loop: the dense adapter tile of these GEMMs comes packed in the
   // same column order (the pack job's perm8).
   auto restore_cols = [&]() {
+    if constexpr (!M16) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          float n0, n1, n2, n3;
-          swap_lane_halves(acc[i][j][4 * k], acc[i][j][4 * k + 2], n0, n1);
-          swap_lane_halves(acc[i][j][4 * k + 1], acc[i][j][4 * k + 3], n2, n3);
-          acc[i][j][4 * k] = n0;
-          acc[i][j][4 * k + 1] = n1;
-          acc[i][j][4 * k + 2] = n2;
-          acc[i][j][4 * k + 3] = n3;
-        }
+          for (int k = 0; k < 4; ++k) {
+            float n0, n1, n2, n3;
+            swap_lane_halves(acc[i][j][4 * k], acc[i][j][4 * k + 2], n0, n1);
+            swap_lane_halves(acc[i][j][4 * k + 1], acc[i][j][4 * k + 3], n2, n3);
+            acc[i][j][4 * k] = n0;
+            acc[i][j][4 * k + 1] = n1;
+            acc[i][j][4 * k + 2] = n2;
+            acc[i][j][4 * k + 3] = n3;
+          }
+    }
   };
   // MFMA cluster with the store half of an unpack interleaved: about five of
   // its vector instructions after each MFMA (its inputs are in registers).
