@@ -93,19 +93,35 @@ namespace {
 
 constexpr int BM = 256, BK = 64;
 
-// XOR swizzle of the 16-byte chunk index inside a 128-byte LDS row.  Rows read
-// together by an MFMA fragment load (8 consecutive rows) and rows written
-// together land in different banks.
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+// XOR swizzle of the 16-byte chunk index inside a 128-byte LDS row (K-contiguous
+// tiles).  A 16-byte LDS read is served a group of lanes at a time, and lanes
+// of one group that touch the same bank are serialised.  Timed on the device
+// (8 wavefronts of back-to-back ds_read_b128, in-bounds offsets):
+//   32x32x16 fragments (lane l: row l % 32, chunk 2 ks + l / 32), swizzle
+//     (r ^ r >> 3) & 7: full rate, the same as 64 consecutive 16-byte chunks;
+//   16x16x32 fragments (lane l: row l % 16, chunk 4 ks + l / 16): half rate
+//     under (r ^ r >> 3) & 7 and several other swizzles, full rate under r & 7.
+// The dense kernels (16x16x32 reads) therefore take r & 7, and the NF4
+// kernels (32x32x16 reads, and an unpack that writes 64 consecutive rows at
+// one chunk) keep (r ^ r >> 3) & 7.
+template <bool M16>
+__device__ __forceinline__ int swz(int row) {
+  return M16 ? (row & 7) : ((row ^ (row >> 3)) & 7);
+}
 
 // NN weight tiles (256-byte rows of 16 chunks): chunk c of K row k sits at
 // c ^ nn_swz(k).  A dense tile is written by global -> LDS loads that fill
 // whole rows, so only the transposing fragment reads (4 rows x 4 chunks at a
-// time) need spreading over the banks: 4 (k & 3).  An NF4 tile is written by
-// the unpack, 16 lanes at a time over 8 rows and 2 chunks 8 apart, so its
-// swizzle also spreads 8 consecutive rows: 4 (k & 3) + ((k >> 1) & 3) keeps
-// any 4 aligned rows x 4 aligned chunks and any 8 aligned rows x {c, c + 8}
-// on distinct chunk positions.
+// time) need spreading over the banks: 4 (k & 3).  Under the 16x16x32 reads
+// (lanes 16 g + 4 j + q: K row 8 g + j) the bank-conflict counter charges each
+// transposing read two extra cycles, which 4 (k & 3) ^ 2 (k >> 3 & 1) removes;
+// that layout measured no faster (those reads issue at about one per five
+// cycles and wavefront anyway, and it needs two more offset registers), so the
+// plain one stays.
+// An NF4 tile is written by the unpack, 16 lanes at a time over 8 rows and 2
+// chunks 8 apart, so its swizzle also spreads 8 consecutive rows:
+// 4 (k & 3) + ((k >> 1) & 3) keeps any 4 aligned rows x 4 aligned chunks and
+// any 8 aligned rows x {c, c + 8} on distinct chunk positions.
 template <bool NF4>
 __device__ __forceinline__ int nn_swz(int k) {
   return NF4 ? (((k & 3) << 2) | ((k >> 1) & 3)) : ((k & 3) << 2);
@@ -893,9 +909,13 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
 
   // ---- loads: 8 blocks of 1 KB per wavefront and step ----
   // K-contiguous block q = 8 wn + i holds rows 8 q + lane / 8; its row r has
-  // swz(r) = (lane / 8) ^ i, so lane takes logical chunk (lane % 8) ^ (lane / 8) ^ i.
+  // swz(r) = (lane / 8) ^ kc_i(i), kc_i(i) = 0 (dense) or i (NF4), so lane
+  // takes logical chunk (lane % 8) ^ (lane / 8) ^ kc_i(i).
   // NN block q' = 8 (wn & 1) + i of half wn >> 1 holds K rows 4 q' + lane / 16,
-  // lane takes logical chunk (lane % 16) ^ 4 (lane / 16).
+  // lane takes logical chunk (lane % 16) ^ 4 (lane / 16) (dense) or the NF4
+  // swizzle of its row (the adapter tile of an NF4 GEMM).
+  constexpr bool M16 = !NF4;  // 16x16x32 MFMA blocks (fragment reads below)
+  const auto kc_i = [](int i) { return M16 ? 0 : i; };
   const int kc_row = wn * 64 + (lane >> 3);
   const int kc_x = (lane & 7) ^ (lane >> 3);
   const int nn_row = (wn & 1) * 32 + (lane >> 4);
@@ -991,7 +1011,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
     const uint32_t base = (uint32_t)r * lld2;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (i >= i0 && i < i1) dma16(ra, base + (uint32_t)((x ^ i) << 4), dst + i * 1024, (uint32_t)(8 * i) * lld2);
+      if (i >= i0 && i < i1) dma16(ra, base + (uint32_t)((x ^ kc_i(i)) << 4), dst + i * 1024, (uint32_t)(8 * i) * lld2);
   };
   auto issue_w = [&](int slot, int i0, int i1) {  // group 1: (dense) weight tile of the next step
     const uint32_t wslot = lds_addr(lds) + W_RING + slot * SLOT_BYTES;
@@ -1005,7 +1025,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
       const uint32_t dst = wslot + wn * 8 * 1024;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        if (i >= i0 && i < i1) dma16(rb, base + (uint32_t)((x ^ i) << 4), dst + i * 1024, (uint32_t)(8 * i) * lld2);
+        if (i >= i0 && i < i1) dma16(rb, base + (uint32_t)((x ^ kc_i(i)) << 4), dst + i * 1024, (uint32_t)(8 * i) * lld2);
     } else if constexpr (!NF4) {
       int nr = nn_row, nc = nn_chunk;
       asm volatile("" : "+v"(nr), "+v"(nc));
@@ -1148,7 +1168,7 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
         off = (wn >> 1) * HALF_BYTES + k * 256 + ((c ^ nn_swz<true>(k)) << 4);
       } else {
         const int c = 4 * h + d;
-        off = b * 128 + ((c ^ swz(b)) << 4);
+        off = b * 128 + ((c ^ swz<false>(b)) << 4);
       }
       *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(wt + (off & omask)) = v;
     }
@@ -1160,7 +1180,6 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   // activation (B) fragments: fa[4 ks + i], fb[8 ks + j] over two K slices ks
   // of 32 (16x16x32), fa[2 ks + i], fb[4 ks + j] over four K slices of 16
   // (32x32x16).
-  constexpr bool M16 = !NF4;
   // NN weights, 32x32x16: lane s of read h (0, 1) of K slice ks points at K row
   //   16 ks + 8 (g >> 1) + 4 h + (s & 15) / 4 and columns nb + 16 (g & 1) + 4 (s & 3), g = s / 16
   // (rows 4 h apart; in the NF4 swizzle the two reads' chunk positions differ).
@@ -1193,27 +1212,21 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   // (2 ks ^ 4 (j & 1)) ^ x with x = (lane / 32) ^ swz(r0): four per-lane offsets
   // cover every (ks, j); the row term is an immediate.
   auto kc_offsets = [&](int r0, int (&o)[4]) {
-    const int x = (lane >> 5) ^ swz(r0);
+    const int x = (lane >> 5) ^ swz<false>(r0);
 #pragma unroll
     for (int y = 0; y < 4; ++y) o[y] = r0 * 128 + (((2 * y) ^ x) * 16);
   };
   // K-contiguous tiles, 16x16x32: lane l reads row r0 + 16 b + l % 16 (r0 a multiple of 16),
-  // chunk 4 ks + l / 16, stored at that chunk ^ swz(row).  There swz(row) =
-  // (l % 16 & 7) ^ (l % 16 >> 3) ^ z(b) with z(b) = ((r0 >> 3) + 2 b) & 7, and
-  // z(b + 2) = z(b) ^ 4, so the chunk sits at (x ^ z(b & 1)) ^ 4 (ks ^ (b >> 1 & 1)),
-  // x = (l / 16) ^ (l % 16 & 7) ^ (l % 16 >> 3): four per-lane offsets o[kc16_at(ks, b)]
-  // cover every (ks, b); the row term 16 b is an immediate.
+  // chunk 4 ks + l / 16, stored at that chunk ^ (l % 16 & 7) (the dense swizzle depends on
+  // the row's low 3 bits only): one per-lane offset per K slice, o[ks]; the row term 16 b
+  // is an immediate.
   auto kc16_offsets = [&](int r0, int (&o)[4]) {
     const int l16 = lane & 15;
-    const int x = (lane >> 4) ^ (l16 & 7) ^ (l16 >> 3);
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int u = x ^ (((r0 >> 3) + 2 * e) & 7);
-#pragma unroll
-      for (int f = 0; f < 2; ++f) o[2 * e + f] = (r0 + l16) * 128 + ((u ^ (4 * f)) * 16);
-    }
+    for (int ks = 0; ks < 2; ++ks) o[ks] = (r0 + l16) * 128 + ((((4 * ks) | (lane >> 4)) ^ swz<true>(l16)) * 16);
+    o[2] = o[3] = 0;
   };
-  const auto kc16_at = [](int ks, int b) { return 2 * (b & 1) + (ks ^ ((b >> 1) & 1)); };
+  const auto kc16_at = [](int ks, int) { return ks; };
   int ao[4];
   if constexpr (M16) kc16_offsets(wm * 128, ao);
   else kc_offsets(wm * 128 + (lane & 31), ao);
