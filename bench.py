@@ -315,7 +315,8 @@ def block_timing_report(rec, name, tile_mfma_cycles=2048):
     K-loop end and epilogue end in 10 ns units; shader clock at entry and
     exit; hardware ids; grid size | K steps << 32).  The K loop's MFMA issue
     fraction is the ideal cycles of one 256 x 256 x 64 step per SIMD (two
-    wavefronts x 32 MFMAs x 32 cycles) over the measured cycles per step."""
+    wavefronts x 64 MFMAs x 16 cycles in the dense kernels, 32 x 32 cycles in
+    the NF4 kernels) over the measured cycles per step."""
     import numpy as np
 
     rec = rec.astype(np.int64)
@@ -400,7 +401,8 @@ def block_timing(args):
                  "# 100 MHz real-time clock at entry, at the start and the end of its K loop and after the",
                  "# epilogue, and the shader clock (s_memtime) at entry and exit",
                  f"#   python -m adapter_mlp_amd.build --timing && {cmd}",
-                 "# k_loop_mfma_issue_frac = 2048 (two wavefronts x 32 MFMAs x 32 cycles per SIMD and K step)",
+                 "# k_loop_mfma_issue_frac = 2048 (two wavefronts x one K step's MFMAs per SIMD: 64 x 16 cycles",
+                 "#   (16x16x32, dense kernels) or 32 x 32 cycles (32x32x16, NF4 kernels))",
                  "#   / measured shader cycles per K step",
                  f"source_digest = {source_digest()}"]
         if names[f].endswith("_nf4"):
@@ -482,7 +484,8 @@ def phase_timing(args):
                  "# group reads the shader clock (s_memtime) at every phase boundary; its stamps change that build's",
                  "# register allocation (scratch and spilled registers), so its K steps run a little slower",
                  f"#   python -m adapter_mlp_amd.build --phases && {cmd}",
-                 "# cycles; an MFMA cluster issues 32 MFMAs (1024 cycles at full rate)",
+                 "# cycles; an MFMA cluster issues one K step's MFMAs (64 of 16x16x32 in the dense kernels,",
+                 "#   32 of 32x32x16 in the NF4 kernels; 1024 cycles at full rate)",
                  f"source_digest = {source_digest()}"]
         lines += [f"{k} = {v:.1f}" if isinstance(v, float) else f"{k} = {v}" for k, v in r.items()]
         with open(os.path.join(ROOT, "profiles", f"{names[f]}_{workload_tag(cfg)}_phase_timing.txt"), "w") as fh:
