@@ -938,6 +938,14 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   int lwcols = 0;
   // every field is assigned on every call (selects, no early exits), so the
   // cursor stays in scalar registers
+  // Dense kernels: the per-lane source offset of this wavefront's 8 loads is
+  // the same for all of them (the swizzle r & 7 of a K-contiguous block
+  // depends only on lane / 8, and a dense NN block needs none per load), so it
+  // is formed once per segment and held in a register; the loads differ only
+  // in their scalar offset.  Forming it per load pair took a v_mul_lo_u32 and
+  // three more vector instructions from every read phase (measured: config 2
+  // -1.3%).
+  uint32_t dma_base = 0;
   auto cur_begin = [&]() {
     const GemmSeg& S = args.seg[lseg];
     const BSrc& B = S.b[reg][DUAL ? (wn >> 1) : 0];
@@ -963,6 +971,15 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
     ln = act ? (M - m0) * S.lda * 2 : nw;
     lld2 = (uint32_t)((act ? S.lda : B.ld) * 2);
     lstep = act ? (int64_t)BK * 2 : sw;
+    if constexpr (M16) {
+      // the loaders' row and chunk (kc_row / kc_x, nn_row / nn_chunk), formed
+      // from the thread index here so that none of them stays live in the loop
+      const int l = (int)threadIdx.x & 63;
+      const int kr = (BKIND == B_NT && DUAL && !act ? (wn & 1) * 64 : wn * 64) + (l >> 3);
+      const int r = (act || BKIND == B_NT) ? kr : (wn & 1) * 32 + (l >> 4);
+      const int c = (act || BKIND == B_NT) ? ((l & 7) ^ (l >> 3)) : ((l & 15) ^ (4 * ((l >> 4) & 3)));
+      dma_base = (uint32_t)r * lld2 + (uint32_t)(c << 4);
+    }
     if constexpr (NF4) {  // NF4 segment (group 1): codes and scales
       lcodes = B.codes;
       lq8 = B.q8;
@@ -1003,8 +1020,16 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   // this measured 1.2% less step time than all 8 after the reads.
   auto issue_a = [&](int slot, int i0, int i1) {  // group 0: activation tile of the next step
     const uint32_t dst = lds_addr(lds) + slot * SLOT_BYTES + wn * 8 * 1024;
-    // opaque copies: keep the per-lane terms from being expanded per block
-    // and hoisted out of the K loop (8 live offsets would not fit)
+    if constexpr (M16) {
+      const i32x4 ra = rsrc_words(lp, ln);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (i >= i0 && i < i1) dma16(ra, dma_base, dst + i * 1024, (uint32_t)(8 * i) * lld2);
+      return;
+    }
+    // NF4 kernels (per-load swizzle terms): opaque copies keep the per-lane
+    // terms from being expanded per load and hoisted out of the K loop (8 live
+    // offsets would not fit)
     int x = kc_x, r = kc_row;
     asm volatile("" : "+v"(x), "+v"(r));
     const i32x4 ra = rsrc_words(lp, ln);
@@ -1016,7 +1041,13 @@ __global__ __launch_bounds__(NTH8, 1) void gemm_kernel(const GemmArgs args) {
   auto issue_w = [&](int slot, int i0, int i1) {  // group 1: (dense) weight tile of the next step
     const uint32_t wslot = lds_addr(lds) + W_RING + slot * SLOT_BYTES;
     const i32x4 rb = rsrc_words(lp, ln);
-    if constexpr (BKIND == B_NT) {
+    if constexpr (M16) {
+      const uint32_t dst = BKIND == B_NT ? wslot + wn * 8 * 1024 : wslot + (wn >> 1) * HALF_BYTES + (wn & 1) * 8 * 1024;
+      const uint32_t step = BKIND == B_NT ? 8 : 4;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (i >= i0 && i < i1) dma16(rb, dma_base, dst + i * 1024, (uint32_t)(step * i) * lld2);
+    } else if constexpr (BKIND == B_NT) {
       // source row in the loader's column group (gate/up tiles: wn & 1 picks
       // the 64-row half); the LDS row and its swizzle are those of the tile
       int x = kc_x, r = DUAL ? (wn & 1) * 64 + (lane >> 3) : kc_row;
